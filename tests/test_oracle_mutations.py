@@ -1,0 +1,121 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one.  Every mutation is applied through monkeypatch, so the real
+oracle is untouched once the test ends."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.dense_oracle as D
+from tests import test_oracle_pins as P
+
+
+def _expect_pin_failure(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_dropped_bias_caught(monkeypatch):
+    real = D.dense_act_fwd
+
+    def no_bias(X, W, b, act):
+        return real(X, W, None, act)
+
+    monkeypatch.setattr(O, "dense_act_fwd", no_bias)
+    _expect_pin_failure(P.test_dense_fwd_brute_force, O.ACT_IDENTITY, (3, 5, 4))
+
+
+def test_transposed_weight_caught(monkeypatch):
+    def transposed(X, W, b, act):
+        X = np.asarray(X, np.float64)
+        W = np.asarray(W, np.float64)
+        n = min(W.shape)
+        Z = X[:, :n] @ W[:n, :n] + np.asarray(b, np.float64)[None, :n]
+        return D.act_fwd(Z, act), Z
+
+    monkeypatch.setattr(O, "dense_act_fwd", transposed)
+    _expect_pin_failure(P.test_dense_fwd_brute_force, O.ACT_RELU, (4, 6, 3))
+
+
+def test_gelu_grad_dropped_term_caught(monkeypatch):
+    real = D.act_grad
+
+    def wrong(z, act):
+        if act == O.ACT_GELU_TANH:
+            t = D._gelu_tanh_inner(np.asarray(z, np.float64))
+            return 0.5 * (1.0 + t)  # the z (1 - t^2) term dropped
+        return real(z, act)
+
+    monkeypatch.setattr(O, "act_grad", wrong)
+    _expect_pin_failure(P.test_act_grad_central_difference, O.ACT_GELU_TANH)
+
+
+def test_vjp_wrong_sign_caught(monkeypatch):
+    real = D.dense_act_vjp
+
+    def wrong(dY, Z, X, W, act, need_dx=True, mask=None):
+        dX, dW, db = real(dY, Z, X, W, act, need_dx, mask)
+        return dX, -dW, db
+
+    monkeypatch.setattr(O, "dense_act_vjp", wrong)
+    _expect_pin_failure(P.test_vjp_central_difference, O.ACT_RELU)
+
+
+def test_db_over_wrong_axis_caught(monkeypatch):
+    real = D.dense_act_vjp
+
+    def wrong(dY, Z, X, W, act, need_dx=True, mask=None):
+        dX, dW, _ = real(dY, Z, X, W, act, need_dx, mask)
+        G = np.asarray(dY, np.float64) * D.act_grad(Z, act)
+        return dX, dW, G.sum(axis=1)[: dW.shape[0]]
+
+    monkeypatch.setattr(O, "dense_act_vjp", wrong)
+    _expect_pin_failure(P.test_vjp_db_is_column_sum_of_masked_grad, O.ACT_IDENTITY)
+
+
+def test_xent_missing_batch_mean_caught(monkeypatch):
+    real = D.softmax_xent_fwd_bwd
+
+    def wrong(z, y):
+        loss, dz, row = real(z, y)
+        return loss, dz * len(y), row
+
+    monkeypatch.setattr(O, "softmax_xent_fwd_bwd", wrong)
+    _expect_pin_failure(P.test_xent_matches_library_routines)
+
+
+def test_xent_wrong_label_index_caught(monkeypatch):
+    def wrong(z, y):
+        return D.softmax_xent_fwd_bwd(z, (np.asarray(y) + 1) % np.asarray(z).shape[1])
+
+    monkeypatch.setattr(O, "softmax_xent_fwd_bwd", wrong)
+    _expect_pin_failure(P.test_xent_matches_library_routines)
+
+
+def test_adamw_missing_bias_correction_caught(monkeypatch):
+    def wrong(w, g, m, v, lr, b1, b2, eps, wd, t):
+        w = np.asarray(w, np.float64) * (1 - lr * wd)
+        m = b1 * np.asarray(m, np.float64) + (1 - b1) * np.asarray(g)
+        v = b2 * np.asarray(v, np.float64) + (1 - b2) * np.asarray(g) ** 2
+        return w - lr * m / (np.sqrt(v) + eps), m, v
+
+    monkeypatch.setattr(O, "adamw_step", wrong)
+    _expect_pin_failure(P.test_adamw_step1_closed_form)
+
+
+def test_adamw_coupled_decay_caught(monkeypatch):
+    def coupled(w, g, m, v, lr, b1, b2, eps, wd, t):
+        g = np.asarray(g, np.float64) + wd * np.asarray(w, np.float64)
+        return D.adamw_step(w, g, m, v, lr, b1, b2, eps, 0.0, t)
+
+    monkeypatch.setattr(O, "adamw_step", coupled)
+    _expect_pin_failure(P.test_adamw_matches_torch_adamw_many_steps)
+
+
+def test_mlp_missing_hidden_mask_caught(monkeypatch):
+    real = D.dense_act_vjp
+
+    def no_mask(dY, Z, X, W, act, need_dx=True, mask=None):
+        return real(dY, Z, X, W, O.ACT_IDENTITY, need_dx, None)
+
+    monkeypatch.setattr(D, "dense_act_vjp", no_mask)
+    _expect_pin_failure(P.test_mlp_step_gradients_central_difference)
