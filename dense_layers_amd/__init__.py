@@ -1,0 +1,338 @@
+"""Python binding of the dense-layer training path for MI355X (gfx950).
+
+A thin ctypes layer over libdense_layers_amd.so: it checks tensor devices,
+dtypes and contiguity, allocates outputs and workspaces with PyTorch (device
+memory and streams are the only things PyTorch provides here), and passes raw
+pointers plus the current HIP stream to the C ABI.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU fallback and
+importing fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libdense_layers_amd.so")
+
+DL_F32, DL_BF16 = 0, 1
+ACT_IDENTITY, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
+OPT_SGD, OPT_ADAMW = 0, 1
+STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "ALIASING",
+          4: "WORKSPACE_TOO_SMALL", 5: "HIP_ERROR"}
+
+_ACTS = {"identity": ACT_IDENTITY, "relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH,
+         None: ACT_IDENTITY}
+
+
+class DenseError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                              ctypes.c_float, ctypes.c_size_t)
+
+
+class DLLayer(ctypes.Structure):
+    _fields_ = [("in_", ctypes.c_int64), ("out", ctypes.c_int64),
+                ("act", ctypes.c_int32),
+                ("W", _vp), ("b", _vp), ("dW", _vp), ("db", _vp),
+                ("mW", _vp), ("vW", _vp), ("mb", _vp), ("vb", _vp)]
+
+
+class DLOpt(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int64)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_c = {
+    "dl_last_error": _sig("dl_last_error", ctypes.c_char_p, []),
+    "dl_build_target": _sig("dl_build_target", ctypes.c_char_p, []),
+    "dense_act_fwd": _sig("dense_act_fwd", _i32,
+                          [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "dense_act_vjp": _sig("dense_act_vjp", _i32,
+                          [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _i32, _vp, _vp, _sz]),
+    "dense_act_vjp_workspace_size": _sig("dense_act_vjp_workspace_size", _sz,
+                                         [_i32, _i32, _i64, _i64, _i64]),
+    "softmax_xent_fwd_bwd": _sig("softmax_xent_fwd_bwd", _i32,
+                                 [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "softmax_xent_workspace_size": _sig("softmax_xent_workspace_size", _sz, [_i64, _i64]),
+    "sgd_step": _sig("sgd_step", _i32, [_vp, _i64, _vp, _vp, _f32]),
+    "adamw_step": _sig("adamw_step", _i32,
+                       [_vp, _i64, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64]),
+    "dense_cast_bf16": _sig("dense_cast_bf16", _i32, [_vp, _i64, _vp, _vp]),
+    "mlp_train_step": _sig("mlp_train_step", _i32,
+                           [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,
+                            ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
+    "mlp_train_step_workspace_size": _sig("mlp_train_step_workspace_size", _sz,
+                                          [_i64, _i32, ctypes.POINTER(DLLayer)]),
+}
+
+EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
+           "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
+           "softmax_xent_workspace_size", "sgd_step", "adamw_step",
+           "dense_cast_bf16", "mlp_train_step", "mlp_train_step_workspace_size"]
+
+
+def build_target() -> str:
+    return _c["dl_build_target"]().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise DenseError(status, _c["dl_last_error"]().decode())
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DL_F32
+    if t.dtype == torch.bfloat16:
+        return DL_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _act(act) -> int:
+    return _ACTS[act] if not isinstance(act, int) else act
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- dense layer
+
+def dense_act_fwd(X: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor] = None,
+                  act=ACT_IDENTITY, Y: Optional[torch.Tensor] = None,
+                  Z: Optional[torch.Tensor] = None, save_z: bool = False):
+    """Y = act(X W^T + b); returns (Y, Z or None)."""
+    _dev(X, "X")
+    dt = X.dtype
+    B, n_in = X.shape
+    n_out = W.shape[0]
+    _dev(W, "W", dt, (n_out, n_in))
+    if b is not None:
+        _dev(b, "b", torch.float32, (n_out,))
+    if Y is None:
+        Y = torch.empty((B, n_out), dtype=dt, device=X.device)
+    _dev(Y, "Y", dt, (B, n_out))
+    if Z is None and save_z:
+        Z = torch.empty((B, n_out), dtype=dt, device=X.device)
+    if Z is not None:
+        _dev(Z, "Z", dt, (B, n_out))
+    _check(_c["dense_act_fwd"](_stream(X), _dtype_code(X), _act(act), B, n_in, n_out,
+                               _ptr(X), _ptr(W), _ptr(b), _ptr(Y), _ptr(Z)))
+    return Y, Z
+
+
+def dense_act_vjp_workspace_size(dtype: int, act, B: int, n_in: int, n_out: int) -> int:
+    return int(_c["dense_act_vjp_workspace_size"](dtype, _act(act), B, n_in, n_out))
+
+
+def dense_act_vjp(dY: torch.Tensor, saved: Optional[torch.Tensor], X: Optional[torch.Tensor],
+                  W: torch.Tensor, act=ACT_IDENTITY, need_dx: bool = True,
+                  need_dw: bool = True, dX: Optional[torch.Tensor] = None,
+                  dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+                  dx_act=ACT_IDENTITY, dx_saved: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None):
+    """G = dY * act'(saved); returns (dX or None, dW or None, db or None).
+
+    With dx_act != identity the returned dX is dX * dx_act'(dx_saved)."""
+    _dev(dY, "dY")
+    dt = dY.dtype
+    B, n_out = dY.shape
+    n_in = W.shape[1]
+    _dev(W, "W", dt, (n_out, n_in))
+    if X is not None:
+        _dev(X, "X", dt, (B, n_in))
+    if saved is not None:
+        _dev(saved, "saved", dt, (B, n_out))
+    if need_dx and dX is None:
+        dX = torch.empty((B, n_in), dtype=dt, device=dY.device)
+    if dX is not None:
+        _dev(dX, "dX", dt, (B, n_in))
+    if need_dw:
+        if dW is None:
+            dW = torch.empty((n_out, n_in), dtype=torch.float32, device=dY.device)
+        if db is None:
+            db = torch.empty((n_out,), dtype=torch.float32, device=dY.device)
+    if dW is not None:
+        _dev(dW, "dW", torch.float32, (n_out, n_in))
+    if db is not None:
+        _dev(db, "db", torch.float32, (n_out,))
+    if dx_saved is not None:
+        _dev(dx_saved, "dx_saved", dt, (B, n_in))
+    code = _dtype_code(dY)
+    need = dense_act_vjp_workspace_size(code, act, B, n_in, n_out)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dY.device)
+    _check(_c["dense_act_vjp"](_stream(dY), code, _act(act), B, n_in, n_out, _ptr(dY),
+                               _ptr(saved), _ptr(X), _ptr(W), _ptr(dX), _ptr(dW), _ptr(db),
+                               _act(dx_act), _ptr(dx_saved), _ptr(ws),
+                               0 if ws is None else ws.numel()))
+    return dX, dW, db
+
+
+# ---------------------------------------------------------------- loss
+
+def softmax_xent_workspace_size(B: int, C: int) -> int:
+    return int(_c["softmax_xent_workspace_size"](B, C))
+
+
+def softmax_xent_fwd_bwd(logits: torch.Tensor, labels: torch.Tensor,
+                         dlogits: Optional[torch.Tensor] = None, inplace: bool = False,
+                         row_loss: Optional[torch.Tensor] = None,
+                         loss: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None):
+    """Mean softmax cross-entropy and its gradient; returns (loss[1], dlogits)."""
+    _dev(logits, "logits", torch.float32)
+    B, C = logits.shape
+    _dev(labels, "labels", torch.int32, (B,))
+    if inplace:
+        dlogits = logits
+    elif dlogits is None:
+        dlogits = torch.empty_like(logits)
+    _dev(dlogits, "dlogits", torch.float32, (B, C))
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+    if row_loss is not None:
+        _dev(row_loss, "row_loss", torch.float32, (B,))
+    need = softmax_xent_workspace_size(B, C)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, logits.device)
+    _check(_c["softmax_xent_fwd_bwd"](_stream(logits), B, C, _ptr(logits), _ptr(labels),
+                                      _ptr(loss), _ptr(row_loss), _ptr(dlogits), _ptr(ws),
+                                      ws.numel()))
+    return loss, dlogits
+
+
+# ---------------------------------------------------------------- optimizers
+
+def sgd_step(w: torch.Tensor, g: torch.Tensor, lr: float):
+    _dev(w, "w", torch.float32)
+    _dev(g, "g", torch.float32, tuple(w.shape))
+    _check(_c["sgd_step"](_stream(w), w.numel(), _ptr(w), _ptr(g), lr))
+    return w
+
+
+def adamw_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float, step: int):
+    for t, n in ((w, "w"), (g, "g"), (m, "m"), (v, "v")):
+        _dev(t, n, torch.float32, tuple(w.shape))
+    _check(_c["adamw_step"](_stream(w), w.numel(), _ptr(w), _ptr(g), _ptr(m), _ptr(v), lr,
+                            beta1, beta2, eps, weight_decay, step))
+    return w
+
+
+def dense_cast_bf16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):
+    _dev(src, "src", torch.float32)
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    _dev(dst, "dst", torch.bfloat16, tuple(src.shape))
+    _check(_c["dense_cast_bf16"](_stream(src), src.numel(), _ptr(src), _ptr(dst)))
+    return dst
+
+
+# ---------------------------------------------------------------- MLP step
+
+class MLP:
+    """Parameters, gradients and optimizer moments of an MLP on one device,
+    plus the ctypes layer table and workspace that mlp_train_step needs.
+    The tensors are ordinary torch tensors the caller may read or replace
+    in place; the table holds their pointers."""
+
+    def __init__(self, Ws: Sequence[torch.Tensor], bs: Sequence[torch.Tensor],
+                 acts: Sequence[int], batch: int, adamw: bool):
+        self.L = len(Ws)
+        dev = Ws[0].device
+        self.W = [_dev(w, f"W{l}", torch.float32).contiguous() for l, w in enumerate(Ws)]
+        self.b = [_dev(x, f"b{l}", torch.float32).contiguous() for l, x in enumerate(bs)]
+        self.dW = [torch.zeros_like(w) for w in self.W]
+        self.db = [torch.zeros_like(x) for x in self.b]
+        if adamw:
+            self.mW = [torch.zeros_like(w) for w in self.W]
+            self.vW = [torch.zeros_like(w) for w in self.W]
+            self.mb = [torch.zeros_like(x) for x in self.b]
+            self.vb = [torch.zeros_like(x) for x in self.b]
+        else:
+            self.mW = self.vW = self.mb = self.vb = [None] * self.L
+        self.acts = [_act(a) for a in acts]
+        self.batch = batch
+        self.table = (DLLayer * self.L)()
+        for l in range(self.L):
+            out, n_in = self.W[l].shape
+            self.table[l] = DLLayer(n_in, out, self.acts[l], _ptr(self.W[l]), _ptr(self.b[l]),
+                                    _ptr(self.dW[l]), _ptr(self.db[l]), _ptr(self.mW[l]),
+                                    _ptr(self.vW[l]), _ptr(self.mb[l]), _ptr(self.vb[l]))
+        need = mlp_train_step_workspace_size(batch, self.table)
+        self.ws = _workspace(need, dev)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.step_count = 0
+
+
+def mlp_train_step_workspace_size(B: int, table) -> int:
+    return int(_c["mlp_train_step_workspace_size"](B, len(table), table))
+
+
+def mlp_train_step(mlp: MLP, X: torch.Tensor, labels: torch.Tensor, kind: int = OPT_SGD,
+                   lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                   eps: float = 1e-8, weight_decay: float = 0.0,
+                   step: Optional[int] = None) -> torch.Tensor:
+    """One forward / softmax-xent / backward / optimizer step; returns the
+    device loss tensor (computed before the update)."""
+    _dev(X, "X", torch.float32, (mlp.batch, mlp.W[0].shape[1]))
+    _dev(labels, "labels", torch.int32, (mlp.batch,))
+    if step is None:
+        step = mlp.step_count + 1
+    mlp.step_count = step
+    opt = DLOpt(kind, lr, beta1, beta2, eps, weight_decay, step)
+    _check(_c["mlp_train_step"](_stream(X), mlp.batch, mlp.L, mlp.table, _ptr(X),
+                                _ptr(labels), ctypes.byref(opt), _ptr(mlp.loss), _ptr(mlp.ws),
+                                0 if mlp.ws is None else mlp.ws.numel()))
+    return mlp.loss

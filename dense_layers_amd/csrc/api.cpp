@@ -1,0 +1,484 @@
+// C ABI of the dense-layer training path: argument validation (everything is
+// checked before the first launch, so a rejected call touches no output),
+// workspace planning, GEMM tile / split-K planning, and the composition of
+// the kernels into the forward, vjp, loss, optimizer and whole-MLP-step calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dense_layers_amd.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(DL_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t esize(int dtype) { return dtype == DL_BF16 ? 2 : 4; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (a == nullptr || b == nullptr || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
+
+// ---- GEMM planning ----------------------------------------------------------
+// Tiles: float32 {0: 128x128, 1: 64x64}; bf16 {0: 256x128, 1: 128x128}.  The
+// large tile is used when it alone yields at least one workgroup per CU (256);
+// otherwise the small one.  Only the weight-gradient product (K = batch) is
+// split along K: slices are added until about two workgroups per CU exist,
+// each slice keeping at least four K tiles.
+
+constexpr int kCUs = 256;
+
+struct Plan {
+  int tile;
+  int splits;
+  int k_per_split;
+};
+
+void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
+  if (dtype == DL_BF16) {
+    bm = tile == 0 ? 256 : 128;
+    bn = 128;
+    bk = 64;
+  } else {
+    bm = bn = tile == 0 ? 128 : 64;
+    bk = 16;
+  }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
+  Plan p{0, 1, (int)K};
+  int bm, bn, bk;
+  tile_shape(dtype, 0, bm, bn, bk);
+  int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+  if (tiles < kCUs) {
+    p.tile = 1;
+    tile_shape(dtype, 1, bm, bn, bk);
+    tiles = ceil_div(M, bm) * ceil_div(N, bn);
+  }
+  if (epi == dl::EPI_DW && tiles < 2 * kCUs) {
+    int64_t want = ceil_div(2 * kCUs, tiles);
+    const int64_t max_by_k = std::max<int64_t>(1, K / (4 * bk));
+    want = std::min<int64_t>(std::min<int64_t>(want, max_by_k), 64);
+    int64_t kps = ceil_div(ceil_div(K, want), bk) * bk;
+    p.k_per_split = (int)kps;
+    p.splits = (int)ceil_div(K, kps);
+  }
+  if (p.splits <= 1) {
+    p.splits = 1;
+    p.k_per_split = (int)K;
+  }
+  return p;
+}
+
+size_t splitk_bytes(const Plan& p, int64_t M, int64_t N) {
+  if (p.splits <= 1) return 0;
+  return align_up((size_t)p.splits * M * N * 4) + align_up((size_t)p.splits * M * 4);
+}
+
+hipError_t run_gemm(int dtype, const dl::GemmDesc& d, int tile, hipStream_t s) {
+  return dtype == DL_BF16 ? dl::launch_gemm_bf16(d, tile, s) : dl::launch_gemm_f32(d, tile, s);
+}
+
+dl::GemmDesc blank_desc() {
+  dl::GemmDesc d;
+  memset(&d, 0, sizeof(d));
+  d.splits = 1;
+  return d;
+}
+
+// Forward GEMM with bias + activation epilogue.
+hipError_t fwd_gemm(int dtype, int act, int64_t B, int64_t in, int64_t out, const void* X,
+                    const void* W, const float* b, void* Y, void* Z, hipStream_t s) {
+  dl::GemmDesc d = blank_desc();
+  d.M = (int)B; d.N = (int)out; d.K = (int)in;
+  d.A = X; d.lda = in; d.a_layout = dl::K_MAJOR;
+  d.B = W; d.ldb = in; d.b_layout = dl::K_MAJOR;
+  d.C = Y; d.ldc = out;
+  d.epi = dl::EPI_FWD;
+  d.bias = b; d.act = act; d.Z = Z;
+  const Plan p = plan_gemm(dtype, dl::EPI_FWD, B, out, in);
+  d.k_per_split = (int)in;
+  return run_gemm(dtype, d, p.tile, s);
+}
+
+// dW = G^T X (+ db = column sums of G), split-K partials in `partial_ws`.
+hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
+                   float* dW, float* db, void* partial_ws, hipStream_t s) {
+  dl::GemmDesc d = blank_desc();
+  d.M = (int)out; d.N = (int)in; d.K = (int)B;
+  d.A = G; d.lda = out; d.a_layout = dl::MN_MAJOR;
+  d.B = X; d.ldb = in; d.b_layout = dl::MN_MAJOR;
+  d.C = dW; d.ldc = in;
+  d.epi = dl::EPI_DW;
+  const Plan p = plan_gemm(dtype, dl::EPI_DW, out, in, B);
+  d.splits = p.splits;
+  d.k_per_split = p.k_per_split;
+  if (p.splits > 1) {
+    char* base = static_cast<char*>(partial_ws);
+    d.partial = reinterpret_cast<float*>(base);
+    d.db_partial = db ? reinterpret_cast<float*>(base + align_up((size_t)p.splits * out * in * 4))
+                      : nullptr;
+    d.db = nullptr;
+  } else {
+    d.db = db;
+  }
+  hipError_t e = run_gemm(dtype, d, p.tile, s);
+  if (e != hipSuccess || p.splits == 1) return e;
+  return dl::launch_splitk_reduce((int)out, (int)in, p.splits, d.partial, d.db_partial, dW, in, db,
+                                  s);
+}
+
+// dX = G W, optionally times mask_act'(mask_src).
+hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* W,
+                   void* dX, int mask_act, const void* mask_src, hipStream_t s) {
+  dl::GemmDesc d = blank_desc();
+  d.M = (int)B; d.N = (int)in; d.K = (int)out;
+  d.A = G; d.lda = out; d.a_layout = dl::K_MAJOR;
+  d.B = W; d.ldb = in; d.b_layout = dl::MN_MAJOR;
+  d.C = dX; d.ldc = in;
+  d.epi = dl::EPI_DX;
+  d.mask_act = mask_act; d.mask_src = mask_src;
+  const Plan p = plan_gemm(dtype, dl::EPI_DX, B, in, out);
+  d.k_per_split = (int)out;
+  return run_gemm(dtype, d, p.tile, s);
+}
+
+size_t vjp_ws(int dtype, int act, int64_t B, int64_t in, int64_t out) {
+  size_t ws = 0;
+  if (act != DL_ACT_IDENTITY) ws += align_up((size_t)B * out * esize(dtype));
+  ws += splitk_bytes(plan_gemm(dtype, dl::EPI_DW, out, in, B), out, in);
+  return ws;
+}
+
+bool act_ok(int act) { return act == DL_ACT_IDENTITY || act == DL_ACT_RELU || act == DL_ACT_GELU_TANH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dl_last_error(void) { return g_last_error.c_str(); }
+
+const char* dl_build_target(void) { return "gfx950"; }
+
+int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
+                  const void* X, const void* W, const float* b, void* Y, void* Z) {
+  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: bad dtype %d", dtype);
+  if (!act_ok(act)) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: bad activation %d", act);
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
+    return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: sizes must be in [1, 2^31): B=%lld in=%lld out=%lld",
+                (long long)B, (long long)in, (long long)out);
+  if (!X || !W || !Y) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: X, W and Y are required");
+  const size_t es = esize(dtype);
+  const size_t nX = (size_t)B * in * es, nW = (size_t)out * in * es, nY = (size_t)B * out * es;
+  if (overlap(Y, nY, X, nX) || overlap(Y, nY, W, nW) || overlap(Y, nY, b, out * 4) ||
+      overlap(Z, nY, Y, nY) || overlap(Z, nY, X, nX) || overlap(Z, nY, W, nW) ||
+      overlap(Z, nY, b, out * 4))
+    return fail(DL_ALIASING, "dense_act_fwd: Y/Z overlap an input or each other");
+  hipError_t e = fwd_gemm(dtype, act, B, in, out, X, W, b, Y, Z, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense_act_fwd");
+  return DL_OK;
+}
+
+size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in, int64_t out) {
+  if ((dtype != DL_F32 && dtype != DL_BF16) || !act_ok(act) || !dim_ok(B) || !dim_ok(in) ||
+      !dim_ok(out))
+    return 0;
+  return vjp_ws(dtype, act, B, in, out);
+}
+
+int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
+                  const void* dY, const void* saved, const void* X, const void* W, void* dX,
+                  float* dW, float* db, int dx_act, const void* dx_saved, void* ws,
+                  size_t ws_bytes) {
+  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad dtype %d", dtype);
+  if (!act_ok(act) || !act_ok(dx_act)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad activation");
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
+    return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: sizes must be in [1, 2^31)");
+  if (!dY) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: dY is required");
+  if (act != DL_ACT_IDENTITY && !saved)
+    return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: saved Z/Y is required for a non-identity activation");
+  if ((dW || db) && !X) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: X is required for dW/db");
+  if (dX && !W) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: W is required for dX");
+  if (db && !dW) return fail(DL_UNSUPPORTED, "dense_act_vjp: db is reduced inside the dW kernel; pass dW too");
+  if (dx_act != DL_ACT_IDENTITY && (!dX || !dx_saved))
+    return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: dx_act needs dX and dx_saved");
+  const size_t need = vjp_ws(dtype, act, B, in, out);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(DL_WORKSPACE_TOO_SMALL, "dense_act_vjp: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: workspace must be 256-byte aligned");
+  const size_t es = esize(dtype);
+  const size_t nY = (size_t)B * out * es, nX = (size_t)B * in * es, nW = (size_t)out * in * es;
+  const size_t ndW = (size_t)out * in * 4, ndb = (size_t)out * 4;
+  // dX may be X itself and/or dx_saved itself (dW and db are finished first).
+  if (dX && (overlap(dX, nX, dY, nY) || overlap(dX, nX, W, nW) || overlap(dX, nX, saved, nY) ||
+             overlap(dX, nX, ws, need) || overlap(dX, nX, dW, ndW) || overlap(dX, nX, db, ndb) ||
+             (dX != X && overlap(dX, nX, X, nX)) ||
+             (dX != dx_saved && overlap(dX, nX, dx_saved, nX))))
+    return fail(DL_ALIASING, "dense_act_vjp: dX overlaps an input it must not");
+  if (dW && (overlap(dW, ndW, dY, nY) || overlap(dW, ndW, X, nX) || overlap(dW, ndW, W, nW) ||
+             overlap(dW, ndW, saved, nY) || overlap(dW, ndW, ws, need) || overlap(dW, ndW, db, ndb)))
+    return fail(DL_ALIASING, "dense_act_vjp: dW overlaps an input or db");
+  if (db && (overlap(db, ndb, dY, nY) || overlap(db, ndb, X, nX) || overlap(db, ndb, W, nW) ||
+             overlap(db, ndb, saved, nY) || overlap(db, ndb, ws, need)))
+    return fail(DL_ALIASING, "dense_act_vjp: db overlaps an input");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsp = static_cast<char*>(ws);
+  const void* G = dY;
+  hipError_t e;
+  if (act != DL_ACT_IDENTITY) {
+    e = dl::launch_act_mask(dtype, act, B, out, dY, saved, wsp, s);
+    if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (mask)");
+    G = wsp;
+    wsp += align_up((size_t)B * out * es);
+  }
+  if (dW) {
+    e = dw_gemm(dtype, B, in, out, G, X, dW, db, wsp, s);
+    if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dW)");
+  }
+  if (dX) {
+    e = dx_gemm(dtype, B, in, out, G, W, dX, dx_act, dx_saved, s);
+    if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dX)");
+  }
+  return DL_OK;
+}
+
+size_t softmax_xent_workspace_size(int64_t B, int64_t C) {
+  if (B <= 0 || C <= 0) return 0;
+  return align_up((size_t)B * 4);
+}
+
+int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits,
+                         const int32_t* labels, float* loss, float* row_loss, float* dlogits,
+                         void* ws, size_t ws_bytes) {
+  if (!dim_ok(B) || !dim_ok(C)) return fail(DL_INVALID_ARGUMENT, "softmax_xent_fwd_bwd: sizes must be in [1, 2^31)");
+  if (!logits || !labels || !loss || !dlogits)
+    return fail(DL_INVALID_ARGUMENT, "softmax_xent_fwd_bwd: logits, labels, loss and dlogits are required");
+  const size_t need = softmax_xent_workspace_size(B, C);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "softmax_xent_fwd_bwd: workspace %zu bytes, need %zu", ws_bytes, need);
+  const size_t nz = (size_t)B * C * 4;
+  if ((dlogits != logits && overlap(dlogits, nz, logits, nz)) || overlap(dlogits, nz, labels, B * 4) ||
+      overlap(dlogits, nz, loss, 4) || overlap(dlogits, nz, row_loss, B * 4) ||
+      overlap(loss, 4, logits, nz) || overlap(row_loss, B * 4, logits, nz) ||
+      overlap(dlogits, nz, ws, need))
+    return fail(DL_ALIASING, "softmax_xent_fwd_bwd: outputs overlap inputs (dlogits may equal logits)");
+  float* rl = row_loss ? row_loss : static_cast<float*>(ws);
+  hipError_t e = dl::launch_xent(B, C, logits, labels, rl, dlogits, loss, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "softmax_xent_fwd_bwd");
+  return DL_OK;
+}
+
+int sgd_step(void* stream, int64_t n, float* w, const float* g, float lr) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "sgd_step: n must be positive");
+  if (!w || !g) return fail(DL_INVALID_ARGUMENT, "sgd_step: w and g are required");
+  if (overlap(w, n * 4, g, n * 4)) return fail(DL_ALIASING, "sgd_step: w overlaps g");
+  hipError_t e = dl::launch_sgd(n, w, g, lr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sgd_step");
+  return DL_OK;
+}
+
+static void adam_factors(float beta1, float beta2, float lr, int64_t t, float& step_size,
+                         float& inv_sqrt_bc2) {
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
+  step_size = (float)((double)lr / bc1);
+  inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+}
+
+int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m, float* v, float lr,
+               float beta1, float beta2, float eps, float weight_decay, int64_t step) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "adamw_step: n must be positive");
+  if (!w || !g || !m || !v) return fail(DL_INVALID_ARGUMENT, "adamw_step: w, g, m and v are required");
+  if (step < 1) return fail(DL_INVALID_ARGUMENT, "adamw_step: step counts from 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return fail(DL_INVALID_ARGUMENT, "adamw_step: betas must be in [0, 1)");
+  const size_t nb = (size_t)n * 4;
+  if (overlap(w, nb, g, nb) || overlap(w, nb, m, nb) || overlap(w, nb, v, nb) ||
+      overlap(g, nb, m, nb) || overlap(g, nb, v, nb) || overlap(m, nb, v, nb))
+    return fail(DL_ALIASING, "adamw_step: w, g, m, v must be distinct");
+  float ss, isb;
+  adam_factors(beta1, beta2, lr, step, ss, isb);
+  hipError_t e = dl::launch_adamw(n, w, g, m, v, lr, beta1, beta2, eps, weight_decay, ss, isb,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "adamw_step");
+  return DL_OK;
+}
+
+int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: n must be positive");
+  if (!src || !dst) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: src and dst are required");
+  if (overlap(src, n * 4, dst, n * 2)) return fail(DL_ALIASING, "dense_cast_bf16: src overlaps dst");
+  hipError_t e = dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16");
+  return DL_OK;
+}
+
+// ---- whole MLP step ---------------------------------------------------------
+// Workspace: per-layer outputs Y_l [B, out_l] (the last one holds the logits,
+// then dlogits in place), the per-row losses, and the largest split-K partial
+// buffer among the layers' weight gradients.  During the backward pass the
+// dX epilogue of layer l writes G_{l-1} = (G_l W_l) * relu'(Y_{l-1}) over
+// Y_{l-1} in place, after layer l's dW has consumed Y_{l-1}.
+
+static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
+                         size_t* rl_off, size_t* part_off) {
+  size_t off = 0;
+  for (int l = 0; l < L; ++l) {
+    y_off[l] = off;
+    off += align_up((size_t)B * layers[l].out * 4);
+  }
+  *rl_off = off;
+  off += align_up((size_t)B * 4);
+  *part_off = off;
+  size_t part = 0;
+  for (int l = 0; l < L; ++l) {
+    const Plan p = plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B);
+    part = std::max(part, splitk_bytes(p, layers[l].out, layers[l].in));
+  }
+  return off + part;
+}
+
+size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer_t* layers) {
+  if (!dim_ok(B) || n_layers < 1 || n_layers > 16 || !layers) return 0;
+  for (int l = 0; l < n_layers; ++l)
+    if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
+  size_t y_off[16], rl, part;
+  return mlp_layout(B, n_layers, layers, y_off, &rl, &part);
+}
+
+int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
+                   const float* X, const int32_t* labels, const dl_opt_t* opt, float* loss,
+                   void* ws, size_t ws_bytes) {
+  if (!dim_ok(B)) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: B must be in [1, 2^31)");
+  if (n_layers < 1 || n_layers > 16 || !layers)
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: n_layers must be in [1, 16]");
+  if (!X || !labels || !opt || !loss) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: X, labels, opt and loss are required");
+  if (opt->kind != DL_OPT_SGD && opt->kind != DL_OPT_ADAMW)
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: bad optimizer kind %d", opt->kind);
+  if (opt->kind == DL_OPT_ADAMW && opt->step < 1)
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: AdamW step counts from 1");
+  if (opt->kind == DL_OPT_ADAMW && (!(opt->beta1 >= 0.f && opt->beta1 < 1.f) || !(opt->beta2 >= 0.f && opt->beta2 < 1.f)))
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: betas must be in [0, 1)");
+  int n_tensors = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const dl_layer_t& ly = layers[l];
+    if (!dim_ok(ly.in) || !dim_ok(ly.out)) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d has a bad shape", l);
+    if (l > 0 && ly.in != layers[l - 1].out)
+      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d in=%lld != layer %d out=%lld", l,
+                  (long long)ly.in, l - 1, (long long)layers[l - 1].out);
+    if (ly.act != DL_ACT_IDENTITY && ly.act != DL_ACT_RELU)
+      return fail(ly.act == DL_ACT_GELU_TANH ? DL_UNSUPPORTED : DL_INVALID_ARGUMENT,
+                  "mlp_train_step: layer %d activation %d (identity or ReLU only)", l, ly.act);
+    if (!ly.W || !ly.b || !ly.dW || !ly.db)
+      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d needs W, b, dW and db", l);
+    if (opt->kind == DL_OPT_ADAMW && (!ly.mW || !ly.vW || !ly.mb || !ly.vb))
+      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d needs AdamW moments", l);
+    if (overlap(ly.dW, ly.out * ly.in * 4, ly.W, ly.out * ly.in * 4) || overlap(ly.db, ly.out * 4, ly.b, ly.out * 4))
+      return fail(DL_ALIASING, "mlp_train_step: layer %d gradient overlaps its parameters", l);
+    n_tensors += 2;
+  }
+  if (n_tensors > dl::kMaxSegs) return fail(DL_UNSUPPORTED, "mlp_train_step: too many layers");
+  // The loss pass overwrites the logits with dlogits, so the last layer has no
+  // activation of its own (its derivative would need the overwritten output).
+  if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
+    return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
+  size_t y_off[16], rl_off, part_off;
+  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, &part_off);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* Y[16];
+  for (int l = 0; l < n_layers; ++l) Y[l] = reinterpret_cast<float*>(base + y_off[l]);
+  float* row_loss = reinterpret_cast<float*>(base + rl_off);
+  void* part = base + part_off;
+  const int L = n_layers;
+  const int64_t C = layers[L - 1].out;
+  hipError_t e;
+
+  // forward
+  for (int l = 0; l < L; ++l) {
+    const dl_layer_t& ly = layers[l];
+    const float* in = l == 0 ? X : Y[l - 1];
+    e = fwd_gemm(DL_F32, ly.act, B, ly.in, ly.out, in, ly.W, ly.b, Y[l], nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (forward)");
+  }
+  // loss + dlogits (in place over the logits)
+  e = dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s);
+  if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
+  // backward
+  for (int l = L - 1; l >= 0; --l) {
+    const dl_layer_t& ly = layers[l];
+    const float* in = l == 0 ? X : Y[l - 1];
+    e = dw_gemm(DL_F32, B, ly.in, ly.out, Y[l], in, ly.dW, ly.db, part, s);
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
+    if (l > 0) {
+      e = dx_gemm(DL_F32, B, ly.in, ly.out, Y[l], ly.W, Y[l - 1], layers[l - 1].act, Y[l - 1], s);
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dX)");
+    }
+  }
+  // optimizer over every W and b in one launch
+  dl::OptSegs segs;
+  memset(&segs, 0, sizeof(segs));
+  int64_t blocks = 0;
+  for (int l = 0; l < L; ++l) {
+    const dl_layer_t& ly = layers[l];
+    float* ws_[2] = {ly.W, ly.b};
+    const float* gs_[2] = {ly.dW, ly.db};
+    float* ms_[2] = {ly.mW, ly.mb};
+    float* vs_[2] = {ly.vW, ly.vb};
+    const int64_t ns_[2] = {ly.out * ly.in, ly.out};
+    for (int t = 0; t < 2; ++t) {
+      const int k = segs.count++;
+      segs.start_block[k] = blocks;
+      segs.n[k] = ns_[t];
+      segs.w[k] = ws_[t];
+      segs.g[k] = gs_[t];
+      segs.m[k] = ms_[t];
+      segs.v[k] = vs_[t];
+      blocks += (ns_[t] + dl::kOptElemsPerBlock - 1) / dl::kOptElemsPerBlock;
+    }
+  }
+  segs.start_block[segs.count] = blocks;
+  float ss = 0.f, isb = 0.f;
+  if (opt->kind == DL_OPT_ADAMW) adam_factors(opt->beta1, opt->beta2, opt->lr, opt->step, ss, isb);
+  e = dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, opt->lr, opt->beta1, opt->beta2,
+                           opt->eps, opt->weight_decay, ss, isb, s);
+  if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");
+  return DL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Small streaming kernels around the GEMMs:
+//   * split-K reduction of weight-gradient partials (and the fused db partials),
+//     summed in slice order so the result is bit-reproducible;
+//   * G = dY * act'(saved) for a vjp whose upstream gradient was not already
+//     masked by the previous dX epilogue;
+//   * float32 -> bf16 round-to-nearest-even working copies.
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(int M, int N, int splits, const float* __restrict__ partial,
+                     const float* __restrict__ db_partial, float* __restrict__ C, int64_t ldc,
+                     float* __restrict__ db) {
+  const int64_t MN = (int64_t)M * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < MN) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += partial[s * MN + i];
+    const int64_t row = i / N, col = i - row * N;
+    C[row * ldc + col] = acc;
+  }
+  if (db != nullptr && i < M) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += db_partial[(int64_t)s * M + i];
+    db[i] = acc;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+act_mask_kernel(int act, int64_t n, const T* __restrict__ dY, const T* __restrict__ saved,
+                T* __restrict__ G) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float g = Elem<T>::load(dY, i) * act_deriv(act, Elem<T>::load(saved, i));
+    Elem<T>::store(G, i, g);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+cast_bf16_kernel(int64_t n, const float* __restrict__ src, bf16_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = f32_to_bf16(src[i]);
+}
+
+unsigned grid_for(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
+                                const float* db_partial, float* C, int64_t ldc, float* db,
+                                hipStream_t s) {
+  const int64_t n = std::max<int64_t>((int64_t)M * N, M);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
+                     N, splits, partial, db_partial, C, ldc, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols, const void* dY,
+                           const void* saved, void* G, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (dtype == 0)
+    hipLaunchKernelGGL(act_mask_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
+                       static_cast<const float*>(dY), static_cast<const float*>(saved),
+                       static_cast<float*>(G));
+  else
+    hipLaunchKernelGGL(act_mask_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
+                       static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(saved),
+                       static_cast<bf16_t*>(G));
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, s, n, src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace dl

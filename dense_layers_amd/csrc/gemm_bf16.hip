@@ -1,0 +1,340 @@
+// bfloat16-operand GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16,
+// float32 accumulation) with the dense-layer epilogues fused in.
+//
+// Same three products as the float32 kernel (forward, dX, dW; the fused
+// LinearAct of the noeira.nn docs, "The design in one page") for operands
+// held as bf16 working copies (the FP32-master-weight scheme of the Orthon
+// page, "Mixed-precision training on CUDA"; round-to-nearest-even copies as in
+// the MuNet page, "Configuration").  Forward and dX results are stored as
+// bf16, dW and db as float32.
+//
+// LDS holds every operand K-contiguous: each tile row (one m or n) is BK = 64
+// bf16 = 128 bytes, eight 16-byte units, and a lane's MFMA fragment (8
+// consecutive k of one row) is one 16-byte LDS read.  Units are XOR-swizzled
+// by row, unit' = unit ^ ((row ^ row >> 3) & 7), so the 8 lanes that read
+// rows r..r+7 of one unit, and the 8 lanes that store rows 8 apart in the
+// transposing path, all land on different banks.
+//
+// K-major operands are copied in 16-byte vectors.  M/N-major operands
+// (dW's A and B, dX's B) are transposed on the way in: a thread loads a
+// 4 (k) x 8 (m) block as four 16-byte row pieces, regroups them in registers
+// into eight 4-k column pieces and stores each with one 8-byte LDS write.
+//
+// As in the float32 kernel, which k a lane supplies inside an MFMA is free as
+// long as A and B agree: at k-step ks, lane half h supplies k = 16 ks + 8 h +
+// (0..7).
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+constexpr int BK = 64;           // k per LDS tile
+constexpr int kRowElems = BK;    // bf16 per LDS row (no padding; swizzled)
+
+__device__ __forceinline__ int swz(int row, int unit) {
+  return unit ^ ((row ^ (row >> 3)) & 7);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int ROWS, int LAY, int NT>
+struct TileLoaderBf16 {
+  static constexpr int kLdsSize = ROWS * kRowElems;  // bf16 elements
+  // K-major: ROWS x 8 vectors of 8 bf16.  MN-major: (BK/4) x (ROWS/8) blocks.
+  static constexpr int kItems = (LAY == K_MAJOR) ? ROWS * (BK / 8) : (BK / 4) * (ROWS / 8);
+  static_assert(kItems % NT == 0, "tile not divisible among threads");
+  static constexpr int kPer = kItems / NT;
+  static constexpr int kRegs = (LAY == K_MAJOR) ? kPer : kPer * 4;
+
+  u32x4 r[kRegs];
+
+  __device__ __forceinline__ static u32x4 load_row8(const bf16_t* __restrict__ p, int valid,
+                                                    bool vec) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (vec && valid >= 8) {
+      x = *reinterpret_cast<const u32x4*>(p);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t e = (j < valid) ? static_cast<uint32_t>(p[j]) : 0u;
+        x[j >> 1] |= e << ((j & 1) * 16);
+      }
+    }
+    return x;
+  }
+
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int64_t ld, int row0,
+                                       int nrows, int k0, int kend, bool vec_ok, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + i * NT;
+      if (LAY == K_MAJOR) {
+        const int row = row0 + q / (BK / 8);
+        const int k = k0 + (q % (BK / 8)) * 8;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < nrows && k < kend)
+          x = load_row8(base + (int64_t)row * ld + k, kend - k, vec_ok);
+        r[i] = x;
+      } else {
+        const int mg = q % (ROWS / 8);
+        const int kq = q / (ROWS / 8);
+        const int m = row0 + mg * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = k0 + kq * 4 + j;
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (k < kend && m < nrows)
+            x = load_row8(base + (int64_t)k * ld + m, nrows - m, vec_ok);
+          r[i * 4 + j] = x;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16_t* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + i * NT;
+      if (LAY == K_MAJOR) {
+        const int row = q / (BK / 8);
+        const int unit = q % (BK / 8);
+        *reinterpret_cast<u32x4*>(lds + row * kRowElems + swz(row, unit) * 8) = r[i];
+      } else {
+        const int mg = q % (ROWS / 8);
+        const int kq = q / (ROWS / 8);
+        // rows j = 0..3 of the block hold k = 4kq + j; element c of a row is m = 8mg + c
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int w = c >> 1;
+          const int sh = (c & 1) * 16;
+          const uint32_t e0 = (r[i * 4 + 0][w] >> sh) & 0xffffu;
+          const uint32_t e1 = (r[i * 4 + 1][w] >> sh) & 0xffffu;
+          const uint32_t e2 = (r[i * 4 + 2][w] >> sh) & 0xffffu;
+          const uint32_t e3 = (r[i * 4 + 3][w] >> sh) & 0xffffu;
+          u32x2 col = {e0 | (e1 << 16), e2 | (e3 << 16)};
+          const int row = mg * 8 + c;
+          const int unit = kq >> 1;
+          *reinterpret_cast<u32x2*>(lds + row * kRowElems + swz(row, unit) * 8 + (kq & 1) * 4) = col;
+        }
+      }
+    }
+  }
+
+  // 8 bf16 of tile row `row` at k-step ks (16 k), lane half h.
+  __device__ __forceinline__ static bf16x8 frag(const bf16_t* __restrict__ lds, int row, int ks,
+                                                int h) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(lds + row * kRowElems + swz(row, ks * 2 + h) * 8);
+    return __builtin_bit_cast(bf16x8, x);
+  }
+};
+
+template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(FM >= 1 && FN >= 1, "bad tile");
+  using LA = TileLoaderBf16<BM, ALAY, NT>;
+  using LB = TileLoaderBf16<BN, BLAY, NT>;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][LA::kLdsSize];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][LB::kLdsSize];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  int split, tm, tn;
+  tile_coords(tiles_m, tiles_n, split, tm, tn);
+
+  const int M = d.M, N = d.N;
+  const int kbeg = split * d.k_per_split;
+  const int kend = min(d.K, kbeg + d.k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(d.A);
+  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(d.B);
+
+  LA la;
+  LB lb;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const bool do_db = (EPI == EPI_DW) && (d.db != nullptr || d.db_partial != nullptr) &&
+                     tn == 0 && wn == 0;
+  float dbacc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
+
+  if (nk > 0) {
+    la.load(A, d.lda, tm * BM, M, kbeg, kend, a_vec, tid);
+    lb.load(B, d.ldb, tn * BN, N, kbeg, kend, b_vec, tid);
+    la.store(As[0], tid);
+    lb.store(Bs[0], tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      const int k0 = kbeg + (kt + 1) * BK;
+      la.load(A, d.lda, tm * BM, M, k0, kend, a_vec, tid);
+      lb.load(B, d.ldb, tn * BN, N, k0, kend, b_vec, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = LA::frag(As[cur], wm * WM + i * 32 + l32, ks, h);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = LB::frag(Bs[cur], wn * WN + j * 32 + l32, ks, h);
+      if (do_db) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += static_cast<float>(a[i][e]);
+          dbacc[i] += s;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const int row_base = tm * BM + wm * WM;
+  const int col_base = tn * BN + wn * WN;
+
+  if (EPI == EPI_DW) {
+    if (do_db) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+        const int row = row_base + i * 32 + l32;
+        if (h == 0 && row < M) {
+          if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
+          else d.db[row] = v;
+        }
+      }
+    }
+    float* __restrict__ out = static_cast<float*>(d.C);
+    int64_t ld = d.ldc;
+    if (d.splits > 1) {
+      out = d.partial + (int64_t)split * M * N;
+      ld = N;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col_base + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (row < M && col < N) out[(int64_t)row * ld + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
+  bf16_t* __restrict__ C = static_cast<bf16_t*>(d.C);
+  if (EPI == EPI_FWD) {
+    const float* __restrict__ bias = d.bias;
+    bf16_t* __restrict__ Zp = static_cast<bf16_t*>(d.Z);
+    const int act = d.act;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col_base + j * 32 + l32;
+      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (row < M && col < N) {
+            const float z = acc[i][j][r] + bj;
+            const int64_t o = (int64_t)row * d.ldc + col;
+            C[o] = f32_to_bf16(act_apply(act, z));
+            if (Zp != nullptr) Zp[o] = f32_to_bf16(z);
+          }
+        }
+    }
+    return;
+  }
+
+  // EPI_DX
+  const bf16_t* __restrict__ msrc = static_cast<const bf16_t*>(d.mask_src);
+  const int mact = d.mask_act;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col_base + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (row < M && col < N) {
+          const int64_t o = (int64_t)row * d.ldc + col;
+          float v = acc[i][j][r];
+          if (mact != ACT_IDENTITY) v *= act_deriv(mact, bf16_to_f32(msrc[o]));
+          C[o] = f32_to_bf16(v);
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
+  const int tiles_m = (d.M + BM - 1) / BM;
+  const int tiles_n = (d.N + BN - 1) / BN;
+  const int64_t nwg = (int64_t)tiles_m * tiles_n * d.splits;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+  auto aligned = [](const void* p, int64_t ld) {
+    return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 8 == 0);
+  };
+  const int a_vec = aligned(d.A, d.lda);
+  const int b_vec = aligned(d.B, d.ldb);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, ALAY, BLAY, EPI>), dim3((unsigned)nwg),
+                     dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n, a_vec, b_vec);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
+  if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+  if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+  if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_tile<BM, BN, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// tile 0: 256x128 (4 waves of 128x64); tile 1: 128x128 (4 waves of 64x64)
+hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
+  switch (tile) {
+    case 0: return dispatch_layout<256, 128, 2, 2>(d, s);
+    case 1: return dispatch_layout<128, 128, 2, 2>(d, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dl

@@ -1,0 +1,318 @@
+// Float32 GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32) with the
+// dense-layer epilogues fused in.
+//
+// One kernel template covers the three products of a dense layer:
+//   forward  Z = X W^T        A = X  [B, in]  K-major, B = W [out, in] K-major
+//   dX       dX = G W         A = G  [B, out] K-major, B = W [out, in] N-major
+//   dW       dW = G^T X       A = G  [B, out] M-major, B = X [B, in]   N-major
+// (the fused Linear / LinearAct of the noeira.nn docs, "The design in one
+// page", with bias and activation in the GEMM epilogue, and split-K for the
+// long-K weight gradient as in its package layout's split-K GEMM).
+//
+// Structure: a workgroup of WGM x WGN waves owns a BM x BN output tile; each
+// wave owns a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks whose
+// accumulators stay in registers for the whole K loop.  Operand tiles go
+// global -> registers -> LDS (double-buffered, one barrier per K step); the
+// next tile's global loads are issued before the current tile's MFMAs so
+// their latency hides behind the matrix work.  LDS keeps the global layout
+// (no transpose on the store side); fragments are read as one 16-byte load
+// (K-major) or four 4-byte loads (M/N-major).
+//
+// The sum over k inside an MFMA does not depend on which k each lane
+// supplies, as long as A and B agree.  Within a group of 8 k values, lane
+// half h (lanes 0-31 / 32-63) supplies k = 4h + s at MFMA step s, so a
+// K-major fragment is 4 consecutive floats.
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+constexpr int kPad = 4;  // floats of padding per LDS row
+
+template <int ROWS, int BK, int LAY, int NT>
+struct TileLoader {
+  // A tile is ROWS (M or N) x BK (K) elements, moved as float4 vectors.
+  static constexpr int kVecs = ROWS * BK / 4;
+  static_assert(kVecs % NT == 0, "tile not divisible among threads");
+  static constexpr int kPer = kVecs / NT;
+  static constexpr int kLdsStride = (LAY == K_MAJOR) ? (BK + kPad) : (ROWS + kPad);
+  static constexpr int kLdsSize = (LAY == K_MAJOR) ? ROWS * (BK + kPad) : BK * (ROWS + kPad);
+
+  f32x4 r[kPer];
+
+  __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld,
+                                       int row0, int nrows, int k0, int kend,
+                                       bool vec_ok, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * NT;
+      int row, k;
+      if (LAY == K_MAJOR) {
+        row = row0 + v / (BK / 4);
+        k = k0 + (v % (BK / 4)) * 4;
+      } else {
+        k = k0 + v / (ROWS / 4);
+        row = row0 + (v % (ROWS / 4)) * 4;
+      }
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (LAY == K_MAJOR) {
+        if (row < nrows) {
+          const float* p = base + (int64_t)row * ld + k;
+          if (vec_ok && k + 3 < kend) {
+            x = *reinterpret_cast<const f32x4*>(p);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (k + j < kend) x[j] = p[j];
+          }
+        }
+      } else {
+        if (k < kend) {
+          const float* p = base + (int64_t)k * ld + row;
+          if (vec_ok && row + 3 < nrows) {
+            x = *reinterpret_cast<const f32x4*>(p);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (row + j < nrows) x[j] = p[j];
+          }
+        }
+      }
+      r[i] = x;
+    }
+  }
+
+  __device__ __forceinline__ void store(float* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * NT;
+      int off;
+      if (LAY == K_MAJOR)
+        off = (v / (BK / 4)) * kLdsStride + (v % (BK / 4)) * 4;
+      else
+        off = (v / (ROWS / 4)) * kLdsStride + (v % (ROWS / 4)) * 4;
+      *reinterpret_cast<f32x4*>(lds + off) = r[i];
+    }
+  }
+
+  // Fragment for a 32-row MFMA block starting at tile row `row` (this lane's
+  // row already added), k group kg (8 values), lane half h.
+  __device__ __forceinline__ void frag(const float* __restrict__ lds, int row,
+                                       int kg, int h, float out[4]) const {
+    if (LAY == K_MAJOR) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(lds + row * kLdsStride + kg * 8 + h * 4);
+      out[0] = x[0]; out[1] = x[1]; out[2] = x[2]; out[3] = x[3];
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) out[s] = lds[(kg * 8 + h * 4 + s) * kLdsStride + row];
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(FM >= 1 && FN >= 1 && BK % 8 == 0, "bad tile");
+  using LA = TileLoader<BM, BK, ALAY, NT>;
+  using LB = TileLoader<BN, BK, BLAY, NT>;
+  __shared__ __attribute__((aligned(16))) float As[2][LA::kLdsSize];
+  __shared__ __attribute__((aligned(16))) float Bs[2][LB::kLdsSize];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  int split, tm, tn;
+  tile_coords(tiles_m, tiles_n, split, tm, tn);
+
+  const int M = d.M, N = d.N;
+  const int kbeg = split * d.k_per_split;
+  const int kend = min(d.K, kbeg + d.k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  const float* __restrict__ A = static_cast<const float*>(d.A);
+  const float* __restrict__ B = static_cast<const float*>(d.B);
+
+  LA la;
+  LB lb;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const bool do_db = (EPI == EPI_DW) && (d.db != nullptr || d.db_partial != nullptr) &&
+                     tn == 0 && wn == 0;
+  float dbacc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
+
+  if (nk > 0) {
+    la.load(A, d.lda, tm * BM, M, kbeg, kend, a_vec, tid);
+    lb.load(B, d.ldb, tn * BN, N, kbeg, kend, b_vec, tid);
+    la.store(As[0], tid);
+    lb.store(Bs[0], tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      const int k0 = kbeg + (kt + 1) * BK;
+      la.load(A, d.lda, tm * BM, M, k0, kend, a_vec, tid);
+      lb.load(B, d.ldb, tn * BN, N, k0, kend, b_vec, tid);
+    }
+#pragma unroll
+    for (int kg = 0; kg < BK / 8; ++kg) {
+      float a[FM][4], b[FN][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) la.frag(As[cur], wm * WM + i * 32 + l32, kg, h, a[i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) lb.frag(Bs[cur], wn * WN + j * 32 + l32, kg, h, b[j]);
+      if (do_db) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) dbacc[i] += (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const int row_base = tm * BM + wm * WM;
+  const int col_base = tn * BN + wn * WN;
+  float* __restrict__ C = static_cast<float*>(d.C);
+
+  if (EPI == EPI_DW) {
+    if (do_db) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+        const int row = row_base + i * 32 + l32;
+        if (h == 0 && row < M) {
+          if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
+          else d.db[row] = v;
+        }
+      }
+    }
+    float* __restrict__ out = C;
+    int64_t ld = d.ldc;
+    if (d.splits > 1) {
+      out = d.partial + (int64_t)split * M * N;
+      ld = N;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col_base + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (row < M && col < N) out[(int64_t)row * ld + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
+  if (EPI == EPI_FWD) {
+    const float* __restrict__ bias = d.bias;
+    float* __restrict__ Zp = static_cast<float*>(d.Z);
+    const int act = d.act;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col_base + j * 32 + l32;
+      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (row < M && col < N) {
+            const float z = acc[i][j][r] + bj;
+            const int64_t o = (int64_t)row * d.ldc + col;
+            C[o] = act_apply(act, z);
+            if (Zp != nullptr) Zp[o] = z;
+          }
+        }
+    }
+    return;
+  }
+
+  // EPI_DX
+  const float* __restrict__ msrc = static_cast<const float*>(d.mask_src);
+  const int mact = d.mask_act;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col_base + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (row < M && col < N) {
+          const int64_t o = (int64_t)row * d.ldc + col;
+          float v = acc[i][j][r];
+          if (mact != ACT_IDENTITY) v *= act_deriv(mact, msrc[o]);
+          C[o] = v;
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
+  const int tiles_m = (d.M + BM - 1) / BM;
+  const int tiles_n = (d.N + BN - 1) / BN;
+  const int64_t nwg = (int64_t)tiles_m * tiles_n * d.splits;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+  auto aligned = [](const void* p, int64_t ld) {
+    return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 4 == 0);
+  };
+  const int a_vec = aligned(d.A, d.lda);
+  const int b_vec = aligned(d.B, d.ldb);
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>),
+                     dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m,
+                     tiles_n, a_vec, b_vec);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN>
+hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
+  if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+  if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+  if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_tile<BM, BN, BK, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// tile 0: 128x128 (4 waves of 64x64); tile 1: 64x64 (4 waves of 32x32)
+hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s) {
+  switch (tile) {
+    case 0: return dispatch_layout<128, 128, 16, 2, 2>(d, s);
+    case 1: return dispatch_layout<64, 64, 16, 2, 2>(d, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dl

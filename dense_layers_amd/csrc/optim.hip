@@ -1,0 +1,128 @@
+// SGD and AdamW updates (MuNet page, "What runs today": SGD and AdamW;
+// noeira.nn docs, "The design in one page": Adam's m and v live with the
+// parameter).  Pure streaming kernels: 16-byte loads and stores, each thread
+// handles four float4 groups so a workgroup moves 16 KB per array.
+//
+// AdamW, per element (decoupled decay first, then the bias-corrected Adam
+// step; step_size = lr / (1 - b1^t) and inv_sqrt_bc2 = 1 / sqrt(1 - b2^t) are
+// computed on the host in double):
+//   w *= 1 - lr wd;  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+//   w -= step_size m / (sqrt(v) inv_sqrt_bc2 + eps)
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+struct AdamParams {
+  float lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2;
+};
+
+__device__ __forceinline__ void adam_elem(float& w, float g, float& m, float& v,
+                                          const AdamParams& p) {
+  w *= 1.0f - p.lr * p.wd;
+  m = p.beta1 * m + (1.0f - p.beta1) * g;
+  v = p.beta2 * v + (1.0f - p.beta2) * g * g;
+  w -= p.step_size * m / (sqrtf(v) * p.inv_sqrt_bc2 + p.eps);
+}
+
+// Process elements [base, base + kOptElemsPerBlock) of one array.
+template <int KIND>
+__device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __restrict__ w,
+                                          const float* __restrict__ g, float* __restrict__ m,
+                                          float* __restrict__ v, const AdamParams& p,
+                                          bool vec) {
+  const int64_t end = min(n, base + (int64_t)kOptElemsPerBlock);
+  if (vec && end - base == kOptElemsPerBlock) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
+      f32x4 wv = *reinterpret_cast<const f32x4*>(w + i);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
+      if (KIND == 0) {
+        wv -= p.lr * gv;
+      } else {
+        f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
+        f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float we = wv[e], me = mv[e], ve = vv[e];
+          adam_elem(we, gv[e], me, ve, p);
+          wv[e] = we; mv[e] = me; vv[e] = ve;
+        }
+        *reinterpret_cast<f32x4*>(m + i) = mv;
+        *reinterpret_cast<f32x4*>(v + i) = vv;
+      }
+      *reinterpret_cast<f32x4*>(w + i) = wv;
+    }
+  } else {
+    for (int64_t i = base + threadIdx.x; i < end; i += kOptBlock) {
+      if (KIND == 0) {
+        w[i] -= p.lr * g[i];
+      } else {
+        float we = w[i], me = m[i], ve = v[i];
+        adam_elem(we, g[i], me, ve, p);
+        w[i] = we; m[i] = me; v[i] = ve;
+      }
+    }
+  }
+}
+
+template <int KIND>
+__global__ void __launch_bounds__(kOptBlock)
+opt_single_kernel(int64_t n, float* w, const float* g, float* m, float* v, AdamParams p, int vec) {
+  opt_block<KIND>(n, (int64_t)blockIdx.x * kOptElemsPerBlock, w, g, m, v, p, vec);
+}
+
+// One launch over several arrays: block b belongs to the segment whose
+// prefix range [start_block[s], start_block[s+1]) contains it.
+template <int KIND>
+__global__ void __launch_bounds__(kOptBlock)
+opt_multi_kernel(OptSegs segs, AdamParams p) {
+  const int64_t b = blockIdx.x;
+  int s = 0;
+  while (s + 1 < segs.count && b >= segs.start_block[s + 1]) ++s;
+  const int64_t local = b - segs.start_block[s];
+  const bool vec = ((reinterpret_cast<uintptr_t>(segs.w[s]) | reinterpret_cast<uintptr_t>(segs.g[s]) |
+                     (KIND ? (reinterpret_cast<uintptr_t>(segs.m[s]) |
+                              reinterpret_cast<uintptr_t>(segs.v[s])) : 0)) & 15) == 0;
+  opt_block<KIND>(segs.n[s], local * kOptElemsPerBlock, segs.w[s], segs.g[s], segs.m[s],
+                  segs.v[s], p, vec);
+}
+
+}  // namespace
+
+hipError_t launch_sgd(int64_t n, float* w, const float* g, float lr, hipStream_t s) {
+  AdamParams p{lr, 0, 0, 0, 0, 0, 0};
+  const int64_t blocks = (n + kOptElemsPerBlock - 1) / kOptElemsPerBlock;
+  const int vec = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(g)) & 15) == 0;
+  hipLaunchKernelGGL(opt_single_kernel<0>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, n, w, g,
+                     nullptr, nullptr, p, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v, float lr,
+                        float beta1, float beta2, float eps, float wd, float step_size,
+                        float inv_sqrt_bc2, hipStream_t s) {
+  AdamParams p{lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2};
+  const int64_t blocks = (n + kOptElemsPerBlock - 1) / kOptElemsPerBlock;
+  const int vec = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(g) |
+                    reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v)) & 15) == 0;
+  hipLaunchKernelGGL(opt_single_kernel<1>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, n, w, g,
+                     m, v, p, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_opt_multi(const OptSegs& segs, int kind, float lr, float beta1, float beta2,
+                            float eps, float wd, float step_size, float inv_sqrt_bc2,
+                            hipStream_t s) {
+  AdamParams p{lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2};
+  const int64_t blocks = segs.start_block[segs.count];
+  if (blocks <= 0) return hipSuccess;
+  if (kind == 0)
+    hipLaunchKernelGGL(opt_multi_kernel<0>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, segs, p);
+  else
+    hipLaunchKernelGGL(opt_multi_kernel<1>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, segs, p);
+  return hipGetLastError();
+}
+
+}  // namespace dl

@@ -1,0 +1,228 @@
+// Fused softmax cross-entropy, forward and backward, in one read of the
+// logits (Orthon page, "Selected Orthon vs. PyTorch results": one fused kernel
+// reads the logits once instead of materialising a log-softmax and gathering;
+// the same page notes the benefit depends on the class count, so the row is
+// mapped to a different number of threads per class-count regime here).
+//
+// A row of C logits is owned by TPR consecutive threads (a lane group inside a
+// wave for TPR <= 64, the whole 256-thread workgroup for TPR = 256).  Each
+// thread keeps its slice of the row in registers, so HBM sees one read and
+// one write per logit; row max, sum of exponentials and the label's logit are
+// combined with cross-lane shuffles (plus LDS across waves for TPR = 256).
+//   lse = max + log(sum exp(z - max)),  loss_i = lse - z[y_i],
+//   dlogits = (exp(z - max) / sum - [c == y_i]) / B.
+// Per-row losses go to a buffer and a single workgroup sums them in a fixed
+// order, so the mean is bit-reproducible.
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+constexpr int kXentBlock = 256;
+
+template <int TPR>
+__device__ __forceinline__ float group_max(float v, float* red) {
+  if (TPR <= 64) {
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kXentBlock / 64; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+  }
+}
+
+template <int TPR>
+__device__ __forceinline__ void group_sum2(float& a, float& b, float* red) {
+  if (TPR <= 64) {
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) {
+      a += __shfl_xor(a, o);
+      b += __shfl_xor(b, o);
+    }
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      a += __shfl_xor(a, o);
+      b += __shfl_xor(b, o);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      red[2 * wave] = a;
+      red[2 * wave + 1] = b;
+    }
+    __syncthreads();
+    a = 0.f;
+    b = 0.f;
+#pragma unroll
+    for (int w = 0; w < kXentBlock / 64; ++w) {
+      a += red[2 * w];
+      b += red[2 * w + 1];
+    }
+  }
+}
+
+// VEC: items are float4 (C % 4 == 0, 16-byte aligned rows), else floats.
+// NI:  items cached per thread; the kernel is only launched with
+//      C <= TPR * NI * (VEC ? 4 : 1).
+template <int TPR, int NI, bool VEC>
+__global__ void __launch_bounds__(kXentBlock)
+xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restrict__ labels,
+                 float* __restrict__ row_loss, float* dlogits, float invB) {
+  constexpr int RPB = kXentBlock / TPR;
+  constexpr int W = VEC ? 4 : 1;
+  __shared__ float red[2 * kXentBlock / 64];
+  const int lr = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool active = row < B;
+  const int64_t base = (active ? row : 0) * (int64_t)C;
+  const int y = active ? labels[row] : 0;
+  const bool valid = (y >= 0) && (y < C);
+
+  float v[NI][W];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int c0 = (lr + j * TPR) * W;
+    if (VEC) {
+      f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (active && c0 < C) x = *reinterpret_cast<const f32x4*>(logits + base + c0);
+#pragma unroll
+      for (int e = 0; e < W; ++e) v[j][e] = x[e];
+    } else {
+      v[j][0] = (active && c0 < C) ? logits[base + c0] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < W; ++e) m = fmaxf(m, v[j][e]);
+  }
+  m = group_max<TPR>(m, red);
+
+  float s = 0.f, zy = 0.f;
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const int c = (lr + j * TPR) * W + e;
+      const float x = v[j][e];
+      if (c < C) {
+        const float ex = __expf(x - m);
+        v[j][e] = ex;
+        s += ex;
+        if (c == y) zy = x;
+      }
+    }
+  group_sum2<TPR>(s, zy, red);
+
+  const float inv_s = 1.0f / s;
+  if (active && lr == 0)
+    row_loss[row] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
+  if (!active) return;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int c0 = (lr + j * TPR) * W;
+    if (c0 >= C) continue;
+    float o[W];
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const float onehot = (c0 + e == y) ? 1.0f : 0.0f;
+      o[e] = (v[j][e] * inv_s - onehot) * invB;
+    }
+    if (VEC) {
+      f32x4 x = {o[0], o[W > 1 ? 1 : 0], o[W > 2 ? 2 : 0], o[W > 3 ? 3 : 0]};
+      *reinterpret_cast<f32x4*>(dlogits + base + c0) = x;
+    } else {
+      dlogits[base + c0] = o[0];
+    }
+  }
+}
+
+// Rows too wide to cache in registers: one workgroup per row, two passes
+// (the second read normally hits L2 / the 256 MB Infinity Cache).
+__global__ void __launch_bounds__(kXentBlock)
+xent_rows_wide_kernel(int64_t B, int64_t C, const float* logits, const int32_t* __restrict__ labels,
+                      float* __restrict__ row_loss, float* dlogits, float invB) {
+  __shared__ float red[2 * kXentBlock / 64];
+  const int64_t row = blockIdx.x;
+  const int64_t base = row * C;
+  const int y = labels[row];
+  const bool valid = (y >= 0) && (y < C);
+  float m = -INFINITY;
+  for (int64_t c = threadIdx.x; c < C; c += kXentBlock) m = fmaxf(m, logits[base + c]);
+  m = group_max<kXentBlock>(m, red);
+  float s = 0.f, zy = 0.f;
+  for (int64_t c = threadIdx.x; c < C; c += kXentBlock) {
+    const float x = logits[base + c];
+    s += __expf(x - m);
+    if (c == y) zy = x;
+  }
+  group_sum2<kXentBlock>(s, zy, red);
+  if (threadIdx.x == 0) row_loss[row] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
+  __syncthreads();  // every read of this row precedes the first in-place write
+  const float inv_s = 1.0f / s;
+  for (int64_t c = threadIdx.x; c < C; c += kXentBlock) {
+    const float x = logits[base + c];
+    dlogits[base + c] = (__expf(x - m) * inv_s - (c == y ? 1.0f : 0.0f)) * invB;
+  }
+}
+
+// Mean of the per-row losses: one workgroup, fixed summation order, float64.
+__global__ void __launch_bounds__(256)
+loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restrict__ loss) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < B; i += 256) acc += (double)row_loss[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(red[0] / (double)B);
+}
+
+template <int TPR, int NI, bool VEC>
+hipError_t launch_rows(int64_t B, int64_t C, const float* logits, const int32_t* labels,
+                       float* row_loss, float* dlogits, hipStream_t s) {
+  constexpr int RPB = kXentBlock / TPR;
+  const int64_t blocks = (B + RPB - 1) / RPB;
+  hipLaunchKernelGGL((xent_rows_kernel<TPR, NI, VEC>), dim3((unsigned)blocks), dim3(kXentBlock), 0,
+                     s, B, (int)C, logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t* labels,
+                       float* row_loss, float* dlogits, float* loss, hipStream_t s) {
+  const bool vec = (C % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(dlogits) & 15) == 0);
+  hipError_t e;
+  if (C <= 32)
+    e = launch_rows<8, 4, false>(B, C, logits, labels, row_loss, dlogits, s);
+  else if (C <= 256)
+    e = vec ? launch_rows<32, 2, true>(B, C, logits, labels, row_loss, dlogits, s)
+            : launch_rows<32, 8, false>(B, C, logits, labels, row_loss, dlogits, s);
+  else if (C <= 2048)
+    e = vec ? launch_rows<64, 8, true>(B, C, logits, labels, row_loss, dlogits, s)
+            : launch_rows<64, 32, false>(B, C, logits, labels, row_loss, dlogits, s);
+  else if (vec && C <= 32768)
+    e = launch_rows<256, 32, true>(B, C, logits, labels, row_loss, dlogits, s);
+  else {
+    hipLaunchKernelGGL(xent_rows_wide_kernel, dim3((unsigned)B), dim3(kXentBlock), 0, s, B, C,
+                       logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, B, row_loss, loss);
+  return hipGetLastError();
+}
+
+}  // namespace dl

@@ -1,0 +1,440 @@
+"""Parity of the HIP path with the float64 oracle, through the C ABI.
+
+Every case draws seeded inputs once, runs the GPU kernels and the oracle on
+the same values, and compares element by element: float32 results within a
+normwise relative error of 1e-4, the loss within 1e-5 relative, bf16-operand
+results within 2e-2, integer and bit-level results exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth_inputs as si
+from tests.gpu_util import (BF16_TOL, F32_TOL, LOSS_TOL, assert_close, device, misaligned,
+                            to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+ACTS = [O.ACT_IDENTITY, O.ACT_RELU, O.ACT_GELU_TANH]
+
+
+@pytest.fixture(scope="module")
+def dl():
+    device()
+    import dense_layers_amd
+    return dense_layers_amd
+
+
+def _layer(seed, B, n_in, n_out, bias=True):
+    X = si.random_matrix(seed, (B, n_in))
+    W = si.random_matrix(seed + 1, (n_out, n_in), scale=1.0 / math.sqrt(n_in))
+    b = si.random_matrix(seed + 2, (n_out,), scale=0.1) if bias else None
+    return X, W, b
+
+
+# ------------------------------------------------------------------ forward
+
+FWD_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (300, 1000, 129),
+              (513, 256, 1000), (256, 1024, 4096), (8192, 128, 10), (33, 4100, 70)]
+
+
+@pytest.mark.parametrize("shape", FWD_SHAPES)
+@pytest.mark.parametrize("act", ACTS)
+def test_dense_fwd_f32(dl, shape, act):
+    B, n_in, n_out = shape
+    X, W, b = _layer(10, B, n_in, n_out, bias=(B % 2 == 1))
+    Y, Z = dl.dense_act_fwd(to_dev(X), to_dev(W), None if b is None else to_dev(b), act,
+                            save_z=True)
+    refY, refZ = O.dense_act_fwd(X, W, b, act)
+    assert_close(to_np(Z), refZ, F32_TOL, "Z")
+    assert_close(to_np(Y), refY, F32_TOL, "Y")
+
+
+def test_dense_fwd_f32_misaligned_operands(dl):
+    B, n_in, n_out = 97, 64, 80
+    X, W, b = _layer(11, B, n_in, n_out)
+    Xd, Wd = misaligned(to_dev(X)), misaligned(to_dev(W))
+    Y, _ = dl.dense_act_fwd(Xd, Wd, to_dev(b), O.ACT_RELU)
+    assert_close(to_np(Y), O.dense_act_fwd(X, W, b, O.ACT_RELU)[0], F32_TOL, "Y")
+
+
+def test_dense_fwd_is_bit_reproducible(dl):
+    X, W, b = _layer(12, 1000, 512, 300)
+    a = dl.dense_act_fwd(to_dev(X), to_dev(W), to_dev(b), O.ACT_GELU_TANH)[0]
+    c = dl.dense_act_fwd(to_dev(X), to_dev(W), to_dev(b), O.ACT_GELU_TANH)[0]
+    assert torch.equal(a, c)
+
+
+def test_dense_fwd_on_side_stream(dl):
+    X, W, b = _layer(13, 300, 200, 100)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Xd, Wd, bd = to_dev(X), to_dev(W), to_dev(b)
+        Y, _ = dl.dense_act_fwd(Xd, Wd, bd, O.ACT_RELU)
+    s.synchronize()
+    assert_close(to_np(Y), O.dense_act_fwd(X, W, b, O.ACT_RELU)[0], F32_TOL, "Y")
+
+
+# ------------------------------------------------------------------ vjp
+
+VJP_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (8192, 784, 256),
+              (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000)]
+
+
+@pytest.mark.parametrize("shape", VJP_SHAPES)
+@pytest.mark.parametrize("act", ACTS)
+def test_dense_vjp_f32(dl, shape, act):
+    B, n_in, n_out = shape
+    X, W, b = _layer(20, B, n_in, n_out)
+    Z = O.round_f32(O.dense_act_fwd(X, W, b, O.ACT_IDENTITY)[1]).astype(np.float32)
+    dY = si.random_matrix(23, (B, n_out), scale=1e-2)
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY), to_dev(Z), to_dev(X), to_dev(W), act)
+    rdX, rdW, rdb = O.dense_act_vjp(dY, Z, X, W, act)
+    assert_close(to_np(dX), rdX, F32_TOL, "dX")
+    assert_close(to_np(dW), rdW, F32_TOL, "dW")
+    assert_close(to_np(db), rdb, F32_TOL, "db")
+
+
+@pytest.mark.parametrize("dx_act", [O.ACT_RELU, O.ACT_GELU_TANH])
+def test_dense_vjp_folds_previous_activation(dl, dx_act):
+    """dX epilogue multiplies by the previous layer's act'(saved), in place."""
+    B, n_in, n_out = 777, 300, 129
+    X, W, b = _layer(30, B, n_in, n_out)
+    Zprev = si.random_matrix(31, (B, n_in))
+    dY = si.random_matrix(32, (B, n_out))
+    Zp = to_dev(Zprev)
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY), None, to_dev(X), to_dev(W), O.ACT_IDENTITY,
+                                  dX=Zp, dx_act=dx_act, dx_saved=Zp)
+    rdX, rdW, rdb = O.dense_act_vjp(dY, None, X, W, O.ACT_IDENTITY)
+    assert dX.data_ptr() == Zp.data_ptr()
+    assert_close(to_np(dX), rdX * O.act_grad(Zprev, dx_act), F32_TOL, "folded dX")
+    assert_close(to_np(dW), rdW, F32_TOL, "dW")
+    assert_close(to_np(db), rdb, F32_TOL, "db")
+
+
+def test_dense_vjp_skips_outputs(dl):
+    B, n_in, n_out = 100, 50, 40
+    X, W, b = _layer(40, B, n_in, n_out)
+    dY = si.random_matrix(41, (B, n_out))
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY), None, to_dev(X), to_dev(W), O.ACT_IDENTITY,
+                                  need_dx=False)
+    assert dX is None
+    rdX, rdW, rdb = O.dense_act_vjp(dY, None, X, W, O.ACT_IDENTITY)
+    assert_close(to_np(dW), rdW, F32_TOL, "dW")
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY), None, None, to_dev(W), O.ACT_IDENTITY,
+                                  need_dw=False)
+    assert dW is None and db is None
+    assert_close(to_np(dX), rdX, F32_TOL, "dX")
+
+
+def test_dense_vjp_is_bit_reproducible(dl):
+    B, n_in, n_out = 8192, 784, 256   # split-K path
+    X, W, b = _layer(50, B, n_in, n_out)
+    dY = si.random_matrix(51, (B, n_out))
+    args = (to_dev(dY), None, to_dev(X), to_dev(W), O.ACT_IDENTITY)
+    r1 = dl.dense_act_vjp(*args)
+    r2 = dl.dense_act_vjp(*args)
+    for a, c in zip(r1, r2):
+        assert torch.equal(a, c)
+
+
+# ------------------------------------------------------------------ bf16
+
+BF16_SHAPES = [(1, 8, 8), (77, 130, 90), (300, 1024, 512), (1024, 1024, 4096), (513, 4096, 1024)]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_dense_fwd_bf16(dl, shape, act):
+    B, n_in, n_out = shape
+    X = si.random_matrix(60, (B, n_in), bf16_exact=True)
+    Wm = si.random_matrix(61, (n_out, n_in), scale=0.02)
+    b = si.random_matrix(62, (n_out,), scale=0.01)
+    Wb = dl.dense_cast_bf16(to_dev(Wm))
+    Y, Z = dl.dense_act_fwd(to_dev(X, torch.bfloat16), Wb, to_dev(b), act, save_z=True)
+    Wr = O.round_bf16(Wm)
+    refY, refZ = O.dense_act_fwd(X, Wr, b, act)
+    assert_close(to_np(Z), refZ, BF16_TOL, "Z")
+    assert_close(to_np(Y), refY, BF16_TOL, "Y")
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_dense_vjp_bf16(dl, shape, act):
+    B, n_in, n_out = shape
+    X = si.random_matrix(70, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(71, (n_out, n_in), scale=0.02, bf16_exact=True)
+    Z = si.random_matrix(72, (B, n_out), bf16_exact=True)
+    dY = si.random_matrix(73, (B, n_out), bf16_exact=True)
+    bf = torch.bfloat16
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY, bf), to_dev(Z, bf), to_dev(X, bf), to_dev(W, bf),
+                                  act)
+    rdX, rdW, rdb = O.dense_act_vjp(dY, Z, X, W, act)
+    assert dX.dtype == bf and dW.dtype == torch.float32
+    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+    assert_close(to_np(dW), rdW, BF16_TOL, "dW")
+    assert_close(to_np(db), rdb, BF16_TOL, "db")
+
+
+def test_bf16_fp32_consistency(dl):
+    """With bf16-exact operands the fp32 path must meet 1e-4 on the same
+    oracle, so the bf16 tolerance hides only output rounding."""
+    B, n_in, n_out = 300, 1024, 512
+    X = si.random_matrix(80, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(81, (n_out, n_in), scale=0.02, bf16_exact=True)
+    b = si.random_matrix(82, (n_out,), scale=0.01)
+    Y32, _ = dl.dense_act_fwd(to_dev(X), to_dev(W), to_dev(b), O.ACT_GELU_TANH)
+    Y16, _ = dl.dense_act_fwd(to_dev(X, torch.bfloat16), to_dev(W, torch.bfloat16), to_dev(b),
+                              O.ACT_GELU_TANH)
+    ref = O.dense_act_fwd(X, W, b, O.ACT_GELU_TANH)[0]
+    assert_close(to_np(Y32), ref, F32_TOL, "fp32 path")
+    assert_close(to_np(Y16), O.round_bf16(ref), 1e-2, "bf16 path vs rounded oracle")
+
+
+def test_cast_bf16_bit_exact(dl):
+    rng = np.random.default_rng(90)
+    x = (rng.standard_normal(100003) * np.exp(rng.uniform(-30, 30, 100003))).astype(np.float32)
+    specials = np.array([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, np.inf, -np.inf, 65504.0,
+                         3.4e38, 1e-40], dtype=np.float32)
+    x[: specials.size] = specials
+    got = dl.dense_cast_bf16(to_dev(x)).view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = O.round_bf16(x).astype(np.float32).view(np.uint32) >> 16
+    assert np.array_equal(got, ref.astype(np.uint16))
+    nan = dl.dense_cast_bf16(to_dev(np.array([np.nan], np.float32)))
+    assert torch.isnan(nan.float()).all()
+
+
+# ------------------------------------------------------------------ softmax xent
+
+XENT_SHAPES = [(1, 1), (5, 10), (64, 10), (8192, 10), (100, 33), (77, 256), (64, 257),
+               (130, 1000), (3, 2047), (17, 2049), (8, 4096), (4, 32000), (2, 32001),
+               (3, 40000), (300, 31)]
+
+
+@pytest.mark.parametrize("shape", XENT_SHAPES)
+def test_softmax_xent(dl, shape):
+    B, C = shape
+    z = si.random_matrix(100 + C, (B, C), scale=3.0)
+    y = si.random_labels(101, B, C)
+    row = torch.empty(B, dtype=torch.float32, device=device())
+    loss, dz = dl.softmax_xent_fwd_bwd(to_dev(z), to_dev(y), row_loss=row)
+    rloss, rdz, rrow = O.softmax_xent_fwd_bwd(z, y)
+    assert abs(float(loss.item()) - rloss) <= LOSS_TOL * abs(rloss)
+    assert_close(to_np(dz), rdz, F32_TOL, "dlogits")
+    assert_close(to_np(row), rrow, F32_TOL, "row loss")
+
+
+def test_softmax_xent_in_place(dl):
+    B, C = 513, 1000
+    z = si.random_matrix(110, (B, C), scale=5.0)
+    y = si.random_labels(111, B, C)
+    zd = to_dev(z)
+    loss, dz = dl.softmax_xent_fwd_bwd(zd, to_dev(y), inplace=True)
+    assert dz.data_ptr() == zd.data_ptr()
+    rloss, rdz, _ = O.softmax_xent_fwd_bwd(z, y)
+    assert abs(float(loss.item()) - rloss) <= LOSS_TOL * abs(rloss)
+    assert_close(to_np(dz), rdz, F32_TOL, "dlogits")
+
+
+def test_softmax_xent_labels_read_back_exactly(dl):
+    y = si.random_labels(112, 4096, 32000)
+    yd = to_dev(y)
+    z = to_dev(np.zeros((4096, 32000), np.float32))
+    loss, dz = dl.softmax_xent_fwd_bwd(z, yd)
+    assert np.array_equal(yd.cpu().numpy(), y)
+    assert abs(float(loss.item()) - math.log(32000)) < 1e-5 * math.log(32000)
+
+
+def test_softmax_xent_bad_label_gives_nan_not_fault(dl):
+    z = si.random_matrix(120, (4, 10))
+    y = np.array([0, 10, 3, -1], dtype=np.int32)
+    row = torch.empty(4, dtype=torch.float32, device=device())
+    loss, dz = dl.softmax_xent_fwd_bwd(to_dev(z), to_dev(y), row_loss=row)
+    r = row.cpu().numpy()
+    assert math.isnan(float(loss.item()))
+    assert np.isnan(r[1]) and np.isnan(r[3]) and np.isfinite(r[0]) and np.isfinite(r[2])
+
+
+# ------------------------------------------------------------------ optimizers
+
+OPT_SIZES = [1, 3, 4096, 16389, (1 << 20) + 3]
+
+
+@pytest.mark.parametrize("n", OPT_SIZES)
+def test_sgd(dl, n):
+    w = si.random_matrix(130, (n,))
+    g = si.random_matrix(131, (n,))
+    wd = to_dev(w)
+    dl.sgd_step(wd, to_dev(g), 1e-3)
+    ref = O.round_f32(O.sgd_step(w, g, 1e-3))
+    got = to_np(wd)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= ulp)
+
+
+@pytest.mark.parametrize("n", OPT_SIZES)
+def test_adamw_ten_steps(dl, n):
+    w = si.random_matrix(140, (n,))
+    wd, md, vd = to_dev(w), torch.zeros(n, device=device()), torch.zeros(n, device=device())
+    wr, mr, vr = O.round_f32(w), np.zeros(n), np.zeros(n)
+    for t in range(1, 11):
+        g = si.random_matrix(150 + t, (n,), scale=0.1)
+        dl.adamw_step(wd, to_dev(g), md, vd, 1e-3, 0.9, 0.999, 1e-8, 0.01, t)
+        wr, mr, vr = [O.round_f32(a) for a in
+                      O.adamw_step(wr, g, mr, vr, 1e-3, 0.9, 0.999, 1e-8, 0.01, t)]
+    assert_close(to_np(wd), wr, 1e-6, "w")
+    assert_close(to_np(md), mr, 1e-5, "m")
+    assert_close(to_np(vd), vr, 1e-5, "v")
+
+
+def test_adamw_zero_gradient_is_pure_decay(dl):
+    w = si.random_matrix(160, (1000,))
+    wd = to_dev(w)
+    z = torch.zeros(1000, device=device())
+    dl.adamw_step(wd, z.clone(), z.clone(), z.clone(), 1e-2, 0.9, 0.999, 1e-8, 0.1, 1)
+    assert_close(to_np(wd), O.round_f32(w * (1 - 1e-3)), 1e-7, "decay")
+
+
+# ------------------------------------------------------------------ MLP step
+
+def _gpu_relu_masks(dl, X, Ws, bs, acts):
+    """GPU forward, layer by layer (the same kernels and launch plan as the
+    fused step), returning each layer's ReLU decision Y > 0."""
+    h = to_dev(X)
+    masks = []
+    for l in range(len(Ws)):
+        h, _ = dl.dense_act_fwd(h, to_dev(Ws[l]), to_dev(bs[l]), acts[l])
+        masks.append((h > 0).cpu().numpy() if acts[l] == O.ACT_RELU else None)
+    return masks
+
+
+def _adopted_masks(gpu_masks, state, X, acts):
+    """Oracle masks, replaced by the GPU's decision only where the oracle's
+    pre-activation lies within twice the float32 rounding band of zero.
+    Returns (masks, adopted count); fails on a disagreement outside it."""
+    h = np.asarray(X, np.float64)
+    out, adopted = [], 0
+    for l in range(len(state.W)):
+        Y, Z = O.dense_act_fwd(h, state.W[l], state.b[l], acts[l])
+        if acts[l] == O.ACT_RELU:
+            band = 2.0 * O.relu_kink_band(h, state.W[l], state.b[l])
+            own = Z > 0
+            near = np.abs(Z) <= band
+            diff = own != gpu_masks[l]
+            assert not np.any(diff & ~near), f"layer {l}: ReLU decision differs outside the band"
+            adopted += int(np.sum(diff & near))
+            out.append(np.where(near, gpu_masks[l], own).astype(np.float64))
+            Y = np.where(out[-1] > 0, Z, 0.0)
+        else:
+            out.append(None)
+        h = Y
+    return out, adopted
+
+
+def _check_step(dl, mlp, ref, st, what):
+    for l in range(mlp.L):
+        assert_close(to_np(mlp.dW[l]), ref["dW"][l], F32_TOL, f"{what} dW{l}")
+        assert_close(to_np(mlp.db[l]), ref["db"][l], F32_TOL, f"{what} db{l}")
+        assert_close(to_np(mlp.W[l]), st.W[l], F32_TOL, f"{what} W{l}")
+        assert_close(to_np(mlp.b[l]), st.b[l], F32_TOL, f"{what} b{l}")
+
+
+def _opt_kind(dl, w):
+    return dl.OPT_ADAMW if w.optim.kind == "adamw" else dl.OPT_SGD
+
+
+def _run_teacher_forced(dl, w, inp, steps, check_steps):
+    """Each checked step starts the oracle from the GPU's state (W, b, m, v),
+    so every step is compared on identical inputs."""
+    dev = device()
+    mlp = dl.MLP([to_dev(a) for a in inp.W], [to_dev(a) for a in inp.b], w.acts, w.batch,
+                 adamw=(w.optim.kind == "adamw"))
+    Xd, yd = to_dev(inp.X), to_dev(inp.labels)
+    o = w.optim
+    for t in range(1, steps + 1):
+        if t in check_steps:
+            st = O.MLPState([to_np(a) for a in mlp.W], [to_np(a) for a in mlp.b])
+            if o.kind == "adamw":
+                st.mW = [to_np(a) for a in mlp.mW]
+                st.vW = [to_np(a) for a in mlp.vW]
+                st.mb = [to_np(a) for a in mlp.mb]
+                st.vb = [to_np(a) for a in mlp.vb]
+            st.t = t - 1
+            gm = _gpu_relu_masks(dl, inp.X, [to_np(a).astype(np.float32) for a in mlp.W],
+                                 [to_np(a).astype(np.float32) for a in mlp.b], w.acts)
+            masks, adopted = _adopted_masks(gm, st, inp.X, w.acts)
+        loss = dl.mlp_train_step(mlp, Xd, yd, _opt_kind(dl, w), lr=o.lr, beta1=o.beta1,
+                                 beta2=o.beta2, eps=o.eps, weight_decay=o.weight_decay, step=t)
+        if t in check_steps:
+            ref = O.mlp_train_step(st, inp.X, inp.labels, w.acts, o, relu_masks=masks)
+            got = float(loss.item())
+            assert abs(got - ref["loss"]) <= LOSS_TOL * abs(ref["loss"]), (t, got, ref["loss"])
+            _check_step(dl, mlp, ref, st, f"step {t}")
+    torch.cuda.synchronize()
+    return mlp
+
+
+def test_mlp_small_one_sgd_step(dl):
+    w = si.WORKLOADS["mlp_small"]
+    _run_teacher_forced(dl, w, si.generate(w), 1, {1})
+
+
+def test_mlp_small_ragged_batch(dl):
+    w = si.WORKLOADS["mlp_small"].scaled(37)
+    _run_teacher_forced(dl, w, si.generate(w), 3, {1, 3})
+
+
+def test_mlp_adamw_full_batch_teacher_forced(dl):
+    w = si.WORKLOADS["mlp_adamw"]
+    _run_teacher_forced(dl, w, si.generate(w), 12, {1, 2, 12})
+
+
+def test_mlp_adamw_loss_trajectory_100_steps(dl):
+    """All 100 losses of the free-running GPU step against the free-running
+    oracle (batch 1024 keeps the oracle at a few seconds)."""
+    w = si.WORKLOADS["mlp_adamw"].scaled(1024)
+    inp = si.generate(w)
+    mlp = dl.MLP([to_dev(a) for a in inp.W], [to_dev(a) for a in inp.b], w.acts, w.batch,
+                 adamw=True)
+    st = O.MLPState(inp.W, inp.b)
+    Xd, yd = to_dev(inp.X), to_dev(inp.labels)
+    o = w.optim
+    losses = torch.empty(100, device=device())
+    for t in range(1, 101):
+        loss = dl.mlp_train_step(mlp, Xd, yd, dl.OPT_ADAMW, lr=o.lr, beta1=o.beta1,
+                                 beta2=o.beta2, eps=o.eps, weight_decay=o.weight_decay, step=t)
+        losses[t - 1] = loss[0]
+    got = losses.cpu().numpy()
+    ref = np.array([O.mlp_train_step(st, inp.X, inp.labels, w.acts, o)["loss"]
+                    for _ in range(100)])
+    rel = np.abs(got - ref) / np.abs(ref)
+    assert np.max(rel) < LOSS_TOL, (np.argmax(rel), np.max(rel))
+    assert ref[-1] < ref[0]
+
+
+def test_mlp_wide_reduced_batch(dl):
+    w = si.WORKLOADS["mlp_wide"].scaled(256)
+    _run_teacher_forced(dl, w, si.generate(w), 1, {1})
+
+
+def test_head_xent_reduced_batch(dl):
+    w = si.WORKLOADS["head_xent"].scaled(256)
+    _run_teacher_forced(dl, w, si.generate(w), 2, {1, 2})
+
+
+def test_mlp_step_bit_reproducible(dl):
+    w = si.WORKLOADS["mlp_adamw"]
+    inp = si.generate(w)
+    outs = []
+    for _ in range(2):
+        mlp = dl.MLP([to_dev(a) for a in inp.W], [to_dev(a) for a in inp.b], w.acts, w.batch,
+                     adamw=True)
+        for t in range(1, 4):
+            dl.mlp_train_step(mlp, to_dev(inp.X), to_dev(inp.labels), dl.OPT_ADAMW,
+                              weight_decay=0.01, step=t)
+        outs.append([a.clone() for a in mlp.W + mlp.b + mlp.mW + mlp.vW])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
