@@ -1,0 +1,314 @@
+"""Throughput of the dense-layer training path on one MI355X.
+
+Default workload: the 784-256-128-10 ReLU MLP, batch 8192, AdamW(lr 1e-3,
+betas (0.9, 0.999), wd 0.01) on one fixed synthetic batch; a step is one full
+forward / softmax-xent / backward / AdamW update through mlp_train_step.
+Other workloads (--config) are measured the same way for the design notes.
+
+Prints one JSON line: whole-step throughput (train steps/s), the step's
+algorithmic GEMM TFLOP/s, a roofline entry for the dominant kernel (its own
+average launch time, HIP events on the launch stream) and the float64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth_inputs as si  # noqa: E402
+
+METRIC = "fused dense fwd+bwd TFLOP/s and MLP train steps/s; % of MFMA peak (1 GPU)"
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
+PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
+PEAK_HBM = 8000.0        # GB/s
+
+
+def _events_time(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(iters):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms per call
+
+
+class MLPBench:
+    """mlp_train_step workloads (784-256-128-10, the wide MLP)."""
+
+    def __init__(self, dl, w, dev):
+        import torch
+        self.dl, self.w = dl, w
+        inp = si.generate(w)
+        self.inp = inp
+        self.X = torch.from_numpy(inp.X).to(dev)
+        self.y = torch.from_numpy(inp.labels).to(dev)
+        self.mlp = dl.MLP([torch.from_numpy(a).to(dev) for a in inp.W],
+                          [torch.from_numpy(a).to(dev) for a in inp.b], w.acts, w.batch,
+                          adamw=(w.optim.kind == "adamw"))
+        self.t = 0
+
+    def step(self):
+        o = self.w.optim
+        self.t += 1
+        kind = self.dl.OPT_ADAMW if o.kind == "adamw" else self.dl.OPT_SGD
+        self.dl.mlp_train_step(self.mlp, self.X, self.y, kind, lr=o.lr, beta1=o.beta1,
+                               beta2=o.beta2, eps=o.eps, weight_decay=o.weight_decay,
+                               step=self.t)
+
+    def flops(self):
+        return self.w.gemm_flops_per_step()
+
+    def kernels(self):
+        """(name, flops per launch, zero-argument launcher of exactly that one
+        kernel with the step's own shapes and launch plan) for each GEMM."""
+        import torch
+        dl, w, m = self.dl, self.w, self.mlp
+        B = w.batch
+        hs = [self.X]
+        for l in range(w.n_layers):
+            hs.append(dl.dense_act_fwd(hs[-1], m.W[l], m.b[l], w.acts[l])[0])
+        out = []
+        for l in range(w.n_layers):
+            n_in, n_out = w.dims[l], w.dims[l + 1]
+            f = 2 * B * n_in * n_out
+            Y = torch.empty(B, n_out, device=self.X.device)
+            out.append((f"fwd_gemm_l{l + 1}", f,
+                        (lambda l=l, Y=Y: dl.dense_act_fwd(hs[l], m.W[l], m.b[l], w.acts[l], Y=Y))))
+            if l > 0:
+                G = torch.randn(B, n_out, device=self.X.device) * 1e-4
+                dX = hs[l].clone()
+                out.append((f"dx_gemm_l{l + 1}", f,
+                            (lambda l=l, G=G, dX=dX: dl.dense_act_vjp(
+                                G, None, None, m.W[l], need_dw=False, dX=dX,
+                                dx_act=w.acts[l - 1], dx_saved=dX))))
+        return out
+
+
+class TmlpBench:
+    """Transformer-MLP block shapes, bf16 operands: fwd + vjp of
+    1024 -> 4096 (GELU tanh) -> 1024 with float32 master weights."""
+
+    def __init__(self, dl, w, dev):
+        import torch
+        self.dl, self.w = dl, w
+        inp = si.generate(w)
+        bf = torch.bfloat16
+        T, d, f = w.batch, w.dims[0], w.dims[1]
+        self.X = torch.from_numpy(inp.X).to(dev).to(bf)
+        self.dY = torch.from_numpy(inp.dY).to(dev).to(bf)
+        self.W = [torch.from_numpy(a).to(dev) for a in inp.W]
+        self.b = [torch.from_numpy(a).to(dev) for a in inp.b]
+        self.Wb = [torch.empty(a.shape, dtype=bf, device=dev) for a in self.W]
+        self.H = torch.empty(T, f, dtype=bf, device=dev)
+        self.Z = torch.empty(T, f, dtype=bf, device=dev)
+        self.Y = torch.empty(T, d, dtype=bf, device=dev)
+        self.dX = torch.empty(T, d, dtype=bf, device=dev)
+        self.dW = [torch.empty_like(a) for a in self.W]
+        self.db = [torch.empty_like(a) for a in self.b]
+        n = max(dl.dense_act_vjp_workspace_size(dl.DL_BF16, 0, T, f, d),
+                dl.dense_act_vjp_workspace_size(dl.DL_BF16, 0, T, d, f), 1)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def step(self):
+        dl = self.dl
+        for l in range(2):
+            dl.dense_cast_bf16(self.W[l], self.Wb[l])
+        dl.dense_act_fwd(self.X, self.Wb[0], self.b[0], dl.ACT_GELU_TANH, Y=self.H, Z=self.Z)
+        dl.dense_act_fwd(self.H, self.Wb[1], self.b[1], dl.ACT_IDENTITY, Y=self.Y)
+        # vjp of layer 2 writes dZ1 = (dY W2) * gelu'(Z1) over Z1 in place
+        dl.dense_act_vjp(self.dY, None, self.H, self.Wb[1], dl.ACT_IDENTITY, dX=self.Z,
+                         dW=self.dW[1], db=self.db[1], dx_act=dl.ACT_GELU_TANH,
+                         dx_saved=self.Z, ws=self.ws)
+        dl.dense_act_vjp(self.Z, None, self.X, self.Wb[0], dl.ACT_IDENTITY, dX=self.dX,
+                         dW=self.dW[0], db=self.db[0], ws=self.ws)
+
+    def flops(self):
+        return 6 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
+
+    def kernels(self):
+        dl = self.dl
+        f = 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
+        return [("fwd_gemm_l1_gelu", f, lambda: dl.dense_act_fwd(
+                    self.X, self.Wb[0], self.b[0], dl.ACT_GELU_TANH, Y=self.H, Z=self.Z)),
+                ("fwd_gemm_l2", f, lambda: dl.dense_act_fwd(
+                    self.H, self.Wb[1], self.b[1], dl.ACT_IDENTITY, Y=self.Y)),
+                ("dx_gemm_l1", f, lambda: dl.dense_act_vjp(
+                    self.Z, None, None, self.Wb[0], need_dw=False, dX=self.dX))]
+
+
+class HeadBench:
+    """Classifier head: Linear 768 -> 32000, softmax-xent, dX/dW/db, AdamW."""
+
+    def __init__(self, dl, w, dev):
+        import torch
+        self.dl, self.w = dl, w
+        inp = si.generate(w)
+        B, d, C = w.batch, w.dims[0], w.dims[1]
+        self.X = torch.from_numpy(inp.X).to(dev)
+        self.y = torch.from_numpy(inp.labels).to(dev)
+        self.W = torch.from_numpy(inp.W[0]).to(dev)
+        self.b = torch.from_numpy(inp.b[0]).to(dev)
+        self.logits = torch.empty(B, C, device=dev)
+        self.dX = torch.empty(B, d, device=dev)
+        self.dW, self.db = torch.empty_like(self.W), torch.empty_like(self.b)
+        self.m = [torch.zeros_like(self.W), torch.zeros_like(self.b)]
+        self.v = [torch.zeros_like(self.W), torch.zeros_like(self.b)]
+        self.loss = torch.empty(1, device=dev)
+        self.ws = torch.empty(max(dl.softmax_xent_workspace_size(B, C),
+                                  dl.dense_act_vjp_workspace_size(0, 0, B, d, C), 1),
+                              dtype=torch.uint8, device=dev)
+        self.t = 0
+
+    def step(self):
+        dl, o = self.dl, self.w.optim
+        self.t += 1
+        dl.dense_act_fwd(self.X, self.W, self.b, dl.ACT_IDENTITY, Y=self.logits)
+        dl.softmax_xent_fwd_bwd(self.logits, self.y, inplace=True, loss=self.loss, ws=self.ws)
+        dl.dense_act_vjp(self.logits, None, self.X, self.W, dX=self.dX, dW=self.dW, db=self.db,
+                         ws=self.ws)
+        for p, g, m, v in ((self.W, self.dW, self.m[0], self.v[0]),
+                           (self.b, self.db, self.m[1], self.v[1])):
+            dl.adamw_step(p, g, m, v, o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.t)
+
+    def flops(self):
+        return 3 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
+
+    def kernels(self):
+        dl = self.dl
+        f = 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
+        return [("fwd_gemm", f, lambda: dl.dense_act_fwd(
+                    self.X, self.W, self.b, dl.ACT_IDENTITY, Y=self.logits)),
+                ("dx_gemm", f, lambda: dl.dense_act_vjp(
+                    self.logits, None, None, self.W, need_dw=False, dX=self.dX))]
+
+
+BENCHES = {"mlp_small": MLPBench, "mlp_adamw": MLPBench, "mlp_wide": MLPBench,
+           "tmlp_bf16": TmlpBench, "head_xent": HeadBench}
+DEFAULTS = {"mlp_small": (200, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
+            "tmlp_bf16": (20, 3), "head_xent": (5, 1)}
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle (as it stands) on a bounded sample of the same
+    workload: whole training steps on the full batch, repeated until the time
+    budget is spent (at least one)."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    inp = si.generate(w)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    st = O.MLPState(inp.W, inp.b)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.mlp_train_step(st, inp.X, inp.labels, w.acts, w.optim)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full {w.batch}-sample {w.optim.kind} training steps of the "
+                      f"{'-'.join(map(str, w.dims))} MLP (float64 NumPy, BLAS threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="mlp_adamw", choices=sorted(BENCHES))
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_layers_amd as dl
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = si.WORKLOADS[args.config]
+    steps, warmup = DEFAULTS[args.config]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    bench = BENCHES[args.config](dl, w, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        bench.step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / steps
+    gpu_ms_step = ev0.elapsed_time(ev1) / steps
+    step_tflops = bench.flops() / (ms_step * 1e-3) / 1e12
+
+    # per-kernel: each GEMM of the step, launched alone with the step's shapes
+    kern = []
+    for name, fl, fn in bench.kernels():
+        ms = _events_time(fn, args.kernel_iters, stream)
+        kern.append({"kernel": name, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12})
+    dom = max(kern, key=lambda k: k["ms"])
+    peak = PEAK_BF16_MFMA if w.dtype == "bf16" else PEAK_FP32_MFMA
+    roofline = {"bound": "mfma", "achieved": round(dom["tflops"], 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4), "traffic": None,
+                "kernel": dom["kernel"]}
+
+    cpu = None
+    if not args.no_cpu_baseline and w.has_loss and args.config in ("mlp_small", "mlp_adamw"):
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "gpu_ms_per_step": round(gpu_ms_step, 5),
+        "step_tflops": round(step_tflops, 3),
+        "step_frac_of_peak": round(step_tflops / peak, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dims": w.dims,
+                   "optimizer": None if w.optim is None else w.optim.kind,
+                   "gemm_flops_per_step": bench.flops()},
+        "roofline": roofline,
+        "kernels": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in x.items()}
+                    for x in kern],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -41,8 +41,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-_vp, _i64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                              ctypes.c_float, ctypes.c_size_t)
+_vp, _i64, _i32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                              ctypes.c_double, ctypes.c_size_t)
 
 
 class DLLayer(ctypes.Structure):
@@ -53,9 +53,9 @@ class DLLayer(ctypes.Structure):
 
 
 class DLOpt(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_float),
-                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
-                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+    _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_double),
+                ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
                 ("step", ctypes.c_int64)]
 
 
@@ -79,9 +79,9 @@ _c = {
     "softmax_xent_fwd_bwd": _sig("softmax_xent_fwd_bwd", _i32,
                                  [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "softmax_xent_workspace_size": _sig("softmax_xent_workspace_size", _sz, [_i64, _i64]),
-    "sgd_step": _sig("sgd_step", _i32, [_vp, _i64, _vp, _vp, _f32]),
+    "sgd_step": _sig("sgd_step", _i32, [_vp, _i64, _vp, _vp, _f64]),
     "adamw_step": _sig("adamw_step", _i32,
-                       [_vp, _i64, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _f32, _f32, _i64]),
+                       [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
     "dense_cast_bf16": _sig("dense_cast_bf16", _i32, [_vp, _i64, _vp, _vp]),
     "mlp_train_step": _sig("mlp_train_step", _i32,
                            [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,

@@ -298,37 +298,45 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
   return DL_OK;
 }
 
-int sgd_step(void* stream, int64_t n, float* w, const float* g, float lr) {
+static dl::OptConsts opt_consts(double lr, double beta1, double beta2, double eps, double wd,
+                                int64_t t) {
+  dl::OptConsts c;
+  c.lr = (float)lr;
+  c.decay = (float)(1.0 - lr * wd);
+  c.b1 = (float)beta1;
+  c.omb1 = (float)(1.0 - beta1);
+  c.b2 = (float)beta2;
+  c.omb2 = (float)(1.0 - beta2);
+  const double bc1 = t >= 1 ? 1.0 - std::pow(beta1, (double)t) : 1.0;
+  const double bc2 = t >= 1 ? 1.0 - std::pow(beta2, (double)t) : 1.0;
+  c.step_size = (float)(lr / bc1);
+  c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  c.eps = (float)eps;
+  return c;
+}
+
+static bool betas_ok(double b1, double b2) { return b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0; }
+
+int sgd_step(void* stream, int64_t n, float* w, const float* g, double lr) {
   if (n <= 0) return fail(DL_INVALID_ARGUMENT, "sgd_step: n must be positive");
   if (!w || !g) return fail(DL_INVALID_ARGUMENT, "sgd_step: w and g are required");
   if (overlap(w, n * 4, g, n * 4)) return fail(DL_ALIASING, "sgd_step: w overlaps g");
-  hipError_t e = dl::launch_sgd(n, w, g, lr, static_cast<hipStream_t>(stream));
+  hipError_t e = dl::launch_sgd(n, w, g, opt_consts(lr, 0, 0, 0, 0, 0), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sgd_step");
   return DL_OK;
 }
 
-static void adam_factors(float beta1, float beta2, float lr, int64_t t, float& step_size,
-                         float& inv_sqrt_bc2) {
-  const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
-  const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
-  step_size = (float)((double)lr / bc1);
-  inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
-}
-
-int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m, float* v, float lr,
-               float beta1, float beta2, float eps, float weight_decay, int64_t step) {
+int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m, float* v, double lr,
+               double beta1, double beta2, double eps, double weight_decay, int64_t step) {
   if (n <= 0) return fail(DL_INVALID_ARGUMENT, "adamw_step: n must be positive");
   if (!w || !g || !m || !v) return fail(DL_INVALID_ARGUMENT, "adamw_step: w, g, m and v are required");
   if (step < 1) return fail(DL_INVALID_ARGUMENT, "adamw_step: step counts from 1");
-  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
-    return fail(DL_INVALID_ARGUMENT, "adamw_step: betas must be in [0, 1)");
+  if (!betas_ok(beta1, beta2)) return fail(DL_INVALID_ARGUMENT, "adamw_step: betas must be in [0, 1)");
   const size_t nb = (size_t)n * 4;
   if (overlap(w, nb, g, nb) || overlap(w, nb, m, nb) || overlap(w, nb, v, nb) ||
       overlap(g, nb, m, nb) || overlap(g, nb, v, nb) || overlap(m, nb, v, nb))
     return fail(DL_ALIASING, "adamw_step: w, g, m, v must be distinct");
-  float ss, isb;
-  adam_factors(beta1, beta2, lr, step, ss, isb);
-  hipError_t e = dl::launch_adamw(n, w, g, m, v, lr, beta1, beta2, eps, weight_decay, ss, isb,
+  hipError_t e = dl::launch_adamw(n, w, g, m, v, opt_consts(lr, beta1, beta2, eps, weight_decay, step),
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "adamw_step");
   return DL_OK;
@@ -387,7 +395,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: bad optimizer kind %d", opt->kind);
   if (opt->kind == DL_OPT_ADAMW && opt->step < 1)
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: AdamW step counts from 1");
-  if (opt->kind == DL_OPT_ADAMW && (!(opt->beta1 >= 0.f && opt->beta1 < 1.f) || !(opt->beta2 >= 0.f && opt->beta2 < 1.f)))
+  if (opt->kind == DL_OPT_ADAMW && !betas_ok(opt->beta1, opt->beta2))
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: betas must be in [0, 1)");
   int n_tensors = 0;
   for (int l = 0; l < n_layers; ++l) {
@@ -473,10 +481,11 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     }
   }
   segs.start_block[segs.count] = blocks;
-  float ss = 0.f, isb = 0.f;
-  if (opt->kind == DL_OPT_ADAMW) adam_factors(opt->beta1, opt->beta2, opt->lr, opt->step, ss, isb);
-  e = dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, opt->lr, opt->beta1, opt->beta2,
-                           opt->eps, opt->weight_decay, ss, isb, s);
+  const dl::OptConsts oc = opt->kind == DL_OPT_ADAMW
+                               ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
+                                            opt->weight_decay, opt->step)
+                               : opt_consts(opt->lr, 0, 0, 0, 0, 0);
+  e = dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, oc, s);
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");
   return DL_OK;
 }

@@ -139,11 +139,20 @@ hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst,
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s);
-hipError_t launch_sgd(int64_t n, float* w, const float* g, float lr,
+// Optimizer constants, each formed in double on the host and rounded once.
+struct OptConsts {
+  float lr;            // SGD step
+  float decay;         // 1 - lr wd
+  float b1, omb1;      // beta1, 1 - beta1
+  float b2, omb2;      // beta2, 1 - beta2
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+hipError_t launch_sgd(int64_t n, float* w, const float* g, const OptConsts& c,
                       hipStream_t s);
 hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
-                        float lr, float beta1, float beta2, float eps, float wd,
-                        float step_size, float inv_sqrt_bc2, hipStream_t s);
+                        const OptConsts& c, hipStream_t s);
 
 // Multi-tensor optimizer: one launch updates up to kMaxSegs arrays.
 constexpr int kMaxSegs = 32;
@@ -158,9 +167,7 @@ struct OptSegs {
 };
 constexpr int kOptBlock = 256;
 constexpr int kOptElemsPerBlock = kOptBlock * 4 * 4;  // 4 float4 per thread
-hipError_t launch_opt_multi(const OptSegs& segs, int kind, float lr,
-                            float beta1, float beta2, float eps, float wd,
-                            float step_size, float inv_sqrt_bc2,
+hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);
 
 }  // namespace dl

@@ -4,24 +4,23 @@
 // handles four float4 groups so a workgroup moves 16 KB per array.
 //
 // AdamW, per element (decoupled decay first, then the bias-corrected Adam
-// step; step_size = lr / (1 - b1^t) and inv_sqrt_bc2 = 1 / sqrt(1 - b2^t) are
-// computed on the host in double):
-//   w *= 1 - lr wd;  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+// step; decay = 1 - lr wd, omb1 = 1 - b1, omb2 = 1 - b2, step_size =
+// lr / (1 - b1^t) and inv_sqrt_bc2 = 1 / sqrt(1 - b2^t) are formed on the host
+// in double and rounded once):
+//   w *= decay;  m = b1 m + omb1 g;  v = b2 v + omb2 g^2;
 //   w -= step_size m / (sqrt(v) inv_sqrt_bc2 + eps)
 #include "common.hpp"
 
 namespace dl {
 namespace {
 
-struct AdamParams {
-  float lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2;
-};
+using AdamParams = OptConsts;
 
 __device__ __forceinline__ void adam_elem(float& w, float g, float& m, float& v,
                                           const AdamParams& p) {
-  w *= 1.0f - p.lr * p.wd;
-  m = p.beta1 * m + (1.0f - p.beta1) * g;
-  v = p.beta2 * v + (1.0f - p.beta2) * g * g;
+  w *= p.decay;
+  m = p.b1 * m + p.omb1 * g;
+  v = p.b2 * v + p.omb2 * (g * g);
   w -= p.step_size * m / (sqrtf(v) * p.inv_sqrt_bc2 + p.eps);
 }
 
@@ -91,8 +90,7 @@ opt_multi_kernel(OptSegs segs, AdamParams p) {
 
 }  // namespace
 
-hipError_t launch_sgd(int64_t n, float* w, const float* g, float lr, hipStream_t s) {
-  AdamParams p{lr, 0, 0, 0, 0, 0, 0};
+hipError_t launch_sgd(int64_t n, float* w, const float* g, const OptConsts& p, hipStream_t s) {
   const int64_t blocks = (n + kOptElemsPerBlock - 1) / kOptElemsPerBlock;
   const int vec = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(g)) & 15) == 0;
   hipLaunchKernelGGL(opt_single_kernel<0>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, n, w, g,
@@ -100,10 +98,8 @@ hipError_t launch_sgd(int64_t n, float* w, const float* g, float lr, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v, float lr,
-                        float beta1, float beta2, float eps, float wd, float step_size,
-                        float inv_sqrt_bc2, hipStream_t s) {
-  AdamParams p{lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2};
+hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
+                        const OptConsts& p, hipStream_t s) {
   const int64_t blocks = (n + kOptElemsPerBlock - 1) / kOptElemsPerBlock;
   const int vec = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(g) |
                     reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v)) & 15) == 0;
@@ -112,10 +108,7 @@ hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
   return hipGetLastError();
 }
 
-hipError_t launch_opt_multi(const OptSegs& segs, int kind, float lr, float beta1, float beta2,
-                            float eps, float wd, float step_size, float inv_sqrt_bc2,
-                            hipStream_t s) {
-  AdamParams p{lr, beta1, beta2, eps, wd, step_size, inv_sqrt_bc2};
+hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& p, hipStream_t s) {
   const int64_t blocks = segs.start_block[segs.count];
   if (blocks <= 0) return hipSuccess;
   if (kind == 0)

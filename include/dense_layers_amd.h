@@ -166,9 +166,10 @@ size_t softmax_xent_workspace_size(int64_t B, int64_t C);
 /*
  * sgd_step -- w <- w - lr g, elementwise over n float32 values (MuNet page,
  * "What runs today" and "Python training": SGD).  Plain: no momentum, no
- * decay.  w and g are device pointers; g must not overlap w.
+ * decay.  lr is rounded once to float32.  w and g are device pointers; g
+ * must not overlap w.
  */
-int sgd_step(void* stream, int64_t n, float* w, const float* g, float lr);
+int sgd_step(void* stream, int64_t n, float* w, const float* g, double lr);
 
 /*
  * adamw_step -- one AdamW step on n float32 values (MuNet page, "What runs
@@ -176,12 +177,15 @@ int sgd_step(void* stream, int64_t n, float* w, const float* g, float lr);
  * live with the parameter and start at zero on the first step):
  *   w <- w (1 - lr wd);  m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
  *   w <- w - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
- * step is t >= 1; the bias corrections are computed on the host in double.
+ * step is t >= 1.  The hyper-parameters are taken in double and the derived
+ * constants (1 - lr wd, 1 - b1, 1 - b2, lr / (1 - b1^t), 1 / sqrt(1 - b2^t))
+ * are formed on the host in double, each then rounded once to float32 for
+ * the element-wise float32 update.  beta1, beta2 in [0, 1).
  * w, g, m, v are distinct device arrays of n floats; m and v are updated.
  */
 int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m,
-               float* v, float lr, float beta1, float beta2, float eps,
-               float weight_decay, int64_t step);
+               float* v, double lr, double beta1, double beta2, double eps,
+               double weight_decay, int64_t step);
 
 /* ---- bf16 working copies -------------------------------------------------- */
 
@@ -211,7 +215,7 @@ typedef struct dl_layer {
 
 typedef struct dl_opt {
   int32_t kind;     /* enum dl_opt_kind */
-  float lr, beta1, beta2, eps, weight_decay;  /* betas/eps/wd: AdamW only */
+  double lr, beta1, beta2, eps, weight_decay;  /* betas/eps/wd: AdamW only */
   int64_t step;     /* AdamW step t >= 1 */
 } dl_opt_t;
 

@@ -264,8 +264,8 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
     ``eps``, ``weight_decay``.  ``relu_masks[l]``, when given, replaces layer
     l's ReLU mask (used only to adopt the other side's decision inside the
     rounding band).  Updates ``state`` in place (rounded to float32) and
-    returns a dict with the loss (pre-update), the float64 gradients and the
-    pre-activations.
+    returns a dict with the loss (pre-update), the float64 gradients, each
+    layer's masked upstream gradient G, its input h and pre-activation Z.
     """
     L = len(state.W)
     h = [np.asarray(X, dtype=np.float64)]
@@ -277,12 +277,14 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
     loss, dz, row_loss = softmax_xent_fwd_bwd(h[-1], labels)
     grads_W: List[np.ndarray] = [None] * L
     grads_b: List[np.ndarray] = [None] * L
+    Gs: List[np.ndarray] = [None] * L
     dY = dz
     for l in reversed(range(L)):
         mask = None if relu_masks is None else relu_masks[l]
         dX, dW, db = dense_act_vjp(dY, Zs[l], h[l], state.W[l], acts[l],
                                    need_dx=(l > 0), mask=mask)
         grads_W[l], grads_b[l] = dW, db
+        Gs[l] = dY * (act_grad(Zs[l], acts[l]) if mask is None else mask)
         dY = dX
     state.t += 1
     for l in range(L):
@@ -303,4 +305,4 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
         else:
             raise ValueError(f"unknown optimizer {opt.kind}")
     return {"loss": loss, "row_loss": row_loss, "dW": grads_W, "db": grads_b,
-            "Z": Zs, "h": h, "dlogits": dz}
+            "G": Gs, "Z": Zs, "h": h, "dlogits": dz}
