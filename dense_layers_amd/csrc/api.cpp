@@ -46,7 +46,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 
 // ---- GEMM planning ----------------------------------------------------------
-// Tiles: float32 {0: 128x128, 1: 64x64}; bf16 {0: 256x128, 1: 128x128}.  The
+// Tiles: float32 {0: 128x128x16, 1: 64x64x32}; bf16 {0: 256x128x64, 1: 128x128x64}.  The
 // large tile is used when it alone yields at least one workgroup per CU (256);
 // otherwise the small one.  Only the weight-gradient product (K = batch) is
 // split along K: slices are added until about two workgroups per CU exist,
@@ -67,7 +67,7 @@ void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
     bk = 64;
   } else {
     bm = bn = tile == 0 ? 128 : 64;
-    bk = 16;
+    bk = tile == 0 ? 16 : 32;
   }
 }
 
@@ -130,8 +130,10 @@ hipError_t fwd_gemm(int dtype, int act, int64_t B, int64_t in, int64_t out, cons
 }
 
 // dW = G^T X (+ db = column sums of G), split-K partials in `partial_ws`.
+// With reduce = false and a split plan, the partial slices are left for the
+// caller (the optimizer kernel of the MLP step adds them up).
 hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
-                   float* dW, float* db, void* partial_ws, hipStream_t s) {
+                   float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true) {
   dl::GemmDesc d = blank_desc();
   d.M = (int)out; d.N = (int)in; d.K = (int)B;
   d.A = G; d.lda = out; d.a_layout = dl::MN_MAJOR;
@@ -151,7 +153,7 @@ hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
     d.db = db;
   }
   hipError_t e = run_gemm(dtype, d, p.tile, s);
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess || p.splits == 1 || !reduce) return e;
   return dl::launch_splitk_reduce((int)out, (int)in, p.splits, d.partial, d.db_partial, dW, in, db,
                                   s);
 }
@@ -353,10 +355,13 @@ int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
 
 // ---- whole MLP step ---------------------------------------------------------
 // Workspace: per-layer outputs Y_l [B, out_l] (the last one holds the logits,
-// then dlogits in place), the per-row losses, and the largest split-K partial
-// buffer among the layers' weight gradients.  During the backward pass the
-// dX epilogue of layer l writes G_{l-1} = (G_l W_l) * relu'(Y_{l-1}) over
-// Y_{l-1} in place, after layer l's dW has consumed Y_{l-1}.
+// then dlogits in place), the per-row losses, and one split-K partial buffer
+// per layer whose weight gradient is split along the batch.  During the
+// backward pass the dX epilogue of layer l writes
+// G_{l-1} = (G_l W_l) * relu'(Y_{l-1}) over Y_{l-1} in place, after layer l's
+// dW has consumed Y_{l-1}.  Split weight gradients are not reduced by a pass
+// of their own: the optimizer kernel adds the slices, stores dW / db and
+// applies the update in one read.
 
 static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
                          size_t* rl_off, size_t* part_off) {
@@ -367,21 +372,20 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
   }
   *rl_off = off;
   off += align_up((size_t)B * 4);
-  *part_off = off;
-  size_t part = 0;
   for (int l = 0; l < L; ++l) {
+    part_off[l] = off;
     const Plan p = plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B);
-    part = std::max(part, splitk_bytes(p, layers[l].out, layers[l].in));
+    off += splitk_bytes(p, layers[l].out, layers[l].in);
   }
-  return off + part;
+  return off;
 }
 
 size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer_t* layers) {
   if (!dim_ok(B) || n_layers < 1 || n_layers > 16 || !layers) return 0;
   for (int l = 0; l < n_layers; ++l)
     if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
-  size_t y_off[16], rl, part;
-  return mlp_layout(B, n_layers, layers, y_off, &rl, &part);
+  size_t y_off[16], rl, part[16];
+  return mlp_layout(B, n_layers, layers, y_off, &rl, part);
 }
 
 int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
@@ -420,8 +424,8 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // activation of its own (its derivative would need the overwritten output).
   if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
     return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
-  size_t y_off[16], rl_off, part_off;
-  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, &part_off);
+  size_t y_off[16], rl_off, part_off[16];
+  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off);
   if (!ws || ws_bytes < need)
     return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -432,7 +436,6 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   float* Y[16];
   for (int l = 0; l < n_layers; ++l) Y[l] = reinterpret_cast<float*>(base + y_off[l]);
   float* row_loss = reinterpret_cast<float*>(base + rl_off);
-  void* part = base + part_off;
   const int L = n_layers;
   const int64_t C = layers[L - 1].out;
   hipError_t e;
@@ -451,24 +454,29 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   for (int l = L - 1; l >= 0; --l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
-    e = dw_gemm(DL_F32, B, ly.in, ly.out, Y[l], in, ly.dW, ly.db, part, s);
+    e = dw_gemm(DL_F32, B, ly.in, ly.out, Y[l], in, ly.dW, ly.db, base + part_off[l], s,
+                /*reduce=*/false);
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
     if (l > 0) {
       e = dx_gemm(DL_F32, B, ly.in, ly.out, Y[l], ly.W, Y[l - 1], layers[l - 1].act, Y[l - 1], s);
       if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dX)");
     }
   }
-  // optimizer over every W and b in one launch
+  // optimizer over every W and b in one launch (finishing split-K sums)
   dl::OptSegs segs;
   memset(&segs, 0, sizeof(segs));
   int64_t blocks = 0;
   for (int l = 0; l < L; ++l) {
     const dl_layer_t& ly = layers[l];
+    const Plan p = plan_gemm(DL_F32, dl::EPI_DW, ly.out, ly.in, B);
+    char* pb = base + part_off[l];
     float* ws_[2] = {ly.W, ly.b};
-    const float* gs_[2] = {ly.dW, ly.db};
+    float* gs_[2] = {ly.dW, ly.db};
     float* ms_[2] = {ly.mW, ly.mb};
     float* vs_[2] = {ly.vW, ly.vb};
     const int64_t ns_[2] = {ly.out * ly.in, ly.out};
+    const float* ps_[2] = {reinterpret_cast<float*>(pb),
+                           reinterpret_cast<float*>(pb + align_up((size_t)p.splits * ly.out * ly.in * 4))};
     for (int t = 0; t < 2; ++t) {
       const int k = segs.count++;
       segs.start_block[k] = blocks;
@@ -477,6 +485,10 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
       segs.g[k] = gs_[t];
       segs.m[k] = ms_[t];
       segs.v[k] = vs_[t];
+      segs.splits[k] = p.splits;
+      segs.part[k] = p.splits > 1 ? ps_[t] : nullptr;
+      segs.part_stride[k] = ns_[t];
+      segs.g_out[k] = gs_[t];
       blocks += (ns_[t] + dl::kOptElemsPerBlock - 1) / dl::kOptElemsPerBlock;
     }
   }

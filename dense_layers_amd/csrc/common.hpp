@@ -154,8 +154,12 @@ hipError_t launch_sgd(int64_t n, float* w, const float* g, const OptConsts& c,
 hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
                         const OptConsts& c, hipStream_t s);
 
-// Multi-tensor optimizer: one launch updates up to kMaxSegs arrays.
 constexpr int kMaxSegs = 32;
+// Multi-tensor optimizer: one launch updates up to kMaxSegs arrays.  The
+// gradient of segment k is g[k] when splits[k] <= 1; otherwise it is the
+// split-K partial sum  sum_s part[k][s * part_stride[k] + i]  (added in slice
+// order), which is also stored to g_out[k] -- the optimizer finishes the
+// weight-gradient reduction instead of a separate pass.
 struct OptSegs {
   int count;
   int64_t start_block[kMaxSegs + 1];  // prefix sums of blocks per segment
@@ -164,6 +168,10 @@ struct OptSegs {
   const float* g[kMaxSegs];
   float* m[kMaxSegs];
   float* v[kMaxSegs];
+  const float* part[kMaxSegs];
+  int64_t part_stride[kMaxSegs];
+  int splits[kMaxSegs];
+  float* g_out[kMaxSegs];
 };
 constexpr int kOptBlock = 256;
 constexpr int kOptElemsPerBlock = kOptBlock * 4 * 4;  // 4 float4 per thread

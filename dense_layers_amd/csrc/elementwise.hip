@@ -9,22 +9,27 @@
 namespace dl {
 namespace {
 
+// dW (contiguous [M, N]) = sum over slices of partial[s][M][N], in slice
+// order; each thread owns 4 consecutive elements when the slice stride keeps
+// 16-byte alignment, one otherwise.  The loads of 8 slices are issued before
+// they are added so the latency of one slice is not paid per slice.
 __global__ void __launch_bounds__(256)
-splitk_reduce_kernel(int M, int N, int splits, const float* __restrict__ partial,
-                     const float* __restrict__ db_partial, float* __restrict__ C, int64_t ldc,
-                     float* __restrict__ db) {
-  const int64_t MN = (int64_t)M * N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < MN) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += partial[s * MN + i];
-    const int64_t row = i / N, col = i - row * N;
-    C[row * ldc + col] = acc;
-  }
-  if (db != nullptr && i < M) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += db_partial[(int64_t)s * M + i];
-    db[i] = acc;
+splitk_reduce_kernel(int64_t MN, int splits, const float* __restrict__ partial, float* __restrict__ C,
+                     int vec) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (vec) {
+    const int64_t i = t * 4;
+    if (i >= MN) return;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + i);
+#pragma unroll 8
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4*>(partial + s * MN + i);
+    *reinterpret_cast<f32x4*>(C + i) = acc;
+  } else {
+    if (t >= MN) return;
+    float acc = partial[t];
+#pragma unroll 8
+    for (int s = 1; s < splits; ++s) acc += partial[s * MN + t];
+    C[t] = acc;
   }
 }
 
@@ -56,9 +61,17 @@ unsigned grid_for(int64_t n) {
 hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 const float* db_partial, float* C, int64_t ldc, float* db,
                                 hipStream_t s) {
-  const int64_t n = std::max<int64_t>((int64_t)M * N, M);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M,
-                     N, splits, partial, db_partial, C, ldc, db);
+  if (ldc != N) return hipErrorInvalidValue;
+  const int64_t MN = (int64_t)M * N;
+  const int vec = (MN % 4 == 0) && (((reinterpret_cast<uintptr_t>(partial) |
+                                      reinterpret_cast<uintptr_t>(C)) & 15) == 0);
+  const int64_t threads = vec ? (MN + 3) / 4 : MN;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     MN, splits, partial, C, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || db == nullptr) return e;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
+                     (int64_t)M, splits, db_partial, db, 0);
   return hipGetLastError();
 }
 

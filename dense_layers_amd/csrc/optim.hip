@@ -24,10 +24,39 @@ __device__ __forceinline__ void adam_elem(float& w, float g, float& m, float& v,
   w -= p.step_size * m / (sqrtf(v) * p.inv_sqrt_bc2 + p.eps);
 }
 
+// Where an array's gradient comes from: a plain array, or split-K partial
+// slices summed in slice order (then also written to `out`).
+struct GradSrc {
+  const float* g;
+  const float* part;
+  int64_t stride;
+  int splits;
+  float* out;
+};
+
+__device__ __forceinline__ float grad1(const GradSrc& s, int64_t i) {
+  if (s.splits <= 1) return s.g[i];
+  float acc = s.part[i];
+#pragma unroll 8
+  for (int k = 1; k < s.splits; ++k) acc += s.part[(int64_t)k * s.stride + i];
+  s.out[i] = acc;
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 grad4(const GradSrc& s, int64_t i) {
+  if (s.splits <= 1) return *reinterpret_cast<const f32x4*>(s.g + i);
+  f32x4 acc = *reinterpret_cast<const f32x4*>(s.part + i);
+#pragma unroll 8
+  for (int k = 1; k < s.splits; ++k)
+    acc += *reinterpret_cast<const f32x4*>(s.part + (int64_t)k * s.stride + i);
+  *reinterpret_cast<f32x4*>(s.out + i) = acc;
+  return acc;
+}
+
 // Process elements [base, base + kOptElemsPerBlock) of one array.
 template <int KIND>
 __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __restrict__ w,
-                                          const float* __restrict__ g, float* __restrict__ m,
+                                          const GradSrc& gs, float* __restrict__ m,
                                           float* __restrict__ v, const AdamParams& p,
                                           bool vec) {
   const int64_t end = min(n, base + (int64_t)kOptElemsPerBlock);
@@ -36,7 +65,7 @@ __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __rest
     for (int it = 0; it < 4; ++it) {
       const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
       f32x4 wv = *reinterpret_cast<const f32x4*>(w + i);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
+      const f32x4 gv = grad4(gs, i);
       if (KIND == 0) {
         wv -= p.lr * gv;
       } else {
@@ -55,11 +84,12 @@ __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __rest
     }
   } else {
     for (int64_t i = base + threadIdx.x; i < end; i += kOptBlock) {
+      const float g = grad1(gs, i);
       if (KIND == 0) {
-        w[i] -= p.lr * g[i];
+        w[i] -= p.lr * g;
       } else {
         float we = w[i], me = m[i], ve = v[i];
-        adam_elem(we, g[i], me, ve, p);
+        adam_elem(we, g, me, ve, p);
         w[i] = we; m[i] = me; v[i] = ve;
       }
     }
@@ -69,7 +99,8 @@ __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __rest
 template <int KIND>
 __global__ void __launch_bounds__(kOptBlock)
 opt_single_kernel(int64_t n, float* w, const float* g, float* m, float* v, AdamParams p, int vec) {
-  opt_block<KIND>(n, (int64_t)blockIdx.x * kOptElemsPerBlock, w, g, m, v, p, vec);
+  const GradSrc gs{g, nullptr, 0, 1, nullptr};
+  opt_block<KIND>(n, (int64_t)blockIdx.x * kOptElemsPerBlock, w, gs, m, v, p, vec);
 }
 
 // One launch over several arrays: block b belongs to the segment whose
@@ -81,11 +112,16 @@ opt_multi_kernel(OptSegs segs, AdamParams p) {
   int s = 0;
   while (s + 1 < segs.count && b >= segs.start_block[s + 1]) ++s;
   const int64_t local = b - segs.start_block[s];
-  const bool vec = ((reinterpret_cast<uintptr_t>(segs.w[s]) | reinterpret_cast<uintptr_t>(segs.g[s]) |
-                     (KIND ? (reinterpret_cast<uintptr_t>(segs.m[s]) |
-                              reinterpret_cast<uintptr_t>(segs.v[s])) : 0)) & 15) == 0;
-  opt_block<KIND>(segs.n[s], local * kOptElemsPerBlock, segs.w[s], segs.g[s], segs.m[s],
-                  segs.v[s], p, vec);
+  const GradSrc gs{segs.g[s], segs.part[s], segs.part_stride[s], segs.splits[s], segs.g_out[s]};
+  uintptr_t addr = reinterpret_cast<uintptr_t>(segs.w[s]);
+  if (KIND) addr |= reinterpret_cast<uintptr_t>(segs.m[s]) | reinterpret_cast<uintptr_t>(segs.v[s]);
+  if (gs.splits > 1)
+    addr |= reinterpret_cast<uintptr_t>(gs.part) | reinterpret_cast<uintptr_t>(gs.out) |
+            static_cast<uintptr_t>(gs.stride * 4);
+  else
+    addr |= reinterpret_cast<uintptr_t>(gs.g);
+  opt_block<KIND>(segs.n[s], local * kOptElemsPerBlock, segs.w[s], gs, segs.m[s], segs.v[s], p,
+                  (addr & 15) == 0);
 }
 
 }  // namespace

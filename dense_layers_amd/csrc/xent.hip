@@ -173,19 +173,29 @@ xent_rows_wide_kernel(int64_t B, int64_t C, const float* logits, const int32_t* 
   }
 }
 
-// Mean of the per-row losses: one workgroup, fixed summation order, float64.
-__global__ void __launch_bounds__(256)
+// Mean of the per-row losses: one workgroup of 1024 threads, fixed summation
+// order (each thread a strided slice, then a tree), float64 accumulation.
+constexpr int kMeanThreads = 1024;
+__global__ void __launch_bounds__(kMeanThreads)
 loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restrict__ loss) {
-  __shared__ double red[256];
+  __shared__ double red[kMeanThreads / 64];
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < B; i += 256) acc += (double)row_loss[i];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
+  int64_t i = threadIdx.x;
+  for (; i + 3 * kMeanThreads < B; i += 4 * kMeanThreads) {
+    const float a = row_loss[i], b = row_loss[i + kMeanThreads];
+    const float c = row_loss[i + 2 * kMeanThreads], d = row_loss[i + 3 * kMeanThreads];
+    acc += ((double)a + (double)b) + ((double)c + (double)d);
   }
-  if (threadIdx.x == 0) loss[0] = (float)(red[0] / (double)B);
+  for (; i < B; i += kMeanThreads) acc += (double)row_loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kMeanThreads / 64; ++w) t += red[w];
+    loss[0] = (float)(t / (double)B);
+  }
 }
 
 template <int TPR, int NI, bool VEC>
@@ -221,7 +231,7 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(256), 0, s, B, row_loss, loss);
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(kMeanThreads), 0, s, B, row_loss, loss);
   return hipGetLastError();
 }
 
