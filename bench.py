@@ -6,9 +6,10 @@ forward / softmax-xent / backward / AdamW update through mlp_train_step.
 Other workloads (--config) are measured the same way for the design notes.
 
 Prints one JSON line: whole-step throughput (train steps/s), the step's
-algorithmic GEMM TFLOP/s, a roofline entry for the dominant kernel (its own
-average launch time, HIP events on the launch stream) and the float64 CPU
-oracle timed on a bounded sample of the same workload.
+algorithmic GEMM TFLOP/s, the time of every launch inside the step (a short
+pass with the library's per-launch HIP-event timing on the launch stream), a
+roofline entry for the dominant launch, and the float64 CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,19 +33,9 @@ PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
-def _events_time(fn, iters, stream):
-    import torch
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        fn()
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(iters):
-            fn()
-        end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / iters  # ms per call
+def _split(label):
+    name, k = label.split("#")
+    return name, int(k)
 
 
 class MLPBench:
@@ -54,7 +45,6 @@ class MLPBench:
         import torch
         self.dl, self.w = dl, w
         inp = si.generate(w)
-        self.inp = inp
         self.X = torch.from_numpy(inp.X).to(dev)
         self.y = torch.from_numpy(inp.labels).to(dev)
         self.mlp = dl.MLP([torch.from_numpy(a).to(dev) for a in inp.W],
@@ -73,30 +63,23 @@ class MLPBench:
     def flops(self):
         return self.w.gemm_flops_per_step()
 
-    def kernels(self):
-        """(name, flops per launch, zero-argument launcher of exactly that one
-        kernel with the step's own shapes and launch plan) for each GEMM."""
-        import torch
-        dl, w, m = self.dl, self.w, self.mlp
-        B = w.batch
-        hs = [self.X]
-        for l in range(w.n_layers):
-            hs.append(dl.dense_act_fwd(hs[-1], m.W[l], m.b[l], w.acts[l])[0])
-        out = []
-        for l in range(w.n_layers):
-            n_in, n_out = w.dims[l], w.dims[l + 1]
-            f = 2 * B * n_in * n_out
-            Y = torch.empty(B, n_out, device=self.X.device)
-            out.append((f"fwd_gemm_l{l + 1}", f,
-                        (lambda l=l, Y=Y: dl.dense_act_fwd(hs[l], m.W[l], m.b[l], w.acts[l], Y=Y))))
-            if l > 0:
-                G = torch.randn(B, n_out, device=self.X.device) * 1e-4
-                dX = hs[l].clone()
-                out.append((f"dx_gemm_l{l + 1}", f,
-                            (lambda l=l, G=G, dX=dX: dl.dense_act_vjp(
-                                G, None, None, m.W[l], need_dw=False, dX=dX,
-                                dx_act=w.acts[l - 1], dx_saved=dX))))
-        return out
+    def stage_work(self, label):
+        """Algorithmic work of one launch, by label name#k (the k-th launch of
+        that name within a step): ("flop", n) or ("byte", n)."""
+        w = self.w
+        B, L = w.batch, w.n_layers
+        name, k = _split(label)
+        if name == "fwd_gemm":
+            l = k
+        elif name in ("dw_gemm", "dx_gemm"):
+            l = L - 1 - k          # the backward pass runs from the last layer
+        elif name == "xent":
+            return "byte", 8 * B * w.dims[-1] + 8 * B
+        elif name in ("adamw_multi", "sgd_multi"):
+            return "byte", (28 if name == "adamw_multi" else 12) * w.n_params()
+        else:
+            return None
+        return "flop", 2 * B * w.dims[l] * w.dims[l + 1]
 
 
 class TmlpBench:
@@ -140,15 +123,14 @@ class TmlpBench:
     def flops(self):
         return 6 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
 
-    def kernels(self):
-        dl = self.dl
-        f = 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
-        return [("fwd_gemm_l1_gelu", f, lambda: dl.dense_act_fwd(
-                    self.X, self.Wb[0], self.b[0], dl.ACT_GELU_TANH, Y=self.H, Z=self.Z)),
-                ("fwd_gemm_l2", f, lambda: dl.dense_act_fwd(
-                    self.H, self.Wb[1], self.b[1], dl.ACT_IDENTITY, Y=self.Y)),
-                ("dx_gemm_l1", f, lambda: dl.dense_act_vjp(
-                    self.Z, None, None, self.Wb[0], need_dw=False, dX=self.dX))]
+    def stage_work(self, label):
+        T, d, f = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, _ = _split(label)
+        if name in ("fwd_gemm", "dw_gemm", "dx_gemm"):
+            return "flop", 2 * T * d * f
+        if name == "cast_bf16":
+            return "byte", 6 * d * f
+        return None
 
 
 class HeadBench:
@@ -188,13 +170,16 @@ class HeadBench:
     def flops(self):
         return 3 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
 
-    def kernels(self):
-        dl = self.dl
-        f = 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
-        return [("fwd_gemm", f, lambda: dl.dense_act_fwd(
-                    self.X, self.W, self.b, dl.ACT_IDENTITY, Y=self.logits)),
-                ("dx_gemm", f, lambda: dl.dense_act_vjp(
-                    self.logits, None, None, self.W, need_dw=False, dX=self.dX))]
+    def stage_work(self, label):
+        B, d, C = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, k = _split(label)
+        if name in ("fwd_gemm", "dw_gemm", "dx_gemm"):
+            return "flop", 2 * B * d * C
+        if name == "xent":
+            return "byte", 8 * B * C + 8 * B
+        if name == "adamw":
+            return "byte", 28 * (C * d if k == 0 else C)
+        return None
 
 
 BENCHES = {"mlp_small": MLPBench, "mlp_adamw": MLPBench, "mlp_wide": MLPBench,
@@ -225,6 +210,33 @@ def cpu_baseline(w, budget_s: float):
                       f"{'-'.join(map(str, w.dims))} MLP (float64 NumPy, BLAS threads)"}
 
 
+def profile_stages(dl, bench, n_steps):
+    """Average time of every launch in the step, from a pass with the
+    library's per-launch event timing on."""
+    import torch
+    dl.profile_begin(100000)
+    for _ in range(n_steps):
+        bench.step()
+    torch.cuda.synchronize()
+    recs = dl.profile_end(100000)
+    per_step = len(recs) // n_steps
+    labels, seen = [], {}
+    for name, _ in recs[:per_step]:
+        labels.append(f"{name}#{seen.get(name, 0)}")
+        seen[name] = seen.get(name, 0) + 1
+    stages = []
+    for j, lab in enumerate(labels):
+        ms = float(np.mean([recs[i * per_step + j][1] for i in range(n_steps)]))
+        st = {"stage": lab, "ms": round(ms, 5)}
+        wk = bench.stage_work(lab)
+        if wk is not None and wk[0] == "flop":
+            st["tflops"] = round(wk[1] / (ms * 1e-3) / 1e12, 3)
+        elif wk is not None:
+            st["gbs"] = round(wk[1] / (ms * 1e-3) / 1e9, 1)
+        stages.append(st)
+    return stages
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,7 +245,7 @@ def main():
     ap.add_argument("--config", default="mlp_adamw", choices=sorted(BENCHES))
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--prof-steps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -268,19 +280,20 @@ def main():
     gpu_ms_step = ev0.elapsed_time(ev1) / steps
     step_tflops = bench.flops() / (ms_step * 1e-3) / 1e12
 
-    # per-kernel: each GEMM of the step, launched alone with the step's shapes
-    kern = []
-    for name, fl, fn in bench.kernels():
-        ms = _events_time(fn, args.kernel_iters, stream)
-        kern.append({"kernel": name, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12})
-    dom = max(kern, key=lambda k: k["ms"])
+    stages = profile_stages(dl, bench, max(1, min(args.prof_steps, steps)))
+    dom = max(stages, key=lambda x: x["ms"])
     peak = PEAK_BF16_MFMA if w.dtype == "bf16" else PEAK_FP32_MFMA
-    roofline = {"bound": "mfma", "achieved": round(dom["tflops"], 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4), "traffic": None,
-                "kernel": dom["kernel"]}
+    if "tflops" in dom:
+        roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(dom["tflops"] / peak, 4), "traffic": None,
+                    "kernel": dom["stage"]}
+    else:
+        roofline = {"bound": "hbm", "achieved": dom.get("gbs"), "peak": PEAK_HBM,
+                    "unit": "GB/s", "frac": round((dom.get("gbs") or 0.0) / PEAK_HBM, 4),
+                    "traffic": None, "kernel": dom["stage"]}
 
     cpu = None
-    if not args.no_cpu_baseline and w.has_loss and args.config in ("mlp_small", "mlp_adamw"):
+    if not args.no_cpu_baseline and args.config in ("mlp_small", "mlp_adamw"):
         cpu = cpu_baseline(w, args.cpu_budget)
 
     line = {
@@ -303,8 +316,7 @@ def main():
                    "optimizer": None if w.optim is None else w.optim.kind,
                    "gemm_flops_per_step": bench.flops()},
         "roofline": roofline,
-        "kernels": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in x.items()}
-                    for x in kern],
+        "stages": stages,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -88,16 +88,36 @@ _c = {
                             ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
     "mlp_train_step_workspace_size": _sig("mlp_train_step_workspace_size", _sz,
                                           [_i64, _i32, ctypes.POINTER(DLLayer)]),
+    "dl_profile_begin": _sig("dl_profile_begin", _i32, [_i32]),
+    "dl_profile_end": _sig("dl_profile_end", _i32, [_i32, _vp, _vp]),
 }
 
 EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
-           "dense_cast_bf16", "mlp_train_step", "mlp_train_step_workspace_size"]
+           "dense_cast_bf16", "mlp_train_step", "mlp_train_step_workspace_size",
+           "dl_profile_begin", "dl_profile_end"]
 
 
 def build_target() -> str:
     return _c["dl_build_target"]().decode()
+
+
+def profile_begin(capacity: int = 4096):
+    """Start timing every launch this library makes from this thread."""
+    _check(_c["dl_profile_begin"](capacity))
+
+
+def profile_end(max_records: int = 4096):
+    """Stop timing; returns [(launch name, milliseconds)] in launch order."""
+    ms = (ctypes.c_float * max_records)()
+    names = ctypes.create_string_buffer(48 * max_records)
+    n = _c["dl_profile_end"](max_records, ms, names)
+    if n < 0:
+        raise DenseError(-n, _c["dl_last_error"]().decode())
+    k = min(n, max_records)
+    raw = names.raw
+    return [(raw[i * 48:(i + 1) * 48].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(k)]
 
 
 def _check(status: int):

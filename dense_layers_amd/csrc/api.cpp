@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/dense_layers_amd.h"
 #include "common.hpp"
@@ -32,6 +33,35 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(DL_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
 }
 
+// ---- optional per-launch timing ----------------------------------------------
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Prof {
+  bool on = false;
+  int capacity = 0;
+  int seen = 0;
+  std::vector<ProfRec> recs;
+};
+thread_local Prof g_prof;
+
+// Run `launch` (one kernel launch on stream s), timed when profiling is on.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof.on) return launch();
+  ++g_prof.seen;
+  if ((int)g_prof.recs.size() >= g_prof.capacity) return launch();
+  ProfRec r{name, nullptr, nullptr};
+  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+    return launch();
+  hipEventRecord(r.start, s);
+  hipError_t e = launch();
+  hipEventRecord(r.stop, s);
+  g_prof.recs.push_back(r);
+  return e;
+}
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -46,11 +76,12 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 
 // ---- GEMM planning ----------------------------------------------------------
-// Tiles: float32 {0: 128x128x16, 1: 64x64x32}; bf16 {0: 256x128x64, 1: 128x128x64}.  The
+// Tiles: float32 {0: 128x128x16, 1: 64x64x32}; bf16 128x128x64 for both.  The
 // large tile is used when it alone yields at least one workgroup per CU (256);
 // otherwise the small one.  Only the weight-gradient product (K = batch) is
-// split along K: slices are added until about two workgroups per CU exist,
-// each slice keeping at least four K tiles.
+// split along K: when it has fewer than two workgroups per CU, slices are
+// added until about four per CU exist (at most 64), each slice keeping at
+// least four K tiles.
 
 constexpr int kCUs = 256;
 
@@ -62,7 +93,7 @@ struct Plan {
 
 void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
   if (dtype == DL_BF16) {
-    bm = tile == 0 ? 256 : 128;
+    bm = 128;
     bn = 128;
     bk = 64;
   } else {
@@ -84,7 +115,7 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
     tiles = ceil_div(M, bm) * ceil_div(N, bn);
   }
   if (epi == dl::EPI_DW && tiles < 2 * kCUs) {
-    int64_t want = ceil_div(2 * kCUs, tiles);
+    int64_t want = ceil_div(4 * kCUs, tiles);
     const int64_t max_by_k = std::max<int64_t>(1, K / (4 * bk));
     want = std::min<int64_t>(std::min<int64_t>(want, max_by_k), 64);
     int64_t kps = ceil_div(ceil_div(K, want), bk) * bk;
@@ -126,7 +157,7 @@ hipError_t fwd_gemm(int dtype, int act, int64_t B, int64_t in, int64_t out, cons
   d.bias = b; d.act = act; d.Z = Z;
   const Plan p = plan_gemm(dtype, dl::EPI_FWD, B, out, in);
   d.k_per_split = (int)in;
-  return run_gemm(dtype, d, p.tile, s);
+  return timed("fwd_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
 }
 
 // dW = G^T X (+ db = column sums of G), split-K partials in `partial_ws`.
@@ -152,10 +183,12 @@ hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
   } else {
     d.db = db;
   }
-  hipError_t e = run_gemm(dtype, d, p.tile, s);
+  hipError_t e = timed("dw_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
   if (e != hipSuccess || p.splits == 1 || !reduce) return e;
-  return dl::launch_splitk_reduce((int)out, (int)in, p.splits, d.partial, d.db_partial, dW, in, db,
-                                  s);
+  return timed("splitk_reduce", s, [&] {
+    return dl::launch_splitk_reduce((int)out, (int)in, p.splits, d.partial, d.db_partial, dW, in,
+                                    db, s);
+  });
 }
 
 // dX = G W, optionally times mask_act'(mask_src).
@@ -170,7 +203,7 @@ hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
   d.mask_act = mask_act; d.mask_src = mask_src;
   const Plan p = plan_gemm(dtype, dl::EPI_DX, B, in, out);
   d.k_per_split = (int)out;
-  return run_gemm(dtype, d, p.tile, s);
+  return timed("dx_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
 }
 
 size_t vjp_ws(int dtype, int act, int64_t B, int64_t in, int64_t out) {
@@ -189,6 +222,47 @@ extern "C" {
 const char* dl_last_error(void) { return g_last_error.c_str(); }
 
 const char* dl_build_target(void) { return "gfx950"; }
+
+int dl_profile_begin(int capacity) {
+  if (capacity < 0) return fail(DL_INVALID_ARGUMENT, "dl_profile_begin: negative capacity");
+  for (auto& r : g_prof.recs) {
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_prof.recs.clear();
+  g_prof.recs.reserve(capacity);
+  g_prof.capacity = capacity;
+  g_prof.seen = 0;
+  g_prof.on = true;
+  return DL_OK;
+}
+
+int dl_profile_end(int max, float* ms, char* names) {
+  g_prof.on = false;
+  int err = 0;
+  int i = 0;
+  for (auto& r : g_prof.recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+      err = 1;
+    if (i < max) {
+      if (ms) ms[i] = t;
+      if (names) {
+        strncpy(names + (size_t)i * 48, r.name, 47);
+        names[(size_t)i * 48 + 47] = 0;
+      }
+    }
+    ++i;
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_prof.recs.clear();
+  if (err) {
+    fail(DL_HIP_ERROR, "dl_profile_end: event query failed");
+    return -DL_HIP_ERROR;
+  }
+  return g_prof.seen;
+}
 
 int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
                   const void* X, const void* W, const float* b, void* Y, void* Z) {
@@ -258,7 +332,7 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
   const void* G = dY;
   hipError_t e;
   if (act != DL_ACT_IDENTITY) {
-    e = dl::launch_act_mask(dtype, act, B, out, dY, saved, wsp, s);
+    e = timed("act_mask", s, [&] { return dl::launch_act_mask(dtype, act, B, out, dY, saved, wsp, s); });
     if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (mask)");
     G = wsp;
     wsp += align_up((size_t)B * out * es);
@@ -295,7 +369,8 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
       overlap(dlogits, nz, ws, need))
     return fail(DL_ALIASING, "softmax_xent_fwd_bwd: outputs overlap inputs (dlogits may equal logits)");
   float* rl = row_loss ? row_loss : static_cast<float*>(ws);
-  hipError_t e = dl::launch_xent(B, C, logits, labels, rl, dlogits, loss, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("xent", st, [&] { return dl::launch_xent(B, C, logits, labels, rl, dlogits, loss, st); });
   if (e != hipSuccess) return hip_fail(e, "softmax_xent_fwd_bwd");
   return DL_OK;
 }
@@ -323,7 +398,8 @@ int sgd_step(void* stream, int64_t n, float* w, const float* g, double lr) {
   if (n <= 0) return fail(DL_INVALID_ARGUMENT, "sgd_step: n must be positive");
   if (!w || !g) return fail(DL_INVALID_ARGUMENT, "sgd_step: w and g are required");
   if (overlap(w, n * 4, g, n * 4)) return fail(DL_ALIASING, "sgd_step: w overlaps g");
-  hipError_t e = dl::launch_sgd(n, w, g, opt_consts(lr, 0, 0, 0, 0, 0), static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("sgd", st, [&] { return dl::launch_sgd(n, w, g, opt_consts(lr, 0, 0, 0, 0, 0), st); });
   if (e != hipSuccess) return hip_fail(e, "sgd_step");
   return DL_OK;
 }
@@ -338,8 +414,9 @@ int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m, floa
   if (overlap(w, nb, g, nb) || overlap(w, nb, m, nb) || overlap(w, nb, v, nb) ||
       overlap(g, nb, m, nb) || overlap(g, nb, v, nb) || overlap(m, nb, v, nb))
     return fail(DL_ALIASING, "adamw_step: w, g, m, v must be distinct");
-  hipError_t e = dl::launch_adamw(n, w, g, m, v, opt_consts(lr, beta1, beta2, eps, weight_decay, step),
-                                  static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dl::OptConsts oc = opt_consts(lr, beta1, beta2, eps, weight_decay, step);
+  hipError_t e = timed("adamw", st, [&] { return dl::launch_adamw(n, w, g, m, v, oc, st); });
   if (e != hipSuccess) return hip_fail(e, "adamw_step");
   return DL_OK;
 }
@@ -348,7 +425,8 @@ int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
   if (n <= 0) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: n must be positive");
   if (!src || !dst) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: src and dst are required");
   if (overlap(src, n * 4, dst, n * 2)) return fail(DL_ALIASING, "dense_cast_bf16: src overlaps dst");
-  hipError_t e = dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("cast_bf16", st, [&] { return dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), st); });
   if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16");
   return DL_OK;
 }
@@ -448,7 +526,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (forward)");
   }
   // loss + dlogits (in place over the logits)
-  e = dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s);
+  e = timed("xent", s, [&] { return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s); });
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
   // backward
   for (int l = L - 1; l >= 0; --l) {
@@ -489,7 +567,8 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
       segs.part[k] = p.splits > 1 ? ps_[t] : nullptr;
       segs.part_stride[k] = ns_[t];
       segs.g_out[k] = gs_[t];
-      blocks += (ns_[t] + dl::kOptElemsPerBlock - 1) / dl::kOptElemsPerBlock;
+      const int64_t per = p.splits > 1 ? dl::kOptSplitElemsPerBlock : dl::kOptElemsPerBlock;
+      blocks += (ns_[t] + per - 1) / per;
     }
   }
   segs.start_block[segs.count] = blocks;
@@ -497,7 +576,8 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
                                ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
                                             opt->weight_decay, opt->step)
                                : opt_consts(opt->lr, 0, 0, 0, 0, 0);
-  e = dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, oc, s);
+  e = timed(opt->kind == DL_OPT_ADAMW ? "adamw_multi" : "sgd_multi", s,
+            [&] { return dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, oc, s); });
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");
   return DL_OK;
 }

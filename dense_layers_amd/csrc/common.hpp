@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dl {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -23,14 +25,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even; NaN stays NaN (quietened).  bf16 is the upper half
-// of an IEEE float32, so rounding adds half an ulp of the lower half plus the
-// parity of the kept part and truncates.
+// Round-to-nearest-even (the hardware conversion, v_cvt_pk_bf16_f32); NaN
+// stays NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two floats to a packed pair of bf16 (low half = a), one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
 }
 
 template <typename T> struct Elem;
@@ -45,23 +51,27 @@ template <> struct Elem<bf16_t> {
 
 // ---- activations ------------------------------------------------------------
 // GELU (tanh form): 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3).
-// tanh(u) = 1 - 2 / (1 + exp(2u)); exp saturates to 0 or inf for large |u|,
-// which yields exactly -1 or 1, so no range reduction is needed here.
+// With r = 1 / (1 + exp(2u)):  tanh(u) = 1 - 2r, so
+//   gelu(z)  = z (1 - r)
+//   gelu'(z) = 0.5 (1 + t) + 0.5 z (1 - t^2) u'   (t = tanh u, u' = du/dz)
+//            = (1 - r) (1 + 2 z r u'),   u' = sqrt(2/pi) (1 + 3 * 0.044715 z^2).
+// exp(2u) is one hardware exp2 of 2u log2(e); it saturates to 0 or +inf for
+// large |u|, giving r = 1 or 0 and the exact limits, so no range reduction is
+// needed.  The reciprocal is the hardware one (about 1 ulp), well inside the
+// float32 tolerance of the results.
 
 constexpr float kSqrt2OverPi = 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
+constexpr float kTwoLog2e = 2.8853900817779268f;  // 2 / ln 2
 
-__device__ __forceinline__ float tanh_from_exp(float u) {
-  float e = __expf(2.0f * u);
-  return 1.0f - 2.0f / (1.0f + e);
+__device__ __forceinline__ float gelu_r(float z, float z2) {
+  const float x = z * (kTwoLog2e * kSqrt2OverPi) * (1.0f + kGeluCubic * z2);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
 __device__ __forceinline__ float act_apply(int act, float z) {
   if (act == ACT_RELU) return z > 0.0f ? z : 0.0f;
-  if (act == ACT_GELU_TANH) {
-    float t = tanh_from_exp(kSqrt2OverPi * (z + kGeluCubic * z * z * z));
-    return 0.5f * z * (1.0f + t);
-  }
+  if (act == ACT_GELU_TANH) return z - z * gelu_r(z, z * z);
   return z;
 }
 
@@ -70,10 +80,10 @@ __device__ __forceinline__ float act_apply(int act, float z) {
 __device__ __forceinline__ float act_deriv(int act, float z) {
   if (act == ACT_RELU) return z > 0.0f ? 1.0f : 0.0f;
   if (act == ACT_GELU_TANH) {
-    float z2 = z * z;
-    float t = tanh_from_exp(kSqrt2OverPi * (z + kGeluCubic * z2 * z));
-    float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * z2);
-    return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * du;
+    const float z2 = z * z;
+    const float r = gelu_r(z, z2);
+    const float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * z2);
+    return (1.0f - r) * (1.0f + 2.0f * z * r * du);
   }
   return 1.0f;
 }
@@ -125,6 +135,129 @@ struct GemmDesc {
   float* partial; float* db_partial;
 };
 
+// ---- GEMM epilogue through LDS ------------------------------------------------
+// The 32x32 MFMA result leaves each lane one column of 16 rows, so direct
+// stores would be 2- or 4-byte scatters.  Instead the whole BM x BN tile is
+// staged as float32 in LDS, then the workgroup streams it out
+// row-contiguously: 4 outputs per thread (8-byte bf16 or 16-byte float32
+// stores), with the bias, activation, derivative mask and bf16 rounding
+// applied on the way.  `stage` must hold BM * (BN + 4) floats and may alias
+// the K-loop buffers (the caller has passed a barrier after its last LDS
+// read).
+//   out_vec: C (and Z / mask_src) allow aligned 4-wide access (pointer and
+//   leading dimension), checked by the launcher.
+
+template <typename T> struct Store4;
+template <> struct Store4<float> {
+  __device__ static __forceinline__ void vec(float* p, const float v[4]) {
+    f32x4 x = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p) = x;
+  }
+  __device__ static __forceinline__ void load_vec(const float* p, float v[4]) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  }
+};
+template <> struct Store4<bf16_t> {
+  __device__ static __forceinline__ void vec(bf16_t* p, const float v[4]) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    u32x2v x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2v*>(p) = x;
+  }
+  __device__ static __forceinline__ void load_vec(const bf16_t* p, float v[4]) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    const u32x2v x = *reinterpret_cast<const u32x2v*>(p);
+    v[0] = __uint_as_float(x[0] << 16); v[1] = __uint_as_float(x[0] & 0xffff0000u);
+    v[2] = __uint_as_float(x[1] << 16); v[3] = __uint_as_float(x[1] & 0xffff0000u);
+  }
+};
+
+template <int BM, int BN>
+constexpr int stage_floats() { return BM * (BN + 4); }
+
+template <typename TOut, int BM, int BN, int WGM, int WGN, int EPI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ stage,
+                                           const GemmDesc& d, int tm, int tn, int split,
+                                           int out_vec) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int SS = BN + 4;
+  constexpr int CPR = BN / 4;  // 4-wide chunks per tile row
+  static_assert(NT % CPR == 0, "each thread keeps the same columns");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int M = d.M, N = d.N;
+  using TO = typename std::conditional<EPI == EPI_DW, float, TOut>::type;
+  TO* __restrict__ out = static_cast<TO*>(d.C);
+  int64_t ld = d.ldc;
+  if (EPI == EPI_DW && d.splits > 1) {
+    out = reinterpret_cast<TO*>(d.partial + (int64_t)split * M * N);
+    ld = N;
+  }
+  TO* __restrict__ zout = static_cast<TO*>(d.Z);
+  const TO* __restrict__ msrc = static_cast<const TO*>(d.mask_src);
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage[(wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3)) * SS + wn * WN + j * 32 + l32] =
+            acc[i][j][r];
+  __syncthreads();
+
+  // every chunk this thread handles has the same 4 columns
+  const int c4 = (tid % CPR) * 4;
+  const int col = tn * BN + c4;
+  if (col >= N) return;
+  const int nv = min(4, N - col);
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (EPI == EPI_FWD && d.bias != nullptr)
+    for (int e = 0; e < nv; ++e) bias[e] = d.bias[col + e];
+  const bool colfull = out_vec && nv == 4;
+#pragma unroll 4
+  for (int rl = tid / CPR; rl < BM; rl += NT / CPR) {
+    const int row = tm * BM + rl;
+    if (row >= M) break;
+    float v[4];
+    Store4<float>::load_vec(stage + rl * SS + c4, v);
+    const int64_t o = (int64_t)row * ld + col;
+    if (EPI == EPI_FWD) {
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[e] = v[e] + bias[e];
+        v[e] = act_apply(d.act, z[e]);
+      }
+      if (colfull) {
+        Store4<TO>::vec(out + o, v);
+        if (zout != nullptr) Store4<TO>::vec(zout + o, z);
+      } else {
+        for (int e = 0; e < nv; ++e) {
+          Elem<TO>::store(out, o + e, v[e]);
+          if (zout != nullptr) Elem<TO>::store(zout, o + e, z[e]);
+        }
+      }
+    } else if (EPI == EPI_DX) {
+      if (d.mask_act != ACT_IDENTITY) {
+        float ms[4] = {0.f, 0.f, 0.f, 0.f};
+        if (colfull) Store4<TO>::load_vec(msrc + o, ms);
+        else for (int e = 0; e < nv; ++e) ms[e] = Elem<TO>::load(msrc, o + e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[e]);
+      }
+      if (colfull) Store4<TO>::vec(out + o, v);
+      else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+    } else {
+      if (colfull) Store4<TO>::vec(out + o, v);
+      else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+    }
+  }
+}
+
 // Host-side launchers (defined in the kernel files).
 hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s);
@@ -175,6 +308,7 @@ struct OptSegs {
 };
 constexpr int kOptBlock = 256;
 constexpr int kOptElemsPerBlock = kOptBlock * 4 * 4;  // 4 float4 per thread
+constexpr int kOptSplitElemsPerBlock = kOptBlock;      // split-K segments: 4 lanes per 4 elements
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);
 

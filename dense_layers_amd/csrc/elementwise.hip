@@ -9,28 +9,35 @@
 namespace dl {
 namespace {
 
-// dW (contiguous [M, N]) = sum over slices of partial[s][M][N], in slice
-// order; each thread owns 4 consecutive elements when the slice stride keeps
-// 16-byte alignment, one otherwise.  The loads of 8 slices are issued before
-// they are added so the latency of one slice is not paid per slice.
+// dW (contiguous [M, N]) = sum over slices of partial[s][M][N].  Four lanes
+// share a group of 4 consecutive elements: lane q adds slices q, q+4, ... in
+// order and the quad combines its partial sums in the fixed tree
+// (p0 + p1) + (p2 + p3), so each thread walks a quarter of the slices and
+// the result is bit-reproducible.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(int64_t MN, int splits, const float* __restrict__ partial, float* __restrict__ C,
                      int vec) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (vec) {
-    const int64_t i = t * 4;
-    if (i >= MN) return;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + i);
-#pragma unroll 8
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4*>(partial + s * MN + i);
-    *reinterpret_cast<f32x4*>(C + i) = acc;
+  const int q = threadIdx.x & 3;
+  const int64_t e0 = ((int64_t)blockIdx.x * 64 + (threadIdx.x >> 2)) * 4;
+  float g[4] = {0.f, 0.f, 0.f, 0.f};
+  if (vec && e0 + 3 < MN) {
+#pragma unroll 4
+    for (int s = q; s < splits; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(partial + s * MN + e0);
+      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
+    }
   } else {
-    if (t >= MN) return;
-    float acc = partial[t];
-#pragma unroll 8
-    for (int s = 1; s < splits; ++s) acc += partial[s * MN + t];
-    C[t] = acc;
+    for (int s = q; s < splits; s += 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e0 + e < MN) g[e] += partial[s * MN + e0 + e];
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    g[e] += __shfl_xor(g[e], 1);
+    g[e] += __shfl_xor(g[e], 2);
+  }
+  if (e0 + q < MN) C[e0 + q] = g[q];
 }
 
 template <typename T>
@@ -63,11 +70,9 @@ hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 hipStream_t s) {
   if (ldc != N) return hipErrorInvalidValue;
   const int64_t MN = (int64_t)M * N;
-  const int vec = (MN % 4 == 0) && (((reinterpret_cast<uintptr_t>(partial) |
-                                      reinterpret_cast<uintptr_t>(C)) & 15) == 0);
-  const int64_t threads = vec ? (MN + 3) / 4 : MN;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     MN, splits, partial, C, vec);
+  const int vec = (MN % 4 == 0) && ((reinterpret_cast<uintptr_t>(partial) & 15) == 0);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, MN,
+                     splits, partial, C, vec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || db == nullptr) return e;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,

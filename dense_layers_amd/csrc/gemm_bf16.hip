@@ -49,23 +49,45 @@ struct TileLoaderBf16 {
 
   u32x4 r[kRegs];
 
-  __device__ __forceinline__ static u32x4 load_row8(const bf16_t* __restrict__ p, int valid,
-                                                    bool vec) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (vec && valid >= 8) {
-      x = *reinterpret_cast<const u32x4*>(p);
-    } else {
+  // Full K step, 16-byte aligned rows: plain vector loads with no
+  // per-element control flow, so the loads of a K step stay in flight
+  // together.  Rows past the end (edge tiles) are clamped to a valid row:
+  // they only feed output rows / columns that are never stored.  For an
+  // M/N-major operand this needs nrows % 8 == 0 so that no vector straddles
+  // the end (checked by the caller).
+  __device__ __forceinline__ void load_fast(const bf16_t* __restrict__ base, int64_t ld, int row0,
+                                            int nrows, int k0, int tid) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t e = (j < valid) ? static_cast<uint32_t>(p[j]) : 0u;
-        x[j >> 1] |= e << ((j & 1) * 16);
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + i * NT;
+      if (LAY == K_MAJOR) {
+        const int row = min(row0 + q / (BK / 8), nrows - 1);
+        const int k = k0 + (q % (BK / 8)) * 8;
+        r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + k);
+      } else {
+        int m = row0 + (q % (ROWS / 8)) * 8;
+        m = m < nrows ? m : 0;
+        const int kq = q / (ROWS / 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          r[i * 4 + j] = *reinterpret_cast<const u32x4*>(base + (int64_t)(k0 + kq * 4 + j) * ld + m);
       }
+    }
+  }
+
+  // Edge tiles: element loads, zero outside [0, nrows) x [k0, kend).
+  __device__ __forceinline__ static u32x4 load_row8(const bf16_t* __restrict__ p, int valid) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = (j < valid) ? static_cast<uint32_t>(p[j]) : 0u;
+      x[j >> 1] |= e << ((j & 1) * 16);
     }
     return x;
   }
 
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int64_t ld, int row0,
-                                       int nrows, int k0, int kend, bool vec_ok, int tid) {
+  __device__ __forceinline__ void load_safe(const bf16_t* __restrict__ base, int64_t ld, int row0,
+                                            int nrows, int k0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int q = tid + i * NT;
@@ -73,8 +95,7 @@ struct TileLoaderBf16 {
         const int row = row0 + q / (BK / 8);
         const int k = k0 + (q % (BK / 8)) * 8;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < nrows && k < kend)
-          x = load_row8(base + (int64_t)row * ld + k, kend - k, vec_ok);
+        if (row < nrows && k < kend) x = load_row8(base + (int64_t)row * ld + k, kend - k);
         r[i] = x;
       } else {
         const int mg = q % (ROWS / 8);
@@ -84,8 +105,7 @@ struct TileLoaderBf16 {
         for (int j = 0; j < 4; ++j) {
           const int k = k0 + kq * 4 + j;
           u32x4 x = {0u, 0u, 0u, 0u};
-          if (k < kend && m < nrows)
-            x = load_row8(base + (int64_t)k * ld + m, nrows - m, vec_ok);
+          if (k < kend && m < nrows) x = load_row8(base + (int64_t)k * ld + m, nrows - m);
           r[i * 4 + j] = x;
         }
       }
@@ -131,15 +151,21 @@ struct TileLoaderBf16 {
 
 template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
-gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
+gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1, "bad tile");
   using LA = TileLoaderBf16<BM, ALAY, NT>;
   using LB = TileLoaderBf16<BN, BLAY, NT>;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][LA::kLdsSize];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][LB::kLdsSize];
+  constexpr int kSmemAB = (2 * LA::kLdsSize + 2 * LB::kLdsSize) * 2;  // bytes
+  constexpr int kStage = stage_floats<BM, BN>() * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemAB > kStage ? kSmemAB : kStage];
+  // buffer b of A at b * LA::kLdsSize, of B after both A buffers
+  auto As = [&](int b) { return reinterpret_cast<bf16_t*>(smem) + b * LA::kLdsSize; };
+  auto Bs = [&](int b) {
+    return reinterpret_cast<bf16_t*>(smem) + 2 * LA::kLdsSize + b * LB::kLdsSize;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -173,28 +199,24 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
 #pragma unroll
   for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
 
-  if (nk > 0) {
-    la.load(A, d.lda, tm * BM, M, kbeg, kend, a_vec, tid);
-    lb.load(B, d.ldb, tn * BN, N, kbeg, kend, b_vec, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-  }
-  __syncthreads();
+  // When both operands allow 16-byte loads, the full K steps run with
+  // branch-free vector loads (edge rows clamped); a last partial K step, or
+  // operands that do not allow vector loads, go through the bounds-checked
+  // loads.  The two
+  // loops are kept apart so that no join of the two load paths sits inside
+  // the loop where the compiler would have to drain the loads in flight.
+  const bool fast = a_vec && b_vec && (ALAY == K_MAJOR || M % 8 == 0) &&
+                    (BLAY == K_MAJOR || N % 8 == 0);
+  const int nk_full = fast ? (kend - kbeg) / BK : 0;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(A, d.lda, tm * BM, M, k0, kend, a_vec, tid);
-      lb.load(B, d.ldb, tn * BN, N, k0, kend, b_vec, tid);
-    }
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = LA::frag(As[cur], wm * WM + i * 32 + l32, ks, h);
+      for (int i = 0; i < FM; ++i) a[i] = LA::frag(As(cur), wm * WM + i * 32 + l32, ks, h);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = LB::frag(Bs[cur], wn * WN + j * 32 + l32, ks, h);
+      for (int j = 0; j < FN; ++j) b[j] = LB::frag(Bs(cur), wn * WN + j * 32 + l32, ks, h);
       if (do_db) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -210,93 +232,68 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if (nk > 0) {
+    if (nk_full > 0) {
+      la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
+      lb.load_fast(B, d.ldb, tn * BN, N, kbeg, tid);
+    } else {
+      la.load_safe(A, d.lda, tm * BM, M, kbeg, kend, tid);
+      lb.load_safe(B, d.ldb, tn * BN, N, kbeg, kend, tid);
+    }
+    la.store(As(0), tid);
+    lb.store(Bs(0), tid);
+  }
+  __syncthreads();
+
+  int kt = 0;
+  for (; kt + 1 < nk_full; ++kt) {
+    const int cur = kt & 1;
+    const int k0 = kbeg + (kt + 1) * BK;
+    la.load_fast(A, d.lda, tm * BM, M, k0, tid);
+    lb.load_fast(B, d.ldb, tn * BN, N, k0, tid);
+    // keep the next step's loads ahead of this step's MFMAs (the scheduler
+    // would otherwise sink them next to their LDS stores)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    la.store(As(cur ^ 1), tid);
+    lb.store(Bs(cur ^ 1), tid);
+    __syncthreads();
+  }
+  for (; kt < nk; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < nk) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+      const int k0 = kbeg + (kt + 1) * BK;
+      la.load_safe(A, d.lda, tm * BM, M, k0, kend, tid);
+      lb.load_safe(B, d.ldb, tn * BN, N, k0, kend, tid);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      la.store(As(cur ^ 1), tid);
+      lb.store(Bs(cur ^ 1), tid);
     }
     __syncthreads();
   }
 
   // ---- epilogue -------------------------------------------------------------
-  const int row_base = tm * BM + wm * WM;
-  const int col_base = tn * BN + wn * WN;
-
-  if (EPI == EPI_DW) {
-    if (do_db) {
+  if (EPI == EPI_DW && do_db) {
+    const int row_base = tm * BM + wm * WM;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
-        const int row = row_base + i * 32 + l32;
-        if (h == 0 && row < M) {
-          if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
-          else d.db[row] = v;
-        }
+    for (int i = 0; i < FM; ++i) {
+      float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      const int row = row_base + i * 32 + l32;
+      if (h == 0 && row < M) {
+        if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
+        else d.db[row] = v;
       }
     }
-    float* __restrict__ out = static_cast<float*>(d.C);
-    int64_t ld = d.ldc;
-    if (d.splits > 1) {
-      out = d.partial + (int64_t)split * M * N;
-      ld = N;
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = col_base + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (row < M && col < N) out[(int64_t)row * ld + col] = acc[i][j][r];
-        }
-      }
-    return;
   }
-
-  bf16_t* __restrict__ C = static_cast<bf16_t*>(d.C);
-  if (EPI == EPI_FWD) {
-    const float* __restrict__ bias = d.bias;
-    bf16_t* __restrict__ Zp = static_cast<bf16_t*>(d.Z);
-    const int act = d.act;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col_base + j * 32 + l32;
-      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (row < M && col < N) {
-            const float z = acc[i][j][r] + bj;
-            const int64_t o = (int64_t)row * d.ldc + col;
-            C[o] = f32_to_bf16(act_apply(act, z));
-            if (Zp != nullptr) Zp[o] = f32_to_bf16(z);
-          }
-        }
-    }
-    return;
-  }
-
-  // EPI_DX
-  const bf16_t* __restrict__ msrc = static_cast<const bf16_t*>(d.mask_src);
-  const int mact = d.mask_act;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col_base + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (row < M && col < N) {
-          const int64_t o = (int64_t)row * d.ldc + col;
-          float v = acc[i][j][r];
-          if (mact != ACT_IDENTITY) v *= act_deriv(mact, bf16_to_f32(msrc[o]));
-          C[o] = f32_to_bf16(v);
-        }
-      }
-    }
+  store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn, split,
+                                            out_vec);
 }
 
 template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
@@ -310,8 +307,18 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   };
   const int a_vec = aligned(d.A, d.lda);
   const int b_vec = aligned(d.B, d.ldb);
+  // output: float32 (dW) needs 16-byte rows of 4, bf16 needs 8-byte rows of 4
+  auto out_ok = [](const void* p, int64_t ld, int bytes) {
+    return ((reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0) && (ld % 4 == 0);
+  };
+  int out_vec;
+  if (EPI == EPI_DW)
+    out_vec = d.splits > 1 ? out_ok(d.partial, d.N, 16) : out_ok(d.C, d.ldc, 16);
+  else
+    out_vec = out_ok(d.C, d.ldc, 8) && (d.Z == nullptr || out_ok(d.Z, d.ldc, 8)) &&
+              (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 8));
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, ALAY, BLAY, EPI>), dim3((unsigned)nwg),
-                     dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n, a_vec, b_vec);
+                     dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n, a_vec, b_vec, out_vec);
   return hipGetLastError();
 }
 
@@ -328,10 +335,11 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
-// tile 0: 256x128 (4 waves of 128x64); tile 1: 128x128 (4 waves of 64x64)
+// 128x128 (4 waves of 64x64, two workgroups per CU); measured faster than
+// 256x128, 128x256 and 256x256 on the transformer-MLP shapes.
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
-    case 0: return dispatch_layout<256, 128, 2, 2>(d, s);
+    case 0:
     case 1: return dispatch_layout<128, 128, 2, 2>(d, s);
     default: return hipErrorInvalidValue;
   }

@@ -40,42 +40,54 @@ struct TileLoader {
 
   f32x4 r[kPer];
 
-  __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld,
-                                       int row0, int nrows, int k0, int kend,
-                                       bool vec_ok, int tid) {
+  // Full K step, 16-byte aligned rows: plain vector loads with no
+  // per-element control flow, so the loads of a K step stay in flight
+  // together.  Rows past the end (edge tiles) are clamped to a valid row:
+  // they only feed output rows / columns that are never stored.  For an
+  // M/N-major operand this needs nrows % 4 == 0 so that no vector straddles
+  // the end (checked by the caller).
+  __device__ __forceinline__ void load_fast(const float* __restrict__ base, int64_t ld,
+                                            int row0, int nrows, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int v = tid + i * NT;
-      int row, k;
       if (LAY == K_MAJOR) {
-        row = row0 + v / (BK / 4);
-        k = k0 + (v % (BK / 4)) * 4;
+        const int row = min(row0 + v / (BK / 4), nrows - 1);
+        const int k = k0 + (v % (BK / 4)) * 4;
+        r[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)row * ld + k);
       } else {
-        k = k0 + v / (ROWS / 4);
-        row = row0 + (v % (ROWS / 4)) * 4;
+        const int k = k0 + v / (ROWS / 4);
+        int row = row0 + (v % (ROWS / 4)) * 4;
+        row = row < nrows ? row : 0;
+        r[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)k * ld + row);
       }
+    }
+  }
+
+  // Edge tiles: element loads, zero outside [0, nrows) x [k0, kend).
+  __device__ __forceinline__ void load_safe(const float* __restrict__ base, int64_t ld,
+                                            int row0, int nrows, int k0, int kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * NT;
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if (LAY == K_MAJOR) {
+        const int row = row0 + v / (BK / 4);
+        const int k = k0 + (v % (BK / 4)) * 4;
         if (row < nrows) {
           const float* p = base + (int64_t)row * ld + k;
-          if (vec_ok && k + 3 < kend) {
-            x = *reinterpret_cast<const f32x4*>(p);
-          } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (k + j < kend) x[j] = p[j];
-          }
+          for (int j = 0; j < 4; ++j)
+            if (k + j < kend) x[j] = p[j];
         }
       } else {
+        const int k = k0 + v / (ROWS / 4);
+        const int row = row0 + (v % (ROWS / 4)) * 4;
         if (k < kend) {
           const float* p = base + (int64_t)k * ld + row;
-          if (vec_ok && row + 3 < nrows) {
-            x = *reinterpret_cast<const f32x4*>(p);
-          } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (row + j < nrows) x[j] = p[j];
-          }
+          for (int j = 0; j < 4; ++j)
+            if (row + j < nrows) x[j] = p[j];
         }
       }
       r[i] = x;
@@ -111,15 +123,19 @@ struct TileLoader {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
-gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
+gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1 && BK % 8 == 0, "bad tile");
   using LA = TileLoader<BM, BK, ALAY, NT>;
   using LB = TileLoader<BN, BK, BLAY, NT>;
-  __shared__ __attribute__((aligned(16))) float As[2][LA::kLdsSize];
-  __shared__ __attribute__((aligned(16))) float Bs[2][LB::kLdsSize];
+  constexpr int kSmemAB = 2 * LA::kLdsSize + 2 * LB::kLdsSize;
+  constexpr int kStage = stage_floats<BM, BN>();
+  __shared__ __attribute__((aligned(16))) float smem[kSmemAB > kStage ? kSmemAB : kStage];
+  // buffer b of A at smem + b * LA::kLdsSize, of B after both A buffers
+  auto As = [&](int b) { return smem + b * LA::kLdsSize; };
+  auto Bs = [&](int b) { return smem + 2 * LA::kLdsSize + b * LB::kLdsSize; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -153,28 +169,24 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
 #pragma unroll
   for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
 
-  if (nk > 0) {
-    la.load(A, d.lda, tm * BM, M, kbeg, kend, a_vec, tid);
-    lb.load(B, d.ldb, tn * BN, N, kbeg, kend, b_vec, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-  }
-  __syncthreads();
+  // When both operands allow 16-byte loads, the full K steps run with
+  // branch-free vector loads (edge rows clamped); a last partial K step, or
+  // operands that do not allow vector loads, go through the bounds-checked
+  // loads.  The two
+  // loops are kept apart so that no join of the two load paths sits inside
+  // the loop where the compiler would have to drain the loads in flight.
+  const bool fast = a_vec && b_vec && (ALAY == K_MAJOR || M % 4 == 0) &&
+                    (BLAY == K_MAJOR || N % 4 == 0);
+  const int nk_full = fast ? (kend - kbeg) / BK : 0;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(A, d.lda, tm * BM, M, k0, kend, a_vec, tid);
-      lb.load(B, d.ldb, tn * BN, N, k0, kend, b_vec, tid);
-    }
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kg = 0; kg < BK / 8; ++kg) {
       float a[FM][4], b[FN][4];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) la.frag(As[cur], wm * WM + i * 32 + l32, kg, h, a[i]);
+      for (int i = 0; i < FM; ++i) la.frag(As(cur), wm * WM + i * 32 + l32, kg, h, a[i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) lb.frag(Bs[cur], wn * WN + j * 32 + l32, kg, h, b[j]);
+      for (int j = 0; j < FN; ++j) lb.frag(Bs(cur), wn * WN + j * 32 + l32, kg, h, b[j]);
       if (do_db) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) dbacc[i] += (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
@@ -187,93 +199,67 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec) {
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if (nk > 0) {
+    if (nk_full > 0) {
+      la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
+      lb.load_fast(B, d.ldb, tn * BN, N, kbeg, tid);
+    } else {
+      la.load_safe(A, d.lda, tm * BM, M, kbeg, kend, tid);
+      lb.load_safe(B, d.ldb, tn * BN, N, kbeg, kend, tid);
+    }
+    la.store(As(0), tid);
+    lb.store(Bs(0), tid);
+  }
+  __syncthreads();
+
+  int kt = 0;
+  for (; kt + 1 < nk_full; ++kt) {
+    const int cur = kt & 1;
+    const int k0 = kbeg + (kt + 1) * BK;
+    la.load_fast(A, d.lda, tm * BM, M, k0, tid);
+    lb.load_fast(B, d.ldb, tn * BN, N, k0, tid);
+    // keep the next step's loads ahead of this step's MFMAs (the scheduler
+    // would otherwise sink them next to their LDS stores)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    la.store(As(cur ^ 1), tid);
+    lb.store(Bs(cur ^ 1), tid);
+    __syncthreads();
+  }
+  for (; kt < nk; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < nk) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+      const int k0 = kbeg + (kt + 1) * BK;
+      la.load_safe(A, d.lda, tm * BM, M, k0, kend, tid);
+      lb.load_safe(B, d.ldb, tn * BN, N, k0, kend, tid);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      la.store(As(cur ^ 1), tid);
+      lb.store(Bs(cur ^ 1), tid);
     }
     __syncthreads();
   }
 
   // ---- epilogue -------------------------------------------------------------
-  const int row_base = tm * BM + wm * WM;
-  const int col_base = tn * BN + wn * WN;
-  float* __restrict__ C = static_cast<float*>(d.C);
-
-  if (EPI == EPI_DW) {
-    if (do_db) {
+  if (EPI == EPI_DW && do_db) {
+    const int row_base = tm * BM + wm * WM;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
-        const int row = row_base + i * 32 + l32;
-        if (h == 0 && row < M) {
-          if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
-          else d.db[row] = v;
-        }
+    for (int i = 0; i < FM; ++i) {
+      float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      const int row = row_base + i * 32 + l32;
+      if (h == 0 && row < M) {
+        if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
+        else d.db[row] = v;
       }
     }
-    float* __restrict__ out = C;
-    int64_t ld = d.ldc;
-    if (d.splits > 1) {
-      out = d.partial + (int64_t)split * M * N;
-      ld = N;
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = col_base + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (row < M && col < N) out[(int64_t)row * ld + col] = acc[i][j][r];
-        }
-      }
-    return;
   }
-
-  if (EPI == EPI_FWD) {
-    const float* __restrict__ bias = d.bias;
-    float* __restrict__ Zp = static_cast<float*>(d.Z);
-    const int act = d.act;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col_base + j * 32 + l32;
-      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (row < M && col < N) {
-            const float z = acc[i][j][r] + bj;
-            const int64_t o = (int64_t)row * d.ldc + col;
-            C[o] = act_apply(act, z);
-            if (Zp != nullptr) Zp[o] = z;
-          }
-        }
-    }
-    return;
-  }
-
-  // EPI_DX
-  const float* __restrict__ msrc = static_cast<const float*>(d.mask_src);
-  const int mact = d.mask_act;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col_base + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (row < M && col < N) {
-          const int64_t o = (int64_t)row * d.ldc + col;
-          float v = acc[i][j][r];
-          if (mact != ACT_IDENTITY) v *= act_deriv(mact, msrc[o]);
-          C[o] = v;
-        }
-      }
-    }
+  store_tile<float, BM, BN, WGM, WGN, EPI>(acc, smem, d, tm, tn, split, out_vec);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
@@ -287,9 +273,15 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   };
   const int a_vec = aligned(d.A, d.lda);
   const int b_vec = aligned(d.B, d.ldb);
+  int out_vec;
+  if (EPI == EPI_DW && d.splits > 1)
+    out_vec = aligned(d.partial, d.N);
+  else
+    out_vec = aligned(d.C, d.ldc) && (d.Z == nullptr || aligned(d.Z, d.ldc)) &&
+              (d.mask_src == nullptr || aligned(d.mask_src, d.ldc));
   hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>),
                      dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m,
-                     tiles_n, a_vec, b_vec);
+                     tiles_n, a_vec, b_vec, out_vec);
   return hipGetLastError();
 }
 

@@ -103,8 +103,56 @@ opt_single_kernel(int64_t n, float* w, const float* g, float* m, float* v, AdamP
   opt_block<KIND>(n, (int64_t)blockIdx.x * kOptElemsPerBlock, w, gs, m, v, p, vec);
 }
 
+// Split-K segments: the slices are summed by 4 lanes per 4-element group,
+// lane q taking slices q, q+4, q+8, ... in order, then the 4 partial sums are
+// combined in a fixed tree ((p0 + p1) + (p2 + p3)) with lane shuffles, so a
+// thread walks a quarter of the slices and the result is bit-reproducible.
+constexpr int kSplitElemsPerBlock = kOptSplitElemsPerBlock;  // one 4-element group per 4 lanes
+
+template <int KIND>
+__device__ __forceinline__ void opt_split_block(int64_t n, int64_t base, float* __restrict__ w,
+                                                const GradSrc& gs, float* __restrict__ m,
+                                                float* __restrict__ v, const AdamParams& p,
+                                                bool vec) {
+  const int q = threadIdx.x & 3;
+  const int64_t e0 = base + (int64_t)(threadIdx.x >> 2) * 4;
+  float g[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool full = vec && e0 + 3 < n;
+  if (full) {
+#pragma unroll 4
+    for (int k = q; k < gs.splits; k += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gs.part + (int64_t)k * gs.stride + e0);
+      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
+    }
+  } else {
+    for (int k = q; k < gs.splits; k += 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e0 + e < n) g[e] += gs.part[(int64_t)k * gs.stride + e0 + e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    g[e] += __shfl_xor(g[e], 1);
+    g[e] += __shfl_xor(g[e], 2);
+  }
+  // every lane of the quad now holds the same sum; lane q updates element q
+  const int64_t i = e0 + q;
+  if (i >= n) return;
+  const float gi = g[q];
+  gs.out[i] = gi;
+  if (KIND == 0) {
+    w[i] -= p.lr * gi;
+  } else {
+    float we = w[i], me = m[i], ve = v[i];
+    adam_elem(we, gi, me, ve, p);
+    w[i] = we; m[i] = me; v[i] = ve;
+  }
+}
+
 // One launch over several arrays: block b belongs to the segment whose
-// prefix range [start_block[s], start_block[s+1]) contains it.
+// prefix range [start_block[s], start_block[s+1]) contains it.  Segments with
+// split-K slices use kSplitElemsPerBlock elements per block, others
+// kOptElemsPerBlock.
 template <int KIND>
 __global__ void __launch_bounds__(kOptBlock)
 opt_multi_kernel(OptSegs segs, AdamParams p) {
@@ -113,13 +161,15 @@ opt_multi_kernel(OptSegs segs, AdamParams p) {
   while (s + 1 < segs.count && b >= segs.start_block[s + 1]) ++s;
   const int64_t local = b - segs.start_block[s];
   const GradSrc gs{segs.g[s], segs.part[s], segs.part_stride[s], segs.splits[s], segs.g_out[s]};
-  uintptr_t addr = reinterpret_cast<uintptr_t>(segs.w[s]);
+  if (gs.splits > 1) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(gs.part) |
+                       static_cast<uintptr_t>(gs.stride * 4)) & 15) == 0;
+    opt_split_block<KIND>(segs.n[s], local * kSplitElemsPerBlock, segs.w[s], gs, segs.m[s],
+                          segs.v[s], p, vec);
+    return;
+  }
+  uintptr_t addr = reinterpret_cast<uintptr_t>(segs.w[s]) | reinterpret_cast<uintptr_t>(gs.g);
   if (KIND) addr |= reinterpret_cast<uintptr_t>(segs.m[s]) | reinterpret_cast<uintptr_t>(segs.v[s]);
-  if (gs.splits > 1)
-    addr |= reinterpret_cast<uintptr_t>(gs.part) | reinterpret_cast<uintptr_t>(gs.out) |
-            static_cast<uintptr_t>(gs.stride * 4);
-  else
-    addr |= reinterpret_cast<uintptr_t>(gs.g);
   opt_block<KIND>(segs.n[s], local * kOptElemsPerBlock, segs.w[s], gs, segs.m[s], segs.v[s], p,
                   (addr & 15) == 0);
 }

@@ -75,6 +75,23 @@ const char* dl_last_error(void);
 /* Offload target the library was built for ("gfx950"). */
 const char* dl_build_target(void);
 
+/*
+ * Per-launch timing for measurement (the per-kernel GPU timestamps of the
+ * MuNet page, "Configuration": profile=True).  Between dl_profile_begin and
+ * dl_profile_end, every kernel launch this library makes from the calling
+ * thread is bracketed by a pair of HIP events recorded on the launch's own
+ * stream.  At most `capacity` launches are recorded (later ones are counted
+ * but not timed).  dl_profile_end waits for the recorded events, writes up to
+ * `max` durations in milliseconds to ms[] and the launch names (each
+ * NUL-terminated, at most 47 characters) to names[i * 48], releases the
+ * events, and returns the number of launches seen; a negative value is a
+ * HIP error.  Timing adds event records between launches, so it is meant for
+ * a short measured pass, not the throughput run.  ms and names are host
+ * arrays and may be NULL when max is 0.
+ */
+int dl_profile_begin(int capacity);
+int dl_profile_end(int max, float* ms, char* names);
+
 /* ---- dense layer forward ------------------------------------------------- */
 
 /*

@@ -81,7 +81,8 @@ def test_dense_fwd_on_side_stream(dl):
 # ------------------------------------------------------------------ vjp
 
 VJP_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (8192, 784, 256),
-              (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000)]
+              (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000), (700, 1000, 300),
+              (2000, 1000, 1000)]
 
 
 @pytest.mark.parametrize("shape", VJP_SHAPES)
@@ -143,7 +144,8 @@ def test_dense_vjp_is_bit_reproducible(dl):
 
 # ------------------------------------------------------------------ bf16
 
-BF16_SHAPES = [(1, 8, 8), (77, 130, 90), (300, 1024, 512), (1024, 1024, 4096), (513, 4096, 1024)]
+BF16_SHAPES = [(1, 8, 8), (77, 130, 90), (300, 1024, 512), (1024, 1024, 4096), (513, 4096, 1024),
+               (300, 1000, 1000), (1000, 200, 1000)]
 
 
 @pytest.mark.parametrize("shape", BF16_SHAPES)
@@ -514,3 +516,20 @@ def test_mlp_step_bit_reproducible(dl):
         outs.append([a.clone() for a in mlp.W + mlp.b + mlp.mW + mlp.vW])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_profile_hook_times_each_launch(dl):
+    X, W, b = _layer(200, 512, 256, 128)
+    Xd, Wd, bd = to_dev(X), to_dev(W), to_dev(b)
+    dl.profile_begin(16)
+    dl.dense_act_fwd(Xd, Wd, bd, O.ACT_RELU)
+    dY = to_dev(si.random_matrix(201, (512, 128)))
+    dl.dense_act_vjp(dY, None, Xd, Wd, O.ACT_IDENTITY)
+    recs = dl.profile_end(16)
+    names = [n for n, _ in recs]
+    assert names[0] == "fwd_gemm" and "dw_gemm" in names and names[-1] == "dx_gemm"
+    assert all(ms > 0 for _, ms in recs)
+    # outside a profiling window nothing is recorded
+    dl.dense_act_fwd(Xd, Wd, bd, O.ACT_RELU)
+    dl.profile_begin(0)
+    assert dl.profile_end(0) == []
