@@ -234,6 +234,12 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
     }
   };
 
+  // Loads run two K steps ahead: register set 1 (la, lb) and set 2 (la2,
+  // lb2) alternate, so each load has two steps of MFMA work to land in.
+  // Invariant at the top of a trip: LDS buffer (kt & 1) holds step kt and
+  // set 2 holds step kt + 1 in flight.
+  LA la2;
+  LB lb2;
   if (nk > 0) {
     if (nk_full > 0) {
       la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
@@ -244,17 +250,48 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
     }
     la.store(As(0), tid);
     lb.store(Bs(0), tid);
+    if (nk_full >= 2) {
+      la2.load_fast(A, d.lda, tm * BM, M, kbeg + BK, tid);
+      lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + BK, tid);
+    }
   }
   __syncthreads();
 
   int kt = 0;
+  for (; kt + 3 < nk_full; kt += 2) {
+    la.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 2) * BK, tid);
+    lb.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 2) * BK, tid);
+    // keep the loads ahead of the MFMAs (the scheduler would otherwise sink
+    // them next to their LDS stores)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    la2.store(As(1), tid);
+    lb2.store(Bs(1), tid);
+    __syncthreads();
+    la2.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 3) * BK, tid);
+    lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 3) * BK, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
+    la.store(As(0), tid);
+    lb.store(Bs(0), tid);
+    __syncthreads();
+  }
+  if (kt + 1 < nk_full) {  // drain set 2
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    la2.store(As((kt + 1) & 1), tid);
+    lb2.store(Bs((kt + 1) & 1), tid);
+    __syncthreads();
+    ++kt;
+  }
   for (; kt + 1 < nk_full; ++kt) {
     const int cur = kt & 1;
     const int k0 = kbeg + (kt + 1) * BK;
     la.load_fast(A, d.lda, tm * BM, M, k0, tid);
     lb.load_fast(B, d.ldb, tn * BN, N, k0, tid);
-    // keep the next step's loads ahead of this step's MFMAs (the scheduler
-    // would otherwise sink them next to their LDS stores)
     __builtin_amdgcn_sched_barrier(0);
     compute(cur);
     __builtin_amdgcn_sched_barrier(0);
