@@ -97,6 +97,7 @@ class TmlpBench:
         self.W = [torch.from_numpy(a).to(dev) for a in inp.W]
         self.b = [torch.from_numpy(a).to(dev) for a in inp.b]
         self.Wb = [torch.empty(a.shape, dtype=bf, device=dev) for a in self.W]
+        self.Wbt = [torch.empty((a.shape[1], a.shape[0]), dtype=bf, device=dev) for a in self.W]
         self.H = torch.empty(T, f, dtype=bf, device=dev)
         self.Z = torch.empty(T, f, dtype=bf, device=dev)
         self.Y = torch.empty(T, d, dtype=bf, device=dev)
@@ -109,16 +110,16 @@ class TmlpBench:
 
     def step(self):
         dl = self.dl
-        for l in range(2):
-            dl.dense_cast_bf16(self.W[l], self.Wb[l])
+        for l in range(2):  # bf16 working copies of the fp32 masters, and transposes
+            dl.dense_cast_bf16_t(self.W[l], self.Wb[l], self.Wbt[l])
         dl.dense_act_fwd(self.X, self.Wb[0], self.b[0], dl.ACT_GELU_TANH, Y=self.H, Z=self.Z)
         dl.dense_act_fwd(self.H, self.Wb[1], self.b[1], dl.ACT_IDENTITY, Y=self.Y)
         # vjp of layer 2 writes dZ1 = (dY W2) * gelu'(Z1) over Z1 in place
         dl.dense_act_vjp(self.dY, None, self.H, self.Wb[1], dl.ACT_IDENTITY, dX=self.Z,
                          dW=self.dW[1], db=self.db[1], dx_act=dl.ACT_GELU_TANH,
-                         dx_saved=self.Z, ws=self.ws)
+                         dx_saved=self.Z, ws=self.ws, Wt=self.Wbt[1])
         dl.dense_act_vjp(self.Z, None, self.X, self.Wb[0], dl.ACT_IDENTITY, dX=self.dX,
-                         dW=self.dW[0], db=self.db[0], ws=self.ws)
+                         dW=self.dW[0], db=self.db[0], ws=self.ws, Wt=self.Wbt[0])
 
     def flops(self):
         return 6 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
@@ -128,8 +129,8 @@ class TmlpBench:
         name, _ = _split(label)
         if name in ("fwd_gemm", "dw_gemm", "dx_gemm"):
             return "flop", 2 * T * d * f
-        if name == "cast_bf16":
-            return "byte", 6 * d * f
+        if name == "cast_bf16_t":
+            return "byte", 8 * d * f
         return None
 
 

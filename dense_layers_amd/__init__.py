@@ -72,7 +72,7 @@ _c = {
     "dense_act_fwd": _sig("dense_act_fwd", _i32,
                           [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "dense_act_vjp": _sig("dense_act_vjp", _i32,
-                          [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                          [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _i32, _vp, _vp, _sz]),
     "dense_act_vjp_workspace_size": _sig("dense_act_vjp_workspace_size", _sz,
                                          [_i32, _i32, _i64, _i64, _i64]),
@@ -83,6 +83,7 @@ _c = {
     "adamw_step": _sig("adamw_step", _i32,
                        [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
     "dense_cast_bf16": _sig("dense_cast_bf16", _i32, [_vp, _i64, _vp, _vp]),
+    "dense_cast_bf16_t": _sig("dense_cast_bf16_t", _i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "mlp_train_step": _sig("mlp_train_step", _i32,
                            [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,
                             ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
@@ -95,7 +96,8 @@ _c = {
 EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
-           "dense_cast_bf16", "mlp_train_step", "mlp_train_step_workspace_size",
+           "dense_cast_bf16", "dense_cast_bf16_t", "mlp_train_step",
+           "mlp_train_step_workspace_size",
            "dl_profile_begin", "dl_profile_end"]
 
 
@@ -200,10 +202,11 @@ def dense_act_vjp(dY: torch.Tensor, saved: Optional[torch.Tensor], X: Optional[t
                   need_dw: bool = True, dX: Optional[torch.Tensor] = None,
                   dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
                   dx_act=ACT_IDENTITY, dx_saved: Optional[torch.Tensor] = None,
-                  ws: Optional[torch.Tensor] = None):
+                  ws: Optional[torch.Tensor] = None, Wt: Optional[torch.Tensor] = None):
     """G = dY * act'(saved); returns (dX or None, dW or None, db or None).
 
-    With dx_act != identity the returned dX is dX * dx_act'(dx_saved)."""
+    With dx_act != identity the returned dX is dX * dx_act'(dx_saved).  Wt,
+    when given, is W transposed ([in, out]); dX then reads it instead of W."""
     _dev(dY, "dY")
     dt = dY.dtype
     B, n_out = dY.shape
@@ -228,12 +231,14 @@ def dense_act_vjp(dY: torch.Tensor, saved: Optional[torch.Tensor], X: Optional[t
         _dev(db, "db", torch.float32, (n_out,))
     if dx_saved is not None:
         _dev(dx_saved, "dx_saved", dt, (B, n_in))
+    if Wt is not None:
+        _dev(Wt, "Wt", dt, (n_in, n_out))
     code = _dtype_code(dY)
     need = dense_act_vjp_workspace_size(code, act, B, n_in, n_out)
     if ws is None or ws.numel() < need:
         ws = _workspace(need, dY.device)
     _check(_c["dense_act_vjp"](_stream(dY), code, _act(act), B, n_in, n_out, _ptr(dY),
-                               _ptr(saved), _ptr(X), _ptr(W), _ptr(dX), _ptr(dW), _ptr(db),
+                               _ptr(saved), _ptr(X), _ptr(W), _ptr(Wt), _ptr(dX), _ptr(dW), _ptr(db),
                                _act(dx_act), _ptr(dx_saved), _ptr(ws),
                                0 if ws is None else ws.numel()))
     return dX, dW, db
@@ -288,6 +293,24 @@ def adamw_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
     _check(_c["adamw_step"](_stream(w), w.numel(), _ptr(w), _ptr(g), _ptr(m), _ptr(v), lr,
                             beta1, beta2, eps, weight_decay, step))
     return w
+
+
+def dense_cast_bf16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
+                      dst_t: Optional[torch.Tensor] = None, copy: bool = True,
+                      transposed: bool = True):
+    """bf16 copy of a [rows, cols] matrix and/or its transpose; returns (dst, dst_t)."""
+    _dev(src, "src", torch.float32)
+    rows, cols = src.shape
+    if copy and dst is None:
+        dst = torch.empty((rows, cols), dtype=torch.bfloat16, device=src.device)
+    if transposed and dst_t is None:
+        dst_t = torch.empty((cols, rows), dtype=torch.bfloat16, device=src.device)
+    if dst is not None:
+        _dev(dst, "dst", torch.bfloat16, (rows, cols))
+    if dst_t is not None:
+        _dev(dst_t, "dst_t", torch.bfloat16, (cols, rows))
+    _check(_c["dense_cast_bf16_t"](_stream(src), rows, cols, _ptr(src), _ptr(dst), _ptr(dst_t)))
+    return dst, dst_t
 
 
 def dense_cast_bf16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):

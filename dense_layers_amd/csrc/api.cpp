@@ -191,13 +191,18 @@ hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
   });
 }
 
-// dX = G W, optionally times mask_act'(mask_src).
+// dX = G W, optionally times mask_act'(mask_src).  With Wt (W transposed,
+// [in, out]) the B operand is read along K.
 hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* W,
-                   void* dX, int mask_act, const void* mask_src, hipStream_t s) {
+                   const void* Wt, void* dX, int mask_act, const void* mask_src, hipStream_t s) {
   dl::GemmDesc d = blank_desc();
   d.M = (int)B; d.N = (int)in; d.K = (int)out;
   d.A = G; d.lda = out; d.a_layout = dl::K_MAJOR;
-  d.B = W; d.ldb = in; d.b_layout = dl::MN_MAJOR;
+  if (Wt != nullptr) {
+    d.B = Wt; d.ldb = out; d.b_layout = dl::K_MAJOR;
+  } else {
+    d.B = W; d.ldb = in; d.b_layout = dl::MN_MAJOR;
+  }
   d.C = dX; d.ldc = in;
   d.epi = dl::EPI_DX;
   d.mask_act = mask_act; d.mask_src = mask_src;
@@ -291,9 +296,9 @@ size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in, i
 }
 
 int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
-                  const void* dY, const void* saved, const void* X, const void* W, void* dX,
-                  float* dW, float* db, int dx_act, const void* dx_saved, void* ws,
-                  size_t ws_bytes) {
+                  const void* dY, const void* saved, const void* X, const void* W,
+                  const void* Wt, void* dX, float* dW, float* db, int dx_act,
+                  const void* dx_saved, void* ws, size_t ws_bytes) {
   if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad dtype %d", dtype);
   if (!act_ok(act) || !act_ok(dx_act)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad activation");
   if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
@@ -302,7 +307,7 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
   if (act != DL_ACT_IDENTITY && !saved)
     return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: saved Z/Y is required for a non-identity activation");
   if ((dW || db) && !X) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: X is required for dW/db");
-  if (dX && !W) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: W is required for dX");
+  if (dX && !W && !Wt) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: W or Wt is required for dX");
   if (db && !dW) return fail(DL_UNSUPPORTED, "dense_act_vjp: db is reduced inside the dW kernel; pass dW too");
   if (dx_act != DL_ACT_IDENTITY && (!dX || !dx_saved))
     return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: dx_act needs dX and dx_saved");
@@ -315,7 +320,8 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
   const size_t nY = (size_t)B * out * es, nX = (size_t)B * in * es, nW = (size_t)out * in * es;
   const size_t ndW = (size_t)out * in * 4, ndb = (size_t)out * 4;
   // dX may be X itself and/or dx_saved itself (dW and db are finished first).
-  if (dX && (overlap(dX, nX, dY, nY) || overlap(dX, nX, W, nW) || overlap(dX, nX, saved, nY) ||
+  if (dX && (overlap(dX, nX, dY, nY) || overlap(dX, nX, W, nW) || overlap(dX, nX, Wt, nW) ||
+             overlap(dX, nX, saved, nY) ||
              overlap(dX, nX, ws, need) || overlap(dX, nX, dW, ndW) || overlap(dX, nX, db, ndb) ||
              (dX != X && overlap(dX, nX, X, nX)) ||
              (dX != dx_saved && overlap(dX, nX, dx_saved, nX))))
@@ -342,7 +348,7 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
     if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dW)");
   }
   if (dX) {
-    e = dx_gemm(dtype, B, in, out, G, W, dX, dx_act, dx_saved, s);
+    e = dx_gemm(dtype, B, in, out, G, W, Wt, dX, dx_act, dx_saved, s);
     if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dX)");
   }
   return DL_OK;
@@ -428,6 +434,22 @@ int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = timed("cast_bf16", st, [&] { return dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), st); });
   if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16");
+  return DL_OK;
+}
+
+int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src, void* dst,
+                      void* dst_t) {
+  if (!dim_ok(rows) || !dim_ok(cols)) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16_t: sizes must be in [1, 2^31)");
+  if (!src || (!dst && !dst_t)) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16_t: src and an output are required");
+  const size_t n = (size_t)rows * cols;
+  if (overlap(src, n * 4, dst, n * 2) || overlap(src, n * 4, dst_t, n * 2) || overlap(dst, n * 2, dst_t, n * 2))
+    return fail(DL_ALIASING, "dense_cast_bf16_t: buffers overlap");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("cast_bf16_t", st, [&] {
+    return dl::launch_cast_bf16_t(rows, cols, src, static_cast<dl::bf16_t*>(dst),
+                                  static_cast<dl::bf16_t*>(dst_t), st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16_t");
   return DL_OK;
 }
 
@@ -536,7 +558,8 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
                 /*reduce=*/false);
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
     if (l > 0) {
-      e = dx_gemm(DL_F32, B, ly.in, ly.out, Y[l], ly.W, Y[l - 1], layers[l - 1].act, Y[l - 1], s);
+      e = dx_gemm(DL_F32, B, ly.in, ly.out, Y[l], ly.W, nullptr, Y[l - 1], layers[l - 1].act,
+                  Y[l - 1], s);
       if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dX)");
     }
   }

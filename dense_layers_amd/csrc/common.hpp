@@ -172,6 +172,28 @@ template <> struct Store4<bf16_t> {
   }
 };
 
+// Four consecutive elements kept in their storage format (one 16-byte or
+// 8-byte register group) until they are used.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void load_vec(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+template <> struct Raw4<bf16_t> {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v v = {0u, 0u};
+  __device__ __forceinline__ void load_vec(const bf16_t* p) { v = *reinterpret_cast<const u32x2v*>(p); }
+  __device__ __forceinline__ void set(int e, float x) {
+    const uint32_t h = f32_to_bf16(x);
+    v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0xffffu) | (h << 16)) : ((v[e >> 1] & 0xffff0000u) | h);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    return (e & 1) ? __uint_as_float(v[e >> 1] & 0xffff0000u) : __uint_as_float(v[e >> 1] << 16);
+  }
+};
+
 template <int BM, int BN>
 constexpr int stage_floats() { return BM * (BN + 4); }
 
@@ -199,6 +221,29 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
   TO* __restrict__ zout = static_cast<TO*>(d.Z);
   const TO* __restrict__ msrc = static_cast<const TO*>(d.mask_src);
 
+  // every chunk this thread handles has the same 4 columns, rows
+  // tid / CPR + it * (NT / CPR)
+  constexpr int RPT = BM / (NT / CPR);
+  const int c4 = (tid % CPR) * 4;
+  const int col = tn * BN + c4;
+  const int nv = col < N ? min(4, N - col) : 0;
+  const bool colfull = out_vec && nv == 4;
+
+  // The dX epilogue's saved activations are fetched (in their storage format)
+  // before the staging barrier so their latency overlaps it.
+  Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
+  if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY) {
+#pragma unroll
+    for (int it = 0; it < RPT; ++it) {
+      const int row = tm * BM + tid / CPR + it * (NT / CPR);
+      const int64_t o = (int64_t)row * ld + col;
+      if (row < M && nv > 0) {
+        if (colfull) ms[it].load_vec(msrc + o);
+        else for (int e = 0; e < nv; ++e) ms[it].set(e, Elem<TO>::load(msrc, o + e));
+      }
+    }
+  }
+
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -209,19 +254,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
             acc[i][j][r];
   __syncthreads();
 
-  // every chunk this thread handles has the same 4 columns
-  const int c4 = (tid % CPR) * 4;
-  const int col = tn * BN + c4;
-  if (col >= N) return;
-  const int nv = min(4, N - col);
+  if (nv == 0) return;
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (EPI == EPI_FWD && d.bias != nullptr)
     for (int e = 0; e < nv; ++e) bias[e] = d.bias[col + e];
-  const bool colfull = out_vec && nv == 4;
-#pragma unroll 4
-  for (int rl = tid / CPR; rl < BM; rl += NT / CPR) {
+#pragma unroll
+  for (int it = 0; it < RPT; ++it) {
+    const int rl = tid / CPR + it * (NT / CPR);
     const int row = tm * BM + rl;
-    if (row >= M) break;
+    if (row >= M) continue;
     float v[4];
     Store4<float>::load_vec(stage + rl * SS + c4, v);
     const int64_t o = (int64_t)row * ld + col;
@@ -243,11 +284,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
       }
     } else if (EPI == EPI_DX) {
       if (d.mask_act != ACT_IDENTITY) {
-        float ms[4] = {0.f, 0.f, 0.f, 0.f};
-        if (colfull) Store4<TO>::load_vec(msrc + o, ms);
-        else for (int e = 0; e < nv; ++e) ms[e] = Elem<TO>::load(msrc, o + e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[e]);
+        for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[it].get(e));
       }
       if (colfull) Store4<TO>::vec(out + o, v);
       else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
@@ -269,6 +307,8 @@ hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols,
                            hipStream_t s);
 hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst,
                             hipStream_t s);
+hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16_t* dst,
+                              bf16_t* dst_t, hipStream_t s);
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s);

@@ -56,6 +56,35 @@ cast_bf16_kernel(int64_t n, const float* __restrict__ src, bf16_t* __restrict__ 
     dst[i] = f32_to_bf16(src[i]);
 }
 
+// src [rows, cols] float32 -> dst = bf16(src) (same layout) and/or
+// dst_t = bf16(src)^T [cols, rows], through a 64 x 64 LDS tile so both the
+// reads and the transposed writes are row-contiguous.
+constexpr int kTT = 64;
+__global__ void __launch_bounds__(256)
+cast_bf16_t_kernel(int64_t rows, int64_t cols, const float* __restrict__ src,
+                   bf16_t* __restrict__ dst, bf16_t* __restrict__ dst_t) {
+  __shared__ bf16_t tile[kTT][kTT + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * kTT, c0 = (int64_t)blockIdx.x * kTT;
+  const int tx = threadIdx.x % kTT, ty = threadIdx.x / kTT;  // 64 x 4
+#pragma unroll
+  for (int k = 0; k < kTT; k += 4) {
+    const int64_t r = r0 + ty + k, c = c0 + tx;
+    bf16_t v = 0;
+    if (r < rows && c < cols) {
+      v = f32_to_bf16(src[r * cols + c]);
+      if (dst != nullptr) dst[r * cols + c] = v;
+    }
+    tile[ty + k][tx] = v;
+  }
+  if (dst_t == nullptr) return;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kTT; k += 4) {
+    const int64_t c = c0 + ty + k, r = r0 + tx;  // output row c, column r
+    if (c < cols && r < rows) dst_t[c * rows + r] = tile[tx][ty + k];
+  }
+}
+
 unsigned grid_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -91,6 +120,13 @@ hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols, const
     hipLaunchKernelGGL(act_mask_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
                        static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(saved),
                        static_cast<bf16_t*>(G));
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16_t* dst,
+                              bf16_t* dst_t, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
+  hipLaunchKernelGGL(cast_bf16_t_kernel, grid, dim3(256), 0, s, rows, cols, src, dst, dst_t);
   return hipGetLastError();
 }
 

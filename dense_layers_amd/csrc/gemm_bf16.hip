@@ -123,16 +123,15 @@ struct TileLoaderBf16 {
       } else {
         const int mg = q % (ROWS / 8);
         const int kq = q / (ROWS / 8);
-        // rows j = 0..3 of the block hold k = 4kq + j; element c of a row is m = 8mg + c
+        // rows j = 0..3 of the block hold k = 4kq + j; element c of a row is
+        // m = 8mg + c.  Column c gathers element c of the 4 rows: one byte
+        // permute per pair of rows (low or high halves of word c / 2).
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int w = c >> 1;
-          const int sh = (c & 1) * 16;
-          const uint32_t e0 = (r[i * 4 + 0][w] >> sh) & 0xffffu;
-          const uint32_t e1 = (r[i * 4 + 1][w] >> sh) & 0xffffu;
-          const uint32_t e2 = (r[i * 4 + 2][w] >> sh) & 0xffffu;
-          const uint32_t e3 = (r[i * 4 + 3][w] >> sh) & 0xffffu;
-          u32x2 col = {e0 | (e1 << 16), e2 | (e3 << 16)};
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          u32x2 col = {__builtin_amdgcn_perm(r[i * 4 + 1][w], r[i * 4 + 0][w], sel),
+                       __builtin_amdgcn_perm(r[i * 4 + 3][w], r[i * 4 + 2][w], sel)};
           const int row = mg * 8 + c;
           const int unit = kq >> 1;
           *reinterpret_cast<u32x2*>(lds + row * kRowElems + swz(row, unit) * 8 + (kq & 1) * 4) = col;
@@ -365,6 +364,8 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
     return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
     return launch_tile<BM, BN, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+  if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX>(d, s);
   if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
     return launch_tile<BM, BN, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
   return hipErrorInvalidValue;

@@ -130,6 +130,9 @@ int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in,
  *           (may be NULL) for identity.
  *   X       device [B, in] (dtype), the forward input
  *   W       device [out, in] (dtype)
+ *   Wt      device [in, out] (dtype), the transpose of W, or NULL.  Only
+ *           read for dX; with it the dX product reads both operands along
+ *           the contraction index (see dense_cast_bf16_t).
  *   dX      device [B, in] (dtype) output, or NULL to skip (first layer)
  *   dW      device float32 [out, in] output, or NULL to skip
  *   db      device float32 [out] output, or NULL to skip
@@ -145,9 +148,9 @@ int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in,
  */
 int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in,
                   int64_t out, const void* dY, const void* saved,
-                  const void* X, const void* W, void* dX, float* dW,
-                  float* db, int dx_act, const void* dx_saved, void* ws,
-                  size_t ws_bytes);
+                  const void* X, const void* W, const void* Wt, void* dX,
+                  float* dW, float* db, int dx_act, const void* dx_saved,
+                  void* ws, size_t ws_bytes);
 
 size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in,
                                     int64_t out);
@@ -214,6 +217,17 @@ int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m,
  *   n > 0; src device float32 [n]; dst device bf16 [n]; no overlap.
  */
 int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst);
+
+/*
+ * dense_cast_bf16_t -- the same rounding for a [rows, cols] float32 matrix
+ * (a weight W [out, in]), writing the bf16 copy dst [rows, cols] and/or its
+ * transpose dst_t [cols, rows] in one pass.  The transposed copy lets the bf16
+ * vjp read W along its contraction index (the `Wt` argument of
+ * dense_act_vjp).  rows, cols > 0; src device float32; dst, dst_t device bf16
+ * or NULL (not both); no overlaps.
+ */
+int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src,
+                      void* dst, void* dst_t);
 
 /* ---- one MLP training step ------------------------------------------------ */
 

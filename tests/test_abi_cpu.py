@@ -85,15 +85,15 @@ def test_rejects_bad_arguments_without_launching(dl):
     # Y overlapping X
     assert c["dense_act_fwd"](None, 0, 0, 4, 4, 4, fake, fake + 8192, None, fake + 16, None) == 3
     # vjp: GELU without the saved pre-activation
-    assert c["dense_act_vjp"](None, 0, 2, 4, 4, 4, fake, None, fake, fake, None, None, None, 0,
-                              None, None, 0) == 1
+    assert c["dense_act_vjp"](None, 0, 2, 4, 4, 4, fake, None, fake, fake, None, None, None, None,
+                              0, None, None, 0) == 1
     # vjp: db without dW
-    assert c["dense_act_vjp"](None, 0, 0, 4, 4, 4, fake, None, fake, fake, None, None,
+    assert c["dense_act_vjp"](None, 0, 0, 4, 4, 4, fake, None, fake, fake, None, None, None,
                               fake + 8192, 0, None, None, 0) == 2
     # vjp: workspace too small (split-K partials needed)
     assert c["dense_act_vjp"](None, 0, 0, 8192, 784, 256, fake, None, fake + (1 << 30),
-                              fake + (1 << 31), None, fake + (1 << 32), None, 0, None, None,
-                              0) == 4
+                              fake + (1 << 31), None, None, fake + (1 << 32), None, 0, None,
+                              None, 0) == 4
     # xent: missing labels, workspace too small, partial overlap of dlogits
     assert c["softmax_xent_fwd_bwd"](None, 4, 10, fake, None, fake, None, fake, fake, 1024) == 1
     assert c["softmax_xent_fwd_bwd"](None, 4, 10, fake, fake + 4096, fake + 8192, None,
@@ -110,6 +110,8 @@ def test_rejects_bad_arguments_without_launching(dl):
     assert c["adamw_step"](None, 16, fake, fake + 64, fake + 128, fake + 192, 1e-3, 1.5, 0.999,
                            1e-8, 0.0, 1) == 1
     assert c["dense_cast_bf16"](None, 16, fake, fake + 8) == 3
+    assert c["dense_cast_bf16_t"](None, 4, 4, fake, None, None) == 1
+    assert c["dense_cast_bf16_t"](None, 4, 4, fake, fake + 32, None) == 3
 
 
 def test_mlp_step_rejects_bad_layers(dl):

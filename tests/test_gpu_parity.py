@@ -533,3 +533,36 @@ def test_profile_hook_times_each_launch(dl):
     dl.dense_act_fwd(Xd, Wd, bd, O.ACT_RELU)
     dl.profile_begin(0)
     assert dl.profile_end(0) == []
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (63, 130), (1024, 4096), (4096, 1000)])
+def test_cast_bf16_transposed_bit_exact(dl, shape):
+    W = si.random_matrix(210, shape, scale=0.02)
+    d, dt = dl.dense_cast_bf16_t(to_dev(W))
+    ref = (O.round_bf16(W).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = d.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_t = dt.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref) and np.array_equal(got_t, ref.T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(300, 1000, 1000), (513, 1024, 4096), (77, 130, 90)])
+def test_dense_vjp_with_transposed_weight(dl, dtype, shape):
+    """dX through the transposed weight (read along the contraction index)
+    equals dX through W, and both match the oracle."""
+    B, n_in, n_out = shape
+    bf = dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    X = si.random_matrix(220, (B, n_in), bf16_exact=bf)
+    W = si.random_matrix(221, (n_out, n_in), scale=0.02, bf16_exact=bf)
+    dY = si.random_matrix(222, (B, n_out), bf16_exact=bf)
+    Wd = to_dev(W, tdt)
+    Wt = Wd.t().contiguous()
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY, tdt), None, to_dev(X, tdt), Wd, O.ACT_IDENTITY,
+                                  Wt=Wt)
+    dX2, _, _ = dl.dense_act_vjp(to_dev(dY, tdt), None, None, Wd, O.ACT_IDENTITY, need_dw=False)
+    rdX, rdW, rdb = O.dense_act_vjp(dY, None, X, W, O.ACT_IDENTITY)
+    tol = BF16_TOL if bf else F32_TOL
+    assert_close(to_np(dX), rdX, tol, "dX via Wt")
+    assert_close(to_np(dX2), rdX, tol, "dX via W")
+    assert_close(to_np(dW), rdW, tol, "dW")
