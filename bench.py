@@ -33,6 +33,35 @@ PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
+KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "xent.hip", "optim.hip",
+                  "elementwise.hip", "api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources: a stored counter measurement is only
+    used while the code it was taken from is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_layers_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or
+    None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("stage") != stage:
+        return None
+    return rec.get("traffic_bytes")
+
+
 def _split(label):
     name, k = label.split("#")
     return name, int(k)
@@ -247,6 +276,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prof-steps", type=int, default=20)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -265,6 +296,13 @@ def main():
     warmup = args.warmup if args.warmup is not None else warmup
     bench = BENCHES[args.config](dl, w, dev)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(warmup):
         bench.step()
@@ -284,14 +322,15 @@ def main():
     stages = profile_stages(dl, bench, max(1, min(args.prof_steps, steps)))
     dom = max(stages, key=lambda x: x["ms"])
     peak = PEAK_BF16_MFMA if w.dtype == "bf16" else PEAK_FP32_MFMA
+    traffic = stored_traffic(w.name, dom["stage"])
     if "tflops" in dom:
         roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(dom["tflops"] / peak, 4), "traffic": None,
+                    "frac": round(dom["tflops"] / peak, 4), "traffic": traffic,
                     "kernel": dom["stage"]}
     else:
         roofline = {"bound": "hbm", "achieved": dom.get("gbs"), "peak": PEAK_HBM,
                     "unit": "GB/s", "frac": round((dom.get("gbs") or 0.0) / PEAK_HBM, 4),
-                    "traffic": None, "kernel": dom["stage"]}
+                    "traffic": traffic, "kernel": dom["stage"]}
 
     cpu = None
     if not args.no_cpu_baseline and args.config in ("mlp_small", "mlp_adamw"):
@@ -318,6 +357,7 @@ def main():
                    "gemm_flops_per_step": bench.flops()},
         "roofline": roofline,
         "stages": stages,
+        "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
