@@ -76,12 +76,15 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 
 // ---- GEMM planning ----------------------------------------------------------
-// Tiles: float32 {0: 128x128x16, 1: 64x64x32}; bf16 128x128x64 for both.  The
-// large tile is used when it alone yields at least one workgroup per CU (256);
-// otherwise the small one.  Only the weight-gradient product (K = batch) is
-// split along K: when it has fewer than two workgroups per CU, slices are
-// added until about four per CU exist (at most 64), each slice keeping at
-// least four K tiles.
+// float32 tiles {0: 128x128x16, 1: 64x64x32}: the large one when it alone
+// yields at least one workgroup per CU (256), otherwise the small one.
+// bf16 tiles {0: 256x256, 1: 128x128} of the direct-to-LDS kernel (K step 64):
+// 256x256 for forward / dX products with at least one such tile per CU,
+// 128x128 otherwise; operands that kernel cannot take (unaligned, K not a
+// multiple of 64) go to the general 128x128 kernel.  Only the weight-gradient
+// product (K = batch) is split along K: when it has fewer than two
+// workgroups per CU, slices are added until about four per CU exist (at most
+// 64), each slice keeping at least four K tiles.
 
 constexpr int kCUs = 256;
 
@@ -93,8 +96,7 @@ struct Plan {
 
 void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
   if (dtype == DL_BF16) {
-    bm = 128;
-    bn = 128;
+    bm = bn = tile == 0 ? 256 : 128;
     bk = 64;
   } else {
     bm = bn = tile == 0 ? 128 : 64;
@@ -109,7 +111,7 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   int bm, bn, bk;
   tile_shape(dtype, 0, bm, bn, bk);
   int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-  if (tiles < kCUs) {
+  if (tiles < kCUs || (dtype == DL_BF16 && epi == dl::EPI_DW)) {
     p.tile = 1;
     tile_shape(dtype, 1, bm, bn, bk);
     tiles = ceil_div(M, bm) * ceil_div(N, bn);

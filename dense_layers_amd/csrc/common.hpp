@@ -141,9 +141,9 @@ struct GemmDesc {
 // staged as float32 in LDS, then the workgroup streams it out
 // row-contiguously: 4 outputs per thread (8-byte bf16 or 16-byte float32
 // stores), with the bias, activation, derivative mask and bf16 rounding
-// applied on the way.  `stage` must hold BM * (BN + 4) floats and may alias
-// the K-loop buffers (the caller has passed a barrier after its last LDS
-// read).
+// applied on the way.  `stage` must hold stage_floats<BM, BN, WGM>() floats
+// and may alias the K-loop buffers (the caller has passed a barrier after
+// its last LDS read).
 //   out_vec: C (and Z / mask_src) allow aligned 4-wide access (pointer and
 //   leading dimension), checked by the launcher.
 
@@ -194,8 +194,13 @@ template <> struct Raw4<bf16_t> {
   }
 };
 
-template <int BM, int BN>
-constexpr int stage_floats() { return BM * (BN + 4); }
+// A tile whose float32 staging copy exceeds kStageBudget bytes is staged in
+// WGM passes of BM / WGM rows (the rows of one row of waves each).
+constexpr int kStageBudget = 80 * 1024;
+template <int BM, int BN, int WGM>
+constexpr int stage_passes() { return BM * (BN + 4) * 4 <= kStageBudget ? 1 : WGM; }
+template <int BM, int BN, int WGM>
+constexpr int stage_floats() { return BM / stage_passes<BM, BN, WGM>() * (BN + 4); }
 
 template <typename TOut, int BM, int BN, int WGM, int WGN, int EPI, int FM, int FN>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ stage,
@@ -205,7 +210,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int SS = BN + 4;
   constexpr int CPR = BN / 4;  // 4-wide chunks per tile row
+  constexpr int PASSES = stage_passes<BM, BN, WGM>();
+  constexpr int PR = BM / PASSES;  // tile rows per pass
   static_assert(NT % CPR == 0, "each thread keeps the same columns");
+  static_assert(PR % (NT / CPR) == 0, "rows per pass not divisible among threads");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -221,84 +229,96 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
   TO* __restrict__ zout = static_cast<TO*>(d.Z);
   const TO* __restrict__ msrc = static_cast<const TO*>(d.mask_src);
 
-  // every chunk this thread handles has the same 4 columns, rows
+  // every chunk this thread handles has the same 4 columns, pass-local rows
   // tid / CPR + it * (NT / CPR)
-  constexpr int RPT = BM / (NT / CPR);
+  constexpr int RPT = PR / (NT / CPR);
   const int c4 = (tid % CPR) * 4;
   const int col = tn * BN + c4;
   const int nv = col < N ? min(4, N - col) : 0;
   const bool colfull = out_vec && nv == 4;
-
-  // The dX epilogue's saved activations are fetched (in their storage format)
-  // before the staging barrier so their latency overlaps it.
-  Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
-  if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY) {
-#pragma unroll
-    for (int it = 0; it < RPT; ++it) {
-      const int row = tm * BM + tid / CPR + it * (NT / CPR);
-      const int64_t o = (int64_t)row * ld + col;
-      if (row < M && nv > 0) {
-        if (colfull) ms[it].load_vec(msrc + o);
-        else for (int e = 0; e < nv; ++e) ms[it].set(e, Elem<TO>::load(msrc, o + e));
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stage[(wm * WM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3)) * SS + wn * WN + j * 32 + l32] =
-            acc[i][j][r];
-  __syncthreads();
-
-  if (nv == 0) return;
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (EPI == EPI_FWD && d.bias != nullptr)
     for (int e = 0; e < nv; ++e) bias[e] = d.bias[col + e];
+
 #pragma unroll
-  for (int it = 0; it < RPT; ++it) {
-    const int rl = tid / CPR + it * (NT / CPR);
-    const int row = tm * BM + rl;
-    if (row >= M) continue;
-    float v[4];
-    Store4<float>::load_vec(stage + rl * SS + c4, v);
-    const int64_t o = (int64_t)row * ld + col;
-    if (EPI == EPI_FWD) {
-      float z[4];
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int prow0 = tm * BM + pass * PR;
+    // The dX epilogue's saved activations are fetched (in their storage
+    // format) before the staging barrier so their latency overlaps it.
+    Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
+    if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[e] = v[e] + bias[e];
-        v[e] = act_apply(d.act, z[e]);
-      }
-      if (colfull) {
-        Store4<TO>::vec(out + o, v);
-        if (zout != nullptr) Store4<TO>::vec(zout + o, z);
-      } else {
-        for (int e = 0; e < nv; ++e) {
-          Elem<TO>::store(out, o + e, v[e]);
-          if (zout != nullptr) Elem<TO>::store(zout, o + e, z[e]);
+      for (int it = 0; it < RPT; ++it) {
+        const int row = prow0 + tid / CPR + it * (NT / CPR);
+        const int64_t o = (int64_t)row * ld + col;
+        if (row < M && nv > 0) {
+          if (colfull) ms[it].load_vec(msrc + o);
+          else for (int e = 0; e < nv; ++e) ms[it].set(e, Elem<TO>::load(msrc, o + e));
         }
       }
-    } else if (EPI == EPI_DX) {
-      if (d.mask_act != ACT_IDENTITY) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[it].get(e));
-      }
-      if (colfull) Store4<TO>::vec(out + o, v);
-      else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
-    } else {
-      if (colfull) Store4<TO>::vec(out + o, v);
-      else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
     }
+
+    if (PASSES == 1 || wm == pass) {
+      const int r0 = PASSES == 1 ? wm * WM : 0;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            stage[(r0 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3)) * SS + wn * WN + j * 32 + l32] =
+                acc[i][j][r];
+    }
+    __syncthreads();
+
+    if (nv > 0) {
+#pragma unroll
+      for (int it = 0; it < RPT; ++it) {
+        const int rl = tid / CPR + it * (NT / CPR);
+        const int row = prow0 + rl;
+        if (row >= M) continue;
+        float v[4];
+        Store4<float>::load_vec(stage + rl * SS + c4, v);
+        const int64_t o = (int64_t)row * ld + col;
+        if (EPI == EPI_FWD) {
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            z[e] = v[e] + bias[e];
+            v[e] = act_apply(d.act, z[e]);
+          }
+          if (colfull) {
+            Store4<TO>::vec(out + o, v);
+            if (zout != nullptr) Store4<TO>::vec(zout + o, z);
+          } else {
+            for (int e = 0; e < nv; ++e) {
+              Elem<TO>::store(out, o + e, v[e]);
+              if (zout != nullptr) Elem<TO>::store(zout, o + e, z[e]);
+            }
+          }
+        } else if (EPI == EPI_DX) {
+          if (d.mask_act != ACT_IDENTITY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[it].get(e));
+          }
+          if (colfull) Store4<TO>::vec(out + o, v);
+          else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+        } else {
+          if (colfull) Store4<TO>::vec(out + o, v);
+          else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+        }
+      }
+    }
+    if (PASSES > 1 && pass + 1 < PASSES) __syncthreads();
   }
 }
 
 // Host-side launchers (defined in the kernel files).
 hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s);
+// Direct-to-LDS bf16 GEMM; hipErrorNotSupported when the operands do not
+// meet its alignment / K-multiple requirements (nothing is launched then).
+hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s);
 hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 const float* db_partial, float* C, int64_t ldc,
                                 float* db, hipStream_t s);

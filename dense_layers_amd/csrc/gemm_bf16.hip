@@ -158,7 +158,7 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
   using LA = TileLoaderBf16<BM, ALAY, NT>;
   using LB = TileLoaderBf16<BN, BLAY, NT>;
   constexpr int kSmemAB = (2 * LA::kLdsSize + 2 * LB::kLdsSize) * 2;  // bytes
-  constexpr int kStage = stage_floats<BM, BN>() * 4;
+  constexpr int kStage = stage_floats<BM, BN, WGM>() * 4;
   __shared__ __attribute__((aligned(16))) char smem[kSmemAB > kStage ? kSmemAB : kStage];
   // buffer b of A at b * LA::kLdsSize, of B after both A buffers
   auto As = [&](int b) { return reinterpret_cast<bf16_t*>(smem) + b * LA::kLdsSize; };
@@ -373,14 +373,15 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
-// 128x128 (4 waves of 64x64, two workgroups per CU); measured faster than
-// 256x128, 128x256 and 256x256 on the transformer-MLP shapes.
+// Tiles 0 and 1 go to the direct-to-LDS kernel (256x256 and 128x128) when
+// the operands allow it; everything else, and operands it declines, runs the
+// general kernel at 128x128 (4 waves of 64x64, two workgroups per CU).
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
-  switch (tile) {
-    case 0:
-    case 1: return dispatch_layout<128, 128, 2, 2>(d, s);
-    default: return hipErrorInvalidValue;
+  if (tile == 0 || tile == 1) {
+    const hipError_t e = launch_gemm_bf16_dma(d, tile, s);
+    if (e != hipErrorNotSupported) return e;
   }
+  return dispatch_layout<128, 128, 2, 2>(d, s);
 }
 
 }  // namespace dl

@@ -1,0 +1,336 @@
+// bfloat16-operand GEMM for large, aligned problems: operand tiles go from
+// HBM straight into LDS (global_load_lds_dwordx4, no staging registers), the
+// matrix cores read them back as MFMA fragments (v_mfma_f32_32x32x16_bf16,
+// float32 accumulation), and the dense-layer epilogues of the general bf16
+// kernel are applied on the way out.
+//
+// The products are the three of the fused LinearAct (noeira.nn docs, "The
+// design in one page"): forward Z = X W^T + b, dX = (dY o act') W and
+// dW = (dY o act')^T X, on the bf16 working copies of the FP32-master-weight
+// scheme (Orthon page, "Mixed-precision training on CUDA").
+//
+// Pipeline: STAGES LDS buffers of BK k each.  The loads of stage
+// kt + STAGES - 1 are issued at the top of stage kt, so each load has
+// STAGES - 1 stages of matrix-core work to land in; nothing is staged in
+// VGPRs.  One barrier per stage publishes the next stage (see the loop).
+//
+// A direct load writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so the
+// LDS layout is chosen by which global 16-byte unit each lane fetches:
+//  * K-major operand (rows contiguous in k): LDS row r holds the 64 k of tile
+//    row r as eight 16-byte units, unit u at position u ^ ((r ^ r >> 3) & 7).
+//    A lane's fragment (8 consecutive k of one row) is one 16-byte LDS read;
+//    the 16 lanes of one read phase land on distinct banks.
+//  * M/N-major operand (rows contiguous in m): LDS k-row k holds the tile's
+//    ROWS m of that k, 16-byte unit u at position u ^ (4 (k & 3)).  Fragments
+//    come from the gfx950 transposing read ds_read_b64_tr_b16: in each group
+//    of 16 lanes, lane i receives element i % 4 of the 8-byte piece addressed
+//    by lane 4 t + i / 4 as its element t.  Lane 4 t + q of the group
+//    addresses k-row (k0 + t), m = m0 + 4 q, so lane i gets k0 .. k0 + 3 of
+//    column m0 + i; two reads give the 8 k of a fragment.  The 4 k-rows read
+//    together sit in different 64-byte bank groups.
+// Which k a lane supplies inside an MFMA is free as long as A and B agree: at
+// k-step ks, lane half h supplies k = 16 ks + 8 h + (0..7) for both layouts.
+//
+// Requirements (checked by the launcher, which reports hipErrorNotSupported
+// otherwise so the caller can use the general kernel): A and B 16-byte
+// aligned with leading dimensions a multiple of 8, K and the split length
+// multiples of 64, and M (N) a multiple of 8 when A (B) is M/N-major.  Tile
+// rows past M or N are clamped to a valid row; they only feed outputs that are
+// never stored.
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations and leaves the LDS and export counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// K-major swizzle: 16-byte unit u of tile row r sits at position u ^ ksw(r).
+// With BK = 64 a row is 8 units (128 bytes), with BK = 32 it is 4 units and
+// four consecutive rows share a 256-byte bank window.
+template <int BK>
+__device__ __forceinline__ int ksw(int row) {
+  return BK == 64 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & 3);
+}
+__device__ __forceinline__ int msw(int k) { return (k & 3) << 2; }
+
+template <int ROWS, int LAY, int NT, int BK>
+struct DmaOperand {
+  static constexpr int kBytes = ROWS * BK * 2;  // one stage
+  static constexpr int kUnits = ROWS * BK / 8;  // 16-byte units per stage
+  static constexpr int kUPR = BK / 8;           // units per K-major row
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kInst = kUnits / (64 * kWaves);  // loads per wave per stage
+  static_assert(kUnits % (64 * kWaves) == 0, "stage not divisible among waves");
+  static_assert(LAY == K_MAJOR || ROWS % 128 == 0, "M/N-major tiles need 16+ units per k-row");
+  static_assert(BK == 32 || BK == 64, "BK");
+
+  const bf16_t* ptr[kInst];  // this lane's source for load i of the next stage
+  int64_t step;              // elements between consecutive stages
+
+  __device__ __forceinline__ void init(const bf16_t* __restrict__ base, int64_t ld, int row0,
+                                       int nrows, int k0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      const int U = (i * kWaves + wave) * 64 + lane;  // LDS position of this lane's unit
+      if (LAY == K_MAJOR) {
+        const int row = U / kUPR;
+        const int u = (U % kUPR) ^ ksw<BK>(row);
+        const int grow = min(row0 + row, nrows - 1);
+        ptr[i] = base + (int64_t)grow * ld + k0 + u * 8;
+      } else {
+        constexpr int UPR = ROWS / 8;
+        const int kr = U / UPR;
+        const int u = (U % UPR) ^ msw(kr);
+        int m = row0 + u * 8;
+        if (m >= nrows) m = row0;
+        ptr[i] = base + (int64_t)(k0 + kr) * ld + m;
+      }
+    }
+    step = LAY == K_MAJOR ? BK : (int64_t)BK * ld;
+  }
+
+  // Issue this wave's loads of one stage into `lds` (the operand's buffer).
+  __device__ __forceinline__ void issue(char* lds, int wave) {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(ptr[i]),
+          (__attribute__((address_space(3))) void*)(lds + (i * kWaves + wave) * 1024), 16, 0, 0);
+      ptr[i] += step;
+    }
+  }
+
+  // Fragment of tile rows mb .. mb + 31 at k-step ks: this lane's 8 k.
+  __device__ __forceinline__ static bf16x8 frag(const char* lds, int mb, int ks, int lane) {
+    if (LAY == K_MAJOR) {
+      const int row = mb + (lane & 31);
+      const int pos = (2 * ks + (lane >> 5)) ^ ksw<BK>(row);
+      return *reinterpret_cast<const bf16x8*>(lds + row * (BK * 2) + pos * 16);
+    } else {
+      const int g = (lane >> 4) & 1, h = lane >> 5, t = (lane >> 2) & 3, q = lane & 3;
+      const int m = mb + 16 * g + 4 * q;
+      const int k0 = ks * 16 + 8 * h + t;
+      const int off = ((m >> 3) ^ (t << 2)) * 16 + ((m >> 2) & 1) * 8;
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(lds + k0 * (ROWS * 2) + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(lds + (k0 + 4) * (ROWS * 2) + off));
+      const s16x8 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, x);
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int KS = BK / 16;  // MFMA k-steps per stage
+  static_assert(FM >= 1 && FN >= 1, "bad tile");
+  static_assert(STAGES >= 2, "stages");
+  using OA = DmaOperand<BM, ALAY, NT, BK>;
+  using OB = DmaOperand<BN, BLAY, NT, BK>;
+  constexpr int kStageBytes = OA::kBytes + OB::kBytes;
+  constexpr int kLoads = OA::kInst + OB::kInst;  // per wave per stage
+  constexpr int kEpiBytes = stage_floats<BM, BN, WGM>() * 4;
+  constexpr int kSmem = STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int h = lane >> 5;
+
+  int split, tm, tn;
+  tile_coords(tiles_m, tiles_n, split, tm, tn);
+
+  const int M = d.M, N = d.N;
+  const int kbeg = split * d.k_per_split;
+  const int kend = min(d.K, kbeg + d.k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+
+  OA oa;
+  OB ob;
+  oa.init(static_cast<const bf16_t*>(d.A), d.lda, tm * BM, M, kbeg, wave, lane);
+  ob.init(static_cast<const bf16_t*>(d.B), d.ldb, tn * BN, N, kbeg, wave, lane);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const bool do_db = (EPI == EPI_DW) && (d.db != nullptr || d.db_partial != nullptr) &&
+                     tn == 0 && wn == 0;
+  float dbacc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
+
+  auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * kStageBytes; };
+  auto issue = [&](int kt) {
+    char* p = stage_ptr(kt);
+    oa.issue(p, wave);
+    ob.issue(p + OA::kBytes, wave);
+  };
+  auto read_frags = [&](const char* cur, int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i] = OA::frag(cur, wm * WM + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = OB::frag(cur + OA::kBytes, wn * WN + j * 32, ks, lane);
+  };
+  auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+    if (do_db) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += static_cast<float>(a[i][e]);
+        dbacc[i] += s;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Fragments are double-buffered in registers (set ks & 1 holds k-step ks),
+  // so the reads of one k-step are in flight while the MFMAs of the previous
+  // one run.  The barrier of stage kt sits before its last k-step: by then
+  // every wave holds its last fragments of stage kt in registers, so after
+  // the barrier the first fragments of stage kt + 1 are read while the last
+  // MFMAs of stage kt run, and the matrix cores do not idle at the barrier.
+  // Each wave drains its LDS reads before that barrier, so once past it no
+  // wave reads stage kt's buffer again; the loads issued at the top of stage
+  // kt + 1 (stage kt + STAGES, same buffer) may then overwrite it.
+  bf16x8 fa[2][FM], fb[2][FN];
+  constexpr int kReads = (ALAY == K_MAJOR ? FM : 2 * FM) + (BLAY == K_MAJOR ? FN : 2 * FN);
+  constexpr int kMfma = FM * FN;
+  // scheduling hint for one k-step: its MFMAs interleaved with the reads of
+  // the next fragments
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < (kReads < kMfma ? kReads : kMfma); ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+    if (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  };
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+  if (nk > 0) {
+    if (nk >= STAGES - 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    read_frags(stage_ptr(0), 0, fa[0], fb[0]);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = stage_ptr(kt);
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mfmas(fa[ks & 1], fb[ks & 1]);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // own reads of stage kt complete; stage kt + 1 landed for this wave
+    // (at most the loads of the stages after it still in flight).  On the
+    // last stage the reads below fetch a buffer whose contents go unused.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    if (kt + STAGES - 1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(stage_ptr(kt + 1), 0, fa[KS & 1], fb[KS & 1]);
+    mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // the epilogue reuses the stage buffers
+
+  if (EPI == EPI_DW && do_db) {
+    const int row_base = tm * BM + wm * WM;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      const int row = row_base + i * 32 + (lane & 31);
+      if (h == 0 && row < M) {
+        if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
+        else d.db[row] = v;
+      }
+    }
+  }
+  store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn, split,
+                                            out_vec);
+}
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
+  auto aligned = [](const void* p, int64_t ld) {
+    return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 8 == 0);
+  };
+  if (!aligned(d.A, d.lda) || !aligned(d.B, d.ldb)) return hipErrorNotSupported;
+  if (d.K % 64 != 0 || d.k_per_split % 64 != 0 || d.k_per_split <= 0) return hipErrorNotSupported;
+  if (ALAY == MN_MAJOR && d.M % 8 != 0) return hipErrorNotSupported;
+  if (BLAY == MN_MAJOR && d.N % 8 != 0) return hipErrorNotSupported;
+  const int tiles_m = (d.M + BM - 1) / BM;
+  const int tiles_n = (d.N + BN - 1) / BN;
+  const int64_t nwg = (int64_t)tiles_m * tiles_n * d.splits;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+  auto out_ok = [](const void* p, int64_t ld, int bytes) {
+    return ((reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0) && (ld % 4 == 0);
+  };
+  int out_vec;
+  if (EPI == EPI_DW)
+    out_vec = d.splits > 1 ? out_ok(d.partial, d.N, 16) : out_ok(d.C, d.ldc, 16);
+  else
+    out_vec = out_ok(d.C, d.ldc, 8) && (d.Z == nullptr || out_ok(d.Z, d.ldc, 8)) &&
+              (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 8));
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI>),
+                     dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n,
+                     out_vec);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
+  if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+  if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX>(d, s);
+  if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+  if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
+  switch (tile) {
+    case 0: return dma_layout<256, 256, 64, 2, 2, 4>(d, s);
+    case 1: return dma_layout<128, 128, 64, 2, 2, 2>(d, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace dl

@@ -131,7 +131,7 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
   using LA = TileLoader<BM, BK, ALAY, NT>;
   using LB = TileLoader<BN, BK, BLAY, NT>;
   constexpr int kSmemAB = 2 * LA::kLdsSize + 2 * LB::kLdsSize;
-  constexpr int kStage = stage_floats<BM, BN>();
+  constexpr int kStage = stage_floats<BM, BN, WGM>();
   __shared__ __attribute__((aligned(16))) float smem[kSmemAB > kStage ? kSmemAB : kStage];
   // buffer b of A at smem + b * LA::kLdsSize, of B after both A buffers
   auto As = [&](int b) { return smem + b * LA::kLdsSize; };

@@ -181,6 +181,52 @@ def test_dense_vjp_bf16(dl, shape, act):
     assert_close(to_np(db), rdb, BF16_TOL, "db")
 
 
+# Shapes that reach the direct-to-LDS bf16 kernel's 256x256 tile (at least
+# 256 such tiles, K a multiple of 64) with ragged M and N, and its 128x128
+# tile on a ragged, split-K weight gradient.
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_bf16_large_tile_fwd_ragged(dl, act):
+    B, n_in, n_out = 4104, 192, 4120
+    X = si.random_matrix(230, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(231, (n_out, n_in), scale=0.05, bf16_exact=True)
+    b = si.random_matrix(232, (n_out,), scale=0.01)
+    bf = torch.bfloat16
+    Y, Z = dl.dense_act_fwd(to_dev(X, bf), to_dev(W, bf), to_dev(b), act, save_z=True)
+    refY, refZ = O.dense_act_fwd(X, W, b, act)
+    assert_close(to_np(Z), refZ, BF16_TOL, "Z")
+    assert_close(to_np(Y), refY, BF16_TOL, "Y")
+
+
+@pytest.mark.parametrize("use_wt", [False, True])
+def test_bf16_large_tile_dx_ragged(dl, use_wt):
+    B, n_in, n_out = 4104, 4120, 192
+    X = si.random_matrix(240, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(241, (n_out, n_in), scale=0.05, bf16_exact=True)
+    Z = si.random_matrix(242, (B, n_out), bf16_exact=True)
+    dY = si.random_matrix(243, (B, n_out), bf16_exact=True)
+    bf = torch.bfloat16
+    Wd = to_dev(W, bf)
+    Wt = Wd.t().contiguous() if use_wt else None
+    dX, _, _ = dl.dense_act_vjp(to_dev(dY, bf), to_dev(Z, bf), None, Wd, O.ACT_GELU_TANH,
+                                need_dw=False, Wt=Wt)
+    rdX, _, _ = O.dense_act_vjp(dY, Z, X, W, O.ACT_GELU_TANH, need_dx=True)
+    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+
+
+def test_bf16_dw_split_ragged(dl):
+    B, n_in, n_out = 1024, 1000, 200
+    X = si.random_matrix(250, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(251, (n_out, n_in), scale=0.05, bf16_exact=True)
+    dY = si.random_matrix(252, (B, n_out), bf16_exact=True)
+    bf = torch.bfloat16
+    dX, dW, db = dl.dense_act_vjp(to_dev(dY, bf), None, to_dev(X, bf), to_dev(W, bf),
+                                  O.ACT_IDENTITY)
+    rdX, rdW, rdb = O.dense_act_vjp(dY, None, X, W, O.ACT_IDENTITY)
+    assert_close(to_np(dW), rdW, BF16_TOL, "dW")
+    assert_close(to_np(db), rdb, BF16_TOL, "db")
+    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+
+
 def test_bf16_fp32_consistency(dl):
     """With bf16-exact operands the fp32 path must meet 1e-4 on the same
     oracle, so the bf16 tolerance hides only output rounding."""
