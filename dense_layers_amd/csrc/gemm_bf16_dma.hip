@@ -94,15 +94,16 @@ struct DmaOperand {
     step = LAY == K_MAJOR ? BK : (int64_t)BK * ld;
   }
 
-  // Issue this wave's loads of one stage into `lds` (the operand's buffer).
-  __device__ __forceinline__ void issue(char* lds, int wave) {
-#pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)(ptr[i]),
-          (__attribute__((address_space(3))) void*)(lds + (i * kWaves + wave) * 1024), 16, 0, 0);
-      ptr[i] += step;
-    }
+  // Issue this wave's load i of the next stage into `lds` (the operand's
+  // buffer).  Past the last stage (`past`) the load repeats the previous
+  // stage instead, so that every stage issues the same number of loads; the
+  // buffer it fills is never read again.
+  __device__ __forceinline__ void issue_one(char* lds, int wave, int i, bool past) {
+    const int64_t back = past ? step : 0;
+    __builtin_amdgcn_global_load_lds(
+        (__attribute__((address_space(1))) void*)(ptr[i] - back),
+        (__attribute__((address_space(3))) void*)(lds + (i * kWaves + wave) * 1024), 16, 0, 0);
+    ptr[i] += step - back;
   }
 
   // Fragment of tile rows mb .. mb + 31 at k-step ks: this lane's 8 k.
@@ -126,6 +127,20 @@ struct DmaOperand {
     }
   }
 };
+
+// Scheduling hint for one k-step: its MFMAs interleaved with the LDS reads of
+// the next fragments and with NV global loads.
+template <int kMfma, int kReads, int NV>
+__device__ __forceinline__ void sched_interleave() {
+#pragma unroll
+  for (int r = 0; r < kMfma; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (r < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (r < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads > kMfma ? kReads - kMfma : 1, 0);
+  if (NV > kMfma) __builtin_amdgcn_sched_group_barrier(0x020, NV > kMfma ? NV - kMfma : 1, 0);
+}
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -178,10 +193,15 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
 
   auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * kStageBytes; };
-  auto issue = [&](int kt) {
+  // loads j0 .. j1 - 1 of stage kt (A's loads first, then B's)
+  auto issue_range = [&](int kt, int j0, int j1) {
     char* p = stage_ptr(kt);
-    oa.issue(p, wave);
-    ob.issue(p + OA::kBytes, wave);
+    const bool past = kt >= nk;
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      if (j < OA::kInst) oa.issue_one(p, wave, j, past);
+      else ob.issue_one(p + OA::kBytes, wave, j - OA::kInst, past);
+    }
   };
   auto read_frags = [&](const char* cur, int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
@@ -213,55 +233,56 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   // the barrier the first fragments of stage kt + 1 are read while the last
   // MFMAs of stage kt run, and the matrix cores do not idle at the barrier.
   // Each wave drains its LDS reads before that barrier, so once past it no
-  // wave reads stage kt's buffer again; the loads issued at the top of stage
-  // kt + 1 (stage kt + STAGES, same buffer) may then overwrite it.
+  // wave reads stage kt's buffer again; the loads of stage kt + STAGES (same
+  // buffer), issued during stage kt + 1, may then overwrite it.
+  //
+  // With three or more stages the loads of stage kt + STAGES - 1 are spread
+  // over the k-steps of stage kt, interleaved with the MFMAs, and every stage
+  // issues kLoads loads (repeats past the end), so at the barrier of stage kt
+  // the loads still allowed in flight are those of the stages after kt + 1:
+  // (STAGES - 2) kLoads minus the part of stage kt + STAGES - 1 not yet
+  // issued.  With two stages the loads of stage kt + 1 all go first (they
+  // must land by the barrier of stage kt) and none are allowed in flight.
   bf16x8 fa[2][FM], fb[2][FN];
   constexpr int kReads = (ALAY == K_MAJOR ? FM : 2 * FM) + (BLAY == K_MAJOR ? FN : 2 * FN);
   constexpr int kMfma = FM * FN;
-  // scheduling hint for one k-step: its MFMAs interleaved with the reads of
-  // the next fragments
-  auto interleave = [&]() {
-#pragma unroll
-    for (int r = 0; r < (kReads < kMfma ? kReads : kMfma); ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
-    if (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-  };
+  // loads per k-step (three or more stages): kMid in each, the remainder in
+  // the last
+  constexpr int kMid = STAGES == 2 ? 0 : kLoads / KS;
+  constexpr int kLast = STAGES == 2 ? 0 : kLoads - (KS - 1) * kMid;
+  constexpr int kAllowed = (STAGES - 2) * kLoads - kLast;
+  auto part = [](int ks) { return ks * kMid; };
 
+  if (nk > 0) {  // (always true for the splits the launcher forms)
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-  if (nk > 0) {
-    if (nk >= STAGES - 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    for (int s = 0; s < STAGES - 1; ++s) issue_range(s, 0, kLoads);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
     __builtin_amdgcn_s_barrier();
     read_frags(stage_ptr(0), 0, fa[0], fb[0]);
   }
 
   for (int kt = 0; kt < nk; ++kt) {
     const char* cur = stage_ptr(kt);
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    if (STAGES == 2 && kt + 1 < nk) issue_range(kt + 1, 0, kLoads);
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
+      if (STAGES > 2) issue_range(kt + STAGES - 1, part(ks), part(ks + 1));
       read_frags(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       mfmas(fa[ks & 1], fb[ks & 1]);
-      interleave();
+      sched_interleave<kMfma, kReads, kMid>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // own reads of stage kt complete; stage kt + 1 landed for this wave
-    // (at most the loads of the stages after it still in flight).  On the
-    // last stage the reads below fetch a buffer whose contents go unused.
+    // own reads of stage kt complete; stage kt + 1 landed for this wave.  On
+    // the last stage the reads below fetch a buffer whose contents go unused.
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    if (kt + STAGES - 1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAllowed));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if (STAGES > 2) issue_range(kt + STAGES - 1, part(KS - 1), kLoads);
     read_frags(stage_ptr(kt + 1), 0, fa[KS & 1], fb[KS & 1]);
     mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
-    interleave();
+    sched_interleave<kMfma, kReads, kLast>();
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // the epilogue reuses the stage buffers
@@ -327,7 +348,7 @@ hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
 
 hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
-    case 0: return dma_layout<256, 256, 64, 2, 2, 4>(d, s);
+    case 0: return dma_layout<256, 256, 32, 4, 2, 4>(d, s);
     case 1: return dma_layout<128, 128, 64, 2, 2, 2>(d, s);
     default: return hipErrorNotSupported;
   }
