@@ -202,16 +202,56 @@ constexpr int stage_passes() { return BM * (BN + 4) * 4 <= kStageBudget ? 1 : WG
 template <int BM, int BN, int WGM>
 constexpr int stage_floats() { return BM / stage_passes<BM, BN, WGM>() * (BN + 4); }
 
-template <typename TOut, int BM, int BN, int WGM, int WGN, int EPI, int FM, int FN>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ stage,
-                                           const GemmDesc& d, int tm, int tn, int split,
-                                           int out_vec) {
-  constexpr int NT = WGM * WGN * 64;
+// Rows handled per thread in one staging pass, and the load of the dX
+// epilogue's saved activations for one pass (kept in their storage format).
+template <int BM, int BN, int WGM, int WGN>
+struct EpiShape {
+  static constexpr int NT = WGM * WGN * 64;
+  static constexpr int CPR = BN / 4;  // 4-wide chunks per tile row
+  static constexpr int PASSES = stage_passes<BM, BN, WGM>();
+  static constexpr int PR = BM / PASSES;  // tile rows per pass
+  static constexpr int RPT = PR / (NT / CPR);
+};
+
+template <typename TO, int BM, int BN, int WGM, int WGN, int RPT>
+__device__ __forceinline__ void load_mask_pass(Raw4<TO> (&ms)[RPT], const GemmDesc& d, int tm,
+                                               int tn, int pass, int out_vec) {
+  using G = EpiShape<BM, BN, WGM, WGN>;  // RPT == G::RPT where a mask is used
+  const int tid = threadIdx.x;
+  const int c4 = (tid % G::CPR) * 4;
+  const int col = tn * BN + c4;
+  const int nv = col < d.N ? min(4, d.N - col) : 0;
+  const bool colfull = out_vec && nv == 4;
+  const TO* __restrict__ msrc = static_cast<const TO*>(d.mask_src);
+#pragma unroll
+  for (int it = 0; it < G::RPT; ++it) {
+    const int row = tm * BM + pass * G::PR + tid / G::CPR + it * (G::NT / G::CPR);
+    const int64_t o = (int64_t)row * d.ldc + col;
+    if (row < d.M && nv > 0) {
+      if (colfull) ms[it].load_vec(msrc + o);
+      else for (int e = 0; e < nv; ++e) ms[it].set(e, Elem<TO>::load(msrc, o + e));
+    }
+  }
+}
+
+// With PRE the caller has already loaded pass 0's saved activations into
+// `pre` (dX epilogue with a derivative mask); otherwise they are loaded here.
+// The saved activations of pass p + 1 are requested while pass p is written.
+template <typename TOut, int BM, int BN, int WGM, int WGN, int EPI, int FM, int FN, bool PRE,
+          typename TO, int NPRE>
+__device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
+                                                float* __restrict__ stage, const GemmDesc& d,
+                                                int tm, int tn, int split, int out_vec,
+                                                Raw4<TO> (&pre)[NPRE]) {
+  static_assert(std::is_same<TO, typename std::conditional<EPI == EPI_DW, float, TOut>::type>::value,
+                "storage type");
+  using G = EpiShape<BM, BN, WGM, WGN>;
+  constexpr int NT = G::NT;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int SS = BN + 4;
-  constexpr int CPR = BN / 4;  // 4-wide chunks per tile row
-  constexpr int PASSES = stage_passes<BM, BN, WGM>();
-  constexpr int PR = BM / PASSES;  // tile rows per pass
+  constexpr int CPR = G::CPR;
+  constexpr int PASSES = G::PASSES;
+  constexpr int PR = G::PR;
   static_assert(NT % CPR == 0, "each thread keeps the same columns");
   static_assert(PR % (NT / CPR) == 0, "rows per pass not divisible among threads");
   const int tid = threadIdx.x;
@@ -219,7 +259,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, h = lane >> 5;
   const int M = d.M, N = d.N;
-  using TO = typename std::conditional<EPI == EPI_DW, float, TOut>::type;
   TO* __restrict__ out = static_cast<TO*>(d.C);
   int64_t ld = d.ldc;
   if (EPI == EPI_DW && d.splits > 1) {
@@ -227,11 +266,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
     ld = N;
   }
   TO* __restrict__ zout = static_cast<TO*>(d.Z);
-  const TO* __restrict__ msrc = static_cast<const TO*>(d.mask_src);
 
   // every chunk this thread handles has the same 4 columns, pass-local rows
   // tid / CPR + it * (NT / CPR)
-  constexpr int RPT = PR / (NT / CPR);
+  constexpr int RPT = G::RPT;
   const int c4 = (tid % CPR) * 4;
   const int col = tn * BN + c4;
   const int nv = col < N ? min(4, N - col) : 0;
@@ -239,25 +277,21 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (EPI == EPI_FWD && d.bias != nullptr)
     for (int e = 0; e < nv; ++e) bias[e] = d.bias[col + e];
+  const bool masked = EPI == EPI_DX && d.mask_act != ACT_IDENTITY;
+
+  Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
+  if (masked) {
+    if (PRE) {
+#pragma unroll
+      for (int it = 0; it < (RPT < NPRE ? RPT : NPRE); ++it) ms[it] = pre[it];
+    } else {
+      load_mask_pass<TO, BM, BN, WGM, WGN>(ms, d, tm, tn, 0, out_vec);
+    }
+  }
 
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     const int prow0 = tm * BM + pass * PR;
-    // The dX epilogue's saved activations are fetched (in their storage
-    // format) before the staging barrier so their latency overlaps it.
-    Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
-    if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY) {
-#pragma unroll
-      for (int it = 0; it < RPT; ++it) {
-        const int row = prow0 + tid / CPR + it * (NT / CPR);
-        const int64_t o = (int64_t)row * ld + col;
-        if (row < M && nv > 0) {
-          if (colfull) ms[it].load_vec(msrc + o);
-          else for (int e = 0; e < nv; ++e) ms[it].set(e, Elem<TO>::load(msrc, o + e));
-        }
-      }
-    }
-
     if (PASSES == 1 || wm == pass) {
       const int r0 = PASSES == 1 ? wm * WM : 0;
 #pragma unroll
@@ -270,6 +304,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
                 acc[i][j][r];
     }
     __syncthreads();
+
+    Raw4<TO> ms_next[EPI == EPI_DX && PASSES > 1 ? RPT : 1];
+    if (masked && pass + 1 < PASSES)
+      load_mask_pass<TO, BM, BN, WGM, WGN>(ms_next, d, tm, tn, pass + 1, out_vec);
 
     if (nv > 0) {
 #pragma unroll
@@ -297,7 +335,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
             }
           }
         } else if (EPI == EPI_DX) {
-          if (d.mask_act != ACT_IDENTITY) {
+          if (masked) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] *= act_deriv(d.mask_act, ms[it].get(e));
           }
@@ -309,8 +347,22 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
         }
       }
     }
+    if (masked && pass + 1 < PASSES) {
+#pragma unroll
+      for (int it = 0; it < RPT; ++it) ms[it] = ms_next[it];
+    }
     if (PASSES > 1 && pass + 1 < PASSES) __syncthreads();
   }
+}
+
+template <typename TOut, int BM, int BN, int WGM, int WGN, int EPI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* __restrict__ stage,
+                                           const GemmDesc& d, int tm, int tn, int split,
+                                           int out_vec) {
+  using TO = typename std::conditional<EPI == EPI_DW, float, TOut>::type;
+  Raw4<TO> none[EpiShape<BM, BN, WGM, WGN>::RPT];
+  store_tile_impl<TOut, BM, BN, WGM, WGN, EPI, FM, FN, false>(acc, stage, d, tm, tn, split,
+                                                              out_vec, none);
 }
 
 // Host-side launchers (defined in the kernel files).

@@ -253,6 +253,14 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   constexpr int kAllowed = (STAGES - 2) * kLoads - kLast;
   auto part = [](int ks) { return ks * kMid; };
 
+  // The dX epilogue's saved activations for its first staging pass are
+  // requested before the first operand loads, so their HBM latency overlaps
+  // the pipeline fill instead of stalling the epilogue.
+  using Epi = EpiShape<BM, BN, WGM, WGN>;
+  Raw4<bf16_t> ms0[EPI == EPI_DX ? Epi::RPT : 1];
+  if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY)
+    load_mask_pass<bf16_t, BM, BN, WGM, WGN>(ms0, d, tm, tn, 0, out_vec);
+
   if (nk > 0) {  // (always true for the splits the launcher forms)
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue_range(s, 0, kLoads);
@@ -299,8 +307,12 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
       }
     }
   }
-  store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn, split,
-                                            out_vec);
+  if constexpr (EPI == EPI_DX)
+    store_tile_impl<bf16_t, BM, BN, WGM, WGN, EPI, FM, FN, true>(
+        acc, reinterpret_cast<float*>(smem), d, tm, tn, split, out_vec, ms0);
+  else
+    store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn,
+                                              split, out_vec);
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
