@@ -33,8 +33,8 @@ PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
-KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip", "optim.hip",
-                  "elementwise.hip", "api.cpp"]
+KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
+                  "head.hip", "optim.hip", "elementwise.hip", "api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -98,12 +98,19 @@ class MLPBench:
         w = self.w
         B, L = w.batch, w.n_layers
         name, k = _split(label)
+        # with the fused narrow head the last layer has no GEMM of its own
+        last = L - 2 if "head_xent#0" in getattr(self, "labels", ()) else L - 1
         if name == "fwd_gemm":
             l = k
         elif name in ("dw_gemm", "dx_gemm"):
-            l = L - 1 - k          # the backward pass runs from the last layer
+            l = last - k           # the backward pass runs from the last GEMM layer
         elif name == "xent":
             return "byte", 8 * B * w.dims[-1] + 8 * B
+        elif name == "head_xent":
+            # last Linear forward, its dW and (for more than one layer) its dX
+            return "flop", (3 if L > 1 else 2) * 2 * B * w.dims[-2] * w.dims[-1]
+        elif name == "loss_mean":
+            return "byte", 4 * B
         elif name in ("adamw_multi", "sgd_multi"):
             return "byte", (28 if name == "adamw_multi" else 12) * w.n_params()
         else:
@@ -254,6 +261,7 @@ def profile_stages(dl, bench, n_steps):
     for name, _ in recs[:per_step]:
         labels.append(f"{name}#{seen.get(name, 0)}")
         seen[name] = seen.get(name, 0) + 1
+    bench.labels = labels
     stages = []
     for j, lab in enumerate(labels):
         ms = float(np.mean([recs[i * per_step + j][1] for i in range(n_steps)]))

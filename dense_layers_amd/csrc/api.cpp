@@ -465,6 +465,19 @@ int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src
 // of their own: the optimizer kernel adds the slices, stores dW / db and
 // applies the update in one read.
 
+// Whether the last layer runs as the fused narrow head (last Linear +
+// softmax-xent + its vjp in one kernel).
+static bool mlp_fused_head(int32_t L, const dl_layer_t* layers) {
+  return dl::head_xent_fits(layers[L - 1].in, layers[L - 1].out);
+}
+
+// Gradient slices a layer's dW / db leave for the optimizer to add up: the
+// split-K slices of its weight-gradient GEMM, or the fused head's slices.
+static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l) {
+  if (l == L - 1 && mlp_fused_head(L, layers)) return dl::head_xent_slices(B);
+  return plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B).splits;
+}
+
 static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
                          size_t* rl_off, size_t* part_off) {
   size_t off = 0;
@@ -476,8 +489,10 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
   off += align_up((size_t)B * 4);
   for (int l = 0; l < L; ++l) {
     part_off[l] = off;
-    const Plan p = plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B);
-    off += splitk_bytes(p, layers[l].out, layers[l].in);
+    const int64_t S = mlp_slices(B, L, layers, l);
+    if (S > 1)
+      off += align_up((size_t)S * layers[l].out * layers[l].in * 4) +
+             align_up((size_t)S * layers[l].out * 4);
   }
   return off;
 }
@@ -542,18 +557,41 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   const int64_t C = layers[L - 1].out;
   hipError_t e;
 
+  // With a narrow last layer the logits never reach HBM: one kernel runs its
+  // forward, the softmax-xent and its vjp (dX written over Y[L-2], dW / db as
+  // slices for the optimizer).
+  const bool fused = mlp_fused_head(L, layers);
+  const int last_gemm = fused ? L - 2 : L - 1;
   // forward
-  for (int l = 0; l < L; ++l) {
+  for (int l = 0; l <= last_gemm; ++l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
     e = fwd_gemm(DL_F32, ly.act, B, ly.in, ly.out, in, ly.W, ly.b, Y[l], nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (forward)");
   }
-  // loss + dlogits (in place over the logits)
-  e = timed("xent", s, [&] { return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s); });
-  if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
+  if (fused) {
+    const dl_layer_t& ly = layers[L - 1];
+    const int64_t S = dl::head_xent_slices(B);
+    // one slice (B <= 32): straight into dW / db, where the optimizer reads it
+    char* pb = base + part_off[L - 1];
+    float* dWp = S > 1 ? reinterpret_cast<float*>(pb) : ly.dW;
+    float* dbp = S > 1 ? reinterpret_cast<float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))
+                       : ly.db;
+    const float* H = L > 1 ? Y[L - 2] : X;
+    float* dH = L > 1 ? Y[L - 2] : nullptr;
+    const int prev_act = L > 1 ? layers[L - 2].act : DL_ACT_IDENTITY;
+    e = timed("head_xent", s, [&] {
+      return dl::launch_head_xent(B, (int)ly.in, (int)ly.out, H, dH, prev_act, ly.W, ly.b, labels,
+                                  row_loss, dWp, dbp, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (head)");
+  } else {
+    // loss + dlogits (in place over the logits)
+    e = timed("xent", s, [&] { return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s); });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
+  }
   // backward
-  for (int l = L - 1; l >= 0; --l) {
+  for (int l = last_gemm; l >= 0; --l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
     e = dw_gemm(DL_F32, B, ly.in, ly.out, Y[l], in, ly.dW, ly.db, base + part_off[l], s,
@@ -571,7 +609,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   int64_t blocks = 0;
   for (int l = 0; l < L; ++l) {
     const dl_layer_t& ly = layers[l];
-    const Plan p = plan_gemm(DL_F32, dl::EPI_DW, ly.out, ly.in, B);
+    const int64_t S = mlp_slices(B, L, layers, l);
     char* pb = base + part_off[l];
     float* ws_[2] = {ly.W, ly.b};
     float* gs_[2] = {ly.dW, ly.db};
@@ -579,7 +617,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     float* vs_[2] = {ly.vW, ly.vb};
     const int64_t ns_[2] = {ly.out * ly.in, ly.out};
     const float* ps_[2] = {reinterpret_cast<float*>(pb),
-                           reinterpret_cast<float*>(pb + align_up((size_t)p.splits * ly.out * ly.in * 4))};
+                           reinterpret_cast<float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))};
     for (int t = 0; t < 2; ++t) {
       const int k = segs.count++;
       segs.start_block[k] = blocks;
@@ -588,15 +626,20 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
       segs.g[k] = gs_[t];
       segs.m[k] = ms_[t];
       segs.v[k] = vs_[t];
-      segs.splits[k] = p.splits;
-      segs.part[k] = p.splits > 1 ? ps_[t] : nullptr;
+      segs.splits[k] = (int)S;
+      segs.part[k] = S > 1 ? ps_[t] : nullptr;
       segs.part_stride[k] = ns_[t];
       segs.g_out[k] = gs_[t];
-      const int64_t per = p.splits > 1 ? dl::kOptSplitElemsPerBlock : dl::kOptElemsPerBlock;
+      const int64_t per = dl::opt_elems_per_block((int)S);
       blocks += (ns_[t] + per - 1) / per;
     }
   }
   segs.start_block[segs.count] = blocks;
+  if (fused) {  // the loss mean rides on the optimizer launch
+    segs.row_loss = row_loss;
+    segs.rows = B;
+    segs.loss = loss;
+  }
   const dl::OptConsts oc = opt->kind == DL_OPT_ADAMW
                                ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
                                             opt->weight_decay, opt->step)

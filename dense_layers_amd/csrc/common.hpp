@@ -384,6 +384,17 @@ hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s);
+// Fixed-order float64 mean of the per-row losses (one workgroup).
+hipError_t launch_loss_mean(int64_t B, const float* row_loss, float* loss, hipStream_t s);
+// Narrow classifier head of the MLP step (C <= 16 classes, K <= 256 inputs):
+// last Linear + softmax-xent + its vjp in one pass; dH (may alias H, or null
+// for a single-layer network) receives (W^T g) * act'(H); dW / db leave as
+// head_xent_slices(B) partial slices [S][C][K] and [S][C].
+bool head_xent_fits(int64_t K, int64_t C);
+int64_t head_xent_slices(int64_t B);
+hipError_t launch_head_xent(int64_t B, int K, int C, const float* H, float* dH, int prev_act,
+                            const float* W, const float* bias, const int32_t* labels,
+                            float* row_loss, float* dW_part, float* db_part, hipStream_t s);
 // Optimizer constants, each formed in double on the host and rounded once.
 struct OptConsts {
   float lr;            // SGD step
@@ -417,10 +428,21 @@ struct OptSegs {
   int64_t part_stride[kMaxSegs];
   int splits[kMaxSegs];
   float* g_out[kMaxSegs];
+  // optional: one extra workgroup (the first) writes loss = mean(row_loss[0 ..
+  // rows)) (float64, fixed order)
+  const float* row_loss;
+  int64_t rows;
+  float* loss;
 };
 constexpr int kOptBlock = 256;
 constexpr int kOptElemsPerBlock = kOptBlock * 4 * 4;  // 4 float4 per thread
 constexpr int kOptSplitElemsPerBlock = kOptBlock;      // split-K segments: 4 lanes per 4 elements
+constexpr int kOptWideSplits = 32;                     // more slices: a wave per 4 elements
+constexpr int kOptWideElemsPerBlock = kOptBlock / 16;
+inline int64_t opt_elems_per_block(int splits) {
+  return splits > kOptWideSplits ? kOptWideElemsPerBlock
+                                 : (splits > 1 ? kOptSplitElemsPerBlock : kOptElemsPerBlock);
+}
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);
 

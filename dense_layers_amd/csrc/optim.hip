@@ -149,14 +149,89 @@ __device__ __forceinline__ void opt_split_block(int64_t n, int64_t base, float* 
   }
 }
 
+// Segments with many slices (more than kOptWideSplits): a whole wave per
+// 4-element group, lane q summing slices q, q+64, ... in order, then a fixed
+// 64-lane shuffle tree; four groups per workgroup.
+template <int KIND>
+__device__ __forceinline__ void opt_wide_split_block(int64_t n, int64_t base,
+                                                     float* __restrict__ w, const GradSrc& gs,
+                                                     float* __restrict__ m, float* __restrict__ v,
+                                                     const AdamParams& p, bool vec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t e0 = base + (int64_t)(threadIdx.x >> 6) * 4;
+  float g[4] = {0.f, 0.f, 0.f, 0.f};
+  if (vec && e0 + 3 < n) {
+#pragma unroll 2
+    for (int k = lane; k < gs.splits; k += 64) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gs.part + (int64_t)k * gs.stride + e0);
+      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
+    }
+  } else {
+    for (int k = lane; k < gs.splits; k += 64)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e0 + e < n) g[e] += gs.part[(int64_t)k * gs.stride + e0 + e];
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] += __shfl_xor(g[e], o);
+  if (lane >= 4) return;
+  const int64_t i = e0 + lane;
+  if (i >= n) return;
+  const float gi = g[lane];
+  gs.out[i] = gi;
+  if (KIND == 0) {
+    w[i] -= p.lr * gi;
+  } else {
+    float we = w[i], me = m[i], ve = v[i];
+    adam_elem(we, gi, me, ve, p);
+    w[i] = we; m[i] = me; v[i] = ve;
+  }
+}
+
 // One launch over several arrays: block b belongs to the segment whose
-// prefix range [start_block[s], start_block[s+1]) contains it.  Segments with
-// split-K slices use kSplitElemsPerBlock elements per block, others
-// kOptElemsPerBlock.
+// prefix range [start_block[s], start_block[s+1]) contains it; a segment's
+// elements per block are opt_elems_per_block(splits).
+// Mean of the per-row losses by one workgroup: thread t takes rows t, t+256,
+// ... in chunks of 8 (loaded together, added in order, float64), then a fixed
+// shuffle tree and the 4 waves in order.
+__device__ __forceinline__ void loss_mean_block(int64_t rows, const float* __restrict__ row_loss,
+                                                float* __restrict__ loss) {
+  __shared__ double red[kOptBlock / 64];
+  double acc = 0.0;
+  for (int64_t i0 = threadIdx.x; i0 < rows; i0 += 8 * kOptBlock) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + (int64_t)u * kOptBlock;
+      x[u] = i < rows ? row_loss[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)x[u];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kOptBlock / 64; ++w) t += red[w];
+    loss[0] = (float)(t / (double)rows);
+  }
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(kOptBlock)
 opt_multi_kernel(OptSegs segs, AdamParams p) {
-  const int64_t b = blockIdx.x;
+  int64_t b = blockIdx.x;
+  if (segs.rows > 0) {  // workgroup 0 (dispatched first) takes the loss mean
+    if (b == 0) {
+      loss_mean_block(segs.rows, segs.row_loss, segs.loss);
+      return;
+    }
+    --b;
+  }
   int s = 0;
   while (s + 1 < segs.count && b >= segs.start_block[s + 1]) ++s;
   const int64_t local = b - segs.start_block[s];
@@ -164,8 +239,12 @@ opt_multi_kernel(OptSegs segs, AdamParams p) {
   if (gs.splits > 1) {
     const bool vec = ((reinterpret_cast<uintptr_t>(gs.part) |
                        static_cast<uintptr_t>(gs.stride * 4)) & 15) == 0;
-    opt_split_block<KIND>(segs.n[s], local * kSplitElemsPerBlock, segs.w[s], gs, segs.m[s],
-                          segs.v[s], p, vec);
+    if (gs.splits > kOptWideSplits)
+      opt_wide_split_block<KIND>(segs.n[s], local * kOptWideElemsPerBlock, segs.w[s], gs,
+                                 segs.m[s], segs.v[s], p, vec);
+    else
+      opt_split_block<KIND>(segs.n[s], local * kSplitElemsPerBlock, segs.w[s], gs, segs.m[s],
+                            segs.v[s], p, vec);
     return;
   }
   uintptr_t addr = reinterpret_cast<uintptr_t>(segs.w[s]) | reinterpret_cast<uintptr_t>(gs.g);
@@ -195,7 +274,7 @@ hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
 }
 
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& p, hipStream_t s) {
-  const int64_t blocks = segs.start_block[segs.count];
+  const int64_t blocks = segs.start_block[segs.count] + (segs.rows > 0 ? 1 : 0);
   if (blocks <= 0) return hipSuccess;
   if (kind == 0)
     hipLaunchKernelGGL(opt_multi_kernel<0>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, segs, p);

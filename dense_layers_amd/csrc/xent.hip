@@ -231,6 +231,10 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
+  return launch_loss_mean(B, row_loss, loss, s);
+}
+
+hipError_t launch_loss_mean(int64_t B, const float* row_loss, float* loss, hipStream_t s) {
   hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(kMeanThreads), 0, s, B, row_loss, loss);
   return hipGetLastError();
 }

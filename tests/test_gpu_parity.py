@@ -549,6 +549,32 @@ def test_head_xent_reduced_batch(dl):
     _trajectory(dl, si.WORKLOADS["head_xent"], 2, {1, 2}, batch=256)
 
 
+# The narrow-head path of the step (last Linear + softmax-xent + its vjp in
+# one kernel, for <= 16 classes and <= 256 inputs) at its corners, and the
+# unfused path just past them.
+_HEADS = {
+    "single_layer": si.Workload("head_single", 21, 100, [64, 10], [O.ACT_IDENTITY], "kaiming",
+                                "uniform001", "f32", si.ADAMW),
+    "max_head_ragged": si.Workload("head_max", 22, 77, [96, 256, 16], [O.ACT_RELU, O.ACT_IDENTITY],
+                                   "kaiming", "uniform001", "f32", si.SGD),
+    "one_slice": si.Workload("head_small_batch", 23, 20, [50, 30, 7], [O.ACT_RELU, O.ACT_IDENTITY],
+                             "kaiming", "uniform001", "f32", si.ADAMW),
+    "many_tiles": si.Workload("head_tiles", 24, 5000, [40, 64, 12], [O.ACT_RELU, O.ACT_IDENTITY],
+                              "kaiming", "uniform001", "f32", si.ADAMW),
+    "identity_hidden": si.Workload("head_linear", 25, 200, [30, 20, 5],
+                                   [O.ACT_IDENTITY, O.ACT_IDENTITY], "kaiming", "uniform001", "f32",
+                                   si.SGD),
+    "unfused_17_classes": si.Workload("head_17", 26, 300, [60, 40, 17],
+                                      [O.ACT_RELU, O.ACT_IDENTITY], "kaiming", "uniform001", "f32",
+                                      si.SGD),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_HEADS))
+def test_mlp_step_head_shapes(dl, case):
+    _trajectory(dl, _HEADS[case], 2, {1, 2})
+
+
 def test_mlp_step_bit_reproducible(dl):
     w = si.WORKLOADS["mlp_adamw"]
     inp = si.generate(w)
