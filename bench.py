@@ -80,14 +80,32 @@ class MLPBench:
                           [torch.from_numpy(a).to(dev) for a in inp.b], w.acts, w.batch,
                           adamw=(w.optim.kind == "adamw"))
         self.t = 0
+        self.graph = None
+        self.device_step = False
+
+    def _opt(self):
+        o = self.w.optim
+        kind = self.dl.OPT_ADAMW if o.kind == "adamw" else self.dl.OPT_SGD
+        return kind, dict(lr=o.lr, beta1=o.beta1, beta2=o.beta2, eps=o.eps,
+                          weight_decay=o.weight_decay)
+
+    def use_graph(self):
+        """Capture the step once (after one eager step) and replay it from
+        then on; AdamW then counts its steps on the device."""
+        kind, opt = self._opt()
+        self.device_step = kind == self.dl.OPT_ADAMW
+        self.dl.mlp_train_step(self.mlp, self.X, self.y, kind, device_step=self.device_step,
+                               **opt)
+        self.graph = self.dl.StepGraph(self.mlp, self.X, self.y, kind, **opt)
 
     def step(self):
-        o = self.w.optim
+        if self.graph is not None:
+            self.graph.replay()
+            return
+        kind, opt = self._opt()
         self.t += 1
-        kind = self.dl.OPT_ADAMW if o.kind == "adamw" else self.dl.OPT_SGD
-        self.dl.mlp_train_step(self.mlp, self.X, self.y, kind, lr=o.lr, beta1=o.beta1,
-                               beta2=o.beta2, eps=o.eps, weight_decay=o.weight_decay,
-                               step=self.t)
+        self.dl.mlp_train_step(self.mlp, self.X, self.y, kind, step=self.t,
+                               device_step=self.device_step, **opt)
 
     def flops(self):
         return self.w.gemm_flops_per_step()
@@ -284,6 +302,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prof-steps", type=int, default=20)
+    ap.add_argument("--graph", action="store_true",
+                    help="MLP workloads: time replays of the step captured as a stream graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
@@ -312,6 +332,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.graph:
+        if not hasattr(bench, "use_graph"):
+            print(f"--graph applies to the MLP step workloads, not {args.config}", file=sys.stderr)
+            sys.exit(2)
+        bench.use_graph()
     for _ in range(warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -327,6 +352,8 @@ def main():
     gpu_ms_step = ev0.elapsed_time(ev1) / steps
     step_tflops = bench.flops() / (ms_step * 1e-3) / 1e12
 
+    if args.graph:
+        bench.graph = None  # the per-launch timing runs the same step eagerly
     stages = profile_stages(dl, bench, max(1, min(args.prof_steps, steps)))
     dom = max(stages, key=lambda x: x["ms"])
     peak = PEAK_BF16_MFMA if w.dtype == "bf16" else PEAK_FP32_MFMA
@@ -362,7 +389,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dims": w.dims,
                    "optimizer": None if w.optim is None else w.optim.kind,
-                   "gemm_flops_per_step": bench.flops()},
+                   "gemm_flops_per_step": bench.flops(),
+                   "graph_replay": bool(args.graph)},
         "roofline": roofline,
         "stages": stages,
         "kernel_source_hash": kernel_source_hash(),

@@ -56,7 +56,7 @@ class DLOpt(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("step", ctypes.c_int64)]
+                ("step", ctypes.c_int64), ("step_dev", ctypes.c_void_p)]
 
 
 def _sig(name, res, args):
@@ -357,6 +357,8 @@ class MLP:
         self.ws = _workspace(need, dev)
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.step_count = 0
+        # steps taken, on the device (AdamW with device_step=True)
+        self.step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
 
 
 def mlp_train_step_workspace_size(B: int, table) -> int:
@@ -366,16 +368,45 @@ def mlp_train_step_workspace_size(B: int, table) -> int:
 def mlp_train_step(mlp: MLP, X: torch.Tensor, labels: torch.Tensor, kind: int = OPT_SGD,
                    lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
                    eps: float = 1e-8, weight_decay: float = 0.0,
-                   step: Optional[int] = None) -> torch.Tensor:
+                   step: Optional[int] = None, device_step: bool = False) -> torch.Tensor:
     """One forward / softmax-xent / backward / optimizer step; returns the
-    device loss tensor (computed before the update)."""
+    device loss tensor (computed before the update).  With device_step the
+    AdamW step count lives in mlp.step_dev and advances on the device (the
+    form a captured graph can replay)."""
     _dev(X, "X", torch.float32, (mlp.batch, mlp.W[0].shape[1]))
     _dev(labels, "labels", torch.int32, (mlp.batch,))
     if step is None:
         step = mlp.step_count + 1
     mlp.step_count = step
-    opt = DLOpt(kind, lr, beta1, beta2, eps, weight_decay, step)
+    opt = DLOpt(kind, lr, beta1, beta2, eps, weight_decay, step,
+                _ptr(mlp.step_dev) if device_step else None)
     _check(_c["mlp_train_step"](_stream(X), mlp.batch, mlp.L, mlp.table, _ptr(X),
                                 _ptr(labels), ctypes.byref(opt), _ptr(mlp.loss), _ptr(mlp.ws),
                                 0 if mlp.ws is None else mlp.ws.numel()))
     return mlp.loss
+
+
+class StepGraph:
+    """One whole training step captured as a stream graph and replayed: the
+    launches of mlp_train_step are recorded once (on a side stream, as torch
+    requires) and replay() issues them again with one call.  X and labels are
+    the tensors the graph reads, so new data goes in by copying into them.
+    AdamW runs with the device step count, so every replay is the next step.
+    The library allocates nothing and records no memory fills, so the graph
+    holds only its kernels."""
+
+    def __init__(self, mlp: MLP, X: torch.Tensor, labels: torch.Tensor, kind: int = OPT_SGD,
+                 **opt):
+        self.mlp, self.X, self.labels = mlp, X, labels
+        self.kind, self.opt = kind, opt
+        self.graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=X.device)
+        side.wait_stream(torch.cuda.current_stream(X.device))
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(self.graph, stream=side):
+                mlp_train_step(mlp, X, labels, kind, device_step=(kind == OPT_ADAMW), **opt)
+        torch.cuda.current_stream(X.device).wait_stream(side)
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.mlp.loss

@@ -386,6 +386,10 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
 static dl::OptConsts opt_consts(double lr, double beta1, double beta2, double eps, double wd,
                                 int64_t t) {
   dl::OptConsts c;
+  memset(&c, 0, sizeof(c));
+  c.lr_d = lr;
+  c.beta1_d = beta1;
+  c.beta2_d = beta2;
   c.lr = (float)lr;
   c.decay = (float)(1.0 - lr * wd);
   c.b1 = (float)beta1;
@@ -514,7 +518,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   if (!X || !labels || !opt || !loss) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: X, labels, opt and loss are required");
   if (opt->kind != DL_OPT_SGD && opt->kind != DL_OPT_ADAMW)
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: bad optimizer kind %d", opt->kind);
-  if (opt->kind == DL_OPT_ADAMW && opt->step < 1)
+  if (opt->kind == DL_OPT_ADAMW && opt->step_dev == nullptr && opt->step < 1)
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: AdamW step counts from 1");
   if (opt->kind == DL_OPT_ADAMW && !betas_ok(opt->beta1, opt->beta2))
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: betas must be in [0, 1)");
@@ -550,6 +554,11 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
+  const bool dev_step = opt->kind == DL_OPT_ADAMW && opt->step_dev != nullptr;
+  if (dev_step) {
+    hipError_t et = dl::launch_step_tick(opt->step_dev, s);
+    if (et != hipSuccess) return hip_fail(et, "mlp_train_step (step count)");
+  }
   float* Y[16];
   for (int l = 0; l < n_layers; ++l) Y[l] = reinterpret_cast<float*>(base + y_off[l]);
   float* row_loss = reinterpret_cast<float*>(base + rl_off);
@@ -640,10 +649,11 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     segs.rows = B;
     segs.loss = loss;
   }
-  const dl::OptConsts oc = opt->kind == DL_OPT_ADAMW
-                               ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
-                                            opt->weight_decay, opt->step)
-                               : opt_consts(opt->lr, 0, 0, 0, 0, 0);
+  dl::OptConsts oc = opt->kind == DL_OPT_ADAMW
+                         ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
+                                      opt->weight_decay, dev_step ? 1 : opt->step)
+                         : opt_consts(opt->lr, 0, 0, 0, 0, 0);
+  if (dev_step) oc.step_dev = opt->step_dev;
   e = timed(opt->kind == DL_OPT_ADAMW ? "adamw_multi" : "sgd_multi", s,
             [&] { return dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, oc, s); });
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");

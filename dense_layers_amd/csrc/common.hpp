@@ -404,7 +404,13 @@ struct OptConsts {
   float step_size;     // lr / (1 - beta1^t)
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
   float eps;
+  // AdamW with a device step count: t = *step_dev, and step_size and
+  // inv_sqrt_bc2 are formed on the device from these doubles instead
+  const int64_t* step_dev;
+  double lr_d, beta1_d, beta2_d;
 };
+// Adds 1 to a device step count (one lane, a vector store).
+hipError_t launch_step_tick(int64_t* step_dev, hipStream_t s);
 hipError_t launch_sgd(int64_t n, float* w, const float* g, const OptConsts& c,
                       hipStream_t s);
 hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,

@@ -53,7 +53,10 @@ __device__ __forceinline__ f32x4 grad4(const GradSrc& s, int64_t i) {
   return acc;
 }
 
-// Process elements [base, base + kOptElemsPerBlock) of one array.
+// Process elements [base, base + kOptElemsPerBlock) of one array.  In the
+// full-block vector path every load of the thread's four float4 groups (w, g
+// and for AdamW m, v) is issued before the first store, so a thread keeps 8
+// or 16 loads in flight instead of waiting once per group.
 template <int KIND>
 __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __restrict__ w,
                                           const GradSrc& gs, float* __restrict__ m,
@@ -61,26 +64,38 @@ __device__ __forceinline__ void opt_block(int64_t n, int64_t base, float* __rest
                                           bool vec) {
   const int64_t end = min(n, base + (int64_t)kOptElemsPerBlock);
   if (vec && end - base == kOptElemsPerBlock) {
+    f32x4 wv[4], gv[4], mv[4], vv[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
-      f32x4 wv = *reinterpret_cast<const f32x4*>(w + i);
-      const f32x4 gv = grad4(gs, i);
+      wv[it] = *reinterpret_cast<const f32x4*>(w + i);
+      if (gs.splits <= 1) gv[it] = *reinterpret_cast<const f32x4*>(gs.g + i);
+      if (KIND) {
+        mv[it] = *reinterpret_cast<const f32x4*>(m + i);
+        vv[it] = *reinterpret_cast<const f32x4*>(v + i);
+      }
+    }
+    if (gs.splits > 1) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        gv[it] = grad4(gs, base + ((int64_t)it * kOptBlock + threadIdx.x) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
       if (KIND == 0) {
-        wv -= p.lr * gv;
+        wv[it] -= p.lr * gv[it];
       } else {
-        f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
-        f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float we = wv[e], me = mv[e], ve = vv[e];
-          adam_elem(we, gv[e], me, ve, p);
-          wv[e] = we; mv[e] = me; vv[e] = ve;
+          float we = wv[it][e], me = mv[it][e], ve = vv[it][e];
+          adam_elem(we, gv[it][e], me, ve, p);
+          wv[it][e] = we; mv[it][e] = me; vv[it][e] = ve;
         }
-        *reinterpret_cast<f32x4*>(m + i) = mv;
-        *reinterpret_cast<f32x4*>(v + i) = vv;
+        *reinterpret_cast<f32x4*>(m + i) = mv[it];
+        *reinterpret_cast<f32x4*>(v + i) = vv[it];
       }
-      *reinterpret_cast<f32x4*>(w + i) = wv;
+      *reinterpret_cast<f32x4*>(w + i) = wv[it];
     }
   } else {
     for (int64_t i = base + threadIdx.x; i < end; i += kOptBlock) {
@@ -221,9 +236,22 @@ __device__ __forceinline__ void loss_mean_block(int64_t rows, const float* __res
   }
 }
 
+// The bias corrections of step t, in double, rounded once (the host forms
+// the same expressions from its own step count).
+__device__ __forceinline__ void device_step_consts(AdamParams& p) {
+  const double t = (double)*p.step_dev;
+  p.step_size = (float)(p.lr_d / (1.0 - pow(p.beta1_d, t)));
+  p.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(p.beta2_d, t)));
+}
+
+__global__ void step_tick_kernel(int64_t* step_dev) {
+  if (threadIdx.x == 0) step_dev[0] = step_dev[0] + 1;
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(kOptBlock)
 opt_multi_kernel(OptSegs segs, AdamParams p) {
+  if (KIND == 1 && p.step_dev != nullptr) device_step_consts(p);
   int64_t b = blockIdx.x;
   if (segs.rows > 0) {  // workgroup 0 (dispatched first) takes the loss mean
     if (b == 0) {
@@ -270,6 +298,11 @@ hipError_t launch_adamw(int64_t n, float* w, const float* g, float* m, float* v,
                     reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v)) & 15) == 0;
   hipLaunchKernelGGL(opt_single_kernel<1>, dim3((unsigned)blocks), dim3(kOptBlock), 0, s, n, w, g,
                      m, v, p, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_tick(int64_t* step_dev, hipStream_t s) {
+  hipLaunchKernelGGL(step_tick_kernel, dim3(1), dim3(64), 0, s, step_dev);
   return hipGetLastError();
 }
 

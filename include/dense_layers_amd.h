@@ -247,7 +247,14 @@ typedef struct dl_layer {
 typedef struct dl_opt {
   int32_t kind;     /* enum dl_opt_kind */
   double lr, beta1, beta2, eps, weight_decay;  /* betas/eps/wd: AdamW only */
-  int64_t step;     /* AdamW step t >= 1 */
+  int64_t step;     /* AdamW step t >= 1 (ignored when step_dev is set) */
+  /* AdamW, optional: device int64 [1] holding the number of steps taken.
+   * When set, each call first adds 1 to it on the device (in stream order)
+   * and the update uses that value as t, its bias corrections formed on the
+   * device in double exactly as the host forms them from `step`.  This makes
+   * the whole step replayable from a captured stream graph, which cannot see
+   * a host-side step count.  Caller-owned; NULL to use `step`. */
+  int64_t* step_dev;
 } dl_opt_t;
 
 /*
