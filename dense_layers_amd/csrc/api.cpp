@@ -76,8 +76,9 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 
 // ---- GEMM planning ----------------------------------------------------------
-// float32 tiles {0: 128x128x16, 1: 64x64x32}: the large one when it alone
-// yields at least one workgroup per CU (256), otherwise the small one.
+// float32 tiles {0: 128x128x16, 1: 64x64x32, 2: 64x128x32 with 8 waves}:
+// 128x128 when it alone yields at least one workgroup per CU (256); else, for
+// forward and dX products, 64x128 when that does; otherwise 64x64.
 // bf16 tiles {0: 256x256, 1: 128x128} of the direct-to-LDS kernel (K step 64):
 // 256x256 for forward / dX products with at least one such tile per CU,
 // 128x128 otherwise; operands that kernel cannot take (unaligned, K not a
@@ -99,7 +100,8 @@ void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
     bm = bn = tile == 0 ? 256 : 128;
     bk = 64;
   } else {
-    bm = bn = tile == 0 ? 128 : 64;
+    bm = tile == 0 ? 128 : 64;
+    bn = tile == 1 ? 64 : 128;
     bk = tile == 0 ? 16 : 32;
   }
 }
@@ -113,7 +115,9 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
   if (tiles < kCUs || (dtype == DL_BF16 && epi == dl::EPI_DW)) {
     p.tile = 1;
-    tile_shape(dtype, 1, bm, bn, bk);
+    if (dtype == DL_F32 && epi != dl::EPI_DW && ceil_div(M, 64) * ceil_div(N, 128) >= kCUs)
+      p.tile = 2;
+    tile_shape(dtype, p.tile, bm, bn, bk);
     tiles = ceil_div(M, bm) * ceil_div(N, bn);
   }
   if (epi == dl::EPI_DW && tiles < 2 * kCUs) {

@@ -338,11 +338,14 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
 }  // namespace
 
 // tile 0: 128x128, K step 16 (4 waves of 64x64); tile 1: 64x64, K step 32
-// (4 waves of 32x32)
+// (4 waves of 32x32); tile 2: 64x128, K step 32 (8 waves of 32x32: one
+// workgroup loads 64 + 128 operand rows per K step where two 64x64 tiles
+// load 256)
 hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
     case 0: return dispatch_layout<128, 128, 16, 2, 2>(d, s);
     case 1: return dispatch_layout<64, 64, 32, 2, 2>(d, s);
+    case 2: return dispatch_layout<64, 128, 32, 2, 4>(d, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -38,7 +38,8 @@ def _layer(seed, B, n_in, n_out, bias=True):
 # ------------------------------------------------------------------ forward
 
 FWD_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (300, 1000, 129),
-              (513, 256, 1000), (256, 1024, 4096), (8192, 128, 10), (33, 4100, 70)]
+              (513, 256, 1000), (256, 1024, 4096), (8192, 128, 10), (33, 4100, 70),
+              (8200, 300, 250)]
 
 
 @pytest.mark.parametrize("shape", FWD_SHAPES)
@@ -82,7 +83,7 @@ def test_dense_fwd_on_side_stream(dl):
 
 VJP_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (8192, 784, 256),
               (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000), (700, 1000, 300),
-              (2000, 1000, 1000)]
+              (2000, 1000, 1000), (8200, 250, 300)]
 
 
 @pytest.mark.parametrize("shape", VJP_SHAPES)
