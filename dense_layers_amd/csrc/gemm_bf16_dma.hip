@@ -142,6 +142,224 @@ __device__ __forceinline__ void sched_interleave() {
   if (NV > kMfma) __builtin_amdgcn_sched_group_barrier(0x020, NV > kMfma ? NV - kMfma : 1, 0);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- epilogue ------------------------------------------------------------------
+// The matrix cores form each 32x32 block transposed (the B fragment is the
+// MFMA's first operand), so lane l holds tile row 32 i + l % 32 of block
+// (i, j) and, in register group g (registers 4 g .. 4 g + 3), the 4
+// consecutive columns 8 g + 4 h + (0..3), h = l / 32.  Exchanging groups
+// 0 <-> 2 and 1 <-> 3 between the wave halves (v_permlane32_swap) leaves
+// each lane with the 16 consecutive columns 16 h + c, c = 0..15, of its row,
+// column c in register col_reg(c).
+//
+// Each wave then finishes its own WM x WN sub-tile through a private LDS
+// region (the stage buffers, free after the main loop): lanes write their
+// 16-value row pieces, and read back whole rows, so that every global store
+// instruction writes 8 rows x 128 bytes (bf16) or 4 rows x 256 bytes
+// (float32).  Row r of the region keeps its 16-byte pieces at position
+// piece ^ (r mod pieces-per-row), which makes both the column-wise writes and
+// the row-wise reads free of bank conflicts.  No workgroup barrier is needed
+// beyond the one that retires the stage buffers.
+__device__ __forceinline__ int col_reg(int c) { return (c & 3) | ((c & 4) << 1) | ((c & 8) >> 1); }
+
+template <int FM, int FN>
+__device__ __forceinline__ void swap_halves(f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][r]),
+                                                        __float_as_uint(acc[i][j][r + 8]), false,
+                                                        false);
+        acc[i][j][r] = __uint_as_float(p[0]);
+        acc[i][j][r + 8] = __uint_as_float(p[1]);
+      }
+}
+
+// One lane's row and first column of block (i, j) in the output.
+struct BlockPos {
+  int row, col;
+};
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ BlockPos block_pos(int tm, int tn, int wm, int wn, int i, int j,
+                                              int lane) {
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  return {tm * BM + wm * WM + i * 32 + (lane & 31), tn * BN + wn * WN + j * 32 + 16 * (lane >> 5)};
+}
+
+// The 16 saved bf16 activations at a lane's block position (zeros outside
+// the matrix), as they are stored.
+__device__ __forceinline__ void load_mask16(u32x4 (&m)[2], const bf16_t* __restrict__ src,
+                                            int64_t ld, BlockPos p, int M, int N, bool vec) {
+  m[0] = u32x4{0u, 0u, 0u, 0u};
+  m[1] = m[0];
+  if (p.row >= M) return;
+  const bf16_t* q = src + (int64_t)p.row * ld + p.col;
+  if (vec && p.col + 16 <= N) {
+    m[0] = *reinterpret_cast<const u32x4*>(q);
+    m[1] = *reinterpret_cast<const u32x4*>(q + 8);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      if (p.col + c < N) m[c >> 3][(c >> 1) & 3] |= (uint32_t)q[c] << (16 * (c & 1));
+  }
+}
+__device__ __forceinline__ float mask_at(const u32x4 (&m)[2], int c) {
+  const uint32_t w = m[c >> 3][(c >> 1) & 3];
+  return __uint_as_float((c & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Orders this wave's LDS accesses (no other wave touches its region).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes a lane's 16 values (columns 16 h .. 16 h + 15 of block column j, row
+// r of the region) in storage format.
+template <typename TO, int WN>
+__device__ __forceinline__ void region_put(char* region, int r, int j, int h, const float (&v)[16]) {
+  constexpr int ES = sizeof(TO), PPR = WN * ES / 16;  // 16-byte pieces per row
+  char* row = region + r * (WN * ES);
+  if constexpr (ES == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = 4 * j + 2 * h + k;
+      const u32x4 x = {pack_bf16x2(v[8 * k], v[8 * k + 1]), pack_bf16x2(v[8 * k + 2], v[8 * k + 3]),
+                       pack_bf16x2(v[8 * k + 4], v[8 * k + 5]),
+                       pack_bf16x2(v[8 * k + 6], v[8 * k + 7])};
+      *reinterpret_cast<u32x4*>(row + ((q ^ (r % PPR)) * 16)) = x;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = 8 * j + 4 * h + k;
+      *reinterpret_cast<f32x4*>(row + ((q ^ (r % PPR)) * 16)) =
+          f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+    }
+  }
+}
+
+// Copies region rows 0 .. ROWS - 1 to out rows row0 .., columns col0 ..
+// col0 + WN - 1 (clipped to M x N), one 16-byte piece per lane per step.
+template <typename TO, int WN, int ROWS>
+__device__ __forceinline__ void region_flush(const char* region, TO* __restrict__ out, int64_t ld,
+                                             int row0, int col0, int M, int N, bool vec, int lane) {
+  constexpr int ES = sizeof(TO), PPR = WN * ES / 16, EPP = 16 / ES, RPS = 64 / PPR;
+  const int p = lane % PPR;
+  const int col = col0 + p * EPP;
+#pragma unroll
+  for (int t = 0; t < ROWS / RPS; ++t) {
+    const int r = t * RPS + lane / PPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(region + r * (WN * ES) + ((p ^ (r % PPR)) * 16));
+    const int row = row0 + r;
+    if (row >= M || col >= N) continue;
+    TO* q = out + (int64_t)row * ld + col;
+    if (vec && col + EPP <= N) {
+      *reinterpret_cast<u32x4*>(q) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        if (col + e >= N) break;
+        if constexpr (ES == 2) q[e] = (bf16_t)(x[e >> 1] >> (16 * (e & 1)));
+        else q[e] = __uint_as_float(x[e]);
+      }
+    }
+  }
+}
+
+// Epilogue of one wave, on accumulators already passed through swap_halves:
+// forward (bias, act; with ZOUT also Z = acc + bias), dX (times act' of the
+// saved activations in `mk`, block b = i FN + j), or dW (float32, to C or to
+// split `split`'s partial).  `region` is this wave's LDS area of kRegion
+// bytes; the wave's rows go through it in rounds of IR block rows.
+template <int BM, int BN, int WGM, int WGN, int EPI, int ACT, bool ZOUT, int FM, int FN, int NMK,
+          int kRegion>
+__device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], const GemmDesc& d,
+                                               int tm, int tn, int split, int wm, int wn, int lane,
+                                               bool vec, const u32x4 (&mk)[NMK][2], char* region) {
+  using TO = typename std::conditional<EPI == EPI_DW, float, bf16_t>::type;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int ES = sizeof(TO);
+  static_assert(WN == 32 * FN && WM == 32 * FM, "wave tile");
+  constexpr int NOUT = ZOUT ? 2 : 1;
+  constexpr int kOutBytes = kRegion / NOUT;  // region part of one output
+  constexpr int IR = kOutBytes / (32 * WN * ES) < FM ? kOutBytes / (32 * WN * ES) : FM;
+  static_assert(IR >= 1 && FM % IR == 0, "region too small for one block row");
+  constexpr bool kMasked = EPI == EPI_DX && ACT != ACT_IDENTITY;
+  static_assert(!kMasked || NMK == FM * FN, "one mask block per accumulator block");
+  const int M = d.M, N = d.N;
+  const int h = lane >> 5, l32 = lane & 31;
+  TO* __restrict__ out = static_cast<TO*>(d.C);
+  int64_t ld = d.ldc;
+  if (EPI == EPI_DW && d.splits > 1) {
+    out = reinterpret_cast<TO*>(d.partial + (int64_t)split * M * N);
+    ld = N;
+  }
+  const int row0 = tm * BM + wm * WM, col0 = tn * BN + wn * WN;
+
+  float bias[FN][16];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int c = 0; c < 16; ++c) bias[j][c] = 0.f;
+  if (EPI == EPI_FWD && d.bias != nullptr) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col0 + 32 * j + 16 * h;
+      if (vec && col + 16 <= N && (reinterpret_cast<uintptr_t>(d.bias) & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(d.bias + col + 4 * k);
+          bias[j][4 * k] = x[0]; bias[j][4 * k + 1] = x[1];
+          bias[j][4 * k + 2] = x[2]; bias[j][4 * k + 3] = x[3];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (col + c < N) bias[j][c] = d.bias[col + c];
+      }
+    }
+  }
+
+  TO* __restrict__ zout = static_cast<TO*>(d.Z);
+#pragma unroll
+  for (int i0 = 0; i0 < FM; i0 += IR) {
+#pragma unroll
+    for (int ii = 0; ii < IR; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float v[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) v[c] = acc[i0 + ii][j][col_reg(c)];
+        if constexpr (EPI == EPI_FWD) {
+          float z[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            z[c] = v[c] + bias[j][c];
+            v[c] = act_apply(ACT, z[c]);
+          }
+          if constexpr (ZOUT) region_put<TO, WN>(region + kOutBytes, ii * 32 + l32, j, h, z);
+        } else if constexpr (kMasked) {
+          const int b = (i0 + ii) * FN + j;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) v[c] *= act_deriv(ACT, mask_at(mk[b < NMK ? b : 0], c));
+        }
+        region_put<TO, WN>(region, ii * 32 + l32, j, h, v);
+      }
+    wave_lds_order();
+    region_flush<TO, WN, IR * 32>(region, out, ld, row0 + i0 * 32, col0, M, N, vec, lane);
+    if constexpr (ZOUT)
+      region_flush<TO, WN, IR * 32>(region + kOutBytes, zout, ld, row0 + i0 * 32, col0, M, N, vec,
+                                    lane);
+    wave_lds_order();
+  }
+}
+
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
@@ -155,8 +373,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   using OB = DmaOperand<BN, BLAY, NT, BK>;
   constexpr int kStageBytes = OA::kBytes + OB::kBytes;
   constexpr int kLoads = OA::kInst + OB::kInst;  // per wave per stage
-  constexpr int kEpiBytes = stage_floats<BM, BN, WGM>() * 4;
-  constexpr int kSmem = STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes;
+  constexpr int kSmem = STAGES * kStageBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int tid = threadIdx.x;
@@ -223,7 +440,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
 
   // Fragments are double-buffered in registers (set ks & 1 holds k-step ks),
@@ -253,13 +470,20 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   constexpr int kAllowed = (STAGES - 2) * kLoads - kLast;
   auto part = [](int ks) { return ks * kMid; };
 
-  // The dX epilogue's saved activations for its first staging pass are
-  // requested before the first operand loads, so their HBM latency overlaps
-  // the pipeline fill instead of stalling the epilogue.
-  using Epi = EpiShape<BM, BN, WGM, WGN>;
-  Raw4<bf16_t> ms0[EPI == EPI_DX ? Epi::RPT : 1];
-  if (EPI == EPI_DX && d.mask_act != ACT_IDENTITY)
-    load_mask_pass<bf16_t, BM, BN, WGM, WGN>(ms0, d, tm, tn, 0, out_vec);
+  // The dX epilogue's saved activations for the first half of the wave's
+  // blocks are requested before the first operand loads, so their HBM
+  // latency overlaps the pipeline fill instead of stalling the epilogue.
+  constexpr int kMk = EPI == EPI_DX ? FM * FN : 1;
+  constexpr int kPre = EPI == EPI_DX ? (FM / 2) * FN : 0;
+  const bool masked = EPI == EPI_DX && d.mask_act != ACT_IDENTITY;
+  u32x4 mk[kMk][2];
+  if (masked) {
+#pragma unroll
+    for (int b = 0; b < kPre; ++b)
+      load_mask16(mk[b], static_cast<const bf16_t*>(d.mask_src), d.ldc,
+                  block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, b / FN, b % FN, lane), M, N,
+                  out_vec);
+  }
 
   if (nk > 0) {  // (always true for the splits the launcher forms)
 #pragma unroll
@@ -293,7 +517,10 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
     sched_interleave<kMfma, kReads, kLast>();
     __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();  // the epilogue reuses the stage buffers
+  // The repeated loads past the last stage still write LDS: let them land,
+  // and retire the stage buffers for the epilogue's per-wave regions.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
 
   if (EPI == EPI_DW && do_db) {
     const int row_base = tm * BM + wm * WM;
@@ -307,12 +534,33 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
       }
     }
   }
-  if constexpr (EPI == EPI_DX)
-    store_tile_impl<bf16_t, BM, BN, WGM, WGN, EPI, FM, FN, true>(
-        acc, reinterpret_cast<float*>(smem), d, tm, tn, split, out_vec, ms0);
-  else
-    store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn,
-                                              split, out_vec);
+  // the other half of the saved activations, requested before the
+  // accumulators are rearranged
+  if (masked) {
+#pragma unroll
+    for (int b = kPre; b < kMk; ++b)
+      load_mask16(mk[b], static_cast<const bf16_t*>(d.mask_src), d.ldc,
+                  block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, b / FN, b % FN, lane), M, N,
+                  out_vec);
+  }
+  swap_halves(acc);
+  const bool vec = out_vec != 0;
+  constexpr int kRegion = kSmem / (NT / 64);
+  char* region = smem + wave * kRegion;
+  const int act = EPI == EPI_FWD ? d.act : EPI == EPI_DX ? d.mask_act : ACT_IDENTITY;
+#define DL_EPILOGUE(A, Z)                                                                     \
+  store_epilogue<BM, BN, WGM, WGN, EPI, A, Z, FM, FN, kMk, kRegion>(acc, d, tm, tn, split, wm, \
+                                                                     wn, lane, vec, mk, region)
+  if (EPI == EPI_FWD && d.Z != nullptr) {
+    if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, true);
+    else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, true);
+    else DL_EPILOGUE(ACT_IDENTITY, true);
+  } else {
+    if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, false);
+    else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, false);
+    else DL_EPILOGUE(ACT_IDENTITY, false);
+  }
+#undef DL_EPILOGUE
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
@@ -335,8 +583,9 @@ hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
   if (EPI == EPI_DW)
     out_vec = d.splits > 1 ? out_ok(d.partial, d.N, 16) : out_ok(d.C, d.ldc, 16);
   else
-    out_vec = out_ok(d.C, d.ldc, 8) && (d.Z == nullptr || out_ok(d.Z, d.ldc, 8)) &&
-              (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 8));
+    out_vec = out_ok(d.C, d.ldc, 16) && d.ldc % 8 == 0 &&
+              (d.Z == nullptr || out_ok(d.Z, d.ldc, 16)) &&
+              (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 16));
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI>),
                      dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n,
                      out_vec);
