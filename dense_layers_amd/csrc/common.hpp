@@ -93,11 +93,9 @@ __device__ __forceinline__ float act_deriv(int act, float z) {
 // with its own L2.  Remap so every XCD receives a contiguous run of tiles,
 // then walk the tiles in bands of 8 tile-rows so that neighbouring workgroups
 // share A rows and B columns in L2.  Returns (split, tm, tn).
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& split,
-                                            int& tm, int& tn) {
-  const int nwg = gridDim.x;
-  int id = blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+// Position `id` in that band order -> (split, tm, tn).
+__device__ __forceinline__ void band_coords(int id, int tiles_m, int tiles_n, int& split, int& tm,
+                                            int& tn) {
   const int ntiles = tiles_m * tiles_n;
   split = id / ntiles;
   const int tile = id - split * ntiles;
@@ -108,6 +106,14 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& split
   const int in_band = tile - band * GROUP * tiles_n;
   tm = first_m + in_band % gsz;
   tn = in_band / gsz;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& split,
+                                            int& tm, int& tn) {
+  const int nwg = gridDim.x;
+  int id = blockIdx.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  band_coords(id, tiles_m, tiles_n, split, tm, tn);
 }
 
 // ---- GEMM launch descriptor ---------------------------------------------
@@ -197,6 +203,8 @@ template <> struct Raw4<bf16_t> {
 // A tile whose float32 staging copy exceeds kStageBudget bytes is staged in
 // WGM passes of BM / WGM rows (the rows of one row of waves each).
 constexpr int kStageBudget = 80 * 1024;
+// LDS of one CU (and the most one workgroup may allocate).
+constexpr int kLdsBytes = 160 * 1024;
 template <int BM, int BN, int WGM>
 constexpr int stage_passes() { return BM * (BN + 4) * 4 <= kStageBudget ? 1 : WGM; }
 template <int BM, int BN, int WGM>

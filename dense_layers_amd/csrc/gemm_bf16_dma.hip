@@ -95,15 +95,20 @@ struct DmaOperand {
   }
 
   // Issue this wave's load i of the next stage into `lds` (the operand's
-  // buffer).  Past the last stage (`past`) the load repeats the previous
-  // stage instead, so that every stage issues the same number of loads; the
-  // buffer it fills is never read again.
-  __device__ __forceinline__ void issue_one(char* lds, int wave, int i, bool past) {
-    const int64_t back = past ? step : 0;
+  // buffer) and advance to the stage after it.
+  __device__ __forceinline__ void issue_one(char* lds, int wave, int i) {
     __builtin_amdgcn_global_load_lds(
-        (__attribute__((address_space(1))) void*)(ptr[i] - back),
+        (__attribute__((address_space(1))) void*)ptr[i],
         (__attribute__((address_space(3))) void*)(lds + (i * kWaves + wave) * 1024), 16, 0, 0);
-    ptr[i] += step - back;
+    ptr[i] += step;
+  }
+
+  // After the last stage: later loads repeat that stage, so that every stage
+  // issues the same number of loads; the buffers they fill are never read.
+  __device__ __forceinline__ void park() {
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) ptr[i] -= step;
+    step = 0;
   }
 
   // Fragment of tile rows mb .. mb + 31 at k-step ks: this lane's 8 k.
@@ -272,26 +277,36 @@ __device__ __forceinline__ void region_flush(const char* region, TO* __restrict_
   }
 }
 
+// Largest power-of-two divisor of fm that is at most cap (at least 1).
+constexpr int block_rows_per_round(int cap, int fm) {
+  int r = 1;
+  while (2 * r <= cap && fm % (2 * r) == 0) r *= 2;
+  return r;
+}
+
 // Epilogue of one wave, on accumulators already passed through swap_halves:
 // forward (bias, act; with ZOUT also Z = acc + bias), dX (times act' of the
-// saved activations in `mk`, block b = i FN + j), or dW (float32, to C or to
+// saved activations, read here one round ahead), or dW (float32, to C or to
 // split `split`'s partial).  `region` is this wave's LDS area of kRegion
 // bytes; the wave's rows go through it in rounds of IR block rows.
-template <int BM, int BN, int WGM, int WGN, int EPI, int ACT, bool ZOUT, int FM, int FN, int NMK,
+template <int BM, int BN, int WGM, int WGN, int EPI, int ACT, bool ZOUT, int FM, int FN,
           int kRegion>
 __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], const GemmDesc& d,
                                                int tm, int tn, int split, int wm, int wn, int lane,
-                                               bool vec, const u32x4 (&mk)[NMK][2], char* region) {
+                                               bool vec, char* region) {
   using TO = typename std::conditional<EPI == EPI_DW, float, bf16_t>::type;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int ES = sizeof(TO);
   static_assert(WN == 32 * FN && WM == 32 * FM, "wave tile");
-  constexpr int NOUT = ZOUT ? 2 : 1;
+  constexpr bool kZ = ZOUT && EPI == EPI_FWD;
+  constexpr int NOUT = kZ ? 2 : 1;
   constexpr int kOutBytes = kRegion / NOUT;  // region part of one output
-  constexpr int IR = kOutBytes / (32 * WN * ES) < FM ? kOutBytes / (32 * WN * ES) : FM;
-  static_assert(IR >= 1 && FM % IR == 0, "region too small for one block row");
+  // (one block row per round when saved activations ride along, to bound
+  // the registers they take)
+  constexpr int IR = block_rows_per_round(
+      EPI == EPI_DX && ACT != ACT_IDENTITY ? 1 : kOutBytes / (32 * WN * ES), FM);
+  static_assert(kOutBytes >= 32 * WN * ES, "region too small for one block row");
   constexpr bool kMasked = EPI == EPI_DX && ACT != ACT_IDENTITY;
-  static_assert(!kMasked || NMK == FM * FN, "one mask block per accumulator block");
   const int M = d.M, N = d.N;
   const int h = lane >> 5, l32 = lane & 31;
   TO* __restrict__ out = static_cast<TO*>(d.C);
@@ -327,6 +342,17 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
   }
 
   TO* __restrict__ zout = static_cast<TO*>(d.Z);
+  // saved activations of the current round's blocks (ii, j) at ii FN + j
+  u32x4 mk[kMasked ? IR * FN : 1][2];
+  auto load_masks = [&](int i0) {
+#pragma unroll
+    for (int ii = 0; ii < IR; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        load_mask16(mk[ii * FN + j], static_cast<const bf16_t*>(d.mask_src), d.ldc,
+                    block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, i0 + ii, j, lane), M, N, vec);
+  };
+  if constexpr (kMasked) load_masks(0);
 #pragma unroll
   for (int i0 = 0; i0 < FM; i0 += IR) {
 #pragma unroll
@@ -343,37 +369,67 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
             z[c] = v[c] + bias[j][c];
             v[c] = act_apply(ACT, z[c]);
           }
-          if constexpr (ZOUT) region_put<TO, WN>(region + kOutBytes, ii * 32 + l32, j, h, z);
+          if constexpr (kZ) region_put<TO, WN>(region + kOutBytes, ii * 32 + l32, j, h, z);
         } else if constexpr (kMasked) {
-          const int b = (i0 + ii) * FN + j;
 #pragma unroll
-          for (int c = 0; c < 16; ++c) v[c] *= act_deriv(ACT, mask_at(mk[b < NMK ? b : 0], c));
+          for (int c = 0; c < 16; ++c) v[c] *= act_deriv(ACT, mask_at(mk[ii * FN + j], c));
         }
         region_put<TO, WN>(region, ii * 32 + l32, j, h, v);
       }
+    if constexpr (kMasked) {
+      if (i0 + IR < FM) load_masks(i0 + IR);
+    }
     wave_lds_order();
     region_flush<TO, WN, IR * 32>(region, out, ld, row0 + i0 * 32, col0, M, N, vec, lane);
-    if constexpr (ZOUT)
+    if constexpr (kZ)
       region_flush<TO, WN, IR * 32>(region + kOutBytes, zout, ld, row0 + i0 * 32, col0, M, N, vec,
                                     lane);
     wave_lds_order();
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+// Work items are (split, tile) pairs, numbered in the XCD-aware band order
+// of tile_coords.  Workgroup b of P takes its k-th item at item_pos(b, k):
+// the 32 workgroups of one XCD walk that XCD's contiguous share of the items
+// together, so they work on neighbouring tiles at any time.  -1: no more.
+__device__ __forceinline__ int item_pos(int b, int k, int P, int T) {
+  if ((P & 7) == 0 && (T & 7) == 0) {
+    const int per = T >> 3, w = (b >> 3) + k * (P >> 3);
+    return w < per ? (b & 7) * per + w : -1;
+  }
+  const int id = b + k * P;
+  return id < T ? id : -1;
+}
+
+struct Item {
+  int split, tm, tn, kbeg, nk;
+};
+
+// PERSIST: the grid holds one workgroup per CU and each walks several items
+// with one continuous pipeline: the loads of the next item's first stages are
+// issued during the current item's last stages, and the epilogue, which works
+// in LDS regions of its own, runs while they land.  Otherwise the grid holds
+// one workgroup per item and the epilogue reuses the stage buffers.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI,
+          bool PERSIST>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   constexpr int NT = WGM * WGN * 64;
+  constexpr int NW = NT / 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KS = BK / 16;  // MFMA k-steps per stage
   static_assert(FM >= 1 && FN >= 1, "bad tile");
   static_assert(STAGES >= 2, "stages");
+  static_assert(KS % 2 == 0, "fragment double buffer assumes an even k-step count");
   using OA = DmaOperand<BM, ALAY, NT, BK>;
   using OB = DmaOperand<BN, BLAY, NT, BK>;
   constexpr int kStageBytes = OA::kBytes + OB::kBytes;
   constexpr int kLoads = OA::kInst + OB::kInst;  // per wave per stage
-  constexpr int kSmem = STAGES * kStageBytes;
+  constexpr int kStageArea = STAGES * kStageBytes;
+  constexpr int kRegion = PERSIST ? (kLdsBytes - kStageArea) / NW / 1024 * 1024 : kStageArea / NW;
+  constexpr int kSmem = PERSIST ? kStageArea + NW * kRegion : kStageArea;
+  static_assert(kSmem <= kLdsBytes, "LDS");
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int tid = threadIdx.x;
@@ -381,85 +437,118 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5;
-
-  int split, tm, tn;
-  tile_coords(tiles_m, tiles_n, split, tm, tn);
-
   const int M = d.M, N = d.N;
-  const int kbeg = split * d.k_per_split;
-  const int kend = min(d.K, kbeg + d.k_per_split);
-  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const int T = tiles_m * tiles_n * d.splits;
+  const int P = gridDim.x, b = blockIdx.x;
 
+  auto make_item = [&](int pos) {
+    Item it;
+    band_coords(pos, tiles_m, tiles_n, it.split, it.tm, it.tn);
+    it.kbeg = it.split * d.k_per_split;
+    const int kend = min(d.K, it.kbeg + d.k_per_split);
+    it.nk = (kend - it.kbeg) / BK;
+    return it;
+  };
+
+  // ---- loader: which item and stage the next issued loads belong to
   OA oa;
   OB ob;
-  oa.init(static_cast<const bf16_t*>(d.A), d.lda, tm * BM, M, kbeg, wave, lane);
-  ob.init(static_cast<const bf16_t*>(d.B), d.ldb, tn * BN, N, kbeg, wave, lane);
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const bool do_db = (EPI == EPI_DW) && (d.db != nullptr || d.db_partial != nullptr) &&
-                     tn == 0 && wn == 0;
-  float dbacc[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) dbacc[i] = 0.f;
-
-  auto stage_ptr = [&](int kt) { return smem + (kt % STAGES) * kStageBytes; };
-  // loads j0 .. j1 - 1 of stage kt (A's loads first, then B's)
-  auto issue_range = [&](int kt, int j0, int j1) {
-    char* p = stage_ptr(kt);
-    const bool past = kt >= nk;
+  int ld_k = 0, ld_kt = 0, lg = 0;  // item index, its stage, global stage
+  bool lpast = false;               // past the last stage of the last item
+  Item ld = make_item(item_pos(b, 0, P, T));
+  auto load_init = [&]() {
+    oa.init(static_cast<const bf16_t*>(d.A), d.lda, ld.tm * BM, M, ld.kbeg, wave, lane);
+    ob.init(static_cast<const bf16_t*>(d.B), d.ldb, ld.tn * BN, N, ld.kbeg, wave, lane);
+  };
+  load_init();
+  // loads j0 .. j1 - 1 of global stage lg (A's loads first, then B's)
+  auto issue_parts = [&](int j0, int j1) {
+    char* p = smem + (lg % STAGES) * kStageBytes;
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
-      if (j < OA::kInst) oa.issue_one(p, wave, j, past);
-      else ob.issue_one(p + OA::kBytes, wave, j - OA::kInst, past);
+      if (j < OA::kInst) oa.issue_one(p, wave, j);
+      else ob.issue_one(p + OA::kBytes, wave, j - OA::kInst);
     }
   };
-  auto read_frags = [&](const char* cur, int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = OA::frag(cur, wm * WM + i * 32, ks, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = OB::frag(cur + OA::kBytes, wn * WN + j * 32, ks, lane);
+  auto next_load_stage = [&]() {
+    ++lg;
+    ++ld_kt;
+    if (!lpast && ld_kt == ld.nk) {
+      const int pos = PERSIST ? item_pos(b, ++ld_k, P, T) : -1;
+      if (pos < 0) {
+        lpast = true;
+        oa.park();
+        ob.park();
+      } else {
+        ld = make_item(pos);
+        ld_kt = 0;
+        load_init();
+      }
+    }
   };
-  auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+
+  // ---- compute state
+  Item cur = ld;
+  int ck = 0;
+  f32x16 acc[FM][FN];
+  float dbacc[FM];
+  auto clear_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      dbacc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+  };
+  clear_acc();
+  const bool want_db = (EPI == EPI_DW) && (d.db != nullptr || d.db_partial != nullptr) && wn == 0;
+  bool do_db = want_db && cur.tn == 0;
+
+  auto read_frags = [&](const char* buf, int ks, bf16x8 (&a)[FM], bf16x8 (&bb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i] = OA::frag(buf, wm * WM + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bb[j] = OB::frag(buf + OA::kBytes, wn * WN + j * 32, ks, lane);
+  };
+  auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&bb)[FN]) {
     if (do_db) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += static_cast<float>(a[i][e]);
-        dbacc[i] += s;
+        for (int e = 0; e < 8; ++e) sum += static_cast<float>(a[i][e]);
+        dbacc[i] += sum;
       }
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[j], a[i], acc[i][j], 0, 0, 0);
   };
+  auto stage_buf = [&](int g) { return smem + (g % STAGES) * kStageBytes; };
 
   // Fragments are double-buffered in registers (set ks & 1 holds k-step ks),
   // so the reads of one k-step are in flight while the MFMAs of the previous
-  // one run.  The barrier of stage kt sits before its last k-step: by then
-  // every wave holds its last fragments of stage kt in registers, so after
-  // the barrier the first fragments of stage kt + 1 are read while the last
-  // MFMAs of stage kt run, and the matrix cores do not idle at the barrier.
-  // Each wave drains its LDS reads before that barrier, so once past it no
-  // wave reads stage kt's buffer again; the loads of stage kt + STAGES (same
-  // buffer), issued during stage kt + 1, may then overwrite it.
+  // one run.  The barrier of global stage g sits before its last k-step: by
+  // then every wave holds its last fragments of stage g in registers, so
+  // after the barrier the first fragments of stage g + 1 are read while the
+  // last MFMAs of stage g run, and the matrix cores do not idle at the
+  // barrier.  Each wave drains its LDS reads before that barrier, so once past
+  // it no wave reads stage g's buffer again; the loads of stage g + STAGES
+  // (same buffer), issued during stage g + 1, may then overwrite it.
   //
-  // With three or more stages the loads of stage kt + STAGES - 1 are spread
-  // over the k-steps of stage kt, interleaved with the MFMAs, and every stage
-  // issues kLoads loads (repeats past the end), so at the barrier of stage kt
-  // the loads still allowed in flight are those of the stages after kt + 1:
-  // (STAGES - 2) kLoads minus the part of stage kt + STAGES - 1 not yet
-  // issued.  With two stages the loads of stage kt + 1 all go first (they
-  // must land by the barrier of stage kt) and none are allowed in flight.
+  // With three or more stages the loads of stage g + STAGES - 1 are spread
+  // over the k-steps of stage g, interleaved with the MFMAs, and every stage
+  // issues kLoads loads (repeats past the end), so at the barrier of stage g
+  // the loads still allowed in flight are those of the stages after g + 1:
+  // (STAGES - 2) kLoads minus the part of stage g + STAGES - 1 not yet
+  // issued.  With two stages the loads of stage g + 1 all go first (they must
+  // land by the barrier of stage g) and none are allowed in flight.  Stores
+  // and saved-activation loads of an epilogue are younger than the loads of
+  // the stage that follows it, so the next barrier also waits for them.
   bf16x8 fa[2][FM], fb[2][FN];
   constexpr int kReads = (ALAY == K_MAJOR ? FM : 2 * FM) + (BLAY == K_MAJOR ? FN : 2 * FN);
   constexpr int kMfma = FM * FN;
@@ -470,100 +559,108 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   constexpr int kAllowed = (STAGES - 2) * kLoads - kLast;
   auto part = [](int ks) { return ks * kMid; };
 
-  // The dX epilogue's saved activations for the first half of the wave's
-  // blocks are requested before the first operand loads, so their HBM
-  // latency overlaps the pipeline fill instead of stalling the epilogue.
-  constexpr int kMk = EPI == EPI_DX ? FM * FN : 1;
-  constexpr int kPre = EPI == EPI_DX ? (FM / 2) * FN : 0;
-  const bool masked = EPI == EPI_DX && d.mask_act != ACT_IDENTITY;
-  u32x4 mk[kMk][2];
-  if (masked) {
-#pragma unroll
-    for (int b = 0; b < kPre; ++b)
-      load_mask16(mk[b], static_cast<const bf16_t*>(d.mask_src), d.ldc,
-                  block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, b / FN, b % FN, lane), M, N,
-                  out_vec);
-  }
+  const bool vec = out_vec != 0;
+  const int act = EPI == EPI_FWD ? d.act : EPI == EPI_DX ? d.mask_act : ACT_IDENTITY;
+  char* region = smem + (PERSIST ? kStageArea : 0) + wave * kRegion;
 
-  if (nk > 0) {  // (always true for the splits the launcher forms)
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue_range(s, 0, kLoads);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
-    __builtin_amdgcn_s_barrier();
-    read_frags(stage_ptr(0), 0, fa[0], fb[0]);
+  for (int st = 0; st < STAGES - 1; ++st) {
+    issue_parts(0, kLoads);
+    next_load_stage();
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kLoads));
+  __builtin_amdgcn_s_barrier();
+  read_frags(stage_buf(0), 0, fa[0], fb[0]);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = stage_ptr(kt);
-    if (STAGES == 2 && kt + 1 < nk) issue_range(kt + 1, 0, kLoads);
+  // One stage: k-steps, barrier, the rest of the next stage's loads; the
+  // first fragments of the next stage are read unless LAST (the item's last
+  // stage, after which the epilogue runs and the next item starts).
+  int g = 0;
+  auto run_stage = [&](auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const char* cbuf = stage_buf(g);
+    if (STAGES == 2) {
+      issue_parts(0, kLoads);
+      next_load_stage();
+    }
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
-      if (STAGES > 2) issue_range(kt + STAGES - 1, part(ks), part(ks + 1));
-      read_frags(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      if (STAGES > 2) issue_parts(part(ks), part(ks + 1));
+      read_frags(cbuf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       mfmas(fa[ks & 1], fb[ks & 1]);
       sched_interleave<kMfma, kReads, kMid>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // own reads of stage kt complete; stage kt + 1 landed for this wave.  On
-    // the last stage the reads below fetch a buffer whose contents go unused.
+    // own reads of stage g complete; stage g + 1 landed for this wave
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAllowed));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (STAGES > 2) issue_range(kt + STAGES - 1, part(KS - 1), kLoads);
-    read_frags(stage_ptr(kt + 1), 0, fa[KS & 1], fb[KS & 1]);
-    mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
-    sched_interleave<kMfma, kReads, kLast>();
+    if (STAGES > 2) {
+      issue_parts(part(KS - 1), kLoads);
+      next_load_stage();
+    }
+    if (!LAST) read_frags(stage_buf(g + 1), 0, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+    sched_interleave<kMfma, kReads, LAST ? 0 : kLast>();
     __builtin_amdgcn_sched_barrier(0);
-  }
-  // The repeated loads past the last stage still write LDS: let them land,
-  // and retire the stage buffers for the epilogue's per-wave regions.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
+    ++g;
+  };
 
-  if (EPI == EPI_DW && do_db) {
-    const int row_base = tm * BM + wm * WM;
+  while (true) {
+    for (int kt = 0; kt + 1 < cur.nk; ++kt) run_stage(std::false_type{});
+    run_stage(std::true_type{});
+
+    // ---- epilogue of item `cur`
+    if (!PERSIST) {
+      // the repeated loads past the last stage still write LDS, and other
+      // waves may still read the stage buffers the regions reuse
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+    }
+    if (EPI == EPI_DW && do_db) {
+      const int row_base = cur.tm * BM + wm * WM;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
-      const int row = row_base + i * 32 + (lane & 31);
-      if (h == 0 && row < M) {
-        if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
-        else d.db[row] = v;
+      for (int i = 0; i < FM; ++i) {
+        const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+        const int row = row_base + i * 32 + (lane & 31);
+        if (h == 0 && row < M) {
+          if (d.splits > 1) d.db_partial[(int64_t)cur.split * M + row] = v;
+          else d.db[row] = v;
+        }
       }
     }
-  }
-  // the other half of the saved activations, requested before the
-  // accumulators are rearranged
-  if (masked) {
-#pragma unroll
-    for (int b = kPre; b < kMk; ++b)
-      load_mask16(mk[b], static_cast<const bf16_t*>(d.mask_src), d.ldc,
-                  block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, b / FN, b % FN, lane), M, N,
-                  out_vec);
-  }
-  swap_halves(acc);
-  const bool vec = out_vec != 0;
-  constexpr int kRegion = kSmem / (NT / 64);
-  char* region = smem + wave * kRegion;
-  const int act = EPI == EPI_FWD ? d.act : EPI == EPI_DX ? d.mask_act : ACT_IDENTITY;
-#define DL_EPILOGUE(A, Z)                                                                     \
-  store_epilogue<BM, BN, WGM, WGN, EPI, A, Z, FM, FN, kMk, kRegion>(acc, d, tm, tn, split, wm, \
-                                                                     wn, lane, vec, mk, region)
-  if (EPI == EPI_FWD && d.Z != nullptr) {
-    if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, true);
-    else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, true);
-    else DL_EPILOGUE(ACT_IDENTITY, true);
-  } else {
-    if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, false);
-    else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, false);
-    else DL_EPILOGUE(ACT_IDENTITY, false);
-  }
+    swap_halves(acc);
+#define DL_EPILOGUE(A, Z)                                                                 \
+  store_epilogue<BM, BN, WGM, WGN, EPI, A, Z, FM, FN, kRegion>(                           \
+      acc, d, cur.tm, cur.tn, cur.split, wm, wn, lane, vec, region)
+    if (EPI == EPI_FWD && d.Z != nullptr) {
+      if constexpr (EPI != EPI_FWD) {
+      } else if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, true);
+      else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, true);
+      else DL_EPILOGUE(ACT_IDENTITY, true);
+    } else {
+      if (act == ACT_GELU_TANH) DL_EPILOGUE(ACT_GELU_TANH, false);
+      else if (act == ACT_RELU) DL_EPILOGUE(ACT_RELU, false);
+      else DL_EPILOGUE(ACT_IDENTITY, false);
+    }
 #undef DL_EPILOGUE
+
+    // ---- next item: its first stage landed before the last barrier
+    const int pos = item_pos(b, ++ck, P, T);
+    if (!PERSIST || pos < 0) break;
+    cur = make_item(pos);
+    do_db = want_db && cur.tn == 0;
+    clear_acc();
+    read_frags(stage_buf(g), 0, fa[0], fb[0]);
+  }
+  // nothing may still write this workgroup's LDS when it retires
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI,
+          bool PERSIST>
 hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
   auto aligned = [](const void* p, int64_t ld) {
     return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 8 == 0);
@@ -574,8 +671,16 @@ hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
   if (BLAY == MN_MAJOR && d.N % 8 != 0) return hipErrorNotSupported;
   const int tiles_m = (d.M + BM - 1) / BM;
   const int tiles_n = (d.N + BN - 1) / BN;
-  const int64_t nwg = (int64_t)tiles_m * tiles_n * d.splits;
-  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)tiles_m * tiles_n * d.splits;
+  if (items <= 0 || items > 0x7fffffff) return hipErrorInvalidValue;
+  int64_t nwg = items;
+  if (PERSIST) {  // one workgroup per CU (the kernel's LDS admits no more)
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    nwg = std::min<int64_t>(items, std::max(cus, 1));
+  }
   auto out_ok = [](const void* p, int64_t ld, int bytes) {
     return ((reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0) && (ld % 4 == 0);
   };
@@ -586,31 +691,45 @@ hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
     out_vec = out_ok(d.C, d.ldc, 16) && d.ldc % 8 == 0 &&
               (d.Z == nullptr || out_ok(d.Z, d.ldc, 16)) &&
               (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 16));
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI>),
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI, PERSIST>),
                      dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n,
                      out_vec);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PERSIST>
 hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
   if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD, PERSIST>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX, PERSIST>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, PERSIST>(d, s);
   if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, PERSIST>(d, s);
   return hipErrorNotSupported;
 }
 
 }  // namespace
 
+// The 256x256 tile runs persistent (three stages, separate epilogue LDS)
+// when every CU gets at least kPersistItems items: there the pipeline fill
+// and the epilogue of each item are the costs it hides.  With fewer items per
+// CU the one-workgroup-per-item form with four stages measured faster.
+constexpr int kPersistItems = 4;
+
 hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
-    case 0: return dma_layout<256, 256, 32, 4, 2, 4>(d, s);
-    case 1: return dma_layout<128, 128, 64, 2, 2, 2>(d, s);
+    case 0: {
+      int dev = 0, cus = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      const int64_t items = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256) * d.splits;
+      if (items >= (int64_t)kPersistItems * cus) return dma_layout<256, 256, 32, 3, 2, 4, true>(d, s);
+      return dma_layout<256, 256, 32, 4, 2, 4, false>(d, s);
+    }
+    case 1: return dma_layout<128, 128, 64, 2, 2, 2, false>(d, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -214,6 +214,40 @@ def test_bf16_large_tile_dx_ragged(dl, use_wt):
     assert_close(to_np(dX), rdX, BF16_TOL, "dX")
 
 
+# At least four 256x256 tiles per CU: the tile runs persistent (each
+# workgroup walks several tiles with one pipeline), ragged in M and N.
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_bf16_persistent_fwd_ragged(dl, act):
+    B, n_in, n_out = 8200, 64, 8200
+    X = si.random_matrix(260, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(261, (n_out, n_in), scale=0.1, bf16_exact=True)
+    b = si.random_matrix(262, (n_out,), scale=0.01)
+    bf = torch.bfloat16
+    save_z = act != O.ACT_IDENTITY
+    Y, Z = dl.dense_act_fwd(to_dev(X, bf), to_dev(W, bf), to_dev(b), act, save_z=save_z)
+    refY, refZ = O.dense_act_fwd(X, W, b, act)
+    if save_z:
+        assert_close(to_np(Z), refZ, BF16_TOL, "Z")
+    assert_close(to_np(Y), refY, BF16_TOL, "Y")
+
+
+def test_bf16_persistent_dx_ragged(dl):
+    B, n_in, n_out = 8200, 8200, 64
+    X = si.random_matrix(270, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(271, (n_out, n_in), scale=0.1, bf16_exact=True)
+    Z = si.random_matrix(272, (B, n_out), bf16_exact=True)
+    dY = si.random_matrix(273, (B, n_out), bf16_exact=True)
+    H = si.random_matrix(274, (B, n_in), bf16_exact=True)
+    bf = torch.bfloat16
+    # dX of this layer with the previous layer's GELU derivative folded in
+    dX, _, _ = dl.dense_act_vjp(to_dev(dY, bf), to_dev(Z, bf), None, to_dev(W, bf),
+                                O.ACT_GELU_TANH, need_dw=False, dx_act=O.ACT_GELU_TANH,
+                                dx_saved=to_dev(H, bf))
+    rdX, _, _ = O.dense_act_vjp(dY, Z, X, W, O.ACT_GELU_TANH, need_dx=True)
+    rdX = rdX * O.act_grad(H, O.ACT_GELU_TANH)
+    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+
+
 def test_bf16_dw_split_ragged(dl):
     B, n_in, n_out = 1024, 1000, 200
     X = si.random_matrix(250, (B, n_in), bf16_exact=True)
