@@ -79,13 +79,15 @@ bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 // float32 tiles {0: 128x128x16, 1: 64x64x32, 2: 64x128x32 with 8 waves}:
 // 128x128 when it alone yields at least one workgroup per CU (256); else, for
 // forward and dX products, 64x128 when that does; otherwise 64x64.
-// bf16 tiles {0: 256x256, 1: 128x128} of the direct-to-LDS kernel (K step 64):
-// 256x256 for forward / dX products with at least one such tile per CU,
-// 128x128 otherwise; operands that kernel cannot take (unaligned, K not a
-// multiple of 64) go to the general 128x128 kernel.  Only the weight-gradient
-// product (K = batch) is split along K: when it has fewer than two
-// workgroups per CU, slices are added until about four per CU exist (at most
-// 64), each slice keeping at least four K tiles.
+// bf16 tiles {0: 256x256 (8 waves), 1: 128x128, 2: 256x256 (4 waves)} of the
+// direct-to-LDS kernel (K a multiple of 64): tile 0 for forward / dX products
+// with at least one such tile per CU, tile 2 for weight gradients with at
+// least 32 such tiles, 128x128 otherwise; operands that kernel cannot take
+// (unaligned, K not a multiple of 64) go to the general 128x128 kernel.  Only
+// the weight-gradient product (K = batch) is split along K: when it has fewer
+// than two workgroups per CU, slices are added until about four per CU exist
+// (two for tile 2, whose LDS admits one workgroup per CU; at most 64 slices),
+// each slice keeping at least four K tiles.
 
 constexpr int kCUs = 256;
 
@@ -97,7 +99,7 @@ struct Plan {
 
 void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
   if (dtype == DL_BF16) {
-    bm = bn = tile == 0 ? 256 : 128;
+    bm = bn = tile == 1 ? 128 : 256;
     bk = 64;
   } else {
     bm = tile == 0 ? 128 : 64;
@@ -113,7 +115,14 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   int bm, bn, bk;
   tile_shape(dtype, 0, bm, bn, bk);
   int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-  if (tiles < kCUs || (dtype == DL_BF16 && epi == dl::EPI_DW)) {
+  // bf16 weight gradients: 256x256 tiles of four waves when there are
+  // enough of them, else 128x128; the split-K count aims at two workgroups
+  // per CU for the former and four for the latter.
+  int64_t per_cu = 4;
+  if (dtype == DL_BF16 && epi == dl::EPI_DW && tiles >= 32) {
+    p.tile = 2;
+    per_cu = 2;
+  } else if (tiles < kCUs || (dtype == DL_BF16 && epi == dl::EPI_DW)) {
     p.tile = 1;
     if (dtype == DL_F32 && epi != dl::EPI_DW && ceil_div(M, 64) * ceil_div(N, 128) >= kCUs)
       p.tile = 2;
@@ -121,7 +130,7 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
     tiles = ceil_div(M, bm) * ceil_div(N, bn);
   }
   if (epi == dl::EPI_DW && tiles < 2 * kCUs) {
-    int64_t want = ceil_div(4 * kCUs, tiles);
+    int64_t want = ceil_div(per_cu * kCUs, tiles);
     const int64_t max_by_k = std::max<int64_t>(1, K / (4 * bk));
     want = std::min<int64_t>(std::min<int64_t>(want, max_by_k), 64);
     int64_t kps = ceil_div(ceil_div(K, want), bk) * bk;

@@ -9,35 +9,35 @@
 namespace dl {
 namespace {
 
-// dW (contiguous [M, N]) = sum over slices of partial[s][M][N].  Four lanes
-// share a group of 4 consecutive elements: lane q adds slices q, q+4, ... in
-// order and the quad combines its partial sums in the fixed tree
-// (p0 + p1) + (p2 + p3), so each thread walks a quarter of the slices and
-// the result is bit-reproducible.
-__global__ void __launch_bounds__(256)
-splitk_reduce_kernel(int64_t MN, int splits, const float* __restrict__ partial, float* __restrict__ C,
-                     int vec) {
-  const int q = threadIdx.x & 3;
-  const int64_t e0 = ((int64_t)blockIdx.x * 64 + (threadIdx.x >> 2)) * 4;
-  float g[4] = {0.f, 0.f, 0.f, 0.f};
-  if (vec && e0 + 3 < MN) {
-#pragma unroll 4
-    for (int s = q; s < splits; s += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(partial + s * MN + e0);
-      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
-    }
+// out[0 .. n) = sum over slices s = 0 .. S - 1 of p[s * n + (0 .. n)], added in
+// slice order (bit-reproducible).  One thread per 4 consecutive outputs
+// reads all of its slices, so a thread has many independent loads in flight.
+__device__ __forceinline__ void reduce_slices(int64_t n, int S, const float* __restrict__ p,
+                                              float* __restrict__ out, bool vec, unsigned blk) {
+  const int64_t e0 = ((int64_t)blk * 256 + threadIdx.x) * 4;
+  if (e0 >= n) return;
+  if (vec && e0 + 3 < n) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p + e0);
+#pragma unroll 8
+    for (int sl = 1; sl < S; ++sl) a += *reinterpret_cast<const f32x4*>(p + sl * n + e0);
+    *reinterpret_cast<f32x4*>(out + e0) = a;
   } else {
-    for (int s = q; s < splits; s += 4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e0 + e < MN) g[e] += partial[s * MN + e0 + e];
+    for (int e = 0; e < 4 && e0 + e < n; ++e) {
+      float a = p[e0 + e];
+      for (int sl = 1; sl < S; ++sl) a += p[sl * n + e0 + e];
+      out[e0 + e] = a;
+    }
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    g[e] += __shfl_xor(g[e], 1);
-    g[e] += __shfl_xor(g[e], 2);
-  }
-  if (e0 + q < MN) C[e0 + q] = g[q];
+}
+
+// Split-K finish of the weight gradient: blocks [0, wblocks) sum the dW
+// slices partial[s][M][N] into C, the rest the db slices db_partial[s][M].
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(int64_t MN, int64_t M, int splits, const float* __restrict__ partial,
+                     const float* __restrict__ db_partial, float* __restrict__ C,
+                     float* __restrict__ db, int vec, int vec_db, unsigned wblocks) {
+  if (blockIdx.x < wblocks) reduce_slices(MN, splits, partial, C, vec != 0, blockIdx.x);
+  else reduce_slices(M, splits, db_partial, db, vec_db != 0, blockIdx.x - wblocks);
 }
 
 template <typename T>
@@ -99,13 +99,15 @@ hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 hipStream_t s) {
   if (ldc != N) return hipErrorInvalidValue;
   const int64_t MN = (int64_t)M * N;
-  const int vec = (MN % 4 == 0) && ((reinterpret_cast<uintptr_t>(partial) & 15) == 0);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, MN,
-                     splits, partial, C, vec);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || db == nullptr) return e;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
-                     (int64_t)M, splits, db_partial, db, 0);
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const int vec = (MN % 4 == 0) && al16(partial) && al16(C);
+  const int vec_db = db != nullptr && (M % 4 == 0) && al16(db_partial) && al16(db);
+  const int64_t wblocks = (MN + 1023) / 1024;
+  const int64_t dblocks = db != nullptr ? ((int64_t)M + 1023) / 1024 : 0;
+  if (wblocks + dblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)(wblocks + dblocks)), dim3(256), 0, s,
+                     MN, (int64_t)M, splits, partial, db_partial, C, db, vec, vec_db,
+                     (unsigned)wblocks);
   return hipGetLastError();
 }
 

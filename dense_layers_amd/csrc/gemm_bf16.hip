@@ -377,7 +377,7 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
 // the operands allow it; everything else, and operands it declines, runs the
 // general kernel at 128x128 (4 waves of 64x64, two workgroups per CU).
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
-  if (tile == 0 || tile == 1) {
+  if (tile >= 0 && tile <= 2) {
     const hipError_t e = launch_gemm_bf16_dma(d, tile, s);
     if (e != hipErrorNotSupported) return e;
   }

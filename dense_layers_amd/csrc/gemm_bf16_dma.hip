@@ -730,6 +730,9 @@ hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
       return dma_layout<256, 256, 32, 4, 2, 4, false>(d, s);
     }
     case 1: return dma_layout<128, 128, 64, 2, 2, 2, false>(d, s);
+    // weight gradients (both operands M/N-major): four waves of 128x128 halve
+    // the transposing LDS reads per MFMA against eight waves of 128x64
+    case 2: return dma_layout<256, 256, 64, 2, 2, 2, false>(d, s);
     default: return hipErrorNotSupported;
   }
 }

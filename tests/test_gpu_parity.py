@@ -248,6 +248,21 @@ def test_bf16_persistent_dx_ragged(dl):
     assert_close(to_np(dX), rdX, BF16_TOL, "dX")
 
 
+def test_bf16_dw_wide_tile_ragged(dl):
+    """Weight gradient on the four-wave 256x256 tile (at least 32 such tiles),
+    split along the batch, ragged in both output dimensions."""
+    B, n_in, n_out = 2048, 1032, 2000
+    X = si.random_matrix(280, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(281, (n_out, n_in), scale=0.05, bf16_exact=True)
+    dY = si.random_matrix(282, (B, n_out), bf16_exact=True)
+    bf = torch.bfloat16
+    _, dW, db = dl.dense_act_vjp(to_dev(dY, bf), None, to_dev(X, bf), to_dev(W, bf),
+                                 O.ACT_IDENTITY, need_dx=False)
+    _, rdW, rdb = O.dense_act_vjp(dY, None, X, W, O.ACT_IDENTITY, need_dx=False)
+    assert_close(to_np(dW), rdW, BF16_TOL, "dW")
+    assert_close(to_np(db), rdb, BF16_TOL, "db")
+
+
 def test_bf16_dw_split_ragged(dl):
     B, n_in, n_out = 1024, 1000, 200
     X = si.random_matrix(250, (B, n_in), bf16_exact=True)
