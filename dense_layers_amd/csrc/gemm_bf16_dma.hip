@@ -1,8 +1,8 @@
 // bfloat16-operand GEMM for large, aligned problems: operand tiles go from
 // HBM straight into LDS (global_load_lds_dwordx4, no staging registers), the
 // matrix cores read them back as MFMA fragments (v_mfma_f32_32x32x16_bf16,
-// float32 accumulation), and the dense-layer epilogues of the general bf16
-// kernel are applied on the way out.
+// float32 accumulation), and the dense-layer epilogues (bias + activation,
+// act' masking, float32 weight-gradient slices) are applied on the way out.
 //
 // The products are the three of the fused LinearAct (noeira.nn docs, "The
 // design in one page"): forward Z = X W^T + b, dX = (dY o act') W and
@@ -10,16 +10,18 @@
 // scheme (Orthon page, "Mixed-precision training on CUDA").
 //
 // Pipeline: STAGES LDS buffers of BK k each.  The loads of stage
-// kt + STAGES - 1 are issued at the top of stage kt, so each load has
-// STAGES - 1 stages of matrix-core work to land in; nothing is staged in
-// VGPRs.  One barrier per stage publishes the next stage (see the loop).
+// g + STAGES - 1 are issued during stage g (spread over its k-steps), so each
+// load has about STAGES - 2 stages of matrix-core work to land in; nothing is
+// staged in VGPRs.  One barrier per stage publishes the next stage (see the
+// loop).  Work items are (split, tile) pairs; in the persistent form a
+// workgroup walks several items with one continuous pipeline.
 //
 // A direct load writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so the
 // LDS layout is chosen by which global 16-byte unit each lane fetches:
-//  * K-major operand (rows contiguous in k): LDS row r holds the 64 k of tile
-//    row r as eight 16-byte units, unit u at position u ^ ((r ^ r >> 3) & 7).
-//    A lane's fragment (8 consecutive k of one row) is one 16-byte LDS read;
-//    the 16 lanes of one read phase land on distinct banks.
+//  * K-major operand (rows contiguous in k): LDS row r holds the BK k of tile
+//    row r as BK / 8 16-byte units, unit u at position u ^ ksw(r).  A lane's
+//    fragment (8 consecutive k of one row) is one 16-byte LDS read; the 16
+//    lanes of one read phase land on distinct banks.
 //  * M/N-major operand (rows contiguous in m): LDS k-row k holds the tile's
 //    ROWS m of that k, 16-byte unit u at position u ^ (4 (k & 3)).  Fragments
 //    come from the gfx950 transposing read ds_read_b64_tr_b16: in each group
