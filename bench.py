@@ -38,13 +38,18 @@ KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources: a stored counter measurement is only
-    used while the code it was taken from is unchanged."""
+    """sha256 over the kernel sources without their // comments and blank
+    lines: a stored counter measurement is only used while the code it was
+    taken from is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dense_layers_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "dense_layers_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
