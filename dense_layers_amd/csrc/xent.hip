@@ -5,7 +5,7 @@
 // mapped to a different number of threads per class-count regime here).
 //
 // A row of C logits is owned by TPR consecutive threads (a lane group inside a
-// wave for TPR <= 64, the whole 256-thread workgroup for TPR = 256).  Each
+// wave for TPR <= 64, the whole workgroup of 1024 threads for wide rows).  Each
 // thread keeps its slice of the row in registers, so HBM sees one read and
 // one write per logit; row max, sum of exponentials and the label's logit are
 // combined with cross-lane shuffles (plus LDS across waves for TPR = 256).
@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kXentBlock = 256;
 
-template <int TPR>
+template <int TPR, int BLOCK>
 __device__ __forceinline__ float group_max(float v, float* red) {
   if (TPR <= 64) {
 #pragma unroll
@@ -34,13 +34,13 @@ __device__ __forceinline__ float group_max(float v, float* red) {
     __syncthreads();
     float r = red[0];
 #pragma unroll
-    for (int w = 1; w < kXentBlock / 64; ++w) r = fmaxf(r, red[w]);
+    for (int w = 1; w < BLOCK / 64; ++w) r = fmaxf(r, red[w]);
     __syncthreads();
     return r;
   }
 }
 
-template <int TPR>
+template <int TPR, int BLOCK>
 __device__ __forceinline__ void group_sum2(float& a, float& b, float* red) {
   if (TPR <= 64) {
 #pragma unroll
@@ -63,7 +63,7 @@ __device__ __forceinline__ void group_sum2(float& a, float& b, float* red) {
     a = 0.f;
     b = 0.f;
 #pragma unroll
-    for (int w = 0; w < kXentBlock / 64; ++w) {
+    for (int w = 0; w < BLOCK / 64; ++w) {
       a += red[2 * w];
       b += red[2 * w + 1];
     }
@@ -72,14 +72,14 @@ __device__ __forceinline__ void group_sum2(float& a, float& b, float* red) {
 
 // VEC: items are float4 (C % 4 == 0, 16-byte aligned rows), else floats.
 // NI:  items cached per thread; the kernel is only launched with
-//      C <= TPR * NI * (VEC ? 4 : 1).
-template <int TPR, int NI, bool VEC>
-__global__ void __launch_bounds__(kXentBlock)
+//      C <= TPR * NI * (VEC ? 4 : 1).  BLOCK: threads per workgroup.
+template <int TPR, int NI, bool VEC, int BLOCK = kXentBlock>
+__global__ void __launch_bounds__(BLOCK)
 xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restrict__ labels,
                  float* __restrict__ row_loss, float* dlogits, float invB) {
-  constexpr int RPB = kXentBlock / TPR;
+  constexpr int RPB = BLOCK / TPR;
   constexpr int W = VEC ? 4 : 1;
-  __shared__ float red[2 * kXentBlock / 64];
+  __shared__ float red[2 * BLOCK / 64];
   const int lr = threadIdx.x % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const bool active = row < B;
@@ -103,7 +103,7 @@ xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restric
 #pragma unroll
     for (int e = 0; e < W; ++e) m = fmaxf(m, v[j][e]);
   }
-  m = group_max<TPR>(m, red);
+  m = group_max<TPR, BLOCK>(m, red);
 
   float s = 0.f, zy = 0.f;
 #pragma unroll
@@ -119,7 +119,7 @@ xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restric
         if (c == y) zy = x;
       }
     }
-  group_sum2<TPR>(s, zy, red);
+  group_sum2<TPR, BLOCK>(s, zy, red);
 
   const float inv_s = 1.0f / s;
   if (active && lr == 0)
@@ -156,14 +156,14 @@ xent_rows_wide_kernel(int64_t B, int64_t C, const float* logits, const int32_t* 
   const bool valid = (y >= 0) && (y < C);
   float m = -INFINITY;
   for (int64_t c = threadIdx.x; c < C; c += kXentBlock) m = fmaxf(m, logits[base + c]);
-  m = group_max<kXentBlock>(m, red);
+  m = group_max<kXentBlock, kXentBlock>(m, red);
   float s = 0.f, zy = 0.f;
   for (int64_t c = threadIdx.x; c < C; c += kXentBlock) {
     const float x = logits[base + c];
     s += __expf(x - m);
     if (c == y) zy = x;
   }
-  group_sum2<kXentBlock>(s, zy, red);
+  group_sum2<kXentBlock, kXentBlock>(s, zy, red);
   if (threadIdx.x == 0) row_loss[row] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
   __syncthreads();  // every read of this row precedes the first in-place write
   const float inv_s = 1.0f / s;
@@ -198,12 +198,12 @@ loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restric
   }
 }
 
-template <int TPR, int NI, bool VEC>
+template <int TPR, int NI, bool VEC, int BLOCK = kXentBlock>
 hipError_t launch_rows(int64_t B, int64_t C, const float* logits, const int32_t* labels,
                        float* row_loss, float* dlogits, hipStream_t s) {
-  constexpr int RPB = kXentBlock / TPR;
+  constexpr int RPB = BLOCK / TPR;
   const int64_t blocks = (B + RPB - 1) / RPB;
-  hipLaunchKernelGGL((xent_rows_kernel<TPR, NI, VEC>), dim3((unsigned)blocks), dim3(kXentBlock), 0,
+  hipLaunchKernelGGL((xent_rows_kernel<TPR, NI, VEC, BLOCK>), dim3((unsigned)blocks), dim3(BLOCK), 0,
                      s, B, (int)C, logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
   return hipGetLastError();
 }
@@ -223,8 +223,8 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
   else if (C <= 2048)
     e = vec ? launch_rows<64, 8, true>(B, C, logits, labels, row_loss, dlogits, s)
             : launch_rows<64, 32, false>(B, C, logits, labels, row_loss, dlogits, s);
-  else if (vec && C <= 32768)
-    e = launch_rows<256, 32, true>(B, C, logits, labels, row_loss, dlogits, s);
+  else if (vec && C <= 32768)  // 1024 threads per row: 8 float4 each, more loads in flight
+    e = launch_rows<1024, 8, true, 1024>(B, C, logits, labels, row_loss, dlogits, s);
   else {
     hipLaunchKernelGGL(xent_rows_wide_kernel, dim3((unsigned)B), dim3(kXentBlock), 0, s, B, C,
                        logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
