@@ -657,7 +657,7 @@ def test_profile_hook_times_each_launch(dl):
     assert dl.profile_end(0) == []
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (63, 130), (1024, 4096), (4096, 1000)])
+@pytest.mark.parametrize("shape", [(1, 1), (63, 130), (1024, 4096), (4096, 1000), (100, 68), (4, 8)])
 def test_cast_bf16_transposed_bit_exact(dl, shape):
     W = si.random_matrix(210, shape, scale=0.02)
     d, dt = dl.dense_cast_bf16_t(to_dev(W))
