@@ -85,9 +85,10 @@ bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 // least 32 such tiles, 128x128 otherwise; operands that kernel cannot take
 // (unaligned, K not a multiple of 64) go to the general 128x128 kernel.  Only
 // the weight-gradient product (K = batch) is split along K: when it has fewer
-// than two workgroups per CU, slices are added until about four per CU exist
-// (two for tile 2, whose LDS admits one workgroup per CU; at most 64 slices),
-// each slice keeping at least four K tiles.
+// than two workgroups per CU, the slice count is the smallest power of two
+// that gives at least four workgroups per CU (two for tile 2, whose LDS
+// admits one workgroup per CU; at most 64 slices), each slice keeping at
+// least four K tiles.
 
 constexpr int kCUs = 256;
 
@@ -130,7 +131,8 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
     tiles = ceil_div(M, bm) * ceil_div(N, bn);
   }
   if (epi == dl::EPI_DW && tiles < 2 * kCUs) {
-    int64_t want = ceil_div(per_cu * kCUs, tiles);
+    int64_t want = 1;  // a power of two: even slices of power-of-two batches
+    while (want * tiles < per_cu * kCUs) want *= 2;
     const int64_t max_by_k = std::max<int64_t>(1, K / (4 * bk));
     want = std::min<int64_t>(std::min<int64_t>(want, max_by_k), 64);
     int64_t kps = ceil_div(ceil_div(K, want), bk) * bk;
