@@ -497,8 +497,29 @@ static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l)
   return plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B).splits;
 }
 
+// Forward of a layer split along K: when its forward product has few tiles
+// (a small batch) but a long contraction, the product leaves float32
+// K-slices and a finishing kernel adds them in slice order with the bias and
+// activation.  The 64-row batch through the 784-input layer: 4 tiles, 5
+// slices of 160.
+constexpr int kFwdSplitTile = 1;  // 64x64, K step 32
+static Plan mlp_fwd_plan(int64_t B, const dl_layer_t& ly) {
+  Plan p{kFwdSplitTile, 1, (int)ly.in};
+  const int64_t tiles = ceil_div(B, 64) * ceil_div(ly.out, 64);
+  const int bk = 32;
+  if (tiles > 16 || ly.in < 16 * bk) return p;
+  int64_t want = 1;
+  while (want * tiles < 64) want *= 2;
+  want = std::min<int64_t>(want, ly.in / (4 * bk));
+  const int64_t kps = ceil_div(ceil_div(ly.in, want), bk) * bk;
+  p.k_per_split = (int)kps;
+  p.splits = (int)ceil_div(ly.in, kps);
+  if (p.splits <= 1) p = Plan{kFwdSplitTile, 1, (int)ly.in};
+  return p;
+}
+
 static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
-                         size_t* rl_off, size_t* part_off) {
+                         size_t* rl_off, size_t* part_off, size_t* fwd_off) {
   size_t off = 0;
   for (int l = 0; l < L; ++l) {
     y_off[l] = off;
@@ -513,15 +534,22 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
       off += align_up((size_t)S * layers[l].out * layers[l].in * 4) +
              align_up((size_t)S * layers[l].out * 4);
   }
-  return off;
+  // the split forwards' K-slices (one layer at a time)
+  *fwd_off = off;
+  size_t fwd = 0;
+  for (int l = 0; l < L; ++l) {
+    const Plan p = mlp_fwd_plan(B, layers[l]);
+    if (p.splits > 1) fwd = std::max(fwd, align_up((size_t)p.splits * B * layers[l].out * 4));
+  }
+  return off + fwd;
 }
 
 size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer_t* layers) {
   if (!dim_ok(B) || n_layers < 1 || n_layers > 16 || !layers) return 0;
   for (int l = 0; l < n_layers; ++l)
     if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
-  size_t y_off[16], rl, part[16];
-  return mlp_layout(B, n_layers, layers, y_off, &rl, part);
+  size_t y_off[16], rl, part[16], fwd;
+  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd);
 }
 
 int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
@@ -560,8 +588,8 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // activation of its own (its derivative would need the overwritten output).
   if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
     return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
-  size_t y_off[16], rl_off, part_off[16];
-  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off);
+  size_t y_off[16], rl_off, part_off[16], fwd_off;
+  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off, &fwd_off);
   if (!ws || ws_bytes < need)
     return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -590,7 +618,26 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   for (int l = 0; l <= last_gemm; ++l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
-    e = fwd_gemm(DL_F32, ly.act, B, ly.in, ly.out, in, ly.W, ly.b, Y[l], nullptr, s);
+    const Plan fp = mlp_fwd_plan(B, ly);
+    if (fp.splits > 1) {
+      float* slices = reinterpret_cast<float*>(base + fwd_off);
+      dl::GemmDesc d = blank_desc();
+      d.M = (int)B; d.N = (int)ly.out; d.K = (int)ly.in;
+      d.A = in; d.lda = ly.in; d.a_layout = dl::K_MAJOR;
+      d.B = ly.W; d.ldb = ly.in; d.b_layout = dl::K_MAJOR;
+      d.C = slices; d.ldc = ly.out;
+      d.epi = dl::EPI_DW;  // float32 slices, no column sums
+      d.splits = fp.splits; d.k_per_split = fp.k_per_split;
+      d.partial = slices;
+      e = timed("fwd_gemm", s, [&] { return dl::launch_gemm_f32(d, fp.tile, s); });
+      if (e == hipSuccess)
+        e = timed("fwd_finish", s, [&] {
+          return dl::launch_splitk_finish_fwd((int)B, (int)ly.out, fp.splits, slices, ly.b, ly.act,
+                                              Y[l], s);
+        });
+    } else {
+      e = fwd_gemm(DL_F32, ly.act, B, ly.in, ly.out, in, ly.W, ly.b, Y[l], nullptr, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (forward)");
   }
   if (fused) {

@@ -382,6 +382,9 @@ hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s);
 hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 const float* db_partial, float* C, int64_t ldc,
                                 float* db, hipStream_t s);
+// Y = act(b + slice-order sum of the float32 K-slices partial[S][M][N]).
+hipError_t launch_splitk_finish_fwd(int M, int N, int splits, const float* partial,
+                                    const float* bias, int act, float* Y, hipStream_t s);
 hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols,
                            const void* dY, const void* saved, void* G,
                            hipStream_t s);

@@ -40,6 +40,33 @@ splitk_reduce_kernel(int64_t MN, int64_t M, int splits, const float* __restrict_
   else reduce_slices(M, splits, db_partial, db, vec_db != 0, blockIdx.x - wblocks);
 }
 
+// Forward product split along K: Y[m, n] = act(b[n] + sum over slices s of
+// partial[s][m][n]), the slices added in order; one thread per 4 consecutive
+// outputs of a row.
+__global__ void __launch_bounds__(256)
+splitk_finish_fwd_kernel(int64_t MN, int N, int splits, const float* __restrict__ partial,
+                         const float* __restrict__ bias, int act, float* __restrict__ Y,
+                         int vec) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= MN) return;
+  if (vec) {  // N % 4 == 0: the 4 outputs share a row
+    f32x4 a = *reinterpret_cast<const f32x4*>(partial + e0);
+#pragma unroll 8
+    for (int sl = 1; sl < splits; ++sl) a += *reinterpret_cast<const f32x4*>(partial + sl * MN + e0);
+    const int n = (int)(e0 % N);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = act_apply(act, a[e] + (bias ? bias[n + e] : 0.f));
+    *reinterpret_cast<f32x4*>(Y + e0) = o;
+  } else {
+    for (int e = 0; e < 4 && e0 + e < MN; ++e) {
+      float a = partial[e0 + e];
+      for (int sl = 1; sl < splits; ++sl) a += partial[sl * MN + e0 + e];
+      Y[e0 + e] = act_apply(act, a + (bias ? bias[(e0 + e) % N] : 0.f));
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 act_mask_kernel(int act, int64_t n, const T* __restrict__ dY, const T* __restrict__ saved,
@@ -142,6 +169,18 @@ hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)(wblocks + dblocks)), dim3(256), 0, s,
                      MN, (int64_t)M, splits, partial, db_partial, C, db, vec, vec_db,
                      (unsigned)wblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_finish_fwd(int M, int N, int splits, const float* partial,
+                                    const float* bias, int act, float* Y, hipStream_t s) {
+  const int64_t MN = (int64_t)M * N;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const int vec = N % 4 == 0 && al16(partial) && al16(Y);
+  const int64_t blocks = (MN + 1023) / 1024;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_finish_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, s, MN, N, splits,
+                     partial, bias, act, Y, vec);
   return hipGetLastError();
 }
 

@@ -332,6 +332,9 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
     return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX>(d, s);
   if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
     return launch_tile<BM, BN, BK, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+  // float32 K-slices of a forward product (the MLP step's split forward)
+  if (d.epi == EPI_DW && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
+    return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DW>(d, s);
   return hipErrorInvalidValue;
 }
 
