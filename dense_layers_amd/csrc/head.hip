@@ -81,7 +81,10 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     const int nrows = (int)min<int64_t>(kHeadRows, B - r0);
     const int n = nrows * K;  // the tile is one contiguous run of H
     const float* src = H + r0 * K;
-    // every load of the tile in flight before the first LDS store
+    // every load of the tile (and the row's label) in flight before the
+    // first LDS store
+    const bool active = r < nrows;
+    const int y = active ? labels[r0 + r] : -1;
     float v[kHeadLoads];
     if (VEC) {
 #pragma unroll
@@ -121,8 +124,6 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     }
     __syncthreads();
 
-    const bool active = r < nrows;
-    const int y = active ? labels[r0 + r] : -1;
     const bool valid = y >= 0 && y < C;
     float z[kHeadCMax];
 #pragma unroll
