@@ -75,6 +75,31 @@ def _split(label):
 class MLPBench:
     """mlp_train_step workloads (784-256-128-10, the wide MLP)."""
 
+    def _layers_of_labels(self):
+        """Layer of each backward / split-forward launch, from the step's
+        launch order: the backward runs from the last GEMM layer down, each
+        layer as dwdx_gemm, or dw_gemm then (above layer 0) dx_gemm."""
+        labels = getattr(self, "labels", ())
+        last = self.w.n_layers - (2 if "head_xent#0" in labels else 1)
+        out, cur, fwd = {}, last, -1
+        for lab in labels:
+            name, _ = _split(lab)
+            if name == "fwd_gemm":
+                fwd += 1
+            elif name == "fwd_finish":
+                out[lab] = fwd
+            elif name == "dwdx_gemm":
+                out[lab] = cur
+                cur -= 1
+            elif name == "dw_gemm":
+                out[lab] = cur
+                if cur == 0:
+                    cur -= 1
+            elif name == "dx_gemm":
+                out[lab] = cur
+                cur -= 1
+        return out
+
     def __init__(self, dl, w, dev):
         import torch
         self.dl, self.w = dl, w
@@ -121,12 +146,16 @@ class MLPBench:
         w = self.w
         B, L = w.batch, w.n_layers
         name, k = _split(label)
-        # with the fused narrow head the last layer has no GEMM of its own
-        last = L - 2 if "head_xent#0" in getattr(self, "labels", ()) else L - 1
+        layer = self._layers_of_labels()
         if name == "fwd_gemm":
             l = k
+        elif name == "fwd_finish":  # latency-bound slice sum of a split forward
+            return None
+        elif name == "dwdx_gemm":   # the layer's dW and dX in one launch
+            l = layer[label]
+            return "flop", 2 * 2 * B * w.dims[l] * w.dims[l + 1]
         elif name in ("dw_gemm", "dx_gemm"):
-            l = last - k           # the backward pass runs from the last GEMM layer
+            l = layer[label]
         elif name == "xent":
             return "byte", 8 * B * w.dims[-1] + 8 * B
         elif name == "head_xent":

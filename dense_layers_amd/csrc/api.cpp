@@ -180,15 +180,14 @@ hipError_t fwd_gemm(int dtype, int act, int64_t B, int64_t in, int64_t out, cons
 // dW = G^T X (+ db = column sums of G), split-K partials in `partial_ws`.
 // With reduce = false and a split plan, the partial slices are left for the
 // caller (the optimizer kernel of the MLP step adds them up).
-hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
-                   float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true) {
+dl::GemmDesc dw_desc(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
+                     float* dW, float* db, void* partial_ws, const Plan& p) {
   dl::GemmDesc d = blank_desc();
   d.M = (int)out; d.N = (int)in; d.K = (int)B;
   d.A = G; d.lda = out; d.a_layout = dl::MN_MAJOR;
   d.B = X; d.ldb = in; d.b_layout = dl::MN_MAJOR;
   d.C = dW; d.ldc = in;
   d.epi = dl::EPI_DW;
-  const Plan p = plan_gemm(dtype, dl::EPI_DW, out, in, B);
   d.splits = p.splits;
   d.k_per_split = p.k_per_split;
   if (p.splits > 1) {
@@ -200,6 +199,14 @@ hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
   } else {
     d.db = db;
   }
+  (void)dtype;
+  return d;
+}
+
+hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
+                   float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true) {
+  const Plan p = plan_gemm(dtype, dl::EPI_DW, out, in, B);
+  const dl::GemmDesc d = dw_desc(dtype, B, in, out, G, X, dW, db, partial_ws, p);
   hipError_t e = timed("dw_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
   if (e != hipSuccess || p.splits == 1 || !reduce) return e;
   return timed("splitk_reduce", s, [&] {
@@ -210,8 +217,8 @@ hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
 
 // dX = G W, optionally times mask_act'(mask_src).  With Wt (W transposed,
 // [in, out]) the B operand is read along K.
-hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* W,
-                   const void* Wt, void* dX, int mask_act, const void* mask_src, hipStream_t s) {
+dl::GemmDesc dx_desc(int64_t B, int64_t in, int64_t out, const void* G, const void* W,
+                     const void* Wt, void* dX, int mask_act, const void* mask_src) {
   dl::GemmDesc d = blank_desc();
   d.M = (int)B; d.N = (int)in; d.K = (int)out;
   d.A = G; d.lda = out; d.a_layout = dl::K_MAJOR;
@@ -223,8 +230,14 @@ hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G,
   d.C = dX; d.ldc = in;
   d.epi = dl::EPI_DX;
   d.mask_act = mask_act; d.mask_src = mask_src;
-  const Plan p = plan_gemm(dtype, dl::EPI_DX, B, in, out);
   d.k_per_split = (int)out;
+  return d;
+}
+
+hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* W,
+                   const void* Wt, void* dX, int mask_act, const void* mask_src, hipStream_t s) {
+  const dl::GemmDesc d = dx_desc(B, in, out, G, W, Wt, dX, mask_act, mask_src);
+  const Plan p = plan_gemm(dtype, dl::EPI_DX, B, in, out);
   return timed("dx_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
 }
 
@@ -476,11 +489,13 @@ int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src
 
 // ---- whole MLP step ---------------------------------------------------------
 // Workspace: per-layer outputs Y_l [B, out_l] (the last one holds the logits,
-// then dlogits in place), the per-row losses, and one split-K partial buffer
-// per layer whose weight gradient is split along the batch.  During the
+// then dlogits in place), the per-row losses, one split-K partial buffer
+// per layer whose weight gradient is split along the batch, the K-slices of
+// a split forward, and the gradient buffers of paired layers.  During the
 // backward pass the dX epilogue of layer l writes
 // G_{l-1} = (G_l W_l) * relu'(Y_{l-1}) over Y_{l-1} in place, after layer l's
-// dW has consumed Y_{l-1}.  Split weight gradients are not reduced by a pass
+// dW has consumed Y_{l-1}; a layer whose dW and dX share one launch writes
+// G_{l-1} to a gradient buffer instead.  Split weight gradients are not reduced by a pass
 // of their own: the optimizer kernel adds the slices, stores dW / db and
 // applies the update in one read.
 
@@ -518,8 +533,19 @@ static Plan mlp_fwd_plan(int64_t B, const dl_layer_t& ly) {
   return p;
 }
 
+// Whether layer l (l > 0) runs its weight gradient and its dX as one launch:
+// both products small (the weight gradient on the 64x64 tile, the dX at
+// most 2^33 flop), so that one launch fills the GPU with both.  The dX then
+// goes to a gradient buffer of its own, since the weight gradient still reads
+// the layer input that the in-place form would overwrite.
+static bool mlp_pair(int64_t B, const dl_layer_t& ly) {
+  const Plan p = plan_gemm(DL_F32, dl::EPI_DW, ly.out, ly.in, B);
+  return p.tile == 1 && 2.0 * (double)B * (double)ly.in * (double)ly.out <= 8589934592.0;
+}
+
 static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
-                         size_t* rl_off, size_t* part_off, size_t* fwd_off) {
+                         size_t* rl_off, size_t* part_off, size_t* fwd_off, size_t* g_off,
+                         size_t* g_bytes) {
   size_t off = 0;
   for (int l = 0; l < L; ++l) {
     y_off[l] = off;
@@ -541,15 +567,27 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
     const Plan p = mlp_fwd_plan(B, layers[l]);
     if (p.splits > 1) fwd = std::max(fwd, align_up((size_t)p.splits * B * layers[l].out * 4));
   }
-  return off + fwd;
+  off += fwd;
+  // gradient buffers of the paired layers (two alternate when several pair)
+  const int last_gemm = mlp_fused_head(L, layers) ? L - 2 : L - 1;
+  int pairs = 0;
+  size_t gb = 0;
+  for (int l = 1; l <= last_gemm; ++l)
+    if (mlp_pair(B, layers[l])) {
+      ++pairs;
+      gb = std::max(gb, align_up((size_t)B * layers[l].in * 4));
+    }
+  *g_off = off;
+  *g_bytes = gb;
+  return off + (size_t)std::min(pairs, 2) * gb;
 }
 
 size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer_t* layers) {
   if (!dim_ok(B) || n_layers < 1 || n_layers > 16 || !layers) return 0;
   for (int l = 0; l < n_layers; ++l)
     if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
-  size_t y_off[16], rl, part[16], fwd;
-  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd);
+  size_t y_off[16], rl, part[16], fwd, g_off, g_bytes;
+  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd, &g_off, &g_bytes);
 }
 
 int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
@@ -588,8 +626,9 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // activation of its own (its derivative would need the overwritten output).
   if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
     return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
-  size_t y_off[16], rl_off, part_off[16], fwd_off;
-  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off, &fwd_off);
+  size_t y_off[16], rl_off, part_off[16], fwd_off, g_off, g_bytes;
+  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off, &fwd_off, &g_off,
+                                 &g_bytes);
   if (!ws || ws_bytes < need)
     return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -661,17 +700,33 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     e = timed("xent", s, [&] { return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s); });
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
   }
-  // backward
+  // backward; G holds the current layer's output gradient
+  float* gbuf[2] = {reinterpret_cast<float*>(base + g_off),
+                    reinterpret_cast<float*>(base + g_off + g_bytes)};
+  const float* G = Y[last_gemm];
   for (int l = last_gemm; l >= 0; --l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
-    e = dw_gemm(DL_F32, B, ly.in, ly.out, Y[l], in, ly.dW, ly.db, base + part_off[l], s,
+    if (l > 0 && mlp_pair(B, ly)) {
+      float* Gn = G == gbuf[0] ? gbuf[1] : gbuf[0];
+      const Plan p = plan_gemm(DL_F32, dl::EPI_DW, ly.out, ly.in, B);
+      const dl::GemmDesc dw = dw_desc(DL_F32, B, ly.in, ly.out, G, in, ly.dW, ly.db,
+                                      base + part_off[l], p);
+      const dl::GemmDesc dx = dx_desc(B, ly.in, ly.out, G, ly.W, nullptr, Gn, layers[l - 1].act,
+                                      Y[l - 1]);
+      e = timed("dwdx_gemm", s, [&] { return dl::launch_gemm_f32_dw_dx(dw, dx, s); });
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW + dX)");
+      G = Gn;
+      continue;
+    }
+    e = dw_gemm(DL_F32, B, ly.in, ly.out, G, in, ly.dW, ly.db, base + part_off[l], s,
                 /*reduce=*/false);
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
     if (l > 0) {
-      e = dx_gemm(DL_F32, B, ly.in, ly.out, Y[l], ly.W, nullptr, Y[l - 1], layers[l - 1].act,
+      e = dx_gemm(DL_F32, B, ly.in, ly.out, G, ly.W, nullptr, Y[l - 1], layers[l - 1].act,
                   Y[l - 1], s);
       if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dX)");
+      G = Y[l - 1];
     }
   }
   // optimizer over every W and b in one launch (finishing split-K sums)

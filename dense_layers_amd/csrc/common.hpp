@@ -108,12 +108,16 @@ __device__ __forceinline__ void band_coords(int id, int tiles_m, int tiles_n, in
   tn = in_band / gsz;
 }
 
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& split,
-                                            int& tm, int& tn) {
-  const int nwg = gridDim.x;
-  int id = blockIdx.x;
+// Workgroup `id` of `nwg` working on one product -> (split, tm, tn).
+__device__ __forceinline__ void tile_coords_at(int id, int nwg, int tiles_m, int tiles_n,
+                                               int& split, int& tm, int& tn) {
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   band_coords(id, tiles_m, tiles_n, split, tm, tn);
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& split,
+                                            int& tm, int& tn) {
+  tile_coords_at(blockIdx.x, gridDim.x, tiles_m, tiles_n, split, tm, tn);
 }
 
 // ---- GEMM launch descriptor ---------------------------------------------
@@ -376,6 +380,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], float* _
 // Host-side launchers (defined in the kernel files).
 hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s);
+// Weight gradient (M/N-major operands) and dX (K-major G, N-major W) of one
+// small float32 layer in one launch, 64x64 tiles for both.
+hipError_t launch_gemm_f32_dw_dx(const GemmDesc& dw, const GemmDesc& dx, hipStream_t s);
 // Direct-to-LDS bf16 GEMM; hipErrorNotSupported when the operands do not
 // meet its alignment / K-multiple requirements (nothing is launched then).
 hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s);

@@ -121,18 +121,28 @@ struct TileLoader {
   }
 };
 
+// LDS floats of one workgroup: two stages of both operand tiles, or the
+// epilogue's staging tile, whichever is larger.
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY>
+constexpr int f32_smem_floats() {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int ab = 2 * TileLoader<BM, BK, ALAY, NT>::kLdsSize + 2 * TileLoader<BN, BK, BLAY, NT>::kLdsSize;
+  constexpr int st = stage_floats<BM, BN, WGM>();
+  return ab > st ? ab : st;
+}
+
+// One workgroup's work item: workgroup `wg` of `nwg` working on the GEMM `d`
+// (tiles in the XCD-aware band order of tile_coords), LDS at `smem`.
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
-__global__ void __launch_bounds__(WGM * WGN * 64)
-gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
+__device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, int tiles_n,
+                                              int a_vec, int b_vec, int out_vec, int wg, int nwg,
+                                              float* smem) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1 && BK % 8 == 0, "bad tile");
   using LA = TileLoader<BM, BK, ALAY, NT>;
   using LB = TileLoader<BN, BK, BLAY, NT>;
-  constexpr int kSmemAB = 2 * LA::kLdsSize + 2 * LB::kLdsSize;
-  constexpr int kStage = stage_floats<BM, BN, WGM>();
-  __shared__ __attribute__((aligned(16))) float smem[kSmemAB > kStage ? kSmemAB : kStage];
   // buffer b of A at smem + b * LA::kLdsSize, of B after both A buffers
   auto As = [&](int b) { return smem + b * LA::kLdsSize; };
   auto Bs = [&](int b) { return smem + 2 * LA::kLdsSize + b * LB::kLdsSize; };
@@ -143,7 +153,7 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
   const int l32 = lane & 31, h = lane >> 5;
 
   int split, tm, tn;
-  tile_coords(tiles_m, tiles_n, split, tm, tn);
+  tile_coords_at(wg, nwg, tiles_m, tiles_n, split, tm, tn);
 
   const int M = d.M, N = d.N;
   const int kbeg = split * d.k_per_split;
@@ -300,25 +310,65 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
-hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
-  const int tiles_m = (d.M + BM - 1) / BM;
-  const int tiles_n = (d.N + BN - 1) / BN;
-  const int64_t nwg = (int64_t)tiles_m * tiles_n * d.splits;
-  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidValue;
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
+  __shared__ __attribute__((aligned(16))) float smem[f32_smem_floats<BM, BN, BK, WGM, WGN, ALAY, BLAY>()];
+  gemm_f32_body<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>(d, tiles_m, tiles_n, a_vec, b_vec, out_vec,
+                                                       blockIdx.x, gridDim.x, smem);
+}
+
+// The weight gradient and the dX of one small layer in one launch (64x64
+// tiles of 4 waves for both): workgroups [0, n_dw) take the dW items, the
+// rest the dX items.  The two products only read common inputs, so they may
+// run side by side; dX must not be written over either product's input.
+struct F32Job {
+  GemmDesc d;
+  int tiles_m, tiles_n, a_vec, b_vec, out_vec, nwg;
+};
+__global__ void __launch_bounds__(256)
+gemm_f32_dw_dx_kernel(F32Job dw, F32Job dx) {
+  constexpr int kDw = f32_smem_floats<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR>();
+  constexpr int kDx = f32_smem_floats<64, 64, 32, 2, 2, K_MAJOR, MN_MAJOR>();
+  __shared__ __attribute__((aligned(16))) float smem[kDw > kDx ? kDw : kDx];
+  const int b = blockIdx.x;
+  if (b < dw.nwg)
+    gemm_f32_body<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR, EPI_DW>(
+        dw.d, dw.tiles_m, dw.tiles_n, dw.a_vec, dw.b_vec, dw.out_vec, b, dw.nwg, smem);
+  else
+    gemm_f32_body<64, 64, 32, 2, 2, K_MAJOR, MN_MAJOR, EPI_DX>(
+        dx.d, dx.tiles_m, dx.tiles_n, dx.a_vec, dx.b_vec, dx.out_vec, b - dw.nwg, dx.nwg, smem);
+}
+
+// Grid shape and vector-access flags of one GEMM on a BM x BN tile.
+template <int BM, int BN>
+hipError_t make_job(const GemmDesc& d, F32Job& j) {
+  j.d = d;
+  j.tiles_m = (d.M + BM - 1) / BM;
+  j.tiles_n = (d.N + BN - 1) / BN;
+  const int64_t nwg = (int64_t)j.tiles_m * j.tiles_n * d.splits;
+  if (nwg <= 0 || nwg > 0x3fffffff) return hipErrorInvalidValue;
+  j.nwg = (int)nwg;
   auto aligned = [](const void* p, int64_t ld) {
     return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 4 == 0);
   };
-  const int a_vec = aligned(d.A, d.lda);
-  const int b_vec = aligned(d.B, d.ldb);
-  int out_vec;
-  if (EPI == EPI_DW && d.splits > 1)
-    out_vec = aligned(d.partial, d.N);
+  j.a_vec = aligned(d.A, d.lda);
+  j.b_vec = aligned(d.B, d.ldb);
+  if (d.epi == EPI_DW && d.splits > 1)
+    j.out_vec = aligned(d.partial, d.N);
   else
-    out_vec = aligned(d.C, d.ldc) && (d.Z == nullptr || aligned(d.Z, d.ldc)) &&
-              (d.mask_src == nullptr || aligned(d.mask_src, d.ldc));
+    j.out_vec = aligned(d.C, d.ldc) && (d.Z == nullptr || aligned(d.Z, d.ldc)) &&
+                (d.mask_src == nullptr || aligned(d.mask_src, d.ldc));
+  return hipSuccess;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
+  F32Job j;
+  const hipError_t e = make_job<BM, BN>(d, j);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>),
-                     dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m,
-                     tiles_n, a_vec, b_vec, out_vec);
+                     dim3((unsigned)j.nwg), dim3(WGM * WGN * 64), 0, s, d, j.tiles_m,
+                     j.tiles_n, j.a_vec, j.b_vec, j.out_vec);
   return hipGetLastError();
 }
 
@@ -351,6 +401,18 @@ hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s) {
     case 2: return dispatch_layout<64, 128, 32, 2, 4>(d, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_f32_dw_dx(const GemmDesc& dw, const GemmDesc& dx, hipStream_t s) {
+  if (dw.epi != EPI_DW || dw.a_layout != MN_MAJOR || dw.b_layout != MN_MAJOR ||
+      dx.epi != EPI_DX || dx.a_layout != K_MAJOR || dx.b_layout != MN_MAJOR)
+    return hipErrorInvalidValue;
+  F32Job a, b;
+  hipError_t e = make_job<64, 64>(dw, a);
+  if (e == hipSuccess) e = make_job<64, 64>(dx, b);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_f32_dw_dx_kernel, dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
+  return hipGetLastError();
 }
 
 }  // namespace dl
