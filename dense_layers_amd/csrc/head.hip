@@ -29,6 +29,24 @@ constexpr int kHeadMaxSlices = 256;                // workgroups (dW / db partia
 constexpr int kHeadPairs = kHeadKMax * (kHeadCMax / 4) / kHeadThreads;  // (k, 4 classes) per thread
 constexpr int kHeadLoads = kHeadRows * kHeadKMax / kHeadThreads;       // tile floats per thread
 
+// DPP move of v from the lane CTRL selects within its row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row, by DPP
+// moves (swap neighbours, swap pairs, mirror each half of 8, mirror the 16)
+// instead of LDS-routed shuffles.  Each lane adds the same two operands at
+// every step (in swapped order), so all 16 results are bit-identical.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Workgroup b takes row tiles [b * tiles_per, (b + 1) * tiles_per).  VEC:
 // K % 4 == 0 and H, dH 16-byte aligned (tile moved as float4).
 template <bool VEC>
@@ -128,7 +146,10 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     float z[kHeadCMax];
 #pragma unroll
     for (int c = 0; c < kHeadCMax; ++c) z[c] = 0.f;
-    for (int k = lr; k < K; k += kHeadTPR) {
+#pragma unroll
+    for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
+      const int k = lr + kk * kHeadTPR;
+      if (k >= K) break;
       const float h = Hs[r * KP + k];
 #pragma unroll
       for (int c4 = 0; c4 < kHeadCMax / 4; ++c4) {
@@ -140,8 +161,7 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     float m = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kHeadCMax; ++c) {
-#pragma unroll
-      for (int o = kHeadTPR / 2; o > 0; o >>= 1) z[c] += __shfl_xor(z[c], o);
+      z[c] = row16_sum(z[c]);
       z[c] += bc[c];
       if (c < C) m = fmaxf(m, z[c]);
     }
@@ -167,7 +187,10 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
       *reinterpret_cast<f32x4*>(&Ds[r * kHeadCMax + lr * 4]) = x;
     }
     if (dH != nullptr) {
-      for (int k = lr; k < K; k += kHeadTPR) {
+#pragma unroll
+      for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
+        const int k = lr + kk * kHeadTPR;
+        if (k >= K) break;
         float d = 0.f;
 #pragma unroll
         for (int c4 = 0; c4 < kHeadCMax / 4; ++c4) {
