@@ -22,6 +22,17 @@ Readings of passages the pages leave open (each listed in the design notes):
 * AdamW is decoupled decay applied before the moment update, bias-corrected,
   eps = 1e-8, one parameter group (biases decayed too), t counts from 1.
 * SGD is plain: no momentum, no decay.
+* Adam takes coupled (L2) decay: g + wd w enters both moments.
+* Gradient clipping scales every gradient of the step by
+  min(1, max_norm / (||g||_2 + 1e-6)), the norm taken over all arrays at once
+  (of the unscaled gradients when a loss scale is in use).
+* EMA: e <- d e + (1 - d) w after each applied update.
+* LR schedules count scheduler steps k = t - 1 from 0 (see ``lr_at``).
+* MSE is the mean over all B*C elements of (p - t)^2.
+* Dynamic loss scaling: the loss (hence every gradient) is multiplied by S; a
+  step whose scaled gradients hold a NaN or Inf is skipped and S is
+  multiplied by the backoff factor; after `interval` applied steps in a row S
+  is multiplied by the growth factor.
 """
 from __future__ import annotations
 
@@ -232,12 +243,167 @@ def adamw_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
     return w, m, v
 
 
+def adam_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+              weight_decay: float, t: int):
+    """One Adam step with coupled (L2) weight decay (t >= 1).
+
+    noeira.nn docs, "Optimizers & losses" and the Orthon page, "Core
+    capabilities" (Adam next to SGD and AdamW).  The decay is added to the
+    gradient, so it passes through both moments:
+    g' = g + wd w;  m <- b1 m + (1 - b1) g';  v <- b2 v + (1 - b2) g'^2;
+    w <- w - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+    Returns (w, m, v) in float64.
+    """
+    if t < 1:
+        raise ValueError("Adam step counts from 1")
+    w = np.asarray(w, np.float64)
+    g = np.asarray(g, np.float64) + weight_decay * w
+    m = beta1 * np.asarray(m, np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, np.float64) + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** t)
+    v_hat = v / (1.0 - beta2 ** t)
+    return w - lr * m_hat / (np.sqrt(v_hat) + eps), m, v
+
+
+CLIP_EPS = 1e-6
+
+
+def global_grad_norm(grads) -> float:
+    """The 2-norm of all gradient arrays taken together (MuNet page, "What
+    runs today": gradient clipping; noeira.nn docs, "Optimizers & losses")."""
+    total = 0.0
+    for g in grads:
+        g = np.asarray(g, np.float64)
+        total += float(np.sum(g * g))
+    return math.sqrt(total)
+
+
+def clip_coef(norm: float, max_norm: float) -> float:
+    """Factor applied to every gradient: min(1, max_norm / (norm + 1e-6))."""
+    return min(1.0, max_norm / (norm + CLIP_EPS))
+
+
+def ema_update(e, w, decay: float) -> np.ndarray:
+    """Exponential moving average of the parameters (MuNet page, "What runs
+    today": EMA in the compiled step): e <- decay e + (1 - decay) w."""
+    return decay * np.asarray(e, np.float64) + (1.0 - decay) * np.asarray(w, np.float64)
+
+
+LR_CONSTANT = 0
+LR_STEP = 1
+LR_WARMUP_COSINE = 2
+LR_WARMUP_LINEAR = 3
+
+
+def lr_at(kind: int, base_lr: float, t: int, warmup: int = 0, total: int = 1,
+          min_lr: float = 0.0, step_size: int = 1, gamma: float = 1.0) -> float:
+    """Learning rate of optimizer step t >= 1 (noeira.nn docs, "Optimizers &
+    losses": LR schedules).  With k = t - 1 scheduler steps taken:
+    constant: base;  step: base gamma^floor(k / step_size);
+    warmup-cosine: base (k + 1) / warmup for k < warmup, then
+      min + (base - min) (1 + cos(pi min(k - warmup, T) / T)) / 2,
+      T = total - warmup;
+    warmup-linear: the same warmup, then min + (base - min) (T - min(k - warmup, T)) / T.
+    """
+    if t < 1:
+        raise ValueError("steps count from 1")
+    k = t - 1
+    if kind == LR_CONSTANT:
+        return base_lr
+    if kind == LR_STEP:
+        return base_lr * gamma ** (k // step_size)
+    if kind in (LR_WARMUP_COSINE, LR_WARMUP_LINEAR):
+        if k < warmup:
+            return base_lr * (k + 1) / warmup
+        T = total - warmup
+        if T <= 0:
+            return min_lr
+        j = min(k - warmup, T)
+        if kind == LR_WARMUP_COSINE:
+            return min_lr + (base_lr - min_lr) * (1.0 + math.cos(math.pi * j / T)) / 2.0
+        return min_lr + (base_lr - min_lr) * (T - j) / T
+    raise ValueError(f"unknown schedule {kind}")
+
+
+def mse_loss_fwd_bwd(pred, target) -> Tuple[float, np.ndarray]:
+    """Mean squared error and its gradient (MuNet page, "Python training":
+    the step's mse_loss; noeira.nn docs, package layout: MSE among the
+    losses).  loss = (1/(B C)) sum (p - t)^2,  dpred = 2 (p - t) / (B C)."""
+    p = np.asarray(pred, np.float64)
+    t = np.asarray(target, np.float64)
+    if p.shape != t.shape:
+        raise ValueError("pred and target shapes differ")
+    n = p.size
+    d = p - t
+    return float(np.sum(d * d) / n), 2.0 * d / n
+
+
+class LossScaler:
+    """Dynamic loss scale (Orthon page, "Core capabilities": GradScaler with
+    finite checks, skipped steps, backoff and growth).  ``update`` takes
+    whether this step's scaled gradients held a NaN or Inf."""
+
+    def __init__(self, scale: float = 65536.0, growth_factor: float = 2.0,
+                 backoff_factor: float = 0.5, growth_interval: int = 2000):
+        self.scale = float(scale)
+        self.growth_factor = float(growth_factor)
+        self.backoff_factor = float(backoff_factor)
+        self.growth_interval = int(growth_interval)
+        self.tracker = 0
+
+    def update(self, found_inf: bool) -> None:
+        if found_inf:
+            self.scale = float(np.float32(self.scale * self.backoff_factor))
+            self.tracker = 0
+            return
+        self.tracker += 1
+        if self.tracker == self.growth_interval:
+            self.scale = float(np.float32(self.scale * self.growth_factor))
+            self.tracker = 0
+
+
+def grad_control(scaled_grads, max_norm: float = 0.0, scale: float = 1.0):
+    """What the optimizer applies to gradients handed over multiplied by the
+    loss scale: (found_inf, norm of the unscaled gradients, multiplier).
+    found_inf: a NaN or Inf among the scaled (stored) gradients.  The
+    multiplier is coef / scale, coef = clip_coef(norm, max_norm) when
+    max_norm > 0, else 1."""
+    found = any(not np.all(np.isfinite(np.asarray(g, np.float64))) for g in scaled_grads)
+    norm = global_grad_norm([np.asarray(g, np.float64) / scale for g in scaled_grads])
+    coef = clip_coef(norm, max_norm) if max_norm > 0 else 1.0
+    return found, norm, coef / scale
+
+
+def optimizer_update(kind: str, w, g, m, v, opt, t: int, lr: float):
+    """One element-wise update of an array by kind ("sgd", "adam", "adamw")
+    with learning rate lr; returns (w, m, v) in float64 (m, v None for SGD)."""
+    if kind == "sgd":
+        return sgd_step(w, g, lr), None, None
+    args = (lr, opt.beta1, opt.beta2, opt.eps, opt.weight_decay, t)
+    if kind == "adamw":
+        return adamw_step(w, g, m, v, *args)
+    if kind == "adam":
+        return adam_step(w, g, m, v, *args)
+    raise ValueError(f"unknown optimizer {kind}")
+
+
+def opt_lr(opt, t: int) -> float:
+    """The optimizer's learning rate at step t: its schedule if it has one."""
+    sched = getattr(opt, "schedule", None)
+    if sched is None:
+        return opt.lr
+    return lr_at(sched.kind, opt.lr, t, sched.warmup, sched.total, sched.min_lr,
+                 sched.step_size, sched.gamma)
+
+
 # ---------------------------------------------------------------------------
 # One MLP training step
 # ---------------------------------------------------------------------------
 
 class MLPState:
-    """Parameters and optimizer state, stored in float32 between steps."""
+    """Parameters and optimizer state, stored in float32 between steps.
+    ``eW`` / ``eb`` hold the parameters' moving averages once ``enable_ema``
+    has set them to copies of the parameters."""
 
     def __init__(self, W: Sequence[np.ndarray], b: Sequence[np.ndarray]):
         self.W = [round_f32(w) for w in W]
@@ -246,12 +412,19 @@ class MLPState:
         self.vW = [np.zeros_like(w) for w in self.W]
         self.mb = [np.zeros_like(x) for x in self.b]
         self.vb = [np.zeros_like(x) for x in self.b]
+        self.eW = None
+        self.eb = None
         self.t = 0
+
+    def enable_ema(self) -> None:
+        self.eW = [w.copy() for w in self.W]
+        self.eb = [x.copy() for x in self.b]
 
 
 def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
-                   relu_masks: Optional[List[Optional[np.ndarray]]] = None):
-    """Forward, softmax-xent, backward and optimizer update of an MLP.
+                   relu_masks: Optional[List[Optional[np.ndarray]]] = None,
+                   scaler: Optional[LossScaler] = None, targets=None):
+    """Forward, loss, backward and optimizer update of an MLP.
 
     MuNet page, "Python training" (the compiled step: zero grads, loss,
     backward, optimizer step, the loss returned as computed before the update)
@@ -260,12 +433,23 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
     pass composes the layers' vjps from the last layer to the first; the first
     layer's dX is not needed.
 
-    ``opt`` has ``kind`` ("sgd"/"adamw"), ``lr``, ``beta1``, ``beta2``,
-    ``eps``, ``weight_decay``.  ``relu_masks[l]``, when given, replaces layer
-    l's ReLU mask (used only to adopt the other side's decision inside the
-    rounding band).  Updates ``state`` in place (rounded to float32) and
-    returns a dict with the loss (pre-update), the float64 gradients, each
-    layer's masked upstream gradient G, its input h and pre-activation Z.
+    The loss is softmax cross-entropy against ``labels``, or, when
+    ``targets`` is given (labels None), the mean squared error against them.
+
+    ``opt`` has ``kind`` ("sgd", "adam", "adamw"), ``lr``, ``beta1``,
+    ``beta2``, ``eps``, ``weight_decay`` and optionally ``max_grad_norm``
+    (> 0: clip the global gradient norm), ``ema_decay`` (moving averages in
+    ``state.eW`` / ``state.eb``) and ``schedule`` (see ``opt_lr``).  With a
+    ``scaler`` the gradients are formed for the loss times its scale, a step
+    with non-finite scaled gradients is skipped (no parameter, moment,
+    average or step-count change) and the scale is updated.
+    ``relu_masks[l]``, when given, replaces layer l's ReLU mask (used only to
+    adopt the other side's decision inside the rounding band).  Updates
+    ``state`` in place (rounded to float32) and returns a dict with the loss
+    (pre-update, unscaled), the float64 gradients (times the loss scale, as
+    the backward forms them), whether the step was skipped, the norm and
+    multiplier applied, each layer's masked upstream gradient G (unscaled),
+    its input h and pre-activation Z.
     """
     L = len(state.W)
     h = [np.asarray(X, dtype=np.float64)]
@@ -274,7 +458,11 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
         Y, Z = dense_act_fwd(h[-1], state.W[l], state.b[l], acts[l])
         Zs.append(Z)
         h.append(Y)
-    loss, dz, row_loss = softmax_xent_fwd_bwd(h[-1], labels)
+    if targets is None:
+        loss, dz, row_loss = softmax_xent_fwd_bwd(h[-1], labels)
+    else:
+        loss, dz = mse_loss_fwd_bwd(h[-1], targets)
+        row_loss = None
     grads_W: List[np.ndarray] = [None] * L
     grads_b: List[np.ndarray] = [None] * L
     Gs: List[np.ndarray] = [None] * L
@@ -286,23 +474,36 @@ def mlp_train_step(state: MLPState, X, labels, acts: Sequence[int], opt,
         grads_W[l], grads_b[l] = dW, db
         Gs[l] = dY * (act_grad(Zs[l], acts[l]) if mask is None else mask)
         dY = dX
+    # gradient control: the backward ran on the scaled loss, so the stored
+    # gradients are S g; the finite check looks at them in float32
+    S = scaler.scale if scaler is not None else 1.0
+    scaled = [round_f32(S * g) for g in grads_W + grads_b]
+    max_norm = getattr(opt, "max_grad_norm", 0.0) or 0.0
+    found, norm, mul = grad_control(scaled, max_norm, S) if (scaler or max_norm > 0) \
+        else (False, None, 1.0)
+    coef = mul * S
+    result = {"loss": loss, "row_loss": row_loss,
+              "dW": [S * g for g in grads_W], "db": [S * g for g in grads_b],
+              "skipped": found, "norm": norm, "coef": coef,
+              "G": Gs, "Z": Zs, "h": h, "dlogits": dz}
+    if scaler is not None:
+        scaler.update(found)
+    if found:
+        return result
     state.t += 1
+    lr = opt_lr(opt, state.t)
+    decay = getattr(opt, "ema_decay", None)
     for l in range(L):
-        if opt.kind == "sgd":
-            state.W[l] = round_f32(sgd_step(state.W[l], grads_W[l], opt.lr))
-            state.b[l] = round_f32(sgd_step(state.b[l], grads_b[l], opt.lr))
-        elif opt.kind == "adamw":
-            args = (opt.lr, opt.beta1, opt.beta2, opt.eps, opt.weight_decay,
-                    state.t)
-            w, m, v = adamw_step(state.W[l], grads_W[l], state.mW[l],
-                                 state.vW[l], *args)
-            state.W[l], state.mW[l], state.vW[l] = (round_f32(w), round_f32(m),
-                                                    round_f32(v))
-            w, m, v = adamw_step(state.b[l], grads_b[l], state.mb[l],
-                                 state.vb[l], *args)
-            state.b[l], state.mb[l], state.vb[l] = (round_f32(w), round_f32(m),
-                                                    round_f32(v))
-        else:
-            raise ValueError(f"unknown optimizer {opt.kind}")
-    return {"loss": loss, "row_loss": row_loss, "dW": grads_W, "db": grads_b,
-            "G": Gs, "Z": Zs, "h": h, "dlogits": dz}
+        for name, mname, vname, ename, g in (("W", "mW", "vW", "eW", grads_W[l]),
+                                            ("b", "mb", "vb", "eb", grads_b[l])):
+            arrs = getattr(state, name)
+            ms, vs = getattr(state, mname), getattr(state, vname)
+            w, m, v = optimizer_update(opt.kind, arrs[l], coef * g, ms[l], vs[l],
+                                       opt, state.t, lr)
+            arrs[l] = round_f32(w)
+            if m is not None:
+                ms[l], vs[l] = round_f32(m), round_f32(v)
+            if decay is not None:
+                es = getattr(state, ename)
+                es[l] = round_f32(ema_update(es[l], arrs[l], decay))
+    return result

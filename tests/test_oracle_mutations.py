@@ -119,3 +119,93 @@ def test_mlp_missing_hidden_mask_caught(monkeypatch):
 
     monkeypatch.setattr(D, "dense_act_vjp", no_mask)
     _expect_pin_failure(P.test_mlp_step_gradients_central_difference)
+
+
+# ---- optimizer, loss and gradient-control variants
+
+from tests import test_oracle_pins_train as PT  # noqa: E402
+
+
+def test_adam_with_decoupled_decay_caught(monkeypatch):
+    monkeypatch.setattr(O, "adam_step", D.adamw_step)
+    _expect_pin_failure(PT.test_adam_matches_torch_adam_many_steps)
+
+
+def test_clip_without_eps_caught(monkeypatch):
+    monkeypatch.setattr(O, "clip_coef", lambda norm, mx: min(1.0, mx / norm))
+    _expect_pin_failure(PT.test_global_norm_and_clip_coef_hand_values)
+
+
+def test_norm_without_square_root_caught(monkeypatch):
+    def sq(grads):
+        return float(sum(np.sum(np.asarray(g, np.float64) ** 2) for g in grads))
+
+    monkeypatch.setattr(O, "global_grad_norm", sq)
+    _expect_pin_failure(PT.test_clip_matches_torch_clip_grad_norm)
+
+
+def test_ema_swapped_weights_caught(monkeypatch):
+    monkeypatch.setattr(O, "ema_update", lambda e, w, d: d * np.asarray(w) + (1 - d) * np.asarray(e))
+    _expect_pin_failure(PT.test_ema_constant_parameter_closed_form)
+
+
+def test_warmup_off_by_one_caught(monkeypatch):
+    real = D.lr_at
+
+    def wrong(kind, base, t, warmup=0, total=1, min_lr=0.0, step_size=1, gamma=1.0):
+        if kind == O.LR_WARMUP_COSINE and t - 1 < warmup:
+            return base * (t - 1) / warmup
+        return real(kind, base, t, warmup, total, min_lr, step_size, gamma)
+
+    monkeypatch.setattr(O, "lr_at", wrong)
+    _expect_pin_failure(PT.test_lr_schedules_match_torch_schedulers)
+
+
+def test_mse_missing_factor_two_caught(monkeypatch):
+    real = D.mse_loss_fwd_bwd
+
+    def wrong(p, t):
+        loss, d = real(p, t)
+        return loss, d / 2
+
+    monkeypatch.setattr(O, "mse_loss_fwd_bwd", wrong)
+    _expect_pin_failure(PT.test_mse_matches_torch_and_central_difference)
+
+
+def test_scaler_early_growth_caught(monkeypatch):
+    def update(self, found_inf):
+        if found_inf:
+            self.scale *= self.backoff_factor
+            self.tracker = 0
+            return
+        self.tracker += 1
+        if self.tracker >= self.growth_interval - 1:
+            self.scale *= self.growth_factor
+            self.tracker = 0
+
+    monkeypatch.setattr(O.LossScaler, "update", update)
+    _expect_pin_failure(PT.test_loss_scaler_hand_trajectory)
+
+
+def test_norm_of_scaled_gradients_caught(monkeypatch):
+    real = D.grad_control
+
+    def wrong(scaled, max_norm=0.0, scale=1.0):
+        found, _, mul = real(scaled, max_norm, scale)
+        return found, O.global_grad_norm(scaled), mul
+
+    monkeypatch.setattr(O, "grad_control", wrong)
+    _expect_pin_failure(PT.test_grad_control_finite_check_and_multiplier)
+
+
+def test_skipped_step_counting_caught(monkeypatch):
+    real = D.mlp_train_step
+
+    def wrong(state, *a, **k):
+        out = real(state, *a, **k)
+        if out["skipped"]:
+            state.t += 1
+        return out
+
+    monkeypatch.setattr(O, "mlp_train_step", wrong)
+    _expect_pin_failure(PT.test_mlp_scaler_skips_non_finite_step_and_backs_off)
