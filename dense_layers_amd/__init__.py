@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "lib", "libdense_layers_amd.so")
 
 DL_F32, DL_BF16 = 0, 1
 ACT_IDENTITY, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
-OPT_SGD, OPT_ADAMW = 0, 1
+OPT_SGD, OPT_ADAMW, OPT_ADAM = 0, 1, 2
+LR_CONSTANT, LR_STEP, LR_WARMUP_COSINE, LR_WARMUP_LINEAR = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "ALIASING",
           4: "WORKSPACE_TOO_SMALL", 5: "HIP_ERROR"}
 
@@ -49,14 +50,36 @@ class DLLayer(ctypes.Structure):
     _fields_ = [("in_", ctypes.c_int64), ("out", ctypes.c_int64),
                 ("act", ctypes.c_int32),
                 ("W", _vp), ("b", _vp), ("dW", _vp), ("db", _vp),
-                ("mW", _vp), ("vW", _vp), ("mb", _vp), ("vb", _vp)]
+                ("mW", _vp), ("vW", _vp), ("mb", _vp), ("vb", _vp),
+                ("eW", _vp), ("eb", _vp)]
+
+
+class DLLrSchedule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("warmup", ctypes.c_int64),
+                ("total", ctypes.c_int64), ("step_size", ctypes.c_int64),
+                ("min_lr", ctypes.c_double), ("gamma", ctypes.c_double)]
+
+
+class DLLossScaler(ctypes.Structure):
+    _fields_ = [("scale", _vp), ("growth_tracker", _vp), ("found_inf", _vp),
+                ("growth_factor", ctypes.c_double), ("backoff_factor", ctypes.c_double),
+                ("growth_interval", ctypes.c_int32)]
 
 
 class DLOpt(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("lr", ctypes.c_double),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("step", ctypes.c_int64), ("step_dev", ctypes.c_void_p)]
+                ("step", ctypes.c_int64), ("step_dev", ctypes.c_void_p),
+                ("max_grad_norm", ctypes.c_double), ("ema_decay", ctypes.c_double),
+                ("schedule", ctypes.POINTER(DLLrSchedule)),
+                ("scaler", ctypes.POINTER(DLLossScaler)),
+                ("grad_norm", _vp)]
+
+
+class DLParam(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("w", _vp), ("g", _vp), ("m", _vp), ("v", _vp),
+                ("ema", _vp), ("w_bf16", _vp)]
 
 
 def _sig(name, res, args):
@@ -89,6 +112,22 @@ _c = {
                             ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
     "mlp_train_step_workspace_size": _sig("mlp_train_step_workspace_size", _sz,
                                           [_i64, _i32, ctypes.POINTER(DLLayer)]),
+    "adam_step": _sig("adam_step", _i32,
+                      [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
+    "ema_update": _sig("ema_update", _i32, [_vp, _i64, _vp, _vp, _f64]),
+    "clip_grad_norm": _sig("clip_grad_norm", _i32,
+                           [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_i64), _f64, _vp,
+                            _vp, _sz]),
+    "clip_grad_norm_workspace_size": _sig("clip_grad_norm_workspace_size", _sz,
+                                          [_i32, ctypes.POINTER(_i64)]),
+    "optimizer_step": _sig("optimizer_step", _i32,
+                           [_vp, ctypes.POINTER(DLOpt), _i32, ctypes.POINTER(DLParam), _vp, _sz]),
+    "optimizer_step_workspace_size": _sig("optimizer_step_workspace_size", _sz,
+                                          [_i32, ctypes.POINTER(DLParam)]),
+    "mse_loss_fwd_bwd": _sig("mse_loss_fwd_bwd", _i32,
+                             [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "mse_loss_workspace_size": _sig("mse_loss_workspace_size", _sz, [_i64, _i64]),
+    "dl_lr_at": _sig("dl_lr_at", _f64, [ctypes.POINTER(DLLrSchedule), _f64, _i64]),
     "dl_profile_begin": _sig("dl_profile_begin", _i32, [_i32]),
     "dl_profile_end": _sig("dl_profile_end", _i32, [_i32, _vp, _vp]),
 }
@@ -97,7 +136,9 @@ EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
            "dense_cast_bf16", "dense_cast_bf16_t", "mlp_train_step",
-           "mlp_train_step_workspace_size",
+           "mlp_train_step_workspace_size", "adam_step", "ema_update", "clip_grad_norm",
+           "clip_grad_norm_workspace_size", "optimizer_step", "optimizer_step_workspace_size",
+           "mse_loss_fwd_bwd", "mse_loss_workspace_size", "dl_lr_at",
            "dl_profile_begin", "dl_profile_end"]
 
 
@@ -295,6 +336,148 @@ def adamw_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
     return w
 
 
+def adam_step(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+              weight_decay: float, step: int):
+    """Adam with coupled (L2) weight decay, in place on w, m, v."""
+    for t, n in ((w, "w"), (g, "g"), (m, "m"), (v, "v")):
+        _dev(t, n, torch.float32, tuple(w.shape))
+    _check(_c["adam_step"](_stream(w), w.numel(), _ptr(w), _ptr(g), _ptr(m), _ptr(v), lr,
+                           beta1, beta2, eps, weight_decay, step))
+    return w
+
+
+def ema_update(ema: torch.Tensor, w: torch.Tensor, decay: float):
+    """ema <- decay ema + (1 - decay) w, in place."""
+    _dev(ema, "ema", torch.float32)
+    _dev(w, "w", torch.float32, tuple(ema.shape))
+    _check(_c["ema_update"](_stream(w), w.numel(), _ptr(ema), _ptr(w), decay))
+    return ema
+
+
+def clip_grad_norm(grads: Sequence[torch.Tensor], max_norm: float,
+                   total_norm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Scale the gradients in place so their global 2-norm is at most max_norm;
+    returns the device norm (before clipping)."""
+    grads = list(grads)
+    for k, g in enumerate(grads):
+        _dev(g, f"grads[{k}]", torch.float32)
+    dev = grads[0].device
+    if total_norm is None:
+        total_norm = torch.empty(1, dtype=torch.float32, device=dev)
+    ptrs = (_vp * len(grads))(*[_ptr(g) for g in grads])
+    ns = (_i64 * len(grads))(*[g.numel() for g in grads])
+    need = int(_c["clip_grad_norm_workspace_size"](len(grads), ns))
+    ws = _workspace(need, dev)
+    _check(_c["clip_grad_norm"](_stream(grads[0]), len(grads), ptrs, ns, max_norm,
+                                _ptr(total_norm), _ptr(ws), 0 if ws is None else ws.numel()))
+    return total_norm
+
+
+class Schedule:
+    """Learning-rate schedule over optimizer steps t >= 1 (see dl_lr_schedule_t)."""
+
+    def __init__(self, kind: int = LR_CONSTANT, warmup: int = 0, total: int = 1,
+                 min_lr: float = 0.0, step_size: int = 1, gamma: float = 1.0):
+        self.c = DLLrSchedule(kind, warmup, total, step_size, min_lr, gamma)
+
+    def lr_at(self, lr: float, step: int) -> float:
+        return float(_c["dl_lr_at"](ctypes.byref(self.c), lr, step))
+
+
+class LossScaler:
+    """Dynamic loss scale held in device memory (scale, growth tracker and the
+    last step's found_inf flag), updated by the optimizer on the device."""
+
+    def __init__(self, device, init_scale: float = 65536.0, growth_factor: float = 2.0,
+                 backoff_factor: float = 0.5, growth_interval: int = 2000):
+        self.scale = torch.full((1,), init_scale, dtype=torch.float32, device=device)
+        self.growth_tracker = torch.zeros(1, dtype=torch.int32, device=device)
+        self.found_inf = torch.zeros(1, dtype=torch.int32, device=device)
+        self.c = DLLossScaler(_ptr(self.scale), _ptr(self.growth_tracker), _ptr(self.found_inf),
+                              growth_factor, backoff_factor, growth_interval)
+
+
+def _opt_struct(kind, lr, beta1, beta2, eps, weight_decay, step, step_dev, max_grad_norm,
+                ema_decay, schedule, scaler, grad_norm) -> DLOpt:
+    o = DLOpt(kind, lr, beta1, beta2, eps, weight_decay, step, _ptr(step_dev), max_grad_norm,
+              ema_decay)
+    if schedule is not None:
+        o.schedule = ctypes.pointer(schedule.c)
+    if scaler is not None:
+        o.scaler = ctypes.pointer(scaler.c)
+    o.grad_norm = _ptr(grad_norm)
+    return o
+
+
+class Param:
+    """One array for optimizer_step: value w, gradient g, Adam moments m and v,
+    and optionally its average and a bf16 copy of the updated value."""
+
+    def __init__(self, w, g, m=None, v=None, ema=None, w_bf16=None):
+        _dev(w, "w", torch.float32)
+        for t, n in ((g, "g"), (m, "m"), (v, "v"), (ema, "ema")):
+            if t is not None:
+                _dev(t, n, torch.float32, tuple(w.shape))
+        if w_bf16 is not None:
+            _dev(w_bf16, "w_bf16", torch.bfloat16, tuple(w.shape))
+        self.w, self.g, self.m, self.v, self.ema, self.w_bf16 = w, g, m, v, ema, w_bf16
+
+    def struct(self) -> DLParam:
+        return DLParam(self.w.numel(), _ptr(self.w), _ptr(self.g), _ptr(self.m), _ptr(self.v),
+                       _ptr(self.ema), _ptr(self.w_bf16))
+
+
+def optimizer_step(params: Sequence[Param], kind: int = OPT_ADAMW, lr: float = 1e-3,
+                   beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                   weight_decay: float = 0.0, step: int = 1, step_dev=None,
+                   max_grad_norm: float = 0.0, ema_decay: float = 0.0, schedule=None,
+                   scaler=None, grad_norm=None, ws=None):
+    """One fused multi-array update (see optimizer_step in the C header)."""
+    params = list(params)
+    table = (DLParam * len(params))(*[p.struct() for p in params])
+    opt = _opt_struct(kind, lr, beta1, beta2, eps, weight_decay, step, step_dev, max_grad_norm,
+                      ema_decay, schedule, scaler, grad_norm)
+    dev = params[0].w.device
+    if ws is None:
+        need = int(_c["optimizer_step_workspace_size"](len(params), table))
+        ws = _workspace(need, dev)
+    _check(_c["optimizer_step"](_stream(params[0].w), ctypes.byref(opt), len(params), table,
+                                _ptr(ws), 0 if ws is None else ws.numel()))
+
+
+def optimizer_step_workspace_size(params: Sequence[Param]) -> int:
+    params = list(params)
+    table = (DLParam * len(params))(*[p.struct() for p in params])
+    return int(_c["optimizer_step_workspace_size"](len(params), table))
+
+
+def mse_loss_workspace_size(B: int, C: int) -> int:
+    return int(_c["mse_loss_workspace_size"](B, C))
+
+
+def mse_loss_fwd_bwd(pred: torch.Tensor, target: torch.Tensor,
+                     dpred: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, in_place: bool = False):
+    """Mean squared error over all elements and its gradient; returns (loss, dpred)."""
+    _dev(pred, "pred", torch.float32)
+    if pred.dim() != 2:
+        raise ValueError("pred must be [B, C]")
+    B, C = pred.shape
+    _dev(target, "target", torch.float32, (B, C))
+    if in_place:
+        dpred = pred
+    elif dpred is None:
+        dpred = torch.empty_like(pred)
+    _dev(dpred, "dpred", torch.float32, (B, C))
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=pred.device)
+    if ws is None:
+        ws = _workspace(mse_loss_workspace_size(B, C), pred.device)
+    _check(_c["mse_loss_fwd_bwd"](_stream(pred), B, C, _ptr(pred), _ptr(target), _ptr(loss),
+                                  _ptr(dpred), _ptr(ws), 0 if ws is None else ws.numel()))
+    return loss, dpred
+
+
 def dense_cast_bf16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
                       dst_t: Optional[torch.Tensor] = None, copy: bool = True,
                       transposed: bool = True):
@@ -331,7 +514,7 @@ class MLP:
     in place; the table holds their pointers."""
 
     def __init__(self, Ws: Sequence[torch.Tensor], bs: Sequence[torch.Tensor],
-                 acts: Sequence[int], batch: int, adamw: bool):
+                 acts: Sequence[int], batch: int, adamw: bool, ema: bool = False):
         self.L = len(Ws)
         dev = Ws[0].device
         self.W = [_dev(w, f"W{l}", torch.float32).contiguous() for l, w in enumerate(Ws)]
@@ -345,6 +528,12 @@ class MLP:
             self.vb = [torch.zeros_like(x) for x in self.b]
         else:
             self.mW = self.vW = self.mb = self.vb = [None] * self.L
+        # parameter averages, starting from the initial parameters
+        if ema:
+            self.eW = [w.clone() for w in self.W]
+            self.eb = [x.clone() for x in self.b]
+        else:
+            self.eW = self.eb = [None] * self.L
         self.acts = [_act(a) for a in acts]
         self.batch = batch
         self.table = (DLLayer * self.L)()
@@ -352,7 +541,8 @@ class MLP:
             out, n_in = self.W[l].shape
             self.table[l] = DLLayer(n_in, out, self.acts[l], _ptr(self.W[l]), _ptr(self.b[l]),
                                     _ptr(self.dW[l]), _ptr(self.db[l]), _ptr(self.mW[l]),
-                                    _ptr(self.vW[l]), _ptr(self.mb[l]), _ptr(self.vb[l]))
+                                    _ptr(self.vW[l]), _ptr(self.mb[l]), _ptr(self.vb[l]),
+                                    _ptr(self.eW[l]), _ptr(self.eb[l]))
         need = mlp_train_step_workspace_size(batch, self.table)
         self.ws = _workspace(need, dev)
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
@@ -368,18 +558,22 @@ def mlp_train_step_workspace_size(B: int, table) -> int:
 def mlp_train_step(mlp: MLP, X: torch.Tensor, labels: torch.Tensor, kind: int = OPT_SGD,
                    lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
                    eps: float = 1e-8, weight_decay: float = 0.0,
-                   step: Optional[int] = None, device_step: bool = False) -> torch.Tensor:
+                   step: Optional[int] = None, device_step: bool = False,
+                   max_grad_norm: float = 0.0, ema_decay: float = 0.0, schedule=None,
+                   scaler=None, grad_norm: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One forward / softmax-xent / backward / optimizer step; returns the
     device loss tensor (computed before the update).  With device_step the
-    AdamW step count lives in mlp.step_dev and advances on the device (the
-    form a captured graph can replay)."""
+    step count lives in mlp.step_dev and advances on the device (the form a
+    captured graph can replay, and the one a loss scaler needs, since a
+    skipped step does not count)."""
     _dev(X, "X", torch.float32, (mlp.batch, mlp.W[0].shape[1]))
     _dev(labels, "labels", torch.int32, (mlp.batch,))
     if step is None:
         step = mlp.step_count + 1
     mlp.step_count = step
-    opt = DLOpt(kind, lr, beta1, beta2, eps, weight_decay, step,
-                _ptr(mlp.step_dev) if device_step else None)
+    opt = _opt_struct(kind, lr, beta1, beta2, eps, weight_decay, step,
+                      mlp.step_dev if device_step else None, max_grad_norm, ema_decay, schedule,
+                      scaler, grad_norm)
     _check(_c["mlp_train_step"](_stream(X), mlp.batch, mlp.L, mlp.table, _ptr(X),
                                 _ptr(labels), ctypes.byref(opt), _ptr(mlp.loss), _ptr(mlp.ws),
                                 0 if mlp.ws is None else mlp.ws.numel()))
@@ -391,7 +585,8 @@ class StepGraph:
     launches of mlp_train_step are recorded once (on a side stream, as torch
     requires) and replay() issues them again with one call.  X and labels are
     the tensors the graph reads, so new data goes in by copying into them.
-    AdamW runs with the device step count, so every replay is the next step.
+    Adam, AdamW, schedules and loss scaling run with the device step count,
+    so every replay is the next step.
     The library allocates nothing and records no memory fills, so the graph
     holds only its kernels."""
 
@@ -404,7 +599,9 @@ class StepGraph:
         side.wait_stream(torch.cuda.current_stream(X.device))
         with torch.cuda.stream(side):
             with torch.cuda.graph(self.graph, stream=side):
-                mlp_train_step(mlp, X, labels, kind, device_step=(kind == OPT_ADAMW), **opt)
+                dev = kind != OPT_SGD or opt.get("schedule") is not None or \
+                    opt.get("scaler") is not None
+                mlp_train_step(mlp, X, labels, kind, device_step=dev, **opt)
         torch.cuda.current_stream(X.device).wait_stream(side)
 
     def replay(self) -> torch.Tensor:

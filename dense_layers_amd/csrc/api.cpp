@@ -411,53 +411,434 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
   return DL_OK;
 }
 
-static dl::OptConsts opt_consts(double lr, double beta1, double beta2, double eps, double wd,
-                                int64_t t) {
+// ---- optimizers ---------------------------------------------------------------
+
+static dl::LrSched to_sched(const dl_lr_schedule_t* s) {
+  dl::LrSched r;
+  memset(&r, 0, sizeof(r));
+  r.step_size = 1;
+  r.gamma = 1.0;
+  if (s != nullptr) {
+    r.kind = s->kind;
+    r.warmup = s->warmup;
+    r.total = s->total;
+    r.step_size = s->step_size;
+    r.min_lr = s->min_lr;
+    r.gamma = s->gamma;
+  }
+  return r;
+}
+
+static const char* sched_problem(const dl_lr_schedule_t* s) {
+  if (s == nullptr) return nullptr;
+  if (s->kind < DL_LR_CONSTANT || s->kind > DL_LR_WARMUP_LINEAR) return "bad schedule kind";
+  if (s->kind == DL_LR_STEP && s->step_size < 1) return "a step schedule needs step_size >= 1";
+  if (s->warmup < 0) return "warmup must be >= 0";
+  return nullptr;
+}
+
+double dl_lr_at(const dl_lr_schedule_t* s, double lr, int64_t step) {
+  if (step < 1 || sched_problem(s) != nullptr) return NAN;
+  return dl::lr_schedule(to_sched(s), lr, step);
+}
+
+// Constants of step t (t < 1: the bias corrections are left at 1, for SGD or
+// when the device forms them).
+static dl::OptConsts opt_consts(const dl_opt_t& o, int64_t t) {
   dl::OptConsts c;
   memset(&c, 0, sizeof(c));
-  c.lr_d = lr;
-  c.beta1_d = beta1;
-  c.beta2_d = beta2;
+  c.sched = to_sched(o.schedule);
+  c.lr_d = o.lr;
+  c.beta1_d = o.beta1;
+  c.beta2_d = o.beta2;
+  c.wd_d = o.weight_decay;
+  const double lr = t >= 1 ? dl::lr_schedule(c.sched, o.lr, t) : o.lr;
   c.lr = (float)lr;
-  c.decay = (float)(1.0 - lr * wd);
-  c.b1 = (float)beta1;
-  c.omb1 = (float)(1.0 - beta1);
-  c.b2 = (float)beta2;
-  c.omb2 = (float)(1.0 - beta2);
-  const double bc1 = t >= 1 ? 1.0 - std::pow(beta1, (double)t) : 1.0;
-  const double bc2 = t >= 1 ? 1.0 - std::pow(beta2, (double)t) : 1.0;
+  c.decay = (float)(1.0 - lr * o.weight_decay);
+  c.wd = (float)o.weight_decay;
+  c.b1 = (float)o.beta1;
+  c.omb1 = (float)(1.0 - o.beta1);
+  c.b2 = (float)o.beta2;
+  c.omb2 = (float)(1.0 - o.beta2);
+  const double bc1 = t >= 1 ? 1.0 - std::pow(o.beta1, (double)t) : 1.0;
+  const double bc2 = t >= 1 ? 1.0 - std::pow(o.beta2, (double)t) : 1.0;
   c.step_size = (float)(lr / bc1);
   c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
-  c.eps = (float)eps;
+  c.eps = (float)o.eps;
+  c.ema_d = (float)o.ema_decay;
+  c.ema_omd = (float)(1.0 - o.ema_decay);
   return c;
 }
 
+static dl_opt_t plain_opt(int kind, double lr, double beta1, double beta2, double eps, double wd,
+                          int64_t step) {
+  dl_opt_t o;
+  memset(&o, 0, sizeof(o));
+  o.kind = kind;
+  o.lr = lr;
+  o.beta1 = beta1;
+  o.beta2 = beta2;
+  o.eps = eps;
+  o.weight_decay = wd;
+  o.step = step;
+  return o;
+}
+
 static bool betas_ok(double b1, double b2) { return b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0; }
+
+// The checks of dl_opt_t that optimizer_step and mlp_train_step share.
+static int check_opt(const dl_opt_t* o, const char* who, bool any_ema) {
+  if (o->kind != DL_OPT_SGD && o->kind != DL_OPT_ADAMW && o->kind != DL_OPT_ADAM)
+    return fail(DL_INVALID_ARGUMENT, "%s: bad optimizer kind %d", who, o->kind);
+  const bool adam = o->kind != DL_OPT_SGD;
+  if (adam && !betas_ok(o->beta1, o->beta2))
+    return fail(DL_INVALID_ARGUMENT, "%s: betas must be in [0, 1)", who);
+  if (const char* p = sched_problem(o->schedule)) return fail(DL_INVALID_ARGUMENT, "%s: %s", who, p);
+  const bool needs_t = adam || o->schedule != nullptr;
+  if (needs_t && o->step_dev == nullptr && o->step < 1)
+    return fail(DL_INVALID_ARGUMENT, "%s: step counts from 1", who);
+  if (any_ema && !(o->ema_decay >= 0.0 && o->ema_decay <= 1.0))
+    return fail(DL_INVALID_ARGUMENT, "%s: ema_decay must be in [0, 1]", who);
+  if (o->max_grad_norm != o->max_grad_norm)
+    return fail(DL_INVALID_ARGUMENT, "%s: max_grad_norm is NaN", who);
+  if (o->scaler != nullptr) {
+    const dl_loss_scaler_t& sc = *o->scaler;
+    if (!sc.scale || !sc.growth_tracker || !sc.found_inf)
+      return fail(DL_INVALID_ARGUMENT, "%s: the loss scaler needs scale, growth_tracker and found_inf", who);
+    if (!(sc.growth_factor > 0.0) || !(sc.backoff_factor > 0.0) || sc.growth_interval < 1)
+      return fail(DL_INVALID_ARGUMENT, "%s: bad loss-scaler factors or interval", who);
+    if (needs_t && o->step_dev == nullptr)
+      return fail(DL_INVALID_ARGUMENT,
+                  "%s: a loss scaler needs a device step count (a skipped step must not advance t)", who);
+  }
+  return DL_OK;
+}
+
+// Byte ranges that must not overlap one another (null or empty ones are
+// ignored): sorted by start, neighbours compared.
+struct Span {
+  uintptr_t a;
+  size_t n;
+};
+static bool spans_overlap(std::vector<Span> v) {
+  v.erase(std::remove_if(v.begin(), v.end(), [](const Span& x) { return x.a == 0 || x.n == 0; }),
+          v.end());
+  std::sort(v.begin(), v.end(), [](const Span& x, const Span& y) { return x.a < y.a; });
+  for (size_t i = 1; i < v.size(); ++i)
+    if (v[i - 1].a + v[i - 1].n > v[i].a) return true;
+  return false;
+}
+static Span span(const void* p, size_t n) { return Span{reinterpret_cast<uintptr_t>(p), n}; }
+
+// Multi-array calls take their arrays kMaxSegs to a launch.  The gradient
+// pass of a chunk leaves stat_grid(units of the chunk) partials.
+constexpr int kMaxArrays = 4096;
+static int64_t units_of(int64_t n) { return (n + dl::kStatUnit - 1) / dl::kStatUnit; }
+extern "C++" {
+template <class N>
+static int64_t stat_parts(int count, N n_of) {
+  int64_t parts = 0;
+  for (int c0 = 0; c0 < count; c0 += dl::kMaxSegs) {
+    int64_t units = 0;
+    for (int k = c0; k < std::min(count, c0 + dl::kMaxSegs); ++k) units += units_of(n_of(k));
+    parts += dl::stat_grid(units);
+  }
+  return parts;
+}
+}
+// Workspace of the gradient control: the GradCtl and clip coefficient, then
+// the float64 partial sums and the int partial counts.
+static size_t ctl_bytes(int64_t parts) {
+  return kAlign + align_up((size_t)parts * 8) + align_up((size_t)parts * 4);
+}
+struct CtlMem {
+  dl::GradCtl* ctl;
+  float* coef;
+  double* sq;
+  int* bad;
+};
+static CtlMem ctl_mem(void* ws, int64_t parts) {
+  char* b = static_cast<char*>(ws);
+  CtlMem m;
+  m.ctl = reinterpret_cast<dl::GradCtl*>(b);
+  m.coef = reinterpret_cast<float*>(b + sizeof(dl::GradCtl));
+  m.sq = reinterpret_cast<double*>(b + kAlign);
+  m.bad = reinterpret_cast<int*>(b + kAlign + align_up((size_t)parts * 8));
+  return m;
+}
+static dl::OptSegs blank_segs() {
+  dl::OptSegs segs;
+  memset(&segs, 0, sizeof(segs));
+  return segs;
+}
+// Appends one array to segs with start_block in units (gradient pass) or in
+// optimizer blocks (update).
+static void add_seg(dl::OptSegs& segs, int64_t& blocks, bool units, int64_t n, float* w,
+                    const float* g, float* m, float* v, float* e, void* wb, const float* part,
+                    int splits, float* g_out) {
+  const int k = segs.count++;
+  segs.start_block[k] = blocks;
+  segs.n[k] = n;
+  segs.w[k] = w;
+  segs.g[k] = g;
+  segs.m[k] = m;
+  segs.v[k] = v;
+  segs.ema[k] = e;
+  segs.wb[k] = static_cast<dl::bf16_t*>(wb);
+  segs.part[k] = splits > 1 ? part : nullptr;
+  segs.part_stride[k] = n;
+  segs.splits[k] = splits;
+  segs.g_out[k] = g_out;
+  const int64_t per = units ? dl::kStatUnit : dl::opt_elems_per_block(splits);
+  blocks += (n + per - 1) / per;
+  segs.start_block[segs.count] = blocks;
+}
+
+static dl::CtlArgs ctl_args(const dl_opt_t* o, const CtlMem& m, int64_t parts) {
+  dl::CtlArgs a;
+  memset(&a, 0, sizeof(a));
+  a.part_sq = m.sq;
+  a.part_bad = m.bad;
+  a.parts = (int)parts;
+  a.max_norm = o->max_grad_norm;
+  if (o->scaler != nullptr) {
+    a.scale = o->scaler->scale;
+    a.growth_tracker = o->scaler->growth_tracker;
+    a.found_inf = o->scaler->found_inf;
+    a.growth_factor = o->scaler->growth_factor;
+    a.backoff_factor = o->scaler->backoff_factor;
+    a.growth_interval = o->scaler->growth_interval;
+  }
+  a.step_dev = o->step_dev;
+  a.norm_out = o->grad_norm;
+  a.ctl = m.ctl;
+  a.clip_coef = m.coef;
+  return a;
+}
 
 int sgd_step(void* stream, int64_t n, float* w, const float* g, double lr) {
   if (n <= 0) return fail(DL_INVALID_ARGUMENT, "sgd_step: n must be positive");
   if (!w || !g) return fail(DL_INVALID_ARGUMENT, "sgd_step: w and g are required");
   if (overlap(w, n * 4, g, n * 4)) return fail(DL_ALIASING, "sgd_step: w overlaps g");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("sgd", st, [&] { return dl::launch_sgd(n, w, g, opt_consts(lr, 0, 0, 0, 0, 0), st); });
+  const dl::OptConsts oc = opt_consts(plain_opt(DL_OPT_SGD, lr, 0, 0, 0, 0, 0), 0);
+  hipError_t e = timed("sgd", st, [&] { return dl::launch_sgd(n, w, g, oc, st); });
   if (e != hipSuccess) return hip_fail(e, "sgd_step");
+  return DL_OK;
+}
+
+static int adam_like(const char* who, int kind, void* stream, int64_t n, float* w, const float* g,
+                     float* m, float* v, double lr, double beta1, double beta2, double eps,
+                     double weight_decay, int64_t step) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "%s: n must be positive", who);
+  if (!w || !g || !m || !v) return fail(DL_INVALID_ARGUMENT, "%s: w, g, m and v are required", who);
+  if (step < 1) return fail(DL_INVALID_ARGUMENT, "%s: step counts from 1", who);
+  if (!betas_ok(beta1, beta2)) return fail(DL_INVALID_ARGUMENT, "%s: betas must be in [0, 1)", who);
+  const size_t nb = (size_t)n * 4;
+  if (overlap(w, nb, g, nb) || overlap(w, nb, m, nb) || overlap(w, nb, v, nb) ||
+      overlap(g, nb, m, nb) || overlap(g, nb, v, nb) || overlap(m, nb, v, nb))
+    return fail(DL_ALIASING, "%s: w, g, m, v must be distinct", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dl::OptConsts oc = opt_consts(plain_opt(kind, lr, beta1, beta2, eps, weight_decay, step), step);
+  hipError_t e = timed(who, st, [&] {
+    return kind == DL_OPT_ADAM ? dl::launch_adam(n, w, g, m, v, oc, st)
+                               : dl::launch_adamw(n, w, g, m, v, oc, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, who);
   return DL_OK;
 }
 
 int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m, float* v, double lr,
                double beta1, double beta2, double eps, double weight_decay, int64_t step) {
-  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "adamw_step: n must be positive");
-  if (!w || !g || !m || !v) return fail(DL_INVALID_ARGUMENT, "adamw_step: w, g, m and v are required");
-  if (step < 1) return fail(DL_INVALID_ARGUMENT, "adamw_step: step counts from 1");
-  if (!betas_ok(beta1, beta2)) return fail(DL_INVALID_ARGUMENT, "adamw_step: betas must be in [0, 1)");
-  const size_t nb = (size_t)n * 4;
-  if (overlap(w, nb, g, nb) || overlap(w, nb, m, nb) || overlap(w, nb, v, nb) ||
-      overlap(g, nb, m, nb) || overlap(g, nb, v, nb) || overlap(m, nb, v, nb))
-    return fail(DL_ALIASING, "adamw_step: w, g, m, v must be distinct");
+  return adam_like("adamw_step", DL_OPT_ADAMW, stream, n, w, g, m, v, lr, beta1, beta2, eps,
+                   weight_decay, step);
+}
+
+int adam_step(void* stream, int64_t n, float* w, const float* g, float* m, float* v, double lr,
+              double beta1, double beta2, double eps, double weight_decay, int64_t step) {
+  return adam_like("adam_step", DL_OPT_ADAM, stream, n, w, g, m, v, lr, beta1, beta2, eps,
+                   weight_decay, step);
+}
+
+int ema_update(void* stream, int64_t n, float* ema, const float* w, double decay) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "ema_update: n must be positive");
+  if (!ema || !w) return fail(DL_INVALID_ARGUMENT, "ema_update: ema and w are required");
+  if (!(decay >= 0.0 && decay <= 1.0)) return fail(DL_INVALID_ARGUMENT, "ema_update: decay must be in [0, 1]");
+  if (overlap(ema, n * 4, w, n * 4)) return fail(DL_ALIASING, "ema_update: ema overlaps w");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dl::OptConsts oc = opt_consts(lr, beta1, beta2, eps, weight_decay, step);
-  hipError_t e = timed("adamw", st, [&] { return dl::launch_adamw(n, w, g, m, v, oc, st); });
-  if (e != hipSuccess) return hip_fail(e, "adamw_step");
+  hipError_t e = timed("ema", st, [&] {
+    return dl::launch_ema(n, ema, w, (float)decay, (float)(1.0 - decay), st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "ema_update");
+  return DL_OK;
+}
+
+size_t clip_grad_norm_workspace_size(int32_t count, const int64_t* n) {
+  if (count < 1 || count > kMaxArrays || !n) return 0;
+  for (int k = 0; k < count; ++k)
+    if (n[k] <= 0) return 0;
+  return ctl_bytes(stat_parts(count, [&](int k) { return n[k]; }));
+}
+
+int clip_grad_norm(void* stream, int32_t count, float* const* grads, const int64_t* n,
+                   double max_norm, float* total_norm, void* ws, size_t ws_bytes) {
+  if (count < 1 || count > kMaxArrays || !grads || !n)
+    return fail(DL_INVALID_ARGUMENT, "clip_grad_norm: count must be in [1, %d] with grads and n", kMaxArrays);
+  if (!(max_norm > 0.0)) return fail(DL_INVALID_ARGUMENT, "clip_grad_norm: max_norm must be positive");
+  std::vector<Span> spans;
+  for (int k = 0; k < count; ++k) {
+    if (!grads[k] || n[k] <= 0) return fail(DL_INVALID_ARGUMENT, "clip_grad_norm: array %d is empty or null", k);
+    spans.push_back(span(grads[k], (size_t)n[k] * 4));
+  }
+  const int64_t parts = stat_parts(count, [&](int k) { return n[k]; });
+  const size_t need = ctl_bytes(parts);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "clip_grad_norm: workspace %zu bytes, need %zu", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DL_INVALID_ARGUMENT, "clip_grad_norm: workspace must be 256-byte aligned");
+  spans.push_back(span(ws, need));
+  spans.push_back(span(total_norm, 4));
+  if (spans_overlap(spans)) return fail(DL_ALIASING, "clip_grad_norm: arrays overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CtlMem mem = ctl_mem(ws, parts);
+  int64_t off = 0;
+  hipError_t e = hipSuccess;
+  for (int c0 = 0; c0 < count && e == hipSuccess; c0 += dl::kMaxSegs) {
+    dl::OptSegs segs = blank_segs();
+    int64_t units = 0;
+    for (int k = c0; k < std::min(count, c0 + dl::kMaxSegs); ++k)
+      add_seg(segs, units, true, n[k], grads[k], grads[k], nullptr, nullptr, nullptr, nullptr,
+              nullptr, 1, nullptr);
+    e = timed("grad_stats", s, [&] {
+      return dl::launch_grad_stats(segs, units, mem.sq + off, mem.bad + off, s);
+    });
+    off += dl::stat_grid(units);
+  }
+  dl_opt_t o = plain_opt(DL_OPT_SGD, 0, 0, 0, 0, 0, 0);
+  o.max_grad_norm = max_norm;
+  o.grad_norm = total_norm;
+  const dl::CtlArgs a = ctl_args(&o, mem, parts);
+  if (e == hipSuccess) e = timed("grad_ctl", s, [&] { return dl::launch_grad_ctl(a, s); });
+  for (int c0 = 0; c0 < count && e == hipSuccess; c0 += dl::kMaxSegs) {
+    dl::OptSegs segs = blank_segs();
+    int64_t units = 0;
+    for (int k = c0; k < std::min(count, c0 + dl::kMaxSegs); ++k)
+      add_seg(segs, units, true, n[k], grads[k], grads[k], nullptr, nullptr, nullptr, nullptr,
+              nullptr, 1, nullptr);
+    e = timed("clip_scale", s, [&] { return dl::launch_scale_by(segs, mem.coef, s); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "clip_grad_norm");
+  return DL_OK;
+}
+
+size_t optimizer_step_workspace_size(int32_t count, const dl_param_t* params) {
+  if (count < 1 || count > kMaxArrays || !params) return 0;
+  for (int k = 0; k < count; ++k)
+    if (params[k].n <= 0) return 0;
+  return ctl_bytes(stat_parts(count, [&](int k) { return params[k].n; }));
+}
+
+int optimizer_step(void* stream, const dl_opt_t* opt, int32_t count, const dl_param_t* params,
+                   void* ws, size_t ws_bytes) {
+  if (!opt || !params || count < 1 || count > kMaxArrays)
+    return fail(DL_INVALID_ARGUMENT, "optimizer_step: opt, params and count in [1, %d] are required", kMaxArrays);
+  const bool adam = opt->kind == DL_OPT_ADAM || opt->kind == DL_OPT_ADAMW;
+  bool any_ema = false;
+  std::vector<Span> spans;
+  for (int k = 0; k < count; ++k) {
+    const dl_param_t& p = params[k];
+    if (p.n <= 0 || !p.w || !p.g) return fail(DL_INVALID_ARGUMENT, "optimizer_step: param %d needs n > 0, w and g", k);
+    if (adam && (!p.m || !p.v)) return fail(DL_INVALID_ARGUMENT, "optimizer_step: param %d needs m and v", k);
+    const size_t nb = (size_t)p.n * 4;
+    spans.push_back(span(p.w, nb));
+    spans.push_back(span(p.g, nb));
+    if (adam) {
+      spans.push_back(span(p.m, nb));
+      spans.push_back(span(p.v, nb));
+    }
+    spans.push_back(span(p.ema, nb));
+    spans.push_back(span(p.w_bf16, (size_t)p.n * 2));
+    any_ema = any_ema || p.ema != nullptr;
+  }
+  if (int st = check_opt(opt, "optimizer_step", any_ema)) return st;
+  const bool ctl_on = opt->max_grad_norm > 0.0 || opt->scaler != nullptr;
+  const int64_t parts = ctl_on ? stat_parts(count, [&](int k) { return params[k].n; }) : 0;
+  const size_t need = ctl_on ? ctl_bytes(parts) : 0;
+  if (ctl_on) {
+    if (!ws || ws_bytes < need)
+      return fail(DL_WORKSPACE_TOO_SMALL, "optimizer_step: workspace %zu bytes, need %zu", ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+      return fail(DL_INVALID_ARGUMENT, "optimizer_step: workspace must be 256-byte aligned");
+    spans.push_back(span(ws, need));
+  }
+  if (spans_overlap(spans)) return fail(DL_ALIASING, "optimizer_step: arrays overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool dev_step = opt->step_dev != nullptr;
+  hipError_t e = hipSuccess;
+  if (dev_step && !ctl_on) e = dl::launch_step_tick(opt->step_dev, s);
+  CtlMem mem{};
+  if (ctl_on) {
+    mem = ctl_mem(ws, parts);
+    int64_t off = 0;
+    for (int c0 = 0; c0 < count && e == hipSuccess; c0 += dl::kMaxSegs) {
+      dl::OptSegs segs = blank_segs();
+      int64_t units = 0;
+      for (int k = c0; k < std::min(count, c0 + dl::kMaxSegs); ++k)
+        add_seg(segs, units, true, params[k].n, params[k].w, params[k].g, nullptr, nullptr,
+                nullptr, nullptr, nullptr, 1, nullptr);
+      e = timed("grad_stats", s, [&] {
+        return dl::launch_grad_stats(segs, units, mem.sq + off, mem.bad + off, s);
+      });
+      off += dl::stat_grid(units);
+    }
+    const dl::CtlArgs a = ctl_args(opt, mem, parts);
+    if (e == hipSuccess) e = timed("grad_ctl", s, [&] { return dl::launch_grad_ctl(a, s); });
+  }
+  dl::OptConsts oc = opt_consts(*opt, dev_step ? 0 : opt->step);
+  if (dev_step) oc.step_dev = opt->step_dev;
+  if (ctl_on) oc.ctl = mem.ctl;
+  for (int c0 = 0; c0 < count && e == hipSuccess; c0 += dl::kMaxSegs) {
+    dl::OptSegs segs = blank_segs();
+    int64_t blocks = 0;
+    for (int k = c0; k < std::min(count, c0 + dl::kMaxSegs); ++k) {
+      const dl_param_t& p = params[k];
+      add_seg(segs, blocks, false, p.n, p.w, p.g, p.m, p.v, p.ema, p.w_bf16, nullptr, 1, nullptr);
+    }
+    e = timed("opt_multi", s, [&] { return dl::launch_opt_multi(segs, opt->kind, oc, s); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "optimizer_step");
+  return DL_OK;
+}
+
+// ---- mean squared error ------------------------------------------------------------
+
+size_t mse_loss_workspace_size(int64_t B, int64_t C) {
+  if (B <= 0 || C <= 0) return 0;
+  return align_up((size_t)dl::mse_grid(B * C) * 8);
+}
+
+int mse_loss_fwd_bwd(void* stream, int64_t B, int64_t C, const float* pred, const float* target,
+                     float* loss, float* dpred, void* ws, size_t ws_bytes) {
+  if (B <= 0 || C <= 0 || B > (int64_t(1) << 40) / C)
+    return fail(DL_INVALID_ARGUMENT, "mse_loss_fwd_bwd: B, C must be positive (B C <= 2^40)");
+  if (!pred || !target || !loss) return fail(DL_INVALID_ARGUMENT, "mse_loss_fwd_bwd: pred, target and loss are required");
+  const int64_t n = B * C;
+  const size_t need = mse_loss_workspace_size(B, C);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "mse_loss_fwd_bwd: workspace %zu bytes, need %zu", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) % 8) != 0)
+    return fail(DL_INVALID_ARGUMENT, "mse_loss_fwd_bwd: workspace must be 8-byte aligned");
+  const size_t nb = (size_t)n * 4;
+  if ((dpred != pred && overlap(dpred, nb, pred, nb)) || overlap(dpred, nb, target, nb) ||
+      overlap(loss, 4, pred, nb) || overlap(loss, 4, target, nb) || overlap(loss, 4, dpred, nb) ||
+      overlap(ws, need, pred, nb) || overlap(ws, need, target, nb) || overlap(ws, need, dpred, nb) ||
+      overlap(ws, need, loss, 4))
+    return fail(DL_ALIASING, "mse_loss_fwd_bwd: outputs overlap inputs (dpred may equal pred)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("mse", s, [&] {
+    return dl::launch_mse(n, pred, target, dpred, static_cast<double*>(ws), loss, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "mse_loss_fwd_bwd");
   return DL_OK;
 }
 
@@ -543,9 +924,17 @@ static bool mlp_pair(int64_t B, const dl_layer_t& ly) {
   return p.tile == 1 && 2.0 * (double)B * (double)ly.in * (double)ly.out <= 8589934592.0;
 }
 
+// Gradient-control partials of the MLP step: one gradient pass over all W and
+// b (at most 32 arrays, one launch).
+static int64_t mlp_stat_parts(int32_t L, const dl_layer_t* layers) {
+  int64_t units = 0;
+  for (int l = 0; l < L; ++l) units += units_of(layers[l].out * layers[l].in) + units_of(layers[l].out);
+  return dl::stat_grid(units);
+}
+
 static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
                          size_t* rl_off, size_t* part_off, size_t* fwd_off, size_t* g_off,
-                         size_t* g_bytes) {
+                         size_t* g_bytes, size_t* ctl_off) {
   size_t off = 0;
   for (int l = 0; l < L; ++l) {
     y_off[l] = off;
@@ -579,15 +968,17 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
     }
   *g_off = off;
   *g_bytes = gb;
-  return off + (size_t)std::min(pairs, 2) * gb;
+  off += (size_t)std::min(pairs, 2) * gb;
+  *ctl_off = off;
+  return off + ctl_bytes(mlp_stat_parts(L, layers));
 }
 
 size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer_t* layers) {
   if (!dim_ok(B) || n_layers < 1 || n_layers > 16 || !layers) return 0;
   for (int l = 0; l < n_layers; ++l)
     if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
-  size_t y_off[16], rl, part[16], fwd, g_off, g_bytes;
-  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd, &g_off, &g_bytes);
+  size_t y_off[16], rl, part[16], fwd, g_off, g_bytes, ctl_off;
+  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd, &g_off, &g_bytes, &ctl_off);
 }
 
 int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
@@ -597,12 +988,9 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   if (n_layers < 1 || n_layers > 16 || !layers)
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: n_layers must be in [1, 16]");
   if (!X || !labels || !opt || !loss) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: X, labels, opt and loss are required");
-  if (opt->kind != DL_OPT_SGD && opt->kind != DL_OPT_ADAMW)
-    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: bad optimizer kind %d", opt->kind);
-  if (opt->kind == DL_OPT_ADAMW && opt->step_dev == nullptr && opt->step < 1)
-    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: AdamW step counts from 1");
-  if (opt->kind == DL_OPT_ADAMW && !betas_ok(opt->beta1, opt->beta2))
-    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: betas must be in [0, 1)");
+  const bool any_ema = layers && n_layers >= 1 && layers[0].eW != nullptr;
+  if (int st = check_opt(opt, "mlp_train_step", any_ema)) return st;
+  const bool adam = opt->kind != DL_OPT_SGD;
   int n_tensors = 0;
   for (int l = 0; l < n_layers; ++l) {
     const dl_layer_t& ly = layers[l];
@@ -615,8 +1003,10 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
                   "mlp_train_step: layer %d activation %d (identity or ReLU only)", l, ly.act);
     if (!ly.W || !ly.b || !ly.dW || !ly.db)
       return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d needs W, b, dW and db", l);
-    if (opt->kind == DL_OPT_ADAMW && (!ly.mW || !ly.vW || !ly.mb || !ly.vb))
-      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d needs AdamW moments", l);
+    if (adam && (!ly.mW || !ly.vW || !ly.mb || !ly.vb))
+      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: layer %d needs Adam moments", l);
+    if ((ly.eW != nullptr) != any_ema || (ly.eb != nullptr) != any_ema)
+      return fail(DL_INVALID_ARGUMENT, "mlp_train_step: parameter averages for all layers or none");
     if (overlap(ly.dW, ly.out * ly.in * 4, ly.W, ly.out * ly.in * 4) || overlap(ly.db, ly.out * 4, ly.b, ly.out * 4))
       return fail(DL_ALIASING, "mlp_train_step: layer %d gradient overlaps its parameters", l);
     n_tensors += 2;
@@ -626,9 +1016,9 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // activation of its own (its derivative would need the overwritten output).
   if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
     return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
-  size_t y_off[16], rl_off, part_off[16], fwd_off, g_off, g_bytes;
+  size_t y_off[16], rl_off, part_off[16], fwd_off, g_off, g_bytes, ctl_off;
   const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off, &fwd_off, &g_off,
-                                 &g_bytes);
+                                 &g_bytes, &ctl_off);
   if (!ws || ws_bytes < need)
     return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -636,8 +1026,12 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  const bool dev_step = opt->kind == DL_OPT_ADAMW && opt->step_dev != nullptr;
-  if (dev_step) {
+  const bool dev_step = opt->step_dev != nullptr;
+  // with clipping or loss scaling a gradient pass precedes the update and its
+  // control kernel advances the device step count (unless the step is skipped)
+  const bool ctl_on = opt->max_grad_norm > 0.0 || opt->scaler != nullptr;
+  const float* dscale = opt->scaler != nullptr ? opt->scaler->scale : nullptr;
+  if (dev_step && !ctl_on) {
     hipError_t et = dl::launch_step_tick(opt->step_dev, s);
     if (et != hipSuccess) return hip_fail(et, "mlp_train_step (step count)");
   }
@@ -692,12 +1086,14 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     const int prev_act = L > 1 ? layers[L - 2].act : DL_ACT_IDENTITY;
     e = timed("head_xent", s, [&] {
       return dl::launch_head_xent(B, (int)ly.in, (int)ly.out, H, dH, prev_act, ly.W, ly.b, labels,
-                                  row_loss, dWp, dbp, s);
+                                  row_loss, dWp, dbp, s, dscale);
     });
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (head)");
   } else {
     // loss + dlogits (in place over the logits)
-    e = timed("xent", s, [&] { return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s); });
+    e = timed("xent", s, [&] {
+      return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s, dscale);
+    });
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
   }
   // backward; G holds the current layer's output gradient
@@ -729,10 +1125,11 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
       G = Y[l - 1];
     }
   }
-  // optimizer over every W and b in one launch (finishing split-K sums)
-  dl::OptSegs segs;
-  memset(&segs, 0, sizeof(segs));
-  int64_t blocks = 0;
+  // optimizer over every W and b in one launch (finishing split-K sums, or,
+  // with the gradient control on, after the gradient pass has finished them)
+  dl::OptSegs segs = blank_segs();
+  dl::OptSegs stat = blank_segs();
+  int64_t blocks = 0, units = 0;
   for (int l = 0; l < L; ++l) {
     const dl_layer_t& ly = layers[l];
     const int64_t S = mlp_slices(B, L, layers, l);
@@ -741,38 +1138,41 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
     float* gs_[2] = {ly.dW, ly.db};
     float* ms_[2] = {ly.mW, ly.mb};
     float* vs_[2] = {ly.vW, ly.vb};
+    float* es_[2] = {ly.eW, ly.eb};
     const int64_t ns_[2] = {ly.out * ly.in, ly.out};
     const float* ps_[2] = {reinterpret_cast<float*>(pb),
                            reinterpret_cast<float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))};
     for (int t = 0; t < 2; ++t) {
-      const int k = segs.count++;
-      segs.start_block[k] = blocks;
-      segs.n[k] = ns_[t];
-      segs.w[k] = ws_[t];
-      segs.g[k] = gs_[t];
-      segs.m[k] = ms_[t];
-      segs.v[k] = vs_[t];
-      segs.splits[k] = (int)S;
-      segs.part[k] = S > 1 ? ps_[t] : nullptr;
-      segs.part_stride[k] = ns_[t];
-      segs.g_out[k] = gs_[t];
-      const int64_t per = dl::opt_elems_per_block((int)S);
-      blocks += (ns_[t] + per - 1) / per;
+      if (ctl_on) {
+        add_seg(stat, units, true, ns_[t], ws_[t], gs_[t], nullptr, nullptr, nullptr, nullptr,
+                ps_[t], (int)S, gs_[t]);
+        add_seg(segs, blocks, false, ns_[t], ws_[t], gs_[t], ms_[t], vs_[t], es_[t], nullptr,
+                nullptr, 1, gs_[t]);
+      } else {
+        add_seg(segs, blocks, false, ns_[t], ws_[t], gs_[t], ms_[t], vs_[t], es_[t], nullptr,
+                ps_[t], (int)S, gs_[t]);
+      }
     }
   }
-  segs.start_block[segs.count] = blocks;
   if (fused) {  // the loss mean rides on the optimizer launch
     segs.row_loss = row_loss;
     segs.rows = B;
     segs.loss = loss;
   }
-  dl::OptConsts oc = opt->kind == DL_OPT_ADAMW
-                         ? opt_consts(opt->lr, opt->beta1, opt->beta2, opt->eps,
-                                      opt->weight_decay, dev_step ? 1 : opt->step)
-                         : opt_consts(opt->lr, 0, 0, 0, 0, 0);
+  dl::OptConsts oc = opt_consts(*opt, dev_step ? 0 : opt->step);
   if (dev_step) oc.step_dev = opt->step_dev;
-  e = timed(opt->kind == DL_OPT_ADAMW ? "adamw_multi" : "sgd_multi", s,
-            [&] { return dl::launch_opt_multi(segs, opt->kind == DL_OPT_ADAMW ? 1 : 0, oc, s); });
+  if (ctl_on) {
+    const int64_t parts = mlp_stat_parts(L, layers);
+    const CtlMem mem = ctl_mem(base + ctl_off, parts);
+    e = timed("grad_stats", s, [&] { return dl::launch_grad_stats(stat, units, mem.sq, mem.bad, s); });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (gradient pass)");
+    const dl::CtlArgs a = ctl_args(opt, mem, parts);
+    e = timed("grad_ctl", s, [&] { return dl::launch_grad_ctl(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (gradient control)");
+    oc.ctl = mem.ctl;
+  }
+  static const char* const kOptNames[3] = {"sgd_multi", "adamw_multi", "adam_multi"};
+  e = timed(kOptNames[opt->kind], s, [&] { return dl::launch_opt_multi(segs, opt->kind, oc, s); });
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");
   return DL_OK;
 }

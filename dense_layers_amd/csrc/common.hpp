@@ -399,9 +399,11 @@ hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst,
                             hipStream_t s);
 hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16_t* dst,
                               bf16_t* dst_t, hipStream_t s);
+// dscale (optional, device float32 [1]): dlogits are multiplied by it (the
+// loss scale).
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
-                       float* loss, hipStream_t s);
+                       float* loss, hipStream_t s, const float* dscale = nullptr);
 // Fixed-order float64 mean of the per-row losses (one workgroup).
 hipError_t launch_loss_mean(int64_t B, const float* row_loss, float* loss, hipStream_t s);
 // Narrow classifier head of the MLP step (C <= 16 classes, K <= 256 inputs):
@@ -412,20 +414,65 @@ bool head_xent_fits(int64_t K, int64_t C);
 int64_t head_xent_slices(int64_t B);
 hipError_t launch_head_xent(int64_t B, int K, int C, const float* H, float* dH, int prev_act,
                             const float* W, const float* bias, const int32_t* labels,
-                            float* row_loss, float* dW_part, float* db_part, hipStream_t s);
+                            float* row_loss, float* dW_part, float* db_part, hipStream_t s,
+                            const float* dscale = nullptr);
+// Optimizer kinds (the values of enum dl_opt_kind).
+enum OptKind { OPT_SGD = 0, OPT_ADAMW = 1, OPT_ADAM = 2 };
+
+// Learning-rate schedule (the fields of dl_lr_schedule_t); kind 0 = constant.
+struct LrSched {
+  int kind;
+  int64_t warmup, total, step_size;
+  double min_lr, gamma;
+};
+
+// The learning rate of step t >= 1: k = t - 1 scheduler steps; a linear
+// warmup to lr over `warmup` steps, then a cosine or linear decay to min_lr
+// reached at k = total, or lr gamma^floor(k / step_size).  Double precision;
+// the same code runs on the host (host step count) and on the device
+// (device step count).
+__host__ __device__ inline double lr_schedule(const LrSched& s, double lr, int64_t t) {
+  const int64_t k = t - 1;
+  if (s.kind == 1) return lr * pow(s.gamma, (double)(k / s.step_size));
+  if (s.kind == 2 || s.kind == 3) {
+    if (k < s.warmup) return lr * (double)(k + 1) / (double)s.warmup;
+    const int64_t T = s.total - s.warmup;
+    if (T <= 0) return s.min_lr;
+    const int64_t j = k - s.warmup < T ? k - s.warmup : T;
+    if (s.kind == 2)
+      return s.min_lr + (lr - s.min_lr) * (1.0 + cos(3.141592653589793 * (double)j / (double)T)) / 2.0;
+    return s.min_lr + (lr - s.min_lr) * (double)(T - j) / (double)T;
+  }
+  return lr;
+}
+
+// What the gradient pass leaves for the optimizer (device memory): every
+// gradient is used multiplied by `mul` (clip coefficient / loss scale), and
+// with `skip` set the update is not applied at all.
+struct GradCtl {
+  float mul;
+  int skip;
+  float norm;
+  int pad;
+};
+
 // Optimizer constants, each formed in double on the host and rounded once.
 struct OptConsts {
   float lr;            // SGD step
-  float decay;         // 1 - lr wd
+  float decay;         // AdamW: 1 - lr wd
+  float wd;            // Adam: coupled decay
   float b1, omb1;      // beta1, 1 - beta1
   float b2, omb2;      // beta2, 1 - beta2
   float step_size;     // lr / (1 - beta1^t)
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
   float eps;
-  // AdamW with a device step count: t = *step_dev, and step_size and
-  // inv_sqrt_bc2 are formed on the device from these doubles instead
+  float ema_d, ema_omd;  // parameter averages: d, 1 - d
+  // With a device step count: t = *step_dev, and lr (scheduled), decay,
+  // step_size and inv_sqrt_bc2 are formed on the device from these doubles
   const int64_t* step_dev;
-  double lr_d, beta1_d, beta2_d;
+  double lr_d, beta1_d, beta2_d, wd_d;
+  LrSched sched;
+  const GradCtl* ctl;  // gradient control of this step, or null
 };
 // Adds 1 to a device step count (one lane, a vector store).
 hipError_t launch_step_tick(int64_t* step_dev, hipStream_t s);
@@ -452,6 +499,8 @@ struct OptSegs {
   int64_t part_stride[kMaxSegs];
   int splits[kMaxSegs];
   float* g_out[kMaxSegs];
+  float* ema[kMaxSegs];   // parameter average, or null
+  bf16_t* wb[kMaxSegs];   // bf16 copy of the updated w, or null
   // optional: one extra workgroup (the first) writes loss = mean(row_loss[0 ..
   // rows)) (float64, fixed order)
   const float* row_loss;
@@ -469,5 +518,46 @@ inline int64_t opt_elems_per_block(int splits) {
 }
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);
+hipError_t launch_adam(int64_t n, float* w, const float* g, float* m, float* v,
+                       const OptConsts& c, hipStream_t s);
+hipError_t launch_ema(int64_t n, float* e, const float* w, float d, float omd, hipStream_t s);
+
+// ---- gradient control (global norm, finite check, loss scale) ---------------
+// The gradient pass reads every gradient once (finishing split-K sums into
+// g_out on the way) and leaves per-workgroup float64 sums of squares and
+// non-finite counts; the control kernel (one workgroup) adds them in a fixed
+// order and writes the GradCtl, updates the loss scaler and ticks the
+// device step count.  The segments' start_block holds prefix sums of units of
+// kStatUnit elements (stat_units: their total); at most kStatBlocks
+// workgroups per launch (stat_grid), each taking units b, b + grid, ...
+constexpr int kStatUnit = kOptElemsPerBlock;
+constexpr int kStatBlocks = 2048;
+int64_t stat_units(const OptSegs& segs);
+int stat_grid(int64_t units);
+hipError_t launch_grad_stats(const OptSegs& segs, int64_t units, double* part_sq, int* part_bad,
+                             hipStream_t s);
+struct CtlArgs {
+  const double* part_sq;
+  const int* part_bad;
+  int parts;
+  double max_norm;          // <= 0: no clipping
+  float* scale;             // loss scale, or null
+  int* growth_tracker;
+  int* found_inf;
+  double growth_factor, backoff_factor;
+  int growth_interval;
+  int64_t* step_dev;        // ticked when the step is applied, or null
+  float* norm_out;          // optional
+  GradCtl* ctl;
+  float* clip_coef;         // optional: min(1, max_norm / (norm + 1e-6))
+};
+hipError_t launch_grad_ctl(const CtlArgs& a, hipStream_t s);
+// g *= *coef where *coef < 1 (clip_grad_norm's in-place scaling).
+hipError_t launch_scale_by(const OptSegs& segs, const float* coef, hipStream_t s);
+
+// ---- mean squared error --------------------------------------------------------
+int mse_grid(int64_t n);
+hipError_t launch_mse(int64_t n, const float* pred, const float* target, float* dpred,
+                      double* part, float* loss, hipStream_t s);
 
 }  // namespace dl

@@ -54,7 +54,9 @@ __global__ void __launch_bounds__(kHeadThreads)
 head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, float* dH,
                  int prev_act, const float* __restrict__ W, const float* __restrict__ bias,
                  const int32_t* __restrict__ labels, float* __restrict__ row_loss,
-                 float* __restrict__ dW_part, float* __restrict__ db_part, float invB) {
+                 float* __restrict__ dW_part, float* __restrict__ db_part, float invB,
+                 const float* dscale) {
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
   constexpr int KP = kHeadKMax + 1;  // padded row stride of the row tiles
   // W transposed, classes padded to 16 with zeros: Wt[k][c]
   __shared__ __attribute__((aligned(16))) float Wt[kHeadKMax * kHeadCMax];
@@ -269,7 +271,8 @@ bool head_xent_fits(int64_t K, int64_t C) {
 
 hipError_t launch_head_xent(int64_t B, int K, int C, const float* H, float* dH, int prev_act,
                             const float* W, const float* bias, const int32_t* labels,
-                            float* row_loss, float* dW_part, float* db_part, hipStream_t s) {
+                            float* row_loss, float* dW_part, float* db_part, hipStream_t s,
+                            const float* dscale) {
   if (!head_xent_fits(K, C) || B < 1) return hipErrorInvalidValue;
   const int64_t ntiles = (B + kHeadRows - 1) / kHeadRows;
   const int64_t per = (ntiles + kHeadMaxSlices - 1) / kHeadMaxSlices;
@@ -278,11 +281,11 @@ hipError_t launch_head_xent(int64_t B, int K, int C, const float* H, float* dH, 
   if (vec)
     hipLaunchKernelGGL(head_xent_kernel<true>, dim3((unsigned)blocks), dim3(kHeadThreads), 0, s, B,
                        K, C, per, H, dH, prev_act, W, bias, labels, row_loss, dW_part, db_part,
-                       (float)(1.0 / (double)B));
+                       (float)(1.0 / (double)B), dscale);
   else
     hipLaunchKernelGGL(head_xent_kernel<false>, dim3((unsigned)blocks), dim3(kHeadThreads), 0, s, B,
                        K, C, per, H, dH, prev_act, W, bias, labels, row_loss, dW_part, db_part,
-                       (float)(1.0 / (double)B));
+                       (float)(1.0 / (double)B), dscale);
   return hipGetLastError();
 }
 

@@ -76,7 +76,9 @@ __device__ __forceinline__ void group_sum2(float& a, float& b, float* red) {
 template <int TPR, int NI, bool VEC, int BLOCK = kXentBlock>
 __global__ void __launch_bounds__(BLOCK)
 xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restrict__ labels,
-                 float* __restrict__ row_loss, float* dlogits, float invB) {
+                 float* __restrict__ row_loss, float* dlogits, float invB,
+                 const float* dscale) {
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
   constexpr int RPB = BLOCK / TPR;
   constexpr int W = VEC ? 4 : 1;
   __shared__ float red[2 * BLOCK / 64];
@@ -148,7 +150,9 @@ xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restric
 // (the second read normally hits L2 / the 256 MB Infinity Cache).
 __global__ void __launch_bounds__(kXentBlock)
 xent_rows_wide_kernel(int64_t B, int64_t C, const float* logits, const int32_t* __restrict__ labels,
-                      float* __restrict__ row_loss, float* dlogits, float invB) {
+                      float* __restrict__ row_loss, float* dlogits, float invB,
+                 const float* dscale) {
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
   __shared__ float red[2 * kXentBlock / 64];
   const int64_t row = blockIdx.x;
   const int64_t base = row * C;
@@ -200,34 +204,36 @@ loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restric
 
 template <int TPR, int NI, bool VEC, int BLOCK = kXentBlock>
 hipError_t launch_rows(int64_t B, int64_t C, const float* logits, const int32_t* labels,
-                       float* row_loss, float* dlogits, hipStream_t s) {
+                       float* row_loss, float* dlogits, const float* dscale, hipStream_t s) {
   constexpr int RPB = BLOCK / TPR;
   const int64_t blocks = (B + RPB - 1) / RPB;
   hipLaunchKernelGGL((xent_rows_kernel<TPR, NI, VEC, BLOCK>), dim3((unsigned)blocks), dim3(BLOCK), 0,
-                     s, B, (int)C, logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
+                     s, B, (int)C, logits, labels, row_loss, dlogits, (float)(1.0 / (double)B),
+                     dscale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t* labels,
-                       float* row_loss, float* dlogits, float* loss, hipStream_t s) {
+                       float* row_loss, float* dlogits, float* loss, hipStream_t s,
+                       const float* dscale) {
   const bool vec = (C % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(dlogits) & 15) == 0);
   hipError_t e;
   if (C <= 32)
-    e = launch_rows<8, 4, false>(B, C, logits, labels, row_loss, dlogits, s);
+    e = launch_rows<8, 4, false>(B, C, logits, labels, row_loss, dlogits, dscale, s);
   else if (C <= 256)
-    e = vec ? launch_rows<32, 2, true>(B, C, logits, labels, row_loss, dlogits, s)
-            : launch_rows<32, 8, false>(B, C, logits, labels, row_loss, dlogits, s);
+    e = vec ? launch_rows<32, 2, true>(B, C, logits, labels, row_loss, dlogits, dscale, s)
+            : launch_rows<32, 8, false>(B, C, logits, labels, row_loss, dlogits, dscale, s);
   else if (C <= 2048)
-    e = vec ? launch_rows<64, 8, true>(B, C, logits, labels, row_loss, dlogits, s)
-            : launch_rows<64, 32, false>(B, C, logits, labels, row_loss, dlogits, s);
+    e = vec ? launch_rows<64, 8, true>(B, C, logits, labels, row_loss, dlogits, dscale, s)
+            : launch_rows<64, 32, false>(B, C, logits, labels, row_loss, dlogits, dscale, s);
   else if (vec && C <= 32768)  // 1024 threads per row: 8 float4 each, more loads in flight
-    e = launch_rows<1024, 8, true, 1024>(B, C, logits, labels, row_loss, dlogits, s);
+    e = launch_rows<1024, 8, true, 1024>(B, C, logits, labels, row_loss, dlogits, dscale, s);
   else {
     hipLaunchKernelGGL(xent_rows_wide_kernel, dim3((unsigned)B), dim3(kXentBlock), 0, s, B, C,
-                       logits, labels, row_loss, dlogits, (float)(1.0 / (double)B));
+                       logits, labels, row_loss, dlogits, (float)(1.0 / (double)B), dscale);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;

@@ -12,8 +12,11 @@
  *   forward  Z = X W^T + b,  Y = act(Z)
  *   vjp      G = dY * act'(Z),  dX = G W,  dW = G^T X,  db = sum_rows G
  *   loss     mean softmax cross-entropy over the batch, dlogits = (p - onehot)/B
+ *            mean squared error, dpred = 2 (p - t) / (B C)
  *   update   SGD  w <- w - lr g
- *            AdamW (decoupled decay, bias-corrected)
+ *            AdamW (decoupled decay, bias-corrected), Adam (coupled decay)
+ *            with global-norm clipping, dynamic loss scaling, LR schedules,
+ *            parameter EMA and a bf16 working copy fused into the update
  *
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major and contiguous.  X is [B, in], W is
@@ -67,7 +70,18 @@ enum dl_status {
   DL_HIP_ERROR = 5             /* a HIP launch failed */
 };
 
-enum dl_opt_kind { DL_OPT_SGD = 0, DL_OPT_ADAMW = 1 };
+enum dl_opt_kind {
+  DL_OPT_SGD = 0,    /* w <- w - lr g */
+  DL_OPT_ADAMW = 1,  /* decoupled decay: w <- w (1 - lr wd), then Adam */
+  DL_OPT_ADAM = 2    /* coupled decay: g <- g + wd w, then Adam */
+};
+
+enum dl_lr_kind {
+  DL_LR_CONSTANT = 0,
+  DL_LR_STEP = 1,            /* lr gamma^floor(k / step_size) */
+  DL_LR_WARMUP_COSINE = 2,   /* linear warmup, then cosine down to min_lr */
+  DL_LR_WARMUP_LINEAR = 3    /* linear warmup, then linear down to min_lr */
+};
 
 /* Message for the last non-zero status returned on the calling thread. */
 const char* dl_last_error(void);
@@ -184,6 +198,87 @@ size_t softmax_xent_workspace_size(int64_t B, int64_t C);
 /* ---- optimizers ---------------------------------------------------------- */
 
 /*
+ * Learning-rate schedule (noeira.nn docs, "Optimizers & losses": LR
+ * schedules).  Step t >= 1 of the optimizer uses k = t - 1 scheduler steps:
+ *   DL_LR_CONSTANT       lr
+ *   DL_LR_STEP           lr * gamma^floor(k / step_size)          (step_size >= 1)
+ *   DL_LR_WARMUP_COSINE  lr (k + 1) / warmup for k < warmup, then
+ *                        min_lr + (lr - min_lr) (1 + cos(pi j / T)) / 2,
+ *                        j = min(k - warmup, T), T = total - warmup
+ *   DL_LR_WARMUP_LINEAR  the same warmup, then min_lr + (lr - min_lr) (T - j) / T
+ * (T <= 0 gives min_lr after the warmup.)  Evaluated in double, on the host
+ * from a host step count or on the device from a device step count.
+ */
+typedef struct dl_lr_schedule {
+  int32_t kind;        /* enum dl_lr_kind */
+  int64_t warmup;      /* >= 0 */
+  int64_t total;       /* step count at which the decay reaches min_lr */
+  int64_t step_size;   /* DL_LR_STEP */
+  double min_lr;
+  double gamma;        /* DL_LR_STEP */
+} dl_lr_schedule_t;
+
+/* The learning rate of step `step` (>= 1) for base rate `lr` under schedule
+ * `s` (NULL: constant).  Host function; returns NaN for a bad argument. */
+double dl_lr_at(const dl_lr_schedule_t* s, double lr, int64_t step);
+
+/*
+ * Dynamic loss scaling (Orthon page, "Core capabilities": a GradScaler with
+ * finite checks, skipped steps, backoff and growth).  The loss gradient is
+ * multiplied by S = *scale, so every gradient the backward forms is S times
+ * the true one.  The optimizer looks at all of a step's gradients: if one of
+ * them holds a NaN or an Inf, the step is skipped (no parameter, moment,
+ * average or step-count change), *found_inf = 1, S <- S backoff_factor and
+ * the tracker resets; otherwise the gradients are used divided by S,
+ * *found_inf = 0, the tracker counts the step and, on reaching
+ * growth_interval, S <- S growth_factor and the tracker resets.  All three
+ * values live in device memory and are updated on the device, so no host
+ * synchronisation is needed.  The caller initialises *scale (e.g. 65536)
+ * and *growth_tracker (0).
+ */
+typedef struct dl_loss_scaler {
+  float* scale;             /* device float32 [1] */
+  int32_t* growth_tracker;  /* device int32 [1] */
+  int32_t* found_inf;       /* device int32 [1] output */
+  double growth_factor;     /* > 1, e.g. 2 */
+  double backoff_factor;    /* in (0, 1), e.g. 0.5 */
+  int32_t growth_interval;  /* >= 1, e.g. 2000 */
+} dl_loss_scaler_t;
+
+/*
+ * Optimizer configuration, shared by optimizer_step and mlp_train_step.
+ */
+typedef struct dl_opt {
+  int32_t kind;     /* enum dl_opt_kind */
+  double lr, beta1, beta2, eps, weight_decay;  /* betas/eps/wd: Adam, AdamW */
+  int64_t step;     /* Adam / AdamW step t >= 1, and the step of the
+                     * schedule (ignored when step_dev is set) */
+  /* optional: device int64 [1] holding the number of steps taken.  When set,
+   * each call adds 1 to it on the device (in stream order; not for a step a
+   * loss scaler skips) and the update uses that value as t, its bias
+   * corrections and scheduled learning rate formed on the device in double
+   * exactly as the host forms them from `step`.  This makes the whole step
+   * replayable from a captured stream graph, which cannot see a host-side
+   * step count.  Caller-owned; NULL to use `step`.  Required with a loss
+   * scaler unless the optimizer is SGD without a schedule. */
+  int64_t* step_dev;
+  /* > 0: clip the global 2-norm of all of the call's gradients (after
+   * unscaling): every gradient is multiplied by
+   * min(1, max_grad_norm / (norm + 1e-6)) (MuNet page, "What runs today":
+   * gradient clipping).  <= 0: no clipping. */
+  double max_grad_norm;
+  /* decay d of the parameter averages: e <- d e + (1 - d) w after the update,
+   * for every array that has an average (MuNet page, "What runs today": EMA) */
+  double ema_decay;
+  const dl_lr_schedule_t* schedule;  /* host pointer, or NULL: constant lr */
+  const dl_loss_scaler_t* scaler;    /* host pointer, or NULL: no loss scaling */
+  /* optional device float32 [1] output: the global norm of the unscaled
+   * gradients (formed when clipping or loss scaling is on) */
+  float* grad_norm;
+} dl_opt_t;
+
+
+/*
  * sgd_step -- w <- w - lr g, elementwise over n float32 values (MuNet page,
  * "What runs today" and "Python training": SGD).  Plain: no momentum, no
  * decay.  lr is rounded once to float32.  w and g are device pointers; g
@@ -206,6 +301,93 @@ int sgd_step(void* stream, int64_t n, float* w, const float* g, double lr);
 int adamw_step(void* stream, int64_t n, float* w, const float* g, float* m,
                float* v, double lr, double beta1, double beta2, double eps,
                double weight_decay, int64_t step);
+
+/*
+ * adam_step -- one Adam step with coupled (L2) weight decay on n float32
+ * values (noeira.nn docs, "Optimizers & losses" and the Orthon page, "Core
+ * capabilities": Adam):
+ *   g' = g + wd w;  m <- b1 m + (1-b1) g';  v <- b2 v + (1-b2) g'^2;
+ *   w <- w - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * Arguments, constants and errors as adamw_step.
+ */
+int adam_step(void* stream, int64_t n, float* w, const float* g, float* m,
+              float* v, double lr, double beta1, double beta2, double eps,
+              double weight_decay, int64_t step);
+
+/*
+ * ema_update -- e <- d e + (1 - d) w over n float32 values (MuNet page,
+ * "What runs today": EMA of the parameters).  d in [0, 1]; e and w distinct
+ * device arrays.
+ */
+int ema_update(void* stream, int64_t n, float* ema, const float* w,
+               double decay);
+
+/*
+ * clip_grad_norm -- scale a set of gradient arrays in place so that their
+ * global 2-norm is at most max_norm (MuNet page, "What runs today": gradient
+ * clipping): norm = sqrt(sum over all arrays of g^2) (float64 partial sums in
+ * a fixed order), every g is multiplied by min(1, max_norm / (norm + 1e-6)).
+ *   count in [1, 4096]; grads a host array of `count` device float32
+ *   pointers; n a host array of their lengths (> 0); max_norm > 0;
+ *   total_norm optional device float32 [1] output (the norm before
+ *   clipping); ws, ws_bytes at least clip_grad_norm_workspace_size().
+ * The arrays must not overlap one another or the workspace.
+ */
+int clip_grad_norm(void* stream, int32_t count, float* const* grads,
+                   const int64_t* n, double max_norm, float* total_norm,
+                   void* ws, size_t ws_bytes);
+
+size_t clip_grad_norm_workspace_size(int32_t count, const int64_t* n);
+
+/*
+ * One array the multi-tensor optimizer updates (noeira.nn docs, "The design
+ * in one page": a Param holds its value, gradient and Adam moments).
+ */
+typedef struct dl_param {
+  int64_t n;         /* element count, > 0 */
+  float* w;          /* device float32 [n], updated in place */
+  const float* g;    /* device float32 [n] gradient (times the loss scale) */
+  float* m;          /* device float32 [n] first moment (Adam, AdamW) */
+  float* v;          /* device float32 [n] second moment (Adam, AdamW) */
+  float* ema;        /* device float32 [n] parameter average, or NULL */
+  void* w_bf16;      /* device bf16 [n]: RNE copy of the updated w, or NULL
+                      * (the FP32-master scheme of the Orthon page,
+                      * "Mixed-precision training on CUDA") */
+} dl_param_t;
+
+/*
+ * optimizer_step -- one update of `count` arrays by opt->kind with every
+ * option of dl_opt_t: loss-scale finite check and unscaling, global-norm
+ * clipping, the schedule's learning rate, the parameter averages and the
+ * bf16 copies, all fused into one pass over the arrays (plus one reading
+ * pass over the gradients and one single-workgroup launch when clipping or
+ * loss scaling is on).  Arrays are processed 32 to a launch.
+ *   count in [1, 4096]; params a host array; opt a host pointer.
+ *   ws, ws_bytes at least optimizer_step_workspace_size().
+ * No two arrays of the call (w, g, m, v, ema, w_bf16 of any param) may
+ * overlap.
+ */
+int optimizer_step(void* stream, const dl_opt_t* opt, int32_t count,
+                   const dl_param_t* params, void* ws, size_t ws_bytes);
+
+size_t optimizer_step_workspace_size(int32_t count, const dl_param_t* params);
+
+/* ---- mean squared error -------------------------------------------------- */
+
+/*
+ * mse_loss_fwd_bwd -- loss = (1/(B C)) sum (pred - target)^2 and
+ * dpred = 2 (pred - target) / (B C) in one pass (MuNet page, "Python
+ * training": the step's mse_loss; noeira.nn docs, package layout: MSE).  The
+ * squares are summed in float64, per workgroup and then in a fixed order.
+ *   B, C > 0; pred, target device float32 [B, C]; loss device float32 [1]
+ *   output; dpred device float32 [B, C] output, may equal pred (in place),
+ *   or NULL (loss only); ws, ws_bytes at least mse_loss_workspace_size(B, C).
+ */
+int mse_loss_fwd_bwd(void* stream, int64_t B, int64_t C, const float* pred,
+                     const float* target, float* loss, float* dpred, void* ws,
+                     size_t ws_bytes);
+
+size_t mse_loss_workspace_size(int64_t B, int64_t C);
 
 /* ---- bf16 working copies -------------------------------------------------- */
 
@@ -242,20 +424,10 @@ typedef struct dl_layer {
   float* vW;        /* device [out, in] AdamW second moment (NULL for SGD) */
   float* mb;        /* device [out] */
   float* vb;        /* device [out] */
+  float* eW;        /* device [out, in] parameter average, or NULL */
+  float* eb;        /* device [out] parameter average, or NULL */
 } dl_layer_t;
 
-typedef struct dl_opt {
-  int32_t kind;     /* enum dl_opt_kind */
-  double lr, beta1, beta2, eps, weight_decay;  /* betas/eps/wd: AdamW only */
-  int64_t step;     /* AdamW step t >= 1 (ignored when step_dev is set) */
-  /* AdamW, optional: device int64 [1] holding the number of steps taken.
-   * When set, each call first adds 1 to it on the device (in stream order)
-   * and the update uses that value as t, its bias corrections formed on the
-   * device in double exactly as the host forms them from `step`.  This makes
-   * the whole step replayable from a captured stream graph, which cannot see
-   * a host-side step count.  Caller-owned; NULL to use `step`. */
-  int64_t* step_dev;
-} dl_opt_t;
 
 /*
  * mlp_train_step -- forward through every layer, softmax cross-entropy on the
@@ -266,6 +438,14 @@ typedef struct dl_opt {
  * Linear MLP).  Float32 throughout.  The loss written is the one computed
  * before the update.  Hidden-layer activations are fused into the GEMM
  * epilogues and their derivatives into the dX epilogues.
+ *
+ * Every option of dl_opt_t applies: SGD, Adam or AdamW; a device step count
+ * and a learning-rate schedule; global-norm clipping over all W and b; a
+ * loss scaler (the loss gradient is multiplied by S, dW / db hold S times the
+ * gradient, a step with non-finite gradients is skipped); and the parameter
+ * averages of the layers that have eW / eb (all or none).  With clipping or
+ * a loss scaler the split weight-gradient sums are finished by the gradient
+ * pass rather than the optimizer.
  *
  *   B > 0; n_layers in [1, 16]; layers is a host array of n_layers entries.
  *   X        device float32 [B, layers[0].in]
