@@ -34,7 +34,7 @@ PEAK_HBM = 8000.0        # GB/s
 
 
 KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
-                  "head.hip", "optim.hip", "elementwise.hip", "api.cpp"]
+                  "head.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip", "api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -271,10 +271,89 @@ class HeadBench:
         return None
 
 
+class OptBench:
+    """The fused multi-array optimizer step over the wide MLP's parameters
+    (41,858,024 floats in 8 arrays): AdamW with a loss scaler, global-norm
+    clipping, parameter averages and bf16 copies, device step count.  One
+    step: a gradient pass, the control kernel and the update."""
+
+    def __init__(self, dl, w, dev):
+        import torch
+        self.dl, self.w = dl, w
+        inp = si.generate(w)
+        self.params = []
+        for k, a in enumerate(inp.W + inp.b):
+            wt = torch.from_numpy(a).to(dev)
+            g = torch.from_numpy(si.random_matrix(w.seed * 100 + k, a.shape, scale=0.05)).to(dev)
+            self.params.append(dl.Param(wt, g, torch.zeros_like(wt), torch.zeros_like(wt),
+                                        wt.clone(), torch.empty(a.shape, dtype=torch.bfloat16,
+                                                                device=dev)))
+        self.n = sum(p.w.numel() for p in self.params)
+        self.step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+        self.scaler = dl.LossScaler(dev, init_scale=1024.0)
+        self.ws = torch.empty(dl.optimizer_step_workspace_size(self.params), dtype=torch.uint8,
+                              device=dev)
+
+    def step(self):
+        o = self.w.optim
+        self.dl.optimizer_step(self.params, self.dl.OPT_ADAMW, lr=o.lr, beta1=o.beta1,
+                               beta2=o.beta2, eps=o.eps, weight_decay=o.weight_decay,
+                               step_dev=self.step_dev, max_grad_norm=1.0, ema_decay=0.999,
+                               scaler=self.scaler, ws=self.ws)
+
+    def flops(self):
+        return 0
+
+    def stage_work(self, label):
+        name, _ = _split(label)
+        if name == "grad_stats":
+            return "byte", 4 * self.n
+        if name == "opt_multi":  # read w, g, m, v, average; write w, m, v, average, bf16 copy
+            return "byte", 38 * self.n
+        return None
+
+
+class MseBench:
+    """Mean squared error forward + backward over [16384, 4096] float32."""
+
+    def __init__(self, dl, w, dev):
+        import torch
+        self.dl, self.w = dl, w
+        B, C = w.batch, w.dims[0]
+        self.p = torch.from_numpy(si.random_matrix(w.seed, (B, C))).to(dev)
+        self.t = torch.from_numpy(si.random_matrix(w.seed + 1, (B, C))).to(dev)
+        self.dp = torch.empty_like(self.p)
+        self.loss = torch.empty(1, device=dev)
+        self.ws = torch.empty(dl.mse_loss_workspace_size(B, C), dtype=torch.uint8, device=dev)
+
+    def step(self):
+        self.dl.mse_loss_fwd_bwd(self.p, self.t, dpred=self.dp, loss=self.loss, ws=self.ws)
+
+    def flops(self):
+        return 0
+
+    def stage_work(self, label):
+        if _split(label)[0] == "mse":  # read pred and target, write dpred
+            return "byte", 12 * self.w.batch * self.w.dims[0]
+        return None
+
+
+# Workloads of the optimizer and loss variants (parameter shapes of the wide
+# MLP; a [16384, 4096] regression output), beside the five step workloads.
+EXTRA_WORKLOADS = {
+    "opt_fused": si.Workload("opt_fused", 6, 16384, [1024, 4096, 4096, 4096, 1000],
+                             [si.ACT_RELU] * 3 + [si.ACT_IDENTITY], "kaiming", "uniform001",
+                             "f32", si.ADAMW, has_loss=False),
+    "mse": si.Workload("mse", 7, 16384, [4096], [], "kaiming", "zero", "f32", None,
+                       has_loss=False),
+}
+WORKLOADS = {**si.WORKLOADS, **EXTRA_WORKLOADS}
+
 BENCHES = {"mlp_small": MLPBench, "mlp_adamw": MLPBench, "mlp_wide": MLPBench,
-           "tmlp_bf16": TmlpBench, "head_xent": HeadBench}
+           "tmlp_bf16": TmlpBench, "head_xent": HeadBench, "opt_fused": OptBench,
+           "mse": MseBench}
 DEFAULTS = {"mlp_small": (200, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
-            "tmlp_bf16": (20, 3), "head_xent": (5, 1)}
+            "tmlp_bf16": (20, 3), "head_xent": (5, 1), "opt_fused": (50, 5), "mse": (50, 5)}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -352,7 +431,7 @@ def main():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    w = si.WORKLOADS[args.config]
+    w = WORKLOADS[args.config]
     steps, warmup = DEFAULTS[args.config]
     steps = args.steps if args.steps is not None else steps
     warmup = args.warmup if args.warmup is not None else warmup

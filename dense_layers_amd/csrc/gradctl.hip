@@ -54,20 +54,79 @@ __device__ __forceinline__ int seg_of(const OptSegs& segs, int64_t u) {
 }
 
 // Unit u of a segment: elements [u * kStatUnit, +kStatUnit); thread t takes
-// the float4 groups at t*4 + {0, 1, 2, 3} * 1024, all loaded before use.
+// the float4 groups at t*4 + {0, 1, 2, 3} * 1024.
+struct UnitPos {
+  int s;
+  int64_t n, base;
+};
+__device__ __forceinline__ UnitPos unit_pos(const OptSegs& segs, int64_t u) {
+  const int s = seg_of(segs, u);
+  return UnitPos{s, segs.n[s], (u - segs.start_block[s]) * kStatUnit + (int64_t)threadIdx.x * 4};
+}
+
+// The thread's 16 gradient values of unit u; places past the array's end
+// read as 0 (which adds nothing to the sum of squares and is finite).
+__device__ __forceinline__ void fetch_unit(const OptSegs& segs, int64_t u, f32x4 (&a)[4]) {
+  const UnitPos q = unit_pos(segs, u);
+  const float* g = segs.g[q.s];
+  if (q.base + 3 * 1024 + 3 < q.n && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) a[it] = *reinterpret_cast<const f32x4*>(g + q.base + it * 1024);
+  } else {
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = q.base + it * 1024 + e;
+        a[it][e] = i < q.n ? g[i] : 0.f;
+      }
+  }
+}
+
+// Plain gradients: software-pipelined, the next unit's loads are issued
+// before the current unit is added up.
 __global__ void __launch_bounds__(kOptBlock)
 grad_stats_kernel(OptSegs segs, int64_t units, double* __restrict__ part_sq,
                   int* __restrict__ part_bad) {
   double acc = 0.0;
   int bad = 0;
+  int64_t u = blockIdx.x;
+  f32x4 cur[4];
+  if (u < units) fetch_unit(segs, u, cur);
+  while (u < units) {
+    const int64_t un = u + gridDim.x;
+    f32x4 nxt[4];
+    if (un < units) fetch_unit(segs, un, nxt);
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) account(cur[it][e], acc, bad);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) cur[it] = nxt[it];
+    u = un;
+  }
+  block_sum(acc, bad);
+  if (threadIdx.x == 0) {
+    part_sq[blockIdx.x] = acc;
+    part_bad[blockIdx.x] = bad;
+  }
+}
+
+// Split-K segments present (the MLP step): the slices of each element are
+// added in slice order and the sum is stored to the segment's gradient
+// array before it is accounted.
+__global__ void __launch_bounds__(kOptBlock)
+grad_stats_split_kernel(OptSegs segs, int64_t units, double* __restrict__ part_sq,
+                        int* __restrict__ part_bad) {
+  double acc = 0.0;
+  int bad = 0;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int s = seg_of(segs, u);
-    const int64_t n = segs.n[s];
-    const int64_t base = (u - segs.start_block[s]) * kStatUnit + (int64_t)threadIdx.x * 4;
-    const int S = segs.splits[s];
-    const float* src = S > 1 ? segs.part[s] : segs.g[s];
-    const int64_t stride = S > 1 ? segs.part_stride[s] : 0;
-    float* out = segs.g_out[s];
+    const UnitPos q = unit_pos(segs, u);
+    const int64_t n = q.n, base = q.base;
+    const int S = segs.splits[q.s];
+    const float* src = S > 1 ? segs.part[q.s] : segs.g[q.s];
+    const int64_t stride = S > 1 ? segs.part_stride[q.s] : 0;
+    float* out = segs.g_out[q.s];
     const bool full = base + 3 * 1024 + 3 < n;
     const bool vec = full && ((reinterpret_cast<uintptr_t>(src) |
                                static_cast<uintptr_t>(stride * 4) |
@@ -192,8 +251,14 @@ int stat_grid(int64_t units) {
 hipError_t launch_grad_stats(const OptSegs& segs, int64_t units, double* part_sq, int* part_bad,
                              hipStream_t s) {
   if (units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(grad_stats_kernel, dim3((unsigned)stat_grid(units)), dim3(kOptBlock), 0, s,
-                     segs, units, part_sq, part_bad);
+  bool split = false;
+  for (int k = 0; k < segs.count; ++k) split = split || segs.splits[k] > 1;
+  if (split)
+    hipLaunchKernelGGL(grad_stats_split_kernel, dim3((unsigned)stat_grid(units)), dim3(kOptBlock),
+                       0, s, segs, units, part_sq, part_bad);
+  else
+    hipLaunchKernelGGL(grad_stats_kernel, dim3((unsigned)stat_grid(units)), dim3(kOptBlock), 0, s,
+                       segs, units, part_sq, part_bad);
   return hipGetLastError();
 }
 

@@ -24,46 +24,65 @@ __device__ __forceinline__ double block_sum_d(double acc) {
 }
 
 // Units of kStatUnit elements; thread t takes the float4 groups at
-// t*4 + {0, 1, 2, 3} * 1024.  dpred may equal pred: every element is read and
-// then written by the same thread.
+// t*4 + {0, 1, 2, 3} * 1024.  Full aligned units go through a software
+// pipeline (the next unit's loads are issued before the current one is
+// used); the array's last, partial unit is done element by element.  dpred
+// may equal pred: every element is read and then written by the same thread.
+__device__ __forceinline__ void mse_fetch(const float* pred, const float* target, int64_t base,
+                                          f32x4 (&p)[4], f32x4 (&t)[4]) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    p[it] = *reinterpret_cast<const f32x4*>(pred + base + it * 1024);
+    t[it] = *reinterpret_cast<const f32x4*>(target + base + it * 1024);
+  }
+}
+
 __global__ void __launch_bounds__(kOptBlock)
 mse_kernel(int64_t n, const float* pred, const float* __restrict__ target, float* dpred,
            double* __restrict__ part, float two_over_n, int vec) {
   double acc = 0.0;
   const int64_t units = (n + kStatUnit - 1) / kStatUnit;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+  // units whose every thread's 16 elements exist (all but a partial last one)
+  const int64_t full_units = vec ? n / kStatUnit : 0;
+  int64_t u = blockIdx.x;
+  f32x4 p[4], t[4];
+  if (u < full_units) mse_fetch(pred, target, u * kStatUnit + (int64_t)threadIdx.x * 4, p, t);
+  while (u < full_units) {
+    const int64_t un = u + gridDim.x;
+    f32x4 pn[4], tn[4];
+    if (un < full_units) mse_fetch(pred, target, un * kStatUnit + (int64_t)threadIdx.x * 4, pn, tn);
     const int64_t base = u * kStatUnit + (int64_t)threadIdx.x * 4;
-    if (vec && base + 3 * 1024 + 3 < n) {
-      f32x4 p[4], t[4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        p[it] = *reinterpret_cast<const f32x4*>(pred + base + it * 1024);
-        t[it] = *reinterpret_cast<const f32x4*>(target + base + it * 1024);
+    for (int it = 0; it < 4; ++it) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double d = (double)p[it][e] - (double)t[it][e];
+        acc += d * d;
       }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double d = (double)p[it][e] - (double)t[it][e];
-          acc += d * d;
-        }
-        if (dpred != nullptr)
-          *reinterpret_cast<f32x4*>(dpred + base + it * 1024) = (p[it] - t[it]) * two_over_n;
-      }
-    } else {
-      for (int it = 0; it < 4; ++it)
-        for (int e = 0; e < 4; ++e) {
-          const int64_t i = base + it * 1024 + e;
-          if (i >= n) continue;
-          const float pi = pred[i], ti = target[i];
-          const double d = (double)pi - (double)ti;
-          acc += d * d;
-          if (dpred != nullptr) dpred[i] = (pi - ti) * two_over_n;
-        }
+      if (dpred != nullptr)
+        *reinterpret_cast<f32x4*>(dpred + base + it * 1024) = (p[it] - t[it]) * two_over_n;
     }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      p[it] = pn[it];
+      t[it] = tn[it];
+    }
+    u = un;
   }
-  const double t = block_sum_d(acc);
-  if (threadIdx.x == 0) part[blockIdx.x] = t;
+  for (; u < units; u += gridDim.x) {
+    const int64_t base = u * kStatUnit + (int64_t)threadIdx.x * 4;
+    for (int it = 0; it < 4; ++it)
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = base + it * 1024 + e;
+        if (i >= n) continue;
+        const float pi = pred[i], ti = target[i];
+        const double d = (double)pi - (double)ti;
+        acc += d * d;
+        if (dpred != nullptr) dpred[i] = (pi - ti) * two_over_n;
+      }
+  }
+  const double r = block_sum_d(acc);
+  if (threadIdx.x == 0) part[blockIdx.x] = r;
 }
 
 __global__ void __launch_bounds__(kOptBlock)
