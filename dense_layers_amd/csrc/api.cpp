@@ -640,7 +640,7 @@ static int adam_like(const char* who, int kind, void* stream, int64_t n, float* 
     return fail(DL_ALIASING, "%s: w, g, m, v must be distinct", who);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dl::OptConsts oc = opt_consts(plain_opt(kind, lr, beta1, beta2, eps, weight_decay, step), step);
-  hipError_t e = timed(who, st, [&] {
+  hipError_t e = timed(kind == DL_OPT_ADAM ? "adam" : "adamw", st, [&] {
     return kind == DL_OPT_ADAM ? dl::launch_adam(n, w, g, m, v, oc, st)
                                : dl::launch_adamw(n, w, g, m, v, oc, st);
   });

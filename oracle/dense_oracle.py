@@ -79,6 +79,27 @@ def round_bf16(a) -> np.ndarray:
     return out.astype(np.float64)
 
 
+F16_MAX = 65504.0
+
+
+def round_f16_sat(a) -> np.ndarray:
+    """Round to IEEE half precision with round-to-nearest-even, saturating
+    at +-65504, NaN preserved.
+
+    The fp16 input convention of the MuNet page ("Configuration", the mixed
+    precision setting: round to nearest, saturating at +-65504, NaN
+    preserved).  The value is first rounded to float32 (as the float32
+    accumulator holds it), then to half by NumPy's round-half-to-even cast;
+    a result that overflowed to +-inf (a finite value at or past the
+    rounding threshold, or an infinite input) becomes +-65504.  Returned as
+    float64 holding half-representable values.
+    """
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    with np.errstate(over="ignore"):
+        h = f.astype(np.float16).astype(np.float64)
+    return np.where(np.isinf(h), np.copysign(F16_MAX, h), h)
+
+
 # ---------------------------------------------------------------------------
 # Activations (noeira.nn docs, "The design in one page": LinearAct fuses
 # MatMul + Bias + Activation; the derivative is the act' of the vjp)

@@ -209,3 +209,23 @@ def test_skipped_step_counting_caught(monkeypatch):
 
     monkeypatch.setattr(O, "mlp_train_step", wrong)
     _expect_pin_failure(PT.test_mlp_scaler_skips_non_finite_step_and_backs_off)
+
+
+def test_f16_overflow_to_inf_caught(monkeypatch):
+    def no_saturation(a):
+        f = np.asarray(a, np.float64).astype(np.float32)
+        with np.errstate(over="ignore"):
+            return f.astype(np.float16).astype(np.float64)
+
+    monkeypatch.setattr(O, "round_f16_sat", no_saturation)
+    _expect_pin_failure(P.test_round_f16_sat_hand_values)
+
+
+def test_f16_truncation_caught(monkeypatch):
+    def truncate(a):
+        f = np.asarray(a, np.float64).astype(np.float32)
+        u = f.view(np.uint32) & np.uint32(0xFFFFE000)  # chop the low 13 mantissa bits
+        return np.clip(u.view(np.float32).astype(np.float64), -65504.0, 65504.0)
+
+    monkeypatch.setattr(O, "round_f16_sat", truncate)
+    _expect_pin_failure(P.test_round_f16_sat_matches_torch_cast_in_range)

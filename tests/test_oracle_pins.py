@@ -49,6 +49,27 @@ def test_round_bf16_matches_torch_cast():
     assert np.array_equal(O.round_bf16(x32), ref)
 
 
+def test_round_f16_sat_hand_values():
+    e = 2.0 ** -24  # smallest half subnormal
+    cases = [(1.0, 1.0), (65504.0, 65504.0), (65519.0, 65504.0), (65520.0, 65504.0),
+             (1e9, 65504.0), (-1e9, -65504.0), (np.inf, 65504.0), (-np.inf, -65504.0),
+             (e, e), (0.5 * e, 0.0), (1.5 * e, 2 * e), (2.5 * e, 2 * e),
+             (1.0 + 2.0 ** -11, 1.0), (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),
+             (-2.0 ** -14, -2.0 ** -14), (0.1, 0.0999755859375)]
+    got = O.round_f16_sat(np.array([c[0] for c in cases]))
+    for (x, want), g in zip(cases, got):
+        assert g == want, (x, g, want)
+    assert np.isnan(O.round_f16_sat(np.array([np.nan]))[0])
+
+
+def test_round_f16_sat_matches_torch_cast_in_range():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-12, 11, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 65504.0]
+    ref = torch.from_numpy(x).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_f16_sat(x), ref)
+
+
 def test_round_f32_matches_cast():
     x = np.array([1.0 + 2.0 ** -30, 0.1, -7.3e-9])
     assert np.array_equal(O.round_f32(x), x.astype(np.float32).astype(np.float64))
