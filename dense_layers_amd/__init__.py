@@ -18,7 +18,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libdense_layers_amd.so")
 
-DL_F32, DL_BF16 = 0, 1
+DL_F32, DL_BF16, DL_F16 = 0, 1, 2
 ACT_IDENTITY, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
 OPT_SGD, OPT_ADAMW, OPT_ADAM = 0, 1, 2
 LR_CONSTANT, LR_STEP, LR_WARMUP_COSINE, LR_WARMUP_LINEAR = 0, 1, 2, 3
@@ -107,6 +107,8 @@ _c = {
                        [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
     "dense_cast_bf16": _sig("dense_cast_bf16", _i32, [_vp, _i64, _vp, _vp]),
     "dense_cast_bf16_t": _sig("dense_cast_bf16_t", _i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "dense_cast_f16": _sig("dense_cast_f16", _i32, [_vp, _i64, _vp, _vp]),
+    "dense_cast_f16_t": _sig("dense_cast_f16_t", _i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "mlp_train_step": _sig("mlp_train_step", _i32,
                            [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,
                             ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
@@ -135,7 +137,8 @@ _c = {
 EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
-           "dense_cast_bf16", "dense_cast_bf16_t", "mlp_train_step",
+           "dense_cast_bf16", "dense_cast_bf16_t", "dense_cast_f16", "dense_cast_f16_t",
+           "mlp_train_step",
            "mlp_train_step_workspace_size", "adam_step", "ema_update", "clip_grad_norm",
            "clip_grad_norm_workspace_size", "optimizer_step", "optimizer_step_workspace_size",
            "mse_loss_fwd_bwd", "mse_loss_workspace_size", "dl_lr_at",
@@ -195,7 +198,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return DL_F32
     if t.dtype == torch.bfloat16:
         return DL_BF16
-    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return DL_F16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _act(act) -> int:
@@ -478,31 +483,51 @@ def mse_loss_fwd_bwd(pred: torch.Tensor, target: torch.Tensor,
     return loss, dpred
 
 
+def _cast_t(name, tdt, src, dst, dst_t, copy, transposed):
+    _dev(src, "src", torch.float32)
+    rows, cols = src.shape
+    if copy and dst is None:
+        dst = torch.empty((rows, cols), dtype=tdt, device=src.device)
+    if transposed and dst_t is None:
+        dst_t = torch.empty((cols, rows), dtype=tdt, device=src.device)
+    if dst is not None:
+        _dev(dst, "dst", tdt, (rows, cols))
+    if dst_t is not None:
+        _dev(dst_t, "dst_t", tdt, (cols, rows))
+    _check(_c[name](_stream(src), rows, cols, _ptr(src), _ptr(dst), _ptr(dst_t)))
+    return dst, dst_t
+
+
+def _cast(name, tdt, src, dst):
+    _dev(src, "src", torch.float32)
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=tdt, device=src.device)
+    _dev(dst, "dst", tdt, tuple(src.shape))
+    _check(_c[name](_stream(src), src.numel(), _ptr(src), _ptr(dst)))
+    return dst
+
+
 def dense_cast_bf16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
                       dst_t: Optional[torch.Tensor] = None, copy: bool = True,
                       transposed: bool = True):
     """bf16 copy of a [rows, cols] matrix and/or its transpose; returns (dst, dst_t)."""
-    _dev(src, "src", torch.float32)
-    rows, cols = src.shape
-    if copy and dst is None:
-        dst = torch.empty((rows, cols), dtype=torch.bfloat16, device=src.device)
-    if transposed and dst_t is None:
-        dst_t = torch.empty((cols, rows), dtype=torch.bfloat16, device=src.device)
-    if dst is not None:
-        _dev(dst, "dst", torch.bfloat16, (rows, cols))
-    if dst_t is not None:
-        _dev(dst_t, "dst_t", torch.bfloat16, (cols, rows))
-    _check(_c["dense_cast_bf16_t"](_stream(src), rows, cols, _ptr(src), _ptr(dst), _ptr(dst_t)))
-    return dst, dst_t
+    return _cast_t("dense_cast_bf16_t", torch.bfloat16, src, dst, dst_t, copy, transposed)
 
 
 def dense_cast_bf16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):
-    _dev(src, "src", torch.float32)
-    if dst is None:
-        dst = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
-    _dev(dst, "dst", torch.bfloat16, tuple(src.shape))
-    _check(_c["dense_cast_bf16"](_stream(src), src.numel(), _ptr(src), _ptr(dst)))
-    return dst
+    return _cast("dense_cast_bf16", torch.bfloat16, src, dst)
+
+
+def dense_cast_f16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
+                     dst_t: Optional[torch.Tensor] = None, copy: bool = True,
+                     transposed: bool = True):
+    """Half copy (saturating at +-65504) of a [rows, cols] matrix and/or its
+    transpose; returns (dst, dst_t)."""
+    return _cast_t("dense_cast_f16_t", torch.float16, src, dst, dst_t, copy, transposed)
+
+
+def dense_cast_f16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):
+    return _cast("dense_cast_f16", torch.float16, src, dst)
 
 
 # ---------------------------------------------------------------- MLP step

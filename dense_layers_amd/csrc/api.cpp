@@ -65,7 +65,9 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-size_t esize(int dtype) { return dtype == DL_BF16 ? 2 : 4; }
+size_t esize(int dtype) { return dtype == DL_F32 ? 4 : 2; }
+
+bool dtype_ok(int dtype) { return dtype == DL_F32 || dtype == DL_BF16 || dtype == DL_F16; }
 
 bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   if (a == nullptr || b == nullptr || an == 0 || bn == 0) return false;
@@ -99,7 +101,7 @@ struct Plan {
 };
 
 void tile_shape(int dtype, int tile, int& bm, int& bn, int& bk) {
-  if (dtype == DL_BF16) {
+  if (dtype != DL_F32) {  // 16-bit operands
     bm = bn = tile == 1 ? 128 : 256;
     bk = 64;
   } else {
@@ -120,10 +122,10 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   // enough of them, else 128x128; the split-K count aims at two workgroups
   // per CU for the former and four for the latter.
   int64_t per_cu = 4;
-  if (dtype == DL_BF16 && epi == dl::EPI_DW && tiles >= 32) {
+  if (dtype != DL_F32 && epi == dl::EPI_DW && tiles >= 32) {
     p.tile = 2;
     per_cu = 2;
-  } else if (tiles < kCUs || (dtype == DL_BF16 && epi == dl::EPI_DW)) {
+  } else if (tiles < kCUs || (dtype != DL_F32 && epi == dl::EPI_DW)) {
     p.tile = 1;
     if (dtype == DL_F32 && epi != dl::EPI_DW && ceil_div(M, 64) * ceil_div(N, 128) >= kCUs)
       p.tile = 2;
@@ -152,7 +154,10 @@ size_t splitk_bytes(const Plan& p, int64_t M, int64_t N) {
 }
 
 hipError_t run_gemm(int dtype, const dl::GemmDesc& d, int tile, hipStream_t s) {
-  return dtype == DL_BF16 ? dl::launch_gemm_bf16(d, tile, s) : dl::launch_gemm_f32(d, tile, s);
+  if (dtype == DL_F32) return dl::launch_gemm_f32(d, tile, s);
+  dl::GemmDesc h = d;
+  h.half_kind = dtype == DL_F16 ? dl::HK_F16 : dl::HK_BF16;
+  return dl::launch_gemm_bf16(h, tile, s);
 }
 
 dl::GemmDesc blank_desc() {
@@ -301,7 +306,7 @@ int dl_profile_end(int max, float* ms, char* names) {
 
 int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
                   const void* X, const void* W, const float* b, void* Y, void* Z) {
-  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: bad dtype %d", dtype);
+  if (!dtype_ok(dtype)) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: bad dtype %d", dtype);
   if (!act_ok(act)) return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: bad activation %d", act);
   if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
     return fail(DL_INVALID_ARGUMENT, "dense_act_fwd: sizes must be in [1, 2^31): B=%lld in=%lld out=%lld",
@@ -319,7 +324,7 @@ int dense_act_fwd(void* stream, int dtype, int act, int64_t B, int64_t in, int64
 }
 
 size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in, int64_t out) {
-  if ((dtype != DL_F32 && dtype != DL_BF16) || !act_ok(act) || !dim_ok(B) || !dim_ok(in) ||
+  if (!dtype_ok(dtype) || !act_ok(act) || !dim_ok(B) || !dim_ok(in) ||
       !dim_ok(out))
     return 0;
   return vjp_ws(dtype, act, B, in, out);
@@ -329,7 +334,7 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
                   const void* dY, const void* saved, const void* X, const void* W,
                   const void* Wt, void* dX, float* dW, float* db, int dx_act,
                   const void* dx_saved, void* ws, size_t ws_bytes) {
-  if (dtype != DL_F32 && dtype != DL_BF16) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad dtype %d", dtype);
+  if (!dtype_ok(dtype)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad dtype %d", dtype);
   if (!act_ok(act) || !act_ok(dx_act)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad activation");
   if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
     return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: sizes must be in [1, 2^31)");
@@ -842,30 +847,53 @@ int mse_loss_fwd_bwd(void* stream, int64_t B, int64_t C, const float* pred, cons
   return DL_OK;
 }
 
-int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
-  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: n must be positive");
-  if (!src || !dst) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16: src and dst are required");
-  if (overlap(src, n * 4, dst, n * 2)) return fail(DL_ALIASING, "dense_cast_bf16: src overlaps dst");
+static int cast_half(const char* who, const char* label, int half_kind, void* stream, int64_t n,
+                     const float* src, void* dst) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "%s: n must be positive", who);
+  if (!src || !dst) return fail(DL_INVALID_ARGUMENT, "%s: src and dst are required", who);
+  if (overlap(src, n * 4, dst, n * 2)) return fail(DL_ALIASING, "%s: src overlaps dst", who);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("cast_bf16", st, [&] { return dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), st); });
-  if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16");
+  hipError_t e = timed(label, st, [&] {
+    return dl::launch_cast_bf16(n, src, static_cast<dl::bf16_t*>(dst), st, half_kind);
+  });
+  if (e != hipSuccess) return hip_fail(e, who);
   return DL_OK;
+}
+
+static int cast_half_t(const char* who, const char* label, int half_kind, void* stream,
+                       int64_t rows, int64_t cols, const float* src, void* dst, void* dst_t) {
+  if (!dim_ok(rows) || !dim_ok(cols)) return fail(DL_INVALID_ARGUMENT, "%s: sizes must be in [1, 2^31)", who);
+  if (!src || (!dst && !dst_t)) return fail(DL_INVALID_ARGUMENT, "%s: src and an output are required", who);
+  const size_t n = (size_t)rows * cols;
+  if (overlap(src, n * 4, dst, n * 2) || overlap(src, n * 4, dst_t, n * 2) || overlap(dst, n * 2, dst_t, n * 2))
+    return fail(DL_ALIASING, "%s: buffers overlap", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(label, st, [&] {
+    return dl::launch_cast_bf16_t(rows, cols, src, static_cast<dl::bf16_t*>(dst),
+                                  static_cast<dl::bf16_t*>(dst_t), st, half_kind);
+  });
+  if (e != hipSuccess) return hip_fail(e, who);
+  return DL_OK;
+}
+
+int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst) {
+  return cast_half("dense_cast_bf16", "cast_bf16", dl::HK_BF16, stream, n, src, dst);
 }
 
 int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src, void* dst,
                       void* dst_t) {
-  if (!dim_ok(rows) || !dim_ok(cols)) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16_t: sizes must be in [1, 2^31)");
-  if (!src || (!dst && !dst_t)) return fail(DL_INVALID_ARGUMENT, "dense_cast_bf16_t: src and an output are required");
-  const size_t n = (size_t)rows * cols;
-  if (overlap(src, n * 4, dst, n * 2) || overlap(src, n * 4, dst_t, n * 2) || overlap(dst, n * 2, dst_t, n * 2))
-    return fail(DL_ALIASING, "dense_cast_bf16_t: buffers overlap");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed("cast_bf16_t", st, [&] {
-    return dl::launch_cast_bf16_t(rows, cols, src, static_cast<dl::bf16_t*>(dst),
-                                  static_cast<dl::bf16_t*>(dst_t), st);
-  });
-  if (e != hipSuccess) return hip_fail(e, "dense_cast_bf16_t");
-  return DL_OK;
+  return cast_half_t("dense_cast_bf16_t", "cast_bf16_t", dl::HK_BF16, stream, rows, cols, src, dst,
+                     dst_t);
+}
+
+int dense_cast_f16(void* stream, int64_t n, const float* src, void* dst) {
+  return cast_half("dense_cast_f16", "cast_f16", dl::HK_F16, stream, n, src, dst);
+}
+
+int dense_cast_f16_t(void* stream, int64_t rows, int64_t cols, const float* src, void* dst,
+                     void* dst_t) {
+  return cast_half_t("dense_cast_f16_t", "cast_f16_t", dl::HK_F16, stream, rows, cols, src, dst,
+                     dst_t);
 }
 
 // ---- whole MLP step ---------------------------------------------------------

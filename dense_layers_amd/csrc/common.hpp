@@ -14,6 +14,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t bf16_t;  // storage type of one bfloat16
+typedef _Float16 f16_t;   // storage type of one IEEE half
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 enum Act { ACT_IDENTITY = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
 enum Layout { K_MAJOR = 0, MN_MAJOR = 1 };
@@ -39,6 +41,56 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
 }
 
+// ---- half (fp16) <-> f32 ------------------------------------------------------
+// The mixed-precision input convention of the MuNet page ("Configuration"):
+// round to nearest even, saturating at +-65504 instead of overflowing to
+// infinity, NaN preserved.  Clamping first gives the saturation (values past
+// 65504 would otherwise round to 65504 or to infinity); NaN skips the clamp.
+__device__ __forceinline__ float f16_sat(float f) {
+  return __builtin_isnan(f) ? f : fminf(fmaxf(f, -65504.f), 65504.f);
+}
+__device__ __forceinline__ f16_t f32_to_f16(float f) { return (f16_t)f16_sat(f); }
+__device__ __forceinline__ float f16_to_f32(f16_t h) { return (float)h; }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const f2 v = {f16_sat(a), f16_sat(b)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+}
+
+// The two 16-bit operand formats of the matrix-core GEMMs, both moved as
+// 16-bit words: the float32 view of one word, the packing of two floats, and
+// the 32x32x16 MFMA of eight-element fragments.
+enum HalfKind { HK_BF16 = 0, HK_F16 = 1 };
+template <int HK> struct HalfOps;
+template <> struct HalfOps<HK_BF16> {
+  using T = bf16_t;
+  __device__ static __forceinline__ float to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  __device__ static __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float elem(bf16x8 a, int e) { return static_cast<float>(a[e]); }
+  __device__ static __forceinline__ uint16_t one(float x) { return f32_to_bf16(x); }
+};
+template <> struct HalfOps<HK_F16> {
+  using T = f16_t;
+  __device__ static __forceinline__ float to_f32(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) { return pack_f16x2(a, b); }
+  __device__ static __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float elem(bf16x8 a, int e) {
+    return static_cast<float>(__builtin_bit_cast(f16x8, a)[e]);
+  }
+  __device__ static __forceinline__ uint16_t one(float x) {
+    return __builtin_bit_cast(uint16_t, f32_to_f16(x));
+  }
+};
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
@@ -47,6 +99,10 @@ template <> struct Elem<float> {
 template <> struct Elem<bf16_t> {
   __device__ static __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ static __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <> struct Elem<f16_t> {
+  __device__ static __forceinline__ float load(const f16_t* p, int64_t i) { return f16_to_f32(p[i]); }
+  __device__ static __forceinline__ void store(f16_t* p, int64_t i, float v) { p[i] = f32_to_f16(v); }
 };
 
 // ---- activations ------------------------------------------------------------
@@ -143,6 +199,7 @@ struct GemmDesc {
   float* db;
   int splits; int k_per_split;
   float* partial; float* db_partial;
+  int half_kind;  // 16-bit operands: HK_BF16 or HK_F16
 };
 
 // ---- GEMM epilogue through LDS ------------------------------------------------
@@ -182,6 +239,20 @@ template <> struct Store4<bf16_t> {
   }
 };
 
+template <> struct Store4<f16_t> {
+  __device__ static __forceinline__ void vec(f16_t* p, const float v[4]) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    u32x2v x = {pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2v*>(p) = x;
+  }
+  __device__ static __forceinline__ void load_vec(const f16_t* p, float v[4]) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    const u32x2v x = *reinterpret_cast<const u32x2v*>(p);
+    v[0] = HalfOps<HK_F16>::to_f32(x[0] & 0xffffu); v[1] = HalfOps<HK_F16>::to_f32(x[0] >> 16);
+    v[2] = HalfOps<HK_F16>::to_f32(x[1] & 0xffffu); v[3] = HalfOps<HK_F16>::to_f32(x[1] >> 16);
+  }
+};
+
 // Four consecutive elements kept in their storage format (one 16-byte or
 // 8-byte register group) until they are used.
 template <typename T> struct Raw4;
@@ -201,6 +272,18 @@ template <> struct Raw4<bf16_t> {
   }
   __device__ __forceinline__ float get(int e) const {
     return (e & 1) ? __uint_as_float(v[e >> 1] & 0xffff0000u) : __uint_as_float(v[e >> 1] << 16);
+  }
+};
+template <> struct Raw4<f16_t> {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v v = {0u, 0u};
+  __device__ __forceinline__ void load_vec(const f16_t* p) { v = *reinterpret_cast<const u32x2v*>(p); }
+  __device__ __forceinline__ void set(int e, float x) {
+    const uint32_t h = __builtin_bit_cast(uint16_t, f32_to_f16(x));
+    v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0xffffu) | (h << 16)) : ((v[e >> 1] & 0xffff0000u) | h);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    return HalfOps<HK_F16>::to_f32((e & 1) ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
   }
 };
 
@@ -395,10 +478,12 @@ hipError_t launch_splitk_finish_fwd(int M, int N, int splits, const float* parti
 hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols,
                            const void* dY, const void* saved, void* G,
                            hipStream_t s);
+// float32 -> 16-bit copies (half_kind HK_BF16 or HK_F16; the 16-bit words of
+// either are moved as bf16_t)
 hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst,
-                            hipStream_t s);
+                            hipStream_t s, int half_kind = HK_BF16);
 hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16_t* dst,
-                              bf16_t* dst_t, hipStream_t s);
+                              bf16_t* dst_t, hipStream_t s, int half_kind = HK_BF16);
 // dscale (optional, device float32 [1]): dlogits are multiplied by it (the
 // loss scale).
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,

@@ -3,7 +3,8 @@
 //     summed in slice order so the result is bit-reproducible;
 //   * G = dY * act'(saved) for a vjp whose upstream gradient was not already
 //     masked by the previous dX epilogue;
-//   * float32 -> bf16 round-to-nearest-even working copies.
+//   * float32 -> bf16 round-to-nearest-even working copies, or half copies
+//     (nearest-even, saturating at +-65504; the MuNet page, "Configuration").
 #include "common.hpp"
 
 namespace dl {
@@ -77,16 +78,18 @@ act_mask_kernel(int act, int64_t n, const T* __restrict__ dY, const T* __restric
   }
 }
 
+template <int HK>
 __global__ void __launch_bounds__(256)
 cast_bf16_kernel(int64_t n, const float* __restrict__ src, bf16_t* __restrict__ dst) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    dst[i] = f32_to_bf16(src[i]);
+    dst[i] = HalfOps<HK>::one(src[i]);
 }
 
 // src [rows, cols] float32 -> dst = bf16(src) (same layout) and/or
 // dst_t = bf16(src)^T [cols, rows], through a 64 x 64 LDS tile so both the
 // reads and the transposed writes are row-contiguous.
 constexpr int kTT = 64;
+template <int HK>
 __global__ void __launch_bounds__(256)
 cast_bf16_t_kernel(int64_t rows, int64_t cols, const float* __restrict__ src,
                    bf16_t* __restrict__ dst, bf16_t* __restrict__ dst_t) {
@@ -98,7 +101,7 @@ cast_bf16_t_kernel(int64_t rows, int64_t cols, const float* __restrict__ src,
     const int64_t r = r0 + ty + k, c = c0 + tx;
     bf16_t v = 0;
     if (r < rows && c < cols) {
-      v = f32_to_bf16(src[r * cols + c]);
+      v = HalfOps<HK>::one(src[r * cols + c]);
       if (dst != nullptr) dst[r * cols + c] = v;
     }
     tile[ty + k][tx] = v;
@@ -115,6 +118,7 @@ cast_bf16_t_kernel(int64_t rows, int64_t cols, const float* __restrict__ src,
 // The same for rows and cols multiples of 4 with 16-byte aligned float rows
 // and 8-byte aligned bf16 rows: each thread moves 4 consecutive elements at a
 // time (a float4 in, 8 bytes out) on both sides of the transpose.
+template <int HK>
 __global__ void __launch_bounds__(256)
 cast_bf16_t_vec_kernel(int64_t rows, int64_t cols, const float* __restrict__ src,
                        bf16_t* __restrict__ dst, bf16_t* __restrict__ dst_t) {
@@ -128,7 +132,7 @@ cast_bf16_t_vec_kernel(int64_t rows, int64_t cols, const float* __restrict__ src
     u32x2v w = {0u, 0u};
     if (r < rows && c < cols) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + r * cols + c);
-      w = u32x2v{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      w = u32x2v{HalfOps<HK>::pack2(x[0], x[1]), HalfOps<HK>::pack2(x[2], x[3])};
       if (dst != nullptr) *reinterpret_cast<u32x2v*>(dst + r * cols + c) = w;
     }
     *reinterpret_cast<u32x2v*>(&tile[p + k][4 * q]) = w;
@@ -191,6 +195,10 @@ hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols, const
     hipLaunchKernelGGL(act_mask_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
                        static_cast<const float*>(dY), static_cast<const float*>(saved),
                        static_cast<float*>(G));
+  else if (dtype == 2)
+    hipLaunchKernelGGL(act_mask_kernel<f16_t>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
+                       static_cast<const f16_t*>(dY), static_cast<const f16_t*>(saved),
+                       static_cast<f16_t*>(G));
   else
     hipLaunchKernelGGL(act_mask_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, s, act, n,
                        static_cast<const bf16_t*>(dY), static_cast<const bf16_t*>(saved),
@@ -199,20 +207,31 @@ hipError_t launch_act_mask(int dtype, int act, int64_t rows, int64_t cols, const
 }
 
 hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16_t* dst,
-                              bf16_t* dst_t, hipStream_t s) {
+                              bf16_t* dst_t, hipStream_t s, int half_kind) {
   const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
   auto al = [](const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; };
   const bool vec = rows % 4 == 0 && cols % 4 == 0 && al(src, 16) && (dst == nullptr || al(dst, 8)) &&
                    (dst_t == nullptr || al(dst_t, 8));
-  if (vec)
-    hipLaunchKernelGGL(cast_bf16_t_vec_kernel, grid, dim3(256), 0, s, rows, cols, src, dst, dst_t);
+  const bool f16 = half_kind == HK_F16;
+  if (vec && f16)
+    hipLaunchKernelGGL(cast_bf16_t_vec_kernel<HK_F16>, grid, dim3(256), 0, s, rows, cols, src, dst,
+                       dst_t);
+  else if (vec)
+    hipLaunchKernelGGL(cast_bf16_t_vec_kernel<HK_BF16>, grid, dim3(256), 0, s, rows, cols, src, dst,
+                       dst_t);
+  else if (f16)
+    hipLaunchKernelGGL(cast_bf16_t_kernel<HK_F16>, grid, dim3(256), 0, s, rows, cols, src, dst, dst_t);
   else
-    hipLaunchKernelGGL(cast_bf16_t_kernel, grid, dim3(256), 0, s, rows, cols, src, dst, dst_t);
+    hipLaunchKernelGGL(cast_bf16_t_kernel<HK_BF16>, grid, dim3(256), 0, s, rows, cols, src, dst,
+                       dst_t);
   return hipGetLastError();
 }
 
-hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst, hipStream_t s) {
-  hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, s, n, src, dst);
+hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst, hipStream_t s, int half_kind) {
+  if (half_kind == HK_F16)
+    hipLaunchKernelGGL(cast_bf16_kernel<HK_F16>, dim3(grid_for(n)), dim3(256), 0, s, n, src, dst);
+  else
+    hipLaunchKernelGGL(cast_bf16_kernel<HK_BF16>, dim3(grid_for(n)), dim3(256), 0, s, n, src, dst);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// bfloat16-operand GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16,
-// float32 accumulation) with the dense-layer epilogues fused in.
+// 16-bit-operand GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16,
+// or _f16 for IEEE half operands, whose outputs round with saturation at
+// +-65504; float32 accumulation) with the dense-layer epilogues fused in.
 //
 // Same three products as the float32 kernel (forward, dX, dW; the fused
 // LinearAct of the noeira.nn docs, "The design in one page") for operands
@@ -148,7 +149,7 @@ struct TileLoaderBf16 {
   }
 };
 
-template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI, int HK>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   constexpr int NT = WGM * WGN * 64;
@@ -221,7 +222,7 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
         for (int i = 0; i < FM; ++i) {
           float s = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += static_cast<float>(a[i][e]);
+          for (int e = 0; e < 8; ++e) s += HalfOps<HK>::elem(a[i], e);
           dbacc[i] += s;
         }
       }
@@ -229,7 +230,7 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = HalfOps<HK>::mfma(a[i], b[j], acc[i][j]);
     }
   };
 
@@ -328,11 +329,11 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
       }
     }
   }
-  store_tile<bf16_t, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem), d, tm, tn, split,
-                                            out_vec);
+  store_tile<typename HalfOps<HK>::T, BM, BN, WGM, WGN, EPI>(acc, reinterpret_cast<float*>(smem),
+                                                              d, tm, tn, split, out_vec);
 }
 
-template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int WGM, int WGN, int ALAY, int BLAY, int EPI, int HK>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   const int tiles_m = (d.M + BM - 1) / BM;
   const int tiles_n = (d.N + BN - 1) / BN;
@@ -353,21 +354,21 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   else
     out_vec = out_ok(d.C, d.ldc, 8) && (d.Z == nullptr || out_ok(d.Z, d.ldc, 8)) &&
               (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 8));
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, ALAY, BLAY, EPI>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, ALAY, BLAY, EPI, HK>), dim3((unsigned)nwg),
                      dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n, a_vec, b_vec, out_vec);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int HK>
 hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
   if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD, HK>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, HK>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX>(d, s);
+    return launch_tile<BM, BN, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX, HK>(d, s);
   if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_tile<BM, BN, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW>(d, s);
+    return launch_tile<BM, BN, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, HK>(d, s);
   return hipErrorInvalidValue;
 }
 
@@ -381,7 +382,8 @@ hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
     const hipError_t e = launch_gemm_bf16_dma(d, tile, s);
     if (e != hipErrorNotSupported) return e;
   }
-  return dispatch_layout<128, 128, 2, 2>(d, s);
+  return d.half_kind == HK_F16 ? dispatch_layout<128, 128, 2, 2, HK_F16>(d, s)
+                                : dispatch_layout<128, 128, 2, 2, HK_BF16>(d, s);
 }
 
 }  // namespace dl

@@ -1,8 +1,11 @@
-// bfloat16-operand GEMM for large, aligned problems: operand tiles go from
-// HBM straight into LDS (global_load_lds_dwordx4, no staging registers), the
-// matrix cores read them back as MFMA fragments (v_mfma_f32_32x32x16_bf16,
-// float32 accumulation), and the dense-layer epilogues (bias + activation,
-// act' masking, float32 weight-gradient slices) are applied on the way out.
+// 16-bit-operand GEMM for large, aligned problems: operand tiles go from HBM
+// straight into LDS (global_load_lds_dwordx4, no staging registers), the
+// matrix cores read them back as MFMA fragments (v_mfma_f32_32x32x16_bf16, or
+// _f16 for IEEE half operands; float32 accumulation), and the dense-layer
+// epilogues (bias + activation, act' masking, float32 weight-gradient slices)
+// are applied on the way out.  bf16 and half take the same path: only the
+// MFMA, the output rounding (half saturates at +-65504) and the reading of
+// saved activations differ (HalfOps).
 //
 // The products are the three of the fused LinearAct (noeira.nn docs, "The
 // design in one page"): forward Z = X W^T + b, dX = (dY o act') W and
@@ -214,9 +217,10 @@ __device__ __forceinline__ void load_mask16(u32x4 (&m)[2], const bf16_t* __restr
       if (p.col + c < N) m[c >> 3][(c >> 1) & 3] |= (uint32_t)q[c] << (16 * (c & 1));
   }
 }
+template <int HK>
 __device__ __forceinline__ float mask_at(const u32x4 (&m)[2], int c) {
   const uint32_t w = m[c >> 3][(c >> 1) & 3];
-  return __uint_as_float((c & 1) ? (w & 0xffff0000u) : (w << 16));
+  return HalfOps<HK>::to_f32((c & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
 // Orders this wave's LDS accesses (no other wave touches its region).
@@ -228,7 +232,7 @@ __device__ __forceinline__ void wave_lds_order() {
 
 // Writes a lane's 16 values (columns 16 h .. 16 h + 15 of block column j, row
 // r of the region) in storage format.
-template <typename TO, int WN>
+template <typename TO, int WN, int HK>
 __device__ __forceinline__ void region_put(char* region, int r, int j, int h, const float (&v)[16]) {
   constexpr int ES = sizeof(TO), PPR = WN * ES / 16;  // 16-byte pieces per row
   char* row = region + r * (WN * ES);
@@ -236,9 +240,9 @@ __device__ __forceinline__ void region_put(char* region, int r, int j, int h, co
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int q = 4 * j + 2 * h + k;
-      const u32x4 x = {pack_bf16x2(v[8 * k], v[8 * k + 1]), pack_bf16x2(v[8 * k + 2], v[8 * k + 3]),
-                       pack_bf16x2(v[8 * k + 4], v[8 * k + 5]),
-                       pack_bf16x2(v[8 * k + 6], v[8 * k + 7])};
+      using H = HalfOps<HK>;
+      const u32x4 x = {H::pack2(v[8 * k], v[8 * k + 1]), H::pack2(v[8 * k + 2], v[8 * k + 3]),
+                       H::pack2(v[8 * k + 4], v[8 * k + 5]), H::pack2(v[8 * k + 6], v[8 * k + 7])};
       *reinterpret_cast<u32x4*>(row + ((q ^ (r % PPR)) * 16)) = x;
     }
   } else {
@@ -292,7 +296,7 @@ constexpr int block_rows_per_round(int cap, int fm) {
 // split `split`'s partial).  `region` is this wave's LDS area of kRegion
 // bytes; the wave's rows go through it in rounds of IR block rows.
 template <int BM, int BN, int WGM, int WGN, int EPI, int ACT, bool ZOUT, int FM, int FN,
-          int kRegion>
+          int kRegion, int HK>
 __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], const GemmDesc& d,
                                                int tm, int tn, int split, int wm, int wn, int lane,
                                                bool vec, char* region) {
@@ -371,12 +375,12 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
             z[c] = v[c] + bias[j][c];
             v[c] = act_apply(ACT, z[c]);
           }
-          if constexpr (kZ) region_put<TO, WN>(region + kOutBytes, ii * 32 + l32, j, h, z);
+          if constexpr (kZ) region_put<TO, WN, HK>(region + kOutBytes, ii * 32 + l32, j, h, z);
         } else if constexpr (kMasked) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c) v[c] *= act_deriv(ACT, mask_at(mk[ii * FN + j], c));
+          for (int c = 0; c < 16; ++c) v[c] *= act_deriv(ACT, mask_at<HK>(mk[ii * FN + j], c));
         }
-        region_put<TO, WN>(region, ii * 32 + l32, j, h, v);
+        region_put<TO, WN, HK>(region, ii * 32 + l32, j, h, v);
       }
     if constexpr (kMasked) {
       if (i0 + IR < FM) load_masks(i0 + IR);
@@ -413,7 +417,7 @@ struct Item {
 // in LDS regions of its own, runs while they land.  Otherwise the grid holds
 // one workgroup per item and the epilogue reuses the stage buffers.
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI,
-          bool PERSIST>
+          bool PERSIST, int HK>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
   constexpr int NT = WGM * WGN * 64;
@@ -520,7 +524,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
       for (int i = 0; i < FM; ++i) {
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += static_cast<float>(a[i][e]);
+        for (int e = 0; e < 8; ++e) sum += HalfOps<HK>::elem(a[i], e);
         dbacc[i] += sum;
       }
     }
@@ -528,7 +532,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = HalfOps<HK>::mfma(bb[j], a[i], acc[i][j]);
   };
   auto stage_buf = [&](int g) { return smem + (g % STAGES) * kStageBytes; };
 
@@ -635,7 +639,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
     }
     swap_halves(acc);
 #define DL_EPILOGUE(A, Z)                                                                 \
-  store_epilogue<BM, BN, WGM, WGN, EPI, A, Z, FM, FN, kRegion>(                           \
+  store_epilogue<BM, BN, WGM, WGN, EPI, A, Z, FM, FN, kRegion, HK>(                       \
       acc, d, cur.tm, cur.tn, cur.split, wm, wn, lane, vec, region)
     if (EPI == EPI_FWD && d.Z != nullptr) {
       if constexpr (EPI != EPI_FWD) {
@@ -662,7 +666,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
 }
 
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int ALAY, int BLAY, int EPI,
-          bool PERSIST>
+          bool PERSIST, int HK>
 hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
   auto aligned = [](const void* p, int64_t ld) {
     return ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (ld % 8 == 0);
@@ -693,22 +697,22 @@ hipError_t launch_dma(const GemmDesc& d, hipStream_t s) {
     out_vec = out_ok(d.C, d.ldc, 16) && d.ldc % 8 == 0 &&
               (d.Z == nullptr || out_ok(d.Z, d.ldc, 16)) &&
               (d.mask_src == nullptr || out_ok(d.mask_src, d.ldc, 16));
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI, PERSIST>),
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, BK, STAGES, WGM, WGN, ALAY, BLAY, EPI, PERSIST, HK>),
                      dim3((unsigned)nwg), dim3(WGM * WGN * 64), 0, s, d, tiles_m, tiles_n,
                      out_vec);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PERSIST>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PERSIST, int HK>
 hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
   if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD, PERSIST>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD, PERSIST, HK>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX, PERSIST>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX, PERSIST, HK>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, PERSIST>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, PERSIST, HK>(d, s);
   if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, PERSIST>(d, s);
+    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, PERSIST, HK>(d, s);
   return hipErrorNotSupported;
 }
 
@@ -720,7 +724,8 @@ hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
 // CU the one-workgroup-per-item form with four stages measured faster.
 constexpr int kPersistItems = 4;
 
-hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
+template <int HK>
+hipError_t launch_tile(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
     case 0: {
       int dev = 0, cus = 0;
@@ -728,15 +733,19 @@ hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
       if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
       const int64_t items = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256) * d.splits;
-      if (items >= (int64_t)kPersistItems * cus) return dma_layout<256, 256, 32, 3, 2, 4, true>(d, s);
-      return dma_layout<256, 256, 32, 4, 2, 4, false>(d, s);
+      if (items >= (int64_t)kPersistItems * cus) return dma_layout<256, 256, 32, 3, 2, 4, true, HK>(d, s);
+      return dma_layout<256, 256, 32, 4, 2, 4, false, HK>(d, s);
     }
-    case 1: return dma_layout<128, 128, 64, 2, 2, 2, false>(d, s);
+    case 1: return dma_layout<128, 128, 64, 2, 2, 2, false, HK>(d, s);
     // weight gradients (both operands M/N-major): four waves of 128x128 halve
     // the transposing LDS reads per MFMA against eight waves of 128x64
-    case 2: return dma_layout<256, 256, 64, 2, 2, 2, false>(d, s);
+    case 2: return dma_layout<256, 256, 64, 2, 2, 2, false, HK>(d, s);
     default: return hipErrorNotSupported;
   }
+}
+
+hipError_t launch_gemm_bf16_dma(const GemmDesc& d, int tile, hipStream_t s) {
+  return d.half_kind == HK_F16 ? launch_tile<HK_F16>(d, tile, s) : launch_tile<HK_BF16>(d, tile, s);
 }
 
 }  // namespace dl

@@ -51,8 +51,11 @@ extern "C" {
 /* ---- enums and status codes --------------------------------------------- */
 
 enum dl_dtype {
-  DL_F32 = 0,  /* float32 operands, float32 accumulation */
-  DL_BF16 = 1  /* bfloat16 operands (RNE copies), float32 accumulation */
+  DL_F32 = 0,   /* float32 operands, float32 accumulation */
+  DL_BF16 = 1,  /* bfloat16 operands (RNE copies), float32 accumulation */
+  DL_F16 = 2    /* IEEE half operands (RNE, saturating at +-65504, NaN kept;
+                 * the mixed precision of the MuNet page, "Configuration"),
+                 * float32 accumulation */
 };
 
 enum dl_act {
@@ -114,8 +117,10 @@ int dl_profile_end(int max, float* ms, char* names);
  * LinearAct; bias and activation folded into the GEMM epilogue).
  *
  *   dtype   DL_F32: X, W, Y, Z are float32.  DL_BF16: X, W, Y, Z are
- *           bfloat16 (W is the bf16 working copy, see dense_cast_bf16);
- *           accumulation is float32 in both cases.
+ *           bfloat16 (W is the bf16 working copy, see dense_cast_bf16).
+ *           DL_F16: X, W, Y, Z are IEEE half (see dense_cast_f16); Y and Z
+ *           round with saturation at +-65504.  Accumulation is float32 in
+ *           every case.
  *   act     enum dl_act.
  *   B, in, out  > 0.
  *   X       device [B, in]
@@ -410,6 +415,17 @@ int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst);
  */
 int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src,
                       void* dst, void* dst_t);
+
+/*
+ * dense_cast_f16, dense_cast_f16_t -- the same two copies in IEEE half:
+ * round to nearest even, saturating at +-65504 (a value past the largest
+ * half, or an infinity, becomes +-65504), NaN kept (the mixed-precision
+ * convention of the MuNet page, "Configuration").  Arguments and errors as
+ * dense_cast_bf16 / dense_cast_bf16_t, with half outputs.
+ */
+int dense_cast_f16(void* stream, int64_t n, const float* src, void* dst);
+int dense_cast_f16_t(void* stream, int64_t rows, int64_t cols, const float* src,
+                     void* dst, void* dst_t);
 
 /* ---- one MLP training step ------------------------------------------------ */
 

@@ -152,10 +152,15 @@ def generate(w: Workload, batch: Optional[int] = None) -> Inputs:
 
 
 def random_matrix(seed: int, shape, scale: float = 1.0,
-                  bf16_exact: bool = False) -> np.ndarray:
-    """Standalone float32 N(0, scale^2) matrix for kernel-level cases."""
+                  bf16_exact: bool = False, f16_exact: bool = False) -> np.ndarray:
+    """Standalone float32 N(0, scale^2) matrix for kernel-level cases.
+    bf16_exact / f16_exact make every value representable in that 16-bit
+    format (bits cleared, or NumPy's half cast), so such inputs reach both
+    sides exactly."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    if f16_exact:
+        return a.astype(np.float16).astype(np.float32)
     return _to_bf16_exact(a) if bf16_exact else a
 
 

@@ -6,6 +6,7 @@ import torch
 F32_TOL = 1e-4     # float32 results: normwise max |gpu - ref| / max |ref|
 LOSS_TOL = 1e-5    # loss: |gpu - ref| / |ref|
 BF16_TOL = 2e-2    # bf16-operand / float32-accumulate results
+F16_TOL = 5e-3     # half-operand / float32-accumulate results (about 10 half ulps)
 
 
 def device():
