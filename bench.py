@@ -171,14 +171,16 @@ class MLPBench:
 
 
 class TmlpBench:
-    """Transformer-MLP block shapes, bf16 operands: fwd + vjp of
-    1024 -> 4096 (GELU tanh) -> 1024 with float32 master weights."""
+    """Transformer-MLP block shapes, 16-bit operands (bf16, or half for the
+    mixed-precision variant): fwd + vjp of 1024 -> 4096 (GELU tanh) -> 1024
+    with float32 master weights."""
 
     def __init__(self, dl, w, dev):
         import torch
         self.dl, self.w = dl, w
         inp = si.generate(w)
-        bf = torch.bfloat16
+        bf = torch.float16 if w.dtype == "f16" else torch.bfloat16
+        self.cast_t = dl.dense_cast_f16_t if w.dtype == "f16" else dl.dense_cast_bf16_t
         T, d, f = w.batch, w.dims[0], w.dims[1]
         self.X = torch.from_numpy(inp.X).to(dev).to(bf)
         self.dY = torch.from_numpy(inp.dY).to(dev).to(bf)
@@ -192,14 +194,15 @@ class TmlpBench:
         self.dX = torch.empty(T, d, dtype=bf, device=dev)
         self.dW = [torch.empty_like(a) for a in self.W]
         self.db = [torch.empty_like(a) for a in self.b]
-        n = max(dl.dense_act_vjp_workspace_size(dl.DL_BF16, 0, T, f, d),
-                dl.dense_act_vjp_workspace_size(dl.DL_BF16, 0, T, d, f), 1)
+        code = dl.DL_F16 if w.dtype == "f16" else dl.DL_BF16
+        n = max(dl.dense_act_vjp_workspace_size(code, 0, T, f, d),
+                dl.dense_act_vjp_workspace_size(code, 0, T, d, f), 1)
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def step(self):
         dl = self.dl
-        for l in range(2):  # bf16 working copies of the fp32 masters, and transposes
-            dl.dense_cast_bf16_t(self.W[l], self.Wb[l], self.Wbt[l])
+        for l in range(2):  # 16-bit working copies of the fp32 masters, and transposes
+            self.cast_t(self.W[l], self.Wb[l], self.Wbt[l])
         dl.dense_act_fwd(self.X, self.Wb[0], self.b[0], dl.ACT_GELU_TANH, Y=self.H, Z=self.Z)
         dl.dense_act_fwd(self.H, self.Wb[1], self.b[1], dl.ACT_IDENTITY, Y=self.Y)
         # vjp of layer 2 writes dZ1 = (dY W2) * gelu'(Z1) over Z1 in place
@@ -217,7 +220,7 @@ class TmlpBench:
         name, _ = _split(label)
         if name in ("fwd_gemm", "dw_gemm", "dx_gemm"):
             return "flop", 2 * T * d * f
-        if name == "cast_bf16_t":
+        if name in ("cast_bf16_t", "cast_f16_t"):
             return "byte", 8 * d * f
         return None
 
@@ -346,14 +349,18 @@ EXTRA_WORKLOADS = {
                              "f32", si.ADAMW, has_loss=False),
     "mse": si.Workload("mse", 7, 16384, [4096], [], "kaiming", "zero", "f32", None,
                        has_loss=False),
+    "tmlp_f16": si.Workload("tmlp_f16", 8, 32768, [1024, 4096, 1024],
+                            [si.ACT_GELU_TANH, si.ACT_IDENTITY], "normal002", "zero", "f16", None,
+                            has_loss=False, has_dy=True),
 }
 WORKLOADS = {**si.WORKLOADS, **EXTRA_WORKLOADS}
 
 BENCHES = {"mlp_small": MLPBench, "mlp_adamw": MLPBench, "mlp_wide": MLPBench,
            "tmlp_bf16": TmlpBench, "head_xent": HeadBench, "opt_fused": OptBench,
-           "mse": MseBench}
+           "mse": MseBench, "tmlp_f16": TmlpBench}
 DEFAULTS = {"mlp_small": (200, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
-            "tmlp_bf16": (20, 3), "head_xent": (5, 1), "opt_fused": (50, 5), "mse": (50, 5)}
+            "tmlp_bf16": (20, 3), "head_xent": (5, 1), "opt_fused": (50, 5), "mse": (50, 5),
+            "tmlp_f16": (20, 3)}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -469,7 +476,7 @@ def main():
         bench.graph = None  # the per-launch timing runs the same step eagerly
     stages = profile_stages(dl, bench, max(1, min(args.prof_steps, steps)))
     dom = max(stages, key=lambda x: x["ms"])
-    peak = PEAK_BF16_MFMA if w.dtype == "bf16" else PEAK_FP32_MFMA
+    peak = PEAK_BF16_MFMA if w.dtype in ("bf16", "f16") else PEAK_FP32_MFMA  # half: same rate
     traffic = stored_traffic(w.name, dom["stage"])
     if "tflops" in dom:
         roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
@@ -498,7 +505,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "dims": w.dims,
                    "optimizer": None if w.optim is None else w.optim.kind,

@@ -51,7 +51,7 @@ class Workload:
     acts: List[int]             # one per layer
     init: str                   # "kaiming" or "normal002"
     bias: str                   # "zero" or "uniform001"
-    dtype: str                  # "f32" or "bf16"
+    dtype: str                  # "f32", "bf16" or "f16"
     optim: Optional[Optim]      # None for fwd+vjp-only workloads
     steps: int = 1
     has_loss: bool = True       # softmax-xent closes the step
@@ -148,6 +148,10 @@ def generate(w: Workload, batch: Optional[int] = None) -> Inputs:
         X = _to_bf16_exact(X)
         if dY is not None:
             dY = _to_bf16_exact(dY)
+    elif w.dtype == "f16":
+        X = X.astype(np.float16).astype(np.float32)
+        if dY is not None:
+            dY = dY.astype(np.float16).astype(np.float32)
     return Inputs(X, labels, Ws, bs, dY)
 
 
