@@ -112,6 +112,9 @@ _c = {
     "mlp_train_step": _sig("mlp_train_step", _i32,
                            [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,
                             ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
+    "mlp_train_step_mse": _sig("mlp_train_step_mse", _i32,
+                               [_vp, _i64, _i32, ctypes.POINTER(DLLayer), _vp, _vp,
+                                ctypes.POINTER(DLOpt), _vp, _vp, _sz]),
     "mlp_train_step_workspace_size": _sig("mlp_train_step_workspace_size", _sz,
                                           [_i64, _i32, ctypes.POINTER(DLLayer)]),
     "adam_step": _sig("adam_step", _i32,
@@ -138,7 +141,7 @@ EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
            "dense_cast_bf16", "dense_cast_bf16_t", "dense_cast_f16", "dense_cast_f16_t",
-           "mlp_train_step",
+           "mlp_train_step", "mlp_train_step_mse",
            "mlp_train_step_workspace_size", "adam_step", "ema_update", "clip_grad_norm",
            "clip_grad_norm_workspace_size", "optimizer_step", "optimizer_step_workspace_size",
            "mse_loss_fwd_bwd", "mse_loss_workspace_size", "dl_lr_at",
@@ -602,6 +605,28 @@ def mlp_train_step(mlp: MLP, X: torch.Tensor, labels: torch.Tensor, kind: int = 
     _check(_c["mlp_train_step"](_stream(X), mlp.batch, mlp.L, mlp.table, _ptr(X),
                                 _ptr(labels), ctypes.byref(opt), _ptr(mlp.loss), _ptr(mlp.ws),
                                 0 if mlp.ws is None else mlp.ws.numel()))
+    return mlp.loss
+
+
+def mlp_train_step_mse(mlp: MLP, X: torch.Tensor, targets: torch.Tensor, kind: int = OPT_SGD,
+                       lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                       eps: float = 1e-8, weight_decay: float = 0.0,
+                       step: Optional[int] = None, device_step: bool = False,
+                       max_grad_norm: float = 0.0, ema_decay: float = 0.0, schedule=None,
+                       scaler=None, grad_norm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mlp_train_step with the mean squared error against float32 targets
+    [B, C] as the loss."""
+    _dev(X, "X", torch.float32, (mlp.batch, mlp.W[0].shape[1]))
+    _dev(targets, "targets", torch.float32, (mlp.batch, mlp.W[-1].shape[0]))
+    if step is None:
+        step = mlp.step_count + 1
+    mlp.step_count = step
+    opt = _opt_struct(kind, lr, beta1, beta2, eps, weight_decay, step,
+                      mlp.step_dev if device_step else None, max_grad_norm, ema_decay, schedule,
+                      scaler, grad_norm)
+    _check(_c["mlp_train_step_mse"](_stream(X), mlp.batch, mlp.L, mlp.table, _ptr(X),
+                                    _ptr(targets), ctypes.byref(opt), _ptr(mlp.loss),
+                                    _ptr(mlp.ws), 0 if mlp.ws is None else mlp.ws.numel()))
     return mlp.loss
 
 

@@ -910,14 +910,14 @@ int dense_cast_f16_t(void* stream, int64_t rows, int64_t cols, const float* src,
 
 // Whether the last layer runs as the fused narrow head (last Linear +
 // softmax-xent + its vjp in one kernel).
-static bool mlp_fused_head(int32_t L, const dl_layer_t* layers) {
-  return dl::head_xent_fits(layers[L - 1].in, layers[L - 1].out);
+static bool mlp_fused_head(int32_t L, const dl_layer_t* layers, bool xent) {
+  return xent && dl::head_xent_fits(layers[L - 1].in, layers[L - 1].out);
 }
 
 // Gradient slices a layer's dW / db leave for the optimizer to add up: the
 // split-K slices of its weight-gradient GEMM, or the fused head's slices.
-static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l) {
-  if (l == L - 1 && mlp_fused_head(L, layers)) return dl::head_xent_slices(B);
+static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
+  if (l == L - 1 && mlp_fused_head(L, layers, xent)) return dl::head_xent_slices(B);
   return plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B).splits;
 }
 
@@ -960,19 +960,22 @@ static int64_t mlp_stat_parts(int32_t L, const dl_layer_t* layers) {
   return dl::stat_grid(units);
 }
 
-static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t* y_off,
-                         size_t* rl_off, size_t* part_off, size_t* fwd_off, size_t* g_off,
-                         size_t* g_bytes, size_t* ctl_off) {
+// `xent`: the loss is softmax cross-entropy (a narrow last layer then runs as
+// the fused head); otherwise MSE, whose partial sums take the per-row loss
+// region.
+static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, bool xent,
+                         size_t* y_off, size_t* rl_off, size_t* part_off, size_t* fwd_off,
+                         size_t* g_off, size_t* g_bytes, size_t* ctl_off) {
   size_t off = 0;
   for (int l = 0; l < L; ++l) {
     y_off[l] = off;
     off += align_up((size_t)B * layers[l].out * 4);
   }
   *rl_off = off;
-  off += align_up((size_t)B * 4);
+  off += std::max(align_up((size_t)B * 4), xent ? 0 : align_up((size_t)dl::mse_grid(B * layers[L - 1].out) * 8));
   for (int l = 0; l < L; ++l) {
     part_off[l] = off;
-    const int64_t S = mlp_slices(B, L, layers, l);
+    const int64_t S = mlp_slices(B, L, layers, l, xent);
     if (S > 1)
       off += align_up((size_t)S * layers[l].out * layers[l].in * 4) +
              align_up((size_t)S * layers[l].out * 4);
@@ -986,7 +989,7 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, size_t*
   }
   off += fwd;
   // gradient buffers of the paired layers (two alternate when several pair)
-  const int last_gemm = mlp_fused_head(L, layers) ? L - 2 : L - 1;
+  const int last_gemm = mlp_fused_head(L, layers, xent) ? L - 2 : L - 1;
   int pairs = 0;
   size_t gb = 0;
   for (int l = 1; l <= last_gemm; ++l)
@@ -1006,16 +1009,28 @@ size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers, const dl_layer
   for (int l = 0; l < n_layers; ++l)
     if (!dim_ok(layers[l].in) || !dim_ok(layers[l].out)) return 0;
   size_t y_off[16], rl, part[16], fwd, g_off, g_bytes, ctl_off;
-  return mlp_layout(B, n_layers, layers, y_off, &rl, part, &fwd, &g_off, &g_bytes, &ctl_off);
+  // the larger of the cross-entropy and the MSE layouts, so one workspace
+  // serves both steps
+  const size_t a = mlp_layout(B, n_layers, layers, true, y_off, &rl, part, &fwd, &g_off, &g_bytes,
+                              &ctl_off);
+  const size_t b = mlp_layout(B, n_layers, layers, false, y_off, &rl, part, &fwd, &g_off, &g_bytes,
+                              &ctl_off);
+  return std::max(a, b);
 }
 
-int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
-                   const float* X, const int32_t* labels, const dl_opt_t* opt, float* loss,
-                   void* ws, size_t ws_bytes) {
+}  // extern "C"
+
+// The whole step for either loss: softmax cross-entropy against `labels`, or
+// (labels null) the mean squared error against `targets`.
+static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
+                    const float* X, const int32_t* labels, const float* targets,
+                    const dl_opt_t* opt, float* loss, void* ws, size_t ws_bytes) {
+  const bool xent = labels != nullptr;
   if (!dim_ok(B)) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: B must be in [1, 2^31)");
   if (n_layers < 1 || n_layers > 16 || !layers)
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: n_layers must be in [1, 16]");
-  if (!X || !labels || !opt || !loss) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: X, labels, opt and loss are required");
+  if (!X || (!labels && !targets) || !opt || !loss)
+    return fail(DL_INVALID_ARGUMENT, "mlp_train_step: X, labels (targets), opt and loss are required");
   const bool any_ema = layers && n_layers >= 1 && layers[0].eW != nullptr;
   if (int st = check_opt(opt, "mlp_train_step", any_ema)) return st;
   const bool adam = opt->kind != DL_OPT_SGD;
@@ -1044,9 +1059,12 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // activation of its own (its derivative would need the overwritten output).
   if (layers[n_layers - 1].act != DL_ACT_IDENTITY)
     return fail(DL_UNSUPPORTED, "mlp_train_step: the last layer must be the identity");
+  if (!xent && overlap(targets, (size_t)B * layers[n_layers - 1].out * 4, X,
+                       (size_t)B * layers[0].in * 4))
+    return fail(DL_ALIASING, "mlp_train_step: targets overlap X");
   size_t y_off[16], rl_off, part_off[16], fwd_off, g_off, g_bytes, ctl_off;
-  const size_t need = mlp_layout(B, n_layers, layers, y_off, &rl_off, part_off, &fwd_off, &g_off,
-                                 &g_bytes, &ctl_off);
+  const size_t need = mlp_layout(B, n_layers, layers, xent, y_off, &rl_off, part_off, &fwd_off,
+                                 &g_off, &g_bytes, &ctl_off);
   if (!ws || ws_bytes < need)
     return fail(DL_WORKSPACE_TOO_SMALL, "mlp_train_step: workspace %zu bytes, need %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -1073,7 +1091,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   // With a narrow last layer the logits never reach HBM: one kernel runs its
   // forward, the softmax-xent and its vjp (dX written over Y[L-2], dW / db as
   // slices for the optimizer).
-  const bool fused = mlp_fused_head(L, layers);
+  const bool fused = mlp_fused_head(L, layers, xent);
   const int last_gemm = fused ? L - 2 : L - 1;
   // forward
   for (int l = 0; l <= last_gemm; ++l) {
@@ -1117,12 +1135,20 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
                                   row_loss, dWp, dbp, s, dscale);
     });
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (head)");
-  } else {
+  } else if (xent) {
     // loss + dlogits (in place over the logits)
     e = timed("xent", s, [&] {
       return dl::launch_xent(B, C, Y[L - 1], labels, row_loss, Y[L - 1], loss, s, dscale);
     });
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (xent)");
+  } else {
+    // MSE + dpred (in place over the predictions); its partial sums use the
+    // per-row loss region
+    e = timed("mse", s, [&] {
+      return dl::launch_mse(B * C, Y[L - 1], targets, Y[L - 1], reinterpret_cast<double*>(row_loss),
+                            loss, s, dscale);
+    });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (mse)");
   }
   // backward; G holds the current layer's output gradient
   float* gbuf[2] = {reinterpret_cast<float*>(base + g_off),
@@ -1160,7 +1186,7 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   int64_t blocks = 0, units = 0;
   for (int l = 0; l < L; ++l) {
     const dl_layer_t& ly = layers[l];
-    const int64_t S = mlp_slices(B, L, layers, l);
+    const int64_t S = mlp_slices(B, L, layers, l, xent);
     char* pb = base + part_off[l];
     float* ws_[2] = {ly.W, ly.b};
     float* gs_[2] = {ly.dW, ly.db};
@@ -1203,6 +1229,22 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* 
   e = timed(kOptNames[opt->kind], s, [&] { return dl::launch_opt_multi(segs, opt->kind, oc, s); });
   if (e != hipSuccess) return hip_fail(e, "mlp_train_step (optimizer)");
   return DL_OK;
+}
+
+extern "C" {
+
+int mlp_train_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
+                   const float* X, const int32_t* labels, const dl_opt_t* opt, float* loss,
+                   void* ws, size_t ws_bytes) {
+  if (!labels) return fail(DL_INVALID_ARGUMENT, "mlp_train_step: labels are required");
+  return mlp_step(stream, B, n_layers, layers, X, labels, nullptr, opt, loss, ws, ws_bytes);
+}
+
+int mlp_train_step_mse(void* stream, int64_t B, int32_t n_layers, const dl_layer_t* layers,
+                       const float* X, const float* targets, const dl_opt_t* opt, float* loss,
+                       void* ws, size_t ws_bytes) {
+  if (!targets) return fail(DL_INVALID_ARGUMENT, "mlp_train_step_mse: targets are required");
+  return mlp_step(stream, B, n_layers, layers, X, nullptr, targets, opt, loss, ws, ws_bytes);
 }
 
 }  // extern "C"

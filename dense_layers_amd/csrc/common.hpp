@@ -642,7 +642,9 @@ hipError_t launch_scale_by(const OptSegs& segs, const float* coef, hipStream_t s
 
 // ---- mean squared error --------------------------------------------------------
 int mse_grid(int64_t n);
+// dscale (optional, device float32 [1]): dpred is multiplied by it (the loss
+// scale).
 hipError_t launch_mse(int64_t n, const float* pred, const float* target, float* dpred,
-                      double* part, float* loss, hipStream_t s);
+                      double* part, float* loss, hipStream_t s, const float* dscale = nullptr);
 
 }  // namespace dl

@@ -39,7 +39,8 @@ __device__ __forceinline__ void mse_fetch(const float* pred, const float* target
 
 __global__ void __launch_bounds__(kOptBlock)
 mse_kernel(int64_t n, const float* pred, const float* __restrict__ target, float* dpred,
-           double* __restrict__ part, float two_over_n, int vec) {
+           double* __restrict__ part, float two_over_n, int vec, const float* dscale) {
+  if (dscale != nullptr) two_over_n *= *dscale;  // loss scale
   double acc = 0.0;
   const int64_t units = (n + kStatUnit - 1) / kStatUnit;
   // units whose every thread's 16 elements exist (all but a partial last one)
@@ -101,12 +102,12 @@ int mse_grid(int64_t n) {
 }
 
 hipError_t launch_mse(int64_t n, const float* pred, const float* target, float* dpred,
-                      double* part, float* loss, hipStream_t s) {
+                      double* part, float* loss, hipStream_t s, const float* dscale) {
   const int grid = mse_grid(n);
   const int vec = ((reinterpret_cast<uintptr_t>(pred) | reinterpret_cast<uintptr_t>(target) |
                     reinterpret_cast<uintptr_t>(dpred)) & 15) == 0;
   hipLaunchKernelGGL(mse_kernel, dim3((unsigned)grid), dim3(kOptBlock), 0, s, n, pred, target,
-                     dpred, part, (float)(2.0 / (double)n), vec);
+                     dpred, part, (float)(2.0 / (double)n), vec, dscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mse_finish_kernel, dim3(1), dim3(kOptBlock), 0, s, part, grid, n, loss);

@@ -475,6 +475,23 @@ int mlp_train_step(void* stream, int64_t B, int32_t n_layers,
                    const int32_t* labels, const dl_opt_t* opt, float* loss,
                    void* ws, size_t ws_bytes);
 
+/*
+ * mlp_train_step_mse -- the same step with the mean squared error against
+ * float32 targets as the loss (MuNet page, "Python training": the compiled
+ * step trains an MLP with mse_loss): loss = (1/(B C)) sum (y - t)^2 over the
+ * last layer's output y [B, C], dy = 2 (y - t) / (B C) (times the loss scale
+ * when a scaler is set).  Every other argument, option and rule as
+ * mlp_train_step; the last layer always runs as a GEMM (the fused narrow
+ * head is a cross-entropy kernel).
+ *   targets  device float32 [B, layers[n-1].out]; must not overlap X
+ */
+int mlp_train_step_mse(void* stream, int64_t B, int32_t n_layers,
+                       const dl_layer_t* layers, const float* X,
+                       const float* targets, const dl_opt_t* opt, float* loss,
+                       void* ws, size_t ws_bytes);
+
+/* Workspace for mlp_train_step and mlp_train_step_mse (the larger of the two
+ * needs). */
 size_t mlp_train_step_workspace_size(int64_t B, int32_t n_layers,
                                      const dl_layer_t* layers);
 

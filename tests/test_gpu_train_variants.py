@@ -527,3 +527,66 @@ def test_graph_replay_with_clip_scaler_ema_schedule(dl):
                 assert torch.equal(a, b), k
         assert torch.equal(sc_g.scale, sc_e.scale)
         assert graphed.step_dev.item() == eager.step_dev.item()
+
+
+# ------------------------------------------------------------------ MLP step with MSE
+
+from tests.test_gpu_parity import _adamw_spread  # noqa: E402
+
+MSE_VARIANTS = {
+    "sgd": dict(opt=_Opt("sgd", lr=0.05)),
+    "sgd_clip_ema_scaled": dict(opt=_Opt("sgd", lr=0.05, max_grad_norm=0.1, ema_decay=0.6),
+                                scale=2.0 ** 8, dev=True),
+    "adamw": dict(opt=_Opt("adamw", lr=1e-3, wd=0.01)),
+}
+
+
+@pytest.mark.parametrize("work", sorted(VARIANT_WORKLOADS))
+@pytest.mark.parametrize("variant", sorted(MSE_VARIANTS))
+def test_mlp_step_mse_matches_oracle(dl, work, variant):
+    v = MSE_VARIANTS[variant]
+    w = VARIANT_WORKLOADS[work]
+    opt = v["opt"]
+    inp = si.generate(w)
+    T = si.random_matrix(990, (w.batch, w.dims[-1]))
+    adam = opt.kind != "sgd"
+    ema = opt.ema_decay is not None
+    mlp = _mlp(dl, inp, w, adam, ema)
+    Xd, Td = to_dev(inp.X), to_dev(T)
+    st = O.MLPState(inp.W, inp.b)
+    if ema:
+        st.enable_ema()
+    for t in range(1, 4):
+        _load_state(mlp, st)
+        if ema:
+            for l in range(mlp.L):
+                mlp.eW[l].copy_(torch.from_numpy(st.eW[l].astype(np.float32)))
+                mlp.eb[l].copy_(torch.from_numpy(st.eb[l].astype(np.float32)))
+        mlp.step_dev.fill_(t - 1)
+        scaler = osc = None
+        if "scale" in v:
+            scaler = dl.LossScaler(device(), init_scale=v["scale"], growth_interval=1000)
+            osc = O.LossScaler(scale=v["scale"], growth_interval=1000)
+        masks, _ = _adopted_masks(_gpu_relu_masks(dl, inp.X, st.W, st.b, w.acts), st, inp.X,
+                                  w.acts)
+        before = _copy_state(st)
+        ref = O.mlp_train_step(st, inp.X, None, w.acts, opt, relu_masks=masks, scaler=osc,
+                               targets=T)
+        loss = float(dl.mlp_train_step_mse(
+            mlp, Xd, Td, _kind(dl, opt.kind), lr=opt.lr, weight_decay=opt.weight_decay, step=t,
+            device_step=v.get("dev", False), max_grad_norm=opt.max_grad_norm,
+            ema_decay=opt.ema_decay or 0.0, scaler=scaler).item())
+        assert abs(loss - ref["loss"]) <= LOSS_TOL * abs(ref["loss"])
+        for l in range(mlp.L):
+            assert_close(to_np(mlp.dW[l]), ref["dW"][l], F32_TOL, f"step {t} dW{l}")
+            assert_close(to_np(mlp.db[l]), ref["db"][l], F32_TOL, f"step {t} db{l}")
+            if adam:
+                dgW, dgb = _grad_rounding_bound(ref["G"][l], ref["h"][l])
+                bw, _, _ = _adamw_spread(before.W[l], ref["dW"][l], dgW, before.mW[l],
+                                         before.vW[l], opt, t)
+                _assert_close_band(to_np(mlp.W[l]), st.W[l], bw, F32_TOL, f"step {t} W{l}")
+            else:
+                assert_close(to_np(mlp.W[l]), st.W[l], F32_TOL, f"step {t} W{l}")
+                assert_close(to_np(mlp.b[l]), st.b[l], F32_TOL, f"step {t} b{l}")
+            if ema:
+                assert_close(to_np(mlp.eW[l]), st.eW[l], F32_TOL, f"step {t} eW{l}")
