@@ -100,6 +100,28 @@ def round_f16_sat(a) -> np.ndarray:
     return np.where(np.isinf(h), np.copysign(F16_MAX, h), h)
 
 
+def f16_safe_scale(a) -> float:
+    """Power-of-two scale of a gradient operand before half conversion (the
+    MuNet page, "Configuration", precision mixed_safe: per-tensor
+    power-of-two rescaling of the gradient operands of half matmuls, exact,
+    so cotangents far below the half normal range keep their relative
+    accuracy).  With m the largest finite |a|: s = 2^(14 - floor(log2 m)),
+    which puts m * s in [2^14, 2^15) (one binade below the half maximum);
+    s = 1 when m is 0 or there is no finite value."""
+    a = np.asarray(a, dtype=np.float64)
+    fin = np.abs(a[np.isfinite(a)])
+    m = float(fin.max()) if fin.size else 0.0
+    if m == 0.0:
+        return 1.0
+    e = math.floor(math.log2(m))
+    # log2 of a value just below a power of two can round up to it
+    if 2.0 ** e > m:
+        e -= 1
+    elif 2.0 ** (e + 1) <= m:
+        e += 1
+    return 2.0 ** (14 - e)
+
+
 # ---------------------------------------------------------------------------
 # Activations (noeira.nn docs, "The design in one page": LinearAct fuses
 # MatMul + Bias + Activation; the derivative is the act' of the vjp)

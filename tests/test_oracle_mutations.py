@@ -229,3 +229,9 @@ def test_f16_truncation_caught(monkeypatch):
 
     monkeypatch.setattr(O, "round_f16_sat", truncate)
     _expect_pin_failure(P.test_round_f16_sat_matches_torch_cast_in_range)
+
+
+def test_safe_scale_off_by_one_binade_caught(monkeypatch):
+    real = D.f16_safe_scale
+    monkeypatch.setattr(O, "f16_safe_scale", lambda a: 2.0 * real(a))
+    _expect_pin_failure(P.test_f16_safe_scale_hand_values)

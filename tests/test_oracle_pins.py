@@ -70,6 +70,35 @@ def test_round_f16_sat_matches_torch_cast_in_range():
     assert np.array_equal(O.round_f16_sat(x), ref)
 
 
+def test_f16_safe_scale_hand_values():
+    assert O.f16_safe_scale(np.array([1.0, -0.5])) == 2.0 ** 14
+    assert O.f16_safe_scale(np.array([3.0])) == 2.0 ** 13
+    assert O.f16_safe_scale(np.array([-2.0 ** 15])) == 0.5
+    assert O.f16_safe_scale(np.array([1e-7, np.nan, np.inf])) == 2.0 ** 38
+    assert O.f16_safe_scale(np.zeros(5)) == 1.0
+    assert O.f16_safe_scale(np.array([np.nan])) == 1.0
+    # just below a power of two stays in the lower binade
+    x = np.nextafter(1.0, 0.0)
+    assert O.f16_safe_scale(np.array([x])) == 2.0 ** 15
+
+
+def test_f16_safe_scale_places_max_in_top_binade_and_keeps_relative_accuracy():
+    rng = np.random.default_rng(7)
+    for mag in (1e-9, 1e-7, 3e-5, 1.0, 700.0):
+        a = (rng.standard_normal(4000) * mag).astype(np.float32).astype(np.float64)
+        s = O.f16_safe_scale(a)
+        assert math.log2(s) == int(math.log2(s))  # a power of two
+        m = np.max(np.abs(a)) * s
+        assert 2.0 ** 14 <= m < 2.0 ** 15
+        back = O.round_f16_sat(a * s) / s
+        big = np.abs(a) > np.max(np.abs(a)) * 2.0 ** -10  # inside the half normal range after scaling
+        assert np.max(np.abs(back - a)[big] / np.abs(a)[big]) <= 2.0 ** -11
+    # without the scale, cotangents of 1e-7 lose their relative accuracy
+    a = rng.standard_normal(4000) * 1e-7
+    plain = O.round_f16_sat(a)
+    assert np.median(np.abs(plain - a) / np.abs(a)) > 0.05
+
+
 def test_round_f32_matches_cast():
     x = np.array([1.0 + 2.0 ** -30, 0.1, -7.3e-9])
     assert np.array_equal(O.round_f32(x), x.astype(np.float32).astype(np.float64))
