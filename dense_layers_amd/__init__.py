@@ -97,6 +97,13 @@ _c = {
     "dense_act_vjp": _sig("dense_act_vjp", _i32,
                           [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _i32, _vp, _vp, _sz]),
+    "dense_act_vjp_scaled": _sig("dense_act_vjp_scaled", _i32,
+                                 [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "dense_cast_f16_scaled": _sig("dense_cast_f16_scaled", _i32,
+                                  [_vp, _i64, _vp, _vp, _vp, _vp, _sz]),
+    "dense_cast_f16_scaled_workspace_size": _sig("dense_cast_f16_scaled_workspace_size", _sz,
+                                                 [_i64]),
     "dense_act_vjp_workspace_size": _sig("dense_act_vjp_workspace_size", _sz,
                                          [_i32, _i32, _i64, _i64, _i64]),
     "softmax_xent_fwd_bwd": _sig("softmax_xent_fwd_bwd", _i32,
@@ -138,6 +145,7 @@ _c = {
 }
 
 EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
+           "dense_act_vjp_scaled", "dense_cast_f16_scaled", "dense_cast_f16_scaled_workspace_size",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
            "dense_cast_bf16", "dense_cast_bf16_t", "dense_cast_f16", "dense_cast_f16_t",
@@ -251,11 +259,14 @@ def dense_act_vjp(dY: torch.Tensor, saved: Optional[torch.Tensor], X: Optional[t
                   need_dw: bool = True, dX: Optional[torch.Tensor] = None,
                   dW: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
                   dx_act=ACT_IDENTITY, dx_saved: Optional[torch.Tensor] = None,
-                  ws: Optional[torch.Tensor] = None, Wt: Optional[torch.Tensor] = None):
+                  ws: Optional[torch.Tensor] = None, Wt: Optional[torch.Tensor] = None,
+                  dy_scale: Optional[torch.Tensor] = None):
     """G = dY * act'(saved); returns (dX or None, dW or None, db or None).
 
     With dx_act != identity the returned dX is dX * dx_act'(dx_saved).  Wt,
-    when given, is W transposed ([in, out]); dX then reads it instead of W."""
+    when given, is W transposed ([in, out]); dX then reads it instead of W.
+    dy_scale (device float32 [1]): dY holds the cotangent times that scale
+    (see dense_cast_f16_scaled); dW and db are divided by it, dX keeps it."""
     _dev(dY, "dY")
     dt = dY.dtype
     B, n_out = dY.shape
@@ -286,10 +297,14 @@ def dense_act_vjp(dY: torch.Tensor, saved: Optional[torch.Tensor], X: Optional[t
     need = dense_act_vjp_workspace_size(code, act, B, n_in, n_out)
     if ws is None or ws.numel() < need:
         ws = _workspace(need, dY.device)
-    _check(_c["dense_act_vjp"](_stream(dY), code, _act(act), B, n_in, n_out, _ptr(dY),
-                               _ptr(saved), _ptr(X), _ptr(W), _ptr(Wt), _ptr(dX), _ptr(dW), _ptr(db),
-                               _act(dx_act), _ptr(dx_saved), _ptr(ws),
-                               0 if ws is None else ws.numel()))
+    args = (_stream(dY), code, _act(act), B, n_in, n_out, _ptr(dY), _ptr(saved), _ptr(X), _ptr(W),
+            _ptr(Wt), _ptr(dX), _ptr(dW), _ptr(db), _act(dx_act), _ptr(dx_saved), _ptr(ws),
+            0 if ws is None else ws.numel())
+    if dy_scale is not None:
+        _dev(dy_scale, "dy_scale", torch.float32, (1,))
+        _check(_c["dense_act_vjp_scaled"](*args, _ptr(dy_scale)))
+    else:
+        _check(_c["dense_act_vjp"](*args))
     return dX, dW, db
 
 
@@ -531,6 +546,24 @@ def dense_cast_f16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
 
 def dense_cast_f16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):
     return _cast("dense_cast_f16", torch.float16, src, dst)
+
+
+def dense_cast_f16_scaled(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
+                          scale: Optional[torch.Tensor] = None):
+    """Half copy of a gradient operand times a power-of-two scale chosen from
+    its largest finite magnitude; returns (dst, scale) with scale a device
+    float32 [1] (pass it as dense_act_vjp's dy_scale)."""
+    _dev(src, "src", torch.float32)
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float16, device=src.device)
+    _dev(dst, "dst", torch.float16, tuple(src.shape))
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=src.device)
+    n = src.numel()
+    ws = _workspace(int(_c["dense_cast_f16_scaled_workspace_size"](n)), src.device)
+    _check(_c["dense_cast_f16_scaled"](_stream(src), n, _ptr(src), _ptr(dst), _ptr(scale),
+                                       _ptr(ws), 0 if ws is None else ws.numel()))
+    return dst, scale
 
 
 # ---------------------------------------------------------------- MLP step

@@ -209,9 +209,11 @@ dl::GemmDesc dw_desc(int dtype, int64_t B, int64_t in, int64_t out, const void* 
 }
 
 hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
-                   float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true) {
+                   float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true,
+                   const float* out_scale = nullptr) {
   const Plan p = plan_gemm(dtype, dl::EPI_DW, out, in, B);
-  const dl::GemmDesc d = dw_desc(dtype, B, in, out, G, X, dW, db, partial_ws, p);
+  dl::GemmDesc d = dw_desc(dtype, B, in, out, G, X, dW, db, partial_ws, p);
+  d.out_scale = out_scale;
   hipError_t e = timed("dw_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
   if (e != hipSuccess || p.splits == 1 || !reduce) return e;
   return timed("splitk_reduce", s, [&] {
@@ -240,8 +242,10 @@ dl::GemmDesc dx_desc(int64_t B, int64_t in, int64_t out, const void* G, const vo
 }
 
 hipError_t dx_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* W,
-                   const void* Wt, void* dX, int mask_act, const void* mask_src, hipStream_t s) {
-  const dl::GemmDesc d = dx_desc(B, in, out, G, W, Wt, dX, mask_act, mask_src);
+                   const void* Wt, void* dX, int mask_act, const void* mask_src, hipStream_t s,
+                   const float* out_scale = nullptr) {
+  dl::GemmDesc d = dx_desc(B, in, out, G, W, Wt, dX, mask_act, mask_src);
+  d.out_scale = out_scale;
   const Plan p = plan_gemm(dtype, dl::EPI_DX, B, in, out);
   return timed("dx_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
 }
@@ -330,10 +334,10 @@ size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in, i
   return vjp_ws(dtype, act, B, in, out);
 }
 
-int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
-                  const void* dY, const void* saved, const void* X, const void* W,
-                  const void* Wt, void* dX, float* dW, float* db, int dx_act,
-                  const void* dx_saved, void* ws, size_t ws_bytes) {
+static int vjp_impl(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
+                    const void* dY, const void* saved, const void* X, const void* W,
+                    const void* Wt, void* dX, float* dW, float* db, int dx_act,
+                    const void* dx_saved, void* ws, size_t ws_bytes, const float* dy_scale) {
   if (!dtype_ok(dtype)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad dtype %d", dtype);
   if (!act_ok(act) || !act_ok(dx_act)) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp: bad activation");
   if (!dim_ok(B) || !dim_ok(in) || !dim_ok(out))
@@ -379,14 +383,38 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64
     wsp += align_up((size_t)B * out * es);
   }
   if (dW) {
-    e = dw_gemm(dtype, B, in, out, G, X, dW, db, wsp, s);
+    e = dw_gemm(dtype, B, in, out, G, X, dW, db, wsp, s, true, dy_scale);
     if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dW)");
   }
   if (dX) {
-    e = dx_gemm(dtype, B, in, out, G, W, Wt, dX, dx_act, dx_saved, s);
+    e = dx_gemm(dtype, B, in, out, G, W, Wt, dX, dx_act, dx_saved, s, dy_scale);
     if (e != hipSuccess) return hip_fail(e, "dense_act_vjp (dX)");
   }
   return DL_OK;
+}
+
+int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
+                  const void* dY, const void* saved, const void* X, const void* W,
+                  const void* Wt, void* dX, float* dW, float* db, int dx_act,
+                  const void* dx_saved, void* ws, size_t ws_bytes) {
+  return vjp_impl(stream, dtype, act, B, in, out, dY, saved, X, W, Wt, dX, dW, db, dx_act,
+                  dx_saved, ws, ws_bytes, nullptr);
+}
+
+int dense_act_vjp_scaled(void* stream, int dtype, int act, int64_t B, int64_t in, int64_t out,
+                         const void* dY, const void* saved, const void* X, const void* W,
+                         const void* Wt, void* dX, float* dW, float* db, int dx_act,
+                         const void* dx_saved, void* ws, size_t ws_bytes,
+                         const float* dy_scale) {
+  if (!dy_scale) return fail(DL_INVALID_ARGUMENT, "dense_act_vjp_scaled: dy_scale is required");
+  const size_t nY = (size_t)B * out * esize(dtype);
+  if (dim_ok(B) && dim_ok(out) && (overlap(dy_scale, 4, dX, (size_t)B * in * esize(dtype)) ||
+                                   overlap(dy_scale, 4, dW, (size_t)out * in * 4) ||
+                                   overlap(dy_scale, 4, db, (size_t)out * 4) ||
+                                   overlap(dy_scale, 4, ws, ws_bytes) || overlap(dy_scale, 4, dY, nY)))
+    return fail(DL_ALIASING, "dense_act_vjp_scaled: dy_scale overlaps an output or the workspace");
+  return vjp_impl(stream, dtype, act, B, in, out, dY, saved, X, W, Wt, dX, dW, db, dx_act,
+                  dx_saved, ws, ws_bytes, dy_scale);
 }
 
 size_t softmax_xent_workspace_size(int64_t B, int64_t C) {
@@ -884,6 +912,32 @@ int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src
                       void* dst_t) {
   return cast_half_t("dense_cast_bf16_t", "cast_bf16_t", dl::HK_BF16, stream, rows, cols, src, dst,
                      dst_t);
+}
+
+size_t dense_cast_f16_scaled_workspace_size(int64_t n) {
+  if (n <= 0) return 0;
+  return align_up((size_t)dl::safe_scale_parts(n) * 4);
+}
+
+int dense_cast_f16_scaled(void* stream, int64_t n, const float* src, void* dst, float* scale,
+                          void* ws, size_t ws_bytes) {
+  if (n <= 0) return fail(DL_INVALID_ARGUMENT, "dense_cast_f16_scaled: n must be positive");
+  if (!src || !dst || !scale) return fail(DL_INVALID_ARGUMENT, "dense_cast_f16_scaled: src, dst and scale are required");
+  const size_t need = dense_cast_f16_scaled_workspace_size(n);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "dense_cast_f16_scaled: workspace %zu bytes, need %zu", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) % 4) != 0)
+    return fail(DL_INVALID_ARGUMENT, "dense_cast_f16_scaled: workspace must be 4-byte aligned");
+  if (overlap(src, n * 4, dst, n * 2) || overlap(scale, 4, src, n * 4) || overlap(scale, 4, dst, n * 2) ||
+      overlap(ws, need, src, n * 4) || overlap(ws, need, dst, n * 2) || overlap(ws, need, scale, 4))
+    return fail(DL_ALIASING, "dense_cast_f16_scaled: buffers overlap");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("cast_f16_scaled", st, [&] {
+    return dl::launch_cast_f16_scaled(n, src, static_cast<dl::bf16_t*>(dst), scale,
+                                      static_cast<float*>(ws), st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "dense_cast_f16_scaled");
+  return DL_OK;
 }
 
 int dense_cast_f16(void* stream, int64_t n, const float* src, void* dst) {

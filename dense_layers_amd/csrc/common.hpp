@@ -200,7 +200,17 @@ struct GemmDesc {
   int splits; int k_per_split;
   float* partial; float* db_partial;
   int half_kind;  // 16-bit operands: HK_BF16 or HK_F16
+  // weight-gradient products (dW, db) whose gradient operand was handed over
+  // times s (device float32 [1], a power of two): the float32 results are
+  // divided by s before they are stored.  dX products keep the scale (dX is
+  // the next layer's gradient operand).  Null: no scale.
+  const float* out_scale;
 };
+
+// 1 / s of a descriptor's gradient-operand scale (1 without one).
+__device__ __forceinline__ float unscale_factor(const GemmDesc& d) {
+  return d.out_scale != nullptr ? 1.0f / d.out_scale[0] : 1.0f;
+}
 
 // ---- GEMM epilogue through LDS ------------------------------------------------
 // The 32x32 MFMA result leaves each lane one column of 16 rows, so direct
@@ -373,6 +383,7 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
   if (EPI == EPI_FWD && d.bias != nullptr)
     for (int e = 0; e < nv; ++e) bias[e] = d.bias[col + e];
   const bool masked = EPI == EPI_DX && d.mask_act != ACT_IDENTITY;
+  const float osc = EPI == EPI_DW ? unscale_factor(d) : 1.0f;
 
   Raw4<TO> ms[EPI == EPI_DX ? RPT : 1];
   if (masked) {
@@ -437,6 +448,8 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
           if (colfull) Store4<TO>::vec(out + o, v);
           else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
         } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= osc;
           if (colfull) Store4<TO>::vec(out + o, v);
           else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
         }
@@ -486,6 +499,11 @@ hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16
                               bf16_t* dst_t, hipStream_t s, int half_kind = HK_BF16);
 // dscale (optional, device float32 [1]): dlogits are multiplied by it (the
 // loss scale).
+// dst = half(src s) with the power-of-two scale s chosen from the largest
+// finite |src| (written to scale[0]); part holds safe_scale_parts(n) floats.
+int safe_scale_parts(int64_t n);
+hipError_t launch_cast_f16_scaled(int64_t n, const float* src, bf16_t* dst, float* scale,
+                                  float* part, hipStream_t s);
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s, const float* dscale = nullptr);

@@ -150,6 +150,73 @@ cast_bf16_t_vec_kernel(int64_t rows, int64_t cols, const float* __restrict__ src
   }
 }
 
+// Half copy with a power-of-two scale (mixed_safe): the largest finite |x|
+// is found (per-workgroup maxima, then one workgroup), s = 2^(14 - floor(log2
+// m)) (m = 0: s = 1; exponent capped at 127) puts it in [2^14, 2^15), and
+// dst = half(x s) with saturation; x s is exact in float32.  The maxima are
+// order-independent, so the result is deterministic.
+constexpr int kAmaxUnit = 4096;  // elements per workgroup per round, 4 float4 per thread
+constexpr int kAmaxBlocks = 2048;
+
+__global__ void __launch_bounds__(256)
+absmax_kernel(int64_t n, const float* __restrict__ x, float* __restrict__ part, int vec) {
+  __shared__ float red[4];
+  float m = 0.f;
+  const int64_t units = (n + kAmaxUnit - 1) / kAmaxUnit;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t base = u * kAmaxUnit + (int64_t)threadIdx.x * 4;
+    if (vec && base + 3 * 1024 + 3 < n) {
+      f32x4 a[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) a[it] = *reinterpret_cast<const f32x4*>(x + base + it * 1024);
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (__builtin_isfinite(a[it][e])) m = fmaxf(m, fabsf(a[it][e]));
+    } else {
+      for (int it = 0; it < 4; ++it)
+        for (int e = 0; e < 4; ++e) {
+          const int64_t i = base + it * 1024 + e;
+          if (i < n && __builtin_isfinite(x[i])) m = fmaxf(m, fabsf(x[i]));
+        }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(256)
+safe_scale_kernel(const float* __restrict__ part, int parts, float* __restrict__ scale) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < parts; i += 256) m = fmaxf(m, part[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = 1.f;
+  if (m > 0.f) {
+    int e;
+    frexpf(m, &e);  // m = f 2^e, f in [0.5, 1): floor(log2 m) = e - 1
+    s = ldexpf(1.f, min(15 - e, 127));
+  }
+  scale[0] = s;
+}
+
+__global__ void __launch_bounds__(256)
+cast_f16_scaled_kernel(int64_t n, const float* __restrict__ src, const float* __restrict__ scale,
+                       bf16_t* __restrict__ dst) {
+  const float s = scale[0];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = HalfOps<HK_F16>::one(src[i] * s);
+}
+
 unsigned grid_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -158,6 +225,25 @@ unsigned grid_for(int64_t n) {
 }
 
 }  // namespace
+
+int safe_scale_parts(int64_t n) {
+  const int64_t units = (n + kAmaxUnit - 1) / kAmaxUnit;
+  return (int)(units < kAmaxBlocks ? units : kAmaxBlocks);
+}
+
+hipError_t launch_cast_f16_scaled(int64_t n, const float* src, bf16_t* dst, float* scale,
+                                  float* part, hipStream_t s) {
+  const int parts = safe_scale_parts(n);
+  const int vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)parts), dim3(256), 0, s, n, src, part, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(safe_scale_kernel, dim3(1), dim3(256), 0, s, part, parts, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cast_f16_scaled_kernel, dim3(grid_for(n)), dim3(256), 0, s, n, src, scale, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_splitk_reduce(int M, int N, int splits, const float* partial,
                                 const float* db_partial, float* C, int64_t ldc, float* db,

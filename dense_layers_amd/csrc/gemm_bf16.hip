@@ -321,7 +321,7 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
     const int row_base = tm * BM + wm * WM;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      float v = (dbacc[i] + __shfl_xor(dbacc[i], 32)) * unscale_factor(d);
       const int row = row_base + i * 32 + l32;
       if (h == 0 && row < M) {
         if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;

@@ -348,6 +348,7 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
   }
 
   TO* __restrict__ zout = static_cast<TO*>(d.Z);
+  const float osc = EPI == EPI_DW ? unscale_factor(d) : 1.0f;
   // saved activations of the current round's blocks (ii, j) at ii FN + j
   u32x4 mk[kMasked ? IR * FN : 1][2];
   auto load_masks = [&](int i0) {
@@ -368,6 +369,10 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
         float v[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) v[c] = acc[i0 + ii][j][col_reg(c)];
+        if constexpr (EPI == EPI_DW) {
+#pragma unroll
+          for (int c = 0; c < 16; ++c) v[c] *= osc;
+        }
         if constexpr (EPI == EPI_FWD) {
           float z[16];
 #pragma unroll
@@ -629,7 +634,7 @@ gemm_bf16_dma_kernel(GemmDesc d, int tiles_m, int tiles_n, int out_vec) {
       const int row_base = cur.tm * BM + wm * WM;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+        const float v = (dbacc[i] + __shfl_xor(dbacc[i], 32)) * unscale_factor(d);
         const int row = row_base + i * 32 + (lane & 31);
         if (h == 0 && row < M) {
           if (d.splits > 1) d.db_partial[(int64_t)cur.split * M + row] = v;

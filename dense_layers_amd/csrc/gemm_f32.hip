@@ -298,7 +298,7 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
     const int row_base = tm * BM + wm * WM;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float v = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      float v = (dbacc[i] + __shfl_xor(dbacc[i], 32)) * unscale_factor(d);
       const int row = row_base + i * 32 + l32;
       if (h == 0 && row < M) {
         if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;

@@ -171,6 +171,27 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in,
                   float* dW, float* db, int dx_act, const void* dx_saved,
                   void* ws, size_t ws_bytes);
 
+/*
+ * dense_act_vjp_scaled -- dense_act_vjp for a gradient operand handed over
+ * times a scale s (the mixed_safe precision of the MuNet page,
+ * "Configuration": per-tensor power-of-two rescaling of the gradient
+ * operand of half matmuls, so cotangents far below the half normal range
+ * keep their relative accuracy).  dY holds the cotangent times s
+ * (dense_cast_f16_scaled writes both).  dW and db are divided by s in
+ * float32 inside the GEMM epilogues, so they come out unscaled (exact when s
+ * is a power of two).  dX keeps the scale: it is the previous layer's
+ * gradient operand, whose own vjp takes it with the same dy_scale (divided
+ * there, a half dX of the unscaled size would fall back below the half
+ * normal range).
+ *   dy_scale  device float32 [1] holding s; must not overlap an output or
+ *             the workspace.  Every other argument as dense_act_vjp.
+ */
+int dense_act_vjp_scaled(void* stream, int dtype, int act, int64_t B, int64_t in,
+                         int64_t out, const void* dY, const void* saved,
+                         const void* X, const void* W, const void* Wt, void* dX,
+                         float* dW, float* db, int dx_act, const void* dx_saved,
+                         void* ws, size_t ws_bytes, const float* dy_scale);
+
 size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in,
                                     int64_t out);
 
@@ -424,6 +445,22 @@ int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src
  * dense_cast_bf16 / dense_cast_bf16_t, with half outputs.
  */
 int dense_cast_f16(void* stream, int64_t n, const float* src, void* dst);
+
+/*
+ * dense_cast_f16_scaled -- the half copy of a gradient operand with a
+ * power-of-two scale (mixed_safe): with m the largest finite |src|,
+ * s = 2^(14 - floor(log2 m)) puts it in [2^14, 2^15) (s = 1 for m = 0; the
+ * exponent is capped at 127); writes *scale = s and dst = half(src s)
+ * (nearest even, saturating, NaN kept; src s is exact in float32).  Pass dst
+ * and scale to dense_act_vjp_scaled.  Deterministic (the maximum does not
+ * depend on the order of reduction).
+ *   n > 0; src device float32 [n]; dst device half [n]; scale device
+ *   float32 [1] output; ws, ws_bytes at least
+ *   dense_cast_f16_scaled_workspace_size(n); no overlaps.
+ */
+int dense_cast_f16_scaled(void* stream, int64_t n, const float* src, void* dst,
+                          float* scale, void* ws, size_t ws_bytes);
+size_t dense_cast_f16_scaled_workspace_size(int64_t n);
 int dense_cast_f16_t(void* stream, int64_t rows, int64_t cols, const float* src,
                      void* dst, void* dst_t);
 

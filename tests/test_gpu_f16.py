@@ -154,3 +154,79 @@ def test_cast_f16_bit_exact(dl, shape):
     for g, r, m in ((got, ref, nan), (got_t, ref.T, nan.T), (got1, ref.reshape(-1), nan.reshape(-1))):
         assert np.array_equal(g[~m], r[~m])
         assert np.isnan(g[m].view(np.float16)).all()
+
+
+# ------------------------------------------------------------------ mixed_safe
+
+@pytest.mark.parametrize("mag", [1e-9, 1e-7, 3e-5, 1.0, 700.0])
+def test_cast_f16_scaled_bit_exact(dl, mag):
+    a = si.random_matrix(970, (257, 129), scale=mag)
+    a.reshape(-1)[5] = np.nan
+    a.reshape(-1)[9] = np.inf
+    h, sc = dl.dense_cast_f16_scaled(to_dev(a))
+    s = O.f16_safe_scale(a)
+    assert sc.item() == s
+    ref = O.round_f16_sat(a * s).astype(np.float16).view(np.uint16)
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    nan = np.isnan(a)
+    assert np.array_equal(got[~nan], ref[~nan]) and np.isnan(got[nan].view(np.float16)).all()
+
+
+VJP_SCALED_SHAPES = [(77, 130, 90), (1024, 1024, 512), (1024, 1000, 200), (4104, 256, 4120)]
+
+
+@pytest.mark.parametrize("shape", VJP_SCALED_SHAPES)
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_vjp_scaled_keeps_tiny_cotangents(dl, shape, act):
+    """Cotangents of 1e-7 (below the half normal range): through the scaled
+    half copy every product keeps half accuracy against the exact vjp; the
+    plain half copy loses it."""
+    B, n_in, n_out = shape
+    X, W, Z = _m(980, (B, n_in)), _m(981, (n_out, n_in), 0.05), _m(982, (B, n_out))
+    dY = si.random_matrix(983, (B, n_out), scale=1e-7)
+    Xd, Wd, Zd = to_dev(X, H), to_dev(W, H), to_dev(Z, H)
+    dYh, sc = dl.dense_cast_f16_scaled(to_dev(dY))
+    dX, dW, db = dl.dense_act_vjp(dYh, Zd, Xd, Wd, act, dy_scale=sc)
+    exact = O.dense_act_vjp(dY, Z, X, W, act)
+    s = O.f16_safe_scale(dY)
+    assert sc.item() == s
+    # dX keeps the scale (the next gradient operand); dW, db come out unscaled
+    assert_close(to_np(dX) / s, exact[0], F16_TOL, "dX / s")
+    assert_close(to_np(dW), exact[1], F16_TOL, "dW")
+    assert_close(to_np(db), exact[2], F16_TOL, "db")
+    # the oracle of the scaled operand itself, to the same bar
+    rdX, rdW, rdb = O.dense_act_vjp(O.round_f16_sat(dY * s) / s, Z, X, W, act)
+    assert_close(to_np(dW), rdW, F16_TOL, "dW (scaled operand)")
+    plain = dl.dense_cast_f16(to_dev(dY))
+    pX, _, _ = dl.dense_act_vjp(plain, Zd, Xd, Wd, act)
+    from tests.gpu_util import normwise
+    assert normwise(to_np(pX), exact[0]) > 0.05
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_vjp_power_of_two_scale_is_exact(dl, dtype):
+    """dY times 2^12 with dy_scale = 2^12: dW and db bit for bit the unscaled
+    ones, dX bit for bit 2^12 times the unscaled dX (where that is a normal
+    number of the dtype), in every dtype (float32
+    accumulation, the division before the float32 store, a power of two).
+    Half takes the identity activation and a dY with no half subnormal: a
+    masked gradient or a cotangent in half's subnormal range unscaled but not
+    scaled is where the scaled form is the more accurate one."""
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": H}[dtype]
+    act = O.ACT_IDENTITY if dtype == "f16" else O.ACT_GELU_TANH
+    for B, n_in, n_out in ((1024, 1000, 200), (1024, 1024, 512)):
+        X, W, Z = _m(990, (B, n_in)), _m(991, (n_out, n_in), 0.05), _m(992, (B, n_out))
+        dY = _m(993, (B, n_out), 0.01)
+        if dtype == "f16":  # every dY a normal half in both runs
+            dY = np.where(np.abs(dY) < 2.0 ** -14, np.copysign(2.0 ** -14, dY), dY).astype(np.float32)
+        Xd, Wd, Zd = to_dev(X, tdt), to_dev(W, tdt), to_dev(Z, tdt)
+        a = dl.dense_act_vjp(to_dev(dY, tdt), Zd, Xd, Wd, act)
+        sc = torch.full((1,), 4096.0, device=device())
+        b = dl.dense_act_vjp(to_dev(dY * 4096.0, tdt), Zd, Xd, Wd, act, dy_scale=sc)
+        # (where the unscaled half dX is subnormal, or rounded up from there
+        # to the smallest normal, the scaled one is the more precise;
+        # elsewhere the two agree bit for bit)
+        normal = a[0].float().abs() > 2.0 ** -14
+        assert torch.equal(b[0][normal], (a[0] * 4096.0)[normal])
+        assert normal.float().mean() > 0.95
+        assert torch.equal(b[1], a[1]) and torch.equal(b[2], a[2])
