@@ -34,7 +34,7 @@ PEAK_HBM = 8000.0        # GB/s
 
 
 KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
-                  "head.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip", "api.cpp"]
+                  "head.hip", "tail.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip", "api.cpp"]
 
 
 def kernel_source_hash() -> str:
@@ -80,7 +80,8 @@ class MLPBench:
         launch order: the backward runs from the last GEMM layer down, each
         layer as dwdx_gemm, or dw_gemm then (above layer 0) dx_gemm."""
         labels = getattr(self, "labels", ())
-        last = self.w.n_layers - (2 if "head_xent#0" in labels else 1)
+        tail = "mlp_tail#0" in labels
+        last = self.w.n_layers - (2 if tail or "head_xent#0" in labels else 1)
         out, cur, fwd = {}, last, -1
         for lab in labels:
             name, _ = _split(lab)
@@ -91,10 +92,14 @@ class MLPBench:
             elif name == "dwdx_gemm":
                 out[lab] = cur
                 cur -= 1
+            elif name == "dwdw_gemm":  # the tail's hidden layer and the first layer
+                out[lab] = cur
+                cur -= 2
             elif name == "dw_gemm":
                 out[lab] = cur
-                if cur == 0:
+                if cur == 0 or tail:  # no dX launch follows (first layer, or the tail's)
                     cur -= 1
+                tail = False
             elif name == "dx_gemm":
                 out[lab] = cur
                 cur -= 1
@@ -158,6 +163,15 @@ class MLPBench:
             l = layer[label]
         elif name == "xent":
             return "byte", 8 * B * w.dims[-1] + 8 * B
+        elif name == "mlp_tail":
+            # the last hidden layer's forward (and dX when it has an input
+            # layer), and the head's forward, dW and dX
+            l = L - 2
+            mnk = B * w.dims[l] * w.dims[l + 1]
+            return "flop", 2 * mnk * (2 if l > 0 else 1) + 3 * 2 * B * w.dims[-2] * w.dims[-1]
+        elif name == "dwdw_gemm":   # weight gradients of layers l and l - 1
+            l = layer[label]
+            return "flop", 2 * B * (w.dims[l] * w.dims[l + 1] + w.dims[l - 1] * w.dims[l])
         elif name == "head_xent":
             # last Linear forward, its dW and (for more than one layer) its dX
             return "flop", (3 if L > 1 else 2) * 2 * B * w.dims[-2] * w.dims[-1]
@@ -424,6 +438,9 @@ def main():
     ap.add_argument("--prof-steps", type=int, default=20)
     ap.add_argument("--graph", action="store_true",
                     help="MLP workloads: time replays of the step captured as a stream graph")
+    ap.add_argument("--mlp-fusion", type=int, default=2, choices=(1, 2),
+                    help="MLP workloads: 2 fuses the last hidden layer into the head kernel, "
+                         "1 fuses the head alone")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
@@ -438,6 +455,7 @@ def main():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    dl.set_mlp_fusion(args.mlp_fusion)
     w = WORKLOADS[args.config]
     steps, warmup = DEFAULTS[args.config]
     steps = args.steps if args.steps is not None else steps
@@ -510,7 +528,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "dims": w.dims,
                    "optimizer": None if w.optim is None else w.optim.kind,
                    "gemm_flops_per_step": bench.flops(),
-                   "graph_replay": bool(args.graph)},
+                   "graph_replay": bool(args.graph), "mlp_fusion": args.mlp_fusion},
         "roofline": roofline,
         "stages": stages,
         "kernel_source_hash": kernel_source_hash(),

@@ -142,6 +142,7 @@ _c = {
     "dl_lr_at": _sig("dl_lr_at", _f64, [ctypes.POINTER(DLLrSchedule), _f64, _i64]),
     "dl_profile_begin": _sig("dl_profile_begin", _i32, [_i32]),
     "dl_profile_end": _sig("dl_profile_end", _i32, [_i32, _vp, _vp]),
+    "dl_set_mlp_fusion": _sig("dl_set_mlp_fusion", _i32, [_i32]),
 }
 
 EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
@@ -153,7 +154,7 @@ EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "mlp_train_step_workspace_size", "adam_step", "ema_update", "clip_grad_norm",
            "clip_grad_norm_workspace_size", "optimizer_step", "optimizer_step_workspace_size",
            "mse_loss_fwd_bwd", "mse_loss_workspace_size", "dl_lr_at",
-           "dl_profile_begin", "dl_profile_end"]
+           "dl_profile_begin", "dl_profile_end", "dl_set_mlp_fusion"]
 
 
 def build_target() -> str:
@@ -175,6 +176,15 @@ def profile_end(max_records: int = 4096):
     k = min(n, max_records)
     raw = names.raw
     return [(raw[i * 48:(i + 1) * 48].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(k)]
+
+
+def set_mlp_fusion(level: int) -> int:
+    """Fusion level of mlp_train_step on this thread (2: tail kernel, 1: head
+    kernel only); returns the previous level."""
+    prev = _c["dl_set_mlp_fusion"](level)
+    if prev < 0:
+        raise DenseError(-prev, _c["dl_last_error"]().decode())
+    return prev
 
 
 def _check(status: int):

@@ -46,6 +46,11 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
+// How much of the MLP step runs fused (dl_set_mlp_fusion): 2 = the tail
+// kernel when the network ends in a small hidden layer and a narrow head,
+// 1 = the head kernel alone.
+thread_local int g_mlp_fusion = 2;
+
 // Run `launch` (one kernel launch on stream s), timed when profiling is on.
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
@@ -266,6 +271,14 @@ extern "C" {
 const char* dl_last_error(void) { return g_last_error.c_str(); }
 
 const char* dl_build_target(void) { return "gfx950"; }
+
+int dl_set_mlp_fusion(int level) {
+  if (level != 1 && level != 2)
+    return -fail(DL_INVALID_ARGUMENT, "dl_set_mlp_fusion: level must be 1 or 2");
+  const int prev = g_mlp_fusion;
+  g_mlp_fusion = level;
+  return prev;
+}
 
 int dl_profile_begin(int capacity) {
   if (capacity < 0) return fail(DL_INVALID_ARGUMENT, "dl_profile_begin: negative capacity");
@@ -968,6 +981,13 @@ static bool mlp_fused_head(int32_t L, const dl_layer_t* layers, bool xent) {
   return xent && dl::head_xent_fits(layers[L - 1].in, layers[L - 1].out);
 }
 
+// Whether the last hidden layer, the narrow head and the hidden layer's dX
+// fit the tail kernel (shapes only; the step also checks alignment).
+static bool mlp_tail_shape(int32_t L, const dl_layer_t* layers, bool xent) {
+  return L >= 2 && mlp_fused_head(L, layers, xent) &&
+         dl::mlp_tail_fits(layers[L - 2].in, layers[L - 2].out, layers[L - 1].out);
+}
+
 // Gradient slices a layer's dW / db leave for the optimizer to add up: the
 // split-K slices of its weight-gradient GEMM, or the fused head's slices.
 static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
@@ -1046,6 +1066,10 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, bool xe
   const int last_gemm = mlp_fused_head(L, layers, xent) ? L - 2 : L - 1;
   int pairs = 0;
   size_t gb = 0;
+  if (L >= 3 && mlp_tail_shape(L, layers, xent)) {  // the tail kernel's dX
+    ++pairs;
+    gb = align_up((size_t)B * layers[L - 2].in * 4);
+  }
   for (int l = 1; l <= last_gemm; ++l)
     if (mlp_pair(B, layers[l])) {
       ++pairs;
@@ -1146,7 +1170,15 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   // forward, the softmax-xent and its vjp (dX written over Y[L-2], dW / db as
   // slices for the optimizer).
   const bool fused = mlp_fused_head(L, layers, xent);
-  const int last_gemm = fused ? L - 2 : L - 1;
+  // With a small last hidden layer the tail kernel also runs that layer's
+  // forward and dX, so its output never reaches HBM either: it writes the
+  // layer's output gradient into Y[L-2] and the dX into a gradient buffer.
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool tail = g_mlp_fusion >= 2 && mlp_tail_shape(L, layers, xent) &&
+                    al16(layers[L - 2].W) && (L >= 3 || al16(X));
+  const int last_gemm = tail ? L - 3 : fused ? L - 2 : L - 1;
+  float* gbuf[2] = {reinterpret_cast<float*>(base + g_off),
+                    reinterpret_cast<float*>(base + g_off + g_bytes)};
   // forward
   for (int l = 0; l <= last_gemm; ++l) {
     const dl_layer_t& ly = layers[l];
@@ -1173,7 +1205,24 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     }
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (forward)");
   }
-  if (fused) {
+  if (tail) {
+    const dl_layer_t& hl = layers[L - 2];
+    const dl_layer_t& ly = layers[L - 1];
+    const int64_t S = dl::head_xent_slices(B);
+    char* pb = base + part_off[L - 1];
+    float* dWp = S > 1 ? reinterpret_cast<float*>(pb) : ly.dW;
+    float* dbp = S > 1 ? reinterpret_cast<float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))
+                       : ly.db;
+    const float* Hin = L >= 3 ? Y[L - 3] : X;
+    float* dH = L >= 3 ? gbuf[0] : nullptr;
+    const int act0 = L >= 3 ? layers[L - 3].act : DL_ACT_IDENTITY;
+    e = timed("mlp_tail", s, [&] {
+      return dl::launch_mlp_tail(B, (int)hl.in, (int)hl.out, (int)ly.out, Hin, hl.W, hl.b, hl.act,
+                                 act0, ly.W, ly.b, labels, row_loss, Y[L - 2], dH, dWp, dbp, s,
+                                 dscale);
+    });
+    if (e != hipSuccess) return hip_fail(e, "mlp_train_step (tail)");
+  } else if (fused) {
     const dl_layer_t& ly = layers[L - 1];
     const int64_t S = dl::head_xent_slices(B);
     // one slice (B <= 32): straight into dW / db, where the optimizer reads it
@@ -1205,10 +1254,33 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (mse)");
   }
   // backward; G holds the current layer's output gradient
-  float* gbuf[2] = {reinterpret_cast<float*>(base + g_off),
-                    reinterpret_cast<float*>(base + g_off + g_bytes)};
-  const float* G = Y[last_gemm];
-  for (int l = last_gemm; l >= 0; --l) {
+  const float* G = last_gemm >= 0 ? Y[last_gemm] : nullptr;
+  int first_bwd = last_gemm;
+  if (tail) {
+    // the weight gradient of the tail's hidden layer (its output gradient in
+    // Y[L-2]), in one launch with the first layer's when that layer comes
+    // right before it (the first layer has no dX)
+    const int lh = L - 2;
+    const dl_layer_t& hl = layers[lh];
+    const float* Hin = lh >= 1 ? Y[lh - 1] : X;
+    const Plan ph = plan_gemm(DL_F32, dl::EPI_DW, hl.out, hl.in, B);
+    const Plan p0 = plan_gemm(DL_F32, dl::EPI_DW, layers[0].out, layers[0].in, B);
+    if (lh == 1 && ph.tile == 1 && p0.tile == 1) {
+      const dl::GemmDesc d0 = dw_desc(DL_F32, B, layers[0].in, layers[0].out, gbuf[0], X,
+                                      layers[0].dW, layers[0].db, base + part_off[0], p0);
+      const dl::GemmDesc dh = dw_desc(DL_F32, B, hl.in, hl.out, Y[lh], Hin, hl.dW, hl.db,
+                                      base + part_off[lh], ph);
+      e = timed("dwdw_gemm", s, [&] { return dl::launch_gemm_f32_dw_dw(d0, dh, s); });
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW + dW)");
+      first_bwd = -1;
+    } else {
+      e = dw_gemm(DL_F32, B, hl.in, hl.out, Y[lh], Hin, hl.dW, hl.db, base + part_off[lh], s,
+                  /*reduce=*/false);
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
+      G = gbuf[0];
+    }
+  }
+  for (int l = first_bwd; l >= 0; --l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
     if (l > 0 && mlp_pair(B, ly)) {

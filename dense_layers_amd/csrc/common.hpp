@@ -519,6 +519,22 @@ hipError_t launch_head_xent(int64_t B, int K, int C, const float* H, float* dH, 
                             const float* W, const float* bias, const int32_t* labels,
                             float* row_loss, float* dW_part, float* db_part, hipStream_t s,
                             const float* dscale = nullptr);
+// The MLP step's tail in one kernel: the forward of a hidden layer
+// [K1 -> N1] (act1), the narrow head after it [N1 -> C] with softmax-xent
+// and its vjp, and the hidden layer's dX masked by act0' of its input (dH
+// null: no dX).  Writes G1 [B, N1] (the hidden layer's output gradient, times
+// act1'), dH [B, K1], the per-row losses and the head's dW / db as
+// head_xent_slices(B) slices.  hipErrorNotSupported when Hin, W1, G1 or dH is
+// not 16-byte aligned (nothing launched).
+bool mlp_tail_fits(int64_t K1, int64_t N1, int64_t C);
+hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, const float* W1,
+                           const float* b1, int act1, int act0, const float* W2, const float* b2,
+                           const int32_t* labels, float* row_loss, float* G1, float* dH,
+                           float* dW_part, float* db_part, hipStream_t s,
+                           const float* dscale = nullptr);
+// Two float32 weight gradients (M/N-major operands, 64x64 tiles) in one
+// launch.
+hipError_t launch_gemm_f32_dw_dw(const GemmDesc& a, const GemmDesc& b, hipStream_t s);
 // Optimizer kinds (the values of enum dl_opt_kind).
 enum OptKind { OPT_SGD = 0, OPT_ADAMW = 1, OPT_ADAM = 2 };
 

@@ -317,26 +317,28 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
                                                        blockIdx.x, gridDim.x, smem);
 }
 
-// The weight gradient and the dX of one small layer in one launch (64x64
-// tiles of 4 waves for both): workgroups [0, n_dw) take the dW items, the
-// rest the dX items.  The two products only read common inputs, so they may
-// run side by side; dX must not be written over either product's input.
+// Two small products in one launch (64x64 tiles of 4 waves for both):
+// workgroups [0, a.nwg) take the weight-gradient items of job a, the rest the
+// items of job b (the same layer's dX, or another layer's weight gradient).
+// The two products only read common inputs, so they may run side by side;
+// neither may write over the other's inputs.
 struct F32Job {
   GemmDesc d;
   int tiles_m, tiles_n, a_vec, b_vec, out_vec, nwg;
 };
+template <int ALAY2, int BLAY2, int EPI2>
 __global__ void __launch_bounds__(256)
-gemm_f32_dw_dx_kernel(F32Job dw, F32Job dx) {
-  constexpr int kDw = f32_smem_floats<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR>();
-  constexpr int kDx = f32_smem_floats<64, 64, 32, 2, 2, K_MAJOR, MN_MAJOR>();
-  __shared__ __attribute__((aligned(16))) float smem[kDw > kDx ? kDw : kDx];
-  const int b = blockIdx.x;
-  if (b < dw.nwg)
+gemm_f32_pair_kernel(F32Job a, F32Job b) {
+  constexpr int kA = f32_smem_floats<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR>();
+  constexpr int kB = f32_smem_floats<64, 64, 32, 2, 2, ALAY2, BLAY2>();
+  __shared__ __attribute__((aligned(16))) float smem[kA > kB ? kA : kB];
+  const int w = blockIdx.x;
+  if (w < a.nwg)
     gemm_f32_body<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR, EPI_DW>(
-        dw.d, dw.tiles_m, dw.tiles_n, dw.a_vec, dw.b_vec, dw.out_vec, b, dw.nwg, smem);
+        a.d, a.tiles_m, a.tiles_n, a.a_vec, a.b_vec, a.out_vec, w, a.nwg, smem);
   else
-    gemm_f32_body<64, 64, 32, 2, 2, K_MAJOR, MN_MAJOR, EPI_DX>(
-        dx.d, dx.tiles_m, dx.tiles_n, dx.a_vec, dx.b_vec, dx.out_vec, b - dw.nwg, dx.nwg, smem);
+    gemm_f32_body<64, 64, 32, 2, 2, ALAY2, BLAY2, EPI2>(
+        b.d, b.tiles_m, b.tiles_n, b.a_vec, b.b_vec, b.out_vec, w - a.nwg, b.nwg, smem);
 }
 
 // Grid shape and vector-access flags of one GEMM on a BM x BN tile.
@@ -411,7 +413,22 @@ hipError_t launch_gemm_f32_dw_dx(const GemmDesc& dw, const GemmDesc& dx, hipStre
   hipError_t e = make_job<64, 64>(dw, a);
   if (e == hipSuccess) e = make_job<64, 64>(dx, b);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_f32_dw_dx_kernel, dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
+  hipLaunchKernelGGL((gemm_f32_pair_kernel<K_MAJOR, MN_MAJOR, EPI_DX>),
+                     dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32_dw_dw(const GemmDesc& dw_a, const GemmDesc& dw_b, hipStream_t s) {
+  auto ok = [](const GemmDesc& d) {
+    return d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR;
+  };
+  if (!ok(dw_a) || !ok(dw_b)) return hipErrorInvalidValue;
+  F32Job a, b;
+  hipError_t e = make_job<64, 64>(dw_a, a);
+  if (e == hipSuccess) e = make_job<64, 64>(dw_b, b);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_f32_pair_kernel<MN_MAJOR, MN_MAJOR, EPI_DW>),
+                     dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
   return hipGetLastError();
 }
 

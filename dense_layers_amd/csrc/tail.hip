@@ -1,0 +1,413 @@
+// The tail of the MLP step in one pass over the rows: the forward of the
+// last hidden layer, the narrow classifier head after it (last Linear,
+// softmax cross-entropy and its vjp) and the dX of that hidden layer.
+//
+// The pieces are the LinearAct forward / vjp and the composed backward pass
+// of the noeira.nn docs ("The design in one page"), with the cross-entropy
+// read once (Orthon page, "Selected Orthon vs. PyTorch results").  For the
+// layers h -> n -> C at the end of a network (h, n <= 256, C <= 16) a
+// workgroup takes 32 rows of the hidden layer's input Hin and, keeping
+// everything in LDS,
+//   H   = act1(Hin W1^T + b1)                     (matrix cores)
+//   z   = W2 h + b2, loss = logsumexp(z) - z[y], g = (softmax(z) - onehot) / B
+//   G1  = (W2^T g) * act1'(H)                     (the head's dX, masked)
+//   dH  = (G1 W1) * act0'(Hin)                    (matrix cores)
+// and writes only G1 and dH (the inputs of the two weight gradients that
+// follow) and the per-row losses; H and the logits never reach HBM.  The
+// head's dW2 / db2 leave as per-workgroup slices (rows added in order), which
+// the optimizer adds in slice order.
+//
+// Every product runs in the order of the standalone kernels: each 32x32
+// block accumulates its whole contraction in one wave, k ascending in groups
+// of 8 (lane half h supplies k = 8 kg + 4 h + s at MFMA step s), and the
+// bias, activation and masks are applied with the same operations, so the
+// results equal those of the forward GEMM, the head kernel and the dX GEMM
+// run one after the other.  A forward wave requests all of its W1 fragments
+// (at most 128 registers) when the workgroup starts and keeps them for every
+// row tile, so its chain of MFMAs never waits on memory; the dX operand
+// streams in chunks, the first requested before the head runs.
+#include "common.hpp"
+
+namespace dl {
+namespace {
+
+constexpr int kTailThreads = 512;
+constexpr int kTailRows = 32;
+constexpr int kTailTPR = kTailThreads / kTailRows;  // 16 threads per row (head)
+constexpr int kTailDMax = 256;                      // h and n
+constexpr int kTailCMax = 16;
+constexpr int kTailMaxSlices = 256;
+constexpr int kTS = kTailDMax + 4;  // LDS row stride (floats): 16-byte aligned rows
+constexpr int kTailPairs = kTailDMax * (kTailCMax / 4) / kTailThreads;
+constexpr int kTailVecs = kTailRows * kTailDMax / 4 / kTailThreads;  // float4 per thread per tile
+constexpr int kGroups = kTailDMax / 8;  // k groups of 8 in the longest contraction
+constexpr int kChunk = 4;               // k groups per streamed dX operand chunk
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row (the DPP
+// butterfly of the head kernel: the same operands at every step).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// The thread index made opaque, so that the row / column of each element in
+// the copies below is computed where it is used rather than hoisted out of
+// the row-tile loop and kept live through every phase.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Moves a [nrows x D] row-major block between global memory and an LDS tile
+// of row stride kTS (D % 4 == 0, 16-byte aligned rows); rows past nrows are
+// filled with zeros on the way in and skipped on the way out.
+__device__ __forceinline__ void tile_load(const float* __restrict__ src, int n,
+                                          f32x4 (&v)[kTailVecs], int tid) {
+  tid = fresh(tid);
+#pragma unroll
+  for (int j = 0; j < kTailVecs; ++j) {
+    const int e = (tid + j * kTailThreads) * 4;
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (e < n) v[j] = *reinterpret_cast<const f32x4*>(src + e);
+  }
+}
+__device__ __forceinline__ void tile_put(float* lds, const f32x4 (&v)[kTailVecs], int D, int tid) {
+  tid = fresh(tid);
+#pragma unroll
+  for (int j = 0; j < kTailVecs; ++j) {
+    const int e = (tid + j * kTailThreads) * 4;
+    if (e < kTailRows * D) {
+      const int q = e / D, k = e - q * D;
+      *reinterpret_cast<f32x4*>(lds + q * kTS + k) = v[j];
+    }
+  }
+}
+__device__ __forceinline__ void tile_store(const float* lds, float* __restrict__ dst, int n, int D,
+                                           int tid) {
+  tid = fresh(tid);
+#pragma unroll
+  for (int j = 0; j < kTailVecs; ++j) {
+    const int e = (tid + j * kTailThreads) * 4;
+    if (e < n) {
+      const int q = e / D, k = e - q * D;
+      *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(lds + q * kTS + k);
+    }
+  }
+}
+
+// Buffer resource over `bytes` bytes at p: loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const float* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, bytes, 0x00020000);
+}
+
+// The 4 MFMAs of k group kg: A from LDS (row lane % 32 at arow, k = 8 kg +
+// 4 h + s), B fragment b of the same k.
+__device__ __forceinline__ void mfma_group(f32x16& acc, const float* arow, int kg, f32x4 b) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(arow + kg * 8);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+// The dX operand of one 32-column block: W1 read as [N1, K1] (4 loads per k
+// group, one per k, consecutive columns across the lanes), streamed in
+// chunks of kChunk groups, each requested one chunk ahead.  The per-lane
+// offset is fixed and the k offset uniform; groups past the end and columns
+// past K1 read zeros (their offset points past the buffer).
+struct DxOperand {
+  __amdgpu_buffer_rsrc_t res;
+  int voff, oob, ldb4, groups;
+  f32x4 q0[kChunk], q1[kChunk];
+
+  __device__ __forceinline__ void fetch(f32x4 (&b)[kChunk], int kg0) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int kg = kg0 + i;
+      const int vo = kg < groups ? voff : oob;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[i][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(res, vo, (kg * 8 + t) * ldb4, 0));
+    }
+  }
+  __device__ __forceinline__ void chunk(f32x16& acc, const float* arow, const f32x4 (&b)[kChunk],
+                                        int kg0) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (kg0 + i >= groups) break;
+      mfma_group(acc, arow, kg0 + i, b[i]);
+    }
+  }
+  // The whole contraction; the first chunk was requested with fetch(q0, 0).
+  __device__ __forceinline__ f32x16 run(const float* arow) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int kg0 = 0; kg0 < groups; kg0 += 2 * kChunk) {
+      if (kg0 + kChunk < groups) fetch(q1, kg0 + kChunk);
+      chunk(acc, arow, q0, kg0);
+      if (kg0 + kChunk >= groups) break;
+      if (kg0 + 2 * kChunk < groups) fetch(q0, kg0 + 2 * kChunk);
+      chunk(acc, arow, q1, kg0 + kChunk);
+    }
+    return acc;
+  }
+};
+
+// Row of accumulator register r of lane half h in a 32x32 block (the lane's
+// column is lane % 32).
+__device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
+
+// Workgroup b takes row tiles [b tiles_per, (b + 1) tiles_per).  Hin, W1,
+// G1, dH 16-byte aligned; K1 (h) and N1 (n) multiples of 8.
+template <bool HAS_DX>
+__global__ void __launch_bounds__(kTailThreads)
+mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
+                const float* __restrict__ Hin, const float* __restrict__ W1,
+                const float* __restrict__ b1, int act1, int act0, const float* __restrict__ W2,
+                const float* __restrict__ b2, const int32_t* __restrict__ labels,
+                float* __restrict__ row_loss, float* __restrict__ G1, float* __restrict__ dH,
+                float* __restrict__ dW_part, float* __restrict__ db_part, float invB,
+                const float* dscale) {
+  __shared__ __attribute__((aligned(16))) float Xs[kTailRows * kTS];  // Hin, then dH
+  __shared__ __attribute__((aligned(16))) float Hs[kTailRows * kTS];  // H
+  __shared__ __attribute__((aligned(16))) float Gs[kTailRows * kTS];  // G1
+  __shared__ __attribute__((aligned(16))) float Wt[kTailDMax * kTailCMax];
+  __shared__ __attribute__((aligned(16))) float Ds[kTailRows * kTailCMax];
+  __shared__ float Bc[kTailCMax];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int r = tid / kTailTPR, lr = tid % kTailTPR;
+  const int K = N1;  // the head's input width
+  const int w1bytes = N1 * K1 * 4;
+  const __amdgpu_buffer_rsrc_t w1res = buffer_of(W1, w1bytes);
+
+  // forward: wave w owns columns 32 w .. 32 w + 31 of H; all of its W1
+  // fragments are requested first and kept for every row tile
+  const int KG = K1 / 8;
+  const bool f_has = wave * 32 < N1;
+  const int fcol = wave * 32 + l32;
+  f32x4 bf[kGroups];
+  if (f_has) {
+    const int vo = fcol < N1 ? (fcol * K1 + 4 * h) * 4 : w1bytes;
+#pragma unroll
+    for (int kg = 0; kg < kGroups; ++kg)
+      bf[kg] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(w1res, kg < KG ? vo : w1bytes, kg * 32, 0));
+  }
+  const float fbias = (f_has && fcol < N1) ? b1[fcol] : 0.f;
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
+  {
+    float wr[kTailDMax * kTailCMax / kTailThreads];
+#pragma unroll
+    for (int j = 0; j < kTailDMax * kTailCMax / kTailThreads; ++j) {
+      const int i = tid + j * kTailThreads;
+      const int k = i / kTailCMax, c = i % kTailCMax;
+      wr[j] = (k < K && c < C) ? W2[(int64_t)c * K + k] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kTailDMax * kTailCMax / kTailThreads; ++j) Wt[tid + j * kTailThreads] = wr[j];
+  }
+  if (tid < kTailCMax) Bc[tid] = tid < C ? b2[tid] : 0.f;
+
+  // dX: wave w owns columns 32 w .. 32 w + 31 of dH
+  const bool x_has = HAS_DX && wave * 32 < K1;
+  const int xcol = wave * 32 + l32;
+  DxOperand xo;
+  xo.res = w1res;
+  xo.oob = w1bytes;
+  xo.ldb4 = K1 * 4;
+  xo.groups = N1 / 8;
+  xo.voff = xcol < K1 ? (4 * h * K1 + xcol) * 4 : w1bytes;
+
+  int pk[kTailPairs], pc[kTailPairs];
+  float acc2[kTailPairs][4];
+#pragma unroll
+  for (int j = 0; j < kTailPairs; ++j) {
+    const int p = tid + j * kTailThreads;
+    pk[j] = p % K;
+    pc[j] = p < K * (kTailCMax / 4) ? (p / K) * 4 : -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc2[j][e] = 0.f;
+  }
+  float dbacc = 0.f;
+  const float* arow_x = Xs + l32 * kTS + 4 * h;
+  const float* arow_g = Gs + l32 * kTS + 4 * h;
+
+  const int64_t ntiles = (B + kTailRows - 1) / kTailRows;
+  const int64_t t_end = min<int64_t>(ntiles, ((int64_t)blockIdx.x + 1) * tiles_per);
+  for (int64_t t = (int64_t)blockIdx.x * tiles_per; t < t_end; ++t) {
+    const int64_t r0 = t * kTailRows;
+    const int nrows = (int)min<int64_t>(kTailRows, B - r0);
+    const bool active = r < nrows;
+    const int y = active ? labels[r0 + r] : -1;
+    {
+      f32x4 v[kTailVecs];
+      tile_load(Hin + r0 * K1, nrows * K1, v, tid);
+      __syncthreads();  // the previous tile's LDS reads are done
+      tile_put(Xs, v, K1, tid);
+    }
+    __syncthreads();
+
+    // ---- forward of the hidden layer: H = act1(Hin W1^T + b1)
+    if (f_has) {
+      f32x16 acc;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < kGroups; ++kg)
+        if (kg < KG) mfma_group(acc, arow_x, kg, bf[kg]);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float z = acc[q] + fbias;
+        Hs[acc_row(q, h) * kTS + fcol] = fcol < N1 ? act_apply(act1, z) : 0.f;
+      }
+    }
+    if (x_has) xo.fetch(xo.q0, 0);
+    __syncthreads();
+
+    // ---- head: logits, softmax cross-entropy, g, G1 = (W2^T g) act1'(H)
+    const bool valid = y >= 0 && y < C;
+    float z[kTailCMax];
+#pragma unroll
+    for (int c = 0; c < kTailCMax; ++c) z[c] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kTailDMax / kTailTPR; ++kk) {
+      const int k = lr + kk * kTailTPR;
+      if (k >= K) break;
+      const float hv = Hs[r * kTS + k];
+#pragma unroll
+      for (int c4 = 0; c4 < kTailCMax / 4; ++c4) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kTailCMax + c4 * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[c4 * 4 + e] += hv * w[e];
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kTailCMax; ++c) {
+      z[c] = row16_sum(z[c]);
+      z[c] += Bc[c];
+      if (c < C) m = fmaxf(m, z[c]);
+    }
+    float s = 0.f, zy = 0.f;
+#pragma unroll
+    for (int c = 0; c < kTailCMax; ++c) {
+      if (c == y) zy = z[c];
+      z[c] = c < C ? __expf(z[c] - m) : 0.f;
+      s += z[c];
+    }
+    const float inv_s = 1.0f / s;
+    if (active && lr == 0) row_loss[r0 + r] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
+    float g[kTailCMax];
+#pragma unroll
+    for (int c = 0; c < kTailCMax; ++c)
+      g[c] = (active && c < C) ? (z[c] * inv_s - (c == y ? 1.0f : 0.0f)) * invB : 0.f;
+    if (lr < kTailCMax / 4) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c4 = 0; c4 < kTailCMax / 4; ++c4)
+        if (c4 == lr) x = f32x4{g[4 * c4], g[4 * c4 + 1], g[4 * c4 + 2], g[4 * c4 + 3]};
+      *reinterpret_cast<f32x4*>(&Ds[r * kTailCMax + lr * 4]) = x;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kTailDMax / kTailTPR; ++kk) {
+      const int k = lr + kk * kTailTPR;
+      if (k >= K) break;
+      float d = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < kTailCMax / 4; ++c4) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kTailCMax + c4 * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d += g[c4 * 4 + e] * w[e];
+      }
+      Gs[r * kTS + k] = d * act_deriv(act1, Hs[r * kTS + k]);
+    }
+    __syncthreads();
+
+    // this tile's rows, in order, into the workgroup's dW2 / db2 slice
+#pragma unroll
+    for (int j = 0; j < kTailPairs; ++j) {
+      if (pc[j] < 0) continue;
+      float a0 = acc2[j][0], a1 = acc2[j][1], a2 = acc2[j][2], a3 = acc2[j][3];
+#pragma unroll 8
+      for (int q = 0; q < kTailRows; ++q) {
+        const float hv = Hs[q * kTS + pk[j]];
+        const f32x4 d = *reinterpret_cast<const f32x4*>(&Ds[q * kTailCMax + pc[j]]);
+        a0 += d[0] * hv; a1 += d[1] * hv; a2 += d[2] * hv; a3 += d[3] * hv;
+      }
+      acc2[j][0] = a0; acc2[j][1] = a1; acc2[j][2] = a2; acc2[j][3] = a3;
+    }
+    if (tid < C)
+      for (int q = 0; q < kTailRows; ++q) dbacc += Ds[q * kTailCMax + tid];
+    tile_store(Gs, G1 + r0 * N1, nrows * N1, N1, tid);
+
+    // ---- dX of the hidden layer: dH = (G1 W1) act0'(Hin), over Hin in LDS
+    if (HAS_DX) {
+      if (x_has) {
+        const f32x16 acc = xo.run(arow_g);
+        if (xcol < K1) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            float* p = &Xs[acc_row(q, h) * kTS + xcol];
+            *p = acc[q] * act_deriv(act0, *p);
+          }
+        }
+      }
+      __syncthreads();
+      tile_store(Xs, dH + r0 * K1, nrows * K1, K1, tid);
+    }
+  }
+
+  float* dWp = dW_part + (int64_t)blockIdx.x * C * K;
+#pragma unroll
+  for (int j = 0; j < kTailPairs; ++j) {
+    if (pc[j] < 0) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (pc[j] + e < C) dWp[(int64_t)(pc[j] + e) * K + pk[j]] = acc2[j][e];
+  }
+  if (tid < C) db_part[(int64_t)blockIdx.x * C + tid] = dbacc;
+}
+
+}  // namespace
+
+bool mlp_tail_fits(int64_t K1, int64_t N1, int64_t C) {
+  return C >= 1 && C <= kTailCMax && K1 >= 8 && K1 <= kTailDMax && K1 % 8 == 0 && N1 >= 8 &&
+         N1 <= kTailDMax && N1 % 8 == 0;
+}
+
+hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, const float* W1,
+                           const float* b1, int act1, int act0, const float* W2, const float* b2,
+                           const int32_t* labels, float* row_loss, float* G1, float* dH,
+                           float* dW_part, float* db_part, hipStream_t s, const float* dscale) {
+  if (!mlp_tail_fits(K1, N1, C) || B < 1) return hipErrorInvalidValue;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(Hin) | reinterpret_cast<uintptr_t>(W1) |
+                       reinterpret_cast<uintptr_t>(G1) | reinterpret_cast<uintptr_t>(dH);
+  if ((al & 15) != 0) return hipErrorNotSupported;
+  // the head kernel's slicing (32-row tiles, at most 256 slices), so the
+  // optimizer finds head_xent_slices(B) slices either way
+  const int64_t ntiles = (B + kTailRows - 1) / kTailRows;
+  const int64_t per = (ntiles + kTailMaxSlices - 1) / kTailMaxSlices;
+  const int64_t blocks = (ntiles + per - 1) / per;
+  const float invB = (float)(1.0 / (double)B);
+  if (dH != nullptr)
+    hipLaunchKernelGGL(mlp_tail_kernel<true>, dim3((unsigned)blocks), dim3(kTailThreads), 0, s, B,
+                       K1, N1, C, per, Hin, W1, b1, act1, act0, W2, b2, labels, row_loss, G1, dH,
+                       dW_part, db_part, invB, dscale);
+  else
+    hipLaunchKernelGGL(mlp_tail_kernel<false>, dim3((unsigned)blocks), dim3(kTailThreads), 0, s,
+                       B, K1, N1, C, per, Hin, W1, b1, act1, act0, W2, b2, labels, row_loss, G1,
+                       dH, dW_part, db_part, invB, dscale);
+  return hipGetLastError();
+}
+
+}  // namespace dl

@@ -109,6 +109,22 @@ const char* dl_build_target(void);
 int dl_profile_begin(int capacity);
 int dl_profile_end(int max, float* ms, char* names);
 
+/*
+ * dl_set_mlp_fusion -- how much of mlp_train_step the calling thread runs
+ * fused, for comparing the fused step with the composition it replaces (the
+ * composed vjps of the noeira.nn docs, "The design in one page").
+ *   2 (default): when the network ends in a hidden layer of at most 256
+ *     inputs and outputs (multiples of 8) and a head of at most 16 classes,
+ *     one kernel runs that layer's forward, the head's forward, softmax-xent
+ *     and vjp, and that layer's dX; the hidden layer's output never reaches
+ *     HBM.
+ *   1: the head alone is fused; the hidden layer runs as GEMMs.
+ * Both levels run every product in the same order and give bit-identical
+ * results.  Returns the previous level, or -DL_INVALID_ARGUMENT for any
+ * other level (the setting is unchanged).  Thread-local; no GPU work.
+ */
+int dl_set_mlp_fusion(int level);
+
 /* ---- dense layer forward ------------------------------------------------- */
 
 /*

@@ -137,3 +137,13 @@ def test_mlp_step_rejects_bad_layers(dl):
     opt = dl.DLOpt(5, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
     assert c["mlp_train_step"](None, 2, 2, table, fake, fake, ctypes.byref(opt), fake, fake,
                                1 << 20) == 1
+
+
+def test_mlp_fusion_level_setting(dl):
+    prev = dl.set_mlp_fusion(1)
+    assert prev == 2  # default: the tail kernel where it fits
+    assert dl.set_mlp_fusion(2) == 1
+    for bad in (0, 3, -1):
+        with pytest.raises(dl.DenseError):
+            dl.set_mlp_fusion(bad)
+    assert dl.set_mlp_fusion(2) == 2  # unchanged by the rejected levels
