@@ -108,10 +108,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const float* p, int 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, bytes, 0x00020000);
 }
 
-// The 4 MFMAs of k group kg: A from LDS (row lane % 32 at arow, k = 8 kg +
-// 4 h + s), B fragment b of the same k.
-__device__ __forceinline__ void mfma_group(f32x16& acc, const float* arow, int kg, f32x4 b) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(arow + kg * 8);
+// A fragment of k group kg (row lane % 32 at arow, k = 8 kg + 4 h .. + 3).
+__device__ __forceinline__ f32x4 afrag(const float* arow, int kg) {
+  return *reinterpret_cast<const f32x4*>(arow + kg * 8);
+}
+
+// The 4 MFMAs of one k group: lane half h supplies k = 8 kg + 4 h + s at
+// step s of both fragments.
+__device__ __forceinline__ void mfma4(f32x16& acc, f32x4 a, f32x4 b) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
 }
@@ -136,25 +140,57 @@ struct DxOperand {
         b[i][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(res, vo, (kg * 8 + t) * ldb4, 0));
     }
   }
+  // The MFMAs of one chunk; each group's A fragment is read while the
+  // previous group's MFMAs run (a holds group kg0's on entry, group
+  // kg0 + kChunk's, clamped to the last, on exit).
   __device__ __forceinline__ void chunk(f32x16& acc, const float* arow, const f32x4 (&b)[kChunk],
-                                        int kg0) {
+                                        int kg0, f32x4& a) {
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       if (kg0 + i >= groups) break;
-      mfma_group(acc, arow, kg0 + i, b[i]);
+      const f32x4 cur = a;
+      a = afrag(arow, min(kg0 + i + 1, groups - 1));
+      mfma4(acc, cur, b[i]);
     }
   }
-  // The whole contraction; the first chunk was requested with fetch(q0, 0).
+  // The whole contraction of a compile-time G groups (G == groups), fully
+  // unrolled: no branches between the MFMAs, and each group's A fragment is
+  // read into registers of its own while the previous group's MFMAs run.
+  // The first chunk was requested with fetch(q0, 0).
+  template <int G>
+  __device__ __forceinline__ f32x16 run_fixed(const float* arow) {
+    static_assert(G % (2 * kChunk) == 0, "whole chunk pairs");
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    f32x4 a = afrag(arow, 0);
+#pragma unroll
+    for (int c = 0; c < G / kChunk; ++c) {
+      f32x4(&cur)[kChunk] = (c & 1) ? q1 : q0;
+      f32x4(&nxt)[kChunk] = (c & 1) ? q0 : q1;
+      if (c + 1 < G / kChunk) fetch(nxt, (c + 1) * kChunk);
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        const int kg = c * kChunk + i;
+        const f32x4 an = kg + 1 < G ? afrag(arow, kg + 1) : a;
+        mfma4(acc, a, cur[i]);
+        a = an;
+      }
+    }
+    return acc;
+  }
+  // Any group count: the first chunk was requested with fetch(q0, 0).
   __device__ __forceinline__ f32x16 run(const float* arow) {
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    f32x4 a = afrag(arow, 0);
     for (int kg0 = 0; kg0 < groups; kg0 += 2 * kChunk) {
       if (kg0 + kChunk < groups) fetch(q1, kg0 + kChunk);
-      chunk(acc, arow, q0, kg0);
+      chunk(acc, arow, q0, kg0, a);
       if (kg0 + kChunk >= groups) break;
       if (kg0 + 2 * kChunk < groups) fetch(q0, kg0 + 2 * kChunk);
-      chunk(acc, arow, q1, kg0 + kChunk);
+      chunk(acc, arow, q1, kg0 + kChunk, a);
     }
     return acc;
   }
@@ -165,8 +201,10 @@ struct DxOperand {
 __device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
 
 // Workgroup b takes row tiles [b tiles_per, (b + 1) tiles_per).  Hin, W1,
-// G1, dH 16-byte aligned; K1 (h) and N1 (n) multiples of 8.
-template <bool HAS_DX>
+// G1, dH 16-byte aligned; K1 (h) and N1 (n) multiples of 8.  KGF / KGX: the
+// forward / dX contraction lengths in groups of 8 (K1 / 8, N1 / 8) when
+// known at compile time (fully unrolled loops), else 0.
+template <bool HAS_DX, int KGF, int KGX>
 __global__ void __launch_bounds__(kTailThreads)
 mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
                 const float* __restrict__ Hin, const float* __restrict__ W1,
@@ -195,11 +233,12 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
   const int KG = K1 / 8;
   const bool f_has = wave * 32 < N1;
   const int fcol = wave * 32 + l32;
-  f32x4 bf[kGroups];
+  constexpr int kBf = KGF > 0 ? KGF : kGroups;
+  f32x4 bf[kBf];
   if (f_has) {
     const int vo = fcol < N1 ? (fcol * K1 + 4 * h) * 4 : w1bytes;
 #pragma unroll
-    for (int kg = 0; kg < kGroups; ++kg)
+    for (int kg = 0; kg < kBf; ++kg)
       bf[kg] = __builtin_bit_cast(
           f32x4, __builtin_amdgcn_raw_buffer_load_b128(w1res, kg < KG ? vo : w1bytes, kg * 32, 0));
   }
@@ -262,9 +301,24 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
       f32x16 acc;
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+      // each group's A fragment is read while the previous group's MFMAs run
+      f32x4 a = afrag(arow_x, 0);
+      if (KGF > 0) {
 #pragma unroll
-      for (int kg = 0; kg < kGroups; ++kg)
-        if (kg < KG) mfma_group(acc, arow_x, kg, bf[kg]);
+        for (int kg = 0; kg < kBf; ++kg) {
+          const f32x4 an = kg + 1 < kBf ? afrag(arow_x, kg + 1) : a;
+          mfma4(acc, a, bf[kg]);
+          a = an;
+        }
+      } else {
+#pragma unroll
+        for (int kg = 0; kg < kBf; ++kg)
+          if (kg < KG) {
+            const f32x4 cur = a;
+            a = afrag(arow_x, min(kg + 1, KG - 1));
+            mfma4(acc, cur, bf[kg]);
+          }
+      }
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const float z = acc[q] + fbias;
@@ -353,7 +407,7 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
     // ---- dX of the hidden layer: dH = (G1 W1) act0'(Hin), over Hin in LDS
     if (HAS_DX) {
       if (x_has) {
-        const f32x16 acc = xo.run(arow_g);
+        const f32x16 acc = KGX > 0 ? xo.template run_fixed<KGX>(arow_g) : xo.run(arow_g);
         if (xcol < K1) {
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
@@ -399,14 +453,22 @@ hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, c
   const int64_t per = (ntiles + kTailMaxSlices - 1) / kTailMaxSlices;
   const int64_t blocks = (ntiles + per - 1) / per;
   const float invB = (float)(1.0 / (double)B);
-  if (dH != nullptr)
-    hipLaunchKernelGGL(mlp_tail_kernel<true>, dim3((unsigned)blocks), dim3(kTailThreads), 0, s, B,
-                       K1, N1, C, per, Hin, W1, b1, act1, act0, W2, b2, labels, row_loss, G1, dH,
-                       dW_part, db_part, invB, dscale);
-  else
-    hipLaunchKernelGGL(mlp_tail_kernel<false>, dim3((unsigned)blocks), dim3(kTailThreads), 0, s,
-                       B, K1, N1, C, per, Hin, W1, b1, act1, act0, W2, b2, labels, row_loss, G1,
-                       dH, dW_part, db_part, invB, dscale);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTailThreads), 0, s, B, K1, N1, C, per,
+                       Hin, W1, b1, act1, act0, W2, b2, labels, row_loss, G1, dH, dW_part, db_part,
+                       invB, dscale);
+  };
+  // the MLP shapes with a 256-wide hidden input get fully unrolled loops
+  const bool fixed = K1 == 256 && (N1 == 128 || N1 == 256);
+  if (dH != nullptr) {
+    if (fixed && N1 == 128) go(mlp_tail_kernel<true, 32, 16>);
+    else if (fixed) go(mlp_tail_kernel<true, 32, 32>);
+    else go(mlp_tail_kernel<true, 0, 0>);
+  } else {
+    if (fixed && N1 == 128) go(mlp_tail_kernel<false, 32, 16>);
+    else if (fixed) go(mlp_tail_kernel<false, 32, 32>);
+    else go(mlp_tail_kernel<false, 0, 0>);
+  }
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ SHAPES = {
     "four_layers_50": ([33, 48, 200, 120, 7], 50, [R, R, R, I]),
     "one_class_40": ([16, 16, 8, 1], 40, [R, R, I]),
     "many_tiles_9000": ([96, 64, 32, 4], 9000, [R, R, I]),
+    # fully unrolled kernel forms: 256-wide hidden input, 256 or 128 outputs
+    "unrolled_256_256_100": ([64, 256, 256, 10], 100, [R, R, I]),
+    "unrolled_no_dx_70": ([256, 128, 10], 70, [R, I]),
+    "unrolled_8200": ([784, 256, 128, 10], 8200, [R, R, I]),
 }
 
 
@@ -110,7 +114,8 @@ def test_tail_bit_identical_to_head_only(dl, shape, opt):
 
 
 @pytest.mark.parametrize("shape", ["narrow_77", "partial_blocks_300", "two_layers_129",
-                                   "four_layers_50", "one_class_40", "identity_hidden_45"])
+                                   "four_layers_50", "one_class_40", "identity_hidden_45",
+                                   "unrolled_256_256_100", "unrolled_no_dx_70"])
 @pytest.mark.parametrize("optim", ["sgd", "adamw"])
 def test_tail_step_matches_oracle(dl, shape, optim):
     o = si.SGD if optim == "sgd" else si.ADAMW
