@@ -91,11 +91,14 @@ bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 // with at least one such tile per CU, tile 2 for weight gradients with at
 // least 32 such tiles, 128x128 otherwise; operands that kernel cannot take
 // (unaligned, K not a multiple of 64) go to the general 128x128 kernel.  Only
-// the weight-gradient product (K = batch) is split along K: when it has fewer
-// than two workgroups per CU, the slice count is the smallest power of two
-// that gives at least four workgroups per CU (two for tile 2, whose LDS
-// admits one workgroup per CU; at most 64 slices), each slice keeping at
-// least four K tiles.
+// the weight-gradient product (K = batch) is split along K, when it has fewer
+// than two workgroups per CU, into a power-of-two number of slices (at most
+// 64, each keeping at least four K tiles): for 16-bit operands the smallest
+// count that gives at least four workgroups per CU (two for tile 2, whose LDS
+// admits one workgroup per CU); for float32 the largest count that keeps the
+// launch within one round of four workgroups per CU (fewer slices mean less
+// fixed cost per slice and a shorter sum over them in the optimizer, and a
+// second, partial round costs more than it hides).
 
 constexpr int kCUs = 256;
 
@@ -139,7 +142,11 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   }
   if (epi == dl::EPI_DW && tiles < 2 * kCUs) {
     int64_t want = 1;  // a power of two: even slices of power-of-two batches
-    while (want * tiles < per_cu * kCUs) want *= 2;
+    if (dtype == DL_F32) {
+      while (2 * want * tiles <= per_cu * kCUs) want *= 2;
+    } else {
+      while (want * tiles < per_cu * kCUs) want *= 2;
+    }
     const int64_t max_by_k = std::max<int64_t>(1, K / (4 * bk));
     want = std::min<int64_t>(std::min<int64_t>(want, max_by_k), 64);
     int64_t kps = ceil_div(ceil_div(K, want), bk) * bk;
@@ -215,8 +222,8 @@ dl::GemmDesc dw_desc(int dtype, int64_t B, int64_t in, int64_t out, const void* 
 
 hipError_t dw_gemm(int dtype, int64_t B, int64_t in, int64_t out, const void* G, const void* X,
                    float* dW, float* db, void* partial_ws, hipStream_t s, bool reduce = true,
-                   const float* out_scale = nullptr) {
-  const Plan p = plan_gemm(dtype, dl::EPI_DW, out, in, B);
+                   const float* out_scale = nullptr, const Plan* plan = nullptr) {
+  const Plan p = plan ? *plan : plan_gemm(dtype, dl::EPI_DW, out, in, B);
   dl::GemmDesc d = dw_desc(dtype, B, in, out, G, X, dW, db, partial_ws, p);
   d.out_scale = out_scale;
   hipError_t e = timed("dw_gemm", s, [&] { return run_gemm(dtype, d, p.tile, s); });
@@ -988,11 +995,37 @@ static bool mlp_tail_shape(int32_t L, const dl_layer_t* layers, bool xent) {
          dl::mlp_tail_fits(layers[L - 2].in, layers[L - 2].out, layers[L - 1].out);
 }
 
+// Weight-gradient plan of layer l inside the MLP step.  When the tail
+// kernel's hidden layer is layer 1 of a network that fits it, its weight
+// gradient shares a launch with the first layer's: it then takes the largest
+// power-of-two slice count that keeps both within one round of four
+// workgroups per CU (fewer, longer slices for the optimizer to add).  Both
+// fusion levels use this plan, so their results stay identical.
+static Plan mlp_dw_plan(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
+  Plan p = plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B);
+  if (l != 1 || L != 3 || !mlp_tail_shape(L, layers, xent) || p.tile != 1 || p.splits <= 1)
+    return p;
+  const Plan p0 = plan_gemm(DL_F32, dl::EPI_DW, layers[0].out, layers[0].in, B);
+  if (p0.tile != 1) return p;
+  const int64_t tiles = ceil_div(layers[l].out, 64) * ceil_div(layers[l].in, 64);
+  const int64_t budget = 4 * kCUs - ceil_div(layers[0].out, 64) * ceil_div(layers[0].in, 64) * p0.splits;
+  int64_t want = 1;
+  while (2 * want <= p.splits && 2 * want * tiles <= budget) want *= 2;
+  const int64_t kps = ceil_div(ceil_div(B, want), 32) * 32;
+  p.k_per_split = (int)kps;
+  p.splits = (int)ceil_div(B, kps);
+  if (p.splits <= 1) {
+    p.splits = 1;
+    p.k_per_split = (int)B;
+  }
+  return p;
+}
+
 // Gradient slices a layer's dW / db leave for the optimizer to add up: the
 // split-K slices of its weight-gradient GEMM, or the fused head's slices.
 static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
   if (l == L - 1 && mlp_fused_head(L, layers, xent)) return dl::head_xent_slices(B);
-  return plan_gemm(DL_F32, dl::EPI_DW, layers[l].out, layers[l].in, B).splits;
+  return mlp_dw_plan(B, L, layers, l, xent).splits;
 }
 
 // Forward of a layer split along K: when its forward product has few tiles
@@ -1263,8 +1296,8 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     const int lh = L - 2;
     const dl_layer_t& hl = layers[lh];
     const float* Hin = lh >= 1 ? Y[lh - 1] : X;
-    const Plan ph = plan_gemm(DL_F32, dl::EPI_DW, hl.out, hl.in, B);
-    const Plan p0 = plan_gemm(DL_F32, dl::EPI_DW, layers[0].out, layers[0].in, B);
+    const Plan ph = mlp_dw_plan(B, L, layers, lh, xent);
+    const Plan p0 = mlp_dw_plan(B, L, layers, 0, xent);
     if (lh == 1 && ph.tile == 1 && p0.tile == 1) {
       const dl::GemmDesc d0 = dw_desc(DL_F32, B, layers[0].in, layers[0].out, gbuf[0], X,
                                       layers[0].dW, layers[0].db, base + part_off[0], p0);
@@ -1275,7 +1308,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       first_bwd = -1;
     } else {
       e = dw_gemm(DL_F32, B, hl.in, hl.out, Y[lh], Hin, hl.dW, hl.db, base + part_off[lh], s,
-                  /*reduce=*/false);
+                  /*reduce=*/false, nullptr, &ph);
       if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
       G = gbuf[0];
     }
@@ -1285,7 +1318,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     const float* in = l == 0 ? X : Y[l - 1];
     if (l > 0 && mlp_pair(B, ly)) {
       float* Gn = G == gbuf[0] ? gbuf[1] : gbuf[0];
-      const Plan p = plan_gemm(DL_F32, dl::EPI_DW, ly.out, ly.in, B);
+      const Plan p = mlp_dw_plan(B, L, layers, l, xent);
       const dl::GemmDesc dw = dw_desc(DL_F32, B, ly.in, ly.out, G, in, ly.dW, ly.db,
                                       base + part_off[l], p);
       const dl::GemmDesc dx = dx_desc(B, ly.in, ly.out, G, ly.W, nullptr, Gn, layers[l - 1].act,
@@ -1295,8 +1328,9 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       G = Gn;
       continue;
     }
+    const Plan pl = mlp_dw_plan(B, L, layers, l, xent);
     e = dw_gemm(DL_F32, B, ly.in, ly.out, G, in, ly.dW, ly.db, base + part_off[l], s,
-                /*reduce=*/false);
+                /*reduce=*/false, nullptr, &pl);
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW)");
     if (l > 0) {
       e = dx_gemm(DL_F32, B, ly.in, ly.out, G, ly.W, nullptr, Y[l - 1], layers[l - 1].act,
