@@ -234,6 +234,11 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   }
   __syncthreads();
 
+  // Each half of a trip stores the register set loaded one half earlier into
+  // the buffer the other half reads, before its own MFMAs: the data has had
+  // a whole half to land, and the stores no longer sit between the MFMAs and
+  // the barrier.  The barrier at the end of each half orders every wave's
+  // reads of a buffer before the next stores into it.
   int kt = 0;
   for (; kt + 3 < nk_full; kt += 2) {
     la.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 2) * BK, tid);
@@ -241,18 +246,20 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
     // keep the loads ahead of the MFMAs (the scheduler would otherwise sink
     // them next to their LDS stores)
     __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    __builtin_amdgcn_sched_barrier(0);
     la2.store(As(1), tid);
     lb2.store(Bs(1), tid);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     la2.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 3) * BK, tid);
     lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 3) * BK, tid);
     __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    __builtin_amdgcn_sched_barrier(0);
     la.store(As(0), tid);
     lb.store(Bs(0), tid);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
   if (kt + 1 < nk_full) {  // drain set 2
