@@ -33,7 +33,7 @@ PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
-KERNEL_SOURCES = ["common.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
+KERNEL_SOURCES = ["common.hpp", "head_rows.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
                   "head.hip", "tail.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip", "api.cpp"]
 
 

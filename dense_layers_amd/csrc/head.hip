@@ -15,37 +15,13 @@
 // tiles and keeps its slice in registers, at most 256 slices).  The logits
 // never reach HBM.  The slices of all workgroups are added in slice order by
 // the optimizer kernel of the step, exactly as split-K partials are.
-#include "common.hpp"
+#include "head_rows.hpp"
 
 namespace dl {
 namespace {
 
-constexpr int kHeadThreads = 512;
-constexpr int kHeadTPR = 16;                       // threads per row
-constexpr int kHeadRows = kHeadThreads / kHeadTPR;  // rows per tile
-constexpr int kHeadCMax = 16;
-constexpr int kHeadKMax = 256;
-constexpr int kHeadMaxSlices = 256;                // workgroups (dW / db partial slices)
-constexpr int kHeadPairs = kHeadKMax * (kHeadCMax / 4) / kHeadThreads;  // (k, 4 classes) per thread
-constexpr int kHeadLoads = kHeadRows * kHeadKMax / kHeadThreads;       // tile floats per thread
-
-// DPP move of v from the lane CTRL selects within its row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over each row of 16 lanes, left in every lane of the row, by DPP
-// moves (swap neighbours, swap pairs, mirror each half of 8, mirror the 16)
-// instead of LDS-routed shuffles.  Each lane adds the same two operands at
-// every step (in swapped order), so all 16 results are bit-identical.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
-}
+constexpr int kHeadLoads = kHeadRows * kHeadKMax / kHeadThreads;  // tile floats per thread
+constexpr int KP = kHeadKMax + 1;  // padded row stride of the row tiles
 
 // Workgroup b takes row tiles [b * tiles_per, (b + 1) * tiles_per).  VEC:
 // K % 4 == 0 and H, dH 16-byte aligned (tile moved as float4).
@@ -57,42 +33,18 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
                  float* __restrict__ dW_part, float* __restrict__ db_part, float invB,
                  const float* dscale) {
   if (dscale != nullptr) invB *= *dscale;  // loss scale
-  constexpr int KP = kHeadKMax + 1;  // padded row stride of the row tiles
   // W transposed, classes padded to 16 with zeros: Wt[k][c]
   __shared__ __attribute__((aligned(16))) float Wt[kHeadKMax * kHeadCMax];
   __shared__ float Hs[kHeadRows * KP];
   __shared__ float Gs[kHeadRows * KP];
   __shared__ __attribute__((aligned(16))) float Ds[kHeadRows * kHeadCMax];
+  __shared__ float Bc[kHeadCMax];
   const int tid = threadIdx.x;
   const int r = tid / kHeadTPR, lr = tid % kHeadTPR;
-  {
-    // all loads of W in flight before the first LDS store
-    float wr[kHeadKMax * kHeadCMax / kHeadThreads];
-#pragma unroll
-    for (int j = 0; j < kHeadKMax * kHeadCMax / kHeadThreads; ++j) {
-      const int i = tid + j * kHeadThreads;
-      const int k = i / kHeadCMax, c = i % kHeadCMax;
-      wr[j] = (k < K && c < C) ? W[(int64_t)c * K + k] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kHeadKMax * kHeadCMax / kHeadThreads; ++j) Wt[tid + j * kHeadThreads] = wr[j];
-  }
-  float bc[kHeadCMax];
-#pragma unroll
-  for (int c = 0; c < kHeadCMax; ++c) bc[c] = c < C ? bias[c] : 0.f;
-
-  // this thread's (k, 4-class group) pairs of the dW slice
-  int pk[kHeadPairs], pc[kHeadPairs];
-  float acc[kHeadPairs][4];
-#pragma unroll
-  for (int j = 0; j < kHeadPairs; ++j) {
-    const int p = tid + j * kHeadThreads;
-    pk[j] = p % K;
-    pc[j] = p < K * (kHeadCMax / 4) ? (p / K) * 4 : -1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[j][e] = 0.f;
-  }
-  float dbacc = 0.f;  // threads < C: db of class tid
+  head_load_wt(W, Wt, tid, K, C);
+  if (tid < kHeadCMax) Bc[tid] = tid < C ? bias[tid] : 0.f;
+  HeadSlice sl;
+  sl.init(tid, K);
 
   const int64_t ntiles = (B + kHeadRows - 1) / kHeadRows;
   const int64_t t_end = min<int64_t>(ntiles, ((int64_t)blockIdx.x + 1) * tiles_per);
@@ -144,82 +96,13 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     }
     __syncthreads();
 
-    const bool valid = y >= 0 && y < C;
-    float z[kHeadCMax];
-#pragma unroll
-    for (int c = 0; c < kHeadCMax; ++c) z[c] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
-      const int k = lr + kk * kHeadTPR;
-      if (k >= K) break;
-      const float h = Hs[r * KP + k];
-#pragma unroll
-      for (int c4 = 0; c4 < kHeadCMax / 4; ++c4) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kHeadCMax + c4 * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[c4 * 4 + e] += h * w[e];
-      }
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < kHeadCMax; ++c) {
-      z[c] = row16_sum(z[c]);
-      z[c] += bc[c];
-      if (c < C) m = fmaxf(m, z[c]);
-    }
-    float s = 0.f, zy = 0.f;
-#pragma unroll
-    for (int c = 0; c < kHeadCMax; ++c) {
-      if (c == y) zy = z[c];
-      z[c] = c < C ? __expf(z[c] - m) : 0.f;
-      s += z[c];
-    }
-    const float inv_s = 1.0f / s;
-    if (active && lr == 0) row_loss[r0 + r] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
     float g[kHeadCMax];
-#pragma unroll
-    for (int c = 0; c < kHeadCMax; ++c)
-      g[c] = (active && c < C) ? (z[c] * inv_s - (c == y ? 1.0f : 0.0f)) * invB : 0.f;
-    if (lr < kHeadCMax / 4) {
-      // lane lr of the row stores classes 4 lr .. 4 lr + 3
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c4 = 0; c4 < kHeadCMax / 4; ++c4)
-        if (c4 == lr) x = f32x4{g[4 * c4], g[4 * c4 + 1], g[4 * c4 + 2], g[4 * c4 + 3]};
-      *reinterpret_cast<f32x4*>(&Ds[r * kHeadCMax + lr * 4]) = x;
-    }
-    if (dH != nullptr) {
-#pragma unroll
-      for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
-        const int k = lr + kk * kHeadTPR;
-        if (k >= K) break;
-        float d = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < kHeadCMax / 4; ++c4) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kHeadCMax + c4 * 4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d += g[c4 * 4 + e] * w[e];
-        }
-        Gs[r * KP + k] = d * act_deriv(prev_act, Hs[r * KP + k]);
-      }
-    }
+    head_row_loss<KP>(Hs, Wt, Bc, Ds, r, lr, K, C, y, active, invB, row_loss, r0 + r, g);
+    if (dH != nullptr) head_row_dx<KP>(Hs, Wt, Gs, r, lr, K, prev_act, g);
     __syncthreads();
 
     // this tile's rows, in order, into the workgroup's dW / db slice
-#pragma unroll
-    for (int j = 0; j < kHeadPairs; ++j) {
-      if (pc[j] < 0) continue;
-      float a0 = acc[j][0], a1 = acc[j][1], a2 = acc[j][2], a3 = acc[j][3];
-#pragma unroll 8
-      for (int q = 0; q < kHeadRows; ++q) {
-        const float h = Hs[q * KP + pk[j]];
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&Ds[q * kHeadCMax + pc[j]]);
-        a0 += d[0] * h; a1 += d[1] * h; a2 += d[2] * h; a3 += d[3] * h;
-      }
-      acc[j][0] = a0; acc[j][1] = a1; acc[j][2] = a2; acc[j][3] = a3;
-    }
-    if (tid < C)
-      for (int q = 0; q < kHeadRows; ++q) dbacc += Ds[q * kHeadCMax + tid];
+    sl.add_tile<KP>(Hs, Ds, tid, C);
     if (dH != nullptr) {
       float* dst = dH + r0 * K;
       if (VEC) {
@@ -246,15 +129,7 @@ head_xent_kernel(int64_t B, int K, int C, int64_t tiles_per, const float* H, flo
     }
   }
 
-  float* dWp = dW_part + (int64_t)blockIdx.x * C * K;
-#pragma unroll
-  for (int j = 0; j < kHeadPairs; ++j) {
-    if (pc[j] < 0) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (pc[j] + e < C) dWp[(int64_t)(pc[j] + e) * K + pk[j]] = acc[j][e];
-  }
-  if (tid < C) db_part[(int64_t)blockIdx.x * C + tid] = dbacc;
+  sl.store(dW_part, db_part, blockIdx.x, tid, K, C);
 }
 
 }  // namespace

@@ -26,37 +26,20 @@
 // (at most 128 registers) when the workgroup starts and keeps them for every
 // row tile, so its chain of MFMAs never waits on memory; the dX operand
 // streams in chunks, the first requested before the head runs.
-#include "common.hpp"
+#include "head_rows.hpp"
 
 namespace dl {
 namespace {
 
-constexpr int kTailThreads = 512;
-constexpr int kTailRows = 32;
-constexpr int kTailTPR = kTailThreads / kTailRows;  // 16 threads per row (head)
-constexpr int kTailDMax = 256;                      // h and n
-constexpr int kTailCMax = 16;
-constexpr int kTailMaxSlices = 256;
+constexpr int kTailThreads = kHeadThreads;  // the head's 16 threads per row of 32
+constexpr int kTailRows = kHeadRows;
+constexpr int kTailDMax = 256;              // h and n
+constexpr int kTailMaxSlices = kHeadMaxSlices;
 constexpr int kTS = kTailDMax + 4;  // LDS row stride (floats): 16-byte aligned rows
-constexpr int kTailPairs = kTailDMax * (kTailCMax / 4) / kTailThreads;
 constexpr int kTailVecs = kTailRows * kTailDMax / 4 / kTailThreads;  // float4 per thread per tile
 constexpr int kGroups = kTailDMax / 8;  // k groups of 8 in the longest contraction
 constexpr int kChunk = 4;               // k groups per streamed dX operand chunk
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over each row of 16 lanes, left in every lane of the row (the DPP
-// butterfly of the head kernel: the same operands at every step).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_mov<0xB1>(v);
-  v += dpp_mov<0x4E>(v);
-  v += dpp_mov<0x141>(v);
-  v += dpp_mov<0x140>(v);
-  return v;
-}
+static_assert(kTailRows == 32, "one 32x32 MFMA block of rows per tile");
 
 // The thread index made opaque, so that the row / column of each element in
 // the copies below is computed where it is used rather than hoisted out of
@@ -216,14 +199,14 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
   __shared__ __attribute__((aligned(16))) float Xs[kTailRows * kTS];  // Hin, then dH
   __shared__ __attribute__((aligned(16))) float Hs[kTailRows * kTS];  // H
   __shared__ __attribute__((aligned(16))) float Gs[kTailRows * kTS];  // G1
-  __shared__ __attribute__((aligned(16))) float Wt[kTailDMax * kTailCMax];
-  __shared__ __attribute__((aligned(16))) float Ds[kTailRows * kTailCMax];
-  __shared__ float Bc[kTailCMax];
+  __shared__ __attribute__((aligned(16))) float Wt[kHeadKMax * kHeadCMax];
+  __shared__ __attribute__((aligned(16))) float Ds[kTailRows * kHeadCMax];
+  __shared__ float Bc[kHeadCMax];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int r = tid / kTailTPR, lr = tid % kTailTPR;
+  const int r = tid / kHeadTPR, lr = tid % kHeadTPR;
   const int K = N1;  // the head's input width
   const int w1bytes = N1 * K1 * 4;
   const __amdgpu_buffer_rsrc_t w1res = buffer_of(W1, w1bytes);
@@ -244,18 +227,8 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
   }
   const float fbias = (f_has && fcol < N1) ? b1[fcol] : 0.f;
   if (dscale != nullptr) invB *= *dscale;  // loss scale
-  {
-    float wr[kTailDMax * kTailCMax / kTailThreads];
-#pragma unroll
-    for (int j = 0; j < kTailDMax * kTailCMax / kTailThreads; ++j) {
-      const int i = tid + j * kTailThreads;
-      const int k = i / kTailCMax, c = i % kTailCMax;
-      wr[j] = (k < K && c < C) ? W2[(int64_t)c * K + k] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kTailDMax * kTailCMax / kTailThreads; ++j) Wt[tid + j * kTailThreads] = wr[j];
-  }
-  if (tid < kTailCMax) Bc[tid] = tid < C ? b2[tid] : 0.f;
+  head_load_wt(W2, Wt, tid, K, C);
+  if (tid < kHeadCMax) Bc[tid] = tid < C ? b2[tid] : 0.f;
 
   // dX: wave w owns columns 32 w .. 32 w + 31 of dH
   const bool x_has = HAS_DX && wave * 32 < K1;
@@ -267,17 +240,8 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
   xo.groups = N1 / 8;
   xo.voff = xcol < K1 ? (4 * h * K1 + xcol) * 4 : w1bytes;
 
-  int pk[kTailPairs], pc[kTailPairs];
-  float acc2[kTailPairs][4];
-#pragma unroll
-  for (int j = 0; j < kTailPairs; ++j) {
-    const int p = tid + j * kTailThreads;
-    pk[j] = p % K;
-    pc[j] = p < K * (kTailCMax / 4) ? (p / K) * 4 : -1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc2[j][e] = 0.f;
-  }
-  float dbacc = 0.f;
+  HeadSlice sl;
+  sl.init(tid, K);
   const float* arow_x = Xs + l32 * kTS + 4 * h;
   const float* arow_g = Gs + l32 * kTS + 4 * h;
 
@@ -329,79 +293,15 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
     __syncthreads();
 
     // ---- head: logits, softmax cross-entropy, g, G1 = (W2^T g) act1'(H)
-    const bool valid = y >= 0 && y < C;
-    float z[kTailCMax];
-#pragma unroll
-    for (int c = 0; c < kTailCMax; ++c) z[c] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < kTailDMax / kTailTPR; ++kk) {
-      const int k = lr + kk * kTailTPR;
-      if (k >= K) break;
-      const float hv = Hs[r * kTS + k];
-#pragma unroll
-      for (int c4 = 0; c4 < kTailCMax / 4; ++c4) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kTailCMax + c4 * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[c4 * 4 + e] += hv * w[e];
-      }
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < kTailCMax; ++c) {
-      z[c] = row16_sum(z[c]);
-      z[c] += Bc[c];
-      if (c < C) m = fmaxf(m, z[c]);
-    }
-    float s = 0.f, zy = 0.f;
-#pragma unroll
-    for (int c = 0; c < kTailCMax; ++c) {
-      if (c == y) zy = z[c];
-      z[c] = c < C ? __expf(z[c] - m) : 0.f;
-      s += z[c];
-    }
-    const float inv_s = 1.0f / s;
-    if (active && lr == 0) row_loss[r0 + r] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
-    float g[kTailCMax];
-#pragma unroll
-    for (int c = 0; c < kTailCMax; ++c)
-      g[c] = (active && c < C) ? (z[c] * inv_s - (c == y ? 1.0f : 0.0f)) * invB : 0.f;
-    if (lr < kTailCMax / 4) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c4 = 0; c4 < kTailCMax / 4; ++c4)
-        if (c4 == lr) x = f32x4{g[4 * c4], g[4 * c4 + 1], g[4 * c4 + 2], g[4 * c4 + 3]};
-      *reinterpret_cast<f32x4*>(&Ds[r * kTailCMax + lr * 4]) = x;
-    }
-#pragma unroll
-    for (int kk = 0; kk < kTailDMax / kTailTPR; ++kk) {
-      const int k = lr + kk * kTailTPR;
-      if (k >= K) break;
-      float d = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < kTailCMax / 4; ++c4) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(&Wt[k * kTailCMax + c4 * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d += g[c4 * 4 + e] * w[e];
-      }
-      Gs[r * kTS + k] = d * act_deriv(act1, Hs[r * kTS + k]);
+    {
+      float g[kHeadCMax];
+      head_row_loss<kTS>(Hs, Wt, Bc, Ds, r, lr, K, C, y, active, invB, row_loss, r0 + r, g);
+      head_row_dx<kTS>(Hs, Wt, Gs, r, lr, K, act1, g);
     }
     __syncthreads();
 
     // this tile's rows, in order, into the workgroup's dW2 / db2 slice
-#pragma unroll
-    for (int j = 0; j < kTailPairs; ++j) {
-      if (pc[j] < 0) continue;
-      float a0 = acc2[j][0], a1 = acc2[j][1], a2 = acc2[j][2], a3 = acc2[j][3];
-#pragma unroll 8
-      for (int q = 0; q < kTailRows; ++q) {
-        const float hv = Hs[q * kTS + pk[j]];
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&Ds[q * kTailCMax + pc[j]]);
-        a0 += d[0] * hv; a1 += d[1] * hv; a2 += d[2] * hv; a3 += d[3] * hv;
-      }
-      acc2[j][0] = a0; acc2[j][1] = a1; acc2[j][2] = a2; acc2[j][3] = a3;
-    }
-    if (tid < C)
-      for (int q = 0; q < kTailRows; ++q) dbacc += Ds[q * kTailCMax + tid];
+    sl.add_tile<kTS>(Hs, Ds, tid, C);
     tile_store(Gs, G1 + r0 * N1, nrows * N1, N1, tid);
 
     // ---- dX of the hidden layer: dH = (G1 W1) act0'(Hin), over Hin in LDS
@@ -421,21 +321,13 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
     }
   }
 
-  float* dWp = dW_part + (int64_t)blockIdx.x * C * K;
-#pragma unroll
-  for (int j = 0; j < kTailPairs; ++j) {
-    if (pc[j] < 0) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (pc[j] + e < C) dWp[(int64_t)(pc[j] + e) * K + pk[j]] = acc2[j][e];
-  }
-  if (tid < C) db_part[(int64_t)blockIdx.x * C + tid] = dbacc;
+  sl.store(dW_part, db_part, blockIdx.x, tid, K, C);
 }
 
 }  // namespace
 
 bool mlp_tail_fits(int64_t K1, int64_t N1, int64_t C) {
-  return C >= 1 && C <= kTailCMax && K1 >= 8 && K1 <= kTailDMax && K1 % 8 == 0 && N1 >= 8 &&
+  return C >= 1 && C <= kHeadCMax && K1 >= 8 && K1 <= kTailDMax && K1 % 8 == 0 && N1 >= 8 &&
          N1 <= kTailDMax && N1 % 8 == 0;
 }
 
