@@ -312,7 +312,9 @@ def test_cast_bf16_bit_exact(dl):
 
 XENT_SHAPES = [(1, 1), (5, 10), (64, 10), (8192, 10), (100, 33), (77, 256), (64, 257),
                (130, 1000), (3, 2047), (17, 2049), (8, 4096), (4, 32000), (2, 32001),
-               (3, 40000), (300, 31)]
+               (3, 40000), (300, 31),
+               # a whole-workgroup row whose last waves hold no class at all
+               (9, 2052)]
 
 
 @pytest.mark.parametrize("shape", XENT_SHAPES)
