@@ -8,7 +8,8 @@
 // wave for TPR <= 64, the whole workgroup of 1024 threads for wide rows).  Each
 // thread keeps its slice of the row in registers, so HBM sees one read and
 // one write per logit; row max, sum of exponentials and the label's logit are
-// combined with cross-lane shuffles (plus LDS across waves for TPR = 256).
+// combined with cross-lane shuffles (plus LDS across waves when a workgroup
+// owns the row).
 //   lse = max + log(sum exp(z - max)),  loss_i = lse - z[y_i],
 //   dlogits = (exp(z - max) / sum - [c == y_i]) / B.
 // Per-row losses go to a buffer and a single workgroup sums them in a fixed
@@ -146,6 +147,67 @@ xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restric
   }
 }
 
+// One row per workgroup of BLOCK threads (C % 4 == 0, C <= BLOCK * NI * 4),
+// NI float4 of the row per thread, addressed through buffer resources over
+// the row (base and size in scalar registers, no 64-bit address per item).
+// An item past the row gets the per-lane offset C * 4 (the range check
+// applies to the per-lane offset, not to the uniform one): its load returns
+// zero, kept out of the max, and its store is dropped.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int BLOCK, int NI>
+__global__ void __launch_bounds__(BLOCK)
+xent_row_wg_kernel(int C, const float* logits, const int32_t* __restrict__ labels,
+                   float* __restrict__ row_loss, float* dlogits, float invB,
+                   const float* dscale) {
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
+  __shared__ float red[2 * BLOCK / 64];
+  const int64_t row = blockIdx.x;
+  const int y = labels[row];
+  const bool valid = (y >= 0) && (y < C);
+  const __amdgpu_buffer_rsrc_t in = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(logits + row * C), 0, C * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t out =
+      __builtin_amdgcn_make_buffer_rsrc(dlogits + row * C, 0, C * 4, 0x00020000);
+  auto item_off = [&](int j) {
+    const int c0 = (int)(threadIdx.x + j * BLOCK) * 4;
+    return c0 < C ? c0 * 4 : C * 4;
+  };
+  f32x4 v[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(in, item_off(j), 0, 0));
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    if ((int)(threadIdx.x + j * BLOCK) * 4 < C)
+      m = fmaxf(fmaxf(m, fmaxf(v[j][0], v[j][1])), fmaxf(v[j][2], v[j][3]));
+  m = group_max<BLOCK, BLOCK>(m, red);
+  float s = 0.f, zy = 0.f;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int c0 = (int)(threadIdx.x + j * BLOCK) * 4;
+    if (c0 < C) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c0 + e == y) zy = v[j][e];
+        v[j][e] = __expf(v[j][e] - m);
+        s += v[j][e];
+      }
+    }
+  }
+  group_sum2<BLOCK, BLOCK>(s, zy, red);
+  if (threadIdx.x == 0) row_loss[row] = valid ? (m + __logf(s)) - zy : __builtin_nanf("");
+  const float inv_s = 1.0f / s;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int c0 = (int)(threadIdx.x + j * BLOCK) * 4;
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (v[j][e] * inv_s - (c0 + e == y ? 1.0f : 0.0f)) * invB;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), out, item_off(j), 0, 0);
+  }
+}
+
 // Rows too wide to cache in registers: one workgroup per row, two passes
 // (the second read normally hits L2 / the 256 MB Infinity Cache).
 __global__ void __launch_bounds__(kXentBlock)
@@ -229,8 +291,11 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
   else if (C <= 2048)
     e = vec ? launch_rows<64, 8, true>(B, C, logits, labels, row_loss, dlogits, dscale, s)
             : launch_rows<64, 32, false>(B, C, logits, labels, row_loss, dlogits, dscale, s);
-  else if (vec && C <= 32768)  // 1024 threads per row: 8 float4 each, more loads in flight
-    e = launch_rows<1024, 8, true, 1024>(B, C, logits, labels, row_loss, dlogits, dscale, s);
+  else if (vec && C <= 32768) {  // a workgroup of 1024 threads per row, 8 float4 each
+    hipLaunchKernelGGL((xent_row_wg_kernel<1024, 8>), dim3((unsigned)B), dim3(1024), 0, s, (int)C,
+                       logits, labels, row_loss, dlogits, (float)(1.0 / (double)B), dscale);
+    e = hipGetLastError();
+  }
   else {
     hipLaunchKernelGGL(xent_rows_wide_kernel, dim3((unsigned)B), dim3(kXentBlock), 0, s, B, C,
                        logits, labels, row_loss, dlogits, (float)(1.0 / (double)B), dscale);
