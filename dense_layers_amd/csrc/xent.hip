@@ -152,8 +152,11 @@ xent_rows_kernel(int64_t B, int C, const float* logits, const int32_t* __restric
 // the row (base and size in scalar registers, no 64-bit address per item).
 // An item past the row gets the per-lane offset C * 4 (the range check
 // applies to the per-lane offset, not to the uniform one): its load returns
-// zero, kept out of the max, and its store is dropped.
+// zero, kept out of the max, and its store is dropped.  The loads carry the
+// non-temporal cache hint (each logit is read once); the stores do not (the
+// hint on the stores, alone or with the loads, measured slower).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kNontemporal = 2;  // cache-policy operand of a buffer access: nt
 template <int BLOCK, int NI>
 __global__ void __launch_bounds__(BLOCK)
 xent_row_wg_kernel(int C, const float* logits, const int32_t* __restrict__ labels,
@@ -175,7 +178,7 @@ xent_row_wg_kernel(int C, const float* logits, const int32_t* __restrict__ label
   f32x4 v[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j)
-    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(in, item_off(j), 0, 0));
+    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(in, item_off(j), 0, kNontemporal));
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NI; ++j)
