@@ -1,9 +1,12 @@
 """Throughput of the dense-layer training path on one MI355X.
 
-Default workload: the 784-256-128-10 ReLU MLP, batch 8192, AdamW(lr 1e-3,
-betas (0.9, 0.999), wd 0.01) on one fixed synthetic batch; a step is one full
-forward / softmax-xent / backward / AdamW update through mlp_train_step.
-Other workloads (--config) are measured the same way for the design notes.
+Default workload: the classifier head, the largest of the five workloads:
+X [65536, 768] float32 -> Linear 768 -> 32000 -> softmax cross-entropy over
+32000 classes, dX, dW and db, and an AdamW(lr 1e-3, betas (0.9, 0.999),
+wd 0.01) update of W and b.  A step is that whole pass over one batch
+(9.66e12 GEMM flop).  The other workloads (--config: the 784-256-128-10 MLP
+at batch 64 and 8192, the wide 1024-4096^3-1000 MLP, the bf16 transformer-MLP
+block, and the optimizer / loss variants) are measured the same way.
 
 Prints one JSON line: whole-step throughput (train steps/s), the step's
 algorithmic GEMM TFLOP/s, the time of every launch inside the step (a short
@@ -65,6 +68,22 @@ def stored_traffic(workload: str, stage: str):
     if rec.get("source_hash") != kernel_source_hash() or rec.get("stage") != stage:
         return None
     return rec.get("traffic_bytes")
+
+
+def gemm_bytes(kind, M, N, K, es=4, bias=False, z=False, mask=False, db=False):
+    """Algorithmic HBM bytes of one GEMM launch: each tensor it must read or
+    write, once (operands in es-byte elements, float32 weight gradients);
+    split-K partial slices are the kernel's own scratch and not counted.
+      fwd: read X [M, K], W [N, K] (+ b), write Y [M, N] (+ Z)
+      dx:  read G [M, K], W [K, N] (+ the saved activation [M, N]), write dX
+      dw:  read G [K, M], X [K, N], write dW [M, N] float32 (+ db [M])"""
+    if kind == "fwd":
+        return es * (M * K + N * K + M * N * (2 if z else 1)) + (4 * N if bias else 0)
+    if kind == "dx":
+        return es * (M * K + K * N + M * N * (2 if mask else 1))
+    if kind == "dw":
+        return es * (K * M + K * N) + 4 * M * N + (4 * M if db else 0)
+    raise ValueError(kind)
 
 
 def _split(label):
@@ -183,6 +202,62 @@ class MLPBench:
             return None
         return "flop", 2 * B * w.dims[l] * w.dims[l + 1]
 
+    def stage_bytes(self, label):
+        """Algorithmic bytes of a GEMM launch of the step (for the traffic
+        ratio of the roofline entry), or None."""
+        w = self.w
+        B = w.batch
+        name, k = _split(label)
+        layer = self._layers_of_labels()
+        d = w.dims
+        if name == "fwd_gemm":
+            return gemm_bytes("fwd", B, d[k + 1], d[k], bias=True)
+        if name == "dw_gemm":
+            l = layer[label]
+            return gemm_bytes("dw", d[l + 1], d[l], B, db=True)
+        if name == "dx_gemm":
+            l = layer[label]
+            return gemm_bytes("dx", B, d[l], d[l + 1], mask=True)
+        if name == "dwdx_gemm":
+            l = layer[label]
+            return (gemm_bytes("dw", d[l + 1], d[l], B, db=True)
+                    + gemm_bytes("dx", B, d[l], d[l + 1], mask=True))
+        if name == "dwdw_gemm":
+            l = layer[label]
+            return (gemm_bytes("dw", d[l + 1], d[l], B, db=True)
+                    + gemm_bytes("dw", d[l], d[l - 1], B, db=True))
+        return None
+
+    # rows of the batch the CPU oracle takes per sampled step (the wide MLP's
+    # full 16384-row step is minutes of float64 work)
+    CPU_ROWS = {"mlp_wide": 512}
+
+    def cpu_sample(self, budget_s):
+        """Oracle training steps on the first `rows` rows of the batch,
+        repeated for the budget; the update of all parameters is timed on its
+        own, so a step is (sampled step - update) x batch / rows + update."""
+        import oracle as O
+        w = self.w
+        inp = si.generate(w)
+        rows = min(w.batch, self.CPU_ROWS.get(w.name, w.batch))
+        st = O.MLPState(inp.W, inp.b)
+        X, y = inp.X[:rows], inp.labels[:rows]
+        t0 = time.perf_counter()
+        for arrs, ms, vs in ((st.W, st.mW, st.vW), (st.b, st.mb, st.vb)):
+            for a, m_, v_ in zip(arrs, ms, vs):
+                O.optimizer_update(w.optim.kind, a, np.zeros_like(a), m_, v_, w.optim, 1,
+                                   w.optim.lr)
+        t_upd = time.perf_counter() - t0
+        n, el = _timed_loop(lambda i: O.mlp_train_step(st, X, y, w.acts, w.optim), budget_s)
+        per = el / n
+        step = per if rows == w.batch else max(per - t_upd, 0.0) * w.batch / rows + t_upd
+        return 1.0 / step, (f"{n} {w.optim.kind} training steps of the "
+                            f"{'-'.join(map(str, w.dims))} MLP on {rows} of the {w.batch} rows"
+                            + ("" if rows == w.batch else
+                               f", scaled by {w.batch}/{rows} less the update of all parameters "
+                               f"({t_upd * 1e3:.0f} ms, counted once)")
+                            + " (float64 NumPy oracle)")
+
 
 class TmlpBench:
     """Transformer-MLP block shapes, 16-bit operands (bf16, or half for the
@@ -238,6 +313,49 @@ class TmlpBench:
             return "byte", 8 * d * f
         return None
 
+    def stage_bytes(self, label):
+        T, d, f = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, k = _split(label)
+        # launch order: fwd 1024->4096 (GELU, Z saved), fwd 4096->1024; the
+        # vjps of layer 2 (dW2, then dX = dZ1 with gelu'(Z1)) and layer 1
+        if name == "fwd_gemm":
+            return gemm_bytes("fwd", T, f, d, 2, bias=True, z=True) if k == 0 else \
+                gemm_bytes("fwd", T, d, f, 2, bias=True)
+        if name == "dw_gemm":
+            return gemm_bytes("dw", d, f, T, 2, db=True) if k == 0 else \
+                gemm_bytes("dw", f, d, T, 2, db=True)
+        if name == "dx_gemm":
+            return gemm_bytes("dx", T, f, d, 2, mask=True) if k == 0 else \
+                gemm_bytes("dx", T, d, f, 2)
+        return None
+
+    def cpu_sample(self, budget_s):
+        """The oracle's forward and both vjps on a sample of the tokens, with
+        every boundary tensor rounded to the 16-bit format, scaled by
+        tokens / sample."""
+        import oracle as O
+        w = self.w
+        inp = si.generate(w)
+        rows = 512
+        r = O.round_bf16 if w.dtype == "bf16" else O.round_f16_sat
+        X, dY = inp.X[:rows], inp.dY[:rows]
+
+        def one(i):
+            W1, W2 = r(inp.W[0]), r(inp.W[1])
+            _, Z1 = O.dense_act_fwd(X, W1, inp.b[0], O.ACT_GELU_TANH)
+            H = r(O.act_fwd(Z1, O.ACT_GELU_TANH))
+            r(O.dense_act_fwd(H, W2, inp.b[1], O.ACT_IDENTITY)[0])
+            dH, _, _ = O.dense_act_vjp(dY, None, H, W2, O.ACT_IDENTITY)
+            dZ = r(dH * O.act_grad(r(Z1), O.ACT_GELU_TANH))
+            dX, _, _ = O.dense_act_vjp(dZ, None, X, W1, O.ACT_IDENTITY)
+            r(dX)
+
+        n, el = _timed_loop(one, budget_s)
+        return 1.0 / (el / n * w.batch / rows), (
+            f"{n} forward + vjp passes of the {'-'.join(map(str, w.dims))} block on {rows} of "
+            f"the {w.batch} tokens, scaled by {w.batch}/{rows} (float64 NumPy oracle, "
+            f"{w.dtype} rounding at the boundaries)")
+
 
 class HeadBench:
     """Classifier head: Linear 768 -> 32000, softmax-xent, dX/dW/db, AdamW."""
@@ -287,6 +405,53 @@ class HeadBench:
             return "byte", 28 * (C * d if k == 0 else C)
         return None
 
+    def stage_bytes(self, label):
+        B, d, C = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, _ = _split(label)
+        if name == "fwd_gemm":
+            return gemm_bytes("fwd", B, C, d, bias=True)
+        if name == "dx_gemm":
+            return gemm_bytes("dx", B, d, C)
+        if name == "dw_gemm":
+            return gemm_bytes("dw", C, d, B, db=True)
+        return None
+
+    def cpu_sample(self, budget_s):
+        """The oracle's forward, softmax-xent and vjp on blocks of 256 rows
+        (cycling through the batch, the divisor the whole batch) for the
+        budget, scaled to the batch, plus one AdamW update of W and b timed
+        on its own."""
+        import oracle as O
+        w = self.w
+        inp = si.generate(w)
+        B = w.batch
+        rows = 256
+        W, b, y = inp.W[0].astype(np.float64), inp.b[0].astype(np.float64), inp.labels
+        o = w.optim
+
+        def one(i):
+            r0 = (i * rows) % B
+            Xc = inp.X[r0:r0 + rows]
+            _, Z = O.dense_act_fwd(Xc, W, b, O.ACT_IDENTITY)
+            _, dz, _ = O.softmax_xent_fwd_bwd(Z, y[r0:r0 + rows], batch_total=B)
+            O.dense_act_vjp(dz, None, Xc, W, O.ACT_IDENTITY)
+
+        n, el = _timed_loop(one, budget_s)
+        t0 = time.perf_counter()
+        for p in (W, b):
+            z0 = np.zeros_like(p)
+            O.adamw_step(p, z0, z0, z0, o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, 1)
+        t_upd = time.perf_counter() - t0
+        step = el / (n * rows) * B + t_upd
+        return 1.0 / step, (
+            f"forward + softmax-xent + vjp of {n} blocks of {rows} rows ({n * rows} of the {B} "
+            f"rows of one step), scaled to {B} rows, plus one AdamW update of the "
+            f"{C_params(w)} parameters ({t_upd:.2f} s) (float64 NumPy oracle)")
+
+
+def C_params(w):
+    return w.n_params()
+
 
 class OptBench:
     """The fused multi-array optimizer step over the wide MLP's parameters
@@ -329,6 +494,36 @@ class OptBench:
             return "byte", 38 * self.n
         return None
 
+    def stage_bytes(self, label):
+        return None
+
+    def cpu_sample(self, budget_s):
+        """The oracle's clipped, loss-scaled AdamW update with parameter
+        averages and bf16 copies over a 4M-element sample of the
+        parameters, scaled to all of them."""
+        import oracle as O
+        w = self.w
+        o = w.optim
+        n = 1 << 22
+        rng = np.random.default_rng(0)
+        p = rng.standard_normal(n).astype(np.float32).astype(np.float64)
+        g = (rng.standard_normal(n) * 0.05 * 1024.0).astype(np.float32).astype(np.float64)
+        m, v, e = np.zeros(n), np.zeros(n), p.copy()
+
+        def one(i):
+            found, norm, mul = O.grad_control([g], 1.0, 1024.0)
+            w1, m1, v1 = O.adamw_step(p, mul * g, m, v, o.lr, o.beta1, o.beta2, o.eps,
+                                      o.weight_decay, i + 1)
+            w1 = O.round_f32(w1)
+            O.round_f32(m1), O.round_f32(v1)
+            O.round_f32(O.ema_update(e, w1, 0.999))
+            O.round_bf16(w1)
+
+        k, el = _timed_loop(one, budget_s)
+        return 1.0 / (el / k * self.n / n), (
+            f"{k} updates of a {n}-element sample (norm, finite check, AdamW, average, bf16 "
+            f"copy), scaled to the {self.n} parameters (float64 NumPy oracle)")
+
 
 class MseBench:
     """Mean squared error forward + backward over [16384, 4096] float32."""
@@ -354,6 +549,21 @@ class MseBench:
             return "byte", 12 * self.w.batch * self.w.dims[0]
         return None
 
+    def stage_bytes(self, label):
+        return None
+
+    def cpu_sample(self, budget_s):
+        """The oracle's MSE forward + backward on 1024 of the rows, scaled."""
+        import oracle as O
+        B, C = self.w.batch, self.w.dims[0]
+        rows = 1024
+        p = si.random_matrix(self.w.seed, (B, C))[:rows]
+        t = si.random_matrix(self.w.seed + 1, (B, C))[:rows]
+        k, el = _timed_loop(lambda i: O.mse_loss_fwd_bwd(p, t), budget_s)
+        return 1.0 / (el / k * B / rows), (
+            f"{k} MSE forward + backward passes over {rows} of the {B} rows, scaled "
+            f"(float64 NumPy oracle)")
+
 
 # Workloads of the optimizer and loss variants (parameter shapes of the wide
 # MLP; a [16384, 4096] regression output), beside the five step workloads.
@@ -377,26 +587,45 @@ DEFAULTS = {"mlp_small": (200, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
             "tmlp_f16": (20, 3)}
 
 
-def cpu_baseline(w, budget_s: float):
-    """The float64 oracle (as it stands) on a bounded sample of the same
-    workload: whole training steps on the full batch, repeated until the time
-    budget is spent (at least one)."""
-    import oracle as O
+def host_cpu():
+    """(cores this process may run on, BLAS threads NumPy uses, CPU model)."""
     from threadpoolctl import threadpool_info
-    inp = si.generate(w)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    st = O.MLPState(inp.W, inp.b)
+    cores = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, blas, model
+
+
+def _timed_loop(fn, budget_s: float):
+    """Call fn() until budget_s has passed (at least once); (calls, seconds)."""
     t0 = time.perf_counter()
     n = 0
     while True:
-        O.mlp_train_step(st, inp.X, inp.labels, w.acts, w.optim)
+        fn(n)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    el = time.perf_counter() - t0
-    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full {w.batch}-sample {w.optim.kind} training steps of the "
-                      f"{'-'.join(map(str, w.dims))} MLP (float64 NumPy, BLAS threads)"}
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(bench, budget_s: float):
+    """The float64 oracle, as it stands, on a bounded sample of the bench's
+    workload, scaled to whole steps per second (see each bench's
+    cpu_sample)."""
+    cores, blas, model = host_cpu()
+    value, sample = bench.cpu_sample(budget_s)
+    return {"value": value, "unit": "steps/s", "cores": blas, "kind": "oracle",
+            "sample": sample, "host_cores": cores, "cpu_model": model,
+            "threads_note": "BLAS products on the reported threads, NumPy elementwise work "
+                            "on one"}
 
 
 def profile_stages(dl, bench, n_steps):
@@ -432,7 +661,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="mlp_adamw", choices=sorted(BENCHES))
+    ap.add_argument("--config", default="head_xent", choices=sorted(BENCHES))
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prof-steps", type=int, default=20)
@@ -499,15 +728,22 @@ def main():
     if "tflops" in dom:
         roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
                     "frac": round(dom["tflops"] / peak, 4), "traffic": traffic,
-                    "kernel": dom["stage"]}
+                    "kernel": dom["stage"], "avg_ms": dom["ms"]}
+        alg = bench.stage_bytes(dom["stage"])
     else:
         roofline = {"bound": "hbm", "achieved": dom.get("gbs"), "peak": PEAK_HBM,
                     "unit": "GB/s", "frac": round((dom.get("gbs") or 0.0) / PEAK_HBM, 4),
-                    "traffic": traffic, "kernel": dom["stage"]}
+                    "traffic": traffic, "kernel": dom["stage"], "avg_ms": dom["ms"]}
+        wk = bench.stage_work(dom["stage"])
+        alg = wk[1] if wk is not None else None
+    if alg is not None:
+        roofline["algorithmic_bytes"] = int(alg)
+        if traffic is not None:
+            roofline["traffic_ratio"] = round(traffic / alg, 3)
 
     cpu = None
-    if not args.no_cpu_baseline and args.config in ("mlp_small", "mlp_adamw"):
-        cpu = cpu_baseline(w, args.cpu_budget)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bench, args.cpu_budget)
 
     line = {
         "metric": METRIC,

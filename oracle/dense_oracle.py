@@ -185,7 +185,7 @@ def dense_act_vjp(dY, Zsaved, X, W, act: int, need_dx: bool = True,
 
     ``mask`` (optional) replaces act'(Z) entirely; it is how a caller adopts
     the other side's ReLU decision for pre-activations within rounding of 0
-    (see ``relu_kink_band``).  Returns (dX or None, dW, db) in float64.
+    (see ``rounding_bands.relu_kink_band``).  Returns (dX or None, dW, db) in float64.
     """
     dY = np.asarray(dY, dtype=np.float64)
     X = np.asarray(X, dtype=np.float64)
@@ -198,29 +198,12 @@ def dense_act_vjp(dY, Zsaved, X, W, act: int, need_dx: bool = True,
     return dX, dW, db
 
 
-def relu_kink_band(X, W, b) -> np.ndarray:
-    """Per-element rounding bound of the float32 pre-activation.
-
-    tau_ij = gamma_K * (sum_k |x_ik w_jk| + |b_j|), gamma_K = K u/(1 - K u),
-    u = 2^-24: the standard bound on a K-term float32 dot product.  Where
-    |z_ij| <= tau_ij, both sides of the ReLU kink are correct results.
-    """
-    X = np.abs(np.asarray(X, dtype=np.float64))
-    W = np.abs(np.asarray(W, dtype=np.float64))
-    K = X.shape[1] + 1
-    u = 2.0 ** -24
-    gamma = K * u / (1.0 - K * u)
-    s = X @ W.T
-    if b is not None:
-        s = s + np.abs(np.asarray(b, dtype=np.float64))[None, :]
-    return gamma * s
-
-
 # ---------------------------------------------------------------------------
 # Softmax cross-entropy, forward and backward
 # ---------------------------------------------------------------------------
 
-def softmax_xent_fwd_bwd(logits, labels) -> Tuple[float, np.ndarray, np.ndarray]:
+def softmax_xent_fwd_bwd(logits, labels, batch_total: Optional[int] = None
+                         ) -> Tuple[float, np.ndarray, np.ndarray]:
     """Mean softmax cross-entropy over the batch and its gradient.
 
     Orthon page, "Selected Orthon vs. PyTorch results" (one fused kernel reads
@@ -229,6 +212,9 @@ def softmax_xent_fwd_bwd(logits, labels) -> Tuple[float, np.ndarray, np.ndarray]
     Per row i with label y_i:  m = max_j z_ij,  s = sum_j exp(z_ij - m),
     lse = m + ln s,  l_i = lse - z_{i,y_i},  p_ij = exp(z_ij - m)/s,
     dz_ij = (p_ij - [j == y_i]) / B,  loss = (1/B) sum_i l_i.
+    B is the number of rows, or ``batch_total`` when these rows are a block
+    of a larger batch (rows are independent, so a batch may be taken in
+    blocks of rows with the divisor of the whole batch).
     Returns (loss, dlogits, per-row loss) in float64.
     """
     z = np.asarray(logits, dtype=np.float64)
@@ -238,6 +224,9 @@ def softmax_xent_fwd_bwd(logits, labels) -> Tuple[float, np.ndarray, np.ndarray]
         raise ValueError("labels must be [B]")
     if np.any(y < 0) or np.any(y >= C):
         raise ValueError("label out of range")
+    n = B if batch_total is None else int(batch_total)
+    if n < B:
+        raise ValueError("batch_total is smaller than the block")
     m = z.max(axis=1, keepdims=True)
     e = np.exp(z - m)
     s = e.sum(axis=1, keepdims=True)
@@ -247,8 +236,18 @@ def softmax_xent_fwd_bwd(logits, labels) -> Tuple[float, np.ndarray, np.ndarray]
     p = e / s
     onehot = np.zeros_like(p)
     onehot[rows, y] = 1.0
-    dz = (p - onehot) / B
-    return float(row_loss.sum() / B), dz, row_loss
+    dz = (p - onehot) / n
+    return float(row_loss.sum() / n), dz, row_loss
+
+
+def softmax_lse(logits) -> np.ndarray:
+    """Per-row log-sum-exp, lse_i = m_i + ln sum_j exp(z_ij - m_i) with
+    m_i = max_j z_ij (the same row statistics as softmax_xent_fwd_bwd; a
+    fused head keeps lse so that its backward can form softmax(z) =
+    exp(z - lse) from the logits again)."""
+    z = np.asarray(logits, dtype=np.float64)
+    m = z.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
 
 
 # ---------------------------------------------------------------------------

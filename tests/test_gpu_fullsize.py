@@ -5,13 +5,20 @@ therefore the same launch plans as bench.py.
   step against the full float64 oracle step.
 * transformer MLP (1024 -> 4096 GELU -> 1024, 32768 tokens, bf16): the
   forward and both vjps against the full float64 oracle.
-* classifier head (65536 x 768 -> 32000): 8.4 GB of logits, more bytes than
-  a 32-bit offset reaches.  The oracle checks sampled rows one by one
-  (row losses, dlogits rows, dX rows); dW and db are checked through
-  properties that hold at any size, evaluated in float64 from the GPU's own
-  dlogits: dW v = dlogits^T (X v) for random v, and db = column sums of
-  dlogits.
+* transformer MLP with the oracle chain rounded to bf16 wherever a tensor
+  crosses a call boundary (H, Z, Y, the masked gradient dZ1, dX), as the
+  bf16 contract of these calls says.
+* classifier head (65536 x 768 -> 32000, AdamW at t = 1): 8.4 GB of
+  logits, more bytes than a 32-bit offset reaches.  The float64 oracle runs
+  the whole batch in blocks of rows (rows are independent; every block is
+  scaled by the whole batch): the loss, every row loss, dX, dW and db, and
+  the AdamW state after the step are compared in full, the logits and
+  dlogits on 4096 seeded rows.
 """
+import os
+import threading
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +26,8 @@ import torch
 import oracle as O
 import synth_inputs as si
 from tests.gpu_util import BF16_TOL, F32_TOL, LOSS_TOL, assert_close, device, to_dev, to_np
-from tests.test_gpu_parity import _adopted_masks, _gpu_relu_masks
+from tests.test_gpu_parity import (_adamw_spread, _adopted_masks, _assert_close_band,
+                                   _gpu_relu_masks)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +63,6 @@ def test_tmlp_bf16_full_tokens(dl):
     w = si.WORKLOADS["tmlp_bf16"]
     inp = si.generate(w)
     bf = torch.bfloat16
-    T, d, f = w.batch, w.dims[0], w.dims[1]
     X = to_dev(inp.X, bf)
     dY = to_dev(inp.dY, bf)
     Wm = [to_dev(a) for a in inp.W]
@@ -70,58 +77,175 @@ def test_tmlp_bf16_full_tokens(dl):
     dX, dW1, db1 = dl.dense_act_vjp(dZ, None, X, Wb[0], dl.ACT_IDENTITY, Wt=Wbt[0])
     torch.cuda.synchronize()
 
-    W1, W2 = O.round_bf16(inp.W[0]), O.round_bf16(inp.W[1])
-    rH, rZ = O.dense_act_fwd(inp.X, W1, inp.b[0], O.ACT_GELU_TANH)
-    rY, _ = O.dense_act_fwd(rH, W2, inp.b[1], O.ACT_IDENTITY)
+    # the oracle chain, each boundary tensor rounded to bf16 (X, dY and the
+    # W copies are bf16 already; H, Z and Y leave the forwards in bf16; the
+    # second vjp writes dZ1 = (dY W2) * gelu'(Z1) in bf16 with Z1 read from
+    # its bf16 copy; dX leaves in bf16)
+    r = O.round_bf16
+    W1, W2 = r(inp.W[0]), r(inp.W[1])
+    _, Z1 = O.dense_act_fwd(inp.X, W1, inp.b[0], O.ACT_GELU_TANH)
+    rZ = r(Z1)
+    rH = r(O.act_fwd(Z1, O.ACT_GELU_TANH))
+    rY = r(O.dense_act_fwd(rH, W2, inp.b[1], O.ACT_IDENTITY)[0])
     assert_close(H_np, rH, BF16_TOL, "H")
     assert_close(Y_np, rY, BF16_TOL, "Y")
     rdH, rdW2, rdb2 = O.dense_act_vjp(inp.dY, None, rH, W2, O.ACT_IDENTITY)
-    rdX, rdW1, rdb1 = O.dense_act_vjp(rdH, rZ, inp.X, W1, O.ACT_GELU_TANH)
+    rdZ = r(rdH * O.act_grad(rZ, O.ACT_GELU_TANH))
+    rdX, rdW1, rdb1 = O.dense_act_vjp(rdZ, None, inp.X, W1, O.ACT_IDENTITY)
     assert_close(to_np(dW2), rdW2, BF16_TOL, "dW2")
     assert_close(to_np(db2), rdb2, BF16_TOL, "db2")
-    assert_close(to_np(dZ), rdH * O.act_grad(rZ, O.ACT_GELU_TANH), BF16_TOL, "dZ1")
+    assert_close(to_np(dZ), rdZ, BF16_TOL, "dZ1")
     assert_close(to_np(dW1), rdW1, BF16_TOL, "dW1")
     assert_close(to_np(db1), rdb1, BF16_TOL, "db1")
-    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+    assert_close(to_np(dX), r(rdX), BF16_TOL, "dX")
 
 
-def test_head_xent_full_rows(dl):
+# ------------------------------------------------------------ classifier head
+
+HEAD_SAMPLE_ROWS = 4096
+
+
+def _head_sample(B):
+    rng = np.random.default_rng(5)
+    s = np.sort(rng.choice(B, HEAD_SAMPLE_ROWS - 2, replace=False))
+    return np.unique(np.concatenate([s, [0, B - 1]]))
+
+
+HEAD_BLOCK = 512
+
+
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.fixture(scope="module")
+def head_ref():
+    """One classifier-head step of the float64 oracle at full size: forward,
+    softmax-xent and vjp over blocks of rows (each with the whole batch as
+    the divisor), then AdamW at t = 1 on W and b.  Also the float32 rounding
+    band of dW and db (sums over all 65536 rows), for the update's
+    comparison near zero gradients.  Rows are independent, so the blocks are
+    shared among threads (thread t takes blocks t, t + T, ...; BLAS on one
+    thread each) and the per-thread sums are added in thread order."""
+    from threadpoolctl import threadpool_limits
     w = si.WORKLOADS["head_xent"]
     inp = si.generate(w)
     B, d, C = w.batch, w.dims[0], w.dims[1]
-    assert B * C * 4 > 2 ** 32
+    W, b, y = inp.W[0].astype(np.float64), inp.b[0].astype(np.float64), inp.labels
+    X = inp.X
+    sample = _head_sample(B)
+    ref = {"row": np.empty(B), "lse": np.empty(B), "dX": np.empty((B, d)),
+           "z_s": np.empty((len(sample), C)), "dz_s": np.empty((len(sample), C))}
+    nt = _threads()
+    blocks = list(range(0, B, HEAD_BLOCK))
+    acc = [None] * nt
+    t0 = time.time()
+
+    def work(t):
+        dW, db = np.zeros((C, d)), np.zeros(C)
+        bw, bb = np.zeros((C, d)), np.zeros(C)
+        for r0 in blocks[t::nt]:
+            r1 = min(B, r0 + HEAD_BLOCK)
+            Xc = X[r0:r1].astype(np.float64)
+            _, Z = O.dense_act_fwd(Xc, W, b, O.ACT_IDENTITY)
+            _, dz, rl = O.softmax_xent_fwd_bwd(Z, y[r0:r1], batch_total=B)
+            ref["row"][r0:r1] = rl
+            ref["lse"][r0:r1] = O.softmax_lse(Z)
+            dG = O.xent_grad_band(Z, O.dot_band(Xc, W, b), B, labels=y[r0:r1])
+            dXc, dWc, dbc = O.dense_act_vjp(dz, None, Xc, W, O.ACT_IDENTITY)
+            ref["dX"][r0:r1] = dXc
+            dW += dWc
+            db += dbc
+            band = O.sum_band(dz, np.hstack([Xc, np.ones((r1 - r0, 1))]), dG, n=B)
+            bw += band[:, :d]
+            bb += band[:, d]
+            ins = (sample >= r0) & (sample < r1)
+            ref["z_s"][ins] = Z[sample[ins] - r0]
+            ref["dz_s"][ins] = dz[sample[ins] - r0]
+        acc[t] = (dW, db, bw, bb)
+
+    with threadpool_limits(limits=1):
+        threads = [threading.Thread(target=work, args=(t,)) for t in range(nt)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+    assert all(a is not None for a in acc), "an oracle thread failed"
+    for key, i in (("dW", 0), ("db", 1), ("bw", 2), ("bb", 3)):
+        total = acc[0][i].copy()
+        for t in range(1, nt):
+            total += acc[t][i]
+        ref[key] = total
+    print(f"oracle of the full head step on {nt} threads: {time.time() - t0:.1f} s", flush=True)
+    ref["loss"] = float(ref["row"].sum() / B)
+    o = w.optim
+    args = (o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, 1)
+    for name, p0, g in (("W", W, ref["dW"]), ("b", b, ref["db"])):
+        z0 = np.zeros_like(g)
+        w1, m1, v1 = O.adamw_step(p0, g, z0, z0, *args)
+        ref[name + "1"], ref["m" + name], ref["v" + name] = (O.round_f32(w1), O.round_f32(m1),
+                                                            O.round_f32(v1))
+    ref["inp"], ref["w"], ref["sample"] = inp, w, sample
+    return ref
+
+
+def _gpu_head_step(dl, ref):
+    """The classifier-head step exactly as bench.py runs it (same entry
+    points, shapes and launch plans), with the sampled logits and dlogits
+    rows gathered on the side.  Returns float64 host arrays."""
+    inp, w, sample = ref["inp"], ref["w"], ref["sample"]
+    o = w.optim
+    B, d, C = w.batch, w.dims[0], w.dims[1]
     X, y = to_dev(inp.X), to_dev(inp.labels)
     W, b = to_dev(inp.W[0]), to_dev(inp.b[0])
+    srows = torch.from_numpy(sample).to(device())
     logits, _ = dl.dense_act_fwd(X, W, b, dl.ACT_IDENTITY)
+    z_s = logits[srows].cpu()
     row = torch.empty(B, device=device())
     loss, dz = dl.softmax_xent_fwd_bwd(logits, y, inplace=True, row_loss=row)
+    dz_s = dz[srows].cpu()
     dX, dW, db = dl.dense_act_vjp(dz, None, X, W, dl.ACT_IDENTITY)
+    del logits, dz
+    mW, vW = torch.zeros_like(W), torch.zeros_like(W)
+    mb, vb = torch.zeros_like(b), torch.zeros_like(b)
+    dl.adamw_step(W, dW, mW, vW, o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, 1)
+    dl.adamw_step(b, db, mb, vb, o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, 1)
     torch.cuda.synchronize()
+    out = {"loss": float(loss.item()), "row": to_np(row), "dX": to_np(dX), "dW": to_np(dW),
+           "db": to_np(db), "W1": to_np(W), "mW": to_np(mW), "vW": to_np(vW), "b1": to_np(b),
+           "mb": to_np(mb), "vb": to_np(vb), "z_s": z_s.double().numpy(),
+           "dz_s": dz_s.double().numpy()}
+    return out
 
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([rng.integers(0, B, 250), [0, B - 1]]))
-    zr, _ = O.dense_act_fwd(inp.X[rows], inp.W[0], inp.b[0], O.ACT_IDENTITY)
-    _, _, rrow = O.softmax_xent_fwd_bwd(zr, inp.labels[rows])
-    p = np.exp(zr - zr.max(axis=1, keepdims=True))
-    p /= p.sum(axis=1, keepdims=True)
-    rdz = (p - np.eye(C)[inp.labels[rows]]) / B
-    rows_t = torch.from_numpy(rows).to(device())
-    assert_close(to_np(row[rows_t]), rrow, F32_TOL, "sampled row losses")
-    assert_close(to_np(dz[rows_t]), rdz, F32_TOL, "sampled dlogits rows")
-    assert_close(to_np(dX[rows_t]), rdz @ inp.W[0].astype(np.float64), F32_TOL, "sampled dX rows")
-    # the mean is the fixed-order mean of the per-row losses
-    mean = float(row.double().mean().item())
-    assert abs(float(loss.item()) - mean) <= 1e-6 * abs(mean)
-    # dW and db against the GPU's own dlogits, in float64 on the device
-    v = torch.randn(d, dtype=torch.float64, device=device(), generator=torch.Generator(
-        device=device()).manual_seed(7))
-    xv = X.double() @ v
-    lhs = dW.double() @ v
-    rhs = torch.zeros(C, dtype=torch.float64, device=device())
-    colsum = torch.zeros(C, dtype=torch.float64, device=device())
-    for s in range(0, B, 4096):
-        blk = dz[s:s + 4096].double()
-        rhs += blk.t() @ xv[s:s + 4096]
-        colsum += blk.sum(dim=0)
-    assert_close(lhs.cpu().numpy(), rhs.cpu().numpy(), F32_TOL, "dW v")
-    assert_close(to_np(db), colsum.cpu().numpy(), F32_TOL, "db")
+
+def _check_head(got, ref, what):
+    inp, w = ref["inp"], ref["w"]
+    o = w.optim
+    assert abs(got["loss"] - ref["loss"]) <= LOSS_TOL * abs(ref["loss"]), \
+        (what, got["loss"], ref["loss"])
+    assert_close(got["row"], ref["row"], F32_TOL, f"{what}: row losses")
+    if "z_s" in got:
+        assert_close(got["z_s"], ref["z_s"], F32_TOL, f"{what}: sampled logits rows")
+    if "dz_s" in got:
+        assert_close(got["dz_s"], ref["dz_s"], F32_TOL, f"{what}: sampled dlogits rows")
+    if "lse" in got:
+        assert_close(got["lse"], ref["lse"], F32_TOL, f"{what}: lse")
+    assert_close(got["dX"], ref["dX"], F32_TOL, f"{what}: dX")
+    assert_close(got["dW"], ref["dW"], F32_TOL, f"{what}: dW")
+    assert_close(got["db"], ref["db"], F32_TOL, f"{what}: db")
+    admitted = 0
+    for name, p0, g, band in (("W", inp.W[0], ref["dW"], ref["bw"]),
+                              ("b", inp.b[0], ref["db"], ref["bb"])):
+        z0 = np.zeros_like(g)
+        bw, bm, bv = _adamw_spread(p0.astype(np.float64), g, band, z0, z0, o, 1)
+        admitted += _assert_close_band(got[name + "1"], ref[name + "1"], bw, F32_TOL,
+                                       f"{what}: {name} after AdamW")
+        _assert_close_band(got["m" + name], ref["m" + name], bm, F32_TOL, f"{what}: m{name}")
+        _assert_close_band(got["v" + name], ref["v" + name], bv, F32_TOL, f"{what}: v{name}")
+    print(f"{what}: updates inside the rounding band of a near-zero gradient: {admitted}")
+
+
+@pytest.mark.timeout(1200)
+def test_head_xent_full_size_composed(dl, head_ref):
+    assert head_ref["w"].batch * head_ref["w"].dims[1] * 4 > 2 ** 32
+    _check_head(_gpu_head_step(dl, head_ref), head_ref, "composed head")

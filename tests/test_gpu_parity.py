@@ -434,31 +434,52 @@ def _gpu_relu_masks(dl, X, Ws, bs, acts):
 
 def _adopted_masks(gpu_masks, state, X, acts):
     """Oracle masks, replaced by the GPU's decision only where the oracle's
-    pre-activation lies within twice the float32 rounding band of zero.
+    pre-activation lies within its float32 rounding band of zero: the band
+    of the layer's own sum plus what the deviation of the layer's float32
+    input (the earlier layers' bands, carried forward) can move it by.
     Returns (masks, adopted count); fails on a disagreement outside it."""
-    h = np.asarray(X, np.float64)
+    taus, _, _, zs = O.mlp_forward_bands(X, state.W, state.b, acts)
     out, adopted = [], 0
     for l in range(len(state.W)):
-        Y, Z = O.dense_act_fwd(h, state.W[l], state.b[l], acts[l])
         if acts[l] == O.ACT_RELU:
-            band = 2.0 * O.relu_kink_band(h, state.W[l], state.b[l])
+            Z = zs[l]
             own = Z > 0
-            near = np.abs(Z) <= band
+            near = np.abs(Z) <= taus[l]
             diff = own != gpu_masks[l]
             assert not np.any(diff & ~near), f"layer {l}: ReLU decision differs outside the band"
             adopted += int(np.sum(diff & near))
             out.append(np.where(near, gpu_masks[l], own).astype(np.float64))
         else:
             out.append(None)
-        h = Y
     return out, adopted
 
 
-def _grad_rounding_bound(G, h):
-    """Float32 rounding bound of dW = G^T h and db = sum G over the batch."""
-    K = G.shape[0] + 64
-    gamma = K * 2.0 ** -24
-    return gamma * (np.abs(G).T @ np.abs(h)), gamma * np.abs(G).sum(axis=0)
+def _grad_bands(ref, before, X, acts, masks, loss="xent", scale=1.0, labels=None):
+    """Float32 rounding bands of every weight and bias gradient of one MLP
+    step, from the oracle's step result `ref` and the state `before` it:
+    the loss gradient's band from the logits' forward band, then each
+    layer's dW = G^T h and db = sum G bands from the deviations of its G
+    (carried down through the dX products) and of its input h (carried up
+    through the forward).  Lists (dW bands, db bands), times the loss
+    scale like the gradients themselves."""
+    L = len(before.W)
+    taus, dhs, hs, zs = O.mlp_forward_bands(X, before.W, before.b, acts)
+    B = hs[0].shape[0]
+    if loss == "xent":
+        dG = O.xent_grad_band(zs[-1], taus[-1], B, labels=labels)
+    else:  # mean squared error: 2 (p - t) / (B C), four roundings
+        n = zs[-1].size
+        dG = (2.0 / n) * (taus[-1] + O.gamma(4) * (np.abs(ref["G"][-1]) * n / 2.0 + taus[-1]))
+    bw, bb = [None] * L, [None] * L
+    for l in reversed(range(L)):
+        G = ref["G"][l]
+        bw[l] = scale * O.sum_band(G, hs[l], dG, dhs[l])
+        bb[l] = scale * O.sum_band(G, np.ones((B, 1)), dG, None)[:, 0]
+        if l > 0:
+            mk = masks[l - 1] if masks is not None and masks[l - 1] is not None else \
+                O.act_grad(zs[l - 1], acts[l - 1])
+            dG = O.dx_band(G, before.W[l], dG, mk)
+    return bw, bb
 
 
 def _adamw_spread(w0, g, dg, m0, v0, o, t):
@@ -472,10 +493,21 @@ def _adamw_spread(w0, g, dg, m0, v0, o, t):
 
 
 def _assert_close_band(got, ref, band, tol, what):
+    """got within tol (normwise) of ref once each element may also move by
+    its band.  The band admits elements whose float32 gradient lies so close
+    to zero (or to eps) that the update itself may go either way; those are
+    counted, and more than 1e-4 of the elements (plus 4) fails: a float32
+    sum of K terms errs by about u sqrt(K) of its size, so the share of
+    updates it can legitimately turn is of that order (about 5e-6 for the
+    8192-row batch), far below the cap."""
     scale = np.max(np.abs(ref))
-    excess = np.abs(got - ref) - band
+    dev = np.abs(got - ref)
+    excess = dev - band
     err = float(np.max(excess) / scale) if scale > 0 else float(np.max(excess))
     assert err < tol, f"{what}: error beyond the rounding band {err:.3e} >= {tol:.1e}"
+    admitted = int(np.sum(dev >= tol * scale)) if scale > 0 else 0
+    assert admitted <= 1e-4 * dev.size + 4, f"{what}: band admits {admitted} of {dev.size}"
+    return admitted
 
 
 def _load_state(mlp, st):
@@ -522,10 +554,11 @@ def _check_one_step(dl, w, inp, mlp, Xd, yd, st):
     loss = float(_gpu_step(dl, mlp, w, Xd, yd, t).item())
     assert abs(loss - ref["loss"]) <= LOSS_TOL * abs(ref["loss"]), (t, loss, ref["loss"])
     o = w.optim
+    bands_w, bands_b = _grad_bands(ref, before, inp.X, w.acts, masks, labels=inp.labels)
     for l in range(mlp.L):
+        dgW, dgb = bands_w[l], bands_b[l]
         assert_close(to_np(mlp.dW[l]), ref["dW"][l], F32_TOL, f"step {t} dW{l}")
         assert_close(to_np(mlp.db[l]), ref["db"][l], F32_TOL, f"step {t} db{l}")
-        dgW, dgb = _grad_rounding_bound(ref["G"][l], ref["h"][l])
         pairs = [("W", mlp.W[l], ref_st.W[l], before.W[l], ref["dW"][l], dgW, before.mW[l],
                   before.vW[l], mlp.mW[l], mlp.vW[l], ref_st.mW[l], ref_st.vW[l]),
                  ("b", mlp.b[l], ref_st.b[l], before.b[l], ref["db"][l], dgb, before.mb[l],

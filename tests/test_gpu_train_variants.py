@@ -15,7 +15,7 @@ import oracle as O
 import synth_inputs as si
 from tests.gpu_util import F32_TOL, LOSS_TOL, assert_close, device, misaligned, to_dev, to_np
 from tests.test_gpu_parity import (_adopted_masks, _assert_close_band, _copy_state,
-                                   _gpu_relu_masks, _grad_rounding_bound, _load_state)
+                                   _gpu_relu_masks, _grad_bands, _load_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -408,8 +408,9 @@ def test_mlp_step_adam_matches_oracle(dl, work):
         ref = O.mlp_train_step(st, inp.X, inp.labels, w.acts, opt, relu_masks=masks)
         loss = float(_gpu_variant_step(dl, mlp, Xd, yd, opt, t, False).item())
         assert abs(loss - ref["loss"]) <= LOSS_TOL * abs(ref["loss"])
+        bands_w, bands_b = _grad_bands(ref, before, inp.X, w.acts, masks, labels=inp.labels)
         for l in range(mlp.L):
-            dgW, dgb = _grad_rounding_bound(ref["G"][l], ref["h"][l])
+            dgW, dgb = bands_w[l], bands_b[l]
             for got, want, w0, g, dg, m0, v0 in (
                     (mlp.W[l], st.W[l], before.W[l], ref["dW"][l], dgW, before.mW[l],
                      before.vW[l]),
@@ -581,7 +582,7 @@ def test_mlp_step_mse_matches_oracle(dl, work, variant):
             assert_close(to_np(mlp.dW[l]), ref["dW"][l], F32_TOL, f"step {t} dW{l}")
             assert_close(to_np(mlp.db[l]), ref["db"][l], F32_TOL, f"step {t} db{l}")
             if adam:
-                dgW, dgb = _grad_rounding_bound(ref["G"][l], ref["h"][l])
+                dgW = _grad_bands(ref, before, inp.X, w.acts, masks, loss="mse")[0][l]
                 bw, _, _ = _adamw_spread(before.W[l], ref["dW"][l], dgW, before.mW[l],
                                          before.vW[l], opt, t)
                 _assert_close_band(to_np(mlp.W[l]), st.W[l], bw, F32_TOL, f"step {t} W{l}")

@@ -235,3 +235,63 @@ def test_safe_scale_off_by_one_binade_caught(monkeypatch):
     real = D.f16_safe_scale
     monkeypatch.setattr(O, "f16_safe_scale", lambda a: 2.0 * real(a))
     _expect_pin_failure(P.test_f16_safe_scale_hand_values)
+
+
+# ---- the rounding bands the parity tests widen comparisons by --------------
+
+from oracle import rounding_bands as RB  # noqa: E402
+from tests import test_oracle_bands as PB  # noqa: E402
+
+
+def test_band_ten_times_too_wide_caught(monkeypatch):
+    real = RB.dot_band
+    monkeypatch.setattr(O, "relu_kink_band", lambda X, W, b, dX=None: 10.0 * real(X, W, b, dX))
+    _expect_pin_failure(PB.test_dot_band_near_attained_by_ties)
+
+
+def test_band_twice_too_wide_caught(monkeypatch):
+    real = RB.dot_band
+    monkeypatch.setattr(O, "relu_kink_band", lambda X, W, b, dX=None: 2.0 * real(X, W, b, dX))
+    _expect_pin_failure(PB.test_dot_band_near_attained_by_ties)
+
+
+def test_band_without_operand_deviation_caught(monkeypatch):
+    real = RB.dot_band
+    monkeypatch.setattr(O, "dot_band", lambda X, W, b=None, dX=None: real(X, W, b, None))
+    _expect_pin_failure(PB.test_dot_band_covers_perturbed_operand)
+
+
+def test_band_deviation_counted_twice_caught(monkeypatch):
+    real = RB.dot_band
+
+    def doubled(X, W, b=None, dX=None):
+        extra = 0.0 if dX is None else np.asarray(dX) @ np.abs(np.asarray(W, np.float64)).T
+        return real(X, W, b, dX) + extra
+
+    monkeypatch.setattr(O, "dot_band", doubled)
+    _expect_pin_failure(PB.test_dot_band_perturbation_term_is_tight)
+
+
+def test_sum_band_gamma_of_fewer_terms_caught(monkeypatch):
+    def short(G, h, dG=None, dh=None):
+        aG = np.abs(np.asarray(G, np.float64))
+        return RB.gamma(aG.shape[0] // 4) * (aG.T @ np.abs(np.asarray(h, np.float64)))
+
+    monkeypatch.setattr(O, "sum_band", short)
+    _expect_pin_failure(PB.test_sum_band_holds_and_is_near_attained)
+
+
+def test_xent_band_without_logit_deviation_caught(monkeypatch):
+    real = RB.xent_grad_band
+    monkeypatch.setattr(O, "xent_grad_band",
+                        lambda z, tau, B, scale=1.0, labels=None:
+                        real(z, 0.0 * np.asarray(tau), B, scale, labels))
+    _expect_pin_failure(PB.test_xent_grad_band_holds)
+
+
+def test_xent_band_far_too_wide_caught(monkeypatch):
+    real = RB.xent_grad_band
+    monkeypatch.setattr(O, "xent_grad_band",
+                        lambda z, tau, B, scale=1.0, labels=None:
+                        10.0 * real(z, tau, B, scale, labels))
+    _expect_pin_failure(PB.test_xent_grad_band_is_tight_for_a_dominant_class)

@@ -99,9 +99,27 @@ def test_f16_safe_scale_places_max_in_top_binade_and_keeps_relative_accuracy():
     assert np.median(np.abs(plain - a) / np.abs(a)) > 0.05
 
 
-def test_round_f32_matches_cast():
-    x = np.array([1.0 + 2.0 ** -30, 0.1, -7.3e-9])
-    assert np.array_equal(O.round_f32(x), x.astype(np.float32).astype(np.float64))
+def test_round_f32_hand_values():
+    """Round-to-nearest-even into float32, from hand-derived values."""
+    u = 2.0 ** -24
+    cases = [
+        (1.0 + u, 1.0),                       # tie between 1 and 1 + 2u: even is 1
+        (1.0 + 3 * u, 1.0 + 4 * u),           # tie between 1 + 2u and 1 + 4u: even is 1 + 4u
+        (1.0 + u * 1.0000001, 1.0 + 2 * u),   # just past the tie rounds up
+        (1.0 + 2 * u, 1.0 + 2 * u),           # representable: unchanged
+        (0.1, 13421773 * 2.0 ** -27),         # 0x3DCCCCCD
+        (-7.0, -7.0),
+        (2.0 ** -149, 2.0 ** -149),           # smallest subnormal
+        (2.0 ** -150, 0.0),                   # tie with 0: even is 0
+        (3 * 2.0 ** -150, 2.0 ** -148),       # tie between 1 and 2 subnormal units: 2
+        (2.0 ** 128 * (1 - 2.0 ** -25), float("inf")),  # rounds past the largest float
+        (2.0 ** 128 * (1 - 2.0 ** -24), 2.0 ** 128 * (1 - 2.0 ** -24)),  # largest float
+    ]
+    for x, want in cases:
+        with np.errstate(over="ignore"):
+            got = O.round_f32(np.array([x]))[0]
+        assert got == want, (x, got, want)
+    assert np.isnan(O.round_f32(np.array([np.nan]))[0])
 
 
 # ---------------------------------------------------------------- activations
@@ -276,23 +294,34 @@ def test_vjp_need_dx_false():
     assert dX is None and dW.shape == (2, 4) and db.shape == (2,)
 
 
-def test_relu_kink_band_bounds_float32_dot_products():
-    """Any float32 evaluation order of a dot product lands within tau."""
-    rng = np.random.default_rng(4)
-    X = rng.standard_normal((20, 300)).astype(np.float32)
-    W = rng.standard_normal((10, 300)).astype(np.float32)
-    b = rng.standard_normal(10).astype(np.float32)
-    tau = O.relu_kink_band(X, W, b)
-    exact = X.astype(np.float64) @ W.astype(np.float64).T + b
-    for order in range(3):
-        idx = rng.permutation(300)
-        acc = np.array(b, dtype=np.float32)[None, :].repeat(20, 0)
-        for k in idx:
-            acc = (acc + X[:, k:k + 1] * W[None, :, k]).astype(np.float32)
-        assert np.all(np.abs(acc - exact) <= tau)
-
-
 # ---------------------------------------------------------------- xent
+
+def test_xent_by_row_blocks_with_batch_total():
+    """Rows are independent: the batch taken in blocks of rows, each with
+    the whole batch as the divisor, gives the same dlogits and row losses,
+    and the block losses add up to the batch loss."""
+    rng = np.random.default_rng(71)
+    z = rng.standard_normal((12, 9)) * 2.0
+    y = rng.integers(0, 9, 12).astype(np.int32)
+    loss, dz, row = O.softmax_xent_fwd_bwd(z, y)
+    parts = [O.softmax_xent_fwd_bwd(z[i:i + 4], y[i:i + 4], batch_total=12) for i in (0, 4, 8)]
+    assert abs(sum(p[0] for p in parts) - loss) < 1e-14
+    assert np.allclose(np.concatenate([p[1] for p in parts]), dz, rtol=1e-14, atol=1e-17)
+    assert np.array_equal(np.concatenate([p[2] for p in parts]), row)
+    with pytest.raises(ValueError):
+        O.softmax_xent_fwd_bwd(z, y, batch_total=11)
+
+
+def test_softmax_lse_matches_scipy_and_row_loss():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(72)
+    z = rng.standard_normal((7, 40)) * 5.0 + 100.0
+    y = rng.integers(0, 40, 7).astype(np.int32)
+    lse = O.softmax_lse(z)
+    assert np.allclose(lse, logsumexp(z, axis=1), rtol=1e-15, atol=1e-12)
+    _, _, row = O.softmax_xent_fwd_bwd(z, y)
+    assert np.allclose(row, lse - z[np.arange(7), y], rtol=1e-13, atol=1e-12)
+
 
 def _xent_case(seed, B, C, scale=3.0):
     rng = np.random.default_rng(seed)
