@@ -23,7 +23,7 @@ ACT_IDENTITY, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
 OPT_SGD, OPT_ADAMW, OPT_ADAM = 0, 1, 2
 LR_CONSTANT, LR_STEP, LR_WARMUP_COSINE, LR_WARMUP_LINEAR = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "ALIASING",
-          4: "WORKSPACE_TOO_SMALL", 5: "HIP_ERROR"}
+          4: "WORKSPACE_TOO_SMALL", 5: "HIP_ERROR", 6: "LABEL_OUT_OF_RANGE"}
 
 _ACTS = {"identity": ACT_IDENTITY, "relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH,
          None: ACT_IDENTITY}
@@ -91,6 +91,8 @@ def _sig(name, res, args):
 
 _c = {
     "dl_last_error": _sig("dl_last_error", ctypes.c_char_p, []),
+    "dense_last_error": _sig("dense_last_error", ctypes.c_char_p, []),
+    "dl_set_validate": _sig("dl_set_validate", _i32, [_i32]),
     "dl_build_target": _sig("dl_build_target", ctypes.c_char_p, []),
     "dense_act_fwd": _sig("dense_act_fwd", _i32,
                           [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -145,7 +147,7 @@ _c = {
     "dl_set_mlp_fusion": _sig("dl_set_mlp_fusion", _i32, [_i32]),
 }
 
-EXPORTS = ["dl_last_error", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
+EXPORTS = ["dl_last_error", "dense_last_error", "dl_set_validate", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_scaled", "dense_cast_f16_scaled", "dense_cast_f16_scaled_workspace_size",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
            "softmax_xent_workspace_size", "sgd_step", "adamw_step",
@@ -187,9 +189,17 @@ def set_mlp_fusion(level: int) -> int:
     return prev
 
 
+def set_validate(on: bool) -> bool:
+    """Validate mode on this thread: cross-entropy calls check their labels
+    on the device first (one stream synchronisation) and raise
+    LABEL_OUT_OF_RANGE instead of producing NaN rows.  Returns the previous
+    setting."""
+    return bool(_c["dl_set_validate"](1 if on else 0))
+
+
 def _check(status: int):
     if status != 0:
-        raise DenseError(status, _c["dl_last_error"]().decode())
+        raise DenseError(status, _c["dense_last_error"]().decode())
 
 
 def _stream(t: torch.Tensor):

@@ -58,13 +58,48 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   ++g_prof.seen;
   if ((int)g_prof.recs.size() >= g_prof.capacity) return launch();
   ProfRec r{name, nullptr, nullptr};
-  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+  if (hipEventCreate(&r.start) != hipSuccess) return launch();
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
     return launch();
-  hipEventRecord(r.start, s);
+  }
+  // a launch whose events could not be recorded runs untimed
+  if (hipEventRecord(r.start, s) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    return launch();
+  }
   hipError_t e = launch();
-  hipEventRecord(r.stop, s);
+  if (hipEventRecord(r.stop, s) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    return e;
+  }
   g_prof.recs.push_back(r);
   return e;
+}
+
+// Validate mode (dl_set_validate): label ranges are checked on the device
+// before a cross-entropy runs, which costs a stream synchronisation.
+thread_local int g_validate = 0;
+
+// In validate mode: count the labels outside [0, C) into the 4-byte device
+// slot `slot` (part of the call's workspace, not yet in use), wait for the
+// count and fail with DL_LABEL_OUT_OF_RANGE when there are any.  Nothing else
+// has been launched when it fails.
+int check_labels(const char* who, hipStream_t s, int64_t B, int64_t C, const int32_t* labels,
+                 void* slot) {
+  if (!g_validate) return DL_OK;
+  hipError_t e = dl::launch_label_check(B, C, labels, static_cast<int*>(slot), s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  int bad = 0;
+  e = hipMemcpyAsync(&bad, slot, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  if (bad > 0)
+    return fail(DL_LABEL_OUT_OF_RANGE, "%s: %d label(s) outside [0, %lld)", who, bad,
+                (long long)C);
+  return DL_OK;
 }
 
 constexpr size_t kAlign = 256;
@@ -277,6 +312,14 @@ extern "C" {
 
 const char* dl_last_error(void) { return g_last_error.c_str(); }
 
+const char* dense_last_error(void) { return g_last_error.c_str(); }
+
+int dl_set_validate(int on) {
+  const int prev = g_validate;
+  g_validate = on != 0;
+  return prev;
+}
+
 const char* dl_build_target(void) { return "gfx950"; }
 
 int dl_set_mlp_fusion(int level) {
@@ -290,8 +333,8 @@ int dl_set_mlp_fusion(int level) {
 int dl_profile_begin(int capacity) {
   if (capacity < 0) return fail(DL_INVALID_ARGUMENT, "dl_profile_begin: negative capacity");
   for (auto& r : g_prof.recs) {
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_prof.recs.clear();
   g_prof.recs.reserve(capacity);
@@ -317,8 +360,8 @@ int dl_profile_end(int max, float* ms, char* names) {
       }
     }
     ++i;
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_prof.recs.clear();
   if (err) {
@@ -459,6 +502,8 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
     return fail(DL_ALIASING, "softmax_xent_fwd_bwd: outputs overlap inputs (dlogits may equal logits)");
   float* rl = row_loss ? row_loss : static_cast<float*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int vs = check_labels("softmax_xent_fwd_bwd", st, B, C, labels, ws);
+  if (vs != DL_OK) return vs;
   hipError_t e = timed("xent", st, [&] { return dl::launch_xent(B, C, logits, labels, rl, dlogits, loss, st); });
   if (e != hipSuccess) return hip_fail(e, "softmax_xent_fwd_bwd");
   return DL_OK;
@@ -1182,6 +1227,11 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     return fail(DL_INVALID_ARGUMENT, "mlp_train_step: workspace must be 256-byte aligned");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (xent) {  // the per-row loss region is free until the loss runs
+    const int vs = check_labels("mlp_train_step", s, B, layers[n_layers - 1].out, labels,
+                                static_cast<char*>(ws) + rl_off);
+    if (vs != DL_OK) return vs;
+  }
   char* base = static_cast<char*>(ws);
   const bool dev_step = opt->step_dev != nullptr;
   // with clipping or loss scaling a gradient pass precedes the update and its

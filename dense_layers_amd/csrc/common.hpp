@@ -507,6 +507,9 @@ hipError_t launch_cast_f16_scaled(int64_t n, const float* src, bf16_t* dst, floa
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s, const float* dscale = nullptr);
+// Number of labels outside [0, C) into bad[0] (one workgroup, no atomics).
+hipError_t launch_label_check(int64_t B, int64_t C, const int32_t* labels, int* bad,
+                              hipStream_t s);
 // Fixed-order float64 mean of the per-row losses (one workgroup).
 hipError_t launch_loss_mean(int64_t B, const float* row_loss, float* loss, hipStream_t s);
 // Narrow classifier head of the MLP step (C <= 16 classes, K <= 256 inputs):

@@ -267,6 +267,27 @@ loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restric
   }
 }
 
+// Labels outside [0, C): one workgroup strides over the batch, counts per
+// thread, then a fixed-order tree; one lane stores the count.
+__global__ void __launch_bounds__(kMeanThreads)
+label_check_kernel(int64_t B, int64_t C, const int32_t* __restrict__ labels, int* __restrict__ bad) {
+  __shared__ int red[kMeanThreads / 64];
+  int n = 0;
+  for (int64_t i = threadIdx.x; i < B; i += kMeanThreads) {
+    const int32_t y = labels[i];
+    n += (y < 0 || (int64_t)y >= C) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < kMeanThreads / 64; ++w) t += red[w];
+    bad[0] = t;
+  }
+}
+
 template <int TPR, int NI, bool VEC, int BLOCK = kXentBlock>
 hipError_t launch_rows(int64_t B, int64_t C, const float* logits, const int32_t* labels,
                        float* row_loss, float* dlogits, const float* dscale, hipStream_t s) {
@@ -306,6 +327,12 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
   }
   if (e != hipSuccess) return e;
   return launch_loss_mean(B, row_loss, loss, s);
+}
+
+hipError_t launch_label_check(int64_t B, int64_t C, const int32_t* labels, int* bad,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(label_check_kernel, dim3(1), dim3(kMeanThreads), 0, s, B, C, labels, bad);
+  return hipGetLastError();
 }
 
 hipError_t launch_loss_mean(int64_t B, const float* row_loss, float* loss, hipStream_t s) {

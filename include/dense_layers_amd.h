@@ -70,7 +70,10 @@ enum dl_status {
   DL_UNSUPPORTED = 2,          /* a dtype / activation combination not built */
   DL_ALIASING = 3,             /* an output overlaps an input it must not */
   DL_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes below the size query's answer */
-  DL_HIP_ERROR = 5             /* a HIP launch failed */
+  DL_HIP_ERROR = 5,            /* a HIP launch failed */
+  DL_LABEL_OUT_OF_RANGE = 6    /* validate mode only (dl_set_validate): a
+                                * label outside [0, C); nothing but the
+                                * label check was launched */
 };
 
 enum dl_opt_kind {
@@ -86,8 +89,23 @@ enum dl_lr_kind {
   DL_LR_WARMUP_LINEAR = 3    /* linear warmup, then linear down to min_lr */
 };
 
-/* Message for the last non-zero status returned on the calling thread. */
+/* Message for the last non-zero status returned on the calling thread.
+ * dense_last_error and dl_last_error are the same function. */
+const char* dense_last_error(void);
 const char* dl_last_error(void);
+
+/*
+ * dl_set_validate -- validate mode for the calling thread (off by default).
+ * When on, softmax_xent_fwd_bwd and mlp_train_step first count the labels
+ * outside [0, C) on the device (one small launch into their workspace) and
+ * wait for the count: a call with any such label returns
+ * DL_LABEL_OUT_OF_RANGE having touched no output.  This is the one place
+ * the library synchronises the caller's stream; outside validate mode an
+ * out-of-range label is never read out of bounds and gives a NaN row loss
+ * instead (see softmax_xent_fwd_bwd).  Returns the previous setting; any
+ * non-zero `on` turns it on.  No GPU work.
+ */
+int dl_set_validate(int on);
 
 /* Offload target the library was built for ("gfx950"). */
 const char* dl_build_target(void);
@@ -222,9 +240,10 @@ size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in,
  *
  *   B, C     > 0 (C = number of classes)
  *   logits   device float32 [B, C]
- *   labels   device int32 [B], each in [0, C).  A label outside the range
- *            makes that row's loss NaN (so the mean is NaN) and its dlogits
- *            row the plain softmax / B; it never causes an out-of-bounds read.
+ *   labels   device int32 [B], each in [0, C).  In validate mode a label
+ *            outside the range is DL_LABEL_OUT_OF_RANGE; otherwise it makes
+ *            that row's loss NaN (so the mean is NaN) and its dlogits row
+ *            the plain softmax / B, and is never read out of bounds.
  *   loss     device float32 [1] output (mean over the batch)
  *   row_loss device float32 [B] output per-row loss, or NULL
  *   dlogits  device float32 [B, C] output; may equal logits (in place)
@@ -518,7 +537,9 @@ typedef struct dl_layer {
  *
  *   B > 0; n_layers in [1, 16]; layers is a host array of n_layers entries.
  *   X        device float32 [B, layers[0].in]
- *   labels   device int32 [B], values in [0, layers[n-1].out)
+ *   labels   device int32 [B], values in [0, layers[n-1].out) (checked in
+ *            validate mode, DL_LABEL_OUT_OF_RANGE; C, the class count, is
+ *            layers[n-1].out and is not passed again)
  *   opt      host pointer
  *   loss     device float32 [1] output
  *   ws, ws_bytes  at least mlp_train_step_workspace_size()

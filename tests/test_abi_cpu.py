@@ -28,8 +28,19 @@ def dl():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["dense_act_fwd", "dense_act_vjp", "softmax_xent_fwd_bwd", "sgd_step",
-              "adamw_step", "mlp_train_step", "dense_cast_bf16", "dl_last_error"]:
+              "adamw_step", "mlp_train_step", "dense_cast_bf16", "dl_last_error",
+              "dense_last_error", "dl_set_validate"]:
         assert n in names
+
+
+def test_last_error_names_and_validate_switch(dl):
+    c = dl._c
+    # a rejected call (no GPU work: the size check comes first)
+    assert c["sgd_step"](None, 0, None, None, 1e-3) == 1
+    assert c["dense_last_error"]() == c["dl_last_error"]() and b"sgd_step" in c["dense_last_error"]()
+    assert dl.set_validate(True) is False
+    assert dl.set_validate(False) is True
+    assert dl.STATUS[6] == "LABEL_OUT_OF_RANGE"
 
 
 def test_library_exports_every_declared_symbol(dl):
