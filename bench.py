@@ -358,7 +358,13 @@ class TmlpBench:
 
 
 class HeadBench:
-    """Classifier head: Linear 768 -> 32000, softmax-xent, dX/dW/db, AdamW."""
+    """Classifier head: Linear 768 -> 32000, softmax-xent, dX/dW/db, AdamW.
+    path "fused" (default): dense_xent_fwd + dense_xent_vjp (the forward
+    GEMM leaves the logits and per-tile row statistics, the backward GEMMs
+    form the loss gradient from the logits as they read them); path
+    "composed": dense_act_fwd, softmax_xent_fwd_bwd in place, dense_act_vjp."""
+
+    path = "fused"
 
     def __init__(self, dl, w, dev):
         import torch
@@ -370,23 +376,34 @@ class HeadBench:
         self.W = torch.from_numpy(inp.W[0]).to(dev)
         self.b = torch.from_numpy(inp.b[0]).to(dev)
         self.logits = torch.empty(B, C, device=dev)
+        self.lse = torch.empty(B, device=dev)
         self.dX = torch.empty(B, d, device=dev)
         self.dW, self.db = torch.empty_like(self.W), torch.empty_like(self.b)
         self.m = [torch.zeros_like(self.W), torch.zeros_like(self.b)]
         self.v = [torch.zeros_like(self.W), torch.zeros_like(self.b)]
         self.loss = torch.empty(1, device=dev)
+        c = dl._c
         self.ws = torch.empty(max(dl.softmax_xent_workspace_size(B, C),
-                                  dl.dense_act_vjp_workspace_size(0, 0, B, d, C), 1),
+                                  dl.dense_act_vjp_workspace_size(0, 0, B, d, C),
+                                  c["dense_xent_fwd_workspace_size"](B, d, C),
+                                  c["dense_xent_vjp_workspace_size"](B, d, C), 1),
                               dtype=torch.uint8, device=dev)
         self.t = 0
 
     def step(self):
         dl, o = self.dl, self.w.optim
         self.t += 1
-        dl.dense_act_fwd(self.X, self.W, self.b, dl.ACT_IDENTITY, Y=self.logits)
-        dl.softmax_xent_fwd_bwd(self.logits, self.y, inplace=True, loss=self.loss, ws=self.ws)
-        dl.dense_act_vjp(self.logits, None, self.X, self.W, dX=self.dX, dW=self.dW, db=self.db,
-                         ws=self.ws)
+        if self.path == "fused":
+            dl.dense_xent_fwd(self.X, self.W, self.b, self.y, logits=self.logits, lse=self.lse,
+                              loss=self.loss, ws=self.ws)
+            dl.dense_xent_vjp(self.logits, self.lse, self.y, self.X, self.W, dX=self.dX,
+                              dW=self.dW, db=self.db, ws=self.ws)
+        else:
+            dl.dense_act_fwd(self.X, self.W, self.b, dl.ACT_IDENTITY, Y=self.logits)
+            dl.softmax_xent_fwd_bwd(self.logits, self.y, inplace=True, loss=self.loss,
+                                    ws=self.ws)
+            dl.dense_act_vjp(self.logits, None, self.X, self.W, dX=self.dX, dW=self.dW,
+                             db=self.db, ws=self.ws)
         for p, g, m, v in ((self.W, self.dW, self.m[0], self.v[0]),
                            (self.b, self.db, self.m[1], self.v[1])):
             dl.adamw_step(p, g, m, v, o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.t)
@@ -394,13 +411,19 @@ class HeadBench:
     def flops(self):
         return 3 * 2 * self.w.batch * self.w.dims[0] * self.w.dims[1]
 
+    def _tiles(self):
+        return -(-self.w.dims[1] // 128)  # column tiles of the forward (128 wide)
+
     def stage_work(self, label):
         B, d, C = self.w.batch, self.w.dims[0], self.w.dims[1]
         name, k = _split(label)
-        if name in ("fwd_gemm", "dw_gemm", "dx_gemm"):
+        if name in ("fwd_gemm", "dw_gemm", "dx_gemm", "xent_fwd_gemm", "xent_dw_gemm",
+                    "xent_dx_gemm"):
             return "flop", 2 * B * d * C
         if name == "xent":
             return "byte", 8 * B * C + 8 * B
+        if name == "xent_lse":  # the per-tile pairs, the label logit, lse and the row loss
+            return "byte", 8 * self._tiles() * B + 16 * B
         if name == "adamw":
             return "byte", 28 * (C * d if k == 0 else C)
         return None
@@ -410,10 +433,16 @@ class HeadBench:
         name, _ = _split(label)
         if name == "fwd_gemm":
             return gemm_bytes("fwd", B, C, d, bias=True)
+        if name == "xent_fwd_gemm":  # + the per-tile row statistics
+            return gemm_bytes("fwd", B, C, d, bias=True) + 8 * self._tiles() * B
         if name == "dx_gemm":
             return gemm_bytes("dx", B, d, C)
+        if name == "xent_dx_gemm":  # + lse and labels
+            return gemm_bytes("dx", B, d, C) + 8 * B
         if name == "dw_gemm":
             return gemm_bytes("dw", C, d, B, db=True)
+        if name == "xent_dw_gemm":
+            return gemm_bytes("dw", C, d, B, db=True) + 8 * B
         return None
 
     def cpu_sample(self, budget_s):
@@ -670,6 +699,9 @@ def main():
     ap.add_argument("--mlp-fusion", type=int, default=2, choices=(1, 2),
                     help="MLP workloads: 2 fuses the last hidden layer into the head kernel, "
                          "1 fuses the head alone")
+    ap.add_argument("--head-path", default="fused", choices=("fused", "composed"),
+                    help="classifier head: the fused head (default) or the composed "
+                         "forward / cross-entropy / vjp")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
@@ -689,6 +721,7 @@ def main():
     steps, warmup = DEFAULTS[args.config]
     steps = args.steps if args.steps is not None else steps
     warmup = args.warmup if args.warmup is not None else warmup
+    HeadBench.path = args.head_path
     bench = BENCHES[args.config](dl, w, dev)
     stream = torch.cuda.current_stream(dev)
     if args.copy_bytes > 0:
@@ -741,6 +774,23 @@ def main():
         if traffic is not None:
             roofline["traffic_ratio"] = round(traffic / alg, 3)
 
+    # launch floor: empty kernels back to back on the same stream
+    dl.empty_launches(200, dev)
+    torch.cuda.synchronize()
+    fe0, fe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_empty = 2000
+    t0 = time.perf_counter()
+    fe0.record(stream)
+    dl.empty_launches(n_empty, dev)
+    fe1.record(stream)
+    torch.cuda.synchronize()
+    empty_wall_us = 1e6 * (time.perf_counter() - t0) / n_empty
+    empty_gpu_us = 1e3 * fe0.elapsed_time(fe1) / n_empty
+    launch_floor = {"empty_kernel_us": round(empty_gpu_us, 3),
+                    "empty_kernel_wall_us": round(empty_wall_us, 3),
+                    "launches_per_step": len(stages),
+                    "floor_us_per_step": round(len(stages) * max(empty_gpu_us, empty_wall_us), 2)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_budget)
@@ -764,8 +814,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "dims": w.dims,
                    "optimizer": None if w.optim is None else w.optim.kind,
                    "gemm_flops_per_step": bench.flops(),
-                   "graph_replay": bool(args.graph), "mlp_fusion": args.mlp_fusion},
+                   "graph_replay": bool(args.graph), "mlp_fusion": args.mlp_fusion,
+                   **({"head_path": args.head_path} if isinstance(bench, HeadBench) else {})},
         "roofline": roofline,
+        "launch_floor": launch_floor,
         "stages": stages,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,

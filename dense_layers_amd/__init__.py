@@ -93,6 +93,7 @@ _c = {
     "dl_last_error": _sig("dl_last_error", ctypes.c_char_p, []),
     "dense_last_error": _sig("dense_last_error", ctypes.c_char_p, []),
     "dl_set_validate": _sig("dl_set_validate", _i32, [_i32]),
+    "dl_empty_launches": _sig("dl_empty_launches", _i32, [_vp, _i32]),
     "dl_build_target": _sig("dl_build_target", ctypes.c_char_p, []),
     "dense_act_fwd": _sig("dense_act_fwd", _i32,
                           [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -111,6 +112,16 @@ _c = {
     "softmax_xent_fwd_bwd": _sig("softmax_xent_fwd_bwd", _i32,
                                  [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "softmax_xent_workspace_size": _sig("softmax_xent_workspace_size", _sz, [_i64, _i64]),
+    "dense_xent_fwd": _sig("dense_xent_fwd", _i32,
+                           [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _sz]),
+    "dense_xent_fwd_workspace_size": _sig("dense_xent_fwd_workspace_size", _sz,
+                                          [_i64, _i64, _i64]),
+    "dense_xent_vjp": _sig("dense_xent_vjp", _i32,
+                           [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _sz]),
+    "dense_xent_vjp_workspace_size": _sig("dense_xent_vjp_workspace_size", _sz,
+                                          [_i64, _i64, _i64]),
     "sgd_step": _sig("sgd_step", _i32, [_vp, _i64, _vp, _vp, _f64]),
     "adamw_step": _sig("adamw_step", _i32,
                        [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
@@ -147,10 +158,14 @@ _c = {
     "dl_set_mlp_fusion": _sig("dl_set_mlp_fusion", _i32, [_i32]),
 }
 
-EXPORTS = ["dl_last_error", "dense_last_error", "dl_set_validate", "dl_build_target", "dense_act_fwd", "dense_act_vjp",
+EXPORTS = ["dl_last_error", "dense_last_error", "dl_set_validate", "dl_empty_launches",
+           "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_scaled", "dense_cast_f16_scaled", "dense_cast_f16_scaled_workspace_size",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
-           "softmax_xent_workspace_size", "sgd_step", "adamw_step",
+           "softmax_xent_workspace_size", "dense_xent_fwd",
+           "dense_xent_fwd_workspace_size", "dense_xent_vjp", "dense_xent_vjp_workspace_size",
+           "sgd_step",
+           "adamw_step",
            "dense_cast_bf16", "dense_cast_bf16_t", "dense_cast_f16", "dense_cast_f16_t",
            "mlp_train_step", "mlp_train_step_mse",
            "mlp_train_step_workspace_size", "adam_step", "ema_update", "clip_grad_norm",
@@ -195,6 +210,12 @@ def set_validate(on: bool) -> bool:
     LABEL_OUT_OF_RANGE instead of producing NaN rows.  Returns the previous
     setting."""
     return bool(_c["dl_set_validate"](1 if on else 0))
+
+
+def empty_launches(n: int, device=None):
+    """n empty-kernel launches on the current stream (the launch floor)."""
+    dev = torch.device("cuda") if device is None else device
+    _check(_c["dl_empty_launches"](torch.cuda.current_stream(dev).cuda_stream, n))
 
 
 def _check(status: int):
@@ -359,6 +380,75 @@ def softmax_xent_fwd_bwd(logits: torch.Tensor, labels: torch.Tensor,
                                       _ptr(loss), _ptr(row_loss), _ptr(dlogits), _ptr(ws),
                                       ws.numel()))
     return loss, dlogits
+
+
+def dense_xent_fwd(X: torch.Tensor, W: torch.Tensor, b: Optional[torch.Tensor],
+                   labels: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
+                   row_loss: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Fused classifier head, forward: logits = X W^T + b, lse per row, mean
+    softmax cross-entropy.  Returns (loss[1], logits, lse)."""
+    _dev(X, "X", torch.float32)
+    B, n_in = X.shape
+    _dev(W, "W", torch.float32)
+    C = W.shape[0]
+    _dev(W, "W", torch.float32, (C, n_in))
+    if b is not None:
+        _dev(b, "b", torch.float32, (C,))
+    _dev(labels, "labels", torch.int32, (B,))
+    if logits is None:
+        logits = torch.empty(B, C, dtype=torch.float32, device=X.device)
+    if lse is None:
+        lse = torch.empty(B, dtype=torch.float32, device=X.device)
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=X.device)
+    _dev(logits, "logits", torch.float32, (B, C))
+    _dev(lse, "lse", torch.float32, (B,))
+    if row_loss is not None:
+        _dev(row_loss, "row_loss", torch.float32, (B,))
+    need = _c["dense_xent_fwd_workspace_size"](B, n_in, C)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, X.device)
+    _check(_c["dense_xent_fwd"](_stream(X), B, n_in, C, _ptr(X), _ptr(W), _ptr(b), _ptr(labels),
+                                _ptr(logits), _ptr(lse), _ptr(loss), _ptr(row_loss), _ptr(ws),
+                                0 if ws is None else ws.numel()))
+    return loss, logits, lse
+
+
+def dense_xent_vjp(logits: torch.Tensor, lse: torch.Tensor, labels: torch.Tensor,
+                   X: Optional[torch.Tensor], W: Optional[torch.Tensor],
+                   dX: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+                   db: Optional[torch.Tensor] = None, need_dx: bool = True,
+                   need_dw: bool = True, ws: Optional[torch.Tensor] = None):
+    """Fused classifier head, backward from the forward's logits and lse:
+    returns (dX, dW, db) (None where not requested)."""
+    _dev(logits, "logits", torch.float32)
+    B, C = logits.shape
+    _dev(lse, "lse", torch.float32, (B,))
+    _dev(labels, "labels", torch.int32, (B,))
+    n_in = (X if X is not None else W).shape[1]
+    if need_dx:
+        _dev(W, "W", torch.float32, (C, n_in))
+        if dX is None:
+            dX = torch.empty(B, n_in, dtype=torch.float32, device=logits.device)
+        _dev(dX, "dX", torch.float32, (B, n_in))
+    if need_dw:
+        _dev(X, "X", torch.float32, (B, n_in))
+        if dW is None:
+            dW = torch.empty(C, n_in, dtype=torch.float32, device=logits.device)
+        if db is None:
+            db = torch.empty(C, dtype=torch.float32, device=logits.device)
+        _dev(dW, "dW", torch.float32, (C, n_in))
+        _dev(db, "db", torch.float32, (C,))
+    need = _c["dense_xent_vjp_workspace_size"](B, n_in, C)
+    if need > 0 and (ws is None or ws.numel() < need):
+        ws = _workspace(need, logits.device)
+    _check(_c["dense_xent_vjp"](_stream(logits), B, n_in, C, _ptr(logits), _ptr(lse),
+                                _ptr(labels), _ptr(X), _ptr(W),
+                                _ptr(dX) if need_dx else None, _ptr(dW) if need_dw else None,
+                                _ptr(db) if need_dw else None, _ptr(ws),
+                                0 if ws is None else ws.numel()))
+    return (dX if need_dx else None), (dW if need_dw else None), (db if need_dw else None)
 
 
 # ---------------------------------------------------------------- optimizers

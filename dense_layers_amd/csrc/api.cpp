@@ -314,6 +314,16 @@ const char* dl_last_error(void) { return g_last_error.c_str(); }
 
 const char* dense_last_error(void) { return g_last_error.c_str(); }
 
+int dl_empty_launches(void* stream, int n) {
+  if (n < 0) return fail(DL_INVALID_ARGUMENT, "dl_empty_launches: negative count");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = dl::launch_empty(s);
+    if (e != hipSuccess) return hip_fail(e, "dl_empty_launches");
+  }
+  return DL_OK;
+}
+
 int dl_set_validate(int on) {
   const int prev = g_validate;
   g_validate = on != 0;
@@ -506,6 +516,144 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C, const float* logits
   if (vs != DL_OK) return vs;
   hipError_t e = timed("xent", st, [&] { return dl::launch_xent(B, C, logits, labels, rl, dlogits, loss, st); });
   if (e != hipSuccess) return hip_fail(e, "softmax_xent_fwd_bwd");
+  return DL_OK;
+}
+
+// ---- fused classifier head over many classes ----------------------------------
+// Forward: one GEMM writes the logits and, per row and column tile, the tile's
+// (max, sum exp) pair; a row pass forms lse and the row losses, and the fixed
+// order mean follows.  Backward: the dX and dW GEMMs read the logits and form
+// the loss gradient from them and lse as they stage them (the gradient never
+// reaches HBM, and no pass over the logits runs between the two GEMMs).
+
+static int xent_tiles(int64_t B, int64_t in, int64_t C) {
+  const Plan p = plan_gemm(DL_F32, dl::EPI_FWD, B, C, in);
+  int bm, bn, bk;
+  tile_shape(DL_F32, p.tile, bm, bn, bk);
+  return (int)ceil_div(C, bn);
+}
+
+size_t dense_xent_fwd_workspace_size(int64_t B, int64_t in, int64_t C) {
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(C)) return 0;
+  return align_up((size_t)xent_tiles(B, in, C) * B * 8) + align_up((size_t)B * 4);
+}
+
+int dense_xent_fwd(void* stream, int64_t B, int64_t in, int64_t C, const float* X,
+                   const float* W, const float* b, const int32_t* labels, float* logits,
+                   float* lse, float* loss, float* row_loss, void* ws, size_t ws_bytes) {
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(C))
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_fwd: sizes must be in [1, 2^31)");
+  if (!X || !W || !labels || !logits || !lse || !loss)
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_fwd: X, W, labels, logits, lse and loss are required");
+  const size_t need = dense_xent_fwd_workspace_size(B, in, C);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "dense_xent_fwd: workspace %zu bytes, need %zu", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_fwd: workspace must be 256-byte aligned");
+  const size_t nz = (size_t)B * C * 4, nX = (size_t)B * in * 4, nW = (size_t)C * in * 4;
+  const struct { const void* p; size_t n; } outs[] = {{logits, nz}, {lse, (size_t)B * 4},
+                                                      {loss, 4}, {row_loss, (size_t)B * 4},
+                                                      {ws, need}};
+  const struct { const void* p; size_t n; } ins[] = {{X, nX}, {W, nW}, {b, (size_t)C * 4},
+                                                     {labels, (size_t)B * 4}};
+  for (size_t i = 0; i < 5; ++i) {
+    for (size_t j = 0; j < 4; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+        return fail(DL_ALIASING, "dense_xent_fwd: an output overlaps an input");
+    for (size_t j = i + 1; j < 5; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(DL_ALIASING, "dense_xent_fwd: two outputs overlap");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsp = static_cast<char*>(ws);
+  const int T = xent_tiles(B, in, C);
+  float* part = reinterpret_cast<float*>(wsp);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(wsp + align_up((size_t)T * B * 8));
+  const int vs = check_labels("dense_xent_fwd", s, B, C, labels, wsp);
+  if (vs != DL_OK) return vs;
+  dl::GemmDesc d = blank_desc();
+  d.M = (int)B; d.N = (int)C; d.K = (int)in;
+  d.A = X; d.lda = in; d.a_layout = dl::K_MAJOR;
+  d.B = W; d.ldb = in; d.b_layout = dl::K_MAJOR;
+  d.C = logits; d.ldc = C;
+  d.epi = dl::EPI_FWD;
+  d.bias = b; d.act = DL_ACT_IDENTITY;
+  d.k_per_split = (int)in;
+  d.xent_part = part;
+  const Plan p = plan_gemm(DL_F32, dl::EPI_FWD, B, C, in);
+  hipError_t e = timed("xent_fwd_gemm", s, [&] { return dl::launch_gemm_f32(d, p.tile, s); });
+  if (e == hipSuccess)
+    e = timed("xent_lse", s, [&] { return dl::launch_xent_lse(B, C, T, part, logits, labels, lse, rl, s); });
+  if (e == hipSuccess)
+    e = timed("loss_mean", s, [&] { return dl::launch_loss_mean(B, rl, loss, s); });
+  if (e != hipSuccess) return hip_fail(e, "dense_xent_fwd");
+  return DL_OK;
+}
+
+size_t dense_xent_vjp_workspace_size(int64_t B, int64_t in, int64_t C) {
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(C)) return 0;
+  // the per-row records (and one spare), then the dW split-K slices
+  return align_up((size_t)(B + 1) * 8) +
+         splitk_bytes(plan_gemm(DL_F32, dl::EPI_DW, C, in, B), C, in);
+}
+
+int dense_xent_vjp(void* stream, int64_t B, int64_t in, int64_t C, const float* logits,
+                   const float* lse, const int32_t* labels, const float* X, const float* W,
+                   float* dX, float* dW, float* db, void* ws, size_t ws_bytes) {
+  if (!dim_ok(B) || !dim_ok(in) || !dim_ok(C))
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_vjp: sizes must be in [1, 2^31)");
+  if (!logits || !lse || !labels)
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_vjp: logits, lse and labels are required");
+  if ((dW || db) && !X) return fail(DL_INVALID_ARGUMENT, "dense_xent_vjp: X is required for dW/db");
+  if (dX && !W) return fail(DL_INVALID_ARGUMENT, "dense_xent_vjp: W is required for dX");
+  if (db && !dW) return fail(DL_UNSUPPORTED, "dense_xent_vjp: db is reduced inside the dW kernel; pass dW too");
+  const size_t need = dense_xent_vjp_workspace_size(B, in, C);
+  if (!ws || ws_bytes < need)
+    return fail(DL_WORKSPACE_TOO_SMALL, "dense_xent_vjp: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DL_INVALID_ARGUMENT, "dense_xent_vjp: workspace must be 256-byte aligned");
+  const size_t nz = (size_t)B * C * 4, nX = (size_t)B * in * 4, nW = (size_t)C * in * 4;
+  const struct { const void* p; size_t n; } outs[] = {{dX, nX}, {dW, nW}, {db, (size_t)C * 4},
+                                                      {ws, need}};
+  const struct { const void* p; size_t n; } ins[] = {{logits, nz}, {lse, (size_t)B * 4},
+                                                     {labels, (size_t)B * 4}, {X, nX}, {W, nW}};
+  for (size_t i = 0; i < 4; ++i) {
+    for (size_t j = 0; j < 5; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+        return fail(DL_ALIASING, "dense_xent_vjp: an output overlaps an input");
+    for (size_t j = i + 1; j < 4; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(DL_ALIASING, "dense_xent_vjp: two outputs overlap");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float invB = (float)(1.0 / (double)B);
+  const float log2B = (float)std::log2((double)B);
+  char* wsp = static_cast<char*>(ws);
+  float* rows = reinterpret_cast<float*>(wsp);
+  hipError_t e = timed("xent_rows", s, [&] {
+    return dl::launch_xent_rows(B, lse, labels, log2B, rows, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "dense_xent_vjp (rows)");
+  if (dW) {
+    const Plan p = plan_gemm(DL_F32, dl::EPI_DW, C, in, B);
+    dl::GemmDesc d = dw_desc(DL_F32, B, in, C, logits, X, dW, db,
+                             wsp + align_up((size_t)(B + 1) * 8), p);
+    d.xent_rows = rows; d.xent_invB = invB;
+    e = timed("xent_dw_gemm", s, [&] { return dl::launch_gemm_f32(d, p.tile, s); });
+    if (e == hipSuccess && p.splits > 1)
+      e = timed("splitk_reduce", s, [&] {
+        return dl::launch_splitk_reduce((int)C, (int)in, p.splits, d.partial, d.db_partial, dW, in,
+                                        db, s);
+      });
+    if (e != hipSuccess) return hip_fail(e, "dense_xent_vjp (dW)");
+  }
+  if (dX) {
+    dl::GemmDesc d = dx_desc(B, in, C, logits, W, nullptr, dX, DL_ACT_IDENTITY, nullptr);
+    d.xent_rows = rows; d.xent_invB = invB;
+    const Plan p = plan_gemm(DL_F32, dl::EPI_DX, B, in, C);
+    e = timed("xent_dx_gemm", s, [&] { return dl::launch_gemm_f32(d, p.tile, s); });
+    if (e != hipSuccess) return hip_fail(e, "dense_xent_vjp (dX)");
+  }
   return DL_OK;
 }
 

@@ -10,6 +10,7 @@
 
 namespace dl {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -205,6 +206,20 @@ struct GemmDesc {
   // divided by s before they are stored.  dX products keep the scale (dX is
   // the next layer's gradient operand).  Null: no scale.
   const float* out_scale;
+  // Fused classifier head over many classes (float32 kernels only).
+  // Forward: with xent_part set, the epilogue also leaves, for every output
+  // row and column tile tn, the tile's (max z, sum exp(z - max)) over its
+  // columns as two floats at xent_part[2 (tn M + row)].
+  float* xent_part;
+  // dX / dW of the head: with xent_rows set, the A operand holds the logits
+  // [rows, C] and becomes the loss gradient
+  //   g = 2^(z log2 e - o_i) - [class == y_i] xent_invB  (= exp(z - lse_i) / B - ...)
+  // as it is staged into LDS (rows are batch rows, classes the head's
+  // outputs; elements past the operand's K range stay zero).  xent_rows
+  // holds one 8-byte record per batch row i: the exponent offset
+  // o_i = lse_i log2 e + log2 B, and the label y_i (its int32 bits).
+  const float* xent_rows;
+  float xent_invB;
 };
 
 // 1 / s of a descriptor's gradient-operand scale (1 without one).
@@ -296,6 +311,36 @@ template <> struct Raw4<f16_t> {
     return HalfOps<HK_F16>::to_f32((e & 1) ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
   }
 };
+
+// Max / sum over groups of N consecutive lanes (N = 16 or 32), left in every
+// lane of the group: DPP moves within each row of 16 lanes (swap neighbours,
+// swap pairs, mirror each half of 8, mirror the 16), then for N = 32 one
+// exchange with the other row.  Each step combines the same two values in
+// every lane (in swapped order), so all lanes of a group end bit-identical.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert(N == 16 || N == 32, "groups of 16 or 32 lanes");
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  if (N == 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 16 || N == 32, "groups of 16 or 32 lanes");
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  if (N == 32) v += __shfl_xor(v, 16);
+  return v;
+}
 
 // A tile whose float32 staging copy exceeds kStageBudget bytes is staged in
 // WGM passes of BM / WGM rows (the rows of one row of waves each).
@@ -415,7 +460,41 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
     if (masked && pass + 1 < PASSES)
       load_mask_pass<TO, BM, BN, WGM, WGN>(ms_next, d, tm, tn, pass + 1, out_vec);
 
-    if (nv > 0) {
+    const bool xent = EPI == EPI_FWD && d.xent_part != nullptr;
+    if (xent) {
+      // Logits and, for a fused softmax over many classes, each row's max
+      // and sum of exp(z - max) over this tile's columns, from the same
+      // float32 z = acc + bias the logits are stored as.  The CPR lanes
+      // sharing a row (consecutive lanes of one wave) reduce across lanes;
+      // every lane takes part (columns past N count as -inf, rows past M
+      // are computed and not stored), and the group's first lane stores.
+#pragma unroll
+      for (int it = 0; it < RPT; ++it) {
+        const int rl = tid / CPR + it * (NT / CPR);
+        const int row = prow0 + rl;
+        float v[4];
+        Store4<float>::load_vec(stage + rl * SS + c4, v);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] += bias[e];
+          if (e < nv) mx = fmaxf(mx, v[e]);
+        }
+        if (row < M && nv > 0) {
+          const int64_t o = (int64_t)row * ld + col;
+          if (colfull) Store4<TO>::vec(out + o, v);
+          else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+        }
+        mx = lanes_max<CPR>(mx);
+        float se = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nv) se += __expf(v[e] - mx);
+        se = lanes_sum<CPR>(se);
+        if ((tid % CPR) == 0 && row < M)
+          *reinterpret_cast<f32x2*>(d.xent_part + 2 * ((int64_t)tn * M + row)) = f32x2{mx, se};
+      }
+    } else if (nv > 0) {
 #pragma unroll
       for (int it = 0; it < RPT; ++it) {
         const int rl = tid / CPR + it * (NT / CPR);
@@ -504,9 +583,19 @@ hipError_t launch_cast_bf16_t(int64_t rows, int64_t cols, const float* src, bf16
 int safe_scale_parts(int64_t n);
 hipError_t launch_cast_f16_scaled(int64_t n, const float* src, bf16_t* dst, float* scale,
                                   float* part, hipStream_t s);
+// Fused classifier head: lse and the per-row losses from the forward's
+// per-tile partials ([T][B] pairs of max and sum exp), in tile order.
+hipError_t launch_xent_lse(int64_t B, int64_t C, int T, const float* part, const float* logits,
+                           const int32_t* labels, float* lse, float* row_loss, hipStream_t s);
+// The fused head's per-row records for its backward GEMMs: rows[2 i] =
+// lse[i] log2 e + log2B, rows[2 i + 1] = the bits of labels[i].
+hipError_t launch_xent_rows(int64_t B, const float* lse, const int32_t* labels, float log2B,
+                            float* rows, hipStream_t s);
 hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        const int32_t* labels, float* row_loss, float* dlogits,
                        float* loss, hipStream_t s, const float* dscale = nullptr);
+// One launch of an empty kernel (the launch floor).
+hipError_t launch_empty(hipStream_t s);
 // Number of labels outside [0, C) into bad[0] (one workgroup, no atomics).
 hipError_t launch_label_check(int64_t B, int64_t C, const int32_t* labels, int* bad,
                               hipStream_t s);

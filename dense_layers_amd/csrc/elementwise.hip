@@ -321,4 +321,13 @@ hipError_t launch_cast_bf16(int64_t n, const float* src, bf16_t* dst, hipStream_
   return hipGetLastError();
 }
 
+// An empty kernel: the cost of a launch and nothing else, for the launch
+// floor of latency-bound steps.
+__global__ void __launch_bounds__(64) empty_kernel() {}
+
+hipError_t launch_empty(hipStream_t s) {
+  hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+}
+
 }  // namespace dl

@@ -29,7 +29,20 @@ namespace {
 
 constexpr int kPad = 4;  // floats of padding per LDS row
 
-template <int ROWS, int BK, int LAY, int NT>
+// XF: the operand holds logits [batch rows, classes] of a fused classifier
+// head and is turned into the softmax cross-entropy gradient
+//   g = (exp(z - lse[i]) - [c == label[i]]) * invB
+// on its way to LDS (in store(), when the loads have landed, so the loads
+// of the next K step stay in flight meanwhile).  Each float4 holds four
+// classes of one batch row: for a K-major operand (dX = G W) the batch row
+// is the tile row and the classes run along K; for an M-major operand
+// (dW = G^T X) the batch row is the K index and the classes are the tile
+// rows.  Each batch row's (exponent offset, label) pair comes from an 8-byte
+// record (xent_rows): for a K-major operand the rows do not change along K
+// and the records are loaded once per tile (prime), for an M-major operand
+// one record per vector is loaded with the logits.  Elements past the K
+// range (zero-filled by the bounds-checked load) stay zero.
+template <int ROWS, int BK, int LAY, int NT, bool XF = false>
 struct TileLoader {
   // A tile is ROWS (M or N) x BK (K) elements, moved as float4 vectors.
   static constexpr int kVecs = ROWS * BK / 4;
@@ -39,6 +52,65 @@ struct TileLoader {
   static constexpr int kLdsSize = (LAY == K_MAJOR) ? ROWS * (BK + kPad) : BK * (ROWS + kPad);
 
   f32x4 r[kPer];
+  // XF state: the batch row's exponent offset (lse log2 e + log2 B) and
+  // label per vector, the K range and first tile row of the last load, and
+  // the operand's constants.
+  float xl[XF ? kPer : 1];
+  int xy[XF ? kPer : 1];
+  int xk0 = 0, xkend = 0, xrow0 = 0;
+  bool xsafe = false;
+  const f32x2* xrec = nullptr;
+  float xinvB = 0.f;
+
+  __device__ __forceinline__ void bind(const GemmDesc& d) {
+    xrec = reinterpret_cast<const f32x2*>(d.xent_rows);
+    xinvB = d.xent_invB;
+  }
+
+  // (offset, label) of vector i's batch row (XF only); `brow` is in range.
+  __device__ __forceinline__ void load_row_stats(int i, int brow) {
+    const f32x2 rec = xrec[brow];
+    xl[i] = rec[0];
+    xy[i] = __float_as_int(rec[1]);
+  }
+
+  // K-major XF operand: the batch rows of this thread's vectors for the
+  // tile starting at row0 (the same in every K step).
+  __device__ __forceinline__ void prime(int row0, int nrows, int tid) {
+    if (!XF || LAY != K_MAJOR) return;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) load_row_stats(i, min(row0 + vec(i, tid) / (BK / 4), nrows - 1));
+  }
+
+  // Which vector of the tile load i of thread tid moves.  In general
+  // consecutive threads take consecutive vectors (tid + i NT).  An M-major
+  // XF operand instead gives each group of kVPR threads (one k-row's
+  // vectors) kPer consecutive k-rows, so a thread's vectors lie in adjacent
+  // batch rows and one load brings all their records.  Only which thread
+  // moves a vector changes: the LDS tile is the same.
+  static constexpr int kVPR = ROWS / 4;  // vectors per k-row (M-major)
+  static constexpr bool kGroupK = XF && LAY == MN_MAJOR;
+  static_assert(!kGroupK || (NT % kVPR == 0 && (NT / kVPR) * kPer == BK && kPer <= 2),
+                "grouped k-rows");
+  __device__ __forceinline__ static int vec(int i, int tid) {
+    return kGroupK ? (tid % kVPR) + kVPR * (kPer * (tid / kVPR) + i) : tid + i * NT;
+  }
+
+  // M-major XF operand: the records of this thread's kPer consecutive batch
+  // rows from k0 on, in one load (the record buffer holds one spare record
+  // past the batch, so the pair may reach one row past kend).
+  __device__ __forceinline__ void load_group_stats(int k0, int kend, int tid) {
+    const int kb = min(k0 + kPer * (tid / kVPR), kend - 1);
+    if (kPer == 2) {
+      const f32x4 rec = *reinterpret_cast<const f32x4*>(xrec + kb);
+      xl[0] = rec[0];
+      xy[0] = __float_as_int(rec[1]);
+      xl[kPer - 1] = rec[2];
+      xy[kPer - 1] = __float_as_int(rec[3]);
+    } else {
+      load_row_stats(0, kb);
+    }
+  }
 
   // Full K step, 16-byte aligned rows: plain vector loads with no
   // per-element control flow, so the loads of a K step stay in flight
@@ -50,7 +122,7 @@ struct TileLoader {
                                             int row0, int nrows, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int v = tid + i * NT;
+      const int v = vec(i, tid);
       if (LAY == K_MAJOR) {
         const int row = min(row0 + v / (BK / 4), nrows - 1);
         const int k = k0 + (v % (BK / 4)) * 4;
@@ -62,6 +134,13 @@ struct TileLoader {
         r[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)k * ld + row);
       }
     }
+    if (XF) {
+      if (kGroupK) load_group_stats(k0, k0 + BK, tid);
+      xk0 = k0;
+      xkend = k0 + BK;
+      xrow0 = row0;
+      xsafe = false;
+    }
   }
 
   // Edge tiles: element loads, zero outside [0, nrows) x [k0, kend).
@@ -69,7 +148,7 @@ struct TileLoader {
                                             int row0, int nrows, int k0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int v = tid + i * NT;
+      const int v = vec(i, tid);
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if (LAY == K_MAJOR) {
         const int row = row0 + v / (BK / 4);
@@ -92,18 +171,51 @@ struct TileLoader {
       }
       r[i] = x;
     }
+    if (XF) {
+      if (kGroupK) load_group_stats(k0, kend, tid);
+      xk0 = k0;
+      xkend = kend;
+      xrow0 = row0;
+      xsafe = true;
+    }
+  }
+
+  // XF: the loss gradient of vector i (see the struct comment), formed as
+  // one base-2 exponential per element: exp(z - lse) / B =
+  // 2^(z log2(e) - (lse log2(e) + log2 B)) with the row's offset from its
+  // record; the one-hot lands on at most one element of a vector.
+  __device__ __forceinline__ f32x4 xent_grad(int i, int v) const {
+    constexpr float kLog2e = 1.4426950408889634f;
+    f32x4 x = r[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -xl[i]));
+    const int c0 = LAY == K_MAJOR ? xk0 + (v % (BK / 4)) * 4 : xrow0 + (v % (ROWS / 4)) * 4;
+    const unsigned dj = (unsigned)(xy[i] - c0);
+    if (dj < 4u) {  // the label is one of these 4 classes: rare, so a branch
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = dj == (unsigned)j ? x[j] - xinvB : x[j];
+    }
+    if (xsafe) {  // bounds-checked load: elements past the K range stay zero
+      if (LAY == K_MAJOR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = c0 + j < xkend ? x[j] : 0.0f;
+      } else if (xk0 + v / (ROWS / 4) >= xkend) {
+        x = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return x;
   }
 
   __device__ __forceinline__ void store(float* __restrict__ lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int v = tid + i * NT;
+      const int v = vec(i, tid);
       int off;
       if (LAY == K_MAJOR)
         off = (v / (BK / 4)) * kLdsStride + (v % (BK / 4)) * 4;
       else
         off = (v / (ROWS / 4)) * kLdsStride + (v % (ROWS / 4)) * 4;
-      *reinterpret_cast<f32x4*>(lds + off) = r[i];
+      *reinterpret_cast<f32x4*>(lds + off) = XF ? xent_grad(i, v) : r[i];
     }
   }
 
@@ -133,7 +245,7 @@ constexpr int f32_smem_floats() {
 
 // One workgroup's work item: workgroup `wg` of `nwg` working on the GEMM `d`
 // (tiles in the XCD-aware band order of tile_coords), LDS at `smem`.
-template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, int tiles_n,
                                               int a_vec, int b_vec, int out_vec, int wg, int nwg,
                                               float* smem) {
@@ -141,7 +253,7 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1 && BK % 8 == 0, "bad tile");
-  using LA = TileLoader<BM, BK, ALAY, NT>;
+  using LA = TileLoader<BM, BK, ALAY, NT, XF>;
   using LB = TileLoader<BN, BK, BLAY, NT>;
   // buffer b of A at smem + b * LA::kLdsSize, of B after both A buffers
   auto As = [&](int b) { return smem + b * LA::kLdsSize; };
@@ -165,6 +277,10 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
 
   LA la;
   LB lb;
+  if (XF) {
+    la.bind(d);
+    la.prime(tm * BM, M, tid);
+  }
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -217,6 +333,10 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   // set 2 holds step kt + 1 in flight.
   LA la2;
   LB lb2;
+  if (XF) {
+    la2.bind(d);
+    la2.prime(tm * BM, M, tid);
+  }
   if (nk > 0) {
     if (nk_full > 0) {
       la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
@@ -316,12 +436,12 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   store_tile<float, BM, BN, WGM, WGN, EPI>(acc, smem, d, tm, tn, split, out_vec);
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   __shared__ __attribute__((aligned(16))) float smem[f32_smem_floats<BM, BN, BK, WGM, WGN, ALAY, BLAY>()];
-  gemm_f32_body<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>(d, tiles_m, tiles_n, a_vec, b_vec, out_vec,
-                                                       blockIdx.x, gridDim.x, smem);
+  gemm_f32_body<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>(d, tiles_m, tiles_n, a_vec, b_vec,
+                                                           out_vec, blockIdx.x, gridDim.x, smem);
 }
 
 // Two small products in one launch (64x64 tiles of 4 waves for both):
@@ -370,12 +490,12 @@ hipError_t make_job(const GemmDesc& d, F32Job& j) {
   return hipSuccess;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   F32Job j;
   const hipError_t e = make_job<BM, BN>(d, j);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI>),
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>),
                      dim3((unsigned)j.nwg), dim3(WGM * WGN * 64), 0, s, d, j.tiles_m,
                      j.tiles_n, j.a_vec, j.b_vec, j.out_vec);
   return hipGetLastError();
@@ -383,6 +503,13 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
 
 template <int BM, int BN, int BK, int WGM, int WGN>
 hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
+  if (d.xent_rows != nullptr) {  // the fused head's dX and dW: A is the logits
+    if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR && d.mask_act == ACT_IDENTITY)
+      return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, true>(d, s);
+    if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
+      return launch_tile<BM, BN, BK, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, true>(d, s);
+    return hipErrorInvalidValue;
+  }
   if (d.epi == EPI_FWD && d.a_layout == K_MAJOR && d.b_layout == K_MAJOR)
     return launch_tile<BM, BN, BK, WGM, WGN, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)

@@ -267,6 +267,46 @@ loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restric
   }
 }
 
+// Fused classifier head, after its forward GEMM: row i's log-sum-exp from the
+// T column tiles' (max, sum exp(z - max)) pairs part[2 (t B + i)]:
+//   m = max_t m_t,  s = sum_t s_t exp(m_t - m)  (tile order),  lse = m + log s,
+// and its loss lse - z[i, y_i] (NaN for a label outside [0, C)).  One thread
+// per row; the pairs of consecutive rows are adjacent, so each tile's read
+// is one coalesced 8-byte access per thread.
+constexpr int kLseBlock = 256;
+__global__ void __launch_bounds__(kLseBlock)
+xent_lse_kernel(int64_t B, int64_t C, int T, const float* __restrict__ part,
+                const float* __restrict__ logits, const int32_t* __restrict__ labels,
+                float* __restrict__ lse, float* __restrict__ row_loss) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const int64_t row = (int64_t)blockIdx.x * kLseBlock + threadIdx.x;
+  if (row >= B) return;
+  const f32x2* p = reinterpret_cast<const f32x2*>(part) + row;
+  float m = -INFINITY;
+  for (int t = 0; t < T; ++t) m = fmaxf(m, p[(int64_t)t * B][0]);
+  float s = 0.f;
+  for (int t = 0; t < T; ++t) {
+    const f32x2 v = p[(int64_t)t * B];
+    s += v[1] * __expf(v[0] - m);
+  }
+  const float l = m + logf(s);
+  lse[row] = l;
+  const int32_t y = labels[row];
+  row_loss[row] = (y >= 0 && (int64_t)y < C) ? l - logits[row * C + y] : __builtin_nanf("");
+}
+
+// Per-row records of the fused head's backward: exponent offset and label.
+__global__ void __launch_bounds__(kLseBlock)
+xent_rows_pack_kernel(int64_t B, const float* __restrict__ lse, const int32_t* __restrict__ labels,
+                      float log2B, float* __restrict__ rows) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const int64_t i = (int64_t)blockIdx.x * kLseBlock + threadIdx.x;
+  if (i >= B) return;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const f32x2 rec = {fmaf(lse[i], kLog2e, log2B), __int_as_float(labels[i])};
+  reinterpret_cast<f32x2*>(rows)[i] = rec;
+}
+
 // Labels outside [0, C): one workgroup strides over the batch, counts per
 // thread, then a fixed-order tree; one lane stores the count.
 __global__ void __launch_bounds__(kMeanThreads)
@@ -327,6 +367,22 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
   }
   if (e != hipSuccess) return e;
   return launch_loss_mean(B, row_loss, loss, s);
+}
+
+hipError_t launch_xent_lse(int64_t B, int64_t C, int T, const float* part, const float* logits,
+                           const int32_t* labels, float* lse, float* row_loss, hipStream_t s) {
+  const int64_t blocks = (B + kLseBlock - 1) / kLseBlock;
+  hipLaunchKernelGGL(xent_lse_kernel, dim3((unsigned)blocks), dim3(kLseBlock), 0, s, B, C, T,
+                     part, logits, labels, lse, row_loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_xent_rows(int64_t B, const float* lse, const int32_t* labels, float log2B,
+                            float* rows, hipStream_t s) {
+  const int64_t blocks = (B + kLseBlock - 1) / kLseBlock;
+  hipLaunchKernelGGL(xent_rows_pack_kernel, dim3((unsigned)blocks), dim3(kLseBlock), 0, s, B, lse,
+                     labels, log2B, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_label_check(int64_t B, int64_t C, const int32_t* labels, int* bad,

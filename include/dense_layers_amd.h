@@ -143,6 +143,15 @@ int dl_profile_end(int max, float* ms, char* names);
  */
 int dl_set_mlp_fusion(int level);
 
+/*
+ * dl_empty_launches -- n launches of an empty kernel (one workgroup of 64
+ * threads) on `stream`, for measurement: the launch floor that a
+ * latency-bound step of k launches cannot go below is k times the time of
+ * one such launch.  Returns DL_OK, DL_INVALID_ARGUMENT for n < 0, or
+ * DL_HIP_ERROR.
+ */
+int dl_empty_launches(void* stream, int n);
+
 /* ---- dense layer forward ------------------------------------------------- */
 
 /*
@@ -255,6 +264,54 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C,
                          void* ws, size_t ws_bytes);
 
 size_t softmax_xent_workspace_size(int64_t B, int64_t C);
+
+
+/* ---- fused classifier head over many classes ----------------------------- */
+
+/*
+ * dense_xent_fwd / dense_xent_vjp -- a Linear head closed by softmax
+ * cross-entropy, for large class counts, in two calls that never
+ * materialise the loss gradient (the fused cross-entropy of the Orthon
+ * page, "Selected Orthon vs. PyTorch results", whose advantage grows with
+ * the class count, taken into the GEMMs; the LinearAct forward / vjp pair of
+ * the noeira.nn docs, "The design in one page").  Float32 throughout.
+ *
+ * dense_xent_fwd: logits = X W^T + b from one GEMM whose epilogue also
+ * leaves, per row and tile of columns, the tile's max and sum of exp; a row
+ * pass then forms lse_i = log sum_j exp(z_ij) and the row loss
+ * lse_i - z[i, y_i], and the loss is their fixed-order mean.
+ *   B, in, C > 0; X device [B, in]; W device [C, in]; b device [C] or NULL;
+ *   labels device int32 [B] in [0, C) (validate mode: DL_LABEL_OUT_OF_RANGE;
+ *   otherwise an out-of-range label gives a NaN row loss and is never read
+ *   out of bounds); logits device [B, C] output; lse device [B] output;
+ *   loss device [1] output (mean over the batch); row_loss device [B]
+ *   output or NULL.  ws: dense_xent_fwd_workspace_size(B, in, C) bytes
+ *   (the per-tile pairs, 8 B per row per 128 classes, and the row losses).
+ *   No output may overlap an input or another output.
+ *
+ * dense_xent_vjp: with g = (exp(z - lse) - onehot(y)) / B formed from the
+ * logits inside both GEMMs as they read them,
+ *   dX = g W,  dW = g^T X,  db = sum_rows g   (dW / db overwritten).
+ *   logits, lse, labels as left by dense_xent_fwd (unchanged since); X, W
+ *   as passed to it.  dX [B, in], dW [C, in], db [C]: outputs, each may be
+ *   NULL (db needs dW: it is summed inside the dW kernel).  ws:
+ *   dense_xent_vjp_workspace_size(B, in, C) bytes, 256-byte aligned (one
+ *   8-byte record per row: the row's exponent offset and label, formed by a
+ *   small pass before the GEMMs; then split-K slices of dW for small
+ *   batches).
+ * The gradient matches softmax_xent_fwd_bwd's to float32 rounding (it is
+ * formed as exp(z - lse) rather than exp(z - max) / sum).
+ */
+int dense_xent_fwd(void* stream, int64_t B, int64_t in, int64_t C,
+                   const float* X, const float* W, const float* b,
+                   const int32_t* labels, float* logits, float* lse, float* loss,
+                   float* row_loss, void* ws, size_t ws_bytes);
+size_t dense_xent_fwd_workspace_size(int64_t B, int64_t in, int64_t C);
+int dense_xent_vjp(void* stream, int64_t B, int64_t in, int64_t C,
+                   const float* logits, const float* lse, const int32_t* labels,
+                   const float* X, const float* W, float* dX, float* dW, float* db,
+                   void* ws, size_t ws_bytes);
+size_t dense_xent_vjp_workspace_size(int64_t B, int64_t in, int64_t C);
 
 /* ---- optimizers ---------------------------------------------------------- */
 

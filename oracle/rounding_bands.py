@@ -84,31 +84,50 @@ def act_out_dev(z, tau, act: int) -> np.ndarray:
     return tau + U32 * (z + tau)
 
 
-def xent_grad_band(z, tau, batch_total: int, scale: float = 1.0, labels=None) -> np.ndarray:
+def xent_grad_band(z, tau, batch_total: int, scale: float = 1.0, labels=None,
+                   form: str = "softmax") -> np.ndarray:
     """Bound on |g' - g| for the softmax cross-entropy gradient
     g = scale (softmax(z) - onehot) / batch_total per row, when g' is formed
     in float32 from logits z' with |z' - z| <= tau (elementwise).
 
-    The float32 evaluation is taken to be: the row max m' (exact), the
-    exponentials e'_j = exp(z'_j - m') with the argument rounded twice (the
-    difference, then its scaling to base 2: relative error 2u|z_j - m| in the
-    result) and the exponential itself within 4u, their float32 sum s' in any
-    order (gamma_C), p'_j = e'_j / s' (one rounding), then p' minus the
-    one-hot times 1/batch_total, itself rounded and times the loss scale
-    (four roundings: gamma_4).
+    form "softmax" (one pass over a row held whole): the row max m'
+    (exact), the exponentials e'_j = exp(z'_j - m') with the argument
+    rounded twice (the difference, then its scaling to base 2: relative
+    error 2u|z_j - m| in the result) and the exponential itself within 4u,
+    their float32 sum s' in any order (gamma_C), p'_j = e'_j / s' (one
+    rounding).
+    form "lse" (a row split into column tiles, as a GEMM epilogue sees it):
+    per tile t its max m_t and s_t = sum exp(z - m_t), then
+    s' = sum_t s_t exp(m_t - m) (each term two exponentials and a product:
+    relative error (2|z_j - m| + 9) u), lse' = m + log s' (log within 2u of
+    its result, the sum rounded once), and p'_j / B formed again from the
+    logits as one base-2 exponential 2^(z log2 e - (lse log2 e + log2 B))
+    (the exponent offset and the exponent each rounded, the exponential
+    within 4u: relative error 2u (|z_j - lse| + |lse| + ln B) + 4u).
+    Either way g' is then p' minus the one-hot times 1/batch_total, itself
+    rounded and times the loss scale (four roundings: gamma_4).
+
     With delta_j = tau_j + max_k tau_k (the shift of z_j - m, since the max
-    moves by at most max_k tau_k):
-      eps_j = exp(delta_j) (1 + 2u|z_j - m| + 4u) - 1     |e'_j / e_j - 1|
+    moves by at most max_k tau_k) and rho_j the rounding just listed:
+      eps_j = exp(delta_j) (1 + rho_j) - 1     (|e'_j / e_j - 1|)
       eps_s = (sum_j e_j eps_j + gamma_C sum_j e_j (1 + eps_j)) / s
-      dp_j  = p_j ((1 + eps_j)(1 + u) / (1 - eps_s) - 1),
-    and since the p'_j of a row add up to 1 within gamma_{C+2} (the sum's
-    and the divisions' roundings), a probability may move by no more than
-    the others move in all: dp_j <= sum_{k != j} dp_k + gamma_{C+2} (the
-    tighter of the two for a dominant class, whose relative bound is loose
-    by 1 / (1 - p_j)).  Then
-      |g'_j - g_j| <= (scale / B) (dp_j + gamma_4 (|p_j - onehot_j| + dp_j)).
-    Without ``labels`` the bound takes |p_j - onehot_j| <= 1.
+    "softmax":
+      dp_j = p_j ((1 + eps_j)(1 + u) / (1 - eps_s) - 1),
+      and since the p'_j of a row add up to 1 within gamma_{C+2}, a
+      probability moves by no more than the others in all:
+      dp_j <= sum_{k != j} dp_k + gamma_{C+2} (tighter for a dominant class).
+    "lse":
+      Lambda = max_k tau_k - log(1 - eps_s) + 2u |log s| + u |lse|,
+      dp_j = p_j (exp(tau_j + Lambda) (1 + 2u (|z_j - lse| + |lse| + ln B)
+                  + 4u) - 1).
+    Then |g'_j - g_j| <= (scale / B) (dp_j + gamma_4 (|p_j - onehot_j| + dp_j)).
+    Without ``labels`` the bound takes |p_j - onehot_j| <= 1.  Both
+    probabilities lie in [0, 1], so dp_j never exceeds 1 (plus rounding);
+    a row whose logit deviation leaves the sum unbounded (eps_s >= 1) gets
+    that cap for every class.
     """
+    if form not in ("softmax", "lse"):
+        raise ValueError(f"unknown form {form}")
     z = np.asarray(z, dtype=np.float64)
     tau = np.asarray(tau, dtype=np.float64)
     B, C = z.shape
@@ -116,29 +135,49 @@ def xent_grad_band(z, tau, batch_total: int, scale: float = 1.0, labels=None) ->
     d = z - m                                   # <= 0
     e = np.exp(d)
     s = e.sum(axis=1, keepdims=True)
-    # eps = exp(tau + max tau) (1 + 4u - 2u d) - 1, built in place
-    eps = tau + tau.max(axis=1, keepdims=True)
+    tmax = tau.max(axis=1, keepdims=True)
+    # eps = exp(tau + max tau) (1 + rho) - 1, rho = (c0 - 2 d) u, built in place
+    eps = tau + tmax
     np.exp(eps, out=eps)
     d *= -2.0 * U32
-    d += 1.0 + 4.0 * U32
+    d += 1.0 + (4.0 if form == "softmax" else 9.0) * U32
     eps *= d
     eps -= 1.0
     del d
     es = (e * eps).sum(axis=1, keepdims=True)
     eps_s = (es + gamma(C) * (s + es)) / s
-    if np.any(eps_s >= 1.0):
-        raise ValueError("logit deviation too large for a meaningful bound")
+    # rows whose logits may move so far that the sum is not bounded away
+    # from zero: only |p' - p| <= 1 (+ rounding) is left there
+    lost = eps_s >= 1.0
+    eps_s = np.where(lost, 0.0, eps_s)
     p = e
     p /= s                                      # e is not needed past here
-    dp = eps
-    dp += 1.0
-    dp *= (1.0 + U32) / (1.0 - eps_s)
-    dp -= 1.0
-    dp *= p                                     # p ((1 + eps)(1 + u) / (1 - eps_s) - 1)
-    others = dp.sum(axis=1, keepdims=True) - dp
-    others += gamma(C + 2)
-    np.minimum(dp, others, out=dp)
-    del others
+    if form == "softmax":
+        dp = eps
+        dp += 1.0
+        dp *= (1.0 + U32) / (1.0 - eps_s)
+        dp -= 1.0
+        dp *= p                                 # p ((1 + eps)(1 + u) / (1 - eps_s) - 1)
+        others = dp.sum(axis=1, keepdims=True) - dp
+        others += gamma(C + 2)
+        np.minimum(dp, others, out=dp)
+        del others
+    else:
+        del eps
+        logs = np.log(s)
+        lse = m + logs
+        lam = tmax - np.log1p(-eps_s) + 2.0 * U32 * np.abs(logs) + U32 * np.abs(lse)
+        dp = z - lse
+        np.abs(dp, out=dp)
+        dp += np.abs(lse) + np.log(batch_total)
+        dp *= 2.0 * U32
+        dp += 1.0 + 4.0 * U32                   # 1 + 2u (|z - lse| + |lse| + ln B) + 4u
+        dp *= np.exp(tau + lam)
+        dp -= 1.0
+        dp *= p
+    cap = 1.0 + 4.0 * U32  # two probabilities in [0, 1], each rounded
+    np.minimum(dp, cap, out=dp)
+    dp[lost[:, 0]] = cap
     if labels is None:
         dist = np.ones_like(p)
     else:

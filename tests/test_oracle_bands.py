@@ -254,3 +254,72 @@ def test_sum_band_by_blocks_equals_whole():
     blocks = sum(O.sum_band(G[i:i + 100], h[i:i + 100], dG[i:i + 100], n=300)
                  for i in range(0, 300, 100))
     assert np.allclose(blocks, whole, rtol=1e-12, atol=0)
+
+
+def test_xent_grad_band_saturates_for_huge_logit_deviation():
+    """A logit deviation that leaves the softmax unconstrained bounds each
+    probability's move by 1 (plus rounding), never more, never an error."""
+    z = np.array([[0.0, 1.0, 2.0]])
+    band = O.xent_grad_band(z, np.full_like(z, 5.0), 4, labels=np.array([1]))
+    assert np.all(band <= (1.0 + 4 * U) * (1 + O.gamma(4)) / 4 * 1.0001 + O.gamma(4) / 4)
+    assert np.all(band >= 1.0 / 4)
+
+
+def _f32_lse_grad(zp, y, B, tile, rng):
+    """Float32 softmax-xent gradient of one row formed as the fused head does:
+    per column tile its max and sum of exp, the tiles combined in order,
+    lse = m + log s, then exp(z - lse) / B from the logits as one base-2
+    exponential, minus 1 / B at the label."""
+    zp = np.asarray(zp, np.float32)
+    C = len(zp)
+    parts = []
+    for t0 in range(0, C, tile):
+        zt = zp[t0:t0 + tile]
+        mt = np.float32(zt.max())
+        st = np.float32(0.0)
+        for k in rng.permutation(len(zt)):
+            st = np.float32(st + np.exp(np.float32(zt[k] - mt)))
+        parts.append((mt, st))
+    m = np.float32(max(mt for mt, _ in parts))
+    s = np.float32(0.0)
+    for mt, st in parts:
+        s = np.float32(s + np.float32(st * np.exp(np.float32(mt - m))))
+    lse = np.float32(m + np.log(s))
+    l2e = np.float32(1.4426950408889634)
+    c = np.float32(lse * l2e + np.float32(np.log2(B)))
+    g = np.exp2((zp * l2e - c).astype(np.float32)).astype(np.float32)  # exp(z - lse) / B
+    g[y] = np.float32(g[y] - np.float32(1.0 / B))
+    return g.astype(np.float64)
+
+
+def test_xent_grad_band_lse_form_holds():
+    rng = np.random.default_rng(23)
+    B, C = 6, 300
+    z = rng.standard_normal((B, C)) * 3.0
+    y = rng.integers(0, C, B)
+    tau = np.abs(rng.standard_normal((B, C))) * 1e-4
+    band = O.xent_grad_band(z, tau, B, labels=y, form="lse")
+    _, g, _ = O.softmax_xent_fwd_bwd(z, y)
+    for trial in range(3):
+        zp = z + tau * rng.choice([-1.0, 1.0], size=z.shape)
+        for i in range(B):
+            for tile in (32, 128):
+                gp = _f32_lse_grad(zp[i], y[i], B, tile, rng)
+                assert np.all(np.abs(gp - g[i]) <= band[i])
+
+
+def test_xent_grad_band_lse_form_is_tight():
+    """Lower every logit but the largest by tau and raise that one: a minor
+    class's probability moves by about p (1 + p_max) tau... within 3x of the
+    bound."""
+    t = 1e-3
+    z = np.array([[4.0, 0.0, 0.0, 0.0, 0.0]])
+    tau = np.full_like(z, t)
+    band = O.xent_grad_band(z, tau, 1, labels=np.array([0]), form="lse")
+    zp = z + np.array([[t, -t, -t, -t, -t]])
+    e = np.exp(zp - zp.max())
+    p1 = e / e.sum()
+    e0 = np.exp(z - z.max())
+    p0 = e0 / e0.sum()
+    dev = abs(p1[0, 1] - p0[0, 1])
+    assert dev <= band[0, 1] < 3.0 * dev

@@ -284,14 +284,31 @@ def test_sum_band_gamma_of_fewer_terms_caught(monkeypatch):
 def test_xent_band_without_logit_deviation_caught(monkeypatch):
     real = RB.xent_grad_band
     monkeypatch.setattr(O, "xent_grad_band",
-                        lambda z, tau, B, scale=1.0, labels=None:
-                        real(z, 0.0 * np.asarray(tau), B, scale, labels))
+                        lambda z, tau, B, scale=1.0, labels=None, form="softmax":
+                        real(z, 0.0 * np.asarray(tau), B, scale, labels, form))
     _expect_pin_failure(PB.test_xent_grad_band_holds)
 
 
 def test_xent_band_far_too_wide_caught(monkeypatch):
     real = RB.xent_grad_band
     monkeypatch.setattr(O, "xent_grad_band",
-                        lambda z, tau, B, scale=1.0, labels=None:
-                        10.0 * real(z, tau, B, scale, labels))
+                        lambda z, tau, B, scale=1.0, labels=None, form="softmax":
+                        10.0 * real(z, tau, B, scale, labels, form))
     _expect_pin_failure(PB.test_xent_grad_band_is_tight_for_a_dominant_class)
+
+
+def test_lse_band_without_lse_deviation_caught(monkeypatch):
+    """The lse form with the deviation of lse itself left out (tau only)."""
+    real = RB.xent_grad_band
+
+    def no_lambda(z, tau, B, scale=1.0, labels=None, form="softmax"):
+        if form != "lse":
+            return real(z, tau, B, scale, labels, form)
+        z = np.asarray(z, np.float64)
+        lse = O.softmax_lse(z)[:, None]
+        p = np.exp(z - lse)
+        dp = p * (np.exp(np.asarray(tau)) - 1.0)
+        return (abs(scale) / B) * (dp + RB.gamma(4) * (1.0 + dp))
+
+    monkeypatch.setattr(O, "xent_grad_band", no_lambda)
+    _expect_pin_failure(PB.test_xent_grad_band_lse_form_is_tight)
