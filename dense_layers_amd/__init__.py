@@ -122,6 +122,8 @@ _c = {
                             _vp, _sz]),
     "dense_xent_vjp_workspace_size": _sig("dense_xent_vjp_workspace_size", _sz,
                                           [_i64, _i64, _i64]),
+    "softmax_xent_fwd_bwd_noalloc": _sig("softmax_xent_fwd_bwd_noalloc", _i32,
+                                         [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "sgd_step": _sig("sgd_step", _i32, [_vp, _i64, _vp, _vp, _f64]),
     "adamw_step": _sig("adamw_step", _i32,
                        [_vp, _i64, _vp, _vp, _vp, _vp, _f64, _f64, _f64, _f64, _f64, _i64]),
@@ -162,7 +164,7 @@ EXPORTS = ["dl_last_error", "dense_last_error", "dl_set_validate", "dl_empty_lau
            "dl_build_target", "dense_act_fwd", "dense_act_vjp",
            "dense_act_vjp_scaled", "dense_cast_f16_scaled", "dense_cast_f16_scaled_workspace_size",
            "dense_act_vjp_workspace_size", "softmax_xent_fwd_bwd",
-           "softmax_xent_workspace_size", "dense_xent_fwd",
+           "softmax_xent_workspace_size", "softmax_xent_fwd_bwd_noalloc", "dense_xent_fwd",
            "dense_xent_fwd_workspace_size", "dense_xent_vjp", "dense_xent_vjp_workspace_size",
            "sgd_step",
            "adamw_step",
@@ -449,6 +451,29 @@ def dense_xent_vjp(logits: torch.Tensor, lse: torch.Tensor, labels: torch.Tensor
                                 _ptr(db) if need_dw else None, _ptr(ws),
                                 0 if ws is None else ws.numel()))
     return (dX if need_dx else None), (dW if need_dw else None), (db if need_dw else None)
+
+
+XENT_NOALLOC_MAX_ROWS = 1 << 20
+
+
+def softmax_xent_fwd_bwd_noalloc(logits: torch.Tensor, labels: torch.Tensor,
+                                 dlogits: torch.Tensor, loss: torch.Tensor,
+                                 row_loss: Optional[torch.Tensor] = None):
+    """softmax_xent_fwd_bwd into caller-provided outputs, with no workspace:
+    the library's own per-device scratch holds the per-row losses (at most
+    XENT_NOALLOC_MAX_ROWS rows unless row_loss is given).  Allocates
+    nothing; calls overlapping in time on one GPU race on the scratch."""
+    _dev(logits, "logits", torch.float32)
+    B, C = logits.shape
+    _dev(labels, "labels", torch.int32, (B,))
+    _dev(dlogits, "dlogits", torch.float32, (B, C))
+    _dev(loss, "loss", torch.float32, (1,))
+    if row_loss is not None:
+        _dev(row_loss, "row_loss", torch.float32, (B,))
+    _check(_c["softmax_xent_fwd_bwd_noalloc"](_stream(logits), B, C, _ptr(logits),
+                                              _ptr(labels), _ptr(loss), _ptr(row_loss),
+                                              _ptr(dlogits)))
+    return loss, dlogits
 
 
 # ---------------------------------------------------------------- optimizers

@@ -19,7 +19,8 @@ LIB = os.path.join(LIBDIR, "libdense_layers_amd.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
-           "head.hip", "tail.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip"]
+           "head.hip", "tail.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip",
+           "noalloc.hip"]
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

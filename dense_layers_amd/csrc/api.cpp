@@ -33,6 +33,16 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(DL_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace dl {
+// The last-error message of the calling thread, for entry points defined in
+// other files.
+int api_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace dl
+
+namespace {
+
 // ---- optional per-launch timing ----------------------------------------------
 struct ProfRec {
   const char* name;

@@ -596,6 +596,9 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits,
                        float* loss, hipStream_t s, const float* dscale = nullptr);
 // One launch of an empty kernel (the launch floor).
 hipError_t launch_empty(hipStream_t s);
+// Sets the calling thread's last-error message (dense_last_error) and
+// returns `code` (defined with the C ABI in api.cpp).
+int api_fail(int code, const char* msg);
 // Number of labels outside [0, C) into bad[0] (one workgroup, no atomics).
 hipError_t launch_label_check(int64_t B, int64_t C, const int32_t* labels, int* bad,
                               hipStream_t s);

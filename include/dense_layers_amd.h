@@ -265,6 +265,26 @@ int softmax_xent_fwd_bwd(void* stream, int64_t B, int64_t C,
 
 size_t softmax_xent_workspace_size(int64_t B, int64_t C);
 
+/*
+ * softmax_xent_fwd_bwd_noalloc -- for callers that cannot allocate device
+ * memory (code under stream-graph capture, tight serving loops, harnesses
+ * that forbid allocation): softmax_xent_fwd_bwd with no workspace argument.
+ * Same kernels, same results bit for bit.  When row_loss is NULL the
+ * per-row losses go to a fixed scratch array the library holds on each GPU
+ * it runs on (DL_XENT_NOALLOC_MAX_ROWS floats, 4 MiB, kept until the process
+ * ends); B above that limit is DL_WORKSPACE_TOO_SMALL unless row_loss is
+ * given.  The call allocates nothing, host or device.  Calls on one GPU
+ * share its scratch, so calls that overlap in time on one GPU (other
+ * streams or threads) race; calls ordered on one stream do not.  Validate
+ * mode does not apply here (its label check reads a count back to the host):
+ * an out-of-range label gives a NaN row loss, as outside validate mode.
+ * Arguments and errors otherwise as softmax_xent_fwd_bwd; the stream must
+ * belong to the current device.
+ */
+#define DL_XENT_NOALLOC_MAX_ROWS (1 << 20)
+int softmax_xent_fwd_bwd_noalloc(void* stream, int64_t B, int64_t C,
+                                 const float* logits, const int32_t* labels,
+                                 float* loss, float* row_loss, float* dlogits);
 
 /* ---- fused classifier head over many classes ----------------------------- */
 

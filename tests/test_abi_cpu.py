@@ -158,3 +158,16 @@ def test_mlp_fusion_level_setting(dl):
         with pytest.raises(dl.DenseError):
             dl.set_mlp_fusion(bad)
     assert dl.set_mlp_fusion(2) == 2  # unchanged by the rejected levels
+
+
+def test_xent_noalloc_rejects_before_any_device_work(dl):
+    """The no-allocation cross-entropy checks sizes, pointers, aliasing and
+    its scratch limit on the host first (fake pointers are never touched)."""
+    c = dl._c["softmax_xent_fwd_bwd_noalloc"]
+    fake = 1 << 40
+    big = dl.XENT_NOALLOC_MAX_ROWS + 1
+    assert c(None, big, 10, fake, fake + (1 << 30), fake + (2 << 30), None, fake + (3 << 30)) == 4
+    assert b"scratch" in dl._c["dense_last_error"]()
+    assert c(None, 0, 10, fake, fake, fake, None, fake) == 1
+    assert c(None, 4, 10, fake, None, fake, None, fake) == 1
+    assert c(None, 4, 10, fake, fake, fake, None, fake) == 3
