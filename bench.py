@@ -36,18 +36,20 @@ PEAK_BF16_MFMA = 2516.6  # TFLOP/s, MI355X dense bf16 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
-KERNEL_SOURCES = ["common.hpp", "head_rows.hpp", "gemm_f32.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "xent.hip",
-                  "head.hip", "tail.hip", "optim.hip", "elementwise.hip", "gradctl.hip", "mse.hip", "api.cpp"]
+KERNEL_SOURCES = ["common.hpp", "head_rows.hpp", "gemm_f32.hip", "gemm_bf16.hip",
+                  "gemm_bf16_dma.hip", "xent.hip", "head.hip", "tail.hip", "optim.hip",
+                  "elementwise.hip", "gradctl.hip", "mse.hip", "noalloc.hip", "api.cpp"]
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources without their // comments and blank
-    lines: a stored counter measurement is only used while the code it was
-    taken from is unchanged."""
+def kernel_source_hash(names=None) -> str:
+    """sha256 over kernel sources (all of them, or the named files of
+    dense_layers_amd/csrc) without their // comments and blank lines: a
+    stored counter measurement is only used while the code it was taken
+    from is unchanged."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in (KERNEL_SOURCES if names is None else names):
         with open(os.path.join(ROOT, "dense_layers_amd", "csrc", name), encoding="utf-8") as f:
             for line in f:
                 code = re.sub(r"//.*", "", line).rstrip()
@@ -59,13 +61,16 @@ def kernel_source_hash() -> str:
 def stored_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or
-    None when there is none or the kernels changed since it was taken."""
+    None when there is none or the sources of that kernel changed since it
+    was taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash() or rec.get("stage") != stage:
+    if rec.get("stage") != stage:
+        return None
+    if rec.get("source_hash") != kernel_source_hash(rec.get("sources")):
         return None
     return rec.get("traffic_bytes")
 
@@ -679,10 +684,34 @@ def profile_stages(dl, bench, n_steps):
         wk = bench.stage_work(lab)
         if wk is not None and wk[0] == "flop":
             st["tflops"] = round(wk[1] / (ms * 1e-3) / 1e12, 3)
+            nb = bench.stage_bytes(lab)
+            if nb is not None:
+                st["bytes"] = int(nb)
         elif wk is not None:
             st["gbs"] = round(wk[1] / (ms * 1e-3) / 1e9, 1)
+            st["bytes"] = int(wk[1])
         stages.append(st)
     return stages
+
+
+def measure_launch_floor(dl, dev, stream, launches):
+    """Time of one empty-kernel launch back to back on the stream (HIP events
+    and wall clock over 2000 launches) and that times the step's launches."""
+    import torch
+    dl.empty_launches(200, dev)
+    torch.cuda.synchronize()
+    fe0, fe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_empty = 2000
+    t0 = time.perf_counter()
+    fe0.record(stream)
+    dl.empty_launches(n_empty, dev)
+    fe1.record(stream)
+    torch.cuda.synchronize()
+    wall_us = 1e6 * (time.perf_counter() - t0) / n_empty
+    gpu_us = 1e3 * fe0.elapsed_time(fe1) / n_empty
+    return {"empty_kernel_us": round(gpu_us, 3), "empty_kernel_wall_us": round(wall_us, 3),
+            "launches_per_step": launches,
+            "floor_us_per_step": round(launches * max(gpu_us, wall_us), 2)}
 
 
 def main():
@@ -702,6 +731,8 @@ def main():
     ap.add_argument("--head-path", default="fused", choices=("fused", "composed"),
                     help="classifier head: the fused head (default) or the composed "
                          "forward / cross-entropy / vjp")
+    ap.add_argument("--no-launch-floor", action="store_true",
+                    help="skip the empty-kernel launch-floor measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
@@ -775,21 +806,9 @@ def main():
             roofline["traffic_ratio"] = round(traffic / alg, 3)
 
     # launch floor: empty kernels back to back on the same stream
-    dl.empty_launches(200, dev)
-    torch.cuda.synchronize()
-    fe0, fe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_empty = 2000
-    t0 = time.perf_counter()
-    fe0.record(stream)
-    dl.empty_launches(n_empty, dev)
-    fe1.record(stream)
-    torch.cuda.synchronize()
-    empty_wall_us = 1e6 * (time.perf_counter() - t0) / n_empty
-    empty_gpu_us = 1e3 * fe0.elapsed_time(fe1) / n_empty
-    launch_floor = {"empty_kernel_us": round(empty_gpu_us, 3),
-                    "empty_kernel_wall_us": round(empty_wall_us, 3),
-                    "launches_per_step": len(stages),
-                    "floor_us_per_step": round(len(stages) * max(empty_gpu_us, empty_wall_us), 2)}
+    launch_floor = None
+    if not args.no_launch_floor:
+        launch_floor = measure_launch_floor(dl, dev, stream, len(stages))
 
     cpu = None
     if not args.no_cpu_baseline:
