@@ -674,7 +674,7 @@ def dense_cast_bf16(src: torch.Tensor, dst: Optional[torch.Tensor] = None):
 def dense_cast_f16_t(src: torch.Tensor, dst: Optional[torch.Tensor] = None,
                      dst_t: Optional[torch.Tensor] = None, copy: bool = True,
                      transposed: bool = True):
-    """Half copy (saturating at +-65504) of a [rows, cols] matrix and/or its
+    """Half copy (clamped to +-65504) of a [rows, cols] matrix and/or its
     transpose; returns (dst, dst_t)."""
     return _cast_t("dense_cast_f16_t", torch.float16, src, dst, dst_t, copy, transposed)
 

@@ -44,8 +44,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // ---- half (fp16) <-> f32 ------------------------------------------------------
 // The mixed-precision input convention of the MuNet page ("Configuration"):
-// round to nearest even, saturating at +-65504 instead of overflowing to
-// infinity, NaN preserved.  Clamping first gives the saturation (values past
+// nearest-even rounding, clamped to +-65504 instead of overflowing to
+// infinity, NaN kept.  Clamping first gives the saturation (values past
 // 65504 would otherwise round to 65504 or to infinity); NaN skips the clamp.
 __device__ __forceinline__ float f16_sat(float f) {
   return __builtin_isnan(f) ? f : fminf(fmaxf(f, -65504.f), 65504.f);

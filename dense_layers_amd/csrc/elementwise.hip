@@ -4,7 +4,7 @@
 //   * G = dY * act'(saved) for a vjp whose upstream gradient was not already
 //     masked by the previous dX epilogue;
 //   * float32 -> bf16 round-to-nearest-even working copies, or half copies
-//     (nearest-even, saturating at +-65504; the MuNet page, "Configuration").
+//     (nearest-even, clamped to +-65504; the MuNet page, "Configuration").
 #include "common.hpp"
 
 namespace dl {

@@ -1,7 +1,8 @@
 // Gradient control of an optimizer step: the global 2-norm for clipping
 // (MuNet page, "What runs today": gradient clipping) and the finite check of
-// dynamic loss scaling (Orthon page, "Core capabilities": a GradScaler with
-// finite checks, skipped steps, backoff and growth).
+// dynamic loss scaling (Orthon page, "Core capabilities": the loss scaler
+// tests the gradients for Inf / NaN, drops such a step, and lowers the scale
+// after one and raises it after a run of good steps).
 //
 // One reading pass over every gradient (finishing split-K slice sums into
 // their gradient arrays on the way) leaves per-workgroup float64 sums of

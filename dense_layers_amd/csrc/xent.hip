@@ -1,8 +1,8 @@
-// Fused softmax cross-entropy, forward and backward, in one read of the
-// logits (Orthon page, "Selected Orthon vs. PyTorch results": one fused kernel
-// reads the logits once instead of materialising a log-softmax and gathering;
-// the same page notes the benefit depends on the class count, so the row is
-// mapped to a different number of threads per class-count regime here).
+// Softmax cross-entropy forward and backward in a single pass over the
+// logits, with no log-probability tensor in between (Orthon page, "Selected
+// Orthon vs. PyTorch results"; that page ties the gain to the number of
+// classes, so here the lanes that own a row are chosen per class-count
+// range).
 //
 // A row of C logits is owned by TPR consecutive threads (a lane group inside a
 // wave for TPR <= 64, the whole workgroup of 1024 threads for wide rows).  Each

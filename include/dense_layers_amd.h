@@ -53,7 +53,7 @@ extern "C" {
 enum dl_dtype {
   DL_F32 = 0,   /* float32 operands, float32 accumulation */
   DL_BF16 = 1,  /* bfloat16 operands (RNE copies), float32 accumulation */
-  DL_F16 = 2    /* IEEE half operands (RNE, saturating at +-65504, NaN kept;
+  DL_F16 = 2    /* IEEE half operands (nearest-even, clamped to +-65504, NaN kept;
                  * the mixed precision of the MuNet page, "Configuration"),
                  * float32 accumulation */
 };
@@ -217,9 +217,9 @@ int dense_act_vjp(void* stream, int dtype, int act, int64_t B, int64_t in,
 /*
  * dense_act_vjp_scaled -- dense_act_vjp for a gradient operand handed over
  * times a scale s (the mixed_safe precision of the MuNet page,
- * "Configuration": per-tensor power-of-two rescaling of the gradient
- * operand of half matmuls, so cotangents far below the half normal range
- * keep their relative accuracy).  dY holds the cotangent times s
+ * "Configuration": each half gradient operand is multiplied by a power of
+ * two before its matmul, so that very small cotangents stay representable in
+ * half with their relative accuracy).  dY holds the cotangent times s
  * (dense_cast_f16_scaled writes both).  dW and db are divided by s in
  * float32 inside the GEMM epilogues, so they come out unscaled (exact when s
  * is a power of two).  dX keeps the scale: it is the previous layer's
@@ -242,8 +242,8 @@ size_t dense_act_vjp_workspace_size(int dtype, int act, int64_t B, int64_t in,
 
 /*
  * softmax_xent_fwd_bwd -- one pass over the logits gives the mean loss and
- * dlogits (Orthon page, "Selected Orthon vs. PyTorch results": one fused
- * kernel reads the logits once).  Per row: lse = max + log(sum exp(z - max)),
+ * dlogits (Orthon page, "Selected Orthon vs. PyTorch results": the
+ * cross-entropy fused into a single pass over the logits).  Per row: lse = max + log(sum exp(z - max)),
  * loss_i = lse - z[label_i], dlogits = (softmax - onehot(label)) / B;
  * loss = (1/B) sum_i loss_i, reduced in a fixed order.
  *
@@ -361,8 +361,9 @@ typedef struct dl_lr_schedule {
 double dl_lr_at(const dl_lr_schedule_t* s, double lr, int64_t step);
 
 /*
- * Dynamic loss scaling (Orthon page, "Core capabilities": a GradScaler with
- * finite checks, skipped steps, backoff and growth).  The loss gradient is
+ * Dynamic loss scaling (Orthon page, "Core capabilities": a loss scaler that
+ * checks the gradients for Inf / NaN, drops such steps, and moves the scale
+ * down after one and up after a run of good steps).  The loss gradient is
  * multiplied by S = *scale, so every gradient the backward forms is S times
  * the true one.  The optimizer looks at all of a step's gradients: if one of
  * them holds a NaN or an Inf, the step is skipped (no parameter, moment,
@@ -530,10 +531,10 @@ size_t mse_loss_workspace_size(int64_t B, int64_t C);
 /* ---- bf16 working copies -------------------------------------------------- */
 
 /*
- * dense_cast_bf16 -- dst = bf16(src) with round-to-nearest-even, NaN kept
- * (the low-precision convention of the MuNet page, "Configuration":
- * round to nearest, NaN preserved; and the FP32-master-weight scheme of the
- * Orthon page, "Mixed-precision training on CUDA").
+ * dense_cast_bf16 -- dst = bf16(src), rounded to the nearest value with ties
+ * to even and NaN kept (the low-precision convention of the MuNet page,
+ * "Configuration"; and the FP32-master-weight scheme of the Orthon page,
+ * "Mixed-precision training on CUDA").
  *   n > 0; src device float32 [n]; dst device bf16 [n]; no overlap.
  */
 int dense_cast_bf16(void* stream, int64_t n, const float* src, void* dst);
@@ -551,8 +552,8 @@ int dense_cast_bf16_t(void* stream, int64_t rows, int64_t cols, const float* src
 
 /*
  * dense_cast_f16, dense_cast_f16_t -- the same two copies in IEEE half:
- * round to nearest even, saturating at +-65504 (a value past the largest
- * half, or an infinity, becomes +-65504), NaN kept (the mixed-precision
+ * nearest-even rounding, clamped to +-65504 (a value past the largest half,
+ * or an infinity, becomes +-65504), NaN kept (the mixed-precision
  * convention of the MuNet page, "Configuration").  Arguments and errors as
  * dense_cast_bf16 / dense_cast_bf16_t, with half outputs.
  */

@@ -59,10 +59,10 @@ def round_f32(a) -> np.ndarray:
 
 
 def round_bf16(a) -> np.ndarray:
-    """Round to bfloat16 with round-to-nearest-even, NaN preserved.
+    """Round to bfloat16, nearest value with ties to even, NaN kept.
 
     The low-precision convention of the MuNet page ("Configuration", the
-    precision setting: round to nearest, NaN preserved).  bf16 is the top 16
+    precision setting).  bf16 is the top 16
     bits of an IEEE float32; the value is first rounded to float32, then the
     low half is rounded away with ties going to the even upper half.
     Returned as float64 holding bf16-representable values.
@@ -83,12 +83,11 @@ F16_MAX = 65504.0
 
 
 def round_f16_sat(a) -> np.ndarray:
-    """Round to IEEE half precision with round-to-nearest-even, saturating
-    at +-65504, NaN preserved.
+    """Round to IEEE half precision, nearest value with ties to even,
+    clamped to +-65504, NaN kept.
 
-    The fp16 input convention of the MuNet page ("Configuration", the mixed
-    precision setting: round to nearest, saturating at +-65504, NaN
-    preserved).  The value is first rounded to float32 (as the float32
+    The half input convention of the MuNet page ("Configuration", the mixed
+    precision setting).  The value is first rounded to float32 (as the float32
     accumulator holds it), then to half by NumPy's round-half-to-even cast;
     a result that overflowed to +-inf (a finite value at or past the
     rounding threshold, or an infinite input) becomes +-65504.  Returned as
@@ -102,10 +101,9 @@ def round_f16_sat(a) -> np.ndarray:
 
 def f16_safe_scale(a) -> float:
     """Power-of-two scale of a gradient operand before half conversion (the
-    MuNet page, "Configuration", precision mixed_safe: per-tensor
-    power-of-two rescaling of the gradient operands of half matmuls, exact,
-    so cotangents far below the half normal range keep their relative
-    accuracy).  With m the largest finite |a|: s = 2^(14 - floor(log2 m)),
+    MuNet page, "Configuration", precision mixed_safe: each half gradient
+    operand is scaled by a power of two, which is exact, so that very small
+    cotangents survive the conversion with their relative accuracy).  With m the largest finite |a|: s = 2^(14 - floor(log2 m)),
     which puts m * s in [2^14, 2^15) (one binade below the half maximum);
     s = 1 when m is 0 or there is no finite value."""
     a = np.asarray(a, dtype=np.float64)
@@ -381,8 +379,9 @@ def mse_loss_fwd_bwd(pred, target) -> Tuple[float, np.ndarray]:
 
 
 class LossScaler:
-    """Dynamic loss scale (Orthon page, "Core capabilities": GradScaler with
-    finite checks, skipped steps, backoff and growth).  ``update`` takes
+    """Dynamic loss scale (Orthon page, "Core capabilities": the scaler drops
+    a step whose gradients hold Inf / NaN and lowers the scale, and raises it
+    after a run of good steps).  ``update`` takes
     whether this step's scaled gradients held a NaN or Inf."""
 
     def __init__(self, scale: float = 65536.0, growth_factor: float = 2.0,
