@@ -1226,10 +1226,19 @@ static Plan mlp_dw_plan(int64_t B, int32_t L, const dl_layer_t* layers, int l, b
   return p;
 }
 
+// Whether the tail fits its narrow-batch form (16-row tiles; shapes only).
+static bool mlp_tail_narrow(int64_t B, int32_t L, const dl_layer_t* layers, bool xent) {
+  return mlp_tail_shape(L, layers, xent) &&
+         dl::mlp_tail_narrow_fits(B, layers[L - 2].in, layers[L - 2].out, layers[L - 1].out);
+}
+
 // Gradient slices a layer's dW / db leave for the optimizer to add up: the
-// split-K slices of its weight-gradient GEMM, or the fused head's slices.
-static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
-  if (l == L - 1 && mlp_fused_head(L, layers, xent)) return dl::head_xent_slices(B);
+// split-K slices of its weight-gradient GEMM, or the fused head's slices (one
+// per 16 rows with the narrow-batch tail, else one per 32-row tile group).
+static int64_t mlp_slices(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent,
+                          bool narrow = false) {
+  if (l == L - 1 && mlp_fused_head(L, layers, xent))
+    return narrow ? dl::mlp_tail_narrow_slices(B) : dl::head_xent_slices(B);
   return mlp_dw_plan(B, L, layers, l, xent).splits;
 }
 
@@ -1287,7 +1296,9 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, bool xe
   off += std::max(align_up((size_t)B * 4), xent ? 0 : align_up((size_t)dl::mse_grid(B * layers[L - 1].out) * 8));
   for (int l = 0; l < L; ++l) {
     part_off[l] = off;
-    const int64_t S = mlp_slices(B, L, layers, l, xent);
+    // room for the slices of either tail form (the form is chosen per call)
+    const int64_t S = std::max(mlp_slices(B, L, layers, l, xent),
+                               mlp_slices(B, L, layers, l, xent, mlp_tail_narrow(B, L, layers, xent)));
     if (S > 1)
       off += align_up((size_t)S * layers[l].out * layers[l].in * 4) +
              align_up((size_t)S * layers[l].out * 4);
@@ -1419,6 +1430,11 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool tail = g_mlp_fusion >= 2 && mlp_tail_shape(L, layers, xent) &&
                     al16(layers[L - 2].W) && (L >= 3 || al16(X));
+  // a small batch takes the tail's narrow form, which also finishes the
+  // split-K forward of the layer before it
+  const bool narrow = tail && mlp_tail_narrow(B, L, layers, xent);
+  const float* fold_part = nullptr;
+  int fold_splits = 0;
   const int last_gemm = tail ? L - 3 : fused ? L - 2 : L - 1;
   float* gbuf[2] = {reinterpret_cast<float*>(base + g_off),
                     reinterpret_cast<float*>(base + g_off + g_bytes)};
@@ -1438,7 +1454,10 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       d.splits = fp.splits; d.k_per_split = fp.k_per_split;
       d.partial = slices;
       e = timed("fwd_gemm", s, [&] { return dl::launch_gemm_f32(d, fp.tile, s); });
-      if (e == hipSuccess)
+      if (narrow && l == last_gemm) {  // the tail finishes it
+        fold_part = slices;
+        fold_splits = fp.splits;
+      } else if (e == hipSuccess)
         e = timed("fwd_finish", s, [&] {
           return dl::launch_splitk_finish_fwd((int)B, (int)ly.out, fp.splits, slices, ly.b, ly.act,
                                               Y[l], s);
@@ -1451,7 +1470,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   if (tail) {
     const dl_layer_t& hl = layers[L - 2];
     const dl_layer_t& ly = layers[L - 1];
-    const int64_t S = dl::head_xent_slices(B);
+    const int64_t S = mlp_slices(B, L, layers, L - 1, xent, narrow);
     char* pb = base + part_off[L - 1];
     float* dWp = S > 1 ? reinterpret_cast<float*>(pb) : ly.dW;
     float* dbp = S > 1 ? reinterpret_cast<float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))
@@ -1459,11 +1478,22 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     const float* Hin = L >= 3 ? Y[L - 3] : X;
     float* dH = L >= 3 ? gbuf[0] : nullptr;
     const int act0 = L >= 3 ? layers[L - 3].act : DL_ACT_IDENTITY;
-    e = timed("mlp_tail", s, [&] {
-      return dl::launch_mlp_tail(B, (int)hl.in, (int)hl.out, (int)ly.out, Hin, hl.W, hl.b, hl.act,
-                                 act0, ly.W, ly.b, labels, row_loss, Y[L - 2], dH, dWp, dbp, s,
-                                 dscale);
-    });
+    if (narrow) {
+      // with a fold the kernel writes Y[L-3]; without one it only reads Hin
+      e = timed("mlp_tail", s, [&] {
+        return dl::launch_mlp_tail_narrow(B, (int)hl.in, (int)hl.out, (int)ly.out,
+                                          const_cast<float*>(Hin), fold_part, fold_splits,
+                                          fold_splits > 0 ? layers[L - 3].b : nullptr, hl.W, hl.b,
+                                          hl.act, act0, ly.W, ly.b, labels, row_loss, Y[L - 2], dH,
+                                          dWp, dbp, s, dscale);
+      });
+    } else {
+      e = timed("mlp_tail", s, [&] {
+        return dl::launch_mlp_tail(B, (int)hl.in, (int)hl.out, (int)ly.out, Hin, hl.W, hl.b,
+                                   hl.act, act0, ly.W, ly.b, labels, row_loss, Y[L - 2], dH, dWp,
+                                   dbp, s, dscale);
+      });
+    }
     if (e != hipSuccess) return hip_fail(e, "mlp_train_step (tail)");
   } else if (fused) {
     const dl_layer_t& ly = layers[L - 1];
@@ -1499,6 +1529,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   // backward; G holds the current layer's output gradient
   const float* G = last_gemm >= 0 ? Y[last_gemm] : nullptr;
   int first_bwd = last_gemm;
+  bool sgd_in_dw = false;  // the SGD step ran inside the weight-gradient launch
   if (tail) {
     // the weight gradient of the tail's hidden layer (its output gradient in
     // Y[L-2]), in one launch with the first layer's when that layer comes
@@ -1509,11 +1540,44 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
     const Plan ph = mlp_dw_plan(B, L, layers, lh, xent);
     const Plan p0 = mlp_dw_plan(B, L, layers, 0, xent);
     if (lh == 1 && ph.tile == 1 && p0.tile == 1) {
-      const dl::GemmDesc d0 = dw_desc(DL_F32, B, layers[0].in, layers[0].out, gbuf[0], X,
-                                      layers[0].dW, layers[0].db, base + part_off[0], p0);
-      const dl::GemmDesc dh = dw_desc(DL_F32, B, hl.in, hl.out, Y[lh], Hin, hl.dW, hl.db,
-                                      base + part_off[lh], ph);
-      e = timed("dwdw_gemm", s, [&] { return dl::launch_gemm_f32_dw_dw(d0, dh, s); });
+      dl::GemmDesc d0 = dw_desc(DL_F32, B, layers[0].in, layers[0].out, gbuf[0], X, layers[0].dW,
+                                layers[0].db, base + part_off[0], p0);
+      dl::GemmDesc dh = dw_desc(DL_F32, B, hl.in, hl.out, Y[lh], Hin, hl.dW, hl.db,
+                                base + part_off[lh], ph);
+      // Plain SGD of the three-layer network: the two weight gradients take
+      // their SGD steps in their epilogue and one more workgroup of the same
+      // launch adds up the head's slices, steps the head and forms the loss
+      // mean, so the step needs no optimizer launch (the same arithmetic as
+      // that launch, so the same results).
+      auto same16 = [](const void* a, const void* b) {
+        return ((reinterpret_cast<uintptr_t>(a) ^ reinterpret_cast<uintptr_t>(b)) & 15) == 0;
+      };
+      sgd_in_dw = L == 3 && opt->kind == DL_OPT_SGD && !ctl_on && !dev_step && !any_ema &&
+                  p0.splits == 1 && ph.splits == 1 && same16(layers[0].W, layers[0].dW) &&
+                  same16(hl.W, hl.dW);
+      dl::SgdFinish fin{};
+      if (sgd_in_dw) {
+        const float lr = opt_consts(*opt, opt->step).lr;
+        d0.sgd_w = layers[0].W; d0.sgd_b = layers[0].b; d0.sgd_lr = lr;
+        dh.sgd_w = hl.W; dh.sgd_b = hl.b; dh.sgd_lr = lr;
+        const dl_layer_t& ly = layers[L - 1];
+        const int64_t S = mlp_slices(B, L, layers, L - 1, xent, narrow);
+        char* pb = base + part_off[L - 1];
+        fin.W = ly.W; fin.b = ly.b; fin.dW = ly.dW; fin.db = ly.db;
+        fin.dW_part = S > 1 ? reinterpret_cast<const float*>(pb) : nullptr;
+        fin.db_part = S > 1 ? reinterpret_cast<const float*>(pb + align_up((size_t)S * ly.out * ly.in * 4))
+                            : nullptr;
+        fin.n_w = ly.out * ly.in;
+        fin.n_b = (int)ly.out;
+        fin.slices = (int)S;
+        fin.lr = lr;
+        fin.rows = B;
+        fin.row_loss = row_loss;
+        fin.loss = loss;
+      }
+      e = timed("dwdw_gemm", s, [&] {
+        return dl::launch_gemm_f32_dw_dw(d0, dh, s, sgd_in_dw ? &fin : nullptr);
+      });
       if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW + dW)");
       first_bwd = -1;
     } else {
@@ -1549,6 +1613,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       G = Y[l - 1];
     }
   }
+  if (sgd_in_dw) return DL_OK;
   // optimizer over every W and b in one launch (finishing split-K sums, or,
   // with the gradient control on, after the gradient pass has finished them)
   dl::OptSegs segs = blank_segs();
@@ -1556,7 +1621,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   int64_t blocks = 0, units = 0;
   for (int l = 0; l < L; ++l) {
     const dl_layer_t& ly = layers[l];
-    const int64_t S = mlp_slices(B, L, layers, l, xent);
+    const int64_t S = mlp_slices(B, L, layers, l, xent, narrow);
     char* pb = base + part_off[l];
     float* ws_[2] = {ly.W, ly.b};
     float* gs_[2] = {ly.dW, ly.db};

@@ -220,6 +220,14 @@ struct GemmDesc {
   // o_i = lse_i log2 e + log2 B, and the label y_i (its int32 bits).
   const float* xent_rows;
   float xent_invB;
+  // Weight gradient with one K slice: with sgd_w set, the epilogue also
+  // takes the SGD step on the parameters at the same places,
+  // sgd_w[m][n] -= sgd_lr dW[m][n] (sgd_w with leading dimension ldc), and
+  // with sgd_b set, sgd_b[m] -= sgd_lr db[m], as the optimizer kernel would
+  // from the stored dW and db.
+  float* sgd_w;
+  float* sgd_b;
+  float sgd_lr;
 };
 
 // 1 / s of a descriptor's gradient-operand scale (1 without one).
@@ -531,6 +539,18 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
           for (int e = 0; e < 4; ++e) v[e] *= osc;
           if (colfull) Store4<TO>::vec(out + o, v);
           else for (int e = 0; e < nv; ++e) Elem<TO>::store(out, o + e, v[e]);
+          if (EPI == EPI_DW && d.sgd_w != nullptr) {
+            float* wp = d.sgd_w + o;
+            if (colfull) {
+              float w[4];
+              Store4<float>::load_vec(wp, w);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w[e] -= d.sgd_lr * v[e];
+              Store4<float>::vec(wp, w);
+            } else {
+              for (int e = 0; e < nv; ++e) wp[e] -= d.sgd_lr * v[e];
+            }
+          }
         }
       }
     }
@@ -627,9 +647,27 @@ hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, c
                            const int32_t* labels, float* row_loss, float* G1, float* dH,
                            float* dW_part, float* db_part, hipStream_t s,
                            const float* dscale = nullptr);
+// The same tail for a small batch (K1 = 256, N1 = 128 or 256, B <= 4096):
+// 16-row tiles on the 16x16x4 MFMA, one per workgroup, dW / db as
+// mlp_tail_narrow_slices(B) slices.  With fold_splits > 0, Hin is first
+// formed as act0(sum of fold_splits K-slices fold_part[s][B][K1] + b0) and
+// written to Hin; else it is read from Hin.  hipErrorNotSupported when Hin,
+// W1, G1 or fold_part is not 16-byte aligned (nothing launched).
+bool mlp_tail_narrow_fits(int64_t B, int64_t K1, int64_t N1, int64_t C);
+int64_t mlp_tail_narrow_slices(int64_t B);
+hipError_t launch_mlp_tail_narrow(int64_t B, int K1, int N1, int C, float* Hin,
+                                  const float* fold_part, int fold_splits, const float* b0,
+                                  const float* W1, const float* b1, int act1, int act0,
+                                  const float* W2, const float* b2, const int32_t* labels,
+                                  float* row_loss, float* G1, float* dH, float* dW_part,
+                                  float* db_part, hipStream_t s, const float* dscale = nullptr);
 // Two float32 weight gradients (M/N-major operands, 64x64 tiles) in one
-// launch.
-hipError_t launch_gemm_f32_dw_dw(const GemmDesc& a, const GemmDesc& b, hipStream_t s);
+// launch; with fin, also the sgd_finish_wgs(*fin) workgroups of
+// sgd_finish_block (a descriptor with sgd_w set then needs one K slice, db
+// and sgd_b, and sgd_w at the alignment of C modulo 16 bytes).
+struct SgdFinish;
+hipError_t launch_gemm_f32_dw_dw(const GemmDesc& a, const GemmDesc& b, hipStream_t s,
+                                 const SgdFinish* fin = nullptr);
 // Optimizer kinds (the values of enum dl_opt_kind).
 enum OptKind { OPT_SGD = 0, OPT_ADAMW = 1, OPT_ADAM = 2 };
 
@@ -732,6 +770,90 @@ inline int64_t opt_elems_per_block(int splits) {
 }
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);
+// Mean of the per-row losses by one workgroup: thread t takes rows t, t+256,
+// ... in chunks of 8 (loaded together, added in order, float64), then a fixed
+// shuffle tree and the 4 waves in order.
+__device__ __forceinline__ void loss_mean_block(int64_t rows, const float* __restrict__ row_loss,
+                                                float* __restrict__ loss) {
+  __shared__ double red[kOptBlock / 64];
+  double acc = 0.0;
+  for (int64_t i0 = threadIdx.x; i0 < rows; i0 += 8 * kOptBlock) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + (int64_t)u * kOptBlock;
+      x[u] = i < rows ? row_loss[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)x[u];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kOptBlock / 64; ++w) t += red[w];
+    loss[0] = (float)(t / (double)rows);
+  }
+}
+
+// SGD of one layer whose dW / db are the split-K or row-tile slices of a
+// fused kernel (or, with one slice, already final), by
+// kOptBlock-thread workgroups that also form the loss mean: each element's
+// slices are added as the multi-array optimizer adds them (slice k into
+// partial sum k mod 4, in slice order, then (p0 + p1) + (p2 + p3)), the sum
+// stored as the gradient, and w -= lr g.
+struct SgdFinish {
+  float* W;
+  float* b;
+  float* dW;
+  float* db;
+  const float* dW_part;  // [slices][n_w], or null with one slice
+  const float* db_part;  // [slices][n_b]
+  int64_t n_w;
+  int n_b, slices;
+  float lr;
+  int64_t rows;  // the loss mean: rows of row_loss into loss
+  const float* row_loss;
+  float* loss;
+};
+// Finishing workgroup `part` of sgd_finish_wgs(f): elements [part kOptBlock,
+// +kOptBlock) of W then b, one per thread with all its slices requested
+// before the first is added; part 0 also forms the loss mean.
+__device__ __forceinline__ void sgd_finish_block(const SgdFinish& f, int part) {
+  if (part == 0) loss_mean_block(f.rows, f.row_loss, f.loss);
+  const int64_t i = (int64_t)part * kOptBlock + threadIdx.x;
+  if (i >= f.n_w + f.n_b) return;
+  const bool isw = i < f.n_w;
+  const int64_t j = isw ? i : i - f.n_w;
+  float* w = isw ? f.W : f.b;
+  float* g_out = isw ? f.dW : f.db;
+  float g;
+  if (f.slices > 1) {
+    const float* part_p = (isw ? f.dW_part : f.db_part) + j;
+    const int64_t stride = isw ? f.n_w : (int64_t)f.n_b;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    for (; k + 4 <= f.slices; k += 4) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = part_p[(int64_t)(k + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += x[u];
+    }
+    for (int u = 0; k + u < f.slices; ++u) a[u] += part_p[(int64_t)(k + u) * stride];
+    g = (a[0] + a[1]) + (a[2] + a[3]);
+    g_out[j] = g;
+  } else {
+    g = g_out[j];
+  }
+  w[j] -= f.lr * g;
+}
+inline int sgd_finish_wgs(const SgdFinish& f) {
+  return (int)((f.n_w + f.n_b + kOptBlock - 1) / kOptBlock);
+}
+
 hipError_t launch_adam(int64_t n, float* w, const float* g, float* m, float* v,
                        const OptConsts& c, hipStream_t s);
 hipError_t launch_ema(int64_t n, float* e, const float* w, float d, float omd, hipStream_t s);

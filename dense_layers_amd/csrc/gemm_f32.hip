@@ -428,8 +428,12 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
       float v = (dbacc[i] + __shfl_xor(dbacc[i], 32)) * unscale_factor(d);
       const int row = row_base + i * 32 + l32;
       if (h == 0 && row < M) {
-        if (d.splits > 1) d.db_partial[(int64_t)split * M + row] = v;
-        else d.db[row] = v;
+        if (d.splits > 1) {
+          d.db_partial[(int64_t)split * M + row] = v;
+        } else {
+          d.db[row] = v;
+          if (d.sgd_b != nullptr) d.sgd_b[row] -= d.sgd_lr * v;
+        }
       }
     }
   }
@@ -445,17 +449,20 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
 }
 
 // Two small products in one launch (64x64 tiles of 4 waves for both):
-// workgroups [0, a.nwg) take the weight-gradient items of job a, the rest the
-// items of job b (the same layer's dX, or another layer's weight gradient).
-// The two products only read common inputs, so they may run side by side;
-// neither may write over the other's inputs.
+// workgroups [0, a.nwg) take the weight-gradient items of job a, the next
+// b.nwg the items of job b (the same layer's dX, or another layer's weight
+// gradient).  The two products only read common inputs, so they may run side
+// by side; neither may write over the other's inputs.  With fin.W set, more
+// workgroups take the loss mean and the SGD step of a third layer from its
+// gradient slices (the weight gradients then take their own SGD steps in the
+// epilogue).
 struct F32Job {
   GemmDesc d;
   int tiles_m, tiles_n, a_vec, b_vec, out_vec, nwg;
 };
 template <int ALAY2, int BLAY2, int EPI2>
 __global__ void __launch_bounds__(256)
-gemm_f32_pair_kernel(F32Job a, F32Job b) {
+gemm_f32_pair_kernel(F32Job a, F32Job b, SgdFinish fin) {
   constexpr int kA = f32_smem_floats<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR>();
   constexpr int kB = f32_smem_floats<64, 64, 32, 2, 2, ALAY2, BLAY2>();
   __shared__ __attribute__((aligned(16))) float smem[kA > kB ? kA : kB];
@@ -463,9 +470,11 @@ gemm_f32_pair_kernel(F32Job a, F32Job b) {
   if (w < a.nwg)
     gemm_f32_body<64, 64, 32, 2, 2, MN_MAJOR, MN_MAJOR, EPI_DW>(
         a.d, a.tiles_m, a.tiles_n, a.a_vec, a.b_vec, a.out_vec, w, a.nwg, smem);
-  else
+  else if (w < a.nwg + b.nwg)
     gemm_f32_body<64, 64, 32, 2, 2, ALAY2, BLAY2, EPI2>(
         b.d, b.tiles_m, b.tiles_n, b.a_vec, b.b_vec, b.out_vec, w - a.nwg, b.nwg, smem);
+  else
+    sgd_finish_block(fin, w - a.nwg - b.nwg);
 }
 
 // Grid shape and vector-access flags of one GEMM on a BM x BN tile.
@@ -547,22 +556,35 @@ hipError_t launch_gemm_f32_dw_dx(const GemmDesc& dw, const GemmDesc& dx, hipStre
   hipError_t e = make_job<64, 64>(dw, a);
   if (e == hipSuccess) e = make_job<64, 64>(dx, b);
   if (e != hipSuccess) return e;
+  const SgdFinish none{};
   hipLaunchKernelGGL((gemm_f32_pair_kernel<K_MAJOR, MN_MAJOR, EPI_DX>),
-                     dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
+                     dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b, none);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_f32_dw_dw(const GemmDesc& dw_a, const GemmDesc& dw_b, hipStream_t s) {
+hipError_t launch_gemm_f32_dw_dw(const GemmDesc& dw_a, const GemmDesc& dw_b, hipStream_t s,
+                                 const SgdFinish* fin) {
   auto ok = [](const GemmDesc& d) {
     return d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR;
   };
   if (!ok(dw_a) || !ok(dw_b)) return hipErrorInvalidValue;
+  // the epilogue's SGD step needs the final gradient (one K slice) and the
+  // parameters at the same 16-byte alignment as dW
+  auto sgd_ok = [](const GemmDesc& d) {
+    if (d.sgd_w == nullptr) return d.sgd_b == nullptr;
+    return d.splits == 1 && d.db != nullptr && d.sgd_b != nullptr &&
+           ((reinterpret_cast<uintptr_t>(d.sgd_w) ^ reinterpret_cast<uintptr_t>(d.C)) & 15) == 0;
+  };
+  if (!sgd_ok(dw_a) || !sgd_ok(dw_b)) return hipErrorInvalidValue;
   F32Job a, b;
   hipError_t e = make_job<64, 64>(dw_a, a);
   if (e == hipSuccess) e = make_job<64, 64>(dw_b, b);
   if (e != hipSuccess) return e;
+  SgdFinish f{};
+  if (fin != nullptr) f = *fin;
+  const unsigned extra = f.W != nullptr ? (unsigned)sgd_finish_wgs(f) : 0u;
   hipLaunchKernelGGL((gemm_f32_pair_kernel<MN_MAJOR, MN_MAJOR, EPI_DW>),
-                     dim3((unsigned)(a.nwg + b.nwg)), dim3(256), 0, s, a, b);
+                     dim3((unsigned)(a.nwg + b.nwg) + extra), dim3(256), 0, s, a, b, f);
   return hipGetLastError();
 }
 

@@ -10,8 +10,9 @@
 //   dh = (W^T g) * act'(h),
 // and over a tile's rows, in order, the partial sums dW += g h^T, db += g.
 // A workgroup of kHeadThreads threads takes kHeadRows rows, kHeadTPR threads
-// per row; the row tile H sits in LDS with row stride S, W transposed in LDS
-// as Wt[k][16] (classes padded to 16 with zeros).
+// per row (the narrow-batch tail: 16 rows, 32 threads per row); the row tile
+// H sits in LDS with row stride S, W transposed in LDS as Wt[k][16] (classes
+// padded to 16 with zeros).
 #pragma once
 #include "common.hpp"
 
@@ -43,12 +44,22 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// Row r (thread lr of the row's kHeadTPR): the logits from H[r][0..K), the
+// Sum over the TPR (16 or 32) lanes of a row: with 32, the two rows of 16
+// add their sums (each lane the same two operands, so again bit-identical).
+template <int TPR>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(TPR == 16 || TPR == 32, "16 or 32 threads per row");
+  v = row16_sum(v);
+  if (TPR == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// Row r (thread lr of the row's TPR): the logits from H[r][0..K), the
 // row's loss (row_loss[row], written by lane 0 of an active row; NaN for a
 // label outside [0, C)), and g = (softmax - onehot) * invB in g[0..C)
 // (zeros past C and for an inactive row).  Lanes lr < 4 store g of classes
 // 4 lr .. 4 lr + 3 to Ds[r][16].
-template <int S>
+template <int S, int TPR = kHeadTPR>
 __device__ __forceinline__ void head_row_loss(const float* Hs, const float* Wt, const float* bias16,
                                               float* Ds, int r, int lr, int K, int C, int y,
                                               bool active, float invB, float* __restrict__ row_loss,
@@ -58,8 +69,8 @@ __device__ __forceinline__ void head_row_loss(const float* Hs, const float* Wt, 
 #pragma unroll
   for (int c = 0; c < kHeadCMax; ++c) z[c] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
-    const int k = lr + kk * kHeadTPR;
+  for (int kk = 0; kk < kHeadKMax / TPR; ++kk) {
+    const int k = lr + kk * TPR;
     if (k >= K) break;
     const float h = Hs[r * S + k];
 #pragma unroll
@@ -72,7 +83,7 @@ __device__ __forceinline__ void head_row_loss(const float* Hs, const float* Wt, 
   float m = -INFINITY;
 #pragma unroll
   for (int c = 0; c < kHeadCMax; ++c) {
-    z[c] = row16_sum(z[c]);
+    z[c] = row_sum<TPR>(z[c]);
     z[c] += bias16[c];
     if (c < C) m = fmaxf(m, z[c]);
   }
@@ -98,12 +109,12 @@ __device__ __forceinline__ void head_row_loss(const float* Hs, const float* Wt, 
 }
 
 // Row r: dh[k] = (sum_c g_c W[c][k]) * act'(H[r][k]) for k < K, into Gs[r][k].
-template <int S>
+template <int S, int TPR = kHeadTPR>
 __device__ __forceinline__ void head_row_dx(const float* Hs, const float* Wt, float* Gs, int r,
                                             int lr, int K, int act, const float (&g)[kHeadCMax]) {
 #pragma unroll
-  for (int kk = 0; kk < kHeadKMax / kHeadTPR; ++kk) {
-    const int k = lr + kk * kHeadTPR;
+  for (int kk = 0; kk < kHeadKMax / TPR; ++kk) {
+    const int k = lr + kk * TPR;
     if (k >= K) break;
     float d = 0.f;
 #pragma unroll
@@ -134,14 +145,14 @@ struct HeadSlice {
     }
     db = 0.f;
   }
-  template <int S>
+  template <int S, int ROWS = kHeadRows>
   __device__ __forceinline__ void add_tile(const float* Hs, const float* Ds, int tid, int C) {
 #pragma unroll
     for (int j = 0; j < kHeadPairs; ++j) {
       if (pc[j] < 0) continue;
       float a0 = acc[j][0], a1 = acc[j][1], a2 = acc[j][2], a3 = acc[j][3];
 #pragma unroll 8
-      for (int q = 0; q < kHeadRows; ++q) {
+      for (int q = 0; q < ROWS; ++q) {
         const float h = Hs[q * S + pk[j]];
         const f32x4 d = *reinterpret_cast<const f32x4*>(&Ds[q * kHeadCMax + pc[j]]);
         a0 += d[0] * h; a1 += d[1] * h; a2 += d[2] * h; a3 += d[3] * h;
@@ -149,7 +160,7 @@ struct HeadSlice {
       acc[j][0] = a0; acc[j][1] = a1; acc[j][2] = a2; acc[j][3] = a3;
     }
     if (tid < C)
-      for (int q = 0; q < kHeadRows; ++q) db += Ds[q * kHeadCMax + tid];
+      for (int q = 0; q < ROWS; ++q) db += Ds[q * kHeadCMax + tid];
   }
   // Slice `slice` of dW_part [S][C][K] and db_part [S][C].
   __device__ __forceinline__ void store(float* dW_part, float* db_part, int64_t slice, int tid,

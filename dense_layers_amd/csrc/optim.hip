@@ -246,34 +246,6 @@ __device__ __forceinline__ void opt_wide_split_block(int64_t n, int64_t base,
 // One launch over several arrays: block b belongs to the segment whose
 // prefix range [start_block[s], start_block[s+1]) contains it; a segment's
 // elements per block are opt_elems_per_block(splits).
-// Mean of the per-row losses by one workgroup: thread t takes rows t, t+256,
-// ... in chunks of 8 (loaded together, added in order, float64), then a fixed
-// shuffle tree and the 4 waves in order.
-__device__ __forceinline__ void loss_mean_block(int64_t rows, const float* __restrict__ row_loss,
-                                                float* __restrict__ loss) {
-  __shared__ double red[kOptBlock / 64];
-  double acc = 0.0;
-  for (int64_t i0 = threadIdx.x; i0 < rows; i0 += 8 * kOptBlock) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + (int64_t)u * kOptBlock;
-      x[u] = i < rows ? row_loss[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += (double)x[u];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int w = 0; w < kOptBlock / 64; ++w) t += red[w];
-    loss[0] = (float)(t / (double)rows);
-  }
-}
-
 // The learning rate (scheduled) and bias corrections of step t, in double,
 // rounded once (the host forms the same expressions from its own step count).
 template <int KIND>

@@ -324,6 +324,283 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
   sl.store(dW_part, db_part, blockIdx.x, tid, K, C);
 }
 
+// ---- the narrow-batch form ---------------------------------------------------
+// With a small batch the 32-row tiles leave all but a few CUs idle, and each
+// wave's product is one chain of dependent 32x32x2 MFMAs (128 of them for a
+// 256-long forward), so the step waits on chain latency.  The narrow form
+// gives each workgroup one tile of 16 rows (a 64-row batch spreads over 4
+// CUs) and runs both products on the 16x16x4 MFMA: H (16 x N1) is N1/16
+// blocks and dH (16 x K1) K1/16 blocks over 8 waves, each block a chain of a
+// quarter of the k steps of the 32-row form.  Inside a block, MFMA step s of
+// k group q takes k = 16 q + 4 g + s from lane group g (lanes 16 g .. 16 g +
+// 15), so a lane reads the A operand of 4 steps as one float4.  The sums run
+// in another order than the 32-row form and the standalone kernels (the same
+// products, rounded differently); the head rows use 32 threads each and the
+// same operations as the head kernel.
+//
+// Optionally the workgroup also finishes the split-K forward of the layer
+// before it: Hin = act0(sum of the K-slices in slice order + b0), as the
+// finishing kernel of that forward computes it, written out for the weight
+// gradient that reads it and kept in LDS.
+// Identity or ReLU, the hidden activations of the MLP step, as selects
+// rather than branches: the values of act_apply / act_deriv for those two
+// (a NaN maps to 0 under ReLU, as there).
+__device__ __forceinline__ float relu_or_id(bool relu, float z) {
+  return (relu && !(z > 0.0f)) ? 0.0f : z;
+}
+__device__ __forceinline__ float relu_or_id_deriv(bool relu, float z) {
+  return (relu && !(z > 0.0f)) ? 0.0f : 1.0f;
+}
+
+constexpr int kNarrowRows = 16;
+constexpr int kNarrowThreads = kHeadThreads;
+constexpr int kNarrowTPR = kNarrowThreads / kNarrowRows;  // threads per head row
+static_assert(kNarrowTPR == 32, "two 32-lane rows per wave in the head");
+
+template <bool HAS_DX, int K1, int N1>
+__global__ void __launch_bounds__(kNarrowThreads)
+mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* __restrict__ fold_part,
+                       int fold_splits, const float* __restrict__ b0, const float* __restrict__ W1,
+                       const float* __restrict__ b1, int act1, int act0,
+                       const float* __restrict__ W2, const float* __restrict__ b2,
+                       const int32_t* __restrict__ labels, float* __restrict__ row_loss,
+                       float* __restrict__ G1, float* __restrict__ dH, float* __restrict__ dW_part,
+                       float* __restrict__ db_part, float invB, const float* dscale) {
+  static_assert(K1 % 128 == 0 && N1 % 128 == 0 && K1 <= kHeadKMax && N1 <= kHeadKMax,
+                "16-column blocks spread evenly over 8 waves");
+  constexpr int NBF = N1 / 128;  // forward blocks per wave
+  constexpr int NBX = K1 / 128;  // dX blocks per wave
+  constexpr int TX = K1 + 4;     // LDS row strides (floats): 16-byte aligned rows
+  constexpr int TH = N1 + 4;
+  __shared__ __attribute__((aligned(16))) float Xs[kNarrowRows * TX];  // Hin
+  __shared__ __attribute__((aligned(16))) float Hs[kNarrowRows * TH];  // H
+  __shared__ __attribute__((aligned(16))) float Gs[kNarrowRows * TH];  // G1
+  __shared__ __attribute__((aligned(16))) float Wt[kHeadKMax * kHeadCMax];
+  __shared__ __attribute__((aligned(16))) float Ds[kNarrowRows * kHeadCMax];
+  __shared__ float Bc[kHeadCMax];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int r = tid / kNarrowTPR, lr = tid % kNarrowTPR;
+  const int64_t r0 = (int64_t)blockIdx.x * kNarrowRows;
+  const int nrows = (int)min<int64_t>(kNarrowRows, B - r0);
+
+  const bool relu0 = act0 == ACT_RELU, relu1 = act1 == ACT_RELU;
+  if (dscale != nullptr) invB *= *dscale;  // loss scale
+
+  // ---- every load of the prologue is requested before the first is used.
+  // Except the forward operand, they go through buffer resources whose
+  // range check turns a lane's out-of-range offset into a zero, so no load
+  // sits behind a branch (the compiler waits for the loads before a branch).
+  // The row tile of Hin first: each thread's float4 groups, or with a fold
+  // the K-slices of a group of kFoldGroup (slice s of the rows from r0 on
+  // starts s B K1 floats further; rows past the batch and slices past the
+  // last read as zeros).
+  constexpr int XV = kNarrowRows * K1 / 4 / kNarrowThreads;
+  constexpr int kFoldGroup = N1 > 128 ? 4 : 8;  // registers: the forward operand is in flight too
+  const int tile_bytes = nrows * K1 * 4;        // from row r0 on
+  const int slice_bytes = (int)(B * K1 * 4);
+  int vo[XV];  // byte offset of the thread's float4 (tile_bytes: past the batch)
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int f = tid + j * kNarrowThreads;
+    const int row = f / (K1 / 4), c = (f % (K1 / 4)) * 4;
+    vo[j] = row < nrows ? (row * K1 + c) * 4 : tile_bytes;
+  }
+  const __amdgpu_buffer_rsrc_t hres =
+      fold_splits > 0 ? buffer_of(fold_part + r0 * K1, (fold_splits - 1) * slice_bytes + tile_bytes)
+                      : buffer_of(Hin + r0 * K1, tile_bytes);
+  f32x4 v[XV];
+  f32x4 p[XV][kFoldGroup];
+  auto fold_fetch = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+#pragma unroll
+      for (int u = 0; u < kFoldGroup; ++u) {
+        const int o = (s0 + u < fold_splits && vo[j] < tile_bytes)
+                          ? vo[j] + (s0 + u) * slice_bytes : 0x7ffffff0;
+        p[j][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, o, 0, 0));
+      }
+  };
+  // slice order, as the finishing kernel of the split forward adds them
+  auto fold_add = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+#pragma unroll
+      for (int u = 0; u < kFoldGroup; ++u)
+        if (s0 + u < fold_splits) v[j] = s0 + u == 0 ? p[j][u] : v[j] + p[j][u];
+  };
+  if (fold_splits > 0) {
+    fold_fetch(0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, vo[j], 0, 0));
+  }
+  // forward operand: W1 rows n = 16 (wave + 8 j) + li, the float4 at k = 16 q + 4 lg
+  f32x4 bf[NBF][K1 / 16];
+  float fb[NBF];
+#pragma unroll
+  for (int j = 0; j < NBF; ++j) {
+    const int n = 16 * (wave + 8 * j) + li;
+#pragma unroll
+    for (int q = 0; q < K1 / 16; ++q)
+      bf[j][q] = *reinterpret_cast<const f32x4*>(W1 + (int64_t)n * K1 + 16 * q + 4 * lg);
+    fb[j] = b1[n];
+  }
+  // the fold's bias b0 at the thread's columns
+  float bb[XV][4];
+  {
+    // (no fold: an empty range over b1, read as zeros and unused)
+    const __amdgpu_buffer_rsrc_t b0res =
+        fold_splits > 0 ? buffer_of(b0, K1 * 4) : buffer_of(b1, 0);
+#pragma unroll
+    for (int j = 0; j < XV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        bb[j][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            b0res, ((tid + j * kNarrowThreads) % (K1 / 4) * 4 + e) * 4, 0, 0));
+  }
+  // W2 transposed into Wt[k][16] (classes past C zero), b2, the labels
+  constexpr int WV = kHeadKMax * kHeadCMax / kNarrowThreads;
+  float wr[WV];
+  {
+    const int w2bytes = C * N1 * 4;
+    const __amdgpu_buffer_rsrc_t w2res = buffer_of(W2, w2bytes);
+#pragma unroll
+    for (int j = 0; j < WV; ++j) {
+      const int i = tid + j * kNarrowThreads;
+      const int k = i / kHeadCMax, c = i % kHeadCMax;
+      const int o = (k < N1 && c < C) ? (c * N1 + k) * 4 : w2bytes;
+      wr[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w2res, o, 0, 0));
+    }
+  }
+  const float bc = __uint_as_float(
+      __builtin_amdgcn_raw_buffer_load_b32(buffer_of(b2, C * 4), tid * 4, 0, 0));
+  const bool active = r < nrows;
+  int y = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_of(reinterpret_cast<const float*>(labels + r0), nrows * 4),
+      active ? r * 4 : nrows * 4, 0, 0);
+  if (!active) y = -1;
+
+  // ---- finish the fold: act0(sum + b0), written out and kept in LDS
+  if (fold_splits > 0) {
+    fold_add(0);
+    for (int s0 = kFoldGroup; s0 < fold_splits; s0 += kFoldGroup) {
+      fold_fetch(s0);
+      fold_add(s0);
+    }
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = relu_or_id(relu0, v[j][e] + bb[j][e]);
+      if (vo[j] < tile_bytes) *reinterpret_cast<f32x4*>(Hin + r0 * K1 + vo[j] / 4) = v[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int f = tid + j * kNarrowThreads;
+    // rows past the batch hold zeros (a fold's act0(b0) is not kept for them)
+    const f32x4 x = vo[j] < tile_bytes ? v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(Xs + (f / (K1 / 4)) * TX + (f % (K1 / 4)) * 4) = x;
+  }
+#pragma unroll
+  for (int j = 0; j < WV; ++j) Wt[tid + j * kNarrowThreads] = wr[j];
+  if (tid < kHeadCMax) Bc[tid] = bc;
+  __syncthreads();
+
+  // ---- forward: H = act1(Hin W1^T + b1), the NBF chains of a wave interleaved
+  {
+    f32x4 acc[NBF];
+#pragma unroll
+    for (int j = 0; j < NBF; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < K1 / 16; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + li * TX + 16 * q + 4 * lg);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < NBF; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], bf[j][q][st], acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NBF; ++j) {
+      const int n = 16 * (wave + 8 * j) + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hs[(4 * lg + e) * TH + n] = relu_or_id(relu1, acc[j][e] + fb[j]);
+    }
+  }
+  // dX operand: W1[n][col] for col = 16 (wave + 8 j) + li and n = 16 q + 4 lg
+  // + st.  With N1 = 128 it fits beside the forward operand and goes out as
+  // early as the compiler places it, arriving while the head runs; with
+  // N1 = 256 (128 registers) it waits until the head is done.
+  float bx[HAS_DX ? NBX : 1][HAS_DX ? N1 / 16 : 1][4];
+  auto load_bx = [&] {
+#pragma unroll
+    for (int j = 0; j < NBX; ++j)
+#pragma unroll
+      for (int q = 0; q < N1 / 16; ++q)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          bx[j][q][st] = W1[(int64_t)(16 * q + 4 * lg + st) * K1 + 16 * (wave + 8 * j) + li];
+  };
+  if (HAS_DX && N1 <= 128) load_bx();
+  __syncthreads();
+
+  // ---- head: logits, softmax cross-entropy, g, G1 = (W2^T g) act1'(H)
+  {
+    float g[kHeadCMax];
+    head_row_loss<TH, kNarrowTPR>(Hs, Wt, Bc, Ds, r, lr, N1, C, y, active, invB, row_loss, r0 + r, g);
+    head_row_dx<TH, kNarrowTPR>(Hs, Wt, Gs, r, lr, N1, act1, g);
+  }
+  __syncthreads();
+  if (HAS_DX && N1 > 128) load_bx();
+
+  // the tile's rows, in order, into this workgroup's dW2 / db2 slice
+  {
+    HeadSlice sl;
+    sl.init(tid, N1);
+    sl.add_tile<TH, kNarrowRows>(Hs, Ds, tid, C);
+    sl.store(dW_part, db_part, blockIdx.x, tid, N1, C);
+  }
+  constexpr int GV = kNarrowRows * N1 / 4 / kNarrowThreads;
+#pragma unroll
+  for (int j = 0; j < GV; ++j) {
+    const int f = tid + j * kNarrowThreads;
+    const int row = f / (N1 / 4), c = (f % (N1 / 4)) * 4;
+    if (row < nrows)
+      *reinterpret_cast<f32x4*>(G1 + (r0 + row) * N1 + c) =
+          *reinterpret_cast<const f32x4*>(Gs + row * TH + c);
+  }
+
+  // ---- dX of the hidden layer: dH = (G1 W1) act0'(Hin)
+  if (HAS_DX) {
+    f32x4 acc[NBX];
+#pragma unroll
+    for (int j = 0; j < NBX; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < N1 / 16; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Gs + li * TH + 16 * q + 4 * lg);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < NBX; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], bx[j][q][st], acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NBX; ++j) {
+      const int col = 16 * (wave + 8 * j) + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * lg + e;
+        if (row < nrows)
+          dH[(r0 + row) * K1 + col] = acc[j][e] * relu_or_id_deriv(relu0, Xs[row * TX + col]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool mlp_tail_fits(int64_t K1, int64_t N1, int64_t C) {
@@ -360,6 +637,43 @@ hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, c
     if (fixed && N1 == 128) go(mlp_tail_kernel<false, 32, 16>);
     else if (fixed) go(mlp_tail_kernel<false, 32, 32>);
     else go(mlp_tail_kernel<false, 0, 0>);
+  }
+  return hipGetLastError();
+}
+
+bool mlp_tail_narrow_fits(int64_t B, int64_t K1, int64_t N1, int64_t C) {
+  return mlp_tail_fits(K1, N1, C) && K1 == 256 && (N1 == 128 || N1 == 256) && B >= 1 &&
+         B <= (int64_t)kNarrowRows * kHeadMaxSlices;
+}
+
+int64_t mlp_tail_narrow_slices(int64_t B) { return (B + kNarrowRows - 1) / kNarrowRows; }
+
+hipError_t launch_mlp_tail_narrow(int64_t B, int K1, int N1, int C, float* Hin,
+                                  const float* fold_part, int fold_splits, const float* b0,
+                                  const float* W1, const float* b1, int act1, int act0,
+                                  const float* W2, const float* b2, const int32_t* labels,
+                                  float* row_loss, float* G1, float* dH, float* dW_part,
+                                  float* db_part, hipStream_t s, const float* dscale) {
+  auto hidden_act = [](int a) { return a == ACT_IDENTITY || a == ACT_RELU; };
+  if (!mlp_tail_narrow_fits(B, K1, N1, C) || fold_splits < 0 ||
+      (fold_splits > 0 && (fold_part == nullptr || b0 == nullptr)) || !hidden_act(act0) ||
+      !hidden_act(act1))
+    return hipErrorInvalidValue;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(Hin) | reinterpret_cast<uintptr_t>(W1) |
+                       reinterpret_cast<uintptr_t>(G1) | reinterpret_cast<uintptr_t>(fold_part);
+  if ((al & 15) != 0) return hipErrorNotSupported;
+  const float invB = (float)(1.0 / (double)B);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)mlp_tail_narrow_slices(B)), dim3(kNarrowThreads), 0, s,
+                       B, C, Hin, fold_part, fold_splits, b0, W1, b1, act1, act0, W2, b2, labels,
+                       row_loss, G1, dH, dW_part, db_part, invB, dscale);
+  };
+  if (dH != nullptr) {
+    if (N1 == 128) go(mlp_tail_narrow_kernel<true, 256, 128>);
+    else go(mlp_tail_narrow_kernel<true, 256, 256>);
+  } else {
+    if (N1 == 128) go(mlp_tail_narrow_kernel<false, 256, 128>);
+    else go(mlp_tail_narrow_kernel<false, 256, 256>);
   }
   return hipGetLastError();
 }

@@ -2,13 +2,18 @@
 head's forward + softmax-xent + vjp, and the hidden layer's dX in one pass
 over the rows) against the composition it replaces.
 
-Both fusion levels run every product in the same order, so every output of a
-training step (loss, dW, db, W, b, Adam moments, parameter averages, the loss
-scale) must be bit-identical at level 2 (tail) and level 1 (head kernel
-alone, the hidden layer as GEMMs), over shapes with ragged row tiles, partial
-32-column blocks, a hidden layer right after the input (no dX), a deeper
-network, one class, and the loss-scale / clipping / EMA options.  The fused
-step is also checked against the float64 oracle on the odd shapes.
+The 32-row form runs every product in the same order as level 1, so every
+output of a training step (loss, dW, db, W, b, Adam moments, parameter
+averages, the loss scale) must be bit-identical at level 2 (tail) and level 1
+(head kernel alone, the hidden layer as GEMMs), over shapes with ragged row
+tiles, partial 32-column blocks, a hidden layer right after the input (no
+dX), a deeper network, one class, and the loss-scale / clipping / EMA options.
+
+A small batch through a 256-wide hidden input with 128 or 256 outputs takes
+the narrow form instead (16-row tiles on the 16x16x4 MFMA, which also
+finishes a split-K forward of the layer before it): its sums run in another
+order, so those shapes are checked against the float64 oracle, as are the
+fused step's odd shapes.
 """
 import numpy as np
 import pytest
@@ -39,7 +44,23 @@ SHAPES = {
     "unrolled_256_256_100": ([64, 256, 256, 10], 100, [R, R, I]),
     "unrolled_no_dx_70": ([256, 128, 10], 70, [R, I]),
     "unrolled_8200": ([784, 256, 128, 10], 8200, [R, R, I]),
+    "unrolled_256_256_4200": ([64, 256, 256, 10], 4200, [R, R, I]),
+    # narrow form; the first two also fold the split-K forward of layer 1
+    "fold_13": ([784, 256, 128, 10], 13, [R, R, I]),
+    "fold_100": ([600, 256, 128, 10], 100, [R, R, I]),
 }
+
+
+def _narrow(name):
+    """Whether the step takes the tail's narrow-batch form for this shape."""
+    dims, B, _ = SHAPES[name]
+    L = len(dims) - 1
+    return L >= 2 and dims[L - 2] == 256 and dims[L - 1] in (128, 256) and dims[L] <= 16 \
+        and B <= 4096
+
+
+BIT_SHAPES = sorted(n for n in SHAPES if not _narrow(n))
+NARROW_SHAPES = sorted(n for n in SHAPES if _narrow(n))
 
 
 @pytest.fixture(scope="module")
@@ -85,8 +106,13 @@ def _tensors(mlp, loss, scaler):
     return [t.clone() for t in out]
 
 
+def test_shape_split():
+    assert NARROW_SHAPES == ["c1_64", "fold_100", "fold_13", "ragged_1000",
+                             "unrolled_256_256_100", "unrolled_no_dx_70"]
+
+
 @pytest.mark.parametrize("opt", sorted(OPTS))
-@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("shape", BIT_SHAPES)
 def test_tail_bit_identical_to_head_only(dl, shape, opt):
     c = OPTS[opt]
     w = _workload(shape, si.SGD)
@@ -114,8 +140,8 @@ def test_tail_bit_identical_to_head_only(dl, shape, opt):
 
 
 @pytest.mark.parametrize("shape", ["narrow_77", "partial_blocks_300", "two_layers_129",
-                                   "four_layers_50", "one_class_40", "identity_hidden_45",
-                                   "unrolled_256_256_100", "unrolled_no_dx_70"])
+                                   "four_layers_50", "one_class_40", "identity_hidden_45"]
+                         + NARROW_SHAPES)
 @pytest.mark.parametrize("optim", ["sgd", "adamw"])
 def test_tail_step_matches_oracle(dl, shape, optim):
     o = si.SGD if optim == "sgd" else si.ADAMW

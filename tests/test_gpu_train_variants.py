@@ -307,6 +307,10 @@ VARIANT_WORKLOADS = {
                            "kaiming", "uniform001", "f32", si.SGD),
     "split_k": si.Workload("var_split", 33, 2048, [784, 256, 10], [O.ACT_RELU, O.ACT_IDENTITY],
                            "kaiming", "uniform001", "f32", si.SGD),
+    # the tail's narrow-batch form, finishing the split-K forward of layer 1
+    "narrow_tail": si.Workload("var_narrow", 34, 64, [784, 256, 128, 10],
+                               [O.ACT_RELU, O.ACT_RELU, O.ACT_IDENTITY], "kaiming", "uniform001",
+                               "f32", si.SGD),
 }
 
 
