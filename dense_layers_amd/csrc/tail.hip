@@ -333,10 +333,11 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
 // blocks and dH (16 x K1) K1/16 blocks over 8 waves, each block a chain of a
 // quarter of the k steps of the 32-row form.  Inside a block, MFMA step s of
 // k group q takes k = 16 q + 4 g + s from lane group g (lanes 16 g .. 16 g +
-// 15), so a lane reads the A operand of 4 steps as one float4.  The sums run
-// in another order than the 32-row form and the standalone kernels (the same
-// products, rounded differently); the head rows use 32 threads each and the
-// same operations as the head kernel.
+// 15), so a lane reads the A operand of 4 steps as one float4.  The head runs
+// on the same MFMA (logits, the head's dX and its dW slice are 16 x 16 x 16
+// products per 16-column block), with the softmax on 16 lanes per row.  The
+// sums run in another order than the 32-row form and the standalone kernels
+// (the same products, rounded differently).
 //
 // Optionally the workgroup also finishes the split-K forward of the layer
 // before it: Hin = act0(sum of the K-slices in slice order + b0), as the
@@ -352,10 +353,17 @@ __device__ __forceinline__ float relu_or_id_deriv(bool relu, float z) {
   return (relu && !(z > 0.0f)) ? 0.0f : 1.0f;
 }
 
+// Maximum over each row of 16 lanes, left in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, head_dpp_mov<0xB1>(v));
+  v = fmaxf(v, head_dpp_mov<0x4E>(v));
+  v = fmaxf(v, head_dpp_mov<0x141>(v));
+  v = fmaxf(v, head_dpp_mov<0x140>(v));
+  return v;
+}
+
 constexpr int kNarrowRows = 16;
 constexpr int kNarrowThreads = kHeadThreads;
-constexpr int kNarrowTPR = kNarrowThreads / kNarrowRows;  // threads per head row
-static_assert(kNarrowTPR == 32, "two 32-lane rows per wave in the head");
 
 template <bool HAS_DX, int K1, int N1>
 __global__ void __launch_bounds__(kNarrowThreads)
@@ -372,17 +380,30 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
   constexpr int NBX = K1 / 128;  // dX blocks per wave
   constexpr int TX = K1 + 4;     // LDS row strides (floats): 16-byte aligned rows
   constexpr int TH = N1 + 4;
-  __shared__ __attribute__((aligned(16))) float Xs[kNarrowRows * TX];  // Hin
-  __shared__ __attribute__((aligned(16))) float Hs[kNarrowRows * TH];  // H
-  __shared__ __attribute__((aligned(16))) float Gs[kNarrowRows * TH];  // G1
-  __shared__ __attribute__((aligned(16))) float Wt[kHeadKMax * kHeadCMax];
-  __shared__ __attribute__((aligned(16))) float Ds[kNarrowRows * kHeadCMax];
+  // With N1 = 128 the forward operand (all of W1, 128 KB) is staged in LDS:
+  // requested as whole 128-byte lines (a wave reads one row per request),
+  // where the MFMA layout read straight from memory would take half a line
+  // per row and request, which measured about twice as slow.  The head's
+  // arrays reuse that space once the forward is done.
+  constexpr bool STAGE = N1 == 128;
+  constexpr int TW = K1 + 4;
+  constexpr int kHeadFloats = 2 * kNarrowRows * TH + N1 * kHeadCMax + 9 * kNarrowRows * kHeadCMax;
+  constexpr int kRegion = STAGE && N1 * TW > kHeadFloats ? N1 * TW : kHeadFloats;
+  __shared__ __attribute__((aligned(16))) float pool[kNarrowRows * TX + kRegion];
+  float* const Xs = pool;                            // Hin [16][TX]
+  float* const W1s = pool + kNarrowRows * TX;        // W1 [N1][TW] (staged forward operand)
+  float* const Hs = W1s;                             // H [16][TH], after the forward
+  float* const Gs = Hs + kNarrowRows * TH;           // G1 [16][TH]
+  float* const Wt = Gs + kNarrowRows * TH;           // W2^T [N1][16]
+  float* const Zp = Wt + N1 * kHeadCMax;             // logit parts [8][16][16]
+  float* const Gm = Zp + 8 * kNarrowRows * kHeadCMax;  // g [16][16]
   __shared__ float Bc[kHeadCMax];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int r = tid / kNarrowTPR, lr = tid % kNarrowTPR;
+  // the head's softmax: threads 0..255, one (row, class) each, 16 lanes per row
+  const int r = tid >> 4, cls = tid & 15;
   const int64_t r0 = (int64_t)blockIdx.x * kNarrowRows;
   const int nrows = (int)min<int64_t>(kNarrowRows, B - r0);
 
@@ -438,17 +459,6 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
     for (int j = 0; j < XV; ++j)
       v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, vo[j], 0, 0));
   }
-  // forward operand: W1 rows n = 16 (wave + 8 j) + li, the float4 at k = 16 q + 4 lg
-  f32x4 bf[NBF][K1 / 16];
-  float fb[NBF];
-#pragma unroll
-  for (int j = 0; j < NBF; ++j) {
-    const int n = 16 * (wave + 8 * j) + li;
-#pragma unroll
-    for (int q = 0; q < K1 / 16; ++q)
-      bf[j][q] = *reinterpret_cast<const f32x4*>(W1 + (int64_t)n * K1 + 16 * q + 4 * lg);
-    fb[j] = b1[n];
-  }
   // the fold's bias b0 at the thread's columns
   float bb[XV][4];
   {
@@ -463,7 +473,7 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
             b0res, ((tid + j * kNarrowThreads) % (K1 / 4) * 4 + e) * 4, 0, 0));
   }
   // W2 transposed into Wt[k][16] (classes past C zero), b2, the labels
-  constexpr int WV = kHeadKMax * kHeadCMax / kNarrowThreads;
+  constexpr int WV = N1 * kHeadCMax / kNarrowThreads;
   float wr[WV];
   {
     const int w2bytes = C * N1 * 4;
@@ -472,17 +482,41 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
     for (int j = 0; j < WV; ++j) {
       const int i = tid + j * kNarrowThreads;
       const int k = i / kHeadCMax, c = i % kHeadCMax;
-      const int o = (k < N1 && c < C) ? (c * N1 + k) * 4 : w2bytes;
+      const int o = c < C ? (c * N1 + k) * 4 : w2bytes;
       wr[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w2res, o, 0, 0));
     }
   }
   const float bc = __uint_as_float(
       __builtin_amdgcn_raw_buffer_load_b32(buffer_of(b2, C * 4), tid * 4, 0, 0));
-  const bool active = r < nrows;
+  const bool active = tid < kNarrowRows * kHeadCMax && r < nrows;
   int y = (int)__builtin_amdgcn_raw_buffer_load_b32(
       buffer_of(reinterpret_cast<const float*>(labels + r0), nrows * 4),
       active ? r * 4 : nrows * 4, 0, 0);
   if (!active) y = -1;
+
+  // The forward operand, requested last: waits are in request order, so the
+  // fold and the LDS stores below do not wait for it.  Staged: thread t takes
+  // the float4s t + 512 i of W1 (row-major, whole lines per wave).  Else the
+  // MFMA layout straight into registers: rows n = 16 (wave + 8 j) + li, the
+  // float4 at k = 16 q + 4 lg, each k group used as it arrives.
+  constexpr int WL = STAGE ? N1 * K1 / 4 / kNarrowThreads : 1;
+  f32x4 wl[WL];
+  f32x4 bf[STAGE ? 1 : NBF][STAGE ? 1 : K1 / 16];
+  float fb[NBF];
+  if (STAGE) {
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+      wl[i] = *reinterpret_cast<const f32x4*>(W1 + (int64_t)(tid + i * kNarrowThreads) * 4);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NBF; ++j)
+#pragma unroll
+      for (int q = 0; q < K1 / 16; ++q)
+        bf[j][q] = *reinterpret_cast<const f32x4*>(
+            W1 + (int64_t)(16 * (wave + 8 * j) + li) * K1 + 16 * q + 4 * lg);
+  }
+#pragma unroll
+  for (int j = 0; j < NBF; ++j) fb[j] = b1[16 * (wave + 8 * j) + li];
 
   // ---- finish the fold: act0(sum + b0), written out and kept in LDS
   if (fold_splits > 0) {
@@ -505,36 +539,19 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
     const f32x4 x = vo[j] < tile_bytes ? v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4*>(Xs + (f / (K1 / 4)) * TX + (f % (K1 / 4)) * 4) = x;
   }
+  if (STAGE) {
 #pragma unroll
-  for (int j = 0; j < WV; ++j) Wt[tid + j * kNarrowThreads] = wr[j];
-  if (tid < kHeadCMax) Bc[tid] = bc;
-  __syncthreads();
-
-  // ---- forward: H = act1(Hin W1^T + b1), the NBF chains of a wave interleaved
-  {
-    f32x4 acc[NBF];
-#pragma unroll
-    for (int j = 0; j < NBF; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < K1 / 16; ++q) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + li * TX + 16 * q + 4 * lg);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int j = 0; j < NBF; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], bf[j][q][st], acc[j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < NBF; ++j) {
-      const int n = 16 * (wave + 8 * j) + li;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Hs[(4 * lg + e) * TH + n] = relu_or_id(relu1, acc[j][e] + fb[j]);
+    for (int i = 0; i < WL; ++i) {
+      const int f = tid + i * kNarrowThreads;
+      *reinterpret_cast<f32x4*>(W1s + (f / (K1 / 4)) * TW + (f % (K1 / 4)) * 4) = wl[i];
     }
   }
+  __syncthreads();
+
   // dX operand: W1[n][col] for col = 16 (wave + 8 j) + li and n = 16 q + 4 lg
-  // + st.  With N1 = 128 it fits beside the forward operand and goes out as
-  // early as the compiler places it, arriving while the head runs; with
-  // N1 = 256 (128 registers) it waits until the head is done.
+  // + st.  With N1 = 128 it is requested now and arrives during the forward
+  // and the head; with N1 = 256 (128 registers) it waits until the head is
+  // done.
   float bx[HAS_DX ? NBX : 1][HAS_DX ? N1 / 16 : 1][4];
   auto load_bx = [&] {
 #pragma unroll
@@ -546,24 +563,103 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
           bx[j][q][st] = W1[(int64_t)(16 * q + 4 * lg + st) * K1 + 16 * (wave + 8 * j) + li];
   };
   if (HAS_DX && N1 <= 128) load_bx();
+
+  // ---- forward: H = act1(Hin W1^T + b1), the NBF chains of a wave interleaved
+  f32x4 facc[NBF];
+#pragma unroll
+  for (int j = 0; j < NBF; ++j) facc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < K1 / 16; ++q) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + li * TX + 16 * q + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < NBF; ++j) {
+      const f32x4 b = STAGE ? *reinterpret_cast<const f32x4*>(
+                                  W1s + (16 * (wave + 8 * j) + li) * TW + 16 * q + 4 * lg)
+                            : bf[STAGE ? 0 : j][STAGE ? 0 : q];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        facc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], facc[j], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with W1s, whose space the head reuses
+#pragma unroll
+  for (int j = 0; j < NBF; ++j) {
+    const int n = 16 * (wave + 8 * j) + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Hs[(4 * lg + e) * TH + n] = relu_or_id(relu1, facc[j][e] + fb[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < WV; ++j) Wt[tid + j * kNarrowThreads] = wr[j];
+  if (tid < kHeadCMax) Bc[tid] = bc;
   __syncthreads();
 
-  // ---- head: logits, softmax cross-entropy, g, G1 = (W2^T g) act1'(H)
+  // ---- head on the matrix cores (classes padded to 16 with zero weights).
+  // Logits Z = H W2^T: wave w adds k in [16 w, 16 w + 16) (+128 for N1 = 256)
+  // into a 16x16 part, and the 8 parts are added in wave order.
   {
-    float g[kHeadCMax];
-    head_row_loss<TH, kNarrowTPR>(Hs, Wt, Bc, Ds, r, lr, N1, C, y, active, invB, row_loss, r0 + r, g);
-    head_row_dx<TH, kNarrowTPR>(Hs, Wt, Gs, r, lr, N1, act1, g);
+    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < N1; kb += 128) {
+      const int k0 = kb + 16 * wave + 4 * lg;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Hs + li * TH + k0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], Wt[(k0 + st) * kHeadCMax + li], zacc, 0,
+                                                    0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Zp[(wave * kNarrowRows + 4 * lg + e) * kHeadCMax + li] = zacc[e];
+  }
+  __syncthreads();
+  // softmax cross-entropy of row r, class cls: loss = logsumexp(z) - z[y],
+  // g = (softmax(z) - onehot(y)) / B (zero past C and for rows past the batch)
+  if (tid < kNarrowRows * kHeadCMax) {
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) z += Zp[(w * kNarrowRows + r) * kHeadCMax + cls];
+    z += Bc[cls];
+    const bool in_c = cls < C;
+    const float m = row16_max(in_c ? z : -INFINITY);
+    const float ez = in_c ? __expf(z - m) : 0.f;
+    const float sum = row16_sum(ez);
+    const float zy = row16_sum(cls == y ? z : 0.f);  // one term
+    const bool valid = y >= 0 && y < C;
+    if (active && cls == 0) row_loss[r0 + r] = valid ? (m + __logf(sum)) - zy : __builtin_nanf("");
+    const float inv_s = 1.0f / sum;
+    Gm[r * kHeadCMax + cls] = (active && in_c) ? (ez * inv_s - (cls == y ? 1.0f : 0.0f)) * invB : 0.f;
+  }
+  __syncthreads();
+  // G1 = (g W2) act1'(H) and the slice dW2 = g^T H on the wave's forward
+  // blocks, db2 = the column sums of g (rows in order)
+#pragma unroll
+  for (int j = 0; j < NBF; ++j) {
+    const int cb = wave + 8 * j;
+    const int n = 16 * cb + li;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(Gm + li * kHeadCMax + 4 * lg);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(Wt + n * kHeadCMax + 4 * lg);
+    f32x4 gacc = {0.f, 0.f, 0.f, 0.f}, wacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], gacc, 0, 0, 0);
+      const int row = 4 * lg + st;
+      wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(Gm[row * kHeadCMax + li], Hs[row * TH + n], wacc,
+                                                  0, 0, 0);
+    }
+    float* dWp = dW_part + (int64_t)blockIdx.x * C * N1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * lg + e;  // a row of G1, a class of dW2
+      Gs[row * TH + n] = gacc[e] * relu_or_id_deriv(relu1, Hs[row * TH + n]);
+      if (row < C) dWp[(int64_t)row * N1 + n] = wacc[e];
+    }
+  }
+  if (tid < C) {
+    float db = 0.f;
+    for (int q = 0; q < kNarrowRows; ++q) db += Gm[q * kHeadCMax + tid];
+    db_part[(int64_t)blockIdx.x * C + tid] = db;
   }
   __syncthreads();
   if (HAS_DX && N1 > 128) load_bx();
-
-  // the tile's rows, in order, into this workgroup's dW2 / db2 slice
-  {
-    HeadSlice sl;
-    sl.init(tid, N1);
-    sl.add_tile<TH, kNarrowRows>(Hs, Ds, tid, C);
-    sl.store(dW_part, db_part, blockIdx.x, tid, N1, C);
-  }
   constexpr int GV = kNarrowRows * N1 / 4 / kNarrowThreads;
 #pragma unroll
   for (int j = 0; j < GV; ++j) {
