@@ -58,6 +58,19 @@ def kernel_source_hash(names=None) -> str:
     return h.hexdigest()[:16]
 
 
+def profiled_stage(workload: str):
+    """The launch the committed counter summary of `workload` measured, or
+    None when there is none or its kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(rec.get("sources")):
+        return None
+    return rec.get("stage")
+
+
 def stored_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or
@@ -787,6 +800,13 @@ def main():
         bench.graph = None  # the per-launch timing runs the same step eagerly
     stages = profile_stages(dl, bench, max(1, min(args.prof_steps, steps)))
     dom = max(stages, key=lambda x: x["ms"])
+    # launches of the same shape run within a few percent of each other; if
+    # the committed counter summary took a launch within 3% of the longest,
+    # the line reports that one, so its traffic figure applies
+    prof = profiled_stage(w.name)
+    for st in stages:
+        if prof is not None and st["stage"] == prof and st["ms"] >= 0.97 * dom["ms"]:
+            dom = st
     peak = PEAK_BF16_MFMA if w.dtype in ("bf16", "f16") else PEAK_FP32_MFMA  # half: same rate
     traffic = stored_traffic(w.name, dom["stage"])
     if "tflops" in dom:
