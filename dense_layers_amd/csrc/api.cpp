@@ -1453,7 +1453,15 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       d.epi = dl::EPI_DW;  // float32 slices, no column sums
       d.splits = fp.splits; d.k_per_split = fp.k_per_split;
       d.partial = slices;
-      e = timed("fwd_gemm", s, [&] { return dl::launch_gemm_f32(d, fp.tile, s); });
+      // before the narrow tail: the slices on 16-row tiles (the tail adds them)
+      const bool fwd_narrow =
+          narrow && l == last_gemm && dl::mlp_fwd_narrow_fits(B, ly.in, ly.out, fp.k_per_split) &&
+          al16(in) && al16(ly.W);
+      e = timed("fwd_gemm", s, [&] {
+        return fwd_narrow ? dl::launch_mlp_fwd_narrow((int)B, (int)ly.in, (int)ly.out, fp.splits,
+                                                      fp.k_per_split, in, ly.W, slices, s)
+                          : dl::launch_gemm_f32(d, fp.tile, s);
+      });
       if (narrow && l == last_gemm) {  // the tail finishes it
         fold_part = slices;
         fold_splits = fp.splits;

@@ -654,6 +654,15 @@ hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, c
 // written to Hin; else it is read from Hin.  hipErrorNotSupported when Hin,
 // W1, G1 or fold_part is not 16-byte aligned (nothing launched).
 bool mlp_tail_narrow_fits(int64_t B, int64_t K1, int64_t N1, int64_t C);
+// The K-slices slices[s][B][N] of X [B, K] W^T (W [N, K]) for a small batch,
+// slice s over k in [s kps, min(K, (s + 1) kps)), on 16-row x 64-column
+// tiles and the 16x16x4 MFMA (the narrow tail then adds them with the bias
+// and activation).  Needs K % 4 == 0, kps a multiple of 16 up to 256, and
+// splits slices covering K exactly; hipErrorNotSupported when X or W is not
+// 16-byte aligned (nothing launched).
+bool mlp_fwd_narrow_fits(int64_t B, int64_t K, int64_t N, int kps);
+hipError_t launch_mlp_fwd_narrow(int B, int K, int N, int splits, int kps, const float* X,
+                                 const float* W, float* slices, hipStream_t s);
 int64_t mlp_tail_narrow_slices(int64_t B);
 hipError_t launch_mlp_tail_narrow(int64_t B, int K1, int N1, int C, float* Hin,
                                   const float* fold_part, int fold_splits, const float* b0,

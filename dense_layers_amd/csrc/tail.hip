@@ -697,6 +697,88 @@ mlp_tail_narrow_kernel(int64_t B, int C, float* __restrict__ Hin, const float* _
   }
 }
 
+// ---- the small-batch forward before the narrow tail ---------------------------
+// K-slices of Y = X W^T (no bias or activation: the narrow tail adds the
+// slices in order and applies them) for a batch of a few 16-row tiles and a
+// long contraction: workgroup (row tile, 64-column block, slice) stages its
+// 16 rows of X and 64 rows of W over the slice's k range in LDS (whole-line
+// loads, rows past the batch or N and k past K read as zero) and its 4 waves
+// each run one 16x16 block on the 16x16x4 MFMA, k = 16 q + 4 g + s as in the
+// narrow tail.  Slice s covers k in [s kps, min(K, (s + 1) kps)) and goes to
+// slices[s][B][N].
+constexpr int kFwdNarrowCols = 64;
+constexpr int kFwdNarrowMaxK = 256;
+
+__global__ void __launch_bounds__(256)
+mlp_fwd_narrow_kernel(int B, int K, int N, int kps, const float* __restrict__ X,
+                      const float* __restrict__ W, float* __restrict__ slices) {
+  constexpr int TS = kFwdNarrowMaxK + 4;  // LDS row stride (floats)
+  __shared__ __attribute__((aligned(16))) float Xs[kNarrowRows * TS];
+  __shared__ __attribute__((aligned(16))) float Ws[kFwdNarrowCols * TS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int tiles_r = (B + kNarrowRows - 1) / kNarrowRows;
+  const int tiles_c = (N + kFwdNarrowCols - 1) / kFwdNarrowCols;
+  const int bid = blockIdx.x;
+  const int sl = bid / (tiles_r * tiles_c);
+  const int rc = bid % (tiles_r * tiles_c);
+  const int r0 = (rc % tiles_r) * kNarrowRows, c0 = (rc / tiles_r) * kFwdNarrowCols;
+  const int k0 = sl * kps;
+  const int kn = min(K, k0 + kps) - k0;  // k in this slice (> 0)
+  const int kv = kps / 4;                 // float4 per staged row
+
+  // stage the 16 rows of X and 64 of W: every load issued before the first
+  // store, through buffer resources whose range check reads an out-of-range
+  // lane as zero (no load behind a branch)
+  constexpr int kXV = kNarrowRows * kFwdNarrowMaxK / 4 / 256;
+  constexpr int kWV = kFwdNarrowCols * kFwdNarrowMaxK / 4 / 256;
+  const int xbytes = B * K * 4, wbytes = N * K * 4;
+  const __amdgpu_buffer_rsrc_t xres = buffer_of(X, xbytes), wres = buffer_of(W, wbytes);
+  f32x4 xv[kXV], wv[kWV];
+  auto offset = [&](int f, int rows, int g0, int glim, int oob) {
+    const int row = f / kv, c = (f % kv) * 4;
+    return (f < rows * kv && c < kn && g0 + row < glim) ? ((g0 + row) * K + k0 + c) * 4 : oob;
+  };
+#pragma unroll
+  for (int j = 0; j < kXV; ++j)
+    xv[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          xres, offset(tid + j * 256, kNarrowRows, r0, B, xbytes), 0, 0));
+#pragma unroll
+  for (int j = 0; j < kWV; ++j)
+    wv[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          wres, offset(tid + j * 256, kFwdNarrowCols, c0, N, wbytes), 0, 0));
+#pragma unroll
+  for (int j = 0; j < kXV; ++j) {
+    const int f = tid + j * 256;
+    if (f < kNarrowRows * kv) *reinterpret_cast<f32x4*>(Xs + (f / kv) * TS + (f % kv) * 4) = xv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kWV; ++j) {
+    const int f = tid + j * 256;
+    if (f < kFwdNarrowCols * kv) *reinterpret_cast<f32x4*>(Ws + (f / kv) * TS + (f % kv) * 4) = wv[j];
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* xa = Xs + li * TS + 4 * lg;
+  const float* wb = Ws + (16 * wave + li) * TS + 4 * lg;
+  for (int q = 0; q < kps / 16; ++q) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(xa + 16 * q);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(wb + 16 * q);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b[st], acc, 0, 0, 0);
+  }
+  const int col = c0 + 16 * wave + li;
+  float* out = slices + (int64_t)sl * B * N;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = r0 + 4 * lg + e;
+    if (row < B && col < N) out[(int64_t)row * N + col] = acc[e];
+  }
+}
+
 }  // namespace
 
 bool mlp_tail_fits(int64_t K1, int64_t N1, int64_t C) {
@@ -743,6 +825,27 @@ bool mlp_tail_narrow_fits(int64_t B, int64_t K1, int64_t N1, int64_t C) {
 }
 
 int64_t mlp_tail_narrow_slices(int64_t B) { return (B + kNarrowRows - 1) / kNarrowRows; }
+
+bool mlp_fwd_narrow_fits(int64_t B, int64_t K, int64_t N, int kps) {
+  // byte offsets of X and W in 31 bits (buffer loads)
+  return B >= 1 && B <= 4096 && N >= 1 && K % 4 == 0 && kps % 16 == 0 && kps > 0 &&
+         kps <= kFwdNarrowMaxK && B * K * 4 < (int64_t)1 << 31 && N * K * 4 < (int64_t)1 << 31;
+}
+
+hipError_t launch_mlp_fwd_narrow(int B, int K, int N, int splits, int kps, const float* X,
+                                 const float* W, float* slices, hipStream_t s) {
+  if (!mlp_fwd_narrow_fits(B, K, N, kps) || splits < 1 || (int64_t)(splits - 1) * kps >= K ||
+      (int64_t)splits * kps < K)
+    return hipErrorInvalidValue;
+  if (((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W)) & 15) != 0)
+    return hipErrorNotSupported;
+  const int64_t blocks = (int64_t)((B + kNarrowRows - 1) / kNarrowRows) *
+                         ((N + kFwdNarrowCols - 1) / kFwdNarrowCols) * splits;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mlp_fwd_narrow_kernel, dim3((unsigned)blocks), dim3(256), 0, s, B, K, N, kps,
+                     X, W, slices);
+  return hipGetLastError();
+}
 
 hipError_t launch_mlp_tail_narrow(int64_t B, int K1, int N1, int C, float* Hin,
                                   const float* fold_part, int fold_splits, const float* b0,
