@@ -647,7 +647,7 @@ hipError_t launch_mlp_tail(int64_t B, int K1, int N1, int C, const float* Hin, c
                            const int32_t* labels, float* row_loss, float* G1, float* dH,
                            float* dW_part, float* db_part, hipStream_t s,
                            const float* dscale = nullptr);
-// The same tail for a small batch (K1 = 256, N1 = 128 or 256, B <= 4096):
+// The same tail for a smaller batch (K1 = 256, N1 = 128 or 256, B <= 8192):
 // 16-row tiles on the 16x16x4 MFMA, one per workgroup, dW / db as
 // mlp_tail_narrow_slices(B) slices.  With fold_splits > 0, Hin is first
 // formed as act0(sum of fold_splits K-slices fold_part[s][B][K1] + b0) and

@@ -44,7 +44,7 @@ SHAPES = {
     "unrolled_256_256_100": ([64, 256, 256, 10], 100, [R, R, I]),
     "unrolled_no_dx_70": ([256, 128, 10], 70, [R, I]),
     "unrolled_8200": ([784, 256, 128, 10], 8200, [R, R, I]),
-    "unrolled_256_256_4200": ([64, 256, 256, 10], 4200, [R, R, I]),
+    "unrolled_256_256_8300": ([64, 256, 256, 10], 8300, [R, R, I]),
     # narrow form; the first two also fold the split-K forward of layer 1
     "fold_13": ([784, 256, 128, 10], 13, [R, R, I]),
     "fold_100": ([600, 256, 128, 10], 100, [R, R, I]),
@@ -56,7 +56,7 @@ def _narrow(name):
     dims, B, _ = SHAPES[name]
     L = len(dims) - 1
     return L >= 2 and dims[L - 2] == 256 and dims[L - 1] in (128, 256) and dims[L] <= 16 \
-        and B <= 4096
+        and B <= 8192
 
 
 BIT_SHAPES = sorted(n for n in SHAPES if not _narrow(n))
@@ -107,7 +107,7 @@ def _tensors(mlp, loss, scaler):
 
 
 def test_shape_split():
-    assert NARROW_SHAPES == ["c1_64", "fold_100", "fold_13", "ragged_1000",
+    assert NARROW_SHAPES == ["c1_64", "c2_8192", "fold_100", "fold_13", "ragged_1000",
                              "unrolled_256_256_100", "unrolled_no_dx_70"]
 
 
