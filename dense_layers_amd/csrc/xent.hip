@@ -269,31 +269,68 @@ loss_mean_kernel(int64_t B, const float* __restrict__ row_loss, float* __restric
 
 // Fused classifier head, after its forward GEMM: row i's log-sum-exp from the
 // T column tiles' (max, sum exp(z - max)) pairs part[2 (t B + i)]:
-//   m = max_t m_t,  s = sum_t s_t exp(m_t - m)  (tile order),  lse = m + log s,
-// and its loss lse - z[i, y_i] (NaN for a label outside [0, C)).  One thread
-// per row; the pairs of consecutive rows are adjacent, so each tile's read
-// is one coalesced 8-byte access per thread.
-constexpr int kLseBlock = 256;
-__global__ void __launch_bounds__(kLseBlock)
+//   m = max_t m_t,  s = sum_t s_t exp(m_t - m),  lse = m + log s,
+// and its loss lse - z[i, y_i] (NaN for a label outside [0, C)).  A
+// workgroup of kLseWaves waves takes 64 rows (a lane per row, so each read of
+// a tile is 512 contiguous bytes); wave w takes the tiles w, w + kLseWaves,
+// ..., keeping them in registers when T <= kLseWaves kLseMaxPer (else it
+// reads them twice).  The maxima combine exactly in any order; the sums are
+// added in tile order within a wave, then the waves' sums in wave order.
+constexpr int kLseWaves = 8;
+constexpr int kLseMaxPer = 32;
+__global__ void __launch_bounds__(kLseWaves * 64)
 xent_lse_kernel(int64_t B, int64_t C, int T, const float* __restrict__ part,
                 const float* __restrict__ logits, const int32_t* __restrict__ labels,
                 float* __restrict__ lse, float* __restrict__ row_loss) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const int64_t row = (int64_t)blockIdx.x * kLseBlock + threadIdx.x;
-  if (row >= B) return;
-  const f32x2* p = reinterpret_cast<const f32x2*>(part) + row;
-  float m = -INFINITY;
-  for (int t = 0; t < T; ++t) m = fmaxf(m, p[(int64_t)t * B][0]);
-  float s = 0.f;
-  for (int t = 0; t < T; ++t) {
-    const f32x2 v = p[(int64_t)t * B];
-    s += v[1] * __expf(v[0] - m);
+  __shared__ float red[kLseWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 64 + lane;
+  const bool ok = row < B;
+  const f32x2* p = reinterpret_cast<const f32x2*>(part) + (ok ? row : 0);  // rows past B: row 0
+  float m = -INFINITY, s = 0.f;
+  if (T <= kLseWaves * kLseMaxPer) {
+    f32x2 v[kLseMaxPer];
+#pragma unroll
+    for (int i = 0; i < kLseMaxPer; ++i) {
+      const int t = w + kLseWaves * i;
+      v[i] = t < T ? p[(int64_t)t * B] : f32x2{-INFINITY, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kLseMaxPer; ++i) m = fmaxf(m, v[i][0]);
+    red[w][lane] = m;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kLseWaves; ++x) m = fmaxf(m, red[x][lane]);
+#pragma unroll
+    for (int i = 0; i < kLseMaxPer; ++i)
+      if (w + kLseWaves * i < T) s += v[i][1] * __expf(v[i][0] - m);
+  } else {
+    for (int t = w; t < T; t += kLseWaves) m = fmaxf(m, p[(int64_t)t * B][0]);
+    red[w][lane] = m;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kLseWaves; ++x) m = fmaxf(m, red[x][lane]);
+    for (int t = w; t < T; t += kLseWaves) {
+      const f32x2 v = p[(int64_t)t * B];
+      s += v[1] * __expf(v[0] - m);
+    }
   }
+  __syncthreads();  // every wave has read the maxima
+  red[w][lane] = s;
+  __syncthreads();
+  if (w != 0 || !ok) return;
+  s = red[0][lane];
+#pragma unroll
+  for (int x = 1; x < kLseWaves; ++x) s += red[x][lane];
   const float l = m + logf(s);
   lse[row] = l;
   const int32_t y = labels[row];
   row_loss[row] = (y >= 0 && (int64_t)y < C) ? l - logits[row * C + y] : __builtin_nanf("");
 }
+
+constexpr int kLseBlock = 256;  // the row-record pass
 
 // Per-row records of the fused head's backward: exponent offset and label.
 __global__ void __launch_bounds__(kLseBlock)
@@ -371,8 +408,9 @@ hipError_t launch_xent(int64_t B, int64_t C, const float* logits, const int32_t*
 
 hipError_t launch_xent_lse(int64_t B, int64_t C, int T, const float* part, const float* logits,
                            const int32_t* labels, float* lse, float* row_loss, hipStream_t s) {
-  const int64_t blocks = (B + kLseBlock - 1) / kLseBlock;
-  hipLaunchKernelGGL(xent_lse_kernel, dim3((unsigned)blocks), dim3(kLseBlock), 0, s, B, C, T,
+  const int64_t blocks = (B + 63) / 64;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xent_lse_kernel, dim3((unsigned)blocks), dim3(kLseWaves * 64), 0, s, B, C, T,
                      part, logits, labels, lse, row_loss);
   return hipGetLastError();
 }
