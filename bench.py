@@ -784,16 +784,25 @@ def main():
     for _ in range(warmup):
         bench.step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps in (up to) 5 samples, an event pair on the launch stream
+    # at each boundary, for the median / min / max of ms per step
+    n_samp = max(1, min(5, steps))
+    bounds = [steps * i // n_samp for i in range(n_samp + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_samp + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        bench.step()
-    ev1.record(stream)
+    evs[0].record(stream)
+    for j in range(n_samp):
+        for _ in range(bounds[j + 1] - bounds[j]):
+            bench.step()
+        evs[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / steps
-    gpu_ms_step = ev0.elapsed_time(ev1) / steps
+    gpu_ms_step = evs[0].elapsed_time(evs[-1]) / steps
+    samp = sorted(evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j])
+                  for j in range(n_samp))
+    step_samples = {"n": n_samp, "median_ms": round(samp[n_samp // 2], 5),
+                    "min_ms": round(samp[0], 5), "max_ms": round(samp[-1], 5)}
     step_tflops = bench.flops() / (ms_step * 1e-3) / 1e12
 
     if args.graph:
@@ -843,6 +852,7 @@ def main():
         "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "gpu_ms_per_step": round(gpu_ms_step, 5),
+        "gpu_step_samples": step_samples,
         "step_tflops": round(step_tflops, 3),
         "step_frac_of_peak": round(step_tflops / peak, 4),
         "higher_is_better": True,
