@@ -330,10 +330,11 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
 // 256-long forward), so the step waits on chain latency.  The narrow form
 // gives each workgroup one tile of 16 rows (a 64-row batch spreads over 4
 // CUs) and runs both products on the 16x16x4 MFMA: H (16 x N1) is N1/16
-// blocks and dH (16 x K1) K1/16 blocks over 8 waves, each block a chain of a
-// quarter of the k steps of the 32-row form.  Inside a block, MFMA step s of
-// k group q takes k = 16 q + 4 g + s from lane group g (lanes 16 g .. 16 g +
-// 15), so a lane reads the A operand of 4 steps as one float4.  The head runs
+// blocks and dH (16 x K1) K1/16 blocks over 8 waves, each block a chain of
+// half as many MFMAs as a 32-row block, each taking half as long.  Inside a
+// block, MFMA step s of k group q takes k = 16 q + 4 g + s from lane group g
+// (lanes 16 g .. 16 g + 15), so a lane reads the A operand of 4 steps as one
+// float4.  The head runs
 // on the same MFMA (logits, the head's dX and its dW slice are 16 x 16 x 16
 // products per 16-column block), with the softmax on 16 lanes per row.  The
 // sums run in another order than the 32-row form and the standalone kernels
@@ -343,6 +344,7 @@ mlp_tail_kernel(int64_t B, int K1, int N1, int C, int64_t tiles_per,
 // before it: Hin = act0(sum of the K-slices in slice order + b0), as the
 // finishing kernel of that forward computes it, written out for the weight
 // gradient that reads it and kept in LDS.
+
 // Identity or ReLU, the hidden activations of the MLP step, as selects
 // rather than branches: the values of act_apply / act_deriv for those two
 // (a NaN maps to 0 under ReLU, as there).
