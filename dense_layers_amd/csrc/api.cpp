@@ -173,14 +173,12 @@ Plan plan_gemm(int dtype, int epi, int64_t M, int64_t N, int64_t K) {
   int bm, bn, bk;
   tile_shape(dtype, 0, bm, bn, bk);
   int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-  // bf16 weight gradients: 256x256 tiles of four waves when there are
-  // enough of them, else 128x128; the split-K count aims at two workgroups
-  // per CU for the former and four for the latter.
+  // 16-bit weight gradients run on the register-staged kernel's 128x128
+  // tile, split along K for about two workgroups per CU (four K-slices
+  // measured the same, one slower); float32 ones aim at four per CU.
   int64_t per_cu = 4;
-  if (dtype != DL_F32 && epi == dl::EPI_DW && tiles >= 32) {
-    p.tile = 2;
-    per_cu = 1;
-  } else if (tiles < kCUs || (dtype != DL_F32 && epi == dl::EPI_DW)) {
+  if (dtype != DL_F32 && epi == dl::EPI_DW) per_cu = 2;
+  if (tiles < kCUs || (dtype != DL_F32 && epi == dl::EPI_DW)) {
     p.tile = 1;
     if (dtype == DL_F32 && epi != dl::EPI_DW && ceil_div(M, 64) * ceil_div(N, 128) >= kCUs)
       p.tile = 2;

@@ -374,11 +374,16 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
-// Tiles 0 and 1 go to the direct-to-LDS kernel (256x256 and 128x128) when
-// the operands allow it; everything else, and operands it declines, runs the
-// general kernel at 128x128 (4 waves of 64x64, two workgroups per CU).
+// Forward and dX products go to the direct-to-LDS kernel (tile 0: 256x256,
+// tile 1: 128x128) when the operands allow it; weight gradients (both
+// operands M/N-major), and operands it declines, run the general kernel at
+// 128x128 (4 waves of 64x64, two workgroups per CU).  For the weight
+// gradients this kernel's transpose in registers, which leaves both operands
+// K-contiguous in LDS for 16-byte fragment reads, measured faster than the
+// direct-to-LDS kernel's transposing 8-byte reads (the 32768-token
+// transformer MLP's two weight gradients: 326-342 against 395-401 us).
 hipError_t launch_gemm_bf16(const GemmDesc& d, int tile, hipStream_t s) {
-  if (tile >= 0 && tile <= 2) {
+  if ((tile == 0 || tile == 1) && d.epi != EPI_DW) {
     const hipError_t e = launch_gemm_bf16_dma(d, tile, s);
     if (e != hipErrorNotSupported) return e;
   }

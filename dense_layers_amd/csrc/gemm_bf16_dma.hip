@@ -7,10 +7,13 @@
 // MFMA, the output rounding (half saturates at +-65504) and the reading of
 // saved activations differ (HalfOps).
 //
-// The products are the three of the fused LinearAct (noeira.nn docs, "The
-// design in one page"): forward Z = X W^T + b, dX = (dY o act') W and
-// dW = (dY o act')^T X, on the bf16 working copies of the FP32-master-weight
-// scheme (Orthon page, "Mixed-precision training on CUDA").
+// The products are those of the fused LinearAct (noeira.nn docs, "The
+// design in one page"): forward Z = X W^T + b and dX = (dY o act') W, on the
+// bf16 working copies of the FP32-master-weight scheme (Orthon page,
+// "Mixed-precision training on CUDA").  The kernel's weight-gradient form
+// dW = (dY o act')^T X (float32 slices, the db sums) is kept in the template
+// but no longer launched: the register-staged kernel of gemm_bf16.hip
+// measured faster for those products, whose operands are both M/N-major.
 //
 // Pipeline: STAGES LDS buffers of BK k each.  The loads of stage
 // g + STAGES - 1 are issued during stage g (spread over its k-steps), so each
@@ -716,9 +719,7 @@ hipError_t dma_layout(const GemmDesc& d, hipStream_t s) {
     return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, K_MAJOR, EPI_DX, PERSIST, HK>(d, s);
   if (d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR)
     return launch_dma<BM, BN, BK, STAGES, WGM, WGN, K_MAJOR, MN_MAJOR, EPI_DX, PERSIST, HK>(d, s);
-  if (d.epi == EPI_DW && d.a_layout == MN_MAJOR && d.b_layout == MN_MAJOR)
-    return launch_dma<BM, BN, BK, STAGES, WGM, WGN, MN_MAJOR, MN_MAJOR, EPI_DW, PERSIST, HK>(d, s);
-  return hipErrorNotSupported;
+  return hipErrorNotSupported;  // weight gradients run the register-staged kernel
 }
 
 }  // namespace
@@ -742,9 +743,6 @@ hipError_t launch_tile(const GemmDesc& d, int tile, hipStream_t s) {
       return dma_layout<256, 256, 32, 4, 2, 4, false, HK>(d, s);
     }
     case 1: return dma_layout<128, 128, 64, 2, 2, 2, false, HK>(d, s);
-    // weight gradients (both operands M/N-major): four waves of 128x128 halve
-    // the transposing LDS reads per MFMA against eight waves of 128x64
-    case 2: return dma_layout<256, 256, 64, 2, 2, 2, false, HK>(d, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -95,8 +95,8 @@ def test_f16_large_tile_dx_with_prev_gelu(dl, use_wt):
 
 @pytest.mark.parametrize("shape", [(2048, 1032, 2000), (1024, 1000, 200)])
 def test_f16_weight_gradient_tiles(dl, shape):
-    """The four-wave 256x256 weight-gradient tile and the split-K 128x128
-    one, ragged in both output dimensions."""
+    """Half weight gradients of two sizes (the register-staged 128x128 tile,
+    split along the batch), ragged in both output dimensions."""
     B, n_in, n_out = shape
     X, dY = _m(940, (B, n_in)), _m(941, (B, n_out))
     W = _m(942, (n_out, n_in), 0.05)

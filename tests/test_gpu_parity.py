@@ -252,8 +252,8 @@ def test_bf16_persistent_dx_ragged(dl):
 
 
 def test_bf16_dw_wide_tile_ragged(dl):
-    """Weight gradient on the four-wave 256x256 tile (at least 32 such tiles),
-    split along the batch, ragged in both output dimensions."""
+    """A large weight gradient (register-staged 128x128 tiles, split along
+    the batch), ragged in both output dimensions."""
     B, n_in, n_out = 2048, 1032, 2000
     X = si.random_matrix(280, (B, n_in), bf16_exact=True)
     W = si.random_matrix(281, (n_out, n_in), scale=0.05, bf16_exact=True)
