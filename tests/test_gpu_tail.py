@@ -48,6 +48,9 @@ SHAPES = {
     # narrow form; the first two also fold the split-K forward of layer 1
     "fold_13": ([784, 256, 128, 10], 13, [R, R, I]),
     "fold_100": ([600, 256, 128, 10], 100, [R, R, I]),
+    # narrow form at the class-count edges: one class, and 16 over a 256-wide layer
+    "narrow_one_class_50": ([64, 256, 128, 1], 50, [R, R, I]),
+    "narrow_16_classes_33": ([64, 256, 256, 16], 33, [R, I, I]),
 }
 
 
@@ -107,8 +110,9 @@ def _tensors(mlp, loss, scaler):
 
 
 def test_shape_split():
-    assert NARROW_SHAPES == ["c1_64", "c2_8192", "fold_100", "fold_13", "ragged_1000",
-                             "unrolled_256_256_100", "unrolled_no_dx_70"]
+    assert NARROW_SHAPES == ["c1_64", "c2_8192", "fold_100", "fold_13", "narrow_16_classes_33",
+                             "narrow_one_class_50", "ragged_1000", "unrolled_256_256_100",
+                             "unrolled_no_dx_70"]
 
 
 @pytest.mark.parametrize("opt", sorted(OPTS))
