@@ -131,6 +131,14 @@ def xent_grad_band(z, tau, batch_total: int, scale: float = 1.0, labels=None,
     z = np.asarray(z, dtype=np.float64)
     tau = np.asarray(tau, dtype=np.float64)
     B, C = z.shape
+    # A deviation beyond the exponential's range makes eps (and the sum's
+    # bound) inf or, where a tiny probability meets it, NaN: such rows are
+    # caught by `lost` below, so the floating-point flags are not errors.
+    with np.errstate(over="ignore", invalid="ignore"):
+        return _xent_grad_band(z, tau, B, C, batch_total, labels, scale, form)
+
+
+def _xent_grad_band(z, tau, B, C, batch_total, labels, scale, form):
     m = z.max(axis=1, keepdims=True)
     d = z - m                                   # <= 0
     e = np.exp(d)
@@ -148,7 +156,7 @@ def xent_grad_band(z, tau, batch_total: int, scale: float = 1.0, labels=None,
     eps_s = (es + gamma(C) * (s + es)) / s
     # rows whose logits may move so far that the sum is not bounded away
     # from zero: only |p' - p| <= 1 (+ rounding) is left there
-    lost = eps_s >= 1.0
+    lost = ~(eps_s < 1.0)                       # NaN included
     eps_s = np.where(lost, 0.0, eps_s)
     p = e
     p /= s                                      # e is not needed past here

@@ -265,6 +265,20 @@ def test_xent_grad_band_saturates_for_huge_logit_deviation():
     assert np.all(band >= 1.0 / 4)
 
 
+def test_xent_grad_band_caps_rows_whose_bound_overflows():
+    """A deviation past the exponential's range, on a row where another
+    class's exponential underflows (0 times inf in the sum's bound), still
+    bounds every probability's move by the cap, with no NaN; rows with a
+    small deviation keep their finite, smaller band."""
+    z = np.array([[0.0, -800.0, 1.0], [0.0, 1.0, 2.0]])
+    tau = np.array([[400.0, 400.0, 400.0], [1e-6, 1e-6, 1e-6]])
+    band = O.xent_grad_band(z, tau, 4, labels=np.array([1, 0]))
+    cap = (1.0 + 4 * U) * (1 + O.gamma(4)) / 4 * 1.0001 + O.gamma(4) / 4
+    assert np.all(np.isfinite(band))
+    assert np.all(band[0] >= 1.0 / 4) and np.all(band[0] <= cap)
+    assert np.all(band[1] < 1e-5)
+
+
 def _f32_lse_grad(zp, y, B, tile, rng):
     """Float32 softmax-xent gradient of one row formed as the fused head does:
     per column tile its max and sum of exp, the tiles combined in order,
