@@ -101,12 +101,12 @@ struct TileLoader {
   // past the batch, so the pair may reach one row past kend).
   __device__ __forceinline__ void load_group_stats(int k0, int kend, int tid) {
     const int kb = min(k0 + kPer * (tid / kVPR), kend - 1);
-    if (kPer == 2) {
+    if constexpr (XF && kPer == 2) {
       const f32x4 rec = *reinterpret_cast<const f32x4*>(xrec + kb);
       xl[0] = rec[0];
       xy[0] = __float_as_int(rec[1]);
-      xl[kPer - 1] = rec[2];
-      xy[kPer - 1] = __float_as_int(rec[3]);
+      xl[1] = rec[2];
+      xy[1] = __float_as_int(rec[3]);
     } else {
       load_row_stats(0, kb);
     }
@@ -243,12 +243,11 @@ constexpr int f32_smem_floats() {
   return ab > st ? ab : st;
 }
 
-// One workgroup's work item: workgroup `wg` of `nwg` working on the GEMM `d`
-// (tiles in the XCD-aware band order of tile_coords), LDS at `smem`.
+// One output tile (K slice `split`, tile row tm, tile column tn) of the
+// GEMM `d`, LDS at `smem`.
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
-__device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, int tiles_n,
-                                              int a_vec, int b_vec, int out_vec, int wg, int nwg,
-                                              float* smem) {
+__device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int tm, int tn,
+                                              int a_vec, int b_vec, int out_vec, float* smem) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -263,9 +262,6 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, h = lane >> 5;
-
-  int split, tm, tn;
-  tile_coords_at(wg, nwg, tiles_m, tiles_n, split, tm, tn);
 
   const int M = d.M, N = d.N;
   const int kbeg = split * d.k_per_split;
@@ -495,12 +491,50 @@ __device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, in
   store_tile<float, BM, BN, WGM, WGN, EPI>(acc, smem, d, tm, tn, split, out_vec);
 }
 
+// Workgroup `wg` of `nwg` working on the GEMM `d`: its tile in the XCD-aware
+// band order of tile_coords.
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
+__device__ __forceinline__ void gemm_f32_body(const GemmDesc& d, int tiles_m, int tiles_n,
+                                              int a_vec, int b_vec, int out_vec, int wg, int nwg,
+                                              float* smem) {
+  int split, tm, tn;
+  tile_coords_at(wg, nwg, tiles_m, tiles_n, split, tm, tn);
+  gemm_f32_tile<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>(d, split, tm, tn, a_vec, b_vec,
+                                                           out_vec, smem);
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   __shared__ __attribute__((aligned(16))) float smem[f32_smem_floats<BM, BN, BK, WGM, WGN, ALAY, BLAY>()];
   gemm_f32_body<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>(d, tiles_m, tiles_n, a_vec, b_vec,
                                                            out_vec, blockIdx.x, gridDim.x, smem);
+}
+
+// Workgroups of the 128x128 tile one CU holds at once (LDS and registers).
+constexpr int kRowsPerCu = 2;
+
+// Long-K products with few tile columns (the classifier head's dX and dW,
+// K = 32000 and 65536 over N = 768): a grid the chip holds at once (a
+// multiple of 8 workgroups), each walking tiles.  Workgroup b runs on XCD
+// b % 8, and the workgroups of XCD x take, round after round, the tiles of
+// tile rows x, x + 8, x + 16, ... in row order, so the tiles of one row
+// (which read the same A rows over the whole K loop) run side by side on one
+// XCD and meet that operand in its L2.  In a grid of one workgroup per tile
+// they drift apart as workgroups of later dispatch rounds start whenever a
+// slot frees.  One K slice.
+template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
+__global__ void __launch_bounds__(WGM * WGN * 64, kRowsPerCu)
+gemm_f32_rows_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
+  __shared__ __attribute__((aligned(16))) float smem[f32_smem_floats<BM, BN, BK, WGM, WGN, ALAY, BLAY>()];
+  const int x = blockIdx.x & 7, per = gridDim.x >> 3;
+  for (int q = blockIdx.x >> 3;; q += per) {
+    const int tm = x + 8 * (q / tiles_n), tn = q % tiles_n;
+    if (tm >= tiles_m) break;
+    gemm_f32_tile<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>(d, 0, tm, tn, a_vec, b_vec, out_vec,
+                                                             smem);
+    __syncthreads();  // the epilogue's LDS reads before the next tile's stores
+  }
 }
 
 // Two small products in one launch (64x64 tiles of 4 waves for both):
@@ -559,6 +593,19 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   F32Job j;
   const hipError_t e = make_job<BM, BN>(d, j);
   if (e != hipSuccess) return e;
+  if constexpr (XF && BM == 128 && BN == 128) {
+    int dev = 0, cus = 0;
+    hipError_t e2 = hipGetDevice(&dev);
+    if (e2 == hipSuccess) e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e2 != hipSuccess) return e2;
+    const int64_t slots = (int64_t)kRowsPerCu * cus / 8 * 8;
+    if (d.splits == 1 && slots >= 8 && j.nwg > slots) {
+      hipLaunchKernelGGL((gemm_f32_rows_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>),
+                         dim3((unsigned)slots), dim3(WGM * WGN * 64), 0, s, d, j.tiles_m,
+                         j.tiles_n, j.a_vec, j.b_vec, j.out_vec);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>),
                      dim3((unsigned)j.nwg), dim3(WGM * WGN * 64), 0, s, d, j.tiles_m,
                      j.tiles_n, j.a_vec, j.b_vec, j.out_vec);
