@@ -468,8 +468,12 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
     if (masked && pass + 1 < PASSES)
       load_mask_pass<TO, BM, BN, WGM, WGN>(ms_next, d, tm, tn, pass + 1, out_vec);
 
-    const bool xent = EPI == EPI_FWD && d.xent_part != nullptr;
-    if (xent) {
+    // (the row statistics are reduced over lane groups of at most 32, so
+    // tiles of up to 128 columns write them; the launcher sends the fused
+    // head's forward to no wider tile)
+    constexpr bool kXent = EPI == EPI_FWD && CPR <= 32;
+    const bool xent = kXent && d.xent_part != nullptr;
+    if constexpr (kXent) if (xent) {
       // Logits and, for a fused softmax over many classes, each row's max
       // and sum of exp(z - max) over this tile's columns, from the same
       // float32 z = acc + bias the logits are stored as.  The CPR lanes
@@ -502,7 +506,8 @@ __device__ __forceinline__ void store_tile_impl(const f32x16 (&acc)[FM][FN],
         if ((tid % CPR) == 0 && row < M)
           *reinterpret_cast<f32x2*>(d.xent_part + 2 * ((int64_t)tn * M + row)) = f32x2{mx, se};
       }
-    } else if (nv > 0) {
+    }
+    if (!xent && nv > 0) {
 #pragma unroll
       for (int it = 0; it < RPT; ++it) {
         const int rl = tid / CPR + it * (NT / CPR);

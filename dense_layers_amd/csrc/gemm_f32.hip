@@ -511,12 +511,13 @@ gemm_f32_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int 
                                                            out_vec, blockIdx.x, gridDim.x, smem);
 }
 
-// Workgroups of the 128x128 tile one CU holds at once (LDS and registers).
-constexpr int kRowsPerCu = 2;
+// Waves per SIMD the walking grid is sized for (the tiles it runs fit two in
+// registers and LDS): two workgroups of 4 waves, or one of 8, per CU.
+constexpr int kRowsWaves = 2;
 
 // Long-K products with few tile columns (the classifier head's dX and dW,
 // K = 32000 and 65536 over N = 768): a grid the chip holds at once (a
-// multiple of 8 workgroups), each walking tiles.  Workgroup b runs on XCD
+// multiple of 8 workgroups, kRowsWaves waves per SIMD), each walking tiles.  Workgroup b runs on XCD
 // b % 8, and the workgroups of XCD x take, round after round, the tiles of
 // tile rows x, x + 8, x + 16, ... in row order, so the tiles of one row
 // (which read the same A rows over the whole K loop) run side by side on one
@@ -524,7 +525,7 @@ constexpr int kRowsPerCu = 2;
 // they drift apart as workgroups of later dispatch rounds start whenever a
 // slot frees.  One K slice.
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
-__global__ void __launch_bounds__(WGM * WGN * 64, kRowsPerCu)
+__global__ void __launch_bounds__(WGM * WGN * 64, kRowsWaves)
 gemm_f32_rows_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
   __shared__ __attribute__((aligned(16))) float smem[f32_smem_floats<BM, BN, BK, WGM, WGN, ALAY, BLAY>()];
   const int x = blockIdx.x & 7, per = gridDim.x >> 3;
@@ -588,17 +589,23 @@ hipError_t make_job(const GemmDesc& d, F32Job& j) {
   return hipSuccess;
 }
 
+hipError_t cu_count(int& cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return e;
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t s) {
   F32Job j;
   const hipError_t e = make_job<BM, BN>(d, j);
   if (e != hipSuccess) return e;
-  if constexpr (XF && BM == 128 && BN == 128) {
-    int dev = 0, cus = 0;
-    hipError_t e2 = hipGetDevice(&dev);
-    if (e2 == hipSuccess) e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if constexpr (XF && BM == 128 && (BN == 128 || BN == 256)) {
+    int cus = 0;
+    const hipError_t e2 = cu_count(cus);
     if (e2 != hipSuccess) return e2;
-    const int64_t slots = (int64_t)kRowsPerCu * cus / 8 * 8;
+    const int64_t slots = (int64_t)(kRowsWaves * 4 / (WGM * WGN)) * cus / 8 * 8;
     if (d.splits == 1 && slots >= 8 && j.nwg > slots) {
       hipLaunchKernelGGL((gemm_f32_rows_kernel<BM, BN, BK, WGM, WGN, ALAY, BLAY, EPI, XF>),
                          dim3((unsigned)slots), dim3(WGM * WGN * 64), 0, s, d, j.tiles_m,
@@ -635,15 +642,44 @@ hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Tile 0.  The forward (without the fused head's row statistics, which are
+// laid out per 128 columns) and dX products run on 128x256 tiles of 8 waves
+// of 64x64, one workgroup per CU, when every CU still gets two tiles: a
+// workgroup then stages 128 + 256 operand rows per K step where two 128x128
+// tiles stage 512, and the fused head's dX forms its loss gradient for half
+// as many tiles (the wide MLP's forwards 1.7% and its dX 1.5% faster, the
+// head's dX 2.5%).  Weight gradients and the rest stay on 128x128 tiles of 4
+// waves, two workgroups per CU (the 8-wave tile measured 2% slower for the
+// head's weight gradient).
+hipError_t launch_tile0(const GemmDesc& d, hipStream_t s) {
+  const bool fwd = d.epi == EPI_FWD && d.xent_part == nullptr && d.a_layout == K_MAJOR &&
+                   d.b_layout == K_MAJOR;
+  const bool dx = d.epi == EPI_DX && d.a_layout == K_MAJOR && d.b_layout == MN_MAJOR &&
+                  (d.xent_rows == nullptr || d.mask_act == ACT_IDENTITY);
+  if (fwd || dx) {
+    int cus = 0;
+    const hipError_t e = cu_count(cus);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (int64_t)((d.M + 127) / 128) * ((d.N + 255) / 256) * d.splits;
+    if (tiles >= 2 * (int64_t)cus) {
+      if (fwd) return launch_tile<128, 256, 16, 2, 4, K_MAJOR, K_MAJOR, EPI_FWD>(d, s);
+      if (d.xent_rows != nullptr)
+        return launch_tile<128, 256, 16, 2, 4, K_MAJOR, MN_MAJOR, EPI_DX, true>(d, s);
+      return launch_tile<128, 256, 16, 2, 4, K_MAJOR, MN_MAJOR, EPI_DX>(d, s);
+    }
+  }
+  return dispatch_layout<128, 128, 16, 2, 2>(d, s);
+}
+
 }  // namespace
 
-// tile 0: 128x128, K step 16 (4 waves of 64x64); tile 1: 64x64, K step 32
-// (4 waves of 32x32); tile 2: 64x128, K step 32 (8 waves of 32x32: one
-// workgroup loads 64 + 128 operand rows per K step where two 64x64 tiles
-// load 256)
+// tile 0: 128x128, K step 16 (4 waves of 64x64; 128x256 of 8 waves for
+// large forward and dX products); tile 1: 64x64, K step 32 (4 waves of
+// 32x32); tile 2: 64x128, K step 32 (8 waves of 32x32: one workgroup loads
+// 64 + 128 operand rows per K step where two 64x64 tiles load 256)
 hipError_t launch_gemm_f32(const GemmDesc& d, int tile, hipStream_t s) {
   switch (tile) {
-    case 0: return dispatch_layout<128, 128, 16, 2, 2>(d, s);
+    case 0: return launch_tile0(d, s);
     case 1: return dispatch_layout<64, 64, 32, 2, 2>(d, s);
     case 2: return dispatch_layout<64, 128, 32, 2, 4>(d, s);
     default: return hipErrorInvalidValue;

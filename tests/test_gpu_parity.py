@@ -37,9 +37,11 @@ def _layer(seed, B, n_in, n_out, bias=True):
 
 # ------------------------------------------------------------------ forward
 
+# (the last: 576 tiles of 128 x 256, ragged in K and N, so the forward runs
+# on the 8-wave tile)
 FWD_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (300, 1000, 129),
               (513, 256, 1000), (256, 1024, 4096), (8192, 128, 10), (33, 4100, 70),
-              (8200, 300, 250)]
+              (8200, 300, 250), (8192, 100, 2100)]
 
 
 @pytest.mark.parametrize("shape", FWD_SHAPES)
@@ -81,9 +83,11 @@ def test_dense_fwd_on_side_stream(dl):
 
 # ------------------------------------------------------------------ vjp
 
+# (the last: a dX of 576 tiles of 128 x 256, ragged in K and N, on the
+# 8-wave tile)
 VJP_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (8192, 784, 256),
               (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000), (700, 1000, 300),
-              (2000, 1000, 1000), (8200, 250, 300)]
+              (2000, 1000, 1000), (8200, 250, 300), (8192, 2100, 100)]
 
 
 @pytest.mark.parametrize("shape", VJP_SHAPES)
@@ -100,10 +104,12 @@ def test_dense_vjp_f32(dl, shape, act):
     assert_close(to_np(db), rdb, F32_TOL, "db")
 
 
+@pytest.mark.parametrize("shape", [(777, 300, 129), (8192, 2100, 100)])
 @pytest.mark.parametrize("dx_act", [O.ACT_RELU, O.ACT_GELU_TANH])
-def test_dense_vjp_folds_previous_activation(dl, dx_act):
-    """dX epilogue multiplies by the previous layer's act'(saved), in place."""
-    B, n_in, n_out = 777, 300, 129
+def test_dense_vjp_folds_previous_activation(dl, dx_act, shape):
+    """dX epilogue multiplies by the previous layer's act'(saved), in place
+    (also on the 8-wave 128 x 256 tile)."""
+    B, n_in, n_out = shape
     X, W, b = _layer(30, B, n_in, n_out)
     Zprev = si.random_matrix(31, (B, n_in))
     dY = si.random_matrix(32, (B, n_out))
