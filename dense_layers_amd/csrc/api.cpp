@@ -129,23 +129,24 @@ bool dim_ok(int64_t v) { return v > 0 && v <= 0x7fffffff; }
 
 // ---- GEMM planning ----------------------------------------------------------
 // float32 tiles {0: 128x128x16, 1: 64x64x32, 2: 64x128x32 with 8 waves}:
-// 128x128 when it alone yields at least one workgroup per CU (256); else, for
-// forward and dX products, 64x128 when that does; otherwise 64x64.
-// bf16 tiles {0: 256x256 (8 waves), 1: 128x128, 2: 256x256 (4 waves)} of the
-// direct-to-LDS kernel (K a multiple of 64): tile 0 for forward / dX products
-// with at least one such tile per CU, tile 2 for weight gradients with at
-// least 32 such tiles, 128x128 otherwise; operands that kernel cannot take
-// (unaligned, K not a multiple of 64) go to the general 128x128 kernel.  Only
-// the weight-gradient product (K = batch) is split along K, when it has fewer
+// tile 0 when it alone yields at least one workgroup per CU (256); else, for
+// forward and dX products, 64x128 when that does; otherwise 64x64.  (The
+// launcher runs large tile-0 forward and dX products on 128x256 tiles of 8
+// waves.)
+// 16-bit tiles {0: 256x256 of 8 waves, 1: 128x128} of the direct-to-LDS
+// kernel (K a multiple of 64) for forward and dX products: tile 0 with at
+// least one such tile per CU, 128x128 otherwise; weight gradients, and
+// operands the direct-load kernel cannot take (unaligned, K not a multiple
+// of 64), run on the register-staged 128x128 kernel.  Only the
+// weight-gradient product (K = batch) is split along K, when it has fewer
 // than two workgroups per CU, into a power-of-two number of slices (at most
 // 64, each keeping at least four K tiles): for 16-bit operands the smallest
-// count that gives at least four workgroups per CU (one for tile 2, whose LDS
-// admits one workgroup per CU: a single round, half the slices of two rounds
-// to write and add, measured 10 us faster per transformer-MLP step); for
-// float32 the largest count that keeps the
-// launch within one round of four workgroups per CU (fewer slices mean less
-// fixed cost per slice and a shorter sum over them in the optimizer, and a
-// second, partial round costs more than it hides).
+// count that gives at least two workgroups per CU (the transformer-MLP
+// block's weight gradients: 2 slices, 4 measured the same, none slower); for
+// float32 the largest count that keeps the launch within one round of four
+// workgroups per CU (fewer slices mean less fixed cost per slice and a
+// shorter sum over them in the optimizer, and a second, partial round costs
+// more than it hides).
 
 constexpr int kCUs = 256;
 
