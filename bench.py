@@ -629,7 +629,7 @@ WORKLOADS = {**si.WORKLOADS, **EXTRA_WORKLOADS}
 BENCHES = {"mlp_small": MLPBench, "mlp_adamw": MLPBench, "mlp_wide": MLPBench,
            "tmlp_bf16": TmlpBench, "head_xent": HeadBench, "opt_fused": OptBench,
            "mse": MseBench, "tmlp_f16": TmlpBench}
-DEFAULTS = {"mlp_small": (200, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
+DEFAULTS = {"mlp_small": (2000, 20), "mlp_adamw": (100, 10), "mlp_wide": (10, 2),
             "tmlp_bf16": (20, 3), "head_xent": (5, 1), "opt_fused": (50, 5), "mse": (50, 5),
             "tmlp_f16": (20, 3)}
 
