@@ -5,7 +5,10 @@
 // HBM-bound: 8 bytes read and 4 written per element.  Each workgroup adds
 // the squares of its units in float64 (differences formed in float64, exact
 // for float32 inputs) and leaves one partial; one workgroup adds the partials
-// in a fixed order, so the loss is bit-reproducible.
+// in a fixed order, so the loss is bit-reproducible.  The grid is two
+// workgroups per CU walking the units, and dpred is written with
+// non-temporal stores (nothing reads it back in this kernel): on [16384,
+// 4096] 141 us against 151 us with 8 workgroups per CU and plain stores.
 #include "common.hpp"
 
 namespace dl {
@@ -61,7 +64,8 @@ mse_kernel(int64_t n, const float* pred, const float* __restrict__ target, float
         acc += d * d;
       }
       if (dpred != nullptr)
-        *reinterpret_cast<f32x4*>(dpred + base + it * 1024) = (p[it] - t[it]) * two_over_n;
+        __builtin_nontemporal_store((p[it] - t[it]) * two_over_n,
+                                    reinterpret_cast<f32x4*>(dpred + base + it * 1024));
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -96,9 +100,12 @@ mse_finish_kernel(const double* __restrict__ part, int parts, int64_t n, float* 
 
 }  // namespace
 
+// Two workgroups per CU of the 256-CU chip.
+constexpr int kMseBlocks = 512;
+
 int mse_grid(int64_t n) {
   const int64_t units = (n + kStatUnit - 1) / kStatUnit;
-  return (int)(units < kStatBlocks ? units : kStatBlocks);
+  return (int)(units < kMseBlocks ? units : kMseBlocks);
 }
 
 hipError_t launch_mse(int64_t n, const float* pred, const float* target, float* dpred,
