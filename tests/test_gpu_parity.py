@@ -425,10 +425,11 @@ def test_validate_mode_in_the_mlp_step(dl):
 # 32000-class head on 1000 rows; a batch whose weight gradient is split
 # along K; the degenerate single-class and single-row heads; and a dX (576
 # tiles) and a weight gradient (585 tiles, ragged in classes and batch) with
-# more tiles than the chip holds at once, which walk tile rows per XCD.
+# more tiles than the chip holds at once, which walk tile rows per XCD; and
+# a dX on 516 ragged 128 x 256 tiles of 8 waves, also walking tile rows.
 XENT_HEAD_SHAPES = [(300, 96, 1000), (257, 64, 2049), (1000, 768, 32000), (64, 33, 130),
                     (8192, 96, 1000), (5, 16, 3), (1, 8, 1), (77, 40, 1),
-                    (8192, 1152, 1000), (520, 1152, 8200)]
+                    (8192, 1152, 1000), (520, 1152, 8200), (16461, 1000, 300)]
 
 
 @pytest.mark.parametrize("shape", XENT_HEAD_SHAPES, ids=lambda s: "x".join(map(str, s)))
