@@ -517,13 +517,13 @@ constexpr int kRowsWaves = 2;
 
 // Long-K products with few tile columns (the classifier head's dX and dW,
 // K = 32000 and 65536 over N = 768): a grid the chip holds at once (a
-// multiple of 8 workgroups, kRowsWaves waves per SIMD), each walking tiles.  Workgroup b runs on XCD
-// b % 8, and the workgroups of XCD x take, round after round, the tiles of
-// tile rows x, x + 8, x + 16, ... in row order, so the tiles of one row
-// (which read the same A rows over the whole K loop) run side by side on one
-// XCD and meet that operand in its L2.  In a grid of one workgroup per tile
-// they drift apart as workgroups of later dispatch rounds start whenever a
-// slot frees.  One K slice.
+// multiple of 8 workgroups, kRowsWaves waves per SIMD), each walking tiles.
+// Workgroup b runs on XCD b % 8, and the workgroups of XCD x take, round
+// after round, the tiles of tile rows x, x + 8, x + 16, ... in row order, so
+// the tiles of one row (which read the same A rows over the whole K loop)
+// run side by side on one XCD and meet that operand in its L2.  In a grid of
+// one workgroup per tile they drift apart as workgroups of later dispatch
+// rounds start whenever a slot frees.  One K slice.
 template <int BM, int BN, int BK, int WGM, int WGN, int ALAY, int BLAY, int EPI, bool XF = false>
 __global__ void __launch_bounds__(WGM * WGN * 64, kRowsWaves)
 gemm_f32_rows_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int out_vec) {
