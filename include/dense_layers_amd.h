@@ -306,7 +306,8 @@ int softmax_xent_fwd_bwd_noalloc(void* stream, int64_t B, int64_t C,
  *   out of bounds); logits device [B, C] output; lse device [B] output;
  *   loss device [1] output (mean over the batch); row_loss device [B]
  *   output or NULL.  ws: dense_xent_fwd_workspace_size(B, in, C) bytes
- *   (the per-tile pairs, 8 B per row per 128 classes, and the row losses).
+ *   (the per-tile pairs, 8 B per row and column tile of 128 classes, or of
+ *   64 for small problems, and the row losses).
  *   No output may overlap an input or another output.
  *
  * dense_xent_vjp: with g = (exp(z - lse) - onehot(y)) / B formed from the
