@@ -312,3 +312,20 @@ def test_lse_band_without_lse_deviation_caught(monkeypatch):
 
     monkeypatch.setattr(O, "xent_grad_band", no_lambda)
     _expect_pin_failure(PB.test_xent_grad_band_lse_form_is_tight)
+
+
+def test_xent_band_nan_row_escaping_the_cap_caught(monkeypatch):
+    """A row whose sum bound overflows (0 times inf: NaN) left out of the cap,
+    as an `eps_s >= 1` test alone would leave it."""
+    real = RB.xent_grad_band
+
+    def uncapped(z, tau, B, scale=1.0, labels=None, form="softmax"):
+        band = real(z, tau, B, scale, labels, form)
+        t = np.asarray(tau, np.float64)
+        with np.errstate(over="ignore"):
+            over = ~np.isfinite(np.exp(t + t.max(axis=1, keepdims=True))).all(axis=1)
+        band[over] = np.nan
+        return band
+
+    monkeypatch.setattr(O, "xent_grad_band", uncapped)
+    _expect_pin_failure(PB.test_xent_grad_band_caps_rows_whose_bound_overflows)
