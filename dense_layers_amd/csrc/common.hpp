@@ -778,9 +778,10 @@ constexpr int kOptElemsPerBlock = kOptBlock * 4 * 4;  // 4 float4 per thread
 constexpr int kOptSplitElemsPerBlock = kOptBlock;      // split-K segments: 4 lanes per 4 elements
 constexpr int kOptWideSplits = 32;                     // more slices: a wave per 4 elements
 constexpr int kOptWideElemsPerBlock = kOptBlock / 16;
+constexpr int kOptFewSplits = 4;                       // up to 4 slices: a thread per 4 elements
 inline int64_t opt_elems_per_block(int splits) {
   return splits > kOptWideSplits ? kOptWideElemsPerBlock
-                                 : (splits > 1 ? kOptSplitElemsPerBlock : kOptElemsPerBlock);
+                                 : (splits > kOptFewSplits ? kOptSplitElemsPerBlock : kOptElemsPerBlock);
 }
 hipError_t launch_opt_multi(const OptSegs& segs, int kind, const OptConsts& c,
                             hipStream_t s);

@@ -167,10 +167,11 @@ opt_single_kernel(int64_t n, float* w, const float* g, float* m, float* v, AdamP
                          Extras{nullptr, nullptr}, 1.f, p, vec);
 }
 
-// Split-K segments: the slices are summed by 4 lanes per 4-element group,
-// lane q taking slices q, q+4, q+8, ... in order, then the 4 partial sums are
-// combined in a fixed tree ((p0 + p1) + (p2 + p3)) with lane shuffles, so a
-// thread walks a quarter of the slices and the result is bit-reproducible.
+// Split-K segments of 5 to 32 slices: the slices are summed by 4 lanes per
+// 4-element group, lane q taking slices q, q+4, q+8, ... in order, then the
+// 4 partial sums are combined in a fixed tree ((p0 + p1) + (p2 + p3)) with
+// lane shuffles, so a thread walks a quarter of the slices and the result is
+// bit-reproducible.  (Up to 4 slices: opt_few_split_block, the same sums.)
 constexpr int kSplitElemsPerBlock = kOptSplitElemsPerBlock;  // one 4-element group per 4 lanes
 
 template <int KIND, bool EXT>
@@ -205,6 +206,74 @@ __device__ __forceinline__ void opt_split_block(int64_t n, int64_t base, float* 
   const float gi = g[q];
   gs.out[i] = gi;
   update_one<KIND, EXT>(i, gi, w, m, v, x, p);
+}
+
+// Segments of 2 to 4 slices: one thread per 4-element group, four groups a
+// thread as in opt_block, each slice of a group one float4 load (a missing
+// slice reads slice 0 and counts as zero), all loads in flight together.
+// The sum (s0 + s1) + (s2 + s3) is the 4-lane tree of opt_split_block when
+// each lane holds one slice, so both forms give the same bits.
+template <int KIND, bool EXT>
+__device__ __forceinline__ void opt_few_split_block(int64_t n, int64_t base, float* __restrict__ w,
+                                                    const GradSrc& gs, float* __restrict__ m,
+                                                    float* __restrict__ v, const Extras& x,
+                                                    const AdamParams& p, bool vec) {
+  const int64_t end = min(n, base + (int64_t)kOptElemsPerBlock);
+  if (vec && end - base == kOptElemsPerBlock) {
+    f32x4 wv[4], mv[4], vv[4], ev[4], sv[4][4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int kk = k < gs.splits ? k : 0;
+        sv[it][k] = *reinterpret_cast<const f32x4*>(gs.part + (int64_t)kk * gs.stride + i);
+      }
+      wv[it] = *reinterpret_cast<const f32x4*>(w + i);
+      if (KIND != OPT_SGD) {
+        mv[it] = *reinterpret_cast<const f32x4*>(m + i);
+        vv[it] = *reinterpret_cast<const f32x4*>(v + i);
+      }
+      if (EXT && x.e != nullptr) ev[it] = *reinterpret_cast<const f32x4*>(x.e + i);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 s2 = gs.splits > 2 ? sv[it][2] : zero;
+      const f32x4 s3 = gs.splits > 3 ? sv[it][3] : zero;
+      const f32x4 gv = (sv[it][0] + sv[it][1]) + (s2 + s3);
+      *reinterpret_cast<f32x4*>(gs.out + i) = gv;
+      if (KIND == OPT_SGD) {
+        wv[it] -= p.lr * gv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float we = wv[it][e], me = mv[it][e], ve = vv[it][e];
+          update_elem<KIND>(we, gv[e], me, ve, p);
+          wv[it][e] = we; mv[it][e] = me; vv[it][e] = ve;
+        }
+        *reinterpret_cast<f32x4*>(m + i) = mv[it];
+        *reinterpret_cast<f32x4*>(v + i) = vv[it];
+      }
+      *reinterpret_cast<f32x4*>(w + i) = wv[it];
+      if (EXT && x.e != nullptr)
+        *reinterpret_cast<f32x4*>(x.e + i) = p.ema_d * ev[it] + p.ema_omd * wv[it];
+      if (EXT && x.wb != nullptr) {
+        const u32x2v h = {pack_bf16x2(wv[it][0], wv[it][1]), pack_bf16x2(wv[it][2], wv[it][3])};
+        *reinterpret_cast<u32x2v*>(x.wb + i) = h;
+      }
+    }
+  } else {
+    for (int64_t i = base + threadIdx.x; i < end; i += kOptBlock) {
+      float s[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s[k] = k < gs.splits ? gs.part[(int64_t)k * gs.stride + i] : 0.f;
+      const float gi = (s[0] + s[1]) + (s[2] + s[3]);
+      gs.out[i] = gi;
+      update_one<KIND, EXT>(i, gi, w, m, v, x, p);
+    }
+  }
 }
 
 // Segments with many slices (more than kOptWideSplits): a whole wave per
@@ -296,7 +365,15 @@ opt_multi_kernel(OptSegs segs, AdamParams p) {
     if (gs.splits > kOptWideSplits)
       opt_wide_split_block<KIND, EXT>(segs.n[s], local * kOptWideElemsPerBlock, segs.w[s], gs,
                                       segs.m[s], segs.v[s], x, p, vec);
-    else
+    else if (gs.splits <= kOptFewSplits) {
+      uintptr_t addr = reinterpret_cast<uintptr_t>(segs.w[s]) | reinterpret_cast<uintptr_t>(gs.out);
+      if (KIND != OPT_SGD)
+        addr |= reinterpret_cast<uintptr_t>(segs.m[s]) | reinterpret_cast<uintptr_t>(segs.v[s]);
+      addr |= reinterpret_cast<uintptr_t>(x.e);
+      const bool vec4 = vec && (addr & 15) == 0 && (reinterpret_cast<uintptr_t>(x.wb) & 7) == 0;
+      opt_few_split_block<KIND, EXT>(segs.n[s], local * kOptElemsPerBlock, segs.w[s], gs,
+                                     segs.m[s], segs.v[s], x, p, vec4);
+    } else
       opt_split_block<KIND, EXT>(segs.n[s], local * kSplitElemsPerBlock, segs.w[s], gs,
                                  segs.m[s], segs.v[s], x, p, vec);
     return;
