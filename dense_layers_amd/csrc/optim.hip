@@ -239,10 +239,11 @@ __device__ __forceinline__ void opt_few_split_block(int64_t n, int64_t base, flo
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int64_t i = base + ((int64_t)it * kOptBlock + threadIdx.x) * 4;
+      // each lane's partial starts from +0 as in the 4-lane tree
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 s2 = gs.splits > 2 ? sv[it][2] : zero;
-      const f32x4 s3 = gs.splits > 3 ? sv[it][3] : zero;
-      const f32x4 gv = (sv[it][0] + sv[it][1]) + (s2 + s3);
+      const f32x4 s2 = gs.splits > 2 ? zero + sv[it][2] : zero;
+      const f32x4 s3 = gs.splits > 3 ? zero + sv[it][3] : zero;
+      const f32x4 gv = ((zero + sv[it][0]) + (zero + sv[it][1])) + (s2 + s3);
       *reinterpret_cast<f32x4*>(gs.out + i) = gv;
       if (KIND == OPT_SGD) {
         wv[it] -= p.lr * gv;
@@ -268,7 +269,7 @@ __device__ __forceinline__ void opt_few_split_block(int64_t n, int64_t base, flo
     for (int64_t i = base + threadIdx.x; i < end; i += kOptBlock) {
       float s[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s[k] = k < gs.splits ? gs.part[(int64_t)k * gs.stride + i] : 0.f;
+      for (int k = 0; k < 4; ++k) s[k] = k < gs.splits ? 0.f + gs.part[(int64_t)k * gs.stride + i] : 0.f;
       const float gi = (s[0] + s[1]) + (s[2] + s[3]);
       gs.out[i] = gi;
       update_one<KIND, EXT>(i, gi, w, m, v, x, p);
