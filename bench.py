@@ -11,7 +11,8 @@ block, and the optimizer / loss variants) are measured the same way.
 Prints one JSON line: whole-step throughput (train steps/s), the step's
 algorithmic GEMM TFLOP/s, the time of every launch inside the step (a short
 pass with the library's per-launch HIP-event timing on the launch stream), a
-roofline entry for the dominant launch, and the float64 CPU oracle timed on a
+roofline entry for the dominant launch, the vendor GEMM (torch.mm) timed at
+that launch's shape as context, and the float64 CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -220,6 +221,19 @@ class MLPBench:
             return None
         return "flop", 2 * B * w.dims[l] * w.dims[l + 1]
 
+    def gemm_shape(self, label):
+        """(M, N, K) of a launch that is one plain GEMM, else None."""
+        w = self.w
+        name, k = _split(label)
+        if name == "fwd_gemm":
+            return w.batch, w.dims[k + 1], w.dims[k]
+        if name in ("dw_gemm", "dx_gemm"):
+            l = self._layers_of_labels()[label]
+            if name == "dw_gemm":
+                return w.dims[l + 1], w.dims[l], w.batch
+            return w.batch, w.dims[l], w.dims[l + 1]
+        return None
+
     def stage_bytes(self, label):
         """Algorithmic bytes of a GEMM launch of the step (for the traffic
         ratio of the roofline entry), or None."""
@@ -329,6 +343,19 @@ class TmlpBench:
             return "flop", 2 * T * d * f
         if name in ("cast_bf16_t", "cast_f16_t"):
             return "byte", 8 * d * f
+        return None
+
+    def gemm_shape(self, label):
+        """(M, N, K) of a launch that is one plain GEMM, else None (launch
+        order as in stage_bytes)."""
+        T, d, f = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, k = _split(label)
+        if name == "fwd_gemm":
+            return (T, f, d) if k == 0 else (T, d, f)
+        if name == "dw_gemm":
+            return (d, f, T) if k == 0 else (f, d, T)
+        if name == "dx_gemm":
+            return (T, f, d) if k == 0 else (T, d, f)
         return None
 
     def stage_bytes(self, label):
@@ -444,6 +471,18 @@ class HeadBench:
             return "byte", 8 * self._tiles() * B + 16 * B
         if name == "adamw":
             return "byte", 28 * (C * d if k == 0 else C)
+        return None
+
+    def gemm_shape(self, label):
+        """(M, N, K) of a launch that is one GEMM, else None."""
+        B, d, C = self.w.batch, self.w.dims[0], self.w.dims[1]
+        name, _ = _split(label)
+        if name in ("fwd_gemm", "xent_fwd_gemm"):
+            return B, C, d
+        if name in ("dw_gemm", "xent_dw_gemm"):
+            return C, d, B
+        if name in ("dx_gemm", "xent_dx_gemm"):
+            return B, d, C
         return None
 
     def stage_bytes(self, label):
@@ -707,6 +746,42 @@ def profile_stages(dl, bench, n_steps):
     return stages
 
 
+def vendor_context(bench, dom, dtype, dev):
+    """The vendor GEMM (torch.mm, hipBLASLt; TF32 off) at the dominant
+    launch's shape, A [M, K] times B [K, N] both row-major: timing context
+    beside the roofline line, never part of the measured path.  None when
+    the launch is not one plain GEMM."""
+    shape = bench.gemm_shape(dom["stage"]) if hasattr(bench, "gemm_shape") else None
+    if shape is None:
+        return None
+    import torch
+    M, N, K = (int(v) for v in shape)
+    td = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    prev = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    try:
+        g = torch.Generator(device=dev).manual_seed(7)
+        a = torch.randn(M, K, device=dev, dtype=torch.float32, generator=g).to(td)
+        b = torch.randn(K, N, device=dev, dtype=torch.float32, generator=g).to(td)
+        for _ in range(2):
+            torch.mm(a, b)
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = prev
+    del a, b
+    torch.cuda.empty_cache()
+    return {"kernel": dom["stage"], "shape_mnk": [M, N, K], "dtype": dtype,
+            "torch_mm_ms": round(ms, 5), "torch_mm_tflops": round(2 * M * N * K / (ms * 1e-3) / 1e12, 3),
+            "this_kernel_ms": dom["ms"]}
+
+
 def measure_launch_floor(dl, dev, stream, launches):
     """Time of one empty-kernel launch back to back on the stream (HIP events
     and wall clock over 2000 launches) and that times the step's launches."""
@@ -746,6 +821,8 @@ def main():
                          "forward / cross-entropy / vjp")
     ap.add_argument("--no-launch-floor", action="store_true",
                     help="skip the empty-kernel launch-floor measurement")
+    ap.add_argument("--no-vendor-context", action="store_true",
+                    help="skip timing torch.mm at the dominant launch's shape")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
@@ -839,6 +916,10 @@ def main():
     if not args.no_launch_floor:
         launch_floor = measure_launch_floor(dl, dev, stream, len(stages))
 
+    vendor = None
+    if not args.no_vendor_context:
+        vendor = vendor_context(bench, dom, w.dtype, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_budget)
@@ -867,6 +948,7 @@ def main():
                    **({"head_path": args.head_path} if isinstance(bench, HeadBench) else {})},
         "roofline": roofline,
         "launch_floor": launch_floor,
+        "vendor_context": vendor,
         "stages": stages,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
