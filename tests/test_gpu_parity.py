@@ -37,11 +37,12 @@ def _layer(seed, B, n_in, n_out, bias=True):
 
 # ------------------------------------------------------------------ forward
 
-# (the last: 576 tiles of 128 x 256, ragged in K and N, so the forward runs
-# on the 8-wave tile)
+# (the last two: 576 tiles of 128 x 256, ragged in K and N, so the forward
+# runs on the 8-wave tile; with N = 2101 its rows take the bounds-checked
+# stores)
 FWD_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (300, 1000, 129),
               (513, 256, 1000), (256, 1024, 4096), (8192, 128, 10), (33, 4100, 70),
-              (8200, 300, 250), (8192, 100, 2100)]
+              (8200, 300, 250), (8192, 100, 2100), (8192, 100, 2101)]
 
 
 @pytest.mark.parametrize("shape", FWD_SHAPES)
@@ -83,11 +84,12 @@ def test_dense_fwd_on_side_stream(dl):
 
 # ------------------------------------------------------------------ vjp
 
-# (the last: a dX of 576 tiles of 128 x 256, ragged in K and N, on the
-# 8-wave tile)
+# (the last two: a dX of 576 tiles of 128 x 256, ragged in K and N, on the
+# 8-wave tile; with in = 2101 its weight operand takes the bounds-checked
+# loads)
 VJP_SHAPES = [(1, 1, 1), (7, 10, 33), (129, 127, 65), (64, 784, 256), (8192, 784, 256),
               (8192, 128, 10), (1000, 300, 513), (4096, 1024, 1000), (700, 1000, 300),
-              (2000, 1000, 1000), (8200, 250, 300), (8192, 2100, 100)]
+              (2000, 1000, 1000), (8200, 250, 300), (8192, 2100, 100), (8192, 2101, 100)]
 
 
 @pytest.mark.parametrize("shape", VJP_SHAPES)
