@@ -13,8 +13,8 @@
 // wave owns a (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks whose
 // accumulators stay in registers for the whole K loop.  Operand tiles go
 // global -> registers -> LDS (double-buffered, one barrier per K step); the
-// next tile's global loads are issued before the current tile's MFMAs so
-// their latency hides behind the matrix work.  LDS keeps the global layout
+// global loads of the K step two ahead are issued before the current step's
+// MFMAs so their latency hides behind the matrix work.  LDS keeps the global layout
 // (no transpose on the store side); fragments are read as one 16-byte load
 // (K-major) or four 4-byte loads (M/N-major).
 //
