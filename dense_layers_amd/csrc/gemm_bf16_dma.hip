@@ -203,21 +203,41 @@ __device__ __forceinline__ BlockPos block_pos(int tm, int tn, int wm, int wn, in
   return {tm * BM + wm * WM + i * 32 + (lane & 31), tn * BN + wn * WN + j * 32 + 16 * (lane >> 5)};
 }
 
+// Edge handling in the epilogue.  `full` (the same for the whole wave):
+// every column of the wave's sub-tile is inside the matrix and the output
+// allows 16-byte accesses, so no lane needs a per-element path.  It is
+// tested first, as a branch of the whole wave.  On the other side the count
+// of valid columns passes through an empty asm statement, which the
+// compiler may not move or compute ahead of its branch: otherwise it
+// evaluates the per-element column tests of every block in the common code
+// and keeps them live in scalar registers, spilled, across the epilogue.
+__device__ __forceinline__ int cols_left(int n) {
+  asm volatile("" : "+v"(n));
+  return n;
+}
+
 // The 16 saved bf16 activations at a lane's block position (zeros outside
 // the matrix), as they are stored.
 __device__ __forceinline__ void load_mask16(u32x4 (&m)[2], const bf16_t* __restrict__ src,
-                                            int64_t ld, BlockPos p, int M, int N, bool vec) {
+                                            int64_t ld, BlockPos p, int M, int N, bool vec,
+                                            bool full) {
   m[0] = u32x4{0u, 0u, 0u, 0u};
   m[1] = m[0];
   if (p.row >= M) return;
   const bf16_t* q = src + (int64_t)p.row * ld + p.col;
-  if (vec && p.col + 16 <= N) {
+  if (full) {
+    m[0] = *reinterpret_cast<const u32x4*>(q);
+    m[1] = *reinterpret_cast<const u32x4*>(q + 8);
+    return;
+  }
+  const int lim = cols_left(N - p.col);
+  if (vec && lim >= 16) {
     m[0] = *reinterpret_cast<const u32x4*>(q);
     m[1] = *reinterpret_cast<const u32x4*>(q + 8);
   } else {
 #pragma unroll
     for (int c = 0; c < 16; ++c)
-      if (p.col + c < N) m[c >> 3][(c >> 1) & 3] |= (uint32_t)q[c] << (16 * (c & 1));
+      if (c < lim) m[c >> 3][(c >> 1) & 3] |= (uint32_t)q[c] << (16 * (c & 1));
   }
 }
 template <int HK>
@@ -262,23 +282,35 @@ __device__ __forceinline__ void region_put(char* region, int r, int j, int h, co
 // col0 + WN - 1 (clipped to M x N), one 16-byte piece per lane per step.
 template <typename TO, int WN, int ROWS>
 __device__ __forceinline__ void region_flush(const char* region, TO* __restrict__ out, int64_t ld,
-                                             int row0, int col0, int M, int N, bool vec, int lane) {
+                                             int row0, int col0, int M, int N, bool vec, bool full,
+                                             int lane) {
   constexpr int ES = sizeof(TO), PPR = WN * ES / 16, EPP = 16 / ES, RPS = 64 / PPR;
   const int p = lane % PPR;
   const int col = col0 + p * EPP;
+  if (full) {  // all columns inside: rows tested alone
+#pragma unroll
+    for (int t = 0; t < ROWS / RPS; ++t) {
+      const int r = t * RPS + lane / PPR;
+      const u32x4 x =
+          *reinterpret_cast<const u32x4*>(region + r * (WN * ES) + ((p ^ (r % PPR)) * 16));
+      if (row0 + r < M) *reinterpret_cast<u32x4*>(out + (int64_t)(row0 + r) * ld + col) = x;
+    }
+    return;
+  }
+  const int lim = cols_left(N - col);
 #pragma unroll
   for (int t = 0; t < ROWS / RPS; ++t) {
     const int r = t * RPS + lane / PPR;
     const u32x4 x = *reinterpret_cast<const u32x4*>(region + r * (WN * ES) + ((p ^ (r % PPR)) * 16));
     const int row = row0 + r;
-    if (row >= M || col >= N) continue;
+    if (row >= M || lim <= 0) continue;
     TO* q = out + (int64_t)row * ld + col;
-    if (vec && col + EPP <= N) {
+    if (vec && lim >= EPP) {
       *reinterpret_cast<u32x4*>(q) = x;
     } else {
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
-        if (col + e >= N) break;
+        if (e >= lim) break;
         if constexpr (ES == 2) q[e] = (bf16_t)(x[e >> 1] >> (16 * (e & 1)));
         else q[e] = __uint_as_float(x[e]);
       }
@@ -325,6 +357,8 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
     ld = N;
   }
   const int row0 = tm * BM + wm * WM, col0 = tn * BN + wn * WN;
+  // the same for every lane of the wave (tm, tn, wm, wn and the flags are)
+  const bool full = vec && col0 + WN <= N;
 
   float bias[FN][16];
 #pragma unroll
@@ -332,20 +366,29 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
 #pragma unroll
     for (int c = 0; c < 16; ++c) bias[j][c] = 0.f;
   if (EPI == EPI_FWD && d.bias != nullptr) {
+    const bool bias_vec = (reinterpret_cast<uintptr_t>(d.bias) & 15) == 0;
+    auto bias16 = [&](int j, int col) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(d.bias + col + 4 * k);
+        bias[j][4 * k] = x[0]; bias[j][4 * k + 1] = x[1];
+        bias[j][4 * k + 2] = x[2]; bias[j][4 * k + 3] = x[3];
+      }
+    };
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = col0 + 32 * j + 16 * h;
-      if (vec && col + 16 <= N && (reinterpret_cast<uintptr_t>(d.bias) & 15) == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(d.bias + col + 4 * k);
-          bias[j][4 * k] = x[0]; bias[j][4 * k + 1] = x[1];
-          bias[j][4 * k + 2] = x[2]; bias[j][4 * k + 3] = x[3];
-        }
+      if (full && bias_vec) {
+        bias16(j, col);
       } else {
+        const int lim = cols_left(N - col);
+        if (vec && lim >= 16 && bias_vec) {
+          bias16(j, col);
+        } else {
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (col + c < N) bias[j][c] = d.bias[col + c];
+          for (int c = 0; c < 16; ++c)
+            if (c < lim) bias[j][c] = d.bias[col + c];
+        }
       }
     }
   }
@@ -360,7 +403,8 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         load_mask16(mk[ii * FN + j], static_cast<const bf16_t*>(d.mask_src), d.ldc,
-                    block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, i0 + ii, j, lane), M, N, vec);
+                    block_pos<BM, BN, WGM, WGN>(tm, tn, wm, wn, i0 + ii, j, lane), M, N, vec,
+                    full);
   };
   if constexpr (kMasked) load_masks(0);
 #pragma unroll
@@ -394,10 +438,10 @@ __device__ __forceinline__ void store_epilogue(const f32x16 (&acc)[FM][FN], cons
       if (i0 + IR < FM) load_masks(i0 + IR);
     }
     wave_lds_order();
-    region_flush<TO, WN, IR * 32>(region, out, ld, row0 + i0 * 32, col0, M, N, vec, lane);
+    region_flush<TO, WN, IR * 32>(region, out, ld, row0 + i0 * 32, col0, M, N, vec, full, lane);
     if constexpr (kZ)
       region_flush<TO, WN, IR * 32>(region + kOutBytes, zout, ld, row0 + i0 * 32, col0, M, N, vec,
-                                    lane);
+                                    full, lane);
     wave_lds_order();
   }
 }
