@@ -50,28 +50,47 @@ struct TileLoaderBf16 {
 
   u32x4 r[kRegs];
 
-  // Full K step, 16-byte aligned rows: plain vector loads with no
-  // per-element control flow, so the loads of a K step stay in flight
-  // together.  Rows past the end (edge tiles) are clamped to a valid row:
-  // they only feed output rows / columns that are never stored.  For an
-  // M/N-major operand this needs nrows % 8 == 0 so that no vector straddles
-  // the end (checked by the caller).
-  __device__ __forceinline__ void load_fast(const bf16_t* __restrict__ base, int64_t ld, int row0,
-                                            int nrows, int k0, int tid) {
+  // The per-thread part of the full K steps' load addresses, fixed for a
+  // tile: item i's row and 16-byte unit at k = 0 (K-major), or its first k
+  // row and m (M/N-major).  A K step then adds k0, or k0 ld and j ld for the
+  // rows of a block, which the whole workgroup shares, instead of forming
+  // each address's 64-bit product again.  Rows past the end (edge tiles) are
+  // clamped to a valid row: they only feed output rows / columns that are
+  // never stored.  For an M/N-major operand this needs nrows % 8 == 0 so that
+  // no vector straddles the end (checked by the caller).
+  struct Origin {
+    const bf16_t* p[kPer];
+  };
+  __device__ __forceinline__ static Origin origin(const bf16_t* __restrict__ base, int64_t ld,
+                                                  int row0, int nrows, int tid) {
+    Origin o;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int q = tid + i * NT;
       if (LAY == K_MAJOR) {
         const int row = min(row0 + q / (BK / 8), nrows - 1);
-        const int k = k0 + (q % (BK / 8)) * 8;
-        r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + k);
+        o.p[i] = base + (int64_t)row * ld + (q % (BK / 8)) * 8;
       } else {
         int m = row0 + (q % (ROWS / 8)) * 8;
         m = m < nrows ? m : 0;
-        const int kq = q / (ROWS / 8);
+        o.p[i] = base + (int64_t)(q / (ROWS / 8) * 4) * ld + m;
+      }
+    }
+    return o;
+  }
+
+  // Full K step, 16-byte aligned rows: plain vector loads with no
+  // per-element control flow, so the loads of a K step stay in flight
+  // together.
+  __device__ __forceinline__ void load_fast(const Origin& o, int64_t ld, int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          r[i * 4 + j] = *reinterpret_cast<const u32x4*>(base + (int64_t)(k0 + kq * 4 + j) * ld + m);
+    for (int i = 0; i < kPer; ++i) {
+      if (LAY == K_MAJOR) {
+        r[i] = *reinterpret_cast<const u32x4*>(o.p[i] + k0);
+      } else {
+        const bf16_t* q = o.p[i] + (int64_t)k0 * ld;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[i * 4 + j] = *reinterpret_cast<const u32x4*>(q + j * ld);
       }
     }
   }
@@ -240,10 +259,12 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
   // set 2 holds step kt + 1 in flight.
   LA la2;
   LB lb2;
+  const typename LA::Origin oa = LA::origin(A, d.lda, tm * BM, M, tid);
+  const typename LB::Origin ob = LB::origin(B, d.ldb, tn * BN, N, tid);
   if (nk > 0) {
     if (nk_full > 0) {
-      la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
-      lb.load_fast(B, d.ldb, tn * BN, N, kbeg, tid);
+      la.load_fast(oa, d.lda, kbeg);
+      lb.load_fast(ob, d.ldb, kbeg);
     } else {
       la.load_safe(A, d.lda, tm * BM, M, kbeg, kend, tid);
       lb.load_safe(B, d.ldb, tn * BN, N, kbeg, kend, tid);
@@ -251,16 +272,16 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
     la.store(As(0), tid);
     lb.store(Bs(0), tid);
     if (nk_full >= 2) {
-      la2.load_fast(A, d.lda, tm * BM, M, kbeg + BK, tid);
-      lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + BK, tid);
+      la2.load_fast(oa, d.lda, kbeg + BK);
+      lb2.load_fast(ob, d.ldb, kbeg + BK);
     }
   }
   __syncthreads();
 
   int kt = 0;
   for (; kt + 3 < nk_full; kt += 2) {
-    la.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 2) * BK, tid);
-    lb.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 2) * BK, tid);
+    la.load_fast(oa, d.lda, kbeg + (kt + 2) * BK);
+    lb.load_fast(ob, d.ldb, kbeg + (kt + 2) * BK);
     // keep the loads ahead of the MFMAs (the scheduler would otherwise sink
     // them next to their LDS stores)
     __builtin_amdgcn_sched_barrier(0);
@@ -269,8 +290,8 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
     la2.store(As(1), tid);
     lb2.store(Bs(1), tid);
     __syncthreads();
-    la2.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 3) * BK, tid);
-    lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 3) * BK, tid);
+    la2.load_fast(oa, d.lda, kbeg + (kt + 3) * BK);
+    lb2.load_fast(ob, d.ldb, kbeg + (kt + 3) * BK);
     __builtin_amdgcn_sched_barrier(0);
     compute(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -290,8 +311,8 @@ gemm_bf16_kernel(GemmDesc d, int tiles_m, int tiles_n, int a_vec, int b_vec, int
   for (; kt + 1 < nk_full; ++kt) {
     const int cur = kt & 1;
     const int k0 = kbeg + (kt + 1) * BK;
-    la.load_fast(A, d.lda, tm * BM, M, k0, tid);
-    lb.load_fast(B, d.ldb, tn * BN, N, k0, tid);
+    la.load_fast(oa, d.lda, k0);
+    lb.load_fast(ob, d.ldb, k0);
     __builtin_amdgcn_sched_barrier(0);
     compute(cur);
     __builtin_amdgcn_sched_barrier(0);

@@ -112,12 +112,55 @@ struct TileLoader {
     }
   }
 
+  // The per-thread part of the full K steps' load addresses, fixed for a
+  // tile: vector i's row and k offset at k = 0 (K-major), or its k row and
+  // first tile row (M/N-major).  A K step then adds k0, or k0 ld, which the
+  // whole workgroup shares, instead of forming each address's 64-bit
+  // product again.  Rows past the end (edge tiles) are clamped to a valid
+  // row: they only feed output rows / columns that are never stored.  For
+  // an M/N-major operand this needs nrows % 4 == 0 so that no vector
+  // straddles the end (checked by the caller).
+  struct Origin {
+    const float* p[kPer];
+  };
+  __device__ __forceinline__ static Origin origin(const float* __restrict__ base, int64_t ld,
+                                                  int row0, int nrows, int tid) {
+    Origin o;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = vec(i, tid);
+      if (LAY == K_MAJOR) {
+        const int row = min(row0 + v / (BK / 4), nrows - 1);
+        o.p[i] = base + (int64_t)row * ld + (v % (BK / 4)) * 4;
+      } else {
+        int row = row0 + (v % (ROWS / 4)) * 4;
+        row = row < nrows ? row : 0;
+        o.p[i] = base + (int64_t)(v / (ROWS / 4)) * ld + row;
+      }
+    }
+    return o;
+  }
+
   // Full K step, 16-byte aligned rows: plain vector loads with no
   // per-element control flow, so the loads of a K step stay in flight
-  // together.  Rows past the end (edge tiles) are clamped to a valid row:
-  // they only feed output rows / columns that are never stored.  For an
-  // M/N-major operand this needs nrows % 4 == 0 so that no vector straddles
-  // the end (checked by the caller).
+  // together.  `row0` is the tile's first row, as given to origin().
+  __device__ __forceinline__ void load_fast(const Origin& o, int64_t ld, int row0, int k0,
+                                            int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (LAY == K_MAJOR) r[i] = *reinterpret_cast<const f32x4*>(o.p[i] + k0);
+      else r[i] = *reinterpret_cast<const f32x4*>(o.p[i] + (int64_t)k0 * ld);
+    }
+    if (XF) {
+      if (kGroupK) load_group_stats(k0, k0 + BK, tid);
+      xk0 = k0;
+      xkend = k0 + BK;
+      xrow0 = row0;
+      xsafe = false;
+    }
+  }
+
+  // The same loads with every address formed in full.
   __device__ __forceinline__ void load_fast(const float* __restrict__ base, int64_t ld,
                                             int row0, int nrows, int k0, int tid) {
 #pragma unroll
@@ -367,10 +410,32 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
     la2.bind(d);
     la2.prime(tm * BM, M, tid);
   }
+  // Full K steps load from per-tile origins, except in the loss-gradient
+  // products (XF), whose loads form every address in full: their walking
+  // kernel has no registers to spare, and the origins measured slower there.
+  struct NoOrigin {};
+  using OA = typename std::conditional<XF, NoOrigin, typename LA::Origin>::type;
+  using OB = typename std::conditional<XF, NoOrigin, typename LB::Origin>::type;
+  OA oa;
+  OB ob;
+  if constexpr (!XF) {
+    oa = LA::origin(A, d.lda, tm * BM, M, tid);
+    ob = LB::origin(B, d.ldb, tn * BN, N, tid);
+  }
+#define DL_FAST_A(l, k0)                                                    \
+  do {                                                                      \
+    if constexpr (XF) l.load_fast(A, d.lda, tm * BM, M, k0, tid);           \
+    else l.load_fast(oa, d.lda, tm * BM, k0, tid);                          \
+  } while (0)
+#define DL_FAST_B(l, k0)                                                    \
+  do {                                                                      \
+    if constexpr (XF) l.load_fast(B, d.ldb, tn * BN, N, k0, tid);           \
+    else l.load_fast(ob, d.ldb, tn * BN, k0, tid);                          \
+  } while (0)
   if (nk > 0) {
     if (nk_full > 0) {
-      la.load_fast(A, d.lda, tm * BM, M, kbeg, tid);
-      lb.load_fast(B, d.ldb, tn * BN, N, kbeg, tid);
+      DL_FAST_A(la, kbeg);
+      DL_FAST_B(lb, kbeg);
     } else {
       la.load_safe(A, d.lda, tm * BM, M, kbeg, kend, tid);
       lb.load_safe(B, d.ldb, tn * BN, N, kbeg, kend, tid);
@@ -378,8 +443,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
     la.store(As(0), tid);
     lb.store(Bs(0), tid);
     if (nk_full >= 2) {
-      la2.load_fast(A, d.lda, tm * BM, M, kbeg + BK, tid);
-      lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + BK, tid);
+      DL_FAST_A(la2, kbeg + BK);
+      DL_FAST_B(lb2, kbeg + BK);
     }
   }
   __syncthreads();
@@ -398,8 +463,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
   int kt = 0;
   constexpr bool kMid = BK == 16 && ALAY == K_MAJOR && BLAY == K_MAJOR && !XF;
   for (; kt + 3 < nk_full; kt += 2) {
-    la.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 2) * BK, tid);
-    lb.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 2) * BK, tid);
+    DL_FAST_A(la, kbeg + (kt + 2) * BK);
+    DL_FAST_B(lb, kbeg + (kt + 2) * BK);
     // keep the loads ahead of the MFMAs (the scheduler would otherwise sink
     // them next to their LDS stores)
     __builtin_amdgcn_sched_barrier(0);
@@ -416,8 +481,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    la2.load_fast(A, d.lda, tm * BM, M, kbeg + (kt + 3) * BK, tid);
-    lb2.load_fast(B, d.ldb, tn * BN, N, kbeg + (kt + 3) * BK, tid);
+    DL_FAST_A(la2, kbeg + (kt + 3) * BK);
+    DL_FAST_B(lb2, kbeg + (kt + 3) * BK);
     __builtin_amdgcn_sched_barrier(0);
     if (kMid) {
       compute_mid(1, [&] {
@@ -445,8 +510,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
   for (; kt + 1 < nk_full; ++kt) {
     const int cur = kt & 1;
     const int k0 = kbeg + (kt + 1) * BK;
-    la.load_fast(A, d.lda, tm * BM, M, k0, tid);
-    lb.load_fast(B, d.ldb, tn * BN, N, k0, tid);
+    DL_FAST_A(la, k0);
+    DL_FAST_B(lb, k0);
     __builtin_amdgcn_sched_barrier(0);
     compute(cur);
     __builtin_amdgcn_sched_barrier(0);
@@ -470,6 +535,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmDesc& d, int split, int 
     }
     __syncthreads();
   }
+#undef DL_FAST_A
+#undef DL_FAST_B
 
   // ---- epilogue -------------------------------------------------------------
   if (EPI == EPI_DW && do_db) {
