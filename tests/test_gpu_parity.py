@@ -259,6 +259,47 @@ def test_bf16_persistent_dx_ragged(dl):
     assert_close(to_np(dX), rdX, BF16_TOL, "dX")
 
 
+# Output rows whose length is not a multiple of 4: no row allows 16-byte
+# access, so every wave of the direct-load epilogue takes its per-element
+# path for the stores, the bias and the saved activations.  4104 x 4106:
+# 289 tiles of 256 x 256 (one workgroup each); 8200 x 8202: 1089 tiles
+# (persistent).
+@pytest.mark.parametrize("B, n_out", [(4104, 4106), (8200, 8202)])
+@pytest.mark.parametrize("act", [O.ACT_IDENTITY, O.ACT_GELU_TANH])
+def test_bf16_fwd_unaligned_rows(dl, act, B, n_out):
+    n_in = 64
+    X = si.random_matrix(280, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(281, (n_out, n_in), scale=0.1, bf16_exact=True)
+    b = si.random_matrix(282, (n_out,), scale=0.01)
+    bf = torch.bfloat16
+    save_z = act != O.ACT_IDENTITY
+    Y, Z = dl.dense_act_fwd(to_dev(X, bf), to_dev(W, bf), to_dev(b), act, save_z=save_z)
+    refY, refZ = O.dense_act_fwd(X, W, b, act)
+    if save_z:
+        assert_close(to_np(Z), refZ, BF16_TOL, "Z")
+    assert_close(to_np(Y), refY, BF16_TOL, "Y")
+
+
+@pytest.mark.parametrize("B, n_in", [(4104, 4106), (8200, 8202)])
+def test_bf16_dx_unaligned_rows(dl, B, n_in):
+    n_out = 64
+    X = si.random_matrix(290, (B, n_in), bf16_exact=True)
+    W = si.random_matrix(291, (n_out, n_in), scale=0.1, bf16_exact=True)
+    Z = si.random_matrix(292, (B, n_out), bf16_exact=True)
+    dY = si.random_matrix(293, (B, n_out), bf16_exact=True)
+    H = si.random_matrix(294, (B, n_in), bf16_exact=True)
+    bf = torch.bfloat16
+    Wd = to_dev(W, bf)
+    # the transposed copy keeps the direct-load kernel (an M/N-major W would
+    # need n_in % 8 == 0); the previous layer's GELU derivative folded in
+    dX, _, _ = dl.dense_act_vjp(to_dev(dY, bf), to_dev(Z, bf), None, Wd, O.ACT_GELU_TANH,
+                                need_dw=False, dx_act=O.ACT_GELU_TANH, dx_saved=to_dev(H, bf),
+                                Wt=Wd.t().contiguous())
+    rdX, _, _ = O.dense_act_vjp(dY, Z, X, W, O.ACT_GELU_TANH, need_dx=True)
+    rdX = rdX * O.act_grad(H, O.ACT_GELU_TANH)
+    assert_close(to_np(dX), rdX, BF16_TOL, "dX")
+
+
 def test_bf16_dw_wide_tile_ragged(dl):
     """A large weight gradient (register-staged 128x128 tiles, split along
     the batch), ragged in both output dimensions."""
