@@ -117,18 +117,25 @@ template <> struct Elem<f16_t> {
 // needed.  The reciprocal is the hardware one (about 1 ulp), well inside the
 // float32 tolerance of the results.
 
-constexpr float kSqrt2OverPi = 0.7978845608028654f;
-constexpr float kGeluCubic = 0.044715f;
-constexpr float kTwoLog2e = 2.8853900817779268f;  // 2 / ln 2
+// 2u log2(e) = z (kX0 + kX2 z^2) and 2u' = kD0 + kD2 z^2, each constant
+// formed in double and rounded once, so that each polynomial is one fused
+// multiply-add.
+constexpr double kSqrt2OverPi = 0.7978845608028654;
+constexpr double kGeluCubic = 0.044715;
+constexpr double kTwoLog2e = 2.8853900817779268;  // 2 / ln 2
+constexpr float kX0 = (float)(kTwoLog2e * kSqrt2OverPi);
+constexpr float kX2 = (float)(kTwoLog2e * kSqrt2OverPi * kGeluCubic);
+constexpr float kD0 = (float)(2.0 * kSqrt2OverPi);
+constexpr float kD2 = (float)(2.0 * kSqrt2OverPi * 3.0 * kGeluCubic);
 
 __device__ __forceinline__ float gelu_r(float z, float z2) {
-  const float x = z * (kTwoLog2e * kSqrt2OverPi) * (1.0f + kGeluCubic * z2);
+  const float x = z * fmaf(kX2, z2, kX0);
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
 __device__ __forceinline__ float act_apply(int act, float z) {
   if (act == ACT_RELU) return z > 0.0f ? z : 0.0f;
-  if (act == ACT_GELU_TANH) return z - z * gelu_r(z, z * z);
+  if (act == ACT_GELU_TANH) return fmaf(-z, gelu_r(z, z * z), z);
   return z;
 }
 
@@ -139,8 +146,8 @@ __device__ __forceinline__ float act_deriv(int act, float z) {
   if (act == ACT_GELU_TANH) {
     const float z2 = z * z;
     const float r = gelu_r(z, z2);
-    const float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * z2);
-    return (1.0f - r) * (1.0f + 2.0f * z * r * du);
+    const float t = z * fmaf(kD2, z2, kD0);  // 2 z u'
+    return (1.0f - r) * fmaf(t, r, 1.0f);
   }
   return 1.0f;
 }
