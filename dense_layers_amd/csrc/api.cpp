@@ -1272,6 +1272,17 @@ static bool mlp_pair(int64_t B, const dl_layer_t& ly) {
   return p.tile == 1 && 2.0 * (double)B * (double)ly.in * (double)ly.out <= 8589934592.0;
 }
 
+// Whether layer l (l > 0, not paired) can take a plain SGD step inside its
+// weight-gradient launch: one K slice, so each tile holds its finished dW and
+// the epilogue can step W (and b) with it.  Its dX then runs first, into a
+// gradient buffer of its own: dX reads W, and the weight gradient still reads
+// the layer input that the in-place dX would overwrite.  (Shapes only; the
+// step also needs plain SGD with no gradient pass, averages or device step
+// count.)
+static bool mlp_sgd_in_dw_shape(int64_t B, int32_t L, const dl_layer_t* layers, int l, bool xent) {
+  return l > 0 && !mlp_pair(B, layers[l]) && mlp_dw_plan(B, L, layers, l, xent).splits == 1;
+}
+
 // Gradient-control partials of the MLP step: one gradient pass over all W and
 // b (at most 32 arrays, one launch).
 static int64_t mlp_stat_parts(int32_t L, const dl_layer_t* layers) {
@@ -1319,7 +1330,7 @@ static size_t mlp_layout(int64_t B, int32_t L, const dl_layer_t* layers, bool xe
     gb = align_up((size_t)B * layers[L - 2].in * 4);
   }
   for (int l = 1; l <= last_gemm; ++l)
-    if (mlp_pair(B, layers[l])) {
+    if (mlp_pair(B, layers[l]) || mlp_sgd_in_dw_shape(B, L, layers, l, xent)) {
       ++pairs;
       gb = std::max(gb, align_up((size_t)B * layers[l].in * 4));
     }
@@ -1594,9 +1605,30 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
       G = gbuf[0];
     }
   }
+  // plain SGD: layers whose weight gradient has one K slice step W and b in
+  // its epilogue (the same arithmetic as the optimizer launch), after their dX
+  const bool sgd_epi = opt->kind == DL_OPT_SGD && !ctl_on && !dev_step && !any_ema;
+  const float sgd_lr = sgd_epi ? opt_consts(*opt, opt->step).lr : 0.0f;
+  bool stepped[16] = {};
   for (int l = first_bwd; l >= 0; --l) {
     const dl_layer_t& ly = layers[l];
     const float* in = l == 0 ? X : Y[l - 1];
+    if (sgd_epi && mlp_sgd_in_dw_shape(B, L, layers, l, xent) &&
+        ((reinterpret_cast<uintptr_t>(ly.W) ^ reinterpret_cast<uintptr_t>(ly.dW)) & 15) == 0) {
+      float* Gn = G == gbuf[0] ? gbuf[1] : gbuf[0];
+      e = dx_gemm(DL_F32, B, ly.in, ly.out, G, ly.W, nullptr, Gn, layers[l - 1].act, Y[l - 1], s);
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dX)");
+      const Plan pl = mlp_dw_plan(B, L, layers, l, xent);
+      dl::GemmDesc d = dw_desc(DL_F32, B, ly.in, ly.out, G, in, ly.dW, ly.db, nullptr, pl);
+      d.sgd_w = ly.W;
+      d.sgd_b = ly.b;
+      d.sgd_lr = sgd_lr;
+      e = timed("dw_gemm", s, [&] { return run_gemm(DL_F32, d, pl.tile, s); });
+      if (e != hipSuccess) return hip_fail(e, "mlp_train_step (dW + SGD)");
+      stepped[l] = true;
+      G = Gn;
+      continue;
+    }
     if (l > 0 && mlp_pair(B, ly)) {
       float* Gn = G == gbuf[0] ? gbuf[1] : gbuf[0];
       const Plan p = mlp_dw_plan(B, L, layers, l, xent);
@@ -1627,6 +1659,7 @@ static int mlp_step(void* stream, int64_t B, int32_t n_layers, const dl_layer_t*
   dl::OptSegs stat = blank_segs();
   int64_t blocks = 0, units = 0;
   for (int l = 0; l < L; ++l) {
+    if (stepped[l]) continue;  // stepped inside its weight-gradient launch
     const dl_layer_t& ly = layers[l];
     const int64_t S = mlp_slices(B, L, layers, l, xent, narrow);
     char* pb = base + part_off[l];
