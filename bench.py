@@ -116,11 +116,16 @@ class MLPBench:
     def _layers_of_labels(self):
         """Layer of each backward / split-forward launch, from the step's
         launch order: the backward runs from the last GEMM layer down, each
-        layer as dwdx_gemm, or dw_gemm then (above layer 0) dx_gemm."""
+        layer as dwdx_gemm, dw_gemm then (above layer 0) dx_gemm, or, when
+        the weight-gradient launch also takes the SGD step, dx_gemm then
+        dw_gemm (those layers are listed in self.stepped)."""
         labels = getattr(self, "labels", ())
         tail = "mlp_tail#0" in labels
         last = self.w.n_layers - (2 if tail or "head_xent#0" in labels else 1)
         out, cur, fwd = {}, last, -1
+        open_dw = False     # a dw_gemm whose layer's dx_gemm follows
+        dx_first = None     # a dx_gemm whose layer's dw_gemm follows
+        self.stepped = set()
         for lab in labels:
             name, _ = _split(lab)
             if name == "fwd_gemm":
@@ -134,13 +139,25 @@ class MLPBench:
                 out[lab] = cur
                 cur -= 2
             elif name == "dw_gemm":
-                out[lab] = cur
-                if cur == 0 or tail:  # no dX launch follows (first layer, or the tail's)
+                if dx_first is not None:  # the same layer's, with its SGD step
+                    out[lab] = dx_first
+                    self.stepped.add(dx_first)
+                    dx_first = None
                     cur -= 1
+                else:
+                    out[lab] = cur
+                    if cur == 0 or tail:  # no dX launch follows (first layer, or the tail's)
+                        cur -= 1
+                    else:
+                        open_dw = True
                 tail = False
             elif name == "dx_gemm":
                 out[lab] = cur
-                cur -= 1
+                if open_dw:
+                    open_dw = False
+                    cur -= 1
+                else:
+                    dx_first = cur
         return out
 
     def __init__(self, dl, w, dev):
@@ -216,7 +233,9 @@ class MLPBench:
         elif name == "loss_mean":
             return "byte", 4 * B
         elif name in ("adamw_multi", "sgd_multi"):
-            return "byte", (28 if name == "adamw_multi" else 12) * w.n_params()
+            stepped = getattr(self, "stepped", set())
+            n = w.n_params() - sum(w.dims[l] * w.dims[l + 1] + w.dims[l + 1] for l in stepped)
+            return "byte", (28 if name == "adamw_multi" else 12) * n
         else:
             return None
         return "flop", 2 * B * w.dims[l] * w.dims[l + 1]
@@ -246,7 +265,8 @@ class MLPBench:
             return gemm_bytes("fwd", B, d[k + 1], d[k], bias=True)
         if name == "dw_gemm":
             l = layer[label]
-            return gemm_bytes("dw", d[l + 1], d[l], B, db=True)
+            sgd = 8 * (d[l + 1] * d[l] + d[l + 1]) if l in self.stepped else 0  # W, b in and out
+            return gemm_bytes("dw", d[l + 1], d[l], B, db=True) + sgd
         if name == "dx_gemm":
             l = layer[label]
             return gemm_bytes("dx", B, d[l], d[l + 1], mask=True)

@@ -612,7 +612,11 @@ typedef struct dl_layer {
  * gradient, a step with non-finite gradients is skipped); and the parameter
  * averages of the layers that have eW / eb (all or none).  With clipping or
  * a loss scaler the split weight-gradient sums are finished by the gradient
- * pass rather than the optimizer.
+ * pass rather than the optimizer.  With plain SGD and none of those options
+ * (nor a device step count), a hidden layer whose weight gradient runs as
+ * one K slice takes its SGD step inside that launch, after its dX, with the
+ * optimizer's arithmetic; the workspace holds the gradient buffers this
+ * order needs.
  *
  *   B > 0; n_layers in [1, 16]; layers is a host array of n_layers entries.
  *   X        device float32 [B, layers[0].in]
