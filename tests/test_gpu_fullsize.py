@@ -48,6 +48,8 @@ def test_mlp_wide_full_batch_sgd_step(dl):
     gm = _gpu_relu_masks(dl, inp.X, st.W, st.b, w.acts)
     masks, adopted = _adopted_masks(gm, st, inp.X, w.acts)
     print(f"adopted ReLU decisions within the rounding band: {adopted}")
+    W0 = [np.array(a, dtype=np.float64) for a in inp.W]
+    b0 = [np.array(a, dtype=np.float64) for a in inp.b]
     loss = float(dl.mlp_train_step(mlp, to_dev(inp.X), to_dev(inp.labels), dl.OPT_SGD,
                                    lr=w.optim.lr, step=1).item())
     ref = O.mlp_train_step(st, inp.X, inp.labels, w.acts, w.optim, relu_masks=masks)
@@ -57,6 +59,18 @@ def test_mlp_wide_full_batch_sgd_step(dl):
         assert_close(to_np(mlp.db[l]), ref["db"][l], F32_TOL, f"db{l}")
         assert_close(to_np(mlp.W[l]), st.W[l], F32_TOL, f"W{l}")
         assert_close(to_np(mlp.b[l]), st.b[l], F32_TOL, f"b{l}")
+        # the update itself, which a normwise check of W hides under W:
+        # both sides round W - lr dW to float32 once (at most one ulp apart)
+        # on top of lr times the gradient's own difference
+        for name, got, want, p0, g in (("W", mlp.W[l], st.W[l], W0[l], ref["dW"][l]),
+                                       ("b", mlp.b[l], st.b[l], b0[l], ref["db"][l])):
+            d_gpu = to_np(got).astype(np.float64) - p0
+            d_ref = np.asarray(want, dtype=np.float64) - p0
+            tol = w.optim.lr * F32_TOL * np.abs(g).max() + 2.0 ** -23 * np.abs(p0).max()
+            err = np.abs(d_gpu - d_ref).max()
+            print(f"{name}{l} update: max |ref| {np.abs(d_ref).max():.3e}, error {err:.3e}, "
+                  f"bound {tol:.3e}")
+            assert err <= tol, (name, l, err, tol)
 
 
 def test_tmlp_bf16_full_tokens(dl):
