@@ -758,7 +758,22 @@ def _check_one_step(dl, w, inp, mlp, Xd, yd, st):
                 _assert_close_band(to_np(gv_), wv_, bv, F32_TOL, f"step {t} v{name}{l}")
             else:
                 assert_close(to_np(got), want, F32_TOL, f"step {t} {name}{l}")
+                _assert_sgd_update(to_np(got), want, w0, g, o.lr, f"step {t} {name}{l}")
     return ref["loss"], adopted
+
+
+def _assert_sgd_update(got, want, p0, g, lr, what):
+    """The SGD update p - p0 on its own, which a normwise check of p hides
+    under p itself: both sides round p0 - lr g to float32 once (at most one
+    ulp of p apart), on top of lr times the gradient's own normwise
+    difference (F32_TOL, checked before)."""
+    p0 = np.asarray(p0, dtype=np.float64)
+    d_gpu = np.asarray(got, dtype=np.float64) - p0
+    d_ref = np.asarray(want, dtype=np.float64) - p0
+    scale = max(np.abs(p0).max(), np.abs(np.asarray(want, dtype=np.float64)).max())
+    tol = lr * F32_TOL * np.abs(g).max() + 2.0 ** -23 * scale
+    err = np.abs(d_gpu - d_ref).max()
+    assert err <= tol, (what, err, tol, np.abs(d_ref).max())
 
 
 def _trajectory(dl, w, steps, check_steps, batch=None):
